@@ -1,0 +1,197 @@
+"""Oracle decoders: whole, patch-halo (mode A) and overlap-blend (mode B). Channels-last, float64.
+
+Test infrastructure: only tests, the smoke check and the benchmark's CPU-baseline leg use it.
+
+The layer plan and parameters come from ``vae_synth``: a list of ops and a parameter list in plan
+order. A residual block is GN+SiLU, conv, GN+SiLU, conv, plus its input.
+
+``decode_patch_halo`` deliberately does not call ``decode``. It is the patch-sharded computation of
+"Add tiled VAE parallelism & extended model support" (PatchConv3d / PatchGroupNorm commit messages):
+- every patch keeps its own activation;
+- a convolution gathers a one-row/column halo from the neighbouring patches and pads zeros only
+  where the patch meets the true image border;
+- GroupNorm merges per-patch (count, mean, M2) with Chan's formula before normalising.
+It must reproduce the whole decode, which tests pin.
+
+``decode_overlap_blend`` is the serial tiled decode of "[TRTLLM-14029][feat] LTX-2 tile-parallel VAE
+decode" (Description and Approach). Each tile is decoded on its own with its own borders and
+GroupNorm statistics. The tile is then blended into a full-size buffer, its weights go into a weight
+buffer, and the buffer is divided by the weights at the end.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .layers import causal_conv3d, causal_time_pad, conv3d_valid, group_norm, silu, \
+    nearest_upsample, depth_to_space
+from .stats import group_moments, chan_combine, normalize_with
+from .tiling import bands, overlap_tiles, ramp_1d
+
+
+def output_shape(spec: dict, latent_shape):
+    """[N, T, H, W, C] of the decoder output for an NDHWC latent shape, following the plan."""
+    n, t, h, w, c = latent_shape
+    for op in spec["layers"]:
+        k = op["op"]
+        if k == "conv":
+            c = op["cout"]
+        elif k == "d2s":
+            st, sh, sw = op["st"], op["sh"], op["sw"]
+            t, h, w, c = st * t - (st - 1), h * sh, w * sw, c // (st * sh * sw)
+        elif k == "nearest":
+            h, w = h * op["sh"], w * op["sw"]
+    return (n, t, h, w, c)
+
+
+# ------------------------------------------------------------------------------------------------
+# Whole decode
+# ------------------------------------------------------------------------------------------------
+
+def decode(spec: dict, z: np.ndarray, params: list) -> np.ndarray:
+    """Untiled decode of the NDHWC latent ``z``; returns the NDHWC float64 output."""
+    groups, eps = spec["groups"], spec["eps"]
+    it = iter(params)
+    h = np.asarray(z, dtype=np.float64)
+    for op in spec["layers"]:
+        k = op["op"]
+        if k == "conv":
+            p = next(it)
+            h = causal_conv3d(h, p["w"], p["b"])
+        elif k == "res":
+            g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+            t = silu(group_norm(h, groups, eps, g1["gamma"], g1["beta"]))
+            t = causal_conv3d(t, c1["w"], c1["b"])
+            t = silu(group_norm(t, groups, eps, g2["gamma"], g2["beta"]))
+            h = causal_conv3d(t, c2["w"], c2["b"]) + h
+            del t
+        elif k == "gn_silu":
+            g = next(it)
+            h = silu(group_norm(h, groups, eps, g["gamma"], g["beta"]))
+        elif k == "d2s":
+            h = depth_to_space(h, op["st"], op["sh"], op["sw"])
+        elif k == "nearest":
+            h = nearest_upsample(h, op["sh"], op["sw"])
+        else:
+            raise ValueError(k)
+    return h
+
+
+# ------------------------------------------------------------------------------------------------
+# Mode A: patch-halo decode
+# ------------------------------------------------------------------------------------------------
+
+def _starts(sizes):
+    return [int(s) for s in np.concatenate([[0], np.cumsum(sizes)[:-1]])]
+
+
+def _conv_patches(patches, w, b):
+    """Convolve every patch with a one-row/column halo gathered from the other patches."""
+    rows = [row[0].shape[2] for row in patches]
+    cols = [p.shape[3] for p in patches[0]]
+    r_at, c_at = _starts(rows), _starts(cols)
+    n, t, _, _, c = patches[0][0].shape
+    out = []
+    for i in range(len(rows)):
+        out_row = []
+        for j in range(len(cols)):
+            r0, r1 = r_at[i] - 1, r_at[i] + rows[i] + 1     # halo-extended region
+            c0, c1 = c_at[j] - 1, c_at[j] + cols[j] + 1
+            ext = np.zeros((n, t, r1 - r0, c1 - c0, c))    # outside the image: zero padding
+            for a in range(len(rows)):
+                lo_r, hi_r = max(r0, r_at[a]), min(r1, r_at[a] + rows[a])
+                if lo_r >= hi_r:
+                    continue
+                for bb in range(len(cols)):
+                    lo_c, hi_c = max(c0, c_at[bb]), min(c1, c_at[bb] + cols[bb])
+                    if lo_c >= hi_c:
+                        continue
+                    ext[:, :, lo_r - r0:hi_r - r0, lo_c - c0:hi_c - c0] = \
+                        patches[a][bb][:, :, lo_r - r_at[a]:hi_r - r_at[a],
+                                       lo_c - c_at[bb]:hi_c - c_at[bb]]
+            y = conv3d_valid(causal_time_pad(ext, 3), w, b)
+            # a convolved patch keeps the size of the patch it came from
+            assert y.shape[2:4] == (rows[i], cols[j]), (y.shape, rows[i], cols[j])
+            out_row.append(y)
+        out.append(out_row)
+    return out
+
+
+def _gn_patches(patches, groups, eps, gamma, beta, act):
+    """GroupNorm over the union of all patches via per-patch moments merged with Chan's formula."""
+    parts = [group_moments(p, groups) for row in patches for p in row]   # owned positions only
+    n, mean, m2 = chan_combine(parts)
+    var = m2 / n                                                          # biased
+    out = [[normalize_with(p, groups, mean, var, eps, gamma, beta) for p in row] for row in patches]
+    if act:
+        out = [[silu(p) for p in row] for row in out]
+    return out
+
+
+def decode_patch_halo(spec: dict, z: np.ndarray, params: list, grid) -> np.ndarray:
+    """Decode with the latent cut into ph x pw patches (bands along H and W)."""
+    ph, pw = grid
+    groups, eps = spec["groups"], spec["eps"]
+    z = np.asarray(z, dtype=np.float64)
+    hb = bands(z.shape[2], ph)
+    wb = bands(z.shape[3], pw)
+    patches = [[z[:, :, h0:h0 + hs, w0:w0 + ws] for (w0, ws) in wb] for (h0, hs) in hb]
+    it = iter(params)
+    for op in spec["layers"]:
+        k = op["op"]
+        if k == "conv":
+            p = next(it)
+            patches = _conv_patches(patches, p["w"], p["b"])
+        elif k == "res":
+            g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+            t = _gn_patches(patches, groups, eps, g1["gamma"], g1["beta"], True)
+            t = _conv_patches(t, c1["w"], c1["b"])
+            t = _gn_patches(t, groups, eps, g2["gamma"], g2["beta"], True)
+            t = _conv_patches(t, c2["w"], c2["b"])
+            patches = [[a + bb for a, bb in zip(ra, rb)] for ra, rb in zip(t, patches)]
+        elif k == "gn_silu":
+            g = next(it)
+            patches = _gn_patches(patches, groups, eps, g["gamma"], g["beta"], True)
+        elif k == "d2s":
+            patches = [[depth_to_space(p, op["st"], op["sh"], op["sw"]) for p in row]
+                       for row in patches]
+        elif k == "nearest":
+            patches = [[nearest_upsample(p, op["sh"], op["sw"]) for p in row] for row in patches]
+        else:
+            raise ValueError(k)
+    return np.concatenate([np.concatenate(row, axis=3) for row in patches], axis=2)
+
+
+# ------------------------------------------------------------------------------------------------
+# Mode B: overlap-blend decode
+# ------------------------------------------------------------------------------------------------
+
+def merge_tiles(tile_outputs, tiles, out_shape) -> np.ndarray:
+    """Blend per-tile outputs into the full output: sum(w * y) / sum(w), weights accumulated."""
+    acc = np.zeros(out_shape, dtype=np.float64)
+    wsum = np.zeros(tuple(out_shape[:4]) + (1,), dtype=np.float64)
+    for y, tl in zip(tile_outputs, tiles):
+        t0, t1, h0, h1, w0, w1 = tl["out"]
+        rt = ramp_1d(t1 - t0, tl["lead"][0], tl["trail"][0])
+        rh = ramp_1d(h1 - h0, tl["lead"][1], tl["trail"][1])
+        rw = ramp_1d(w1 - w0, tl["lead"][2], tl["trail"][2])
+        wt = (rt[:, None, None] * rh[None, :, None] * rw[None, None, :])[None, ..., None]
+        acc[:, t0:t1, h0:h1, w0:w1] += np.asarray(y, dtype=np.float64) * wt
+        wsum[:, t0:t1, h0:h1, w0:w1] += wt
+    return acc / wsum
+
+
+def decode_overlap_blend(spec: dict, z: np.ndarray, params: list, tile_hw, stride_hw,
+                         scale) -> np.ndarray:
+    """Serial overlap-blend tiled decode of the NDHWC latent ``z``."""
+    z = np.asarray(z, dtype=np.float64)
+    _, t, h, w, _ = z.shape
+    tiles = overlap_tiles(t, h, w, tile_hw, stride_hw, scale)
+    out_shape = output_shape(spec, z.shape)
+    outs = []
+    for tl in tiles:
+        _, _, h0, h1, w0, w1 = tl["latent"]
+        y = decode(spec, z[:, :, h0:h1, w0:w1], params)    # own borders, own statistics
+        o = tl["out"]
+        assert y.shape[1:4] == (o[1] - o[0], o[3] - o[2], o[5] - o[4]), (y.shape, o)
+        outs.append(y)
+    return merge_tiles(outs, tiles, out_shape)

@@ -1,0 +1,136 @@
+"""Oracle layers: causal Conv3d, GroupNorm, SiLU, upsampling. Channels-last, float64.
+
+Test infrastructure: only tests, the smoke check and the benchmark's CPU-baseline leg use it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Size cap (elements) of the unfolded input built per batch of output frames inside the
+# convolution. It bounds memory only: every output element is the same full sum either way.
+_COLS_ELEMENTS = 1 << 26
+
+
+def causal_time_pad(x: np.ndarray, k_t: int = 3) -> np.ndarray:
+    """Prepend k_t-1 copies of frame 0 along T.
+
+    Causal temporal padding repeats the first frame, one-sided, along an axis that is never split
+    ("Add tiled VAE parallelism & extended model support", commit messages on the LTX-2 decoder
+    adapter and on the HunyuanVideo causal decoders).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return np.concatenate([x[:, :1]] * (k_t - 1) + [x], axis=1)
+
+
+def conv3d_valid(xp: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
+    """Valid (unpadded) 3-D cross-correlation, stride 1.
+
+    xp: [N, T+kt-1, H+kh-1, W+kw-1, Cin] (already padded); w: [Cout, Cin, kt, kh, kw].
+    y[n, t, h, w, o] = b[o] + sum_{c, a, p, q} w[o, c, a, p, q] * xp[n, t+a, h+p, w+q, c].
+    Evaluated as one matmul of the unfolded input cols[.., (a, p, q), c] = xp[n, t+a, h+p, w+q, c]
+    with the weights laid out as wmat[o, (a, p, q), c] = w[o, c, a, p, q].
+    """
+    xp = np.asarray(xp, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    n, tp, hp, wp, cin = xp.shape
+    cout, cin2, kt, kh, kw = w.shape
+    assert cin == cin2, (cin, cin2)
+    t_out, h_out, w_out = tp - kt + 1, hp - kh + 1, wp - kw + 1
+    assert t_out >= 1 and h_out >= 1 and w_out >= 1, xp.shape
+    wmat = np.ascontiguousarray(w.transpose(0, 2, 3, 4, 1)).reshape(cout, kt * kh * kw * cin)
+    y = np.empty((n, t_out, h_out, w_out, cout), dtype=np.float64)
+    step = max(1, min(t_out, _COLS_ELEMENTS // (n * h_out * w_out * wmat.shape[1])))
+    # buffers reused across frame batches (frame-batch axis first so every batch is contiguous)
+    cols = np.empty((step, n, h_out, w_out, kt * kh * kw, cin), dtype=np.float64)
+    prod = np.empty((step * n * h_out * w_out, cout), dtype=np.float64)
+    for t0 in range(0, t_out, step):
+        m = min(step, t_out - t0)
+        k = 0
+        for a in range(kt):
+            for p in range(kh):
+                for q in range(kw):
+                    cols[:m, :, :, :, k, :] = \
+                        xp[:, t0 + a:t0 + a + m, p:p + h_out, q:q + w_out, :].swapaxes(0, 1)
+                    k += 1
+        rows = m * n * h_out * w_out
+        np.matmul(cols[:m].reshape(rows, -1), wmat.T, out=prod[:rows])
+        y[:, t0:t0 + m] = prod[:rows].reshape(m, n, h_out, w_out, cout).swapaxes(0, 1)
+    if b is not None:
+        y += np.asarray(b, dtype=np.float64)
+    return y
+
+
+def causal_conv3d(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
+    """Causal Conv3d, kernel 3x3x3, stride 1, on a whole (unsplit) tensor.
+
+    Temporal: two copies of frame 0 in front, so output frame t sees input frames t-2..t, clamped
+    at 0. Spatial: one row/column of zeros on every side; zeros appear only at the true image
+    border ("Add tiled VAE parallelism & extended model support", commit message on how the direct
+    path pads a patch; the single-conv workload states zero padding 1).
+    """
+    w = np.asarray(w)
+    _, _, kt, kh, kw = w.shape
+    xp = causal_time_pad(x, kt)
+    xp = np.pad(xp, ((0, 0), (0, 0), (kh // 2, kh // 2), (kw // 2, kw // 2), (0, 0)))
+    return conv3d_valid(xp, w, b)
+
+
+def group_norm(x: np.ndarray, groups: int, eps: float, gamma=None, beta=None) -> np.ndarray:
+    """torch.nn.GroupNorm's definition: per (sample, group), over the group's channels and T, H, W.
+
+    mean = average; var = average of squared deviations from that mean (biased, divide by the
+    count, no Bessel correction); y = (x - mean) / sqrt(var + eps) * gamma + beta. The DistVAE
+    PatchGroupNorm fix names exactly these two properties: the global mean and the count as divisor
+    ("Add tiled VAE parallelism & extended model support", PatchGroupNorm commit message).
+    Two passes: the mean first, then the squared deviations about it.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, c = x.shape[0], x.shape[-1]
+    assert c % groups == 0, (c, groups)
+    xg = x.reshape(n, -1, groups, c // groups)
+    y = np.empty_like(xg)
+    for g in range(groups):
+        part = xg[:, :, g, :]
+        mean = part.mean(axis=(1, 2), keepdims=True)
+        dev = part - mean
+        var = (dev * dev).mean(axis=(1, 2), keepdims=True)
+        y[:, :, g, :] = dev / np.sqrt(var + eps)
+    y = y.reshape(x.shape)
+    if gamma is not None:
+        y *= np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        y += np.asarray(beta, dtype=np.float64)
+    return y
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def nearest_upsample(x: np.ndarray, sh: int, sw: int) -> np.ndarray:
+    """out[t, h, w] = in[t, h // sh, w // sw]."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.repeat(np.repeat(x, sh, axis=2), sw, axis=3)
+
+
+def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
+    """Depth-to-space upsampling, then causal drop of the first st-1 frames.
+
+    The upsampler moves channels into space, one input position per output ("Add tiled VAE
+    parallelism & extended model support", LTX-2 decoder adapter commit message). The pages do not fix
+    the channel order. Here input channel ((dt*sh + dh)*sw + dw)*C + c feeds output channel c at
+    (st*t + dt, sh*h + dh, sw*w + dw): the sub-position is slowest and the channel fastest. With
+    st > 1 the first st-1 frames are dropped, so T frames become st*T - (st-1) (16 -> 31 -> 61 -> 121
+    for the LTX-2-shaped workload).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, t, h, w, ck = x.shape
+    k = st * sh * sw
+    assert ck % k == 0, (ck, k)
+    c = ck // k
+    y = x.reshape(n, t, h, w, st, sh, sw, c)
+    y = y.transpose(0, 1, 4, 2, 5, 3, 6, 7).reshape(n, t * st, h * sh, w * sw, c)
+    return np.ascontiguousarray(y[:, st - 1:])

@@ -1,0 +1,131 @@
+"""Pins of the oracle decoders: the patch-halo decode must equal the whole decode, a 1x1
+overlap-blend grid must equal the whole decode, shapes follow the plan. No GPU."""
+import numpy as np
+import pytest
+
+import oracle
+import vae_synth
+
+
+def ndhwc(a):
+    return np.ascontiguousarray(np.asarray(a).transpose(0, 2, 3, 4, 1))
+
+
+def _conv_gn_spec():
+    s = vae_synth.CONV_GN
+    return {"groups": s["groups"], "eps": s["eps"],
+            "layers": [{"op": "conv", "cin": 32, "cout": 32}, {"op": "gn_silu"}]}
+
+
+def _conv_gn_params(affine_seed=None):
+    s = vae_synth.CONV_GN
+    return [vae_synth.conv_params(0, s["cin"], s["cout"], "f32", affine_seed),
+            vae_synth.gn_params(0, s["cout"], affine_seed)]
+
+
+@pytest.mark.parametrize("affine", [None, 5])
+def test_single_conv_gn_patches_equal_whole(affine):
+    """Single conv + GN(8) + SiLU on [1,32,5,32,32], whole vs two width patches of 16 columns."""
+    x = ndhwc(vae_synth.latent(vae_synth.CONV_GN))
+    spec, params = _conv_gn_spec(), _conv_gn_params(affine)
+    whole = oracle.decode(spec, x, params)
+    split = oracle.decode_patch_halo(spec, x, params, (1, 2))
+    assert whole.shape == (1, 5, 32, 32, 32)
+    rel = np.abs(split - whole).max() / np.abs(whole).max()
+    assert rel < 1e-12, rel
+
+
+def test_tiny_decoder_shapes_and_patch_halo_equals_whole():
+    spec = vae_synth.TINY_DECODER
+    z = ndhwc(vae_synth.latent(spec))
+    params = vae_synth.decoder_params(spec, affine_seed=3)
+    whole = oracle.decode(spec, z, params)
+    assert whole.shape == (1, 5, 64, 64, 3) == oracle.output_shape(spec, z.shape)
+    for grid in [(2, 2), (1, 3), (3, 1)]:
+        split = oracle.decode_patch_halo(spec, z, params, grid)
+        rel = np.abs(split - whole).max() / np.abs(whole).max()
+        assert rel < 1e-11, (grid, rel)
+
+
+def test_overlap_blend_single_tile_is_whole_decode():
+    spec = vae_synth.TINY_DECODER
+    z = ndhwc(vae_synth.latent(spec))
+    params = vae_synth.decoder_params(spec)
+    whole = oracle.decode(spec, z, params)
+    one = oracle.decode_overlap_blend(spec, z, params, (16, 16), (16, 16), spec["scale"])
+    assert np.array_equal(one, whole)
+
+
+def test_overlap_blend_differs_from_whole_only_by_tiling():
+    """Mode B uses per-tile GroupNorm statistics and borders, so it must not equal the untiled
+    decode; it is finite, has the right shape, and stays close in scale."""
+    spec = vae_synth.TINY_DECODER
+    z = ndhwc(vae_synth.latent(spec))
+    params = vae_synth.decoder_params(spec)
+    whole = oracle.decode(spec, z, params)
+    tiled = oracle.decode_overlap_blend(spec, z, params, spec["overlap_tile"],
+                                        spec["overlap_stride"], spec["scale"])
+    assert tiled.shape == whole.shape and np.all(np.isfinite(tiled))
+    diff = np.abs(tiled - whole).max()
+    assert 1e-6 < diff < 10 * np.abs(whole).max()
+
+
+def test_ltx2_small_patch_halo_equals_whole():
+    spec = vae_synth.LTX2_SMALL
+    z = ndhwc(vae_synth.latent(spec))
+    params = vae_synth.decoder_params(spec)
+    whole = oracle.decode(spec, z, params)
+    assert whole.shape == oracle.output_shape(spec, z.shape) == (1, 9, 96, 160, 3)
+    split = oracle.decode_patch_halo(spec, z, params, spec["patch_grid"])
+    assert np.abs(split - whole).max() / np.abs(whole).max() < 1e-11
+
+
+def test_720p_output_shape():
+    spec = vae_synth.LTX2_720P
+    assert oracle.output_shape(spec, (1, 16, 22, 40, 128)) == (1, 121, 704, 1280, 3)
+    assert oracle.output_shape(vae_synth.LTX2_MID, (1, 3, 4, 6, 128)) == (1, 17, 128, 192, 3)
+
+
+def _torch_decode(spec, z, params):
+    """The same layer plan built from torch CPU library ops (float64, NCDHW)."""
+    import torch
+    import torch.nn.functional as F
+    g, eps = spec["groups"], spec["eps"]
+    it = iter(params)
+
+    def conv(h, p):
+        hp = F.pad(torch.cat([h[:, :, :1], h[:, :, :1], h], dim=2), (1, 1, 1, 1, 0, 0))
+        return F.conv3d(hp, torch.from_numpy(p["w"]).double(), torch.from_numpy(p["b"]).double())
+
+    def gn(h, p):
+        return F.silu(F.group_norm(h, g, torch.from_numpy(p["gamma"]).double(),
+                                   torch.from_numpy(p["beta"]).double(), eps))
+
+    h = torch.from_numpy(z).double().permute(0, 4, 1, 2, 3)
+    for op in spec["layers"]:
+        k = op["op"]
+        if k == "conv":
+            h = conv(h, next(it))
+        elif k == "res":
+            g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+            h = conv(gn(conv(gn(h, g1), c1), g2), c2) + h
+        elif k == "gn_silu":
+            h = gn(h, next(it))
+        elif k == "nearest":
+            h = F.interpolate(h, scale_factor=(1, op["sh"], op["sw"]), mode="nearest")
+        elif k == "d2s":
+            st, sh, sw = op["st"], op["sh"], op["sw"]
+            n, ck, t, hh, ww = h.shape
+            c = ck // (st * sh * sw)
+            h = h.reshape(n, st, sh, sw, c, t, hh, ww).permute(0, 4, 5, 1, 6, 2, 7, 3)
+            h = h.reshape(n, c, t * st, hh * sh, ww * sw)[:, :, st - 1:]
+    return h.permute(0, 2, 3, 4, 1).numpy()
+
+
+def test_tiny_decoder_matches_torch_library_graph():
+    spec = vae_synth.TINY_DECODER
+    z = ndhwc(vae_synth.latent(spec))
+    params = vae_synth.decoder_params(spec, affine_seed=7)
+    ref = _torch_decode(spec, z, params)
+    got = oracle.decode(spec, z, params)
+    assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-11

@@ -1,0 +1,225 @@
+"""Seeded synthetic inputs and workload descriptions for the tiled causal 3-D VAE decode.
+
+This module is shared by the CPU oracle and the GPU path and holds none of the method's arithmetic:
+- the layer plan of each decoder workload (shapes only);
+- random draws from numpy's PCG64 with fixed seeds;
+- the rounding of drawn values to bfloat16 (round-to-nearest-even), so that both sides receive the
+  very same numbers.
+
+Workloads (the pages publish no checkpoints, so every weight is random-init, as the DistVAE PR #14
+"Add tiled VAE parallelism & extended model support" does in its benchmark harness commit, where a VAE
+is built from its config.json with random weights):
+- ``CONV_GN``: one causal Conv3d 32->32 followed by GroupNorm(8)+SiLU on [1,32,5,32,32], fp32.
+- ``TINY_DECODER``: a small fp32 causal decoder, latent [1,16,3,16,16] -> video [1,3,5,64,64].
+- ``LTX2_720P``: an LTX-2-shaped bf16 decoder, latent [1,128,16,22,40] -> video [1,3,121,704,1280].
+- ``LTX2_SMALL`` / ``LTX2_MID``: the same layer plan at small latents, for parity at oracle-friendly
+  sizes.
+
+Layer plan vocabulary (every op works on a channels-last activation):
+- ``conv``: causal Conv3d 3x3x3, stride 1, ``cin`` -> ``cout``; ``"f32_out": True`` keeps the result
+  in fp32 (the last convolution of a bf16 decoder);
+- ``res``: residual block of width ``c``: GN+SiLU, conv, GN+SiLU, conv, plus the block input;
+- ``gn_silu``: GroupNorm followed by SiLU;
+- ``d2s``: depth-to-space by (st, sh, sw); with st > 1 the first st-1 output frames are dropped;
+- ``nearest``: nearest-neighbour spatial upsampling by (sh, sw).
+
+Parameters are drawn in plan order: each ``conv`` gives one weight [cout, cin, 3, 3, 3] and one bias
+[cout]; each ``res`` gives GN(c), conv(c, c), GN(c), conv(c, c); each ``gn_silu`` gives GN(c). Conv
+weight number k (0-based, counting every conv in plan order) is N(0, 1) * 1/sqrt(27 * cin) drawn from
+PCG64([1, k]). Biases are 0, GN gamma is 1 and beta is 0, unless ``affine_seed`` asks for random
+values (used by tests to exercise the bias, gamma and beta paths).
+"""
+from __future__ import annotations
+
+import copy
+
+import numpy as np
+
+__all__ = [
+    "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "WORKLOADS",
+    "round_bf16", "bf16_bits", "normal", "uniform", "latent", "decoder_params", "conv_params",
+    "walk_plan", "with_latent",
+]
+
+
+# ----------------------------------------------------------------------------------------------
+# Workloads
+# ----------------------------------------------------------------------------------------------
+
+CONV_GN = {
+    "name": "conv_gn_32",
+    "dtype": "f32",
+    "input": (1, 32, 5, 32, 32),          # N, C, T, H, W
+    "cin": 32, "cout": 32, "groups": 8, "eps": 1e-6,
+    "patches_w": 2,
+}
+
+TINY_DECODER = {
+    "name": "tiny_decoder",
+    "dtype": "f32",
+    "latent": (1, 16, 3, 16, 16),
+    "groups": 32, "eps": 1e-6,
+    "layers": [
+        {"op": "conv", "cin": 16, "cout": 128},
+        {"op": "res", "c": 128},
+        {"op": "res", "c": 128},
+        {"op": "res", "c": 128},
+        {"op": "nearest", "sh": 2, "sw": 2},
+        {"op": "conv", "cin": 128, "cout": 64},
+        {"op": "res", "c": 64},
+        {"op": "nearest", "sh": 2, "sw": 2},
+        {"op": "conv", "cin": 64, "cout": 32},
+        {"op": "conv", "cin": 32, "cout": 64},
+        {"op": "d2s", "st": 2, "sh": 1, "sw": 1},
+        {"op": "gn_silu"},
+        {"op": "conv", "cin": 32, "cout": 3},
+    ],
+    "scale": (2, 4, 4),                   # latent -> video: T_out = 1 + (T-1)*2, H*4, W*4
+    "patch_grid": (2, 2),
+    "overlap_tile": (8, 8), "overlap_stride": (6, 6),
+}
+
+_LTX2_LAYERS = [
+    {"op": "conv", "cin": 128, "cout": 1024},
+    {"op": "res", "c": 1024},
+    {"op": "res", "c": 1024},
+    {"op": "conv", "cin": 1024, "cout": 4096},
+    {"op": "d2s", "st": 2, "sh": 2, "sw": 2},
+    {"op": "res", "c": 512},
+    {"op": "res", "c": 512},
+    {"op": "conv", "cin": 512, "cout": 2048},
+    {"op": "d2s", "st": 2, "sh": 2, "sw": 2},
+    {"op": "res", "c": 256},
+    {"op": "res", "c": 256},
+    {"op": "conv", "cin": 256, "cout": 1024},
+    {"op": "d2s", "st": 2, "sh": 2, "sw": 2},
+    {"op": "res", "c": 128},
+    {"op": "res", "c": 128},
+    {"op": "gn_silu"},
+    {"op": "conv", "cin": 128, "cout": 48, "f32_out": True},
+    {"op": "d2s", "st": 1, "sh": 4, "sw": 4},
+]
+
+LTX2_720P = {
+    "name": "ltx2_720p",
+    "dtype": "bf16",
+    "latent": (1, 128, 16, 22, 40),
+    "groups": 32, "eps": 1e-6,
+    "layers": _LTX2_LAYERS,
+    "scale": (8, 32, 32),
+    "patch_grid": (1, 4),
+    "overlap_tile": (16, 16), "overlap_stride": (14, 14),
+}
+
+
+def with_latent(spec: dict, latent_shape, name: str, **extra) -> dict:
+    """A copy of ``spec`` with another latent shape (and optionally other tiling fields)."""
+    out = copy.deepcopy(spec)
+    out["latent"] = tuple(latent_shape)
+    out["name"] = name
+    out.update(extra)
+    return out
+
+
+LTX2_SMALL = with_latent(LTX2_720P, (1, 128, 2, 3, 5), "ltx2_small",
+                         patch_grid=(1, 2), overlap_tile=(2, 3), overlap_stride=(1, 2))
+LTX2_MID = with_latent(LTX2_720P, (1, 128, 3, 4, 6), "ltx2_mid",
+                       patch_grid=(2, 3), overlap_tile=(3, 4), overlap_stride=(2, 3))
+
+WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID)}
+
+
+# ----------------------------------------------------------------------------------------------
+# Draws and bf16 rounding
+# ----------------------------------------------------------------------------------------------
+
+def bf16_bits(a) -> np.ndarray:
+    """uint16 bit patterns of ``a`` rounded to bfloat16, round-to-nearest-even (finite inputs)."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = f.view(np.uint32)
+    # finite inputs stay below 2^32 after adding the rounding bias, so uint32 does not wrap
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def round_bf16(a) -> np.ndarray:
+    """``a`` rounded to the nearest bfloat16 (ties to even), returned as float32."""
+    bits = bf16_bits(a).astype(np.uint32) << 16
+    return bits.view(np.float32)
+
+
+def normal(shape, seed, scale: float = 1.0, mean: float = 0.0, dtype: str = "f32") -> np.ndarray:
+    """N(mean, scale^2) float32 draw from PCG64(seed); bf16-rounded when dtype == 'bf16'."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    v = (g.standard_normal(size=tuple(shape)) * scale + mean).astype(np.float32)
+    return round_bf16(v) if dtype == "bf16" else v
+
+
+def uniform(shape, seed, lo: float = -1.0, hi: float = 1.0, dtype: str = "f32") -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(seed))
+    v = g.uniform(lo, hi, size=tuple(shape)).astype(np.float32)
+    return round_bf16(v) if dtype == "bf16" else v
+
+
+def latent(spec: dict, seed=0) -> np.ndarray:
+    """The decoder input, NCDHW float32 (bf16-exact for bf16 workloads)."""
+    shape = spec["latent"] if "latent" in spec else spec["input"]
+    return normal(shape, seed, dtype=spec["dtype"])
+
+
+def conv_params(index: int, cin: int, cout: int, dtype: str, affine_seed=None) -> dict:
+    w = normal((cout, cin, 3, 3, 3), [1, index], scale=1.0 / np.sqrt(27.0 * cin), dtype=dtype)
+    if affine_seed is None:
+        b = np.zeros(cout, np.float32)
+    else:
+        b = normal((cout,), [2, affine_seed, index], scale=0.1)
+    return {"kind": "conv", "w": w, "b": b, "cin": cin, "cout": cout}
+
+
+def gn_params(index: int, c: int, affine_seed=None) -> dict:
+    if affine_seed is None:
+        gamma, beta = np.ones(c, np.float32), np.zeros(c, np.float32)
+    else:
+        gamma = normal((c,), [3, affine_seed, index], scale=0.2, mean=1.0)
+        beta = normal((c,), [4, affine_seed, index], scale=0.1)
+    return {"kind": "gn", "gamma": gamma, "beta": beta, "c": c}
+
+
+def walk_plan(spec: dict):
+    """Yield (op, channels_in, channels_out) along the plan, following the channel count only."""
+    c = spec["latent"][1]
+    for op in spec["layers"]:
+        kind = op["op"]
+        if kind == "conv":
+            yield op, op["cin"], op["cout"]
+            c = op["cout"]
+        elif kind == "res":
+            yield op, op["c"], op["c"]
+        elif kind == "gn_silu":
+            yield op, c, c
+        elif kind == "d2s":
+            k = op["st"] * op["sh"] * op["sw"]
+            yield op, c, c // k
+            c //= k
+        elif kind == "nearest":
+            yield op, c, c
+        else:
+            raise ValueError(f"unknown op {kind!r}")
+
+
+def decoder_params(spec: dict, affine_seed=None) -> list:
+    """Parameter list of a decoder plan, in plan order (see the module docstring)."""
+    out, n_conv, n_gn = [], 0, 0
+    dt = spec["dtype"]
+    for op, cin, cout in walk_plan(spec):
+        kind = op["op"]
+        if kind == "conv":
+            out.append(conv_params(n_conv, cin, cout, dt, affine_seed)); n_conv += 1
+        elif kind == "res":
+            out.append(gn_params(n_gn, cin, affine_seed)); n_gn += 1
+            out.append(conv_params(n_conv, cin, cin, dt, affine_seed)); n_conv += 1
+            out.append(gn_params(n_gn, cin, affine_seed)); n_gn += 1
+            out.append(conv_params(n_conv, cin, cin, dt, affine_seed)); n_conv += 1
+        elif kind == "gn_silu":
+            out.append(gn_params(n_gn, cin, affine_seed)); n_gn += 1
+    return out
