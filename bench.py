@@ -1,0 +1,184 @@
+"""Benchmark: tiled causal-3D VAE decode at 720p on one MI355X.
+
+One step is one full decode of the LTX-2-shaped plan:
+- input: seeded latent [1,128,16,22,40], random-init bf16 weights;
+- output: [1,3,121,704,1280] fp32 (109,035,520 pixel-frames);
+- default tiling: 1x4 patch-halo (mode A); ``--mode overlap`` times the 2x3 overlap-blend decode.
+
+Inputs and weights are resident in HBM before the timed region. Exactly --steps decodes are timed
+between two device synchronisations. HIP events recorded by the library on the decode's own stream
+give each op's GPU time inside that same timed region, and the conv roofline comes from them.
+
+Output: one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "decoded Mpixel-frames/s (720p VAE decode, 1 GPU) + conv MFMA % of peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def conv_flops(spec, latent_shape):
+    """Algorithmic conv flops of one decode: 2 * 27 * Cin * Cout * output positions per conv."""
+    n, t, h, w, c = latent_shape
+    total = 0.0
+    for op in spec["layers"]:
+        k = op["op"]
+        if k == "conv":
+            total += 2 * 27 * op["cin"] * op["cout"] * n * t * h * w
+        elif k == "res":
+            total += 2 * (2 * 27 * op["c"] * op["c"] * n * t * h * w)
+        elif k == "d2s":
+            t, h, w = op["st"] * t - (op["st"] - 1), h * op["sh"], w * op["sw"]
+        elif k == "nearest":
+            h, w = h * op["sh"], w * op["sw"]
+    return total
+
+
+def cpu_baseline(spec, params, frames=1):
+    """The oracle, as it stands, on a bounded sample: the full 720p spatial plan on `frames`
+    latent frames, scaled by conv flops to the 16-frame decode."""
+    import threadpoolctl
+    import oracle
+    import vae_synth
+    z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))[:, :frames]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    out = oracle.decode(spec, z, params)
+    sample_s = time.perf_counter() - t0
+    full_shape = (1, 16, 22, 40, 128)
+    scale = conv_flops(spec, full_shape) / conv_flops(spec, z.shape)
+    est_full_s = sample_s * scale
+    px = 121 * 704 * 1280
+    return {
+        "value": px / est_full_s / 1e6, "unit": "Mpx-frames/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"oracle fp64 decode of latent [1,128,{frames},22,40] -> {list(out.shape)} "
+                   f"in {sample_s:.1f} s, scaled by conv flops x{scale:.1f} to the 16-frame "
+                   f"720p decode (est. {est_full_s:.0f} s); os.cpu_count()={os.cpu_count()}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", choices=["patch", "overlap"], default="patch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frames", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this decode has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vae_synth
+    import video_diffusion_vae_amd as v
+
+    spec = vae_synth.LTX2_720P
+    t_setup = time.perf_counter()
+    z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))
+    params = vae_synth.decoder_params(spec)
+    dev = torch.device("cuda:0")
+    dec = v.upload_decoder(spec, params, dev)
+    zd = torch.as_tensor(z).to(device=dev, dtype=torch.bfloat16)
+    if args.mode == "patch":
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 4))
+        workload = "ltx2_720p_decode_patch_halo_1x4"
+    else:
+        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, z.shape, spec["scale"],
+                             tile=spec["overlap_tile"], stride=spec["overlap_stride"])
+        workload = "ltx2_720p_decode_overlap_blend_2x3"
+    ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, 121, 704, 1280, 3), dtype=torch.float32, device=dev)
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s, workspace "
+        f"{ws.numel() / 2**30:.2f} GiB")
+
+    for i in range(args.warmup):
+        dec.vae_decode_tiled(zd, desc, out, ws)
+    torch.cuda.synchronize(dev)
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    dec.set_timing(True)
+    per_op = []
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        dec.vae_decode_tiled(zd, desc, out, ws)
+        per_op.append(dec.timing())          # waits for this step's last event
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    dec.set_timing(False)
+    ms = elapsed * 1000.0 / args.steps
+    px = 121 * 704 * 1280
+    value = px / (ms / 1000.0) / 1e6
+    log(f"[bench] {args.steps} timed steps: {ms:.2f} ms/step, {value:.1f} Mpx-frames/s")
+
+    kinds = {}
+    for step in per_op:
+        for r in step:
+            k = kinds.setdefault(r["kind"], {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0})
+            k["ms"] += r["ms"]
+            k["flops"] += r["flops"]
+            k["bytes"] += r["bytes"]
+            k["n"] += 1
+    summary = {}
+    for name, k in kinds.items():
+        s = {"ms_per_step": k["ms"] / args.steps, "launch_groups_per_step": k["n"] // args.steps}
+        if k["flops"]:
+            s["tflops"] = k["flops"] / (k["ms"] / 1000.0) / 1e12
+            s["frac_mfma_peak"] = s["tflops"] / PEAK_BF16_TFLOPS
+        if k["bytes"] and name != "conv":
+            s["gbs"] = k["bytes"] / (k["ms"] / 1000.0) / 1e9
+            s["frac_hbm_peak"] = s["gbs"] / PEAK_HBM_GBS
+        summary[name] = s
+    for r in per_op[-1]:
+        if r["kind"] == "conv":
+            log(f"  conv layer {r['layer']:2d} tile {r['tile']:2d}: {r['ms']:8.3f} ms "
+                f"{r['flops'] / r['ms'] / 1e9:8.1f} TFLOP/s")
+    for name, s in summary.items():
+        log(f"  {name}: {json.dumps(s)}")
+
+    conv = kinds["conv"]
+    achieved = conv["flops"] / (conv["ms"] / 1000.0) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": "conv3d_mfma_kernel (all conv launches of a decode)"}
+
+    baseline = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on its bounded sample ...")
+        baseline = cpu_baseline(spec, params, args.cpu_frames)
+        log(f"[bench] cpu baseline: {baseline}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "Mpx-frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded latent, random-init weights)",
+        "config": {"workload": workload, "latent": [1, 128, 16, 22, 40],
+                   "output": [1, 3, 121, 704, 1280], "parallelism": "none (1 GPU)",
+                   "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
+        "roofline": roofline, "kernels": summary, "cpu_baseline": baseline,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

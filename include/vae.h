@@ -1,0 +1,329 @@
+/*
+ * vae.h - C ABI of libvae_mi355x: the tiled, halo-extended decode of a causal 3-D video VAE on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes what these pages describe:
+ *   [P1] "[TRTLLM-14029][feat] LTX-2 tile-parallel VAE decode" (NVIDIA/TensorRT-LLM PR #15753)
+ *   [P2] "[Feature] Support VAE tiling parallel encode for LTX-2" (vllm-project/vllm-omni PR #4831)
+ *   [P4] "Add tiled VAE parallelism & extended model support" (xdit-project/DistVAE PR #14)
+ *   [P5] "[TRTLLM-14123][feat] add ParallelVAE_TrtllmWan for native Wan VAE" (TensorRT-LLM PR #16066)
+ * Each declaration below names the passage that defines its operation.
+ *
+ * Conventions for every call
+ *  - Layout: activations are dense NDHWC (channels fastest), addressed with 64-bit offsets.
+ *    Conv weights are [Cout][kt=3][kh=3][kw=3][Cin]. Bias, gamma and beta are fp32 vectors.
+ *  - Dtypes: VAE_DTYPE_BF16 (bfloat16 storage, fp32 arithmetic) or VAE_DTYPE_F32.
+ *  - Ownership: the caller owns every buffer. Device buffers are passed as raw device pointers;
+ *    the library never allocates or frees device memory and never synchronises the stream. It
+ *    keeps no pointer after a call returns, except the weight pointers held by a decoder object,
+ *    which must outlive that object.
+ *  - Streams: every device call is asynchronous and enqueued on `stream` (a hipStream_t passed as
+ *    void*, NULL = the default stream). vae_tile_split is host-only and synchronous.
+ *  - Errors: every call returns a vae_status_t. On failure nothing is enqueued, and
+ *    vae_last_error() / vae_last_error_info() describe the cause for the calling thread. No C++
+ *    exception crosses this boundary.
+ *  - Boxes: half-open [t0,t1) x [h0,h1) x [w0,w1) in the grid of the tensor they refer to;
+ *    NULL means the whole tensor.
+ */
+#ifndef VAE_MI355X_H
+#define VAE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define VAE_API __attribute__((visibility("default")))
+#else
+#define VAE_API
+#endif
+
+typedef void* vae_stream_t; /* a hipStream_t */
+
+typedef enum {
+    VAE_OK = 0,
+    VAE_ERR_INVALID_ARG = 1,  /* malformed arguments: null pointers, mismatched shapes/dtypes */
+    VAE_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the library computes; see info */
+    VAE_ERR_HIP = 3,          /* a HIP runtime call failed */
+    VAE_ERR_WORKSPACE = 4     /* workspace missing or smaller than the size query returned */
+} vae_status_t;
+
+enum { VAE_DTYPE_BF16 = 1, VAE_DTYPE_F32 = 2 };
+
+typedef struct vae_tensor {
+    void* data;       /* device pointer, NDHWC dense */
+    int32_t dtype;    /* VAE_DTYPE_* */
+    int32_t reserved; /* set to 0 */
+    int64_t n, t, h, w, c;
+} vae_tensor_t;
+
+typedef struct vae_box {
+    int32_t t0, t1, h0, h1, w0, w1;
+} vae_box_t;
+
+/* Structured details of the last failure (P4, commit on rectangular tile plans: callers get the
+ * numbers instead of parsing error text). Unused fields are -1. */
+typedef struct vae_error_info {
+    int32_t status;            /* vae_status_t of the failure */
+    int32_t axis;              /* 0 = N, 1 = T, 2 = H, 3 = W, 4 = C */
+    int64_t extent;            /* the offending extent */
+    int64_t required_multiple; /* a divisor the extent must have */
+    int64_t min_width;         /* the smallest extent that would be accepted */
+} vae_error_info_t;
+
+/* Thread-local text of the last failure on this thread ("" after success). */
+VAE_API const char* vae_last_error(void);
+/* Copies the structured details of the last failure on this thread. */
+VAE_API vae_status_t vae_last_error_info(vae_error_info_t* info);
+/* Library version, major * 10000 + minor * 100 + patch. */
+VAE_API int32_t vae_version(void);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Causal Conv3d                                                                              */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * y[n,t,h,w,o] = bias[o] + residual[n,t,h,w,o]
+ *              + sum_{c,a,p,q} W[o,a,p,q,c] * x[n, max(t+a-2, 0), h+p-1, w+q-1, c]
+ * with zeros where h+p-1 or w+q-1 leaves the image. Kernel 3x3x3, stride 1.
+ *
+ * Sources:
+ *  - causal temporal padding repeats frame 0 on an axis that is never split (P4, commits on the
+ *    LTX-2 and HunyuanVideo decoder adapters);
+ *  - spatial padding is zero only at true image borders; a patch's halo rows come from its
+ *    neighbours (P4, commit on how the direct path pads a patch);
+ *  - halos are read in place in channels-last layout, never concatenated (P5, Description).
+ *
+ * The output positions computed are those in `out_box` (in y's grid; NULL = all). The inputs read
+ * are out_box grown by one row/column on each side (the halo) and by two frames back, clamped to
+ * the tensor. Such a box is one patch of a patch-halo decode.
+ *
+ * Arguments:
+ *  x: [N,T,H,W,Cin] input (device).
+ *  weight: [Cout][3][3][3][Cin] (device), same dtype as x.
+ *  bias: [Cout] fp32 (device), or NULL.
+ *  residual: tensor of y's shape and dtype added to the result, or NULL. It may alias y.
+ *  y: [N,T,H,W,Cout] output. bf16 or fp32 for bf16 x; fp32 for fp32 x. It must not overlap x.
+ * bf16 runs on the MFMA path and requires Cin % 32 == 0; other shapes run on a slower path.
+ */
+VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
+                                       const float* bias, const vae_tensor_t* residual,
+                                       vae_tensor_t* y, const vae_box_t* out_box,
+                                       vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* GroupNorm (+SiLU) with statistics merged across patches                                    */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * GroupNorm over a tensor that is cut into patches (boxes). The statistics are those of the whole
+ * union of the boxes:
+ *  - the global mean, and the variance about it divided by the count (biased);
+ *  - not per-patch means and not Bessel's correction (P4, PatchGroupNorm commit message).
+ * Each box reports (count, mean, M2) per (sample, group) over the positions it owns. The parts are
+ * merged in box order with Chan et al.'s pairwise update:
+ *  n = sum n_i;  mean = sum n_i mean_i / n;  M2 = sum (M2_i + n_i (mean_i - mean)^2).
+ * Then y = act((x - mean) * rsqrt(M2/n + eps) * gamma + beta), with act = SiLU(z) = z / (1 + e^-z)
+ * or the identity. Channel c belongs to group c / (C / groups).
+ *
+ * vae_groupnorm_silu performs stats, combine and apply in one call.
+ *  boxes: the patches owning the statistics (n_boxes >= 1; NULL with n_boxes == 1 = whole tensor).
+ *         The apply step writes y over every box.
+ *  gamma, beta: [C] fp32 (device) or NULL (1 and 0).
+ *  y: same shape as x; dtype bf16 or fp32. It may alias x.
+ *  ws: device scratch of at least vae_groupnorm_silu_workspace() bytes.
+ * Partials are combined in a fixed order: results are bitwise reproducible run to run.
+ */
+VAE_API vae_status_t vae_groupnorm_silu_workspace(const vae_tensor_t* x, const vae_box_t* boxes,
+                                                  int32_t n_boxes, int32_t groups, size_t* bytes);
+VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* boxes,
+                                        int32_t n_boxes, int32_t groups, float eps,
+                                        const float* gamma, const float* beta, int32_t apply_silu,
+                                        vae_tensor_t* y, void* ws, size_t ws_bytes,
+                                        vae_stream_t stream);
+
+/* The same operation in three steps, for callers that move the per-box partials themselves.
+ * vae_groupnorm_stats: per box, (count, mean, M2) as fp64 into part[n_boxes][N][groups][3]
+ *   (device). ws is sized by vae_groupnorm_stats_workspace().
+ * vae_groupnorm_combine: merges part[0..n_parts) in order and writes mean_rstd[N][groups][2]
+ *   fp32 (mean, 1/sqrt(var + eps)) (device).
+ * vae_groupnorm_apply: the normalise (+SiLU) step over `box` (NULL = whole) with given mean_rstd.
+ */
+VAE_API vae_status_t vae_groupnorm_stats_workspace(const vae_tensor_t* x, const vae_box_t* boxes,
+                                                   int32_t n_boxes, int32_t groups, size_t* bytes);
+VAE_API vae_status_t vae_groupnorm_stats(const vae_tensor_t* x, const vae_box_t* boxes,
+                                         int32_t n_boxes, int32_t groups, double* part, void* ws,
+                                         size_t ws_bytes, vae_stream_t stream);
+VAE_API vae_status_t vae_groupnorm_combine(const double* part, int32_t n_parts, int32_t n,
+                                           int32_t groups, float eps, float* mean_rstd,
+                                           vae_stream_t stream);
+VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t* box,
+                                         int32_t groups, const float* mean_rstd,
+                                         const float* gamma, const float* beta,
+                                         int32_t apply_silu, vae_tensor_t* y, vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Upsampling                                                                                 */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * VAE_UPSAMPLE_NEAREST: y[t, sh*h+dh, sw*w+dw, c] = x[t, h, w, c]; requires st == 1.
+ * VAE_UPSAMPLE_D2S: depth-to-space, one input position per output position (P4, LTX-2 decoder
+ *   adapter commit): y[st*t+dt-(st-1), sh*h+dh, sw*w+dw, c] = x[t, h, w, ((dt*sh+dh)*sw+dw)*C + c],
+ *   keeping only output frames >= 0. That is the causal drop of the first st-1 frames:
+ *   T -> st*T - (st-1). The pages leave the channel order open; this one (sub-position slowest,
+ *   channel fastest) makes every output row a contiguous slice of an input row. Any other fixed
+ *   order is one permutation of the producing conv's output channels.
+ * box: input positions to upsample (in x's grid; NULL = all). y must have the upsampled shape.
+ * x and y have the same dtype and must not overlap.
+ */
+enum { VAE_UPSAMPLE_NEAREST = 1, VAE_UPSAMPLE_D2S = 2 };
+VAE_API vae_status_t vae_upsample(const vae_tensor_t* x, const vae_box_t* box, int32_t mode,
+                                  int32_t st, int32_t sh, int32_t sw, vae_tensor_t* y,
+                                  vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Tile split / merge                                                                         */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * Two ways to cut a decode:
+ *  VAE_TILING_PATCH_HALO (mode A). The latent is cut into patches_h x patches_w bands. With L rows
+ *    over p bands, the first L % p bands get one row more (P4, Patchify commit message). Every conv
+ *    reads a one-row halo from the neighbouring patches, and GroupNorm merges per-patch statistics.
+ *    The result equals the untiled decode up to float re-association.
+ *  VAE_TILING_OVERLAP_BLEND (mode B). Tiles of tile_* latent rows start at 0, stride, 2*stride,
+ *    ... < L, each min(tile, L - start) long. An axis no longer than its tile is not cut (P2, review
+ *    thread: tile 512 / stride 448 px turns 576 into 512 + 128; 256 stays untiled). Each tile is
+ *    decoded alone and blended with separable linear ramps (P1, Approach: a mask built from
+ *    per-axis parts, a weight buffer, a divide). Where consecutive tiles overlap by E output
+ *    samples, the later tile rises as (j+1)/(E+1) and the earlier one falls as (E-j)/(E+1),
+ *    j = 0..E-1.
+ * Output boxes: spatial = latent box * scale. T is never cut and maps to 1 + (T-1)*scale_t frames
+ * (causal decode).
+ */
+enum { VAE_TILING_PATCH_HALO = 1, VAE_TILING_OVERLAP_BLEND = 2 };
+
+typedef struct vae_tiling_desc {
+    int32_t mode;                        /* VAE_TILING_* */
+    int32_t n, t, h, w;                  /* latent extents */
+    int32_t scale_t, scale_h, scale_w;   /* latent -> output scale */
+    int32_t patches_h, patches_w;        /* mode A grid */
+    int32_t tile_h, tile_w;              /* mode B tile size, latent rows */
+    int32_t stride_h, stride_w;          /* mode B tile stride, latent rows */
+} vae_tiling_desc_t;
+
+typedef struct vae_tile {
+    int32_t index, row, col;
+    vae_box_t latent;                    /* latent grid */
+    vae_box_t out;                       /* output grid */
+    int32_t lead_t, lead_h, lead_w;      /* overlap with the previous tile, output samples */
+    int32_t trail_t, trail_h, trail_w;   /* overlap with the next tile, output samples */
+} vae_tile_t;
+
+/* Host-only. tiles == NULL: *n_tiles receives the count. Otherwise up to `capacity` tiles, in
+ * row-major order, are written and *n_tiles is the count. Refused (VAE_ERR_UNSUPPORTED, info
+ * filled): a band that would be empty (a patch narrower than the one-row halo, P4,
+ * calc_bottom_halo_width commit); a stride outside 1..tile. */
+VAE_API vae_status_t vae_tile_split(const vae_tiling_desc_t* desc, vae_tile_t* tiles,
+                                    int32_t capacity, int32_t* n_tiles);
+
+/* Blends one decoded tile into the full output. `out` accumulates (fp32):
+ *   out[box] += w(t,h,w) * tile_out, with w = product of the tile's 1-D ramps.
+ * flags: VAE_MERGE_ZERO zeroes all of `out` before this tile is added (give it to the first tile).
+ *        VAE_MERGE_FINALIZE divides all of `out` by the summed weights after this tile is added
+ *        (give it to the last tile). The sums come from the tile grid of `desc`, per axis.
+ * tile_out: fp32 [N, out box extents, C]; out: fp32 [N, T_out, H_out, W_out, C].
+ * This is the vae_tiling_desc_t / vae_tile_t returned by vae_tile_split for mode B. */
+enum { VAE_MERGE_ZERO = 1, VAE_MERGE_FINALIZE = 2 };
+VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile_t* tile,
+                                    const vae_tiling_desc_t* desc, vae_tensor_t* out,
+                                    int32_t flags, vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Whole decoder                                                                              */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * A decoder is a layer plan plus device weight pointers. Each op reads and writes a channels-last
+ * activation:
+ *  VAE_OP_CONV    causal Conv3d cin -> cout (f32_out = 1 writes fp32: the last conv of a bf16 plan)
+ *  VAE_OP_RES     residual block of width cin: GN+SiLU, conv, GN+SiLU, conv, plus the block input
+ *  VAE_OP_GN_SILU GroupNorm + SiLU
+ *  VAE_OP_D2S     depth-to-space (st, sh, sw) with the causal frame drop
+ *  VAE_OP_NEAREST nearest spatial upsampling (sh, sw)
+ * The parameter pointers come in plan order, two per entry:
+ *  conv -> (weight, bias);
+ *  GN -> (gamma, beta);
+ *  res -> GN, conv, GN, conv.
+ * bias, gamma and beta may be NULL.
+ */
+enum { VAE_OP_CONV = 1, VAE_OP_RES = 2, VAE_OP_GN_SILU = 3, VAE_OP_D2S = 4, VAE_OP_NEAREST = 5 };
+
+typedef struct vae_layer_desc {
+    int32_t op;
+    int32_t cin, cout;
+    int32_t st, sh, sw;
+    int32_t f32_out;
+} vae_layer_desc_t;
+
+typedef struct vae_decoder_spec {
+    int32_t dtype;              /* weights and activations: VAE_DTYPE_* */
+    int32_t latent_channels;
+    int32_t groups;
+    float eps;
+    int32_t n_layers;
+    const vae_layer_desc_t* layers;
+} vae_decoder_spec_t;
+
+typedef struct vae_decoder vae_decoder_t;
+
+/* Validates the plan and keeps a copy of it, along with the `n_ptrs` device pointers (no copy
+ * of the weights themselves). */
+VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
+                                        const void* const* params, int32_t n_ptrs,
+                                        vae_decoder_t** out);
+VAE_API void vae_decoder_destroy(vae_decoder_t* dec);
+
+/* Device scratch needed by vae_decode_tiled for this tiling (latent extents come from desc). */
+VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,
+                                               const vae_tiling_desc_t* desc, size_t* bytes);
+
+/*
+ * Decodes `latent` ([N,T,H,W,latent_channels], the plan's dtype) into `out` (fp32, NDHWC).
+ * mode A (patch-halo):
+ *  - convs, upsampling and the final placement run over the whole activation, and each patch's
+ *    halo is its neighbour's data read in place;
+ *  - GroupNorm statistics are formed per patch and merged across patches.
+ *  The result equals the untiled decode.
+ * mode B (overlap-blend):
+ *  - each tile is decoded alone, one tile in flight, with its own borders and statistics;
+ *  - every tile is blended into `out` with vae_tile_merge's weights and normalised at the end.
+ *  This is the serial tiled decode of P1.
+ * desc's latent extents must match `latent`, and its scales the plan. ws must hold at least
+ * vae_decode_workspace_size() bytes. All work goes on `stream`; per-tile host work is only
+ * integer geometry, computed once per call.
+ */
+VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec, const vae_tensor_t* latent,
+                                      const vae_tiling_desc_t* desc, vae_tensor_t* out, void* ws,
+                                      size_t ws_bytes, vae_stream_t stream);
+
+/* Per-op GPU timing of the most recent vae_decode_tiled call (events recorded on its stream).
+ * Enabled with vae_decoder_set_timing(dec, 1); collecting waits for the last recorded event. */
+enum { VAE_KIND_CONV = 1, VAE_KIND_GN = 2, VAE_KIND_UPSAMPLE = 3, VAE_KIND_MERGE = 4,
+       VAE_KIND_OTHER = 5 };
+typedef struct vae_op_timing {
+    int32_t kind;       /* VAE_KIND_* */
+    int32_t layer;      /* index in the plan */
+    int32_t tile;       /* tile index (mode B) or -1 */
+    int32_t reserved;
+    double ms;          /* GPU time between the events around the op */
+    double flops;       /* algorithmic flops (convs: 2 * 27 * Cin * Cout * positions) */
+    double bytes;       /* algorithmic HBM bytes (streaming passes: bytes read + written) */
+} vae_op_timing_t;
+VAE_API vae_status_t vae_decoder_set_timing(vae_decoder_t* dec, int32_t enable);
+VAE_API vae_status_t vae_decoder_get_timing(vae_decoder_t* dec, vae_op_timing_t* out,
+                                            int32_t capacity, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VAE_MI355X_H */

@@ -1,0 +1,144 @@
+"""Host-side tests of the C-ABI library: exported symbols, the tile split against the oracle
+(bit-exact integers), and refusals. No GPU: only host code of the library runs."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def v():
+    import video_diffusion_vae_amd as v
+    return v
+
+
+def header_symbols():
+    with open(os.path.join(ROOT, "include", "vae.h")) as f:
+        text = f.read()
+    return set(re.findall(r"VAE_API\s+[\w\s\*]+?\b(vae_\w+)\s*\(", text))
+
+
+def test_library_exports_every_header_symbol(v):
+    names = header_symbols()
+    assert len(names) >= 19
+    lib = ctypes.CDLL(v._binding.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert names == set(v.EXPORTS)
+
+
+def _fields(t):
+    return {"latent": (t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
+                       t.latent.w1),
+            "out": (t.out.t0, t.out.t1, t.out.h0, t.out.h1, t.out.w0, t.out.w1),
+            "lead": (t.lead_t, t.lead_h, t.lead_w), "trail": (t.trail_t, t.trail_h, t.trail_w),
+            "row": t.row, "col": t.col}
+
+
+PATCH_CASES = [
+    (16, 22, 40, 1, 4, (8, 32, 32)), (3, 16, 16, 2, 2, (2, 4, 4)), (5, 17, 23, 3, 4, (1, 1, 1)),
+    (1, 7, 7, 7, 7, (8, 32, 32)), (9, 22, 40, 4, 4, (2, 8, 8)), (13, 5, 11, 1, 3, (4, 2, 2)),
+]
+
+OVERLAP_CASES = [
+    (16, 22, 40, (16, 16), (14, 14), (8, 32, 32)), (1, 576, 576, (512, 512), (448, 448), (1, 1, 1)),
+    (1, 256, 256, (512, 512), (448, 448), (1, 1, 1)), (3, 16, 16, (8, 8), (6, 6), (2, 4, 4)),
+    (5, 30, 17, (16, 5), (14, 2), (2, 3, 5)), (2, 9, 9, (4, 9), (4, 3), (1, 8, 8)),
+    (9, 13, 29, (7, 6), (7, 1), (1, 4, 4)), (1, 1, 1, (1, 1), (1, 1), (1, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", PATCH_CASES)
+def test_patch_split_bit_exact(v, case):
+    t, h, w, ph, pw, scale = case
+    got = v.vae_tile_split(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (2, t, h, w, 8), scale,
+                                         patches=(ph, pw)))
+    ref = oracle.patch_tiles(t, h, w, ph, pw, scale)
+    assert len(got) == len(ref)
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert g.index == i
+        f = _fields(g)
+        assert f["latent"] == r["latent"] and f["out"] == r["out"]
+        assert f["lead"] == r["lead"] and f["trail"] == r["trail"]
+        assert (f["row"], f["col"]) == (r["row"], r["col"])
+
+
+@pytest.mark.parametrize("case", OVERLAP_CASES)
+def test_overlap_split_bit_exact(v, case):
+    t, h, w, tile, stride, scale = case
+    got = v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, t, h, w, 8), scale,
+                                         tile=tile, stride=stride))
+    ref = oracle.overlap_tiles(t, h, w, tile, stride, scale)
+    assert len(got) == len(ref)
+    for g, r in zip(got, ref):
+        f = _fields(g)
+        for k in ("latent", "out", "lead", "trail"):
+            assert f[k] == r[k], (k, f[k], r[k])
+
+
+def test_refusals_carry_numbers(v):
+    with pytest.raises(v.VaeError) as e:
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 4, 3, 40, 8), (1, 1, 1),
+                                       patches=(4, 1)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    assert e.value.info["axis"] == 2 and e.value.info["extent"] == 3
+    assert e.value.info["min_width"] == 4
+    with pytest.raises(v.VaeError) as e:
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 4, 40, 40, 8), (1, 1, 1),
+                                       tile=(8, 8), stride=(9, 8)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 2
+    with pytest.raises(v.VaeError) as e:
+        v.vae_tile_split(v.tiling_desc(7, (1, 4, 40, 40, 8), (1, 1, 1)))
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+
+
+def test_decoder_plan_validation(v):
+    import vae_synth
+    spec = vae_synth.TINY_DECODER
+    fake = [None] * 100
+    with pytest.raises(v.VaeError) as e:      # wrong pointer count
+        v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, spec["layers"], fake[:3])
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    bad = [dict(op) for op in spec["layers"]]
+    bad[0] = {"op": "conv", "cin": 8, "cout": 128}
+    with pytest.raises(v.VaeError):           # channels do not chain
+        v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, bad, fake[:0])
+    with pytest.raises(v.VaeError) as e:      # a bf16 plan must end in fp32
+        v.Decoder(v.VAE_DTYPE_BF16, 16, 32, 1e-6, spec["layers"], fake[:0])
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+
+
+def test_workspace_query_needs_no_gpu(v):
+    import vae_synth
+    spec = vae_synth.LTX2_720P
+    n_ptr = sum({"conv": 2, "res": 8, "gn_silu": 2}.get(op["op"], 0) for op in spec["layers"])
+    # dummy non-null, 16-byte aligned pointers: creating a decoder never dereferences them
+    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(n_ptr)]
+
+    class P:
+        def __init__(self, p):
+            self.p = p
+
+        def data_ptr(self):
+            return self.p.value
+    dec = v.Decoder(v.VAE_DTYPE_BF16, 128, 32, 1e-6, spec["layers"], [P(p) for p in ptrs])
+    a = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
+                                         (8, 32, 32), patches=(1, 4)))
+    b = dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 16, 22, 40, 128),
+                                         (8, 32, 32), tile=(16, 16), stride=(14, 14)))
+    # three rotating buffers of the largest activation (the 1024-channel S2 conv output, bf16)
+    assert a >= 3 * 858880 * 1024 * 2
+    assert b < a                                  # tiles are smaller than the whole tensor
+    with pytest.raises(v.VaeError) as e:          # more patches than the decoder's 16
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
+                                         (8, 32, 32), patches=(5, 4)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError):               # scales that do not match the plan
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
+                                         (8, 16, 32), patches=(1, 4)))
+    dec.close()

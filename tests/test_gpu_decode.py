@@ -1,0 +1,166 @@
+"""GPU parity of the whole decode (vae_decode_tiled) against the CPU oracle.
+
+Tolerances:
+- fp32 workloads (the single conv+GN workload, the tiny decoder): relative max-abs <= 1e-4;
+- bf16 workloads: PSNR >= 50 dB and max-abs <= 2e-2 against the fp64 oracle on the same
+  bf16-exact inputs and weights.
+Patch-halo decodes are compared with the oracle's untiled decode, which they must equal.
+Overlap-blend decodes are compared with the oracle's overlap-blend decode.
+"""
+import functools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import vae_synth
+from _util import ndhwc, dev, host, rel_max_abs, psnr
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def v():
+    import torch
+    import video_diffusion_vae_amd as v
+    assert torch.cuda.is_available()
+    return v
+
+
+CONV_GN_PLAN = {
+    "name": "conv_gn_32", "dtype": "f32", "latent": vae_synth.CONV_GN["input"], "groups": 8,
+    "eps": 1e-6, "layers": [{"op": "conv", "cin": 32, "cout": 32}, {"op": "gn_silu"}],
+    "scale": (1, 1, 1),
+}
+
+
+def params_of(name, affine=None):
+    # the LTX-2-shaped workloads share one layer plan, hence one weight set
+    key = "ltx2_720p" if name.startswith("ltx2_") and name != "ltx2_tiny" else name
+    return _params(key, affine)
+
+
+@functools.lru_cache(maxsize=None)
+def _params(name, affine):
+    spec = CONV_GN_PLAN if name == "conv_gn_32" else vae_synth.WORKLOADS[name]
+    return vae_synth.decoder_params(spec, affine_seed=affine)
+
+
+def spec_of(name):
+    return CONV_GN_PLAN if name == "conv_gn_32" else vae_synth.WORKLOADS[name]
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_out(name, mode, affine=None):
+    spec = spec_of(name)
+    z = ndhwc(vae_synth.latent(spec))
+    p = params_of(name, affine)
+    if mode == "whole":
+        return oracle.decode(spec, z, p)
+    return oracle.decode_overlap_blend(spec, z, p, spec["overlap_tile"], spec["overlap_stride"],
+                                       spec["scale"])
+
+
+def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1):
+    import torch
+    spec = spec_of(name)
+    z = ndhwc(vae_synth.latent(spec))
+    dec = v.upload_decoder(spec, params_of(name, affine))
+    zd = dev(z, spec["dtype"])
+    if mode == "patch":
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
+    else:
+        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, z.shape, spec["scale"],
+                             tile=spec["overlap_tile"], stride=spec["overlap_stride"])
+    ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out_shape = oracle.output_shape(spec, z.shape)
+    outs = []
+    for _ in range(repeat):
+        out = torch.full(out_shape, float("nan"), device="cuda", dtype=torch.float32)
+        dec.vae_decode_tiled(zd, desc, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    dec.close()
+    return outs if repeat > 1 else outs[0]
+
+
+@pytest.mark.parametrize("patches", [(1, 1), (1, 2), (2, 1)])
+@pytest.mark.parametrize("affine", [None, 4])
+def test_conv_gn_workload(v, patches, affine):
+    """One causal conv 32->32 + GN(8) + SiLU on [1,32,5,32,32], whole and as width patches."""
+    got = host(gpu_decode(v, "conv_gn_32", "patch", patches, affine))
+    assert rel_max_abs(got, oracle_out("conv_gn_32", "whole", affine)) <= 1e-4
+
+
+@pytest.mark.parametrize("patches", [(1, 1), (2, 2), (1, 3)])
+def test_tiny_decoder_patch_halo(v, patches):
+    got = host(gpu_decode(v, "tiny_decoder", "patch", patches, affine=3))
+    assert got.shape == (1, 5, 64, 64, 3)
+    assert rel_max_abs(got, oracle_out("tiny_decoder", "whole", 3)) <= 1e-4
+
+
+def test_tiny_decoder_overlap_blend(v):
+    got = host(gpu_decode(v, "tiny_decoder", "overlap", affine=3))
+    assert rel_max_abs(got, oracle_out("tiny_decoder", "overlap", 3)) <= 1e-4
+
+
+def _bf16_bar(got, ref):
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+    return p, m
+
+
+@pytest.mark.parametrize("name,patches", [("ltx2_small", (1, 2)), ("ltx2_small", (1, 1)),
+                                          ("ltx2_mid", (2, 3))])
+def test_ltx2_shaped_patch_halo(v, name, patches):
+    got = host(gpu_decode(v, name, "patch", patches))
+    _bf16_bar(got, oracle_out(name, "whole"))
+
+
+@pytest.mark.parametrize("name", ["ltx2_small", "ltx2_mid"])
+def test_ltx2_shaped_overlap_blend(v, name):
+    got = host(gpu_decode(v, name, "overlap"))
+    _bf16_bar(got, oracle_out(name, "overlap"))
+
+
+def test_decode_is_deterministic(v):
+    import torch
+    a, b = gpu_decode(v, "ltx2_small", "patch", (1, 2), repeat=2)
+    assert torch.equal(a, b)
+    a, b = gpu_decode(v, "ltx2_small", "overlap", repeat=2)
+    assert torch.equal(a, b)
+
+
+def _golden(mode):
+    path = os.path.join(GOLDEN, f"ltx2_720p_{mode}_samples.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return np.load(path)
+
+
+def test_ltx2_720p_patch_halo_against_golden(v):
+    """Full 720p decode (latent [1,128,16,22,40] -> [1,121,704,1280,3]), 1x4 width patches, at
+    the pixels the oracle's full fp64 decode stored."""
+    g = _golden("whole")
+    out = gpu_decode(v, "ltx2_720p", "patch", (1, 4))
+    pos = g["positions"]
+    got = out[0, pos[:, 0], pos[:, 1], pos[:, 2], :].double().cpu().numpy()
+    ref = g["values"]
+    assert np.all(np.isfinite(got))
+    p = 10 * np.log10((float(g["out_max"]) - float(g["out_min"])) ** 2 /
+                      np.mean((got - ref) ** 2))
+    m = float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+    o = out.double()
+    assert abs(float(o.mean()) - float(g["out_mean"])) <= 1e-3 * float(g["out_std"])
+    assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
+
+
+def test_ltx2_tiny_both_modes(v):
+    got = host(gpu_decode(v, "ltx2_tiny", "patch", (1, 2)))
+    _bf16_bar(got, oracle_out("ltx2_tiny", "whole"))
+    got = host(gpu_decode(v, "ltx2_tiny", "overlap"))
+    _bf16_bar(got, oracle_out("ltx2_tiny", "overlap"))

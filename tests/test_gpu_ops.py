@@ -1,0 +1,253 @@
+"""GPU parity of each C-ABI call against the CPU oracle, on seeded inputs.
+
+Tolerances:
+- fp32 paths: relative max-abs <= 1e-4;
+- bf16 inputs with fp32 output: products are exact in fp32, so the same 1e-4;
+- bf16 outputs: half a bf16 ulp of the reference plus 1e-4 relative (one rounding per store);
+- integer/permutation work (upsampling): bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import vae_synth
+from _util import ndhwc, dev, host, rel_max_abs, bf16_round_bound
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def v():
+    import torch
+    import video_diffusion_vae_amd as v
+    assert torch.cuda.is_available()
+    return v
+
+
+def _conv_inputs(shape, cin, cout, dtype, seed):
+    n, t, h, w = shape
+    x = ndhwc(vae_synth.normal((n, cin, t, h, w), [10, seed], dtype=dtype))
+    wt = vae_synth.normal((cout, cin, 3, 3, 3), [11, seed], scale=1 / np.sqrt(27 * cin), dtype=dtype)
+    b = vae_synth.normal((cout,), [12, seed], scale=0.1)
+    r = ndhwc(vae_synth.normal((n, cout, t, h, w), [13, seed], dtype=dtype))
+    return x, np.asarray(wt, np.float64), np.asarray(b, np.float64), r
+
+
+CONV_CASES = [
+    # (N, T, H, W), Cin, Cout, out dtype, residual, box (t0,t1,h0,h1,w0,w1) or None
+    ((1, 3, 9, 17), 32, 64, "bf16", False, None),
+    ((1, 5, 10, 20), 64, 128, "f32", True, None),
+    ((2, 2, 8, 16), 32, 48, "f32", False, None),
+    ((1, 4, 11, 23), 128, 256, "bf16", True, (1, 4, 2, 9, 5, 15)),
+    ((1, 1, 7, 5), 96, 128, "bf16", False, None),
+    ((1, 6, 16, 32), 256, 384, "f32", True, (0, 6, 0, 16, 8, 24)),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES)
+def test_conv3d_mfma_matches_oracle(v, case):
+    import torch
+    (n, t, h, w), cin, cout, odt, use_res, bx = case
+    x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", CONV_CASES.index(case))
+    ref = oracle.causal_conv3d(x, wt, b)
+    if use_res:
+        ref = ref + r
+    xd = dev(x)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, odt) if use_res else None
+    y = torch.full((n, t, h, w, cout), 7.0, device="cuda",
+                   dtype=torch.float32 if odt == "f32" else torch.bfloat16)
+    v.vae_conv3d_causal(xd, wd, bd, rd, y, bx)
+    torch.cuda.synchronize()
+    got = host(y)
+    if bx is None:
+        bx = (0, t, 0, h, 0, w)
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    mask = np.zeros(got.shape, bool)
+    mask[sl] = True
+    assert np.all(got[~mask] == 7.0), "conv wrote outside its box"
+    g, rf = got[sl], ref[sl]
+    if odt == "f32":
+        assert rel_max_abs(g, rf) <= 1e-4
+    else:
+        assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
+
+
+@pytest.mark.parametrize("dtype,cin", [("f32", 16), ("f32", 32), ("bf16", 16), ("bf16", 24)])
+def test_conv3d_direct_paths(v, dtype, cin):
+    import torch
+    x, wt, b, _ = _conv_inputs((1, 3, 6, 9), cin, 20, dtype, cin)
+    ref = oracle.causal_conv3d(x, wt, b)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = torch.empty((1, 3, 6, 9, 20), device="cuda", dtype=torch.float32)
+    v.vae_conv3d_causal(dev(x, dtype), v.conv_weight_layout(wt, tdt, "cuda"),
+                        torch.as_tensor(b, dtype=torch.float32, device="cuda"), None, y)
+    torch.cuda.synchronize()
+    assert rel_max_abs(host(y), ref) <= 1e-4
+
+
+def test_conv3d_rejects_bad_arguments(v):
+    import torch
+    x = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.bfloat16)
+    w = torch.zeros((16, 3, 3, 3, 32), device="cuda", dtype=torch.bfloat16)
+    y = torch.zeros((1, 2, 4, 5, 16), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(v.VaeError) as e:
+        v.vae_conv3d_causal(x, w, None, None, y)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    y = torch.zeros((1, 2, 4, 4, 16), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(v.VaeError):
+        v.vae_conv3d_causal(x, w, None, None, y, (0, 3, 0, 4, 0, 4))
+
+
+GN_CASES = [
+    # dtype, (N, T, H, W, C), groups, patch cuts (h cuts, w cuts)
+    ("f32", (1, 5, 32, 32, 32), 8, ([], [16])),
+    ("f32", (2, 3, 16, 16, 64), 32, ([7], [3, 11])),
+    ("bf16", (1, 3, 12, 20, 128), 32, ([5], [10])),
+    ("bf16", (1, 2, 8, 10, 1024), 32, ([], [1, 5, 9])),
+    ("bf16", (1, 4, 9, 13, 256), 32, ([], [])),
+    ("f32", (1, 3, 8, 8, 32), 32, ([4], [4])),
+]
+
+
+def _boxes(shape, cuts):
+    _, t, h, w, _ = shape
+    hs = [0] + cuts[0] + [h]
+    ws = [0] + cuts[1] + [w]
+    return [(0, t, hs[i], hs[i + 1], ws[j], ws[j + 1])
+            for i in range(len(hs) - 1) for j in range(len(ws) - 1)]
+
+
+@pytest.mark.parametrize("case", GN_CASES)
+def test_groupnorm_silu_patch_stats(v, case):
+    import torch
+    dtype, shape, groups, cuts = case
+    n, t, h, w, c = shape
+    x = ndhwc(vae_synth.normal((n, c, t, h, w), [20, c, h], scale=1.5, mean=0.3, dtype=dtype))
+    gamma = vae_synth.normal((c,), [21, c], scale=0.2, mean=1.0)
+    beta = vae_synth.normal((c,), [22, c], scale=0.1)
+    ref = oracle.silu(oracle.group_norm(x, groups, 1e-6, gamma, beta))
+    boxes = _boxes(shape, cuts)
+    xd = dev(x, dtype)
+    y = torch.empty_like(xd)
+    v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, torch.as_tensor(gamma, device="cuda"),
+                         torch.as_tensor(beta, device="cuda"), True, y)
+    torch.cuda.synchronize()
+    got = host(y)
+    if dtype == "f32":
+        assert rel_max_abs(got, ref) <= 1e-4
+    else:
+        assert np.all(np.abs(got - ref) <= bf16_round_bound(ref) + 1e-4 * np.abs(ref).max())
+    # determinism: same call, bitwise same result (in place this time)
+    v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, torch.as_tensor(gamma, device="cuda"),
+                         torch.as_tensor(beta, device="cuda"), True, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(xd, y)
+
+
+def test_groupnorm_stats_export_and_combine(v):
+    import torch
+    shape, groups = (2, 3, 10, 12, 64), 32
+    x = ndhwc(vae_synth.normal((2, 64, 3, 10, 12), [23], scale=2.0, mean=-1.0))
+    boxes = _boxes(shape, ([4], [5, 9]))
+    xd = dev(x, "f32")
+    part = torch.zeros((len(boxes), 2, groups, 3), dtype=torch.float64, device="cuda")
+    v.vae_groupnorm_stats(xd, boxes, groups, part)
+    mr = torch.zeros((2, groups, 2), dtype=torch.float32, device="cuda")
+    v.vae_groupnorm_combine(part, len(boxes), 2, groups, 1e-6, mr)
+    torch.cuda.synchronize()
+    p = part.cpu().numpy()
+    for i, bx in enumerate(boxes):
+        cnt, mean, m2 = oracle.group_moments(x[:, bx[0]:bx[1], bx[2]:bx[3], bx[4]:bx[5]], groups)
+        assert np.array_equal(p[i, :, :, 0], cnt.astype(np.float64))
+        np.testing.assert_allclose(p[i, :, :, 1], mean, rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(p[i, :, :, 2], m2, rtol=1e-5)
+    cnt, mean, m2 = oracle.group_moments(x, groups)
+    got = mr.cpu().numpy()
+    np.testing.assert_allclose(got[..., 0], mean, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(got[..., 1], 1 / np.sqrt(m2 / cnt + 1e-6), rtol=1e-5)
+    # apply with the exported statistics equals the one-call path
+    y1 = torch.empty_like(xd)
+    v.vae_groupnorm_apply(xd, None, groups, mr, None, None, False, y1)
+    ref = oracle.group_norm(x, groups, 1e-6)
+    torch.cuda.synchronize()
+    assert rel_max_abs(host(y1), ref) <= 1e-4
+
+
+def test_groupnorm_large_mean_stress(v):
+    """fp32 input with mean 1e3 and std 1: the case random weights never produce."""
+    import torch
+    x = ndhwc(vae_synth.normal((1, 32, 4, 16, 24), [24], scale=1.0, mean=1e3))
+    ref = oracle.group_norm(x, 8, 1e-6)
+    xd = dev(x, "f32")
+    y = torch.empty_like(xd)
+    v.vae_groupnorm_silu(xd, _boxes((1, 4, 16, 24, 32), ([], [12])), 8, 1e-6, None, None, False, y)
+    torch.cuda.synchronize()
+    assert rel_max_abs(host(y), ref) <= 1e-4
+
+
+UP_CASES = [
+    ("bf16", (1, 3, 4, 5, 64), "d2s", (2, 2, 2), None),
+    ("bf16", (2, 2, 3, 4, 32), "d2s", (2, 2, 2), (1, 2, 0, 3, 1, 4)),
+    ("f32", (1, 3, 4, 6, 48), "d2s", (1, 4, 4), None),
+    ("f32", (1, 2, 5, 3, 12), "d2s", (2, 1, 1), None),
+    ("bf16", (1, 2, 3, 4, 16), "nearest", (1, 2, 2), None),
+    ("f32", (1, 1, 3, 3, 4), "nearest", (1, 2, 3), (0, 1, 1, 3, 0, 2)),
+]
+
+
+@pytest.mark.parametrize("case", UP_CASES)
+def test_upsample_bit_exact(v, case):
+    import torch
+    dtype, shape, mode, (st, sh, sw), bx = case
+    n, t, h, w, c = shape
+    x = ndhwc(vae_synth.normal((n, c, t, h, w), [25, c], dtype=dtype))
+    if mode == "d2s":
+        ref = oracle.depth_to_space(x, st, sh, sw)
+        m = v.VAE_UPSAMPLE_D2S
+    else:
+        ref = oracle.nearest_upsample(x, sh, sw)
+        m = v.VAE_UPSAMPLE_NEAREST
+    xd = dev(x, dtype)
+    y = torch.full(ref.shape, -3.0, device="cuda", dtype=xd.dtype)
+    v.vae_upsample(xd, bx, m, st, sh, sw, y)
+    torch.cuda.synchronize()
+    got = host(y)
+    if bx is None:
+        assert np.array_equal(got, ref)
+    else:
+        t0, t1, h0, h1, w0, w1 = bx
+        lo_t = max(0, st * t0 - (st - 1))
+        sl = (slice(None), slice(lo_t, st * t1 - (st - 1)), slice(sh * h0, sh * h1),
+              slice(sw * w0, sw * w1))
+        assert np.array_equal(got[sl], ref[sl])
+        mask = np.zeros(got.shape, bool)
+        mask[sl] = True
+        assert np.all(got[~mask] == -3.0)
+
+
+@pytest.mark.parametrize("grid", [((16, 16), (14, 14), (22, 40), (2, 4, 4)),
+                                  ((4, 5), (3, 2), (9, 11), (1, 3, 2)),
+                                  ((8, 8), (8, 8), (8, 8), (1, 2, 2))])
+def test_tile_merge_matches_oracle(v, grid):
+    import torch
+    tile, stride, (lh, lw), scale = grid
+    desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 2, lh, lw, 3), scale, tile=tile,
+                         stride=stride)
+    tiles = v.vae_tile_split(desc)
+    ref_tiles = oracle.overlap_tiles(2, lh, lw, tile, stride, scale)
+    out_shape = (1, 1 + (2 - 1) * scale[0], lh * scale[1], lw * scale[2], 3)
+    outs = []
+    for k, tl in enumerate(ref_tiles):
+        o = tl["out"]
+        outs.append(vae_synth.normal((1, o[1] - o[0], o[3] - o[2], o[5] - o[4], 3), [26, k])
+                    .astype(np.float64))
+    ref = oracle.merge_tiles(outs, ref_tiles, out_shape)
+    out = torch.full(out_shape, 5.0, device="cuda", dtype=torch.float32)
+    for k, tl in enumerate(tiles):
+        flags = (v.VAE_MERGE_ZERO if k == 0 else 0) | \
+                (v.VAE_MERGE_FINALIZE if k == len(tiles) - 1 else 0)
+        v.vae_tile_merge(dev(outs[k], "f32"), tl, desc, out, flags)
+    torch.cuda.synchronize()
+    assert rel_max_abs(host(out), ref) <= 1e-5

@@ -13,7 +13,8 @@ is built from its config.json with random weights):
 - ``TINY_DECODER``: a small fp32 causal decoder, latent [1,16,3,16,16] -> video [1,3,5,64,64].
 - ``LTX2_720P``: an LTX-2-shaped bf16 decoder, latent [1,128,16,22,40] -> video [1,3,121,704,1280].
 - ``LTX2_SMALL`` / ``LTX2_MID``: the same layer plan at small latents, for parity at oracle-friendly
-  sizes.
+  sizes;
+- ``LTX2_TINY``: the same structure at a quarter of the widths, for a quick smoke check.
 
 Layer plan vocabulary (every op works on a channels-last activation):
 - ``conv``: causal Conv3d 3x3x3, stride 1, ``cin`` -> ``cout``; ``"f32_out": True`` keeps the result
@@ -36,7 +37,7 @@ import copy
 import numpy as np
 
 __all__ = [
-    "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "WORKLOADS",
+    "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "LTX2_TINY", "WORKLOADS",
     "round_bf16", "bf16_bits", "normal", "uniform", "latent", "decoder_params", "conv_params",
     "walk_plan", "with_latent",
 ]
@@ -122,11 +123,40 @@ def with_latent(spec: dict, latent_shape, name: str, **extra) -> dict:
 
 
 LTX2_SMALL = with_latent(LTX2_720P, (1, 128, 2, 3, 5), "ltx2_small",
-                         patch_grid=(1, 2), overlap_tile=(2, 3), overlap_stride=(1, 2))
+                         patch_grid=(1, 2), overlap_tile=(3, 4), overlap_stride=(2, 3))
 LTX2_MID = with_latent(LTX2_720P, (1, 128, 3, 4, 6), "ltx2_mid",
                        patch_grid=(2, 3), overlap_tile=(3, 4), overlap_stride=(2, 3))
 
-WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID)}
+# The LTX-2 layer plan at a quarter of the widths (256/128/64/32), on a small latent: every kernel
+# path of the 720p plan at a size the oracle decodes in about a second (smoke check).
+LTX2_TINY = {
+    "name": "ltx2_tiny",
+    "dtype": "bf16",
+    "latent": (1, 128, 2, 4, 6),
+    "groups": 32, "eps": 1e-6,
+    "layers": [
+        {"op": "conv", "cin": 128, "cout": 256},
+        {"op": "res", "c": 256},
+        {"op": "conv", "cin": 256, "cout": 1024},
+        {"op": "d2s", "st": 2, "sh": 2, "sw": 2},
+        {"op": "res", "c": 128},
+        {"op": "conv", "cin": 128, "cout": 512},
+        {"op": "d2s", "st": 2, "sh": 2, "sw": 2},
+        {"op": "res", "c": 64},
+        {"op": "conv", "cin": 64, "cout": 256},
+        {"op": "d2s", "st": 2, "sh": 2, "sw": 2},
+        {"op": "res", "c": 32},
+        {"op": "gn_silu"},
+        {"op": "conv", "cin": 32, "cout": 48, "f32_out": True},
+        {"op": "d2s", "st": 1, "sh": 4, "sw": 4},
+    ],
+    "scale": (8, 32, 32),
+    "patch_grid": (1, 2),
+    "overlap_tile": (3, 4), "overlap_stride": (2, 3),
+}
+
+WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
+                                    LTX2_TINY)}
 
 
 # ----------------------------------------------------------------------------------------------

@@ -1,0 +1,356 @@
+"""ctypes binding of libvae_mi355x.so: the same entry points as include/vae.h.
+
+Argument marshalling only. Torch tensors supply device memory and the current HIP stream. Every
+step of the decode runs in the library's HIP kernels, and there is no Python or CPU fallback: if the
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvae_mi355x.so")
+
+VAE_OK, VAE_ERR_INVALID_ARG, VAE_ERR_UNSUPPORTED, VAE_ERR_HIP, VAE_ERR_WORKSPACE = range(5)
+VAE_DTYPE_BF16, VAE_DTYPE_F32 = 1, 2
+VAE_UPSAMPLE_NEAREST, VAE_UPSAMPLE_D2S = 1, 2
+VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
+VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
+VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
+VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
+
+# Every symbol include/vae.h declares.
+EXPORTS = (
+    "vae_last_error", "vae_last_error_info", "vae_version", "vae_conv3d_causal",
+    "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
+    "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_upsample",
+    "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
+    "vae_decode_workspace_size", "vae_decode_tiled", "vae_decoder_set_timing",
+    "vae_decoder_get_timing",
+)
+
+
+class vae_tensor_t(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("t", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("w", ctypes.c_int64), ("c", ctypes.c_int64)]
+
+
+class vae_box_t(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("t0", "t1", "h0", "h1", "w0", "w1")]
+
+
+class vae_error_info_t(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("axis", ctypes.c_int32), ("extent", ctypes.c_int64),
+                ("required_multiple", ctypes.c_int64), ("min_width", ctypes.c_int64)]
+
+
+class vae_tiling_desc_t(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in (
+        "mode", "n", "t", "h", "w", "scale_t", "scale_h", "scale_w", "patches_h", "patches_w",
+        "tile_h", "tile_w", "stride_h", "stride_w")]
+
+
+class vae_tile_t(ctypes.Structure):
+    _fields_ = [("index", ctypes.c_int32), ("row", ctypes.c_int32), ("col", ctypes.c_int32),
+                ("latent", vae_box_t), ("out", vae_box_t),
+                ("lead_t", ctypes.c_int32), ("lead_h", ctypes.c_int32), ("lead_w", ctypes.c_int32),
+                ("trail_t", ctypes.c_int32), ("trail_h", ctypes.c_int32),
+                ("trail_w", ctypes.c_int32)]
+
+
+class vae_layer_desc_t(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("op", "cin", "cout", "st", "sh", "sw", "f32_out")]
+
+
+class vae_decoder_spec_t(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("latent_channels", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("eps", ctypes.c_float), ("n_layers", ctypes.c_int32),
+                ("layers", ctypes.POINTER(vae_layer_desc_t))]
+
+
+class vae_op_timing_t(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("layer", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m video_diffusion_vae_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    T = ctypes.POINTER(vae_tensor_t)
+    B = ctypes.POINTER(vae_box_t)
+    D = ctypes.POINTER(vae_tiling_desc_t)
+    sig = {
+        "vae_last_error": ([], ctypes.c_char_p),
+        "vae_last_error_info": ([ctypes.POINTER(vae_error_info_t)], I32),
+        "vae_version": ([], I32),
+        "vae_conv3d_causal": ([T, P, P, T, T, B, P], I32),
+        "vae_groupnorm_silu_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
+        "vae_groupnorm_silu": ([T, B, I32, I32, F, P, P, I32, T, P, SZ, P], I32),
+        "vae_groupnorm_stats_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
+        "vae_groupnorm_stats": ([T, B, I32, I32, P, P, SZ, P], I32),
+        "vae_groupnorm_combine": ([P, I32, I32, I32, F, P, P], I32),
+        "vae_groupnorm_apply": ([T, B, I32, P, P, P, I32, T, P], I32),
+        "vae_upsample": ([T, B, I32, I32, I32, I32, T, P], I32),
+        "vae_tile_split": ([D, ctypes.POINTER(vae_tile_t), I32, ctypes.POINTER(I32)], I32),
+        "vae_tile_merge": ([T, ctypes.POINTER(vae_tile_t), D, T, I32, P], I32),
+        "vae_decoder_create": ([ctypes.POINTER(vae_decoder_spec_t), ctypes.POINTER(P), I32,
+                                ctypes.POINTER(P)], I32),
+        "vae_decoder_destroy": ([P], None),
+        "vae_decode_workspace_size": ([P, D, ctypes.POINTER(SZ)], I32),
+        "vae_decode_tiled": ([P, T, D, T, P, SZ, P], I32),
+        "vae_decoder_set_timing": ([P, I32], I32),
+        "vae_decoder_get_timing": ([P, ctypes.POINTER(vae_op_timing_t), I32,
+                                    ctypes.POINTER(I32)], I32),
+    }
+    for name in EXPORTS:
+        fn = getattr(lib, name)
+        fn.argtypes, fn.restype = sig[name]
+    return lib
+
+
+LIB = _load()
+
+
+class VaeError(RuntimeError):
+    def __init__(self, status, message, info):
+        super().__init__(f"vae status {status}: {message}")
+        self.status = status
+        self.info = info
+
+
+def _check(status):
+    if status != VAE_OK:
+        info = vae_error_info_t()
+        LIB.vae_last_error_info(ctypes.byref(info))
+        msg = LIB.vae_last_error().decode()
+        raise VaeError(status, msg, {k: getattr(info, k) for k, _ in info._fields_})
+
+
+def last_error_info():
+    info = vae_error_info_t()
+    LIB.vae_last_error_info(ctypes.byref(info))
+    return {k: getattr(info, k) for k, _ in info._fields_}
+
+
+# ------------------------------------------------------------------------------------------------
+# Marshalling helpers
+# ------------------------------------------------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return VAE_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return VAE_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def tensor_desc(t):
+    """vae_tensor_t of a contiguous NDHWC torch tensor (device memory)."""
+    if t.dim() != 5:
+        raise ValueError("expected an NDHWC tensor [N, T, H, W, C]")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous (NDHWC dense)")
+    n, tt, h, w, c = t.shape
+    return vae_tensor_t(t.data_ptr(), _dtype_code(t), 0, n, tt, h, w, c)
+
+
+def box(b):
+    if b is None:
+        return None
+    return vae_box_t(*[int(v) for v in b])
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def _workspace(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------------------------
+# Entry points (names as in include/vae.h)
+# ------------------------------------------------------------------------------------------------
+
+def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, stream=None):
+    """Causal Conv3d; weight is [Cout, 3, 3, 3, Cin] on the device."""
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    rd = tensor_desc(residual) if residual is not None else None
+    _check(LIB.vae_conv3d_causal(ctypes.byref(xd), _ptr(weight), _ptr(bias), _ref(rd),
+                                 ctypes.byref(yd), _ref(box(out_box)), _stream(stream)))
+    return y
+
+
+def _boxes(boxes):
+    if boxes is None:
+        return None, 1
+    arr = (vae_box_t * len(boxes))(*[box(b) for b in boxes])
+    return arr, len(boxes)
+
+
+def vae_groupnorm_silu_workspace(x, boxes, groups):
+    xd = tensor_desc(x)
+    arr, nb = _boxes(boxes)
+    n = ctypes.c_size_t()
+    _check(LIB.vae_groupnorm_silu_workspace(ctypes.byref(xd), arr, nb, groups, ctypes.byref(n)))
+    return n.value
+
+
+def vae_groupnorm_silu(x, boxes, groups, eps, gamma, beta, apply_silu, y, ws=None, stream=None):
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    arr, nb = _boxes(boxes)
+    if ws is None:
+        ws = _workspace(vae_groupnorm_silu_workspace(x, boxes, groups), x.device)
+    _check(LIB.vae_groupnorm_silu(ctypes.byref(xd), arr, nb, groups, eps, _ptr(gamma), _ptr(beta),
+                                  int(apply_silu), ctypes.byref(yd), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return y
+
+
+def vae_groupnorm_stats(x, boxes, groups, part, ws=None, stream=None):
+    xd = tensor_desc(x)
+    arr, nb = _boxes(boxes)
+    if ws is None:
+        n = ctypes.c_size_t()
+        _check(LIB.vae_groupnorm_stats_workspace(ctypes.byref(xd), arr, nb, groups,
+                                                 ctypes.byref(n)))
+        ws = _workspace(n.value, x.device)
+    _check(LIB.vae_groupnorm_stats(ctypes.byref(xd), arr, nb, groups, _ptr(part), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+    return part
+
+
+def vae_groupnorm_combine(part, n_parts, n, groups, eps, mean_rstd, stream=None):
+    _check(LIB.vae_groupnorm_combine(_ptr(part), n_parts, n, groups, eps, _ptr(mean_rstd),
+                                     _stream(stream)))
+    return mean_rstd
+
+
+def vae_groupnorm_apply(x, out_box, groups, mean_rstd, gamma, beta, apply_silu, y, stream=None):
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    _check(LIB.vae_groupnorm_apply(ctypes.byref(xd), _ref(box(out_box)), groups, _ptr(mean_rstd),
+                                   _ptr(gamma), _ptr(beta), int(apply_silu), ctypes.byref(yd),
+                                   _stream(stream)))
+    return y
+
+
+def vae_upsample(x, in_box, mode, st, sh, sw, y, stream=None):
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    _check(LIB.vae_upsample(ctypes.byref(xd), _ref(box(in_box)), mode, st, sh, sw,
+                            ctypes.byref(yd), _stream(stream)))
+    return y
+
+
+def tiling_desc(mode, latent_shape, scale, patches=(1, 1), tile=(0, 0), stride=(0, 0)):
+    """vae_tiling_desc_t from an NDHWC latent shape [N, T, H, W, C]."""
+    n, t, h, w = latent_shape[:4]
+    return vae_tiling_desc_t(mode, n, t, h, w, scale[0], scale[1], scale[2], patches[0],
+                             patches[1], tile[0], tile[1], stride[0], stride[1])
+
+
+def vae_tile_split(desc):
+    """Host-only. Returns the list of vae_tile_t."""
+    n = ctypes.c_int32()
+    _check(LIB.vae_tile_split(ctypes.byref(desc), None, 0, ctypes.byref(n)))
+    arr = (vae_tile_t * max(n.value, 1))()
+    _check(LIB.vae_tile_split(ctypes.byref(desc), arr, n.value, ctypes.byref(n)))
+    return list(arr[:n.value])
+
+
+def vae_tile_merge(tile_out, tile, desc, out, flags, stream=None):
+    td, od = tensor_desc(tile_out), tensor_desc(out)
+    _check(LIB.vae_tile_merge(ctypes.byref(td), ctypes.byref(tile), ctypes.byref(desc),
+                              ctypes.byref(od), flags, _stream(stream)))
+    return out
+
+
+_OPS = {"conv": VAE_OP_CONV, "res": VAE_OP_RES, "gn_silu": VAE_OP_GN_SILU, "d2s": VAE_OP_D2S,
+        "nearest": VAE_OP_NEAREST}
+
+
+def layer_descs(plan):
+    out = []
+    for op in plan:
+        k = op["op"]
+        if k == "conv":
+            out.append(vae_layer_desc_t(VAE_OP_CONV, op["cin"], op["cout"], 1, 1, 1,
+                                        int(op.get("f32_out", False))))
+        elif k == "res":
+            out.append(vae_layer_desc_t(VAE_OP_RES, op["c"], op["c"], 1, 1, 1, 0))
+        elif k == "gn_silu":
+            out.append(vae_layer_desc_t(VAE_OP_GN_SILU, 0, 0, 1, 1, 1, 0))
+        elif k == "d2s":
+            out.append(vae_layer_desc_t(VAE_OP_D2S, 0, 0, op["st"], op["sh"], op["sw"], 0))
+        elif k == "nearest":
+            out.append(vae_layer_desc_t(VAE_OP_NEAREST, 0, 0, 1, op["sh"], op["sw"], 0))
+        else:
+            raise ValueError(k)
+    return out
+
+
+class Decoder:
+    """vae_decoder_t over a layer plan and device parameter tensors (plan order, two per entry).
+
+    ``params`` is a flat list of device tensors or None: conv -> (weight [Cout,3,3,3,Cin], bias),
+    GN -> (gamma, beta); the tensors must outlive the decoder.
+    """
+
+    def __init__(self, dtype, latent_channels, groups, eps, plan, params):
+        self._keep = list(params)
+        descs = layer_descs(plan)
+        self._layers = (vae_layer_desc_t * len(descs))(*descs)
+        spec = vae_decoder_spec_t(dtype, latent_channels, groups, eps, len(descs), self._layers)
+        ptrs = (ctypes.c_void_p * max(len(params), 1))(
+            *[None if p is None else p.data_ptr() for p in params])
+        h = ctypes.c_void_p()
+        _check(LIB.vae_decoder_create(ctypes.byref(spec), ptrs, len(params), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            LIB.vae_decoder_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def workspace_size(self, desc):
+        n = ctypes.c_size_t()
+        _check(LIB.vae_decode_workspace_size(self._h, ctypes.byref(desc), ctypes.byref(n)))
+        return n.value
+
+    def vae_decode_tiled(self, latent, desc, out, ws, stream=None):
+        ld, od = tensor_desc(latent), tensor_desc(out)
+        _check(LIB.vae_decode_tiled(self._h, ctypes.byref(ld), ctypes.byref(desc),
+                                    ctypes.byref(od), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def set_timing(self, enable):
+        _check(LIB.vae_decoder_set_timing(self._h, int(enable)))
+
+    def timing(self):
+        n = ctypes.c_int32()
+        _check(LIB.vae_decoder_get_timing(self._h, None, 0, ctypes.byref(n)))
+        arr = (vae_op_timing_t * max(n.value, 1))()
+        _check(LIB.vae_decoder_get_timing(self._h, arr, n.value, ctypes.byref(n)))
+        return [{"kind": VAE_KIND_NAMES[r.kind], "layer": r.layer, "tile": r.tile, "ms": r.ms,
+                 "flops": r.flops, "bytes": r.bytes} for r in arr[:n.value]]

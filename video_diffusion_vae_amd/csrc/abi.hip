@@ -1,0 +1,429 @@
+// Exported C entry points: argument validation, thread-local error reporting, the host-only tile
+// split, and dispatch to the kernel launchers. No exception crosses this boundary.
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "host.h"
+
+namespace vae {
+
+ErrorState& error_state() {
+    static thread_local ErrorState st;
+    return st;
+}
+
+vae_status_t fail(vae_status_t st, const std::string& msg, int32_t axis, int64_t extent,
+                  int64_t multiple, int64_t min_width) {
+    ErrorState& e = error_state();
+    e.text = msg;
+    e.info = vae_error_info_t{st, axis, extent, multiple, min_width};
+    return st;
+}
+
+void clear_error() {
+    ErrorState& e = error_state();
+    e.text.clear();
+    e.info = vae_error_info_t{VAE_OK, -1, -1, -1, -1};
+}
+
+// ------------------------------------------------------------------------------------------------
+// Validation helpers
+// ------------------------------------------------------------------------------------------------
+vae_status_t check_tensor(const vae_tensor_t* t, const char* name) {
+    if (!t) return fail(VAE_ERR_INVALID_ARG, std::string(name) + " is NULL");
+    if (t->dtype != VAE_DTYPE_BF16 && t->dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": unknown dtype");
+    const int64_t d[5] = {t->n, t->t, t->h, t->w, t->c};
+    for (int i = 0; i < 5; ++i)
+        if (d[i] < 0 || d[i] > INT32_MAX)
+            return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": extent out of range", i, d[i]);
+    if (t->c < 1) return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": no channels", 4, t->c);
+    if (t->h * t->w > INT32_MAX || t->t * t->h > INT32_MAX)
+        return fail(VAE_ERR_UNSUPPORTED, std::string(name) + ": spatial extent too large");
+    if (numel(*t) > 0 && !t->data)
+        return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": data is NULL");
+    if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": data must be 16-byte aligned");
+    return VAE_OK;
+}
+
+vae_status_t check_box(const vae_box_t* b, const vae_tensor_t& t, const char* name) {
+    if (!b) return VAE_OK;
+    if (b->t0 < 0 || b->t0 > b->t1 || b->t1 > t.t)
+        return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": T range outside the tensor", 1, t.t);
+    if (b->h0 < 0 || b->h0 > b->h1 || b->h1 > t.h)
+        return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": H range outside the tensor", 2, t.h);
+    if (b->w0 < 0 || b->w0 > b->w1 || b->w1 > t.w)
+        return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": W range outside the tensor", 3, t.w);
+    return VAE_OK;
+}
+
+bool overlaps(const vae_tensor_t& a, const vae_tensor_t& b) {
+    const uint8_t* pa = static_cast<const uint8_t*>(a.data);
+    const uint8_t* pb = static_cast<const uint8_t*>(b.data);
+    const int64_t la = numel(a) * elem_size(a.dtype), lb = numel(b) * elem_size(b.dtype);
+    if (la == 0 || lb == 0) return false;
+    return pa < pb + lb && pb < pa + la;
+}
+
+bool same_grid(const vae_tensor_t& a, const vae_tensor_t& b) {
+    return a.n == b.n && a.t == b.t && a.h == b.h && a.w == b.w;
+}
+
+vae_status_t box_list(const vae_tensor_t& x, const vae_box_t* boxes, int32_t n_boxes,
+                      BoxList* out) {
+    if (n_boxes < 1 || n_boxes > kMaxBoxes)
+        return fail(VAE_ERR_UNSUPPORTED, "n_boxes must be in 1..16", -1, n_boxes, -1, 1);
+    if (!boxes && n_boxes != 1) return fail(VAE_ERR_INVALID_ARG, "boxes is NULL but n_boxes > 1");
+    out->n = n_boxes;
+    for (int i = 0; i < n_boxes; ++i) {
+        if (boxes) VAE_TRY(check_box(&boxes[i], x, "boxes[i]"));
+        out->b[i] = to_box(boxes ? &boxes[i] : nullptr, x);
+    }
+    for (int i = 0; i < n_boxes; ++i)
+        for (int j = 0; j < i; ++j) {
+            const Box& a = out->b[i];
+            const Box& b = out->b[j];
+            if (a.volume() && b.volume() && a.t0 < b.t1 && b.t0 < a.t1 && a.h0 < b.h1 &&
+                b.h0 < a.h1 && a.w0 < b.w1 && b.w0 < a.w1)
+                return fail(VAE_ERR_INVALID_ARG, "boxes must not overlap");
+        }
+    return VAE_OK;
+}
+
+vae_status_t check_gn(const vae_tensor_t* x, int32_t groups) {
+    VAE_TRY(check_tensor(x, "x"));
+    if (groups < 1 || x->c % groups != 0)
+        return fail(VAE_ERR_UNSUPPORTED, "channels must be divisible by groups", 4, x->c, groups);
+    if (!gn_shape_supported(*x, groups))
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "group norm needs C/vec to divide 256 and groups aligned to 16-byte vectors",
+                    4, x->c, x->dtype == VAE_DTYPE_BF16 ? 8 : 4);
+    return VAE_OK;
+}
+
+size_t gn_full_workspace(const vae_tensor_t& x, const BoxList& bl, int32_t groups) {
+    return align_up(gn_stats_workspace(x, bl, groups), 256) +
+           align_up((size_t)x.n * groups * 2 * sizeof(float), 256);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Tile split (host integer maths)
+// ------------------------------------------------------------------------------------------------
+struct Band {
+    int32_t start, size;
+};
+
+vae_status_t bands(int32_t length, int32_t parts, int axis, std::vector<Band>* out) {
+    if (parts < 1)
+        return fail(VAE_ERR_INVALID_ARG, "patch count must be >= 1", axis, parts, -1, 1);
+    if (parts > length)
+        // every patch needs at least one row: the one-row halo must come from a direct neighbour
+        return fail(VAE_ERR_UNSUPPORTED, "a patch would be narrower than the one-row halo", axis,
+                    length, -1, parts);
+    const int32_t q = length / parts, r = length % parts;
+    int32_t s = 0;
+    out->clear();
+    for (int32_t i = 0; i < parts; ++i) {
+        const int32_t sz = i < r ? q + 1 : q;
+        out->push_back(Band{s, sz});
+        s += sz;
+    }
+    return VAE_OK;
+}
+
+vae_status_t check_tiling(const vae_tiling_desc_t* d) {
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "tiling desc is NULL");
+    if (d->n < 1 || d->t < 1 || d->h < 1 || d->w < 1)
+        return fail(VAE_ERR_INVALID_ARG, "latent extents must be >= 1");
+    if (d->scale_t < 1 || d->scale_h < 1 || d->scale_w < 1)
+        return fail(VAE_ERR_INVALID_ARG, "scales must be >= 1");
+    if (d->mode == VAE_TILING_PATCH_HALO) {
+        std::vector<Band> b;
+        VAE_TRY(bands(d->h, d->patches_h, 2, &b));
+        VAE_TRY(bands(d->w, d->patches_w, 3, &b));
+    } else if (d->mode == VAE_TILING_OVERLAP_BLEND) {
+        const AxisTiling ax[2] = {{d->h, d->tile_h, d->stride_h, d->scale_h},
+                                  {d->w, d->tile_w, d->stride_w, d->scale_w}};
+        for (int i = 0; i < 2; ++i) {
+            if (axis_is_cut(ax[i]) && (ax[i].stride < 1 || ax[i].stride > ax[i].tile))
+                return fail(VAE_ERR_UNSUPPORTED, "tile stride must be in 1..tile (no gaps)",
+                            2 + i, ax[i].stride, -1, 1);
+        }
+    } else {
+        return fail(VAE_ERR_INVALID_ARG, "unknown tiling mode");
+    }
+    return VAE_OK;
+}
+
+int32_t out_frames(int32_t t, int32_t scale_t) { return 1 + (t - 1) * scale_t; }
+
+std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
+    std::vector<vae_tile_t> tiles;
+    const int32_t to = out_frames(d.t, d.scale_t);
+    if (d.mode == VAE_TILING_PATCH_HALO) {
+        std::vector<Band> hb, wb;
+        bands(d.h, d.patches_h, 2, &hb);
+        bands(d.w, d.patches_w, 3, &wb);
+        for (size_t i = 0; i < hb.size(); ++i)
+            for (size_t j = 0; j < wb.size(); ++j) {
+                vae_tile_t t{};
+                t.index = (int32_t)tiles.size();
+                t.row = (int32_t)i;
+                t.col = (int32_t)j;
+                t.latent = vae_box_t{0, d.t, hb[i].start, hb[i].start + hb[i].size, wb[j].start,
+                                     wb[j].start + wb[j].size};
+                t.out = vae_box_t{0, to, hb[i].start * d.scale_h,
+                                  (hb[i].start + hb[i].size) * d.scale_h, wb[j].start * d.scale_w,
+                                  (wb[j].start + wb[j].size) * d.scale_w};
+                tiles.push_back(t);
+            }
+    } else {
+        const AxisTiling ah{d.h, d.tile_h, d.stride_h, d.scale_h};
+        const AxisTiling aw{d.w, d.tile_w, d.stride_w, d.scale_w};
+        for (int32_t i = 0; i < axis_count(ah); ++i)
+            for (int32_t j = 0; j < axis_count(aw); ++j) {
+                int32_t hs, hn, ws, wn;
+                axis_span(ah, i, &hs, &hn);
+                axis_span(aw, j, &ws, &wn);
+                vae_tile_t t{};
+                t.index = (int32_t)tiles.size();
+                t.row = i;
+                t.col = j;
+                t.latent = vae_box_t{0, d.t, hs, hs + hn, ws, ws + wn};
+                t.out = vae_box_t{0, to, hs * d.scale_h, (hs + hn) * d.scale_h, ws * d.scale_w,
+                                  (ws + wn) * d.scale_w};
+                t.lead_h = axis_lead(ah, i);
+                t.trail_h = axis_trail(ah, i);
+                t.lead_w = axis_lead(aw, j);
+                t.trail_w = axis_trail(aw, j);
+                tiles.push_back(t);
+            }
+    }
+    return tiles;
+}
+
+}  // namespace vae
+
+using namespace vae;
+
+extern "C" {
+
+VAE_API const char* vae_last_error(void) { return error_state().text.c_str(); }
+
+VAE_API vae_status_t vae_last_error_info(vae_error_info_t* info) {
+    if (!info) return VAE_ERR_INVALID_ARG;
+    *info = error_state().info;
+    return VAE_OK;
+}
+
+VAE_API int32_t vae_version(void) { return 100; }
+
+VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
+                                       const float* bias, const vae_tensor_t* residual,
+                                       vae_tensor_t* y, const vae_box_t* out_box,
+                                       vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_tensor(x, "x"));
+    VAE_TRY(check_tensor(y, "y"));
+    if (!weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
+    if (reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "weight must be 16-byte aligned");
+    if (!same_grid(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "x and y must share N, T, H, W");
+    if (x->dtype == VAE_DTYPE_F32 && y->dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_UNSUPPORTED, "fp32 input needs an fp32 output");
+    if (residual) {
+        VAE_TRY(check_tensor(residual, "residual"));
+        if (!same_grid(*residual, *y) || residual->c != y->c || residual->dtype != y->dtype)
+            return fail(VAE_ERR_INVALID_ARG, "residual must match y in shape and dtype");
+        if (overlaps(*residual, *x)) return fail(VAE_ERR_INVALID_ARG, "residual overlaps x");
+    }
+    if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
+    VAE_TRY(check_box(out_box, *y, "out_box"));
+    return launch_conv3d(*x, weight, bias, residual, *y, to_box(out_box, *y), as_stream(stream));
+}
+
+VAE_API vae_status_t vae_groupnorm_stats_workspace(const vae_tensor_t* x, const vae_box_t* boxes,
+                                                   int32_t n_boxes, int32_t groups,
+                                                   size_t* bytes) {
+    clear_error();
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");
+    VAE_TRY(check_gn(x, groups));
+    BoxList bl;
+    VAE_TRY(box_list(*x, boxes, n_boxes, &bl));
+    *bytes = gn_stats_workspace(*x, bl, groups);
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_groupnorm_silu_workspace(const vae_tensor_t* x, const vae_box_t* boxes,
+                                                  int32_t n_boxes, int32_t groups, size_t* bytes) {
+    clear_error();
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");
+    VAE_TRY(check_gn(x, groups));
+    BoxList bl;
+    VAE_TRY(box_list(*x, boxes, n_boxes, &bl));
+    *bytes = gn_full_workspace(*x, bl, groups);
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_groupnorm_stats(const vae_tensor_t* x, const vae_box_t* boxes,
+                                         int32_t n_boxes, int32_t groups, double* part, void* ws,
+                                         size_t ws_bytes, vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_gn(x, groups));
+    BoxList bl;
+    VAE_TRY(box_list(*x, boxes, n_boxes, &bl));
+    if (!part) return fail(VAE_ERR_INVALID_ARG, "part is NULL");
+    const size_t need = gn_stats_workspace(*x, bl, groups);
+    if (!ws || ws_bytes < need)
+        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
+                    (int64_t)need);
+    return launch_gn_stats(*x, bl, groups, static_cast<double*>(ws), part, nullptr, 0.0f,
+                           as_stream(stream));
+}
+
+VAE_API vae_status_t vae_groupnorm_combine(const double* part, int32_t n_parts, int32_t n,
+                                           int32_t groups, float eps, float* mean_rstd,
+                                           vae_stream_t stream) {
+    clear_error();
+    if (!part || !mean_rstd) return fail(VAE_ERR_INVALID_ARG, "part or mean_rstd is NULL");
+    if (n_parts < 1 || n < 1 || groups < 1 || !(eps >= 0.0f))
+        return fail(VAE_ERR_INVALID_ARG, "n_parts, n, groups must be >= 1 and eps >= 0");
+    return launch_gn_combine(part, n_parts, n, groups, eps, mean_rstd, as_stream(stream));
+}
+
+VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t* box,
+                                         int32_t groups, const float* mean_rstd,
+                                         const float* gamma, const float* beta,
+                                         int32_t apply_silu, vae_tensor_t* y,
+                                         vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_gn(x, groups));
+    VAE_TRY(check_tensor(y, "y"));
+    if (!same_grid(*x, *y) || x->c != y->c || x->dtype != y->dtype)
+        return fail(VAE_ERR_INVALID_ARG, "y must match x in shape and dtype");
+    if (x->data != y->data && overlaps(*x, *y))
+        return fail(VAE_ERR_INVALID_ARG, "y must be x itself or not overlap it");
+    if (!mean_rstd) return fail(VAE_ERR_INVALID_ARG, "mean_rstd is NULL");
+    VAE_TRY(check_box(box, *x, "box"));
+    return launch_gn_apply(*x, to_box(box, *x), groups, mean_rstd, gamma, beta, apply_silu != 0,
+                           *y, as_stream(stream));
+}
+
+VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* boxes,
+                                        int32_t n_boxes, int32_t groups, float eps,
+                                        const float* gamma, const float* beta, int32_t apply_silu,
+                                        vae_tensor_t* y, void* ws, size_t ws_bytes,
+                                        vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_gn(x, groups));
+    VAE_TRY(check_tensor(y, "y"));
+    if (!same_grid(*x, *y) || x->c != y->c || x->dtype != y->dtype)
+        return fail(VAE_ERR_INVALID_ARG, "y must match x in shape and dtype");
+    if (x->data != y->data && overlaps(*x, *y))
+        return fail(VAE_ERR_INVALID_ARG, "y must be x itself or not overlap it");
+    if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
+    BoxList bl;
+    VAE_TRY(box_list(*x, boxes, n_boxes, &bl));
+    const size_t need = gn_full_workspace(*x, bl, groups);
+    if (!ws || ws_bytes < need)
+        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
+                    (int64_t)need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    double* stats = static_cast<double*>(ws);
+    float* mr = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                         align_up(gn_stats_workspace(*x, bl, groups), 256));
+    hipStream_t s = as_stream(stream);
+    VAE_TRY(launch_gn_stats(*x, bl, groups, stats, nullptr, mr, eps, s));
+    for (int i = 0; i < bl.n; ++i)
+        VAE_TRY(launch_gn_apply(*x, bl.b[i], groups, mr, gamma, beta, apply_silu != 0, *y, s));
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_upsample(const vae_tensor_t* x, const vae_box_t* box, int32_t mode,
+                                  int32_t st, int32_t sh, int32_t sw, vae_tensor_t* y,
+                                  vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_tensor(x, "x"));
+    VAE_TRY(check_tensor(y, "y"));
+    if (st < 1 || sh < 1 || sw < 1) return fail(VAE_ERR_INVALID_ARG, "factors must be >= 1");
+    if (x->dtype != y->dtype) return fail(VAE_ERR_INVALID_ARG, "x and y dtypes differ");
+    if (x->n != y->n) return fail(VAE_ERR_INVALID_ARG, "x and y batch differ");
+    if (mode == VAE_UPSAMPLE_D2S) {
+        const int64_t k = (int64_t)st * sh * sw;
+        if (x->c != y->c * k)
+            return fail(VAE_ERR_INVALID_ARG, "d2s: x channels must be y channels * st*sh*sw", 4,
+                        x->c, k);
+        if (y->t != st * x->t - (st - 1) || y->h != x->h * sh || y->w != x->w * sw)
+            return fail(VAE_ERR_INVALID_ARG, "d2s: y shape must be (st*T-(st-1), sh*H, sw*W)");
+    } else if (mode == VAE_UPSAMPLE_NEAREST) {
+        if (st != 1) return fail(VAE_ERR_UNSUPPORTED, "nearest: temporal factor must be 1");
+        if (x->c != y->c || y->t != x->t || y->h != x->h * sh || y->w != x->w * sw)
+            return fail(VAE_ERR_INVALID_ARG, "nearest: y shape must be (T, sh*H, sw*W, C)");
+    } else {
+        return fail(VAE_ERR_INVALID_ARG, "unknown upsample mode");
+    }
+    if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
+    VAE_TRY(check_box(box, *x, "box"));
+    return launch_upsample(*x, to_box(box, *x), mode, st, sh, sw, *y, as_stream(stream));
+}
+
+VAE_API vae_status_t vae_tile_split(const vae_tiling_desc_t* desc, vae_tile_t* tiles,
+                                    int32_t capacity, int32_t* n_tiles) {
+    clear_error();
+    if (!n_tiles) return fail(VAE_ERR_INVALID_ARG, "n_tiles is NULL");
+    VAE_TRY(check_tiling(desc));
+    std::vector<vae_tile_t> v;
+    try {
+        v = make_tiles(*desc);
+    } catch (const std::bad_alloc&) {
+        return fail(VAE_ERR_INVALID_ARG, "out of host memory");
+    }
+    *n_tiles = (int32_t)v.size();
+    if (!tiles) return VAE_OK;
+    if (capacity < (int32_t)v.size())
+        return fail(VAE_ERR_INVALID_ARG, "capacity smaller than the tile count", -1, capacity, -1,
+                    (int64_t)v.size());
+    std::memcpy(tiles, v.data(), v.size() * sizeof(vae_tile_t));
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile_t* tile,
+                                    const vae_tiling_desc_t* desc, vae_tensor_t* out,
+                                    int32_t flags, vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_tensor(tile_out, "tile_out"));
+    VAE_TRY(check_tensor(out, "out"));
+    VAE_TRY(check_tiling(desc));
+    if (!tile) return fail(VAE_ERR_INVALID_ARG, "tile is NULL");
+    if (desc->mode != VAE_TILING_OVERLAP_BLEND)
+        return fail(VAE_ERR_INVALID_ARG, "merge takes an overlap-blend tiling");
+    if (tile_out->dtype != VAE_DTYPE_F32 || out->dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_UNSUPPORTED, "merge accumulates fp32 tensors");
+    if (out->n != desc->n || out->t != out_frames(desc->t, desc->scale_t) ||
+        out->h != (int64_t)desc->h * desc->scale_h || out->w != (int64_t)desc->w * desc->scale_w)
+        return fail(VAE_ERR_INVALID_ARG, "out shape does not match the tiling");
+    const vae_box_t& ob = tile->out;
+    VAE_TRY(check_box(&ob, *out, "tile->out"));
+    if (tile_out->n != out->n || tile_out->c != out->c || tile_out->t != ob.t1 - ob.t0 ||
+        tile_out->h != ob.h1 - ob.h0 || tile_out->w != ob.w1 - ob.w0)
+        return fail(VAE_ERR_INVALID_ARG, "tile_out shape must be the tile's output box");
+    if (overlaps(*tile_out, *out)) return fail(VAE_ERR_INVALID_ARG, "tile_out overlaps out");
+    if (flags & ~(VAE_MERGE_ZERO | VAE_MERGE_FINALIZE))
+        return fail(VAE_ERR_INVALID_ARG, "unknown merge flags");
+    hipStream_t s = as_stream(stream);
+    if (flags & VAE_MERGE_ZERO) VAE_TRY(launch_zero(out->data, numel(*out) * 4, s));
+    VAE_TRY(launch_merge(*tile_out, to_box(&ob, *out), tile->lead_h, tile->trail_h, tile->lead_w,
+                         tile->trail_w, *out, s));
+    if (flags & VAE_MERGE_FINALIZE) {
+        const AxisTiling ah{desc->h, desc->tile_h, desc->stride_h, desc->scale_h};
+        const AxisTiling aw{desc->w, desc->tile_w, desc->stride_w, desc->scale_w};
+        VAE_TRY(launch_merge_finalize(*out, ah, aw, s));
+    }
+    return VAE_OK;
+}
+
+}  // extern "C"

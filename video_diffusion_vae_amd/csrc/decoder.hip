@@ -1,0 +1,546 @@
+// Decode executor: a layer plan over caller-owned device weights and workspace.
+//
+// Mode A (patch-halo). On one GPU all patches share one activation tensor per layer:
+//  - a conv launch covers every patch box at once, and each patch's halo is simply its
+//    neighbour's data in that tensor;
+//  - GroupNorm statistics are still formed per patch box and merged across patches with Chan's
+//    update ("Add tiled VAE parallelism & extended model support", PatchGroupNorm commit message);
+//  - the final unpatchify places every patch's pixels disjointly, straight into `out`.
+// Mode B (overlap-blend). The serial tiled decode of "[TRTLLM-14029][feat] LTX-2 tile-parallel VAE
+// decode" (Description): one tile in flight. Each tile's latent box is cropped, decoded with its own
+// borders and statistics, and blended into `out`, which is normalised after the last tile.
+// Host work per call is integer geometry only; no host-built masks, no host-to-device copies.
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "host.h"
+
+struct vae_decoder {
+    int32_t dtype = 0, latent_c = 0, groups = 0;
+    float eps = 0.0f;
+    std::vector<vae_layer_desc_t> layers;
+    std::vector<const void*> ptrs;
+    bool timing = false;
+    struct Rec {
+        int32_t kind, layer, tile;
+        double flops, bytes;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> events;
+};
+
+namespace vae {
+namespace {
+
+struct Shape {
+    int64_t n, t, h, w, c;
+    int32_t dtype;
+    int64_t bytes() const { return n * t * h * w * c * elem_size(dtype); }
+};
+
+// Number of device pointers each op consumes.
+int ptrs_for(const vae_layer_desc_t& l) {
+    switch (l.op) {
+        case VAE_OP_CONV: return 2;
+        case VAE_OP_RES: return 8;
+        case VAE_OP_GN_SILU: return 2;
+        default: return 0;
+    }
+}
+
+// Shape after each op, starting from the latent extents.
+vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, int* total_st,
+                  int* total_sh, int* total_sw) {
+    Shape s = in;
+    int st = 1, sh = 1, sw = 1;
+    if (shapes) shapes->clear();
+    for (size_t i = 0; i < d.layers.size(); ++i) {
+        const vae_layer_desc_t& l = d.layers[i];
+        switch (l.op) {
+            case VAE_OP_CONV:
+                s.c = l.cout;
+                if (l.f32_out) s.dtype = VAE_DTYPE_F32;
+                break;
+            case VAE_OP_D2S:
+                s.t = l.st * s.t - (l.st - 1);
+                s.h *= l.sh;
+                s.w *= l.sw;
+                s.c /= (int64_t)l.st * l.sh * l.sw;
+                st *= l.st;
+                sh *= l.sh;
+                sw *= l.sw;
+                break;
+            case VAE_OP_NEAREST:
+                s.h *= l.sh;
+                s.w *= l.sw;
+                sh *= l.sh;
+                sw *= l.sw;
+                break;
+            default:
+                break;
+        }
+        if (shapes) shapes->push_back(s);
+    }
+    if (total_st) *total_st = st;
+    if (total_sh) *total_sh = sh;
+    if (total_sw) *total_sw = sw;
+    return VAE_OK;
+}
+
+vae_tensor_t tensor_of(void* p, const Shape& s) {
+    vae_tensor_t t{};
+    t.data = p;
+    t.dtype = s.dtype;
+    t.n = s.n;
+    t.t = s.t;
+    t.h = s.h;
+    t.w = s.w;
+    t.c = s.c;
+    return t;
+}
+
+Shape shape_of(const vae_tensor_t& t) { return Shape{t.n, t.t, t.h, t.w, t.c, t.dtype}; }
+
+// Latent-grid patch boxes scaled to an activation with cumulative spatial scale (ch, cw).
+BoxList scaled_boxes(const std::vector<Box>& latent_boxes, int64_t t, int ch, int cw) {
+    BoxList bl;
+    bl.n = (int32_t)latent_boxes.size();
+    for (size_t i = 0; i < latent_boxes.size(); ++i) {
+        const Box& b = latent_boxes[i];
+        bl.b[i] = Box{0, (int32_t)t, b.h0 * ch, b.h1 * ch, b.w0 * cw, b.w1 * cw};
+    }
+    return bl;
+}
+
+struct Req {
+    int64_t act = 0;      // bytes of the largest activation kept in a rotating buffer
+    int64_t gn = 0;       // GroupNorm stats workspace
+    int64_t mr = 0;       // mean/rstd
+    int64_t crop = 0;     // latent crop (mode B)
+    int64_t tile = 0;     // one decoded tile, fp32 pixels (mode B)
+};
+
+// Requirements of one run of the plan on an input of shape `in` with patch boxes `boxes`.
+void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>& boxes,
+                  bool final_in_buffer, Req* r) {
+    std::vector<Shape> shapes;
+    walk(d, in, &shapes, nullptr, nullptr, nullptr);
+    Shape cur = in;
+    int ch = 1, cw = 1;
+    for (size_t i = 0; i < d.layers.size(); ++i) {
+        const vae_layer_desc_t& l = d.layers[i];
+        const Shape& s = shapes[i];
+        const bool last = i + 1 == d.layers.size();
+        if (!last) r->act = std::max(r->act, s.bytes());
+        if (last && final_in_buffer) r->tile = std::max(r->tile, s.bytes());
+        if (l.op == VAE_OP_RES || l.op == VAE_OP_GN_SILU) {
+            r->act = std::max(r->act, cur.bytes());
+            vae_tensor_t x = tensor_of(nullptr, cur);
+            r->gn = std::max<int64_t>(
+                r->gn, (int64_t)gn_stats_workspace(x, scaled_boxes(boxes, cur.t, ch, cw), d.groups));
+            r->mr = std::max<int64_t>(r->mr, cur.n * d.groups * 2 * (int64_t)sizeof(float));
+        }
+        if (l.op == VAE_OP_D2S || l.op == VAE_OP_NEAREST) {
+            ch *= l.sh;
+            cw *= l.sw;
+        }
+        cur = s;
+    }
+}
+
+struct Layout {
+    size_t buf[3], gn, mr, crop, tile, total;
+    int64_t act_bytes;
+};
+
+Layout layout_of(const Req& r) {
+    Layout L{};
+    size_t off = 0;
+    const size_t act = align_up((size_t)r.act, 256);
+    for (int i = 0; i < 3; ++i) {
+        L.buf[i] = off;
+        off += act;
+    }
+    L.gn = off;
+    off += align_up((size_t)r.gn, 256);
+    L.mr = off;
+    off += align_up((size_t)r.mr, 256);
+    L.crop = off;
+    off += align_up((size_t)r.crop, 256);
+    L.tile = off;
+    off += align_up((size_t)r.tile, 256);
+    L.total = off;
+    L.act_bytes = (int64_t)act;
+    return L;
+}
+
+struct Runner {
+    vae_decoder* d;
+    hipStream_t s;
+    uint8_t* ws;
+    Layout L;
+    int32_t tile;
+    size_t ev;  // next event index
+
+    vae_status_t mark(int32_t kind, int32_t layer, double flops, double bytes) {
+        if (!d->timing) return VAE_OK;
+        if (ev >= d->events.size()) {
+            hipEvent_t e;
+            VAE_HIP_CHECK(hipEventCreate(&e));
+            d->events.push_back(e);
+        }
+        VAE_HIP_CHECK(hipEventRecord(d->events[ev], s));
+        if (ev > 0) d->recs.push_back({kind, layer, tile, flops, bytes});
+        ++ev;
+        return VAE_OK;
+    }
+
+    vae_status_t gn(const vae_tensor_t& x, const vae_tensor_t& y, const BoxList& bl,
+                    const void* gamma, const void* beta, int layer) {
+        double* stats = reinterpret_cast<double*>(ws + L.gn);
+        float* mr = reinterpret_cast<float*>(ws + L.mr);
+        VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
+        // the patch boxes partition the tensor, so one apply launch covers them all
+        VAE_TRY(launch_gn_apply(x, whole_box(x), d->groups, mr, static_cast<const float*>(gamma),
+                                static_cast<const float*>(beta), true, y, s));
+        const double b = (double)numel(x) * elem_size(x.dtype);
+        return mark(VAE_KIND_GN, layer, 0.0, 3.0 * b);
+    }
+
+    vae_status_t conv(const vae_tensor_t& x, const void* w, const void* b,
+                      const vae_tensor_t* res, const vae_tensor_t& y, int layer) {
+        VAE_TRY(launch_conv3d(x, w, static_cast<const float*>(b), res, y, whole_box(y), s));
+        const double flops = 2.0 * 27.0 * (double)x.c * (double)y.c * (double)positions(y);
+        const double bytes = (double)numel(x) * elem_size(x.dtype) +
+                             (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
+        return mark(VAE_KIND_CONV, layer, flops, bytes);
+    }
+
+    // Run the whole plan on `in`; the last op writes `final_out`.
+    vae_status_t run(const vae_tensor_t& in, const std::vector<Box>& boxes,
+                     const vae_tensor_t& final_out) {
+        std::vector<Shape> shapes;
+        walk(*d, shape_of(in), &shapes, nullptr, nullptr, nullptr);
+        vae_tensor_t cur = in;
+        int cur_buf = -1;  // -1: the caller's input, never written
+        int ch = 1, cw = 1;
+        size_t p = 0;
+        auto buf = [&](int i, const Shape& sh) { return tensor_of(ws + L.buf[i], sh); };
+        auto free_buf = [&](int avoid1, int avoid2) {
+            for (int i = 0; i < 3; ++i)
+                if (i != avoid1 && i != avoid2) return i;
+            return -1;
+        };
+        for (size_t li = 0; li < d->layers.size(); ++li) {
+            const vae_layer_desc_t& l = d->layers[li];
+            const bool last = li + 1 == d->layers.size();
+            const Shape& os = shapes[li];
+            const int layer = (int)li;
+            if (l.op == VAE_OP_CONV) {
+                const int nb = free_buf(cur_buf, -1);
+                vae_tensor_t y = last ? final_out : buf(nb, os);
+                VAE_TRY(conv(cur, d->ptrs[p], d->ptrs[p + 1], nullptr, y, layer));
+                p += 2;
+                cur = y;
+                cur_buf = last ? -2 : nb;
+            } else if (l.op == VAE_OP_RES) {
+                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
+                const int b1 = free_buf(cur_buf, -1);
+                const int b2 = free_buf(cur_buf, b1);
+                const Shape cs = shape_of(cur);
+                vae_tensor_t t1 = buf(b1, cs), t2 = buf(b2, cs);
+                VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
+                VAE_TRY(conv(t1, d->ptrs[p + 2], d->ptrs[p + 3], nullptr, t2, layer));
+                VAE_TRY(gn(t2, t2, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
+                vae_tensor_t y = last ? final_out : t1;
+                VAE_TRY(conv(t2, d->ptrs[p + 6], d->ptrs[p + 7], &cur, y, layer));
+                p += 8;
+                cur = y;
+                cur_buf = last ? -2 : b1;
+            } else if (l.op == VAE_OP_GN_SILU) {
+                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
+                vae_tensor_t y;
+                int nb = cur_buf;
+                if (last) {
+                    y = final_out;
+                    nb = -2;
+                } else if (cur_buf < 0) {
+                    nb = free_buf(cur_buf, -1);
+                    y = buf(nb, shape_of(cur));
+                } else {
+                    y = cur;  // in place
+                }
+                VAE_TRY(gn(cur, y, bl, d->ptrs[p], d->ptrs[p + 1], layer));
+                p += 2;
+                cur = y;
+                cur_buf = nb;
+            } else {  // D2S / NEAREST
+                const int nb = free_buf(cur_buf, -1);
+                vae_tensor_t y = last ? final_out : buf(nb, os);
+                const int mode = l.op == VAE_OP_D2S ? VAE_UPSAMPLE_D2S : VAE_UPSAMPLE_NEAREST;
+                const int st = l.op == VAE_OP_D2S ? l.st : 1;
+                VAE_TRY(launch_upsample(cur, whole_box(cur), mode, st, l.sh, l.sw, y, s));
+                VAE_TRY(mark(VAE_KIND_UPSAMPLE, layer, 0.0,
+                             (double)numel(cur) * elem_size(cur.dtype) +
+                                 (double)numel(y) * elem_size(y.dtype)));
+                ch *= l.sh;
+                cw *= l.sw;
+                cur = y;
+                cur_buf = last ? -2 : nb;
+            }
+        }
+        return VAE_OK;
+    }
+};
+
+vae_status_t plan_output(const vae_decoder& d, const vae_tiling_desc_t& desc, Shape* out,
+                         int* st, int* sh, int* sw) {
+    Shape in{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype};
+    std::vector<Shape> shapes;
+    walk(d, in, &shapes, st, sh, sw);
+    *out = shapes.back();
+    return VAE_OK;
+}
+
+vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layout* L,
+                      std::vector<vae_tile_t>* tiles) {
+    VAE_TRY(check_tiling(&desc));
+    int st, sh, sw;
+    Shape out;
+    plan_output(d, desc, &out, &st, &sh, &sw);
+    if (st != desc.scale_t || sh != desc.scale_h || sw != desc.scale_w)
+        return fail(VAE_ERR_INVALID_ARG, "tiling scales do not match the decoder plan");
+    if (desc.mode == VAE_TILING_PATCH_HALO && (int64_t)desc.patches_h * desc.patches_w > kMaxBoxes)
+        return fail(VAE_ERR_UNSUPPORTED, "the decoder takes at most 16 patches", -1,
+                    (int64_t)desc.patches_h * desc.patches_w, -1, 1);
+    *tiles = make_tiles(desc);
+    Req r;
+    if (desc.mode == VAE_TILING_PATCH_HALO) {
+        std::vector<Box> boxes;
+        for (const vae_tile_t& t : *tiles)
+            boxes.push_back(Box{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
+                                t.latent.w1});
+        requirements(d, Shape{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype}, boxes, false,
+                     &r);
+    } else {
+        for (const vae_tile_t& t : *tiles) {
+            Shape in{desc.n, t.latent.t1 - t.latent.t0, t.latent.h1 - t.latent.h0,
+                     t.latent.w1 - t.latent.w0, d.latent_c, d.dtype};
+            std::vector<Box> one{Box{0, (int32_t)in.t, 0, (int32_t)in.h, 0, (int32_t)in.w}};
+            requirements(d, in, one, true, &r);
+            r.crop = std::max(r.crop, in.bytes());
+        }
+    }
+    *L = layout_of(r);
+    return VAE_OK;
+}
+
+}  // namespace
+}  // namespace vae
+
+using namespace vae;
+
+extern "C" {
+
+VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
+                                        const void* const* params, int32_t n_ptrs,
+                                        vae_decoder_t** out) {
+    clear_error();
+    if (!spec || !out) return fail(VAE_ERR_INVALID_ARG, "spec or out is NULL");
+    *out = nullptr;
+    if (spec->dtype != VAE_DTYPE_BF16 && spec->dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_INVALID_ARG, "unknown plan dtype");
+    if (spec->latent_channels < 1 || spec->groups < 1 || !(spec->eps >= 0.0f))
+        return fail(VAE_ERR_INVALID_ARG, "latent_channels and groups must be >= 1, eps >= 0");
+    if (spec->n_layers < 1 || !spec->layers) return fail(VAE_ERR_INVALID_ARG, "empty layer plan");
+    int64_t c = spec->latent_channels;
+    int32_t act = spec->dtype;
+    int need = 0;
+    for (int i = 0; i < spec->n_layers; ++i) {
+        const vae_layer_desc_t& l = spec->layers[i];
+        switch (l.op) {
+            case VAE_OP_CONV:
+                if (l.cin != c || l.cout < 1)
+                    return fail(VAE_ERR_INVALID_ARG, "conv channels do not chain", 4, l.cin, -1, c);
+                if (act != spec->dtype)
+                    return fail(VAE_ERR_UNSUPPORTED, "no conv after an fp32-output conv");
+                c = l.cout;
+                if (l.f32_out) act = VAE_DTYPE_F32;
+                break;
+            case VAE_OP_RES:
+                if (l.cin != c) return fail(VAE_ERR_INVALID_ARG, "res width does not chain");
+                if (act != spec->dtype)
+                    return fail(VAE_ERR_UNSUPPORTED, "no res block after an fp32-output conv");
+                if (c % spec->groups)
+                    return fail(VAE_ERR_UNSUPPORTED, "width not divisible by groups", 4, c,
+                                spec->groups);
+                break;
+            case VAE_OP_GN_SILU:
+                if (c % spec->groups)
+                    return fail(VAE_ERR_UNSUPPORTED, "width not divisible by groups", 4, c,
+                                spec->groups);
+                break;
+            case VAE_OP_D2S: {
+                if (l.st < 1 || l.sh < 1 || l.sw < 1)
+                    return fail(VAE_ERR_INVALID_ARG, "d2s factors must be >= 1");
+                const int64_t k = (int64_t)l.st * l.sh * l.sw;
+                if (c % k) return fail(VAE_ERR_INVALID_ARG, "d2s: channels not divisible", 4, c, k);
+                c /= k;
+                break;
+            }
+            case VAE_OP_NEAREST:
+                if (l.sh < 1 || l.sw < 1)
+                    return fail(VAE_ERR_INVALID_ARG, "nearest factors must be >= 1");
+                break;
+            default:
+                return fail(VAE_ERR_INVALID_ARG, "unknown op in layer plan");
+        }
+        need += ptrs_for(l);
+    }
+    if (act != VAE_DTYPE_F32)
+        return fail(VAE_ERR_UNSUPPORTED, "the plan must end in fp32 (use f32_out on the last conv)");
+    if (n_ptrs != need || (need > 0 && !params))
+        return fail(VAE_ERR_INVALID_ARG, "parameter pointer count does not match the plan", -1,
+                    n_ptrs, -1, need);
+    int p = 0;
+    for (int i = 0; i < spec->n_layers; ++i) {
+        const vae_layer_desc_t& l = spec->layers[i];
+        if (l.op == VAE_OP_CONV && !params[p])
+            return fail(VAE_ERR_INVALID_ARG, "conv weight pointer is NULL");
+        if (l.op == VAE_OP_RES && (!params[p + 2] || !params[p + 6]))
+            return fail(VAE_ERR_INVALID_ARG, "res conv weight pointer is NULL");
+        p += ptrs_for(l);
+    }
+    vae_decoder* d = new (std::nothrow) vae_decoder();
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "out of host memory");
+    d->dtype = spec->dtype;
+    d->latent_c = spec->latent_channels;
+    d->groups = spec->groups;
+    d->eps = spec->eps;
+    d->layers.assign(spec->layers, spec->layers + spec->n_layers);
+    d->ptrs.assign(params, params + need);
+    *out = d;
+    return VAE_OK;
+}
+
+VAE_API void vae_decoder_destroy(vae_decoder_t* dec) {
+    if (!dec) return;
+    for (hipEvent_t e : dec->events) (void)hipEventDestroy(e);
+    delete dec;
+}
+
+VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,
+                                               const vae_tiling_desc_t* desc, size_t* bytes) {
+    clear_error();
+    if (!dec || !desc || !bytes) return fail(VAE_ERR_INVALID_ARG, "NULL argument");
+    Layout L;
+    std::vector<vae_tile_t> tiles;
+    VAE_TRY(size_for(*dec, *desc, &L, &tiles));
+    *bytes = L.total;
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tensor_t* latent,
+                                      const vae_tiling_desc_t* desc, vae_tensor_t* out, void* ws,
+                                      size_t ws_bytes, vae_stream_t stream) {
+    clear_error();
+    vae_decoder* dec = const_cast<vae_decoder*>(dec_c);
+    if (!dec || !desc) return fail(VAE_ERR_INVALID_ARG, "NULL decoder or tiling");
+    VAE_TRY(check_tensor(latent, "latent"));
+    VAE_TRY(check_tensor(out, "out"));
+    if (latent->dtype != dec->dtype || latent->c != dec->latent_c)
+        return fail(VAE_ERR_INVALID_ARG, "latent dtype/channels do not match the plan");
+    if (latent->n != desc->n || latent->t != desc->t || latent->h != desc->h ||
+        latent->w != desc->w)
+        return fail(VAE_ERR_INVALID_ARG, "latent extents do not match the tiling desc");
+    Layout L;
+    std::vector<vae_tile_t> tiles;
+    VAE_TRY(size_for(*dec, *desc, &L, &tiles));
+    Shape os;
+    int st, sh, sw;
+    plan_output(*dec, *desc, &os, &st, &sh, &sw);
+    if (out->dtype != VAE_DTYPE_F32 || out->n != os.n || out->t != os.t || out->h != os.h ||
+        out->w != os.w || out->c != os.c)
+        return fail(VAE_ERR_INVALID_ARG, "out must be fp32 of the decoded shape");
+    if (!ws || ws_bytes < L.total)
+        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
+                    (int64_t)L.total);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (overlaps(*latent, *out)) return fail(VAE_ERR_INVALID_ARG, "out overlaps latent");
+    {
+        const uint8_t* w0 = static_cast<const uint8_t*>(ws);
+        vae_tensor_t wt{const_cast<uint8_t*>(w0), VAE_DTYPE_F32, 0, 1, 1, 1, 1,
+                        (int64_t)(L.total / 4)};
+        if (overlaps(wt, *latent) || overlaps(wt, *out))
+            return fail(VAE_ERR_INVALID_ARG, "workspace overlaps latent or out");
+    }
+
+    dec->recs.clear();
+    Runner r{dec, as_stream(stream), static_cast<uint8_t*>(ws), L, -1, 0};
+    VAE_TRY(r.mark(VAE_KIND_OTHER, -1, 0, 0));
+    if (desc->mode == VAE_TILING_PATCH_HALO) {
+        std::vector<Box> boxes;
+        for (const vae_tile_t& t : tiles)
+            boxes.push_back(Box{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
+                                t.latent.w1});
+        VAE_TRY(r.run(*latent, boxes, *out));
+    } else {
+        const AxisTiling ah{desc->h, desc->tile_h, desc->stride_h, desc->scale_h};
+        const AxisTiling aw{desc->w, desc->tile_w, desc->stride_w, desc->scale_w};
+        for (size_t i = 0; i < tiles.size(); ++i) {
+            const vae_tile_t& t = tiles[i];
+            r.tile = (int32_t)i;
+            const Box lb{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
+                         t.latent.w1};
+            Shape cs{latent->n, lb.bt(), lb.bh(), lb.bw(), latent->c, latent->dtype};
+            vae_tensor_t crop = tensor_of(r.ws + L.crop, cs);
+            VAE_TRY(launch_crop(*latent, lb, crop, r.s));
+            VAE_TRY(r.mark(VAE_KIND_OTHER, -1, 0, 2.0 * (double)cs.bytes()));
+            std::vector<Box> one{Box{0, (int32_t)cs.t, 0, (int32_t)cs.h, 0, (int32_t)cs.w}};
+            Shape ts{os.n, t.out.t1 - t.out.t0, t.out.h1 - t.out.h0, t.out.w1 - t.out.w0, os.c,
+                     VAE_DTYPE_F32};
+            vae_tensor_t tile_out = tensor_of(r.ws + L.tile, ts);
+            VAE_TRY(r.run(crop, one, tile_out));
+            const Box ob{t.out.t0, t.out.t1, t.out.h0, t.out.h1, t.out.w0, t.out.w1};
+            if (i == 0) VAE_TRY(launch_zero(out->data, numel(*out) * 4, r.s));
+            VAE_TRY(launch_merge(tile_out, ob, t.lead_h, t.trail_h, t.lead_w, t.trail_w, *out, r.s));
+            double mb = 3.0 * (double)ts.bytes() + (i == 0 ? (double)numel(*out) * 4 : 0.0);
+            if (i + 1 == tiles.size()) {
+                VAE_TRY(launch_merge_finalize(*out, ah, aw, r.s));
+                mb += 2.0 * (double)numel(*out) * 4;
+            }
+            VAE_TRY(r.mark(VAE_KIND_MERGE, -1, 0, mb));
+        }
+    }
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decoder_set_timing(vae_decoder_t* dec, int32_t enable) {
+    clear_error();
+    if (!dec) return fail(VAE_ERR_INVALID_ARG, "decoder is NULL");
+    dec->timing = enable != 0;
+    dec->recs.clear();
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decoder_get_timing(vae_decoder_t* dec, vae_op_timing_t* out,
+                                            int32_t capacity, int32_t* n) {
+    clear_error();
+    if (!dec || !n) return fail(VAE_ERR_INVALID_ARG, "NULL argument");
+    *n = (int32_t)dec->recs.size();
+    if (!out || dec->recs.empty()) return VAE_OK;
+    if (capacity < *n) return fail(VAE_ERR_INVALID_ARG, "capacity too small", -1, capacity, -1, *n);
+    VAE_HIP_CHECK(hipEventSynchronize(dec->events[dec->recs.size()]));
+    for (size_t i = 0; i < dec->recs.size(); ++i) {
+        float ms = 0.0f;
+        VAE_HIP_CHECK(hipEventElapsedTime(&ms, dec->events[i], dec->events[i + 1]));
+        const auto& r = dec->recs[i];
+        out[i] = vae_op_timing_t{r.kind, r.layer, r.tile, 0, (double)ms, r.flops, r.bytes};
+    }
+    return VAE_OK;
+}
+
+}  // extern "C"

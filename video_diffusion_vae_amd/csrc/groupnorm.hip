@@ -1,0 +1,351 @@
+// GroupNorm (+SiLU) whose statistics are merged across patches.
+//
+// The statistics must be those of the whole tensor: the global mean, and the variance about it
+// divided by the count. Per-patch means and Bessel's correction are both wrong ("Add tiled VAE
+// parallelism & extended model support", PatchGroupNorm commit message). Three steps:
+//  1. gn_stats_kernel. Each block streams a range of rows of one patch box. A "row" is the
+//     positions of the box at fixed (n, t, h), which are contiguous in NDHWC. Every thread keeps a
+//     Welford (count, mean, M2) per channel for a fixed 16-byte channel vector. The block merges
+//     its threads into per-group partials (fp64) and writes them to its own slot: no atomics.
+//  2. gn_finalize_kernel. One block per (group, sample). It merges the block partials of each box
+//     with Chan's pairwise update in a fixed order, then merges the boxes in box order. It writes
+//     per-box (count, mean, M2) and (mean, rstd).
+//  3. gn_apply_kernel. Streams rows again: y = act((x - mean) * rstd * gamma + beta).
+// Every reduction has a fixed order, so results are bitwise reproducible.
+#include "kernels.h"
+
+namespace vae {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kElemsPerBlock = 1 << 17;   // target elements one stats block streams
+constexpr int kMaxStatsBlocks = 4096;
+
+struct GnBoxes {
+    Box b[kMaxBoxes];
+    int32_t start[kMaxBoxes + 1];  // first block of each box; start[n] = total blocks
+    int32_t n;
+};
+
+struct Moments {
+    double n, mean, m2;
+};
+
+__device__ __forceinline__ void chan_merge(Moments& a, double nb, double mb, double m2b) {
+    if (nb <= 0.0) return;
+    if (a.n <= 0.0) {
+        a.n = nb;
+        a.mean = mb;
+        a.m2 = m2b;
+        return;
+    }
+    double n = a.n + nb;
+    double d = mb - a.mean;
+    a.mean += d * (nb / n);
+    a.m2 += m2b + d * d * (a.n * nb / n);
+    a.n = n;
+}
+
+// Number of stats blocks per box for a given tensor.
+int32_t blocks_for_box(const Box& b, int64_t c, int32_t n_boxes) {
+    int64_t rows = b.bt() * b.bh();
+    int64_t elems = b.volume() * c;
+    int64_t nb = ceil_div(elems, kElemsPerBlock);
+    int64_t cap = kMaxStatsBlocks / n_boxes;
+    if (nb > cap) nb = cap;
+    if (nb > rows) nb = rows;
+    if (nb < 1) nb = 1;
+    return (int32_t)nb;
+}
+
+GnBoxes make_boxes(const vae_tensor_t& x, const BoxList& bl) {
+    GnBoxes g{};
+    g.n = bl.n;
+    int32_t s = 0;
+    for (int i = 0; i < bl.n; ++i) {
+        g.b[i] = bl.b[i];
+        g.start[i] = s;
+        s += blocks_for_box(bl.b[i], x.c, bl.n);
+    }
+    g.start[bl.n] = s;
+    return g;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gn_stats_kernel(const T* __restrict__ x, int32_t Tn,
+                                                            int32_t H, int32_t W, int32_t C,
+                                                            int32_t groups, GnBoxes boxes,
+                                                            double* __restrict__ ws) {
+    constexpr int V = Elem<T>::kVec;
+    const int n = blockIdx.y;
+    const int N = gridDim.y;
+    const int blk = blockIdx.x;
+    int bi = 0;
+    while (bi + 1 < boxes.n && blk >= boxes.start[bi + 1]) ++bi;
+    const Box b = boxes.b[bi];
+    const int nb = boxes.start[bi + 1] - boxes.start[bi];
+    const int local = blk - boxes.start[bi];
+    const int64_t rows = b.bt() * b.bh();
+    const int64_t r0 = rows * local / nb, r1 = rows * (local + 1) / nb;
+
+    const int CV = C / V;                 // 16-byte vectors per position (divides 256)
+    const int tid = threadIdx.x;
+    const int seg = (int)b.bw() * CV;     // vectors per row
+    float cnt = 0.0f;
+    float mean[V], m2[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) mean[k] = m2[k] = 0.0f;
+
+    for (int64_t r = r0; r < r1; ++r) {
+        const int t = b.t0 + (int)(r / b.bh());
+        const int h = b.h0 + (int)(r % b.bh());
+        const T* row = x + ((((int64_t)n * Tn + t) * H + h) * W + b.w0) * C;
+        for (int e = tid; e < seg; e += kThreads) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(row + (int64_t)e * V);
+            const T* v = reinterpret_cast<const T*>(&raw);
+            cnt += 1.0f;
+            const float inv = 1.0f / cnt;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xv = Elem<T>::load(v + k);
+                const float d = xv - mean[k];
+                mean[k] += d * inv;
+                m2[k] += d * (xv - mean[k]);
+            }
+        }
+    }
+
+    // Per-thread group partials. Thread tid always sees channels [(tid % CV) * V, +V).
+    const int cpg = C / groups;
+    __shared__ float sp[kThreads][V][3];
+    if (cpg <= V) {
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+            if (q * cpg >= V) break;
+            float gm = 0.0f;
+            for (int k = 0; k < cpg; ++k) gm += mean[q * cpg + k];
+            gm /= (float)cpg;
+            float gm2 = 0.0f;
+            for (int k = 0; k < cpg; ++k) {
+                const float d = mean[q * cpg + k] - gm;
+                gm2 += m2[q * cpg + k] + cnt * d * d;
+            }
+            sp[tid][q][0] = cnt * cpg;
+            sp[tid][q][1] = gm;
+            sp[tid][q][2] = gm2;
+        }
+    } else {
+        float gm = 0.0f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) gm += mean[k];
+        gm /= (float)V;
+        float gm2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const float d = mean[k] - gm;
+            gm2 += m2[k] + cnt * d * d;
+        }
+        sp[tid][0][0] = cnt * V;
+        sp[tid][0][1] = gm;
+        sp[tid][0][2] = gm2;
+    }
+    __syncthreads();
+
+    for (int g = tid; g < groups; g += kThreads) {
+        Moments m{0.0, 0.0, 0.0};
+        int v0, v1, slot;
+        if (cpg <= V) {
+            v0 = (g * cpg) / V;
+            v1 = v0 + 1;
+            slot = (g * cpg - v0 * V) / cpg;
+        } else {
+            v0 = (g * cpg) / V;
+            v1 = ((g + 1) * cpg) / V;
+            slot = 0;
+        }
+        for (int t2 = 0; t2 < kThreads; ++t2) {
+            const int v = t2 % CV;
+            if (v < v0 || v >= v1) continue;
+            chan_merge(m, sp[t2][slot][0], sp[t2][slot][1], sp[t2][slot][2]);
+        }
+        double* o = ws + (((int64_t)blk * N + n) * groups + g) * 3;
+        o[0] = m.n;
+        o[1] = m.mean;
+        o[2] = m.m2;
+    }
+}
+
+// Merge (count, mean, M2) triples `src[i * stride]`, i in [lo, hi), over 256 threads in a fixed
+// order; thread 0 returns the result.
+__device__ Moments block_merge(const double* src, int64_t stride, int lo, int hi) {
+    __shared__ double red[kThreads][3];
+    Moments m{0.0, 0.0, 0.0};
+    for (int i = lo + threadIdx.x; i < hi; i += kThreads) {
+        const double* p = src + (int64_t)i * stride;
+        chan_merge(m, p[0], p[1], p[2]);
+    }
+    red[threadIdx.x][0] = m.n;
+    red[threadIdx.x][1] = m.mean;
+    red[threadIdx.x][2] = m.m2;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) {
+            Moments a{red[threadIdx.x][0], red[threadIdx.x][1], red[threadIdx.x][2]};
+            chan_merge(a, red[threadIdx.x + s][0], red[threadIdx.x + s][1],
+                       red[threadIdx.x + s][2]);
+            red[threadIdx.x][0] = a.n;
+            red[threadIdx.x][1] = a.mean;
+            red[threadIdx.x][2] = a.m2;
+        }
+        __syncthreads();
+    }
+    Moments r{red[0][0], red[0][1], red[0][2]};
+    __syncthreads();
+    return r;
+}
+
+// grid (groups, N). ws: [blocks][N][G][3]; part_out: [n_boxes][N][G][3].
+__global__ __launch_bounds__(kThreads) void gn_finalize_kernel(const double* __restrict__ ws,
+                                                               GnBoxes boxes, int32_t groups,
+                                                               float eps, double* part_out,
+                                                               float* mean_rstd) {
+    const int g = blockIdx.x, n = blockIdx.y, N = gridDim.y;
+    const int64_t stride = (int64_t)N * groups * 3;
+    const double* base = ws + ((int64_t)n * groups + g) * 3;
+    Moments total{0.0, 0.0, 0.0};
+    for (int bi = 0; bi < boxes.n; ++bi) {
+        Moments m = block_merge(base, stride, boxes.start[bi], boxes.start[bi + 1]);
+        if (threadIdx.x == 0) {
+            if (part_out) {
+                double* o = part_out + (((int64_t)bi * N + n) * groups + g) * 3;
+                o[0] = m.n;
+                o[1] = m.mean;
+                o[2] = m.m2;
+            }
+            chan_merge(total, m.n, m.mean, m.m2);
+        }
+    }
+    if (threadIdx.x == 0 && mean_rstd) {
+        const double var = total.n > 0.0 ? total.m2 / total.n : 0.0;
+        mean_rstd[((int64_t)n * groups + g) * 2] = (float)total.mean;
+        mean_rstd[((int64_t)n * groups + g) * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+    }
+}
+
+// grid (groups, N). part: [n_parts][N][G][3].
+__global__ __launch_bounds__(kThreads) void gn_combine_kernel(const double* __restrict__ part,
+                                                              int32_t n_parts, int32_t groups,
+                                                              float eps, float* mean_rstd) {
+    const int g = blockIdx.x, n = blockIdx.y, N = gridDim.y;
+    Moments m{0.0, 0.0, 0.0};
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < n_parts; ++i) {
+            const double* p = part + (((int64_t)i * N + n) * groups + g) * 3;
+            chan_merge(m, p[0], p[1], p[2]);
+        }
+        const double var = m.n > 0.0 ? m.m2 / m.n : 0.0;
+        mean_rstd[((int64_t)n * groups + g) * 2] = (float)m.mean;
+        mean_rstd[((int64_t)n * groups + g) * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+    }
+}
+
+// grid (rows of the box, N): one block per contiguous row segment.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gn_apply_kernel(
+    const T* x, T* y, int32_t Tn, int32_t H, int32_t W, int32_t C, int32_t groups, Box b,
+    const float* __restrict__ mean_rstd, const float* __restrict__ gamma,
+    const float* __restrict__ beta, int32_t silu) {
+    constexpr int V = Elem<T>::kVec;
+    const int n = blockIdx.y;
+    const int64_t r = blockIdx.x;
+    const int t = b.t0 + (int)(r / b.bh());
+    const int h = b.h0 + (int)(r % b.bh());
+    const int64_t off = ((((int64_t)n * Tn + t) * H + h) * W + b.w0) * C;
+    const T* xr = x + off;
+    T* yr = y + off;
+    const int CV = C / V;
+    const int seg = (int)b.bw() * CV;
+    const int cpg = C / groups;
+    const float* mr = mean_rstd + (int64_t)n * groups * 2;
+    for (int e = threadIdx.x; e < seg; e += kThreads) {
+        const int c0 = (e % CV) * V;
+        uint4 raw = *reinterpret_cast<const uint4*>(xr + (int64_t)e * V);
+        T* v = reinterpret_cast<T*>(&raw);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const int c = c0 + k;
+            const int g = c / cpg;
+            float z = (Elem<T>::load(v + k) - mr[2 * g]) * mr[2 * g + 1];
+            if (gamma) z *= gamma[c];
+            if (beta) z += beta[c];
+            if (silu) z = z / (1.0f + __expf(-z));
+            Elem<T>::store(v + k, z);
+        }
+        *reinterpret_cast<uint4*>(yr + (int64_t)e * V) = raw;
+    }
+}
+
+}  // namespace
+
+bool gn_shape_supported(const vae_tensor_t& x, int32_t groups) {
+    const int64_t V = x.dtype == VAE_DTYPE_BF16 ? 8 : 4;
+    if (groups <= 0 || x.c % groups != 0 || x.c % V != 0) return false;
+    const int64_t cv = x.c / V;
+    if (cv > kThreads || kThreads % cv != 0) return false;
+    const int64_t cpg = x.c / groups;
+    return (V % cpg == 0) || (cpg % V == 0);
+}
+
+size_t gn_stats_workspace(const vae_tensor_t& x, const BoxList& boxes, int32_t groups) {
+    GnBoxes g = make_boxes(x, boxes);
+    return (size_t)g.start[g.n] * (size_t)x.n * (size_t)groups * 3 * sizeof(double);
+}
+
+vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_t groups,
+                             double* ws, double* part_out, float* mean_rstd, float eps,
+                             hipStream_t stream) {
+    GnBoxes g = make_boxes(x, boxes);
+    dim3 grid((unsigned)g.start[g.n], (unsigned)x.n);
+    if (x.dtype == VAE_DTYPE_BF16)
+        hipLaunchKernelGGL(gn_stats_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(x.data), (int32_t)x.t, (int32_t)x.h,
+                           (int32_t)x.w, (int32_t)x.c, groups, g, ws);
+    else
+        hipLaunchKernelGGL(gn_stats_kernel<float>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const float*>(x.data), (int32_t)x.t, (int32_t)x.h,
+                           (int32_t)x.w, (int32_t)x.c, groups, g, ws);
+    VAE_HIP_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)groups, (unsigned)x.n), dim3(kThreads),
+                       0, stream, ws, g, groups, eps, part_out, mean_rstd);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, int32_t groups,
+                               float eps, float* mean_rstd, hipStream_t stream) {
+    hipLaunchKernelGGL(gn_combine_kernel, dim3((unsigned)groups, (unsigned)n), dim3(64), 0, stream,
+                       part, n_parts, groups, eps, mean_rstd);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t groups,
+                             const float* mean_rstd, const float* gamma, const float* beta,
+                             bool silu, const vae_tensor_t& y, hipStream_t stream) {
+    if (box.volume() == 0 || x.n == 0) return VAE_OK;
+    dim3 grid((unsigned)(box.bt() * box.bh()), (unsigned)x.n);
+    if (x.dtype == VAE_DTYPE_BF16)
+        hipLaunchKernelGGL(gn_apply_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(x.data), static_cast<uint16_t*>(y.data),
+                           (int32_t)x.t, (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, groups, box,
+                           mean_rstd, gamma, beta, (int32_t)silu);
+    else
+        hipLaunchKernelGGL(gn_apply_kernel<float>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const float*>(x.data), static_cast<float*>(y.data),
+                           (int32_t)x.t, (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, groups, box,
+                           mean_rstd, gamma, beta, (int32_t)silu);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+}  // namespace vae

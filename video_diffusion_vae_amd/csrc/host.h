@@ -1,0 +1,17 @@
+// Host-side helpers shared between the ABI layer and the decode executor (not part of the C ABI).
+#pragma once
+
+#include <vector>
+
+#include "kernels.h"
+
+namespace vae {
+
+vae_status_t check_tensor(const vae_tensor_t* t, const char* name);
+vae_status_t check_tiling(const vae_tiling_desc_t* d);
+bool overlaps(const vae_tensor_t& a, const vae_tensor_t& b);
+std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d);
+int32_t out_frames(int32_t t, int32_t scale_t);
+size_t gn_full_workspace(const vae_tensor_t& x, const BoxList& bl, int32_t groups);
+
+}  // namespace vae

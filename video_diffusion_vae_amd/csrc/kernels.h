@@ -1,0 +1,52 @@
+// Internal kernel launchers (not part of the C ABI). Every launcher assumes its arguments were
+// validated by the ABI layer; it only enqueues work on `stream` and reports launch errors.
+#pragma once
+
+#include "common.h"
+#include "tiling_math.h"
+
+namespace vae {
+
+constexpr int kMaxBoxes = 16;
+
+struct BoxList {
+    Box b[kMaxBoxes];
+    int32_t n;
+};
+
+// ---- convolution ----
+vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, const float* bias,
+                           const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                           hipStream_t stream);
+bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y);
+
+// ---- group norm ----
+// Workspace: per-block partials of every box, fp64 [blocks][N][G][3].
+size_t gn_stats_workspace(const vae_tensor_t& x, const BoxList& boxes, int32_t groups);
+// Per-block partials -> per-box partials (part_out, optional) and mean/rstd (optional).
+vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_t groups,
+                             double* ws, double* part_out, float* mean_rstd, float eps,
+                             hipStream_t stream);
+vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, int32_t groups,
+                               float eps, float* mean_rstd, hipStream_t stream);
+vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t groups,
+                             const float* mean_rstd, const float* gamma, const float* beta,
+                             bool silu, const vae_tensor_t& y, hipStream_t stream);
+bool gn_shape_supported(const vae_tensor_t& x, int32_t groups);
+
+// ---- upsampling ----
+vae_status_t launch_upsample(const vae_tensor_t& x, const Box& box, int32_t mode, int32_t st,
+                             int32_t sh, int32_t sw, const vae_tensor_t& y, hipStream_t stream);
+
+// ---- tiles ----
+vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& out_box, int32_t lead_h,
+                          int32_t trail_h, int32_t lead_w, int32_t trail_w,
+                          const vae_tensor_t& out, hipStream_t stream);
+vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& ah,
+                                   const AxisTiling& aw, hipStream_t stream);
+vae_status_t launch_zero(void* p, int64_t bytes, hipStream_t stream);
+// Copy x[:, box] (latent grid) into the dense tensor y (shape of the box).
+vae_status_t launch_crop(const vae_tensor_t& x, const Box& box, const vae_tensor_t& y,
+                         hipStream_t stream);
+
+}  // namespace vae

@@ -1,0 +1,137 @@
+// Overlap-blend merge of decoded tiles, and small helpers (zero fill, latent crop).
+//
+// The serial tiled decode blends each tile into a full-size buffer with a mask assembled from
+// per-axis parts, keeps the summed weights, and divides at the end ("[TRTLLM-14029][feat] LTX-2
+// tile-parallel VAE decode", Approach). Building that mask on the host and copying it over per
+// tile left the GPU about half idle, so here the mask is never materialised:
+//  - each kernel evaluates the separable ramps from the tile's overlaps while it streams;
+//  - the final divide evaluates the per-axis weight sums from the tile grid itself.
+// All passes go over contiguous rows (fixed n, t, h) of fp32 NDHWC data.
+#include "kernels.h"
+
+namespace vae {
+namespace {
+
+constexpr int kThreads = 256;
+
+// grid (tile rows bt*bh, N). out[box] += w * tile; w = ramp_h(h) * ramp_w(w) (T is never cut).
+__global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ tile,
+                                                         float* __restrict__ out, int32_t oT,
+                                                         int32_t oH, int32_t oW, int32_t C, Box b,
+                                                         int32_t lead_h, int32_t trail_h,
+                                                         int32_t lead_w, int32_t trail_w) {
+    const int n = blockIdx.y;
+    const int64_t r = blockIdx.x;
+    const int tl = (int)(r / b.bh()), hl = (int)(r % b.bh());
+    const float wh = ramp_weight(hl, (int)b.bh(), lead_h, trail_h);
+    const float* src = tile + (((int64_t)n * b.bt() + tl) * b.bh() + hl) * b.bw() * C;
+    float* dst = out + ((((int64_t)n * oT + b.t0 + tl) * oH + b.h0 + hl) * oW + b.w0) * C;
+    const int seg = (int)b.bw() * C;
+    for (int e = threadIdx.x; e < seg; e += kThreads) {
+        const int wl = e / C;
+        dst[e] += wh * ramp_weight(wl, (int)b.bw(), lead_w, trail_w) * src[e];
+    }
+}
+
+// grid (rows oT*oH, N). out /= S_h(h) * S_w(w).
+__global__ __launch_bounds__(kThreads) void merge_finalize_kernel(float* __restrict__ out,
+                                                                  int32_t oT, int32_t oH,
+                                                                  int32_t oW, int32_t C,
+                                                                  AxisTiling ah, AxisTiling aw) {
+    const int n = blockIdx.y;
+    const int64_t r = blockIdx.x;
+    const int h = (int)(r % oH);
+    const float sh = axis_weight_sum(ah, h);
+    float* row = out + ((int64_t)n * oT * oH + r) * oW * C;
+    const int seg = oW * C;
+    for (int e = threadIdx.x; e < seg; e += kThreads) {
+        const float s = sh * axis_weight_sum(aw, e / C);
+        row[e] /= s;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(uint4* p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * kThreads)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(64) void zero_tail_kernel(uint8_t* p, int64_t n) {
+    if ((int64_t)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+// grid (box rows, N): copy one contiguous row segment of bytes.
+__global__ __launch_bounds__(kThreads) void crop_kernel(const uint8_t* __restrict__ x,
+                                                        uint8_t* __restrict__ y, int32_t T,
+                                                        int32_t H, int32_t W, int64_t pos_bytes,
+                                                        Box b) {
+    const int n = blockIdx.y;
+    const int64_t r = blockIdx.x;
+    const int tl = (int)(r / b.bh()), hl = (int)(r % b.bh());
+    const uint8_t* src =
+        x + ((((int64_t)n * T + b.t0 + tl) * H + b.h0 + hl) * W + b.w0) * pos_bytes;
+    uint8_t* dst = y + (((int64_t)n * b.bt() + tl) * b.bh() + hl) * b.bw() * pos_bytes;
+    const int64_t seg = b.bw() * pos_bytes;
+    if (seg % 16 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0) {
+        for (int64_t e = threadIdx.x; e < seg / 16; e += kThreads)
+            reinterpret_cast<uint4*>(dst)[e] = reinterpret_cast<const uint4*>(src)[e];
+    } else {
+        for (int64_t e = threadIdx.x; e < seg; e += kThreads) dst[e] = src[e];
+    }
+}
+
+}  // namespace
+
+vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& b, int32_t lead_h,
+                          int32_t trail_h, int32_t lead_w, int32_t trail_w,
+                          const vae_tensor_t& out, hipStream_t stream) {
+    if (b.volume() == 0 || out.n == 0) return VAE_OK;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(b.bt() * b.bh()), (unsigned)out.n),
+                       dim3(kThreads), 0, stream, static_cast<const float*>(tile_out.data),
+                       static_cast<float*>(out.data), (int32_t)out.t, (int32_t)out.h,
+                       (int32_t)out.w, (int32_t)out.c, b, lead_h, trail_h, lead_w, trail_w);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& ah,
+                                   const AxisTiling& aw, hipStream_t stream) {
+    if (numel(out) == 0) return VAE_OK;
+    hipLaunchKernelGGL(merge_finalize_kernel, dim3((unsigned)(out.t * out.h), (unsigned)out.n),
+                       dim3(kThreads), 0, stream, static_cast<float*>(out.data), (int32_t)out.t,
+                       (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, ah, aw);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+vae_status_t launch_zero(void* p, int64_t bytes, hipStream_t stream) {
+    if (bytes <= 0) return VAE_OK;
+    if ((uintptr_t)p % 16 != 0) return fail(VAE_ERR_INVALID_ARG, "zero: pointer not 16-byte aligned");
+    const int64_t n16 = bytes / 16;
+    if (n16 > 0) {
+        int64_t blocks = ceil_div(n16, kThreads);
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                           static_cast<uint4*>(p), n16);
+        VAE_HIP_CHECK(hipGetLastError());
+    }
+    if (bytes % 16) {
+        hipLaunchKernelGGL(zero_tail_kernel, dim3(1), dim3(64), 0, stream,
+                           static_cast<uint8_t*>(p) + n16 * 16, bytes % 16);
+        VAE_HIP_CHECK(hipGetLastError());
+    }
+    return VAE_OK;
+}
+
+vae_status_t launch_crop(const vae_tensor_t& x, const Box& b, const vae_tensor_t& y,
+                         hipStream_t stream) {
+    if (b.volume() == 0 || x.n == 0) return VAE_OK;
+    hipLaunchKernelGGL(crop_kernel, dim3((unsigned)(b.bt() * b.bh()), (unsigned)x.n),
+                       dim3(kThreads), 0, stream, static_cast<const uint8_t*>(x.data),
+                       static_cast<uint8_t*>(y.data), (int32_t)x.t, (int32_t)x.h, (int32_t)x.w,
+                       x.c * elem_size(x.dtype), b);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+}  // namespace vae

@@ -1,0 +1,40 @@
+"""Upload a decoder's parameters to the device in the library's layouts.
+
+This is setup-time marshalling, not part of the decode itself:
+- conv weights go from [Cout, Cin, 3, 3, 3] to [Cout, 3, 3, 3, Cin] (the K dimension, taps then
+  channels, contiguous per output channel);
+- biases, gamma and beta become fp32 vectors.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from ._binding import Decoder, VAE_DTYPE_BF16, VAE_DTYPE_F32
+
+
+def conv_weight_layout(w, dtype, device):
+    """[Cout, Cin, 3, 3, 3] array -> contiguous device tensor [Cout, 3, 3, 3, Cin]."""
+    import torch
+    t = torch.as_tensor(np.ascontiguousarray(np.asarray(w, dtype=np.float32)))
+    t = t.permute(0, 2, 3, 4, 1).contiguous()
+    return t.to(device=device, dtype=dtype)
+
+
+def upload_decoder(spec: dict, params: list, device="cuda"):
+    """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
+
+    Each parameter dict is {"kind": "conv", "w", "b"} or {"kind": "gn", "gamma", "beta"} holding
+    host arrays. Returns the Decoder; it keeps the device tensors alive.
+    """
+    import torch
+    tdt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+    flat = []
+    for p in params:
+        if p["kind"] == "conv":
+            flat.append(conv_weight_layout(p["w"], tdt, device))
+            flat.append(torch.as_tensor(np.asarray(p["b"], np.float32)).to(device))
+        else:
+            flat.append(torch.as_tensor(np.asarray(p["gamma"], np.float32)).to(device))
+            flat.append(torch.as_tensor(np.asarray(p["beta"], np.float32)).to(device))
+    code = VAE_DTYPE_BF16 if spec["dtype"] == "bf16" else VAE_DTYPE_F32
+    return Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat)
