@@ -174,6 +174,8 @@ def main():
         "data": "synthetic (seeded latent, random-init weights)",
         "config": {"workload": workload, "latent": [1, 128, 16, 22, 40],
                    "output": [1, 3, 121, 704, 1280], "parallelism": "none (1 GPU)",
+                   "operands": "bf16 weights; fp32 conv inputs as bf16 hi+lo; fp32 accumulate",
+                   "activations": "fp32 between ops, bf16 GroupNorm outputs inside res blocks",
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
         "roofline": roofline, "kernels": summary, "cpu_baseline": baseline,
     }

@@ -101,16 +101,23 @@ VAE_API int32_t vae_version(void);
  * the tensor. Such a box is one patch of a patch-halo decode.
  *
  * Arguments:
- *  x: [N,T,H,W,Cin] input (device).
- *  weight: [Cout][3][3][3][Cin] (device), same dtype as x.
+ *  x: [N,T,H,W,Cin] input (device), bf16 or fp32.
+ *  weight: [Cout][3][3][3][Cin] (device) of dtype weight_dtype.
  *  bias: [Cout] fp32 (device), or NULL.
  *  residual: tensor of y's shape and dtype added to the result, or NULL. It may alias y.
- *  y: [N,T,H,W,Cout] output. bf16 or fp32 for bf16 x; fp32 for fp32 x. It must not overlap x.
- * bf16 runs on the MFMA path and requires Cin % 32 == 0; other shapes run on a slower path.
+ *  y: [N,T,H,W,Cout] output, bf16 or fp32. It must not overlap x.
+ *  flags: 0, or VAE_CONV_SPLIT_FP32.
+ * bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (MFMA). Products
+ * accumulate in fp32. An fp32 x is rounded to bf16 (nearest-even) as the operand, or, with
+ * VAE_CONV_SPLIT_FP32, applied as two bf16 operands hi = bf16(x) and lo = bf16(x - hi). The split
+ * keeps about 16 significant bits of x and costs twice the matrix-core work. Every other case runs
+ * on a direct fp32-accumulating path, where the flag changes nothing.
  */
+enum { VAE_CONV_SPLIT_FP32 = 1 };
 VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
-                                       const float* bias, const vae_tensor_t* residual,
-                                       vae_tensor_t* y, const vae_box_t* out_box,
+                                       int32_t weight_dtype, const float* bias,
+                                       const vae_tensor_t* residual, vae_tensor_t* y,
+                                       const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
@@ -131,7 +138,8 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
  *  boxes: the patches owning the statistics (n_boxes >= 1; NULL with n_boxes == 1 = whole tensor).
  *         The apply step writes y over every box.
  *  gamma, beta: [C] fp32 (device) or NULL (1 and 0).
- *  y: same shape as x; dtype bf16 or fp32. It may alias x.
+ *  y: same shape as x; dtype bf16 or fp32 (it may differ from x: an fp32 activation normalised
+ *     into the bf16 operand of the next convolution). It may alias x when the dtypes match.
  *  ws: device scratch of at least vae_groupnorm_silu_workspace() bytes.
  * Partials are combined in a fixed order: results are bitwise reproducible run to run.
  */
@@ -250,6 +258,16 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  *  VAE_OP_GN_SILU GroupNorm + SiLU
  *  VAE_OP_D2S     depth-to-space (st, sh, sw) with the causal frame drop
  *  VAE_OP_NEAREST nearest spatial upsampling (sh, sw)
+ * Dtypes:
+ *  - conv weights and GroupNorm outputs (the operands of the next conv) have the plan dtype;
+ *  - conv outputs and the residual stream have act_dtype;
+ *  - the latent has the plan dtype, and the decoded output is fp32.
+ * With bf16 weights, fp32 activations keep the bf16 rounding to the conv operands alone: about
+ * 40 fewer roundings on the way through the LTX-2-shaped plan.
+ * VAE_DECODE_SPLIT_FP32_OPERANDS goes further for convs that read an fp32 activation (the
+ * upsampling convs read the fp32 residual stream). It makes a standalone GN_SILU write fp32 (the
+ * output conv then reads fp32), and every such conv runs with VAE_CONV_SPLIT_FP32. The convs
+ * inside residual blocks keep one rounding of their GroupNorm operand.
  * The parameter pointers come in plan order, two per entry:
  *  conv -> (weight, bias);
  *  GN -> (gamma, beta);
@@ -265,8 +283,11 @@ typedef struct vae_layer_desc {
     int32_t f32_out;
 } vae_layer_desc_t;
 
+enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1 };
 typedef struct vae_decoder_spec {
-    int32_t dtype;              /* weights and activations: VAE_DTYPE_* */
+    int32_t dtype;              /* weights and convolution operands: VAE_DTYPE_* */
+    int32_t act_dtype;          /* activations stored between ops (conv outputs, residual stream) */
+    int32_t flags;              /* VAE_DECODE_SPLIT_FP32_OPERANDS or 0 */
     int32_t latent_channels;
     int32_t groups;
     float eps;

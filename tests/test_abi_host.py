@@ -108,8 +108,13 @@ def test_decoder_plan_validation(v):
     bad[0] = {"op": "conv", "cin": 8, "cout": 128}
     with pytest.raises(v.VaeError):           # channels do not chain
         v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, bad, fake[:0])
-    with pytest.raises(v.VaeError) as e:      # a bf16 plan must end in fp32
-        v.Decoder(v.VAE_DTYPE_BF16, 16, 32, 1e-6, spec["layers"], fake[:0])
+    with pytest.raises(v.VaeError) as e:      # bf16 activations: the last conv must be fp32
+        v.Decoder(v.VAE_DTYPE_BF16, 16, 32, 1e-6, spec["layers"], fake[:0],
+                  act_dtype=v.VAE_DTYPE_BF16)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:      # an fp32 plan cannot store bf16 activations
+        v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, spec["layers"], fake[:0],
+                  act_dtype=v.VAE_DTYPE_BF16)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
 
 

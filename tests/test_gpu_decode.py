@@ -64,11 +64,11 @@ def oracle_out(name, mode, affine=None):
                                        spec["scale"])
 
 
-def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1):
+def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32"):
     import torch
     spec = spec_of(name)
     z = ndhwc(vae_synth.latent(spec))
-    dec = v.upload_decoder(spec, params_of(name, affine))
+    dec = v.upload_decoder(spec, params_of(name, affine), act_dtype=act)
     zd = dev(z, spec["dtype"])
     if mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
@@ -164,3 +164,12 @@ def test_ltx2_tiny_both_modes(v):
     _bf16_bar(got, oracle_out("ltx2_tiny", "whole"))
     got = host(gpu_decode(v, "ltx2_tiny", "overlap"))
     _bf16_bar(got, oracle_out("ltx2_tiny", "overlap"))
+
+
+def test_bf16_activation_storage_variant(v):
+    """Storing every activation in bf16 (act_dtype=bf16) is the faster, less exact variant. About
+    40 extra roundings keep it above 50 dB PSNR, but it is not held to the 2e-2 max-abs bar; the
+    default (fp32 activations) is."""
+    got = host(gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16"))
+    ref = oracle_out("ltx2_tiny", "whole")
+    assert psnr(got, ref) >= 50.0

@@ -34,25 +34,34 @@ def _conv_inputs(shape, cin, cout, dtype, seed):
 
 
 CONV_CASES = [
-    # (N, T, H, W), Cin, Cout, out dtype, residual, box (t0,t1,h0,h1,w0,w1) or None
-    ((1, 3, 9, 17), 32, 64, "bf16", False, None),
-    ((1, 5, 10, 20), 64, 128, "f32", True, None),
-    ((2, 2, 8, 16), 32, 48, "f32", False, None),
-    ((1, 4, 11, 23), 128, 256, "bf16", True, (1, 4, 2, 9, 5, 15)),
-    ((1, 1, 7, 5), 96, 128, "bf16", False, None),
-    ((1, 6, 16, 32), 256, 384, "f32", True, (0, 6, 0, 16, 8, 24)),
+    # (N, T, H, W), Cin, Cout, in dtype, out dtype, residual, box (t0,t1,h0,h1,w0,w1) or None
+    ((1, 3, 9, 17), 32, 64, "bf16", "bf16", False, None),
+    ((1, 5, 10, 20), 64, 128, "bf16", "f32", True, None),
+    ((2, 2, 8, 16), 32, 48, "bf16", "f32", False, None),
+    ((1, 4, 11, 23), 128, 256, "bf16", "bf16", True, (1, 4, 2, 9, 5, 15)),
+    ((1, 1, 7, 5), 96, 128, "bf16", "bf16", False, None),
+    ((1, 6, 16, 32), 256, 384, "bf16", "f32", True, (0, 6, 0, 16, 8, 24)),
+    ((1, 3, 9, 19), 64, 256, "f32", "f32", True, None),
+    ((2, 4, 6, 17), 32, 64, "f32", "bf16", False, (0, 3, 1, 6, 3, 17)),
+    ((1, 2, 8, 16), 128, 52, "f32", "f32", False, None),
 ]
 
 
 @pytest.mark.parametrize("case", CONV_CASES)
 def test_conv3d_mfma_matches_oracle(v, case):
+    """bf16 weights on the matrix cores. An fp32 input is the operand after its nearest-even
+    rounding to bf16, so the reference convolves that rounded input."""
     import torch
-    (n, t, h, w), cin, cout, odt, use_res, bx = case
+    (n, t, h, w), cin, cout, idt, odt, use_res, bx = case
     x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", CONV_CASES.index(case))
-    ref = oracle.causal_conv3d(x, wt, b)
+    if idt == "f32":   # an fp32 activation with finer values than bf16
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [14, cin], scale=1e-3))
+        ref = oracle.causal_conv3d(vae_synth.round_bf16(x), wt, b)
+    else:
+        ref = oracle.causal_conv3d(x, wt, b)
     if use_res:
         ref = ref + r
-    xd = dev(x)
+    xd = dev(x, idt)
     wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
     bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
     rd = dev(r, odt) if use_res else None
@@ -72,6 +81,36 @@ def test_conv3d_mfma_matches_oracle(v, case):
         assert rel_max_abs(g, rf) <= 1e-4
     else:
         assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
+
+
+@pytest.mark.parametrize("shape,cin,cout,box", [((1, 3, 9, 19), 64, 256, None),
+                                                 ((1, 5, 7, 33), 32, 48, (1, 5, 0, 7, 4, 30))])
+def test_conv3d_split_operands(v, shape, cin, cout, box):
+    """VAE_CONV_SPLIT_FP32: an fp32 input applied as bf16 hi + lo. The reference convolves
+    hi + lo, which carries about 16 significant bits of x, so fp32 output matches it at 1e-4."""
+    import torch
+    n, t, h, w = shape
+    x, wt, b, _ = _conv_inputs(shape, cin, cout, "bf16", 40 + cin)
+    x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [15, cin], scale=3e-3))
+    hi = vae_synth.round_bf16(x).astype(np.float64)
+    lo = vae_synth.round_bf16(x - hi).astype(np.float64)
+    ref = oracle.causal_conv3d(hi + lo, wt, b)
+    y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=torch.float32)
+    v.vae_conv3d_causal(dev(x, "f32"), v.conv_weight_layout(wt, torch.bfloat16, "cuda"),
+                        torch.as_tensor(b, dtype=torch.float32, device="cuda"), None, y, box,
+                        flags=v.VAE_CONV_SPLIT_FP32)
+    torch.cuda.synchronize()
+    got = host(y)
+    bx = box or (0, t, 0, h, 0, w)
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    assert rel_max_abs(got[sl], ref[sl]) <= 1e-4
+    # the single-rounding result is measurably further from the exact fp32 convolution
+    exact = oracle.causal_conv3d(x, wt, b)[sl]
+    y1 = torch.empty_like(y)
+    v.vae_conv3d_causal(dev(x, "f32"), v.conv_weight_layout(wt, torch.bfloat16, "cuda"),
+                        torch.as_tensor(b, dtype=torch.float32, device="cuda"), None, y1, box)
+    torch.cuda.synchronize()
+    assert rel_max_abs(got[sl], exact) < 0.25 * rel_max_abs(host(y1)[sl], exact)
 
 
 @pytest.mark.parametrize("dtype,cin", [("f32", 16), ("f32", 32), ("bf16", 16), ("bf16", 24)])
@@ -101,13 +140,16 @@ def test_conv3d_rejects_bad_arguments(v):
 
 
 GN_CASES = [
-    # dtype, (N, T, H, W, C), groups, patch cuts (h cuts, w cuts)
-    ("f32", (1, 5, 32, 32, 32), 8, ([], [16])),
-    ("f32", (2, 3, 16, 16, 64), 32, ([7], [3, 11])),
-    ("bf16", (1, 3, 12, 20, 128), 32, ([5], [10])),
-    ("bf16", (1, 2, 8, 10, 1024), 32, ([], [1, 5, 9])),
-    ("bf16", (1, 4, 9, 13, 256), 32, ([], [])),
-    ("f32", (1, 3, 8, 8, 32), 32, ([4], [4])),
+    # in dtype > out dtype, (N, T, H, W, C), groups, patch cuts (h cuts, w cuts)
+    ("f32>f32", (1, 5, 32, 32, 32), 8, ([], [16])),
+    ("f32>f32", (2, 3, 16, 16, 64), 32, ([7], [3, 11])),
+    ("bf16>bf16", (1, 3, 12, 20, 128), 32, ([5], [10])),
+    ("bf16>bf16", (1, 2, 8, 10, 1024), 32, ([], [1, 5, 9])),
+    ("bf16>bf16", (1, 4, 9, 13, 256), 32, ([], [])),
+    ("f32>f32", (1, 3, 8, 8, 32), 32, ([4], [4])),
+    ("f32>bf16", (1, 3, 11, 20, 128), 32, ([], [5, 10, 15])),
+    ("f32>bf16", (1, 2, 8, 10, 1024), 32, ([4], [])),
+    ("bf16>f32", (1, 2, 6, 7, 256), 32, ([3], [])),
 ]
 
 
@@ -122,28 +164,30 @@ def _boxes(shape, cuts):
 @pytest.mark.parametrize("case", GN_CASES)
 def test_groupnorm_silu_patch_stats(v, case):
     import torch
-    dtype, shape, groups, cuts = case
+    dts, shape, groups, cuts = case
+    idt, odt = dts.split(">")
     n, t, h, w, c = shape
-    x = ndhwc(vae_synth.normal((n, c, t, h, w), [20, c, h], scale=1.5, mean=0.3, dtype=dtype))
+    x = ndhwc(vae_synth.normal((n, c, t, h, w), [20, c, h], scale=1.5, mean=0.3, dtype=idt))
     gamma = vae_synth.normal((c,), [21, c], scale=0.2, mean=1.0)
     beta = vae_synth.normal((c,), [22, c], scale=0.1)
     ref = oracle.silu(oracle.group_norm(x, groups, 1e-6, gamma, beta))
     boxes = _boxes(shape, cuts)
-    xd = dev(x, dtype)
-    y = torch.empty_like(xd)
-    v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, torch.as_tensor(gamma, device="cuda"),
-                         torch.as_tensor(beta, device="cuda"), True, y)
+    xd = dev(x, idt)
+    y = torch.empty(xd.shape, device="cuda",
+                    dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
+    g_d, b_d = torch.as_tensor(gamma, device="cuda"), torch.as_tensor(beta, device="cuda")
+    v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, g_d, b_d, True, y)
     torch.cuda.synchronize()
     got = host(y)
-    if dtype == "f32":
+    if odt == "f32":
         assert rel_max_abs(got, ref) <= 1e-4
     else:
         assert np.all(np.abs(got - ref) <= bf16_round_bound(ref) + 1e-4 * np.abs(ref).max())
-    # determinism: same call, bitwise same result (in place this time)
-    v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, torch.as_tensor(gamma, device="cuda"),
-                         torch.as_tensor(beta, device="cuda"), True, xd)
+    # determinism: the same call gives a bitwise identical result (in place when dtypes match)
+    y2 = xd if idt == odt else torch.empty_like(y)
+    v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, g_d, b_d, True, y2)
     torch.cuda.synchronize()
-    assert torch.equal(xd, y)
+    assert torch.equal(y2, y)
 
 
 def test_groupnorm_stats_export_and_combine(v):

@@ -16,6 +16,8 @@ VAE_DTYPE_BF16, VAE_DTYPE_F32 = 1, 2
 VAE_UPSAMPLE_NEAREST, VAE_UPSAMPLE_D2S = 1, 2
 VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
+VAE_CONV_SPLIT_FP32 = 1
+VAE_DECODE_SPLIT_FP32_OPERANDS = 1
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
 VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
 
@@ -64,7 +66,8 @@ class vae_layer_desc_t(ctypes.Structure):
 
 
 class vae_decoder_spec_t(ctypes.Structure):
-    _fields_ = [("dtype", ctypes.c_int32), ("latent_channels", ctypes.c_int32),
+    _fields_ = [("dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("latent_channels", ctypes.c_int32),
                 ("groups", ctypes.c_int32), ("eps", ctypes.c_float), ("n_layers", ctypes.c_int32),
                 ("layers", ctypes.POINTER(vae_layer_desc_t))]
 
@@ -87,7 +90,7 @@ def _load():
         "vae_last_error": ([], ctypes.c_char_p),
         "vae_last_error_info": ([ctypes.POINTER(vae_error_info_t)], I32),
         "vae_version": ([], I32),
-        "vae_conv3d_causal": ([T, P, P, T, T, B, P], I32),
+        "vae_conv3d_causal": ([T, P, I32, P, T, T, B, I32, P], I32),
         "vae_groupnorm_silu_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_groupnorm_silu": ([T, B, I32, I32, F, P, P, I32, T, P, SZ, P], I32),
         "vae_groupnorm_stats_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
@@ -191,12 +194,13 @@ def _workspace(nbytes, device):
 # Entry points (names as in include/vae.h)
 # ------------------------------------------------------------------------------------------------
 
-def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, stream=None):
-    """Causal Conv3d; weight is [Cout, 3, 3, 3, Cin] on the device."""
+def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, stream=None):
+    """Causal Conv3d; weight is a [Cout, 3, 3, 3, Cin] device tensor (bf16 or fp32)."""
     xd, yd = tensor_desc(x), tensor_desc(y)
     rd = tensor_desc(residual) if residual is not None else None
-    _check(LIB.vae_conv3d_causal(ctypes.byref(xd), _ptr(weight), _ptr(bias), _ref(rd),
-                                 ctypes.byref(yd), _ref(box(out_box)), _stream(stream)))
+    _check(LIB.vae_conv3d_causal(ctypes.byref(xd), _ptr(weight), _dtype_code(weight), _ptr(bias),
+                                 _ref(rd), ctypes.byref(yd), _ref(box(out_box)), int(flags),
+                                 _stream(stream)))
     return y
 
 
@@ -314,11 +318,13 @@ class Decoder:
     GN -> (gamma, beta); the tensors must outlive the decoder.
     """
 
-    def __init__(self, dtype, latent_channels, groups, eps, plan, params):
+    def __init__(self, dtype, latent_channels, groups, eps, plan, params, act_dtype=VAE_DTYPE_F32,
+                 flags=0):
         self._keep = list(params)
         descs = layer_descs(plan)
         self._layers = (vae_layer_desc_t * len(descs))(*descs)
-        spec = vae_decoder_spec_t(dtype, latent_channels, groups, eps, len(descs), self._layers)
+        spec = vae_decoder_spec_t(dtype, act_dtype, flags, latent_channels, groups, eps, len(descs),
+                                  self._layers)
         ptrs = (ctypes.c_void_p * max(len(params), 1))(
             *[None if p is None else p.data_ptr() for p in params])
         h = ctypes.c_void_p()

@@ -104,6 +104,16 @@ vae_status_t check_gn(const vae_tensor_t* x, int32_t groups) {
     return VAE_OK;
 }
 
+// y: same shape as x; any dtype. In place only with the same dtype, otherwise disjoint.
+vae_status_t check_gn_output(const vae_tensor_t& x, const vae_tensor_t& y) {
+    if (!same_grid(x, y) || x.c != y.c)
+        return fail(VAE_ERR_INVALID_ARG, "y must match x in shape");
+    if (x.data == y.data && x.dtype == y.dtype) return VAE_OK;
+    if (overlaps(x, y))
+        return fail(VAE_ERR_INVALID_ARG, "y must be x itself (same dtype) or not overlap it");
+    return VAE_OK;
+}
+
 size_t gn_full_workspace(const vae_tensor_t& x, const BoxList& bl, int32_t groups) {
     return align_up(gn_stats_workspace(x, bl, groups), 256) +
            align_up((size_t)x.n * groups * 2 * sizeof(float), 256);
@@ -222,18 +232,20 @@ VAE_API vae_status_t vae_last_error_info(vae_error_info_t* info) {
 VAE_API int32_t vae_version(void) { return 100; }
 
 VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
-                                       const float* bias, const vae_tensor_t* residual,
-                                       vae_tensor_t* y, const vae_box_t* out_box,
+                                       int32_t weight_dtype, const float* bias,
+                                       const vae_tensor_t* residual, vae_tensor_t* y,
+                                       const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream) {
     clear_error();
+    if (flags & ~VAE_CONV_SPLIT_FP32) return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
     VAE_TRY(check_tensor(x, "x"));
     VAE_TRY(check_tensor(y, "y"));
     if (!weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
+    if (weight_dtype != VAE_DTYPE_BF16 && weight_dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_INVALID_ARG, "unknown weight dtype");
     if (reinterpret_cast<uintptr_t>(weight) % 16 != 0)
         return fail(VAE_ERR_INVALID_ARG, "weight must be 16-byte aligned");
     if (!same_grid(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "x and y must share N, T, H, W");
-    if (x->dtype == VAE_DTYPE_F32 && y->dtype != VAE_DTYPE_F32)
-        return fail(VAE_ERR_UNSUPPORTED, "fp32 input needs an fp32 output");
     if (residual) {
         VAE_TRY(check_tensor(residual, "residual"));
         if (!same_grid(*residual, *y) || residual->c != y->c || residual->dtype != y->dtype)
@@ -242,7 +254,8 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
     }
     if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
     VAE_TRY(check_box(out_box, *y, "out_box"));
-    return launch_conv3d(*x, weight, bias, residual, *y, to_box(out_box, *y), as_stream(stream));
+    return launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, to_box(out_box, *y), flags,
+                         as_stream(stream));
 }
 
 VAE_API vae_status_t vae_groupnorm_stats_workspace(const vae_tensor_t* x, const vae_box_t* boxes,
@@ -302,10 +315,7 @@ VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t*
     clear_error();
     VAE_TRY(check_gn(x, groups));
     VAE_TRY(check_tensor(y, "y"));
-    if (!same_grid(*x, *y) || x->c != y->c || x->dtype != y->dtype)
-        return fail(VAE_ERR_INVALID_ARG, "y must match x in shape and dtype");
-    if (x->data != y->data && overlaps(*x, *y))
-        return fail(VAE_ERR_INVALID_ARG, "y must be x itself or not overlap it");
+    VAE_TRY(check_gn_output(*x, *y));
     if (!mean_rstd) return fail(VAE_ERR_INVALID_ARG, "mean_rstd is NULL");
     VAE_TRY(check_box(box, *x, "box"));
     return launch_gn_apply(*x, to_box(box, *x), groups, mean_rstd, gamma, beta, apply_silu != 0,
@@ -320,10 +330,7 @@ VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* 
     clear_error();
     VAE_TRY(check_gn(x, groups));
     VAE_TRY(check_tensor(y, "y"));
-    if (!same_grid(*x, *y) || x->c != y->c || x->dtype != y->dtype)
-        return fail(VAE_ERR_INVALID_ARG, "y must match x in shape and dtype");
-    if (x->data != y->data && overlaps(*x, *y))
-        return fail(VAE_ERR_INVALID_ARG, "y must be x itself or not overlap it");
+    VAE_TRY(check_gn_output(*x, *y));
     if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
     BoxList bl;
     VAE_TRY(box_list(*x, boxes, n_boxes, &bl));

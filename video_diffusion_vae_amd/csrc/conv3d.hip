@@ -1,6 +1,6 @@
 // Causal Conv3d (3x3x3, stride 1) on channels-last (NDHWC) activations.
 //
-// bf16 path: implicit GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+// bf16 weights: implicit GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //  - GEMM view: M = output positions, N = Cout, K = 27 * Cin, ordered (channel chunk, tap).
 //  - One workgroup computes a 2 x 8 x 16 (T x H x W) block of 256 output positions for NT
 //    output channels.
@@ -12,14 +12,21 @@
 //    frame index below 0 reads frame 0. The pages motivate this: a halo built by concatenation
 //    cost 1.31x ("[TRTLLM-14123][feat] add ParallelVAE_TrtllmWan for native Wan VAE",
 //    Description).
+//  - fp32 inputs are rounded to bf16 (nearest-even) as they are staged, because MFMA operands are
+//    bf16. Accumulation is fp32. With the split flag an fp32 input is applied as two bf16
+//    operands, hi = bf16(x) and lo = bf16(x - hi). The K loop visits every channel chunk twice,
+//    about 16 significant bits of x reach the matrix cores, and the MFMA work doubles.
 //  - The weights of the next tap are prefetched into registers while the current tap runs, and
 //    double-buffered in LDS.
 //  - LDS rows are padded from 64 to 80 bytes, so the 16-byte operand reads of 8 consecutive
 //    lanes hit 8 distinct 16-byte bank groups.
+//  - Epilogue: each wave parks one 32 x WN accumulator tile at a time in LDS (reusing the input
+//    tile), then every lane writes four consecutive channels with one 16-byte (fp32) or 8-byte
+//    (bf16) store. Bias and residual are added on the way.
 //  - Workgroups are ordered output-channel tile slowest, and remapped so that each XCD (the
 //    hardware deals workgroup i to XCD i % 8) runs a contiguous range of them. An XCD then keeps
 //    one weight slice in its own L2 while it streams input blocks.
-// fp32 (and any shape the MFMA path does not take): a direct kernel, one thread per output.
+// fp32 weights, or Cin % 32 != 0, or Cout % 4 != 0: a direct kernel, one thread per output.
 #include "kernels.h"
 
 namespace vae {
@@ -37,7 +44,7 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
 struct MfmaArgs {
-    const uint16_t* x;
+    const void* x;
     const uint16_t* w;
     const float* bias;
     const void* res;
@@ -55,7 +62,63 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return (bid % kXcds) * per + bid / kXcds;
 }
 
-template <int NT, bool OUT_F32>
+// 8 input channels starting at p, as 8 bf16 in one 16-byte word.
+template <typename TI> __device__ __forceinline__ uint4 load8(const TI* p);
+template <> __device__ __forceinline__ uint4 load8<uint16_t>(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+template <> __device__ __forceinline__ uint4 load8<float>(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    uint4 r;
+    r.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    r.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    r.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
+    r.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+    return r;
+}
+
+// The low half of the hi + lo bf16 split of 8 fp32 values: bf16(x - bf16(x)).
+__device__ __forceinline__ uint16_t lo_bf16(float x) {
+    return f32_to_bf16(x - bf16_to_f32(f32_to_bf16(x)));
+}
+template <typename TI> __device__ __forceinline__ uint4 load8_lo(const TI* p);
+template <> __device__ __forceinline__ uint4 load8_lo<uint16_t>(const uint16_t*) {
+    return make_uint4(0, 0, 0, 0);
+}
+template <> __device__ __forceinline__ uint4 load8_lo<float>(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    uint4 r;
+    r.x = (uint32_t)lo_bf16(a.x) | ((uint32_t)lo_bf16(a.y) << 16);
+    r.y = (uint32_t)lo_bf16(a.z) | ((uint32_t)lo_bf16(a.w) << 16);
+    r.z = (uint32_t)lo_bf16(b.x) | ((uint32_t)lo_bf16(b.y) << 16);
+    r.w = (uint32_t)lo_bf16(b.z) | ((uint32_t)lo_bf16(b.w) << 16);
+    return r;
+}
+
+template <typename TO> __device__ __forceinline__ void load4(const TO* p, float* v);
+template <> __device__ __forceinline__ void load4<float>(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+template <> __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_to_f32((uint16_t)(a.x & 0xffff)); v[1] = bf16_to_f32((uint16_t)(a.x >> 16));
+    v[2] = bf16_to_f32((uint16_t)(a.y & 0xffff)); v[3] = bf16_to_f32((uint16_t)(a.y >> 16));
+}
+template <typename TO> __device__ __forceinline__ void store4(TO* p, const float* v);
+template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float* v) {
+    uint2 a;
+    a.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    a.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = a;
+}
+
+template <int NT, typename TI, typename TO, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t halo[kHaloPos * kRow];
     __shared__ __attribute__((aligned(16))) uint8_t bbuf[2][NT * kRow];
@@ -87,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
     const int khalf = lane >> 5;      // which 8 of the 16 k values this lane feeds
 
     const int64_t cin = a.cin;
-    const uint16_t* xn = a.x + (int64_t)n * a.T * a.H * a.W * cin;
+    const TI* xn = static_cast<const TI*>(a.x) + (int64_t)n * a.T * a.H * a.W * cin;
 
     f32x16_t acc[4][NJ];
 #pragma unroll
@@ -122,7 +185,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
         }
     };
 
-    for (int c0 = 0; c0 < a.cin; c0 += kCK) {
+    const int n_passes = (a.cin / kCK) * (SPLIT ? 2 : 1);
+    for (int kc = 0; kc < n_passes; ++kc) {
+        const int c0 = (SPLIT ? (kc >> 1) : kc) * kCK;
+        const bool lo = SPLIT && (kc & 1);
         __syncthreads();  // the previous chunk's LDS reads are done
         for (int u = tid; u < kHaloPos * 4; u += kThreads) {
             int pos = u >> 2, g = u & 3;
@@ -134,9 +200,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
             tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
             int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
             uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
-            if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W)
-                v = *reinterpret_cast<const uint4*>(
-                    xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8);
+            if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
+                const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
+                v = lo ? load8_lo<TI>(src) : load8<TI>(src);
+            }
             *reinterpret_cast<uint4*>(&halo[pos * kRow + g * 16]) = v;
         }
         load_b(0, c0);
@@ -171,41 +238,73 @@ __global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
         }
     }
 
-    // Epilogue: lane holds column (lane & 31) of each 32x32 tile; register r holds row
-    // (r / 4) * 8 + (lane / 32) * 4 + r % 4.
+    // Epilogue. In a 32x32 accumulator tile, lane l holds column l % 32 and register r holds
+    // row (r / 4) * 8 + (l / 32) * 4 + r % 4. Each wave parks one 32 x WN sub-tile at a time in
+    // its own slice of the (now idle) input tile, then reads rows back four channels per lane.
+    constexpr int EP = WN + 4;                      // padded staging row, floats
+    constexpr int LPR = WN / 4;                     // lanes per staged row
+    constexpr int RPP = 64 / LPR;                   // rows per pass
+    static_assert(4 * 32 * EP * 4 <= kHaloPos * kRow, "epilogue staging must fit the input tile");
+    float* ep = reinterpret_cast<float*>(halo) + wave * (32 * EP);
+    const TO* res = static_cast<const TO*>(a.res);
+    TO* y = static_cast<TO*>(a.y);
     const int t = t_blk + wave_m;
+    const int c4 = (lane % LPR) * 4;
+    const int co = n_blk + wave_n * WN + c4;
+    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.bias)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int co = n_blk + wave_n * WN + j * 32 + lrow;
-        if (co >= a.cout || t >= a.box.t1) continue;
-        const float bv = a.bias ? a.bias[co] : 0.0f;
+        for (int k = 0; k < 4; ++k)
+            if (co + k < a.cout) bv[k] = a.bias[co + k];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = i * 32 + (r >> 2) * 8 + khalf * 4 + (r & 3);
-                const int h = h_blk + (row >> 4), w = w_blk + (row & 15);
-                if (h >= a.box.h1 || w >= a.box.w1) continue;
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ep[((r >> 2) * 8 + khalf * 4 + (r & 3)) * EP + j * 32 + lrow] = acc[i][j][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int pass = 0; pass < 32 / RPP; ++pass) {
+            const int row = pass * RPP + lane / LPR;
+            const int m = i * 32 + row;
+            const int h = h_blk + (m >> 4), w = w_blk + (m & 15);
+            if (t < a.box.t1 && h < a.box.h1 && w < a.box.w1 && co < a.cout) {
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = ep[row * EP + c4 + k] + bv[k];
                 const int64_t o = ((((int64_t)n * a.T + t) * a.H + h) * a.W + w) * a.cout + co;
-                float v = acc[i][j][r] + bv;
-                if (OUT_F32) {
-                    if (a.res) v += reinterpret_cast<const float*>(a.res)[o];
-                    reinterpret_cast<float*>(a.y)[o] = v;
+                if (co + 4 <= a.cout) {
+                    if (res) {
+                        float rv[4];
+                        load4<TO>(res + o, rv);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) v[k] += rv[k];
+                    }
+                    store4<TO>(y + o, v);
                 } else {
-                    if (a.res) v += bf16_to_f32(reinterpret_cast<const uint16_t*>(a.res)[o]);
-                    reinterpret_cast<uint16_t*>(a.y)[o] = f32_to_bf16(v);
+                    for (int k = 0; co + k < a.cout; ++k) {
+                        float vk = v[k];
+                        if (res) vk += Elem<TO>::load(res + o + k);
+                        Elem<TO>::store(y + o + k, vk);
+                    }
                 }
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // Direct path: one thread per (output position, output channel).
 // ------------------------------------------------------------------------------------------------
-template <typename TI, typename TO>
+template <typename TX, typename TW, typename TO>
 __global__ __launch_bounds__(256) void conv3d_direct_kernel(
-    const TI* __restrict__ x, const TI* __restrict__ w, const float* __restrict__ bias,
+    const TX* __restrict__ x, const TW* __restrict__ w, const float* __restrict__ bias,
     const TO* res, TO* y, int32_t N, int32_t T, int32_t H, int32_t W, int32_t cin, int32_t cout,
     Box box) {
     const int64_t total = (int64_t)N * box.volume() * cout;
@@ -221,7 +320,7 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
     const int n = (int)(p / box.bt());
     const int t = box.t0 + tl, h = box.h0 + hl, ww = box.w0 + wl;
     float acc = bias ? bias[co] : 0.0f;
-    const TI* xn = x + (int64_t)n * T * H * W * cin;
+    const TX* xn = x + (int64_t)n * T * H * W * cin;
     for (int kt = 0; kt < 3; ++kt) {
         int ti = t + kt - 2;
         ti = ti < 0 ? 0 : ti;
@@ -231,9 +330,9 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
             for (int kw = 0; kw < 3; ++kw) {
                 int wi = ww + kw - 1;
                 if (wi < 0 || wi >= W) continue;
-                const TI* xp = xn + ((int64_t)(ti * H + hi) * W + wi) * cin;
-                const TI* wp = w + ((int64_t)co * 27 + (kt * 9 + kh * 3 + kw)) * cin;
-                for (int c = 0; c < cin; ++c) acc += Elem<TI>::load(xp + c) * Elem<TI>::load(wp + c);
+                const TX* xp = xn + ((int64_t)(ti * H + hi) * W + wi) * cin;
+                const TW* wp = w + ((int64_t)co * 27 + (kt * 9 + kh * 3 + kw)) * cin;
+                for (int c = 0; c < cin; ++c) acc += Elem<TX>::load(xp + c) * Elem<TW>::load(wp + c);
             }
         }
     }
@@ -242,12 +341,12 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
     Elem<TO>::store(y + o, acc);
 }
 
-template <int NT, bool OUT_F32>
+template <int NT, typename TI, typename TO, bool SPLIT>
 vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
                       hipStream_t stream) {
     MfmaArgs a;
-    a.x = static_cast<const uint16_t*>(x.data);
+    a.x = x.data;
     a.w = static_cast<const uint16_t*>(w);
     a.bias = bias;
     a.res = residual ? residual->data : nullptr;
@@ -265,21 +364,40 @@ vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
     int64_t total = mblocks * ceil_div(y.c, NT);
     if (total > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "conv3d: grid too large");
     a.n_mblocks = (int32_t)mblocks;
-    hipLaunchKernelGGL((conv3d_mfma_kernel<NT, OUT_F32>), dim3((unsigned)total), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT>), dim3((unsigned)total),
+                       dim3(kThreads), 0, stream, a);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
 
-template <typename TI, typename TO>
+template <int NT, typename TI, bool SPLIT>
+vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bias,
+                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                          hipStream_t stream) {
+    if (y.dtype == VAE_DTYPE_F32)
+        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, stream);
+    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, stream);
+}
+
+template <int NT>
+vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
+                         const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                         bool split, hipStream_t stream) {
+    if (x.dtype == VAE_DTYPE_BF16)
+        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, stream);
+    if (split) return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, stream);
+    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, stream);
+}
+
+template <typename TX, typename TW, typename TO>
 vae_status_t run_direct(const vae_tensor_t& x, const void* w, const float* bias,
                         const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
                         hipStream_t stream) {
     int64_t total = x.n * box.volume() * y.c;
     int64_t blocks = ceil_div(total, 256);
     if (blocks > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "conv3d: grid too large");
-    hipLaunchKernelGGL((conv3d_direct_kernel<TI, TO>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const TI*>(x.data), static_cast<const TI*>(w), bias,
+    hipLaunchKernelGGL((conv3d_direct_kernel<TX, TW, TO>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, static_cast<const TX*>(x.data), static_cast<const TW*>(w), bias,
                        residual ? static_cast<const TO*>(residual->data) : nullptr,
                        static_cast<TO*>(y.data), (int32_t)x.n, (int32_t)x.t, (int32_t)x.h,
                        (int32_t)x.w, (int32_t)x.c, (int32_t)y.c, box);
@@ -287,29 +405,36 @@ vae_status_t run_direct(const vae_tensor_t& x, const void* w, const float* bias,
     return VAE_OK;
 }
 
-}  // namespace
-
-bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y) {
-    (void)y;
-    return x.dtype == VAE_DTYPE_BF16 && x.c % kCK == 0;
+template <typename TX, typename TW>
+vae_status_t run_direct_out(const vae_tensor_t& x, const void* w, const float* bias,
+                            const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                            hipStream_t stream) {
+    if (y.dtype == VAE_DTYPE_F32)
+        return run_direct<TX, TW, float>(x, w, bias, residual, y, box, stream);
+    return run_direct<TX, TW, uint16_t>(x, w, bias, residual, y, box, stream);
 }
 
-vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, const float* bias,
-                           const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                           hipStream_t stream) {
+}  // namespace
+
+bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype) {
+    return weight_dtype == VAE_DTYPE_BF16 && x.c % kCK == 0 && y.c % 4 == 0;
+}
+
+vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
+                           const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
+                           const Box& box, int32_t flags, hipStream_t stream) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
-    const bool out_f32 = y.dtype == VAE_DTYPE_F32;
-    if (conv_uses_mfma(x, y)) {
-        if (y.c >= 128)
-            return out_f32 ? run_mfma<128, true>(x, w, bias, residual, y, box, stream)
-                           : run_mfma<128, false>(x, w, bias, residual, y, box, stream);
-        return out_f32 ? run_mfma<64, true>(x, w, bias, residual, y, box, stream)
-                       : run_mfma<64, false>(x, w, bias, residual, y, box, stream);
+    const bool xf = x.dtype == VAE_DTYPE_F32;
+    const bool split = (flags & VAE_CONV_SPLIT_FP32) != 0;
+    if (conv_uses_mfma(x, y, weight_dtype)) {
+        if (y.c >= 128) return run_mfma_in<128>(x, w, bias, residual, y, box, split, stream);
+        return run_mfma_in<64>(x, w, bias, residual, y, box, split, stream);
     }
-    if (x.dtype == VAE_DTYPE_F32)
-        return run_direct<float, float>(x, w, bias, residual, y, box, stream);
-    return out_f32 ? run_direct<uint16_t, float>(x, w, bias, residual, y, box, stream)
-                   : run_direct<uint16_t, uint16_t>(x, w, bias, residual, y, box, stream);
+    if (weight_dtype == VAE_DTYPE_F32)
+        return xf ? run_direct_out<float, float>(x, w, bias, residual, y, box, stream)
+                  : run_direct_out<uint16_t, float>(x, w, bias, residual, y, box, stream);
+    return xf ? run_direct_out<float, uint16_t>(x, w, bias, residual, y, box, stream)
+              : run_direct_out<uint16_t, uint16_t>(x, w, bias, residual, y, box, stream);
 }
 
 }  // namespace vae

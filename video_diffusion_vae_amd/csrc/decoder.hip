@@ -18,7 +18,7 @@
 #include "host.h"
 
 struct vae_decoder {
-    int32_t dtype = 0, latent_c = 0, groups = 0;
+    int32_t dtype = 0, act_dtype = 0, flags = 0, latent_c = 0, groups = 0;
     float eps = 0.0f;
     std::vector<vae_layer_desc_t> layers;
     std::vector<const void*> ptrs;
@@ -39,6 +39,12 @@ struct Shape {
     int32_t dtype;
     int64_t bytes() const { return n * t * h * w * c * elem_size(dtype); }
 };
+
+// Output dtype of a standalone GN_SILU: the next conv's operand dtype, or the activation dtype
+// when that conv takes fp32 inputs as split operands.
+int32_t gn_silu_dtype(const vae_decoder& d) {
+    return (d.flags & VAE_DECODE_SPLIT_FP32_OPERANDS) ? d.act_dtype : d.dtype;
+}
 
 // Number of device pointers each op consumes.
 int ptrs_for(const vae_layer_desc_t& l) {
@@ -61,7 +67,13 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
         switch (l.op) {
             case VAE_OP_CONV:
                 s.c = l.cout;
-                if (l.f32_out) s.dtype = VAE_DTYPE_F32;
+                s.dtype = l.f32_out ? VAE_DTYPE_F32 : d.act_dtype;
+                break;
+            case VAE_OP_RES:
+                s.dtype = d.act_dtype;
+                break;
+            case VAE_OP_GN_SILU:
+                s.dtype = gn_silu_dtype(d);
                 break;
             case VAE_OP_D2S:
                 s.t = l.st * s.t - (l.st - 1);
@@ -136,7 +148,9 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         if (!last) r->act = std::max(r->act, s.bytes());
         if (last && final_in_buffer) r->tile = std::max(r->tile, s.bytes());
         if (l.op == VAE_OP_RES || l.op == VAE_OP_GN_SILU) {
-            r->act = std::max(r->act, cur.bytes());
+            Shape g = cur;
+            g.dtype = l.op == VAE_OP_RES ? d.dtype : gn_silu_dtype(d);
+            r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
             vae_tensor_t x = tensor_of(nullptr, cur);
             r->gn = std::max<int64_t>(
                 r->gn, (int64_t)gn_stats_workspace(x, scaled_boxes(boxes, cur.t, ch, cw), d.groups));
@@ -211,7 +225,10 @@ struct Runner {
 
     vae_status_t conv(const vae_tensor_t& x, const void* w, const void* b,
                       const vae_tensor_t* res, const vae_tensor_t& y, int layer) {
-        VAE_TRY(launch_conv3d(x, w, static_cast<const float*>(b), res, y, whole_box(y), s));
+        const int32_t cf =
+            (d->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) ? VAE_CONV_SPLIT_FP32 : 0;
+        VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(b), res, y, whole_box(y),
+                              cf, s));
         const double flops = 2.0 * 27.0 * (double)x.c * (double)y.c * (double)positions(y);
         const double bytes = (double)numel(x) * elem_size(x.dtype) +
                              (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
@@ -246,29 +263,34 @@ struct Runner {
                 cur = y;
                 cur_buf = last ? -2 : nb;
             } else if (l.op == VAE_OP_RES) {
+                // x -> GN1 -> t1 -> conv1 -> t2 -> GN2 -> t1 -> conv2 (+ x) -> t2
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
                 const int b1 = free_buf(cur_buf, -1);
                 const int b2 = free_buf(cur_buf, b1);
-                const Shape cs = shape_of(cur);
-                vae_tensor_t t1 = buf(b1, cs), t2 = buf(b2, cs);
+                Shape gs = shape_of(cur), as = shape_of(cur);
+                gs.dtype = d->dtype;
+                as.dtype = d->act_dtype;
+                vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
                 VAE_TRY(conv(t1, d->ptrs[p + 2], d->ptrs[p + 3], nullptr, t2, layer));
-                VAE_TRY(gn(t2, t2, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
-                vae_tensor_t y = last ? final_out : t1;
-                VAE_TRY(conv(t2, d->ptrs[p + 6], d->ptrs[p + 7], &cur, y, layer));
+                VAE_TRY(gn(t2, t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
+                vae_tensor_t y = last ? final_out : t2;
+                VAE_TRY(conv(t1, d->ptrs[p + 6], d->ptrs[p + 7], &cur, y, layer));
                 p += 8;
                 cur = y;
-                cur_buf = last ? -2 : b1;
+                cur_buf = last ? -2 : b2;
             } else if (l.op == VAE_OP_GN_SILU) {
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
                 vae_tensor_t y;
                 int nb = cur_buf;
+                Shape gs = shape_of(cur);
+                gs.dtype = gn_silu_dtype(*d);
                 if (last) {
                     y = final_out;
                     nb = -2;
-                } else if (cur_buf < 0) {
+                } else if (cur_buf < 0 || cur.dtype != gs.dtype) {
                     nb = free_buf(cur_buf, -1);
-                    y = buf(nb, shape_of(cur));
+                    y = buf(nb, gs);
                 } else {
                     y = cur;  // in place
                 }
@@ -352,6 +374,13 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
     *out = nullptr;
     if (spec->dtype != VAE_DTYPE_BF16 && spec->dtype != VAE_DTYPE_F32)
         return fail(VAE_ERR_INVALID_ARG, "unknown plan dtype");
+    if (spec->act_dtype != VAE_DTYPE_BF16 && spec->act_dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_INVALID_ARG, "unknown activation dtype");
+    if (spec->dtype == VAE_DTYPE_F32 && spec->act_dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_UNSUPPORTED, "an fp32 plan keeps fp32 activations");
+    if (spec->flags & ~VAE_DECODE_SPLIT_FP32_OPERANDS)
+        return fail(VAE_ERR_INVALID_ARG, "unknown decoder flags");
+    const bool split = (spec->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) != 0;
     if (spec->latent_channels < 1 || spec->groups < 1 || !(spec->eps >= 0.0f))
         return fail(VAE_ERR_INVALID_ARG, "latent_channels and groups must be >= 1, eps >= 0");
     if (spec->n_layers < 1 || !spec->layers) return fail(VAE_ERR_INVALID_ARG, "empty layer plan");
@@ -364,15 +393,14 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
             case VAE_OP_CONV:
                 if (l.cin != c || l.cout < 1)
                     return fail(VAE_ERR_INVALID_ARG, "conv channels do not chain", 4, l.cin, -1, c);
-                if (act != spec->dtype)
-                    return fail(VAE_ERR_UNSUPPORTED, "no conv after an fp32-output conv");
                 c = l.cout;
-                if (l.f32_out) act = VAE_DTYPE_F32;
+                act = l.f32_out ? VAE_DTYPE_F32 : spec->act_dtype;
                 break;
             case VAE_OP_RES:
                 if (l.cin != c) return fail(VAE_ERR_INVALID_ARG, "res width does not chain");
-                if (act != spec->dtype)
-                    return fail(VAE_ERR_UNSUPPORTED, "no res block after an fp32-output conv");
+                if (act != spec->act_dtype)
+                    return fail(VAE_ERR_UNSUPPORTED,
+                                "a residual block input must have the activation dtype");
                 if (c % spec->groups)
                     return fail(VAE_ERR_UNSUPPORTED, "width not divisible by groups", 4, c,
                                 spec->groups);
@@ -381,6 +409,7 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
                 if (c % spec->groups)
                     return fail(VAE_ERR_UNSUPPORTED, "width not divisible by groups", 4, c,
                                 spec->groups);
+                act = split ? spec->act_dtype : spec->dtype;
                 break;
             case VAE_OP_D2S: {
                 if (l.st < 1 || l.sh < 1 || l.sw < 1)
@@ -400,7 +429,7 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
         need += ptrs_for(l);
     }
     if (act != VAE_DTYPE_F32)
-        return fail(VAE_ERR_UNSUPPORTED, "the plan must end in fp32 (use f32_out on the last conv)");
+        return fail(VAE_ERR_UNSUPPORTED, "the plan must end in fp32 (fp32 activations or f32_out)");
     if (n_ptrs != need || (need > 0 && !params))
         return fail(VAE_ERR_INVALID_ARG, "parameter pointer count does not match the plan", -1,
                     n_ptrs, -1, need);
@@ -416,6 +445,8 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
     vae_decoder* d = new (std::nothrow) vae_decoder();
     if (!d) return fail(VAE_ERR_INVALID_ARG, "out of host memory");
     d->dtype = spec->dtype;
+    d->act_dtype = spec->act_dtype;
+    d->flags = spec->flags;
     d->latent_c = spec->latent_channels;
     d->groups = spec->groups;
     d->eps = spec->eps;

@@ -4,13 +4,18 @@
 // divided by the count. Per-patch means and Bessel's correction are both wrong ("Add tiled VAE
 // parallelism & extended model support", PatchGroupNorm commit message). Three steps:
 //  1. gn_stats_kernel. Each block streams a range of rows of one patch box. A "row" is the
-//     positions of the box at fixed (n, t, h), which are contiguous in NDHWC. Every thread keeps a
-//     Welford (count, mean, M2) per channel for a fixed 16-byte channel vector. The block merges
-//     its threads into per-group partials (fp64) and writes them to its own slot: no atomics.
+//     positions of the box at fixed (n, t, h), which are contiguous in NDHWC. Every thread owns a
+//     fixed 16-byte channel vector. Per channel it accumulates sums of (x - K) and (x - K)^2, where
+//     the shift K is the first value it reads (the shifted-data variance algorithm; no division in
+//     the loop, and robust to a large mean). At the end these become (count, mean, M2). The block
+//     merges its threads into per-group partials (fp64, Chan) and writes them to its own slot: no
+//     atomics.
 //  2. gn_finalize_kernel. One block per (group, sample). It merges the block partials of each box
 //     with Chan's pairwise update in a fixed order, then merges the boxes in box order. It writes
 //     per-box (count, mean, M2) and (mean, rstd).
-//  3. gn_apply_kernel. Streams rows again: y = act((x - mean) * rstd * gamma + beta).
+//  3. gn_apply_kernel. Streams rows again. Each thread folds (mean, rstd, gamma, beta) of its
+//     channels into one scale and shift, so an element costs one FMA plus the SiLU. It may read
+//     fp32 and write bf16 (the next convolution's operand).
 // Every reduction has a fixed order, so results are bitwise reproducible.
 #include "kernels.h"
 
@@ -18,8 +23,9 @@ namespace vae {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int64_t kElemsPerBlock = 1 << 17;   // target elements one stats block streams
+constexpr int64_t kElemsPerBlock = 1 << 18;   // target elements one stats block streams
 constexpr int kMaxStatsBlocks = 4096;
+constexpr int kUnroll = 4;
 
 struct GnBoxes {
     Box b[kMaxBoxes];
@@ -92,27 +98,60 @@ __global__ __launch_bounds__(kThreads) void gn_stats_kernel(const T* __restrict_
     const int tid = threadIdx.x;
     const int seg = (int)b.bw() * CV;     // vectors per row
     float cnt = 0.0f;
-    float mean[V], m2[V];
+    float shift[V], s1[V], s2[V];
 #pragma unroll
-    for (int k = 0; k < V; ++k) mean[k] = m2[k] = 0.0f;
+    for (int k = 0; k < V; ++k) shift[k] = s1[k] = s2[k] = 0.0f;
+    bool have_shift = false;
 
     for (int64_t r = r0; r < r1; ++r) {
         const int t = b.t0 + (int)(r / b.bh());
         const int h = b.h0 + (int)(r % b.bh());
         const T* row = x + ((((int64_t)n * Tn + t) * H + h) * W + b.w0) * C;
-        for (int e = tid; e < seg; e += kThreads) {
+        int e = tid;
+        if (!have_shift && e < seg) {
             const uint4 raw = *reinterpret_cast<const uint4*>(row + (int64_t)e * V);
             const T* v = reinterpret_cast<const T*>(&raw);
-            cnt += 1.0f;
-            const float inv = 1.0f / cnt;
+#pragma unroll
+            for (int k = 0; k < V; ++k) shift[k] = Elem<T>::load(v + k);
+            have_shift = true;
+        }
+        for (; e + (kUnroll - 1) * kThreads < seg; e += kUnroll * kThreads) {
+            uint4 raw[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                raw[u] = *reinterpret_cast<const uint4*>(row + (int64_t)(e + u * kThreads) * V);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const T* v = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float d = Elem<T>::load(v + k) - shift[k];
+                    s1[k] += d;
+                    s2[k] = fmaf(d, d, s2[k]);
+                }
+            }
+            cnt += (float)kUnroll;
+        }
+        for (; e < seg; e += kThreads) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(row + (int64_t)e * V);
+            const T* v = reinterpret_cast<const T*>(&raw);
 #pragma unroll
             for (int k = 0; k < V; ++k) {
-                const float xv = Elem<T>::load(v + k);
-                const float d = xv - mean[k];
-                mean[k] += d * inv;
-                m2[k] += d * (xv - mean[k]);
+                const float d = Elem<T>::load(v + k) - shift[k];
+                s1[k] += d;
+                s2[k] = fmaf(d, d, s2[k]);
             }
+            cnt += 1.0f;
         }
+    }
+
+    // per-channel (mean, M2) of this thread
+    float mean[V], m2[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const float mk = cnt > 0.0f ? s1[k] / cnt : 0.0f;
+        mean[k] = shift[k] + mk;
+        m2[k] = fmaxf(s2[k] - s1[k] * mk, 0.0f);
     }
 
     // Per-thread group partials. Thread tid always sees channels [(tid % CV) * V, +V).
@@ -233,9 +272,9 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(const double* __r
 }
 
 // grid (groups, N). part: [n_parts][N][G][3].
-__global__ __launch_bounds__(kThreads) void gn_combine_kernel(const double* __restrict__ part,
-                                                              int32_t n_parts, int32_t groups,
-                                                              float eps, float* mean_rstd) {
+__global__ __launch_bounds__(64) void gn_combine_kernel(const double* __restrict__ part,
+                                                        int32_t n_parts, int32_t groups, float eps,
+                                                        float* mean_rstd) {
     const int g = blockIdx.x, n = blockIdx.y, N = gridDim.y;
     Moments m{0.0, 0.0, 0.0};
     if (threadIdx.x == 0) {
@@ -249,40 +288,66 @@ __global__ __launch_bounds__(kThreads) void gn_combine_kernel(const double* __re
     }
 }
 
-// grid (rows of the box, N): one block per contiguous row segment.
-template <typename T>
+// grid (rows of the box, N): one block per contiguous row segment. V input elements (16 bytes)
+// per thread per step; the channel vector of a thread is fixed because CV divides 256.
+template <typename TI, typename TO>
 __global__ __launch_bounds__(kThreads) void gn_apply_kernel(
-    const T* x, T* y, int32_t Tn, int32_t H, int32_t W, int32_t C, int32_t groups, Box b,
+    const TI* x, TO* y, int32_t Tn, int32_t H, int32_t W, int32_t C, int32_t groups, Box b,
     const float* __restrict__ mean_rstd, const float* __restrict__ gamma,
     const float* __restrict__ beta, int32_t silu) {
-    constexpr int V = Elem<T>::kVec;
+    constexpr int V = Elem<TI>::kVec;
     const int n = blockIdx.y;
     const int64_t r = blockIdx.x;
     const int t = b.t0 + (int)(r / b.bh());
     const int h = b.h0 + (int)(r % b.bh());
     const int64_t off = ((((int64_t)n * Tn + t) * H + h) * W + b.w0) * C;
-    const T* xr = x + off;
-    T* yr = y + off;
+    const TI* xr = x + off;
+    TO* yr = y + off;
     const int CV = C / V;
     const int seg = (int)b.bw() * CV;
     const int cpg = C / groups;
     const float* mr = mean_rstd + (int64_t)n * groups * 2;
+    const int c0 = (threadIdx.x % CV) * V;
+    float sc[V], sh[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int c = c0 + k;
+        const int g = c / cpg;
+        const float gm = gamma ? gamma[c] : 1.0f;
+        const float bt = beta ? beta[c] : 0.0f;
+        sc[k] = mr[2 * g + 1] * gm;
+        sh[k] = bt - mr[2 * g] * sc[k];
+    }
     for (int e = threadIdx.x; e < seg; e += kThreads) {
-        const int c0 = (e % CV) * V;
-        uint4 raw = *reinterpret_cast<const uint4*>(xr + (int64_t)e * V);
-        T* v = reinterpret_cast<T*>(&raw);
+        const uint4 raw = *reinterpret_cast<const uint4*>(xr + (int64_t)e * V);
+        const TI* v = reinterpret_cast<const TI*>(&raw);
+        TO out[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            const int c = c0 + k;
-            const int g = c / cpg;
-            float z = (Elem<T>::load(v + k) - mr[2 * g]) * mr[2 * g + 1];
-            if (gamma) z *= gamma[c];
-            if (beta) z += beta[c];
-            if (silu) z = z / (1.0f + __expf(-z));
-            Elem<T>::store(v + k, z);
+            float z = fmaf(Elem<TI>::load(v + k), sc[k], sh[k]);
+            if (silu) z = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+            Elem<TO>::store(out + k, z);
         }
-        *reinterpret_cast<uint4*>(yr + (int64_t)e * V) = raw;
+        if constexpr (sizeof(TO) * V == 16) {
+            *reinterpret_cast<uint4*>(yr + (int64_t)e * V) = *reinterpret_cast<const uint4*>(out);
+        } else if constexpr (sizeof(TO) * V == 8) {
+            *reinterpret_cast<uint2*>(yr + (int64_t)e * V) = *reinterpret_cast<const uint2*>(out);
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) yr[(int64_t)e * V + k] = out[k];
+        }
     }
+}
+
+template <typename TI, typename TO>
+void apply_launch(const vae_tensor_t& x, const Box& box, int32_t groups, const float* mean_rstd,
+                  const float* gamma, const float* beta, bool silu, const vae_tensor_t& y,
+                  hipStream_t stream) {
+    dim3 grid((unsigned)(box.bt() * box.bh()), (unsigned)x.n);
+    hipLaunchKernelGGL((gn_apply_kernel<TI, TO>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const TI*>(x.data), static_cast<TO*>(y.data), (int32_t)x.t,
+                       (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, groups, box, mean_rstd, gamma,
+                       beta, (int32_t)silu);
 }
 
 }  // namespace
@@ -333,17 +398,15 @@ vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t grou
                              const float* mean_rstd, const float* gamma, const float* beta,
                              bool silu, const vae_tensor_t& y, hipStream_t stream) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
-    dim3 grid((unsigned)(box.bt() * box.bh()), (unsigned)x.n);
-    if (x.dtype == VAE_DTYPE_BF16)
-        hipLaunchKernelGGL(gn_apply_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
-                           static_cast<const uint16_t*>(x.data), static_cast<uint16_t*>(y.data),
-                           (int32_t)x.t, (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, groups, box,
-                           mean_rstd, gamma, beta, (int32_t)silu);
+    const bool xb = x.dtype == VAE_DTYPE_BF16, yb = y.dtype == VAE_DTYPE_BF16;
+    if (xb && yb)
+        apply_launch<uint16_t, uint16_t>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
+    else if (xb)
+        apply_launch<uint16_t, float>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
+    else if (yb)
+        apply_launch<float, uint16_t>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
     else
-        hipLaunchKernelGGL(gn_apply_kernel<float>, grid, dim3(kThreads), 0, stream,
-                           static_cast<const float*>(x.data), static_cast<float*>(y.data),
-                           (int32_t)x.t, (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, groups, box,
-                           mean_rstd, gamma, beta, (int32_t)silu);
+        apply_launch<float, float>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }

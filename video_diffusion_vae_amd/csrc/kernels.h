@@ -15,10 +15,10 @@ struct BoxList {
 };
 
 // ---- convolution ----
-vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, const float* bias,
-                           const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                           hipStream_t stream);
-bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y);
+vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
+                           const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
+                           const Box& box, int32_t flags, hipStream_t stream);
+bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype);
 
 // ---- group norm ----
 // Workspace: per-block partials of every box, fp64 [blocks][N][G][3].

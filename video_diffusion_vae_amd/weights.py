@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from ._binding import Decoder, VAE_DTYPE_BF16, VAE_DTYPE_F32
+from ._binding import Decoder, VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DECODE_SPLIT_FP32_OPERANDS
 
 
 def conv_weight_layout(w, dtype, device):
@@ -20,11 +20,13 @@ def conv_weight_layout(w, dtype, device):
     return t.to(device=device, dtype=dtype)
 
 
-def upload_decoder(spec: dict, params: list, device="cuda"):
+def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", split=True):
     """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
 
     Each parameter dict is {"kind": "conv", "w", "b"} or {"kind": "gn", "gamma", "beta"} holding
-    host arrays. Returns the Decoder; it keeps the device tensors alive.
+    host arrays. ``act_dtype`` is the storage dtype of the activations between ops ("f32" or
+    "bf16"). ``split`` applies fp32 conv inputs as hi + lo bf16 operands
+    (VAE_DECODE_SPLIT_FP32_OPERANDS). Returns the Decoder; it keeps the device tensors alive.
     """
     import torch
     tdt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
@@ -37,4 +39,7 @@ def upload_decoder(spec: dict, params: list, device="cuda"):
             flat.append(torch.as_tensor(np.asarray(p["gamma"], np.float32)).to(device))
             flat.append(torch.as_tensor(np.asarray(p["beta"], np.float32)).to(device))
     code = VAE_DTYPE_BF16 if spec["dtype"] == "bf16" else VAE_DTYPE_F32
-    return Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat)
+    act = VAE_DTYPE_BF16 if act_dtype == "bf16" else VAE_DTYPE_F32
+    flags = VAE_DECODE_SPLIT_FP32_OPERANDS if (split and code == VAE_DTYPE_BF16) else 0
+    return Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat,
+                   act_dtype=act, flags=flags)
