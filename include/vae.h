@@ -106,19 +106,30 @@ VAE_API int32_t vae_version(void);
  *  bias: [Cout] fp32 (device), or NULL.
  *  residual: tensor of y's shape and dtype added to the result, or NULL. It may alias y.
  *  y: [N,T,H,W,Cout] output, bf16 or fp32. It must not overlap x.
- *  flags: 0, or VAE_CONV_SPLIT_FP32.
+ *  flags: 0, or a combination of VAE_CONV_SPLIT_FP32 and VAE_CONV_PACKED_WEIGHTS (weight is then
+ *         the fragment-packed copy written by vae_conv_weight_pack; MFMA path only).
  * bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (MFMA). Products
  * accumulate in fp32. An fp32 x is rounded to bf16 (nearest-even) as the operand, or, with
  * VAE_CONV_SPLIT_FP32, applied as two bf16 operands hi = bf16(x) and lo = bf16(x - hi). The split
  * keeps about 16 significant bits of x and costs twice the matrix-core work. Every other case runs
  * on a direct fp32-accumulating path, where the flag changes nothing.
  */
-enum { VAE_CONV_SPLIT_FP32 = 1 };
+enum { VAE_CONV_SPLIT_FP32 = 1, VAE_CONV_PACKED_WEIGHTS = 2 };
 VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
                                        int32_t weight_dtype, const float* bias,
                                        const vae_tensor_t* residual, vae_tensor_t* y,
                                        const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream);
+
+/* Fragment-packed copy of bf16 conv weights, for the MFMA path. Layout:
+ * [ceil(Cout/32)][27 taps][Cin/32][2][32][2][8], i.e. output channels in tiles of 32 and input
+ * channels in chunks of 32, ordered so that each 16-byte matrix-core operand fragment of a
+ * wavefront is one contiguous 1 KB read. Cout is padded to a multiple of 32 with zeros; requires
+ * Cin % 32 == 0. The caller owns `packed` (device, vae_conv_weight_pack_size bytes).
+ * Layout-only: the packed convolution computes exactly what the standard layout does. */
+VAE_API vae_status_t vae_conv_weight_pack_size(int32_t cout, int32_t cin, size_t* bytes);
+VAE_API vae_status_t vae_conv_weight_pack(const void* weight, int32_t cout, int32_t cin,
+                                          void* packed, vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* GroupNorm (+SiLU) with statistics merged across patches                                    */
@@ -303,6 +314,14 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
                                         const void* const* params, int32_t n_ptrs,
                                         vae_decoder_t** out);
 VAE_API void vae_decoder_destroy(vae_decoder_t* dec);
+
+/* Optional fragment-packed weights for the decoder's MFMA convs. The caller supplies a device
+ * buffer of vae_decoder_packed_weight_size bytes, which must outlive the decoder. The pack is
+ * enqueued on `stream`, and later decodes read the packed copies instead of the standard ones.
+ * The results are identical; the packed copies are faster to load. */
+VAE_API vae_status_t vae_decoder_packed_weight_size(const vae_decoder_t* dec, size_t* bytes);
+VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, size_t bytes,
+                                              vae_stream_t stream);
 
 /* Device scratch needed by vae_decode_tiled for this tiling (latent extents come from desc). */
 VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,

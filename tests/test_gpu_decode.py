@@ -173,3 +173,21 @@ def test_bf16_activation_storage_variant(v):
     got = host(gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16"))
     ref = oracle_out("ltx2_tiny", "whole")
     assert psnr(got, ref) >= 50.0
+
+
+def test_packed_and_standard_weights_decode_identically(v):
+    import torch
+    spec = vae_synth.LTX2_TINY
+    z = ndhwc(vae_synth.latent(spec))
+    zd = dev(z, "bf16")
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 2))
+    outs = []
+    for packed in (False, True):
+        dec = v.upload_decoder(spec, params_of("ltx2_tiny"), packed=packed)
+        ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
+        out = torch.empty(oracle.output_shape(spec, z.shape), dtype=torch.float32, device="cuda")
+        dec.vae_decode_tiled(zd, desc, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+        dec.close()
+    assert torch.equal(outs[0], outs[1])

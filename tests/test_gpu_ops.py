@@ -295,3 +295,25 @@ def test_tile_merge_matches_oracle(v, grid):
         v.vae_tile_merge(dev(outs[k], "f32"), tl, desc, out, flags)
     torch.cuda.synchronize()
     assert rel_max_abs(host(out), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("case", [((1, 3, 9, 19), 64, 256, "bf16"), ((2, 2, 8, 16), 32, 48, "f32"),
+                                  ((1, 2, 8, 16), 128, 52, "f32"), ((1, 5, 10, 12), 96, 128, "bf16")])
+def test_conv3d_packed_weights_bitwise_equal(v, case):
+    """Packed weights only change the load layout: the result must be bitwise identical to the
+    standard layout, and match the oracle."""
+    import torch
+    (n, t, h, w), cin, cout, idt = case
+    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 60 + cout)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    packed = v.vae_conv_weight_pack(wd)
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    y0 = torch.empty((n, t, h, w, cout), device="cuda", dtype=torch.float32)
+    y1 = torch.empty_like(y0)
+    xd = dev(x, idt)
+    v.vae_conv3d_causal(xd, wd, bd, None, y0)
+    v.vae_conv3d_causal(xd, packed.view(torch.bfloat16), bd, None, y1,
+                        flags=v.VAE_CONV_PACKED_WEIGHTS)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert rel_max_abs(host(y1), oracle.causal_conv3d(x, wt, b)) <= 1e-4

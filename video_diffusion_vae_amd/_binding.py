@@ -16,7 +16,7 @@ VAE_DTYPE_BF16, VAE_DTYPE_F32 = 1, 2
 VAE_UPSAMPLE_NEAREST, VAE_UPSAMPLE_D2S = 1, 2
 VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
-VAE_CONV_SPLIT_FP32 = 1
+VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS = 1, 2
 VAE_DECODE_SPLIT_FP32_OPERANDS = 1
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
 VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
@@ -24,6 +24,8 @@ VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
 # Every symbol include/vae.h declares.
 EXPORTS = (
     "vae_last_error", "vae_last_error_info", "vae_version", "vae_conv3d_causal",
+    "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_decoder_packed_weight_size",
+    "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_upsample",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
@@ -80,7 +82,7 @@ class vae_op_timing_t(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m video_diffusion_vae_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python video_diffusion_vae_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     T = ctypes.POINTER(vae_tensor_t)
@@ -91,6 +93,10 @@ def _load():
         "vae_last_error_info": ([ctypes.POINTER(vae_error_info_t)], I32),
         "vae_version": ([], I32),
         "vae_conv3d_causal": ([T, P, I32, P, T, T, B, I32, P], I32),
+        "vae_conv_weight_pack_size": ([I32, I32, ctypes.POINTER(SZ)], I32),
+        "vae_conv_weight_pack": ([P, I32, I32, P, P], I32),
+        "vae_decoder_packed_weight_size": ([P, ctypes.POINTER(SZ)], I32),
+        "vae_decoder_pack_weights": ([P, P, SZ, P], I32),
         "vae_groupnorm_silu_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_groupnorm_silu": ([T, B, I32, I32, F, P, P, I32, T, P, SZ, P], I32),
         "vae_groupnorm_stats_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
@@ -202,6 +208,17 @@ def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, strea
                                  _ref(rd), ctypes.byref(yd), _ref(box(out_box)), int(flags),
                                  _stream(stream)))
     return y
+
+
+def vae_conv_weight_pack(weight, stream=None):
+    """Fragment-packed copy of a bf16 [Cout, 3, 3, 3, Cin] device weight (a new uint8 tensor)."""
+    import torch
+    cout, cin = weight.shape[0], weight.shape[-1]
+    n = ctypes.c_size_t()
+    _check(LIB.vae_conv_weight_pack_size(cout, cin, ctypes.byref(n)))
+    packed = torch.empty(n.value, dtype=torch.uint8, device=weight.device)
+    _check(LIB.vae_conv_weight_pack(_ptr(weight), cout, cin, _ptr(packed), _stream(stream)))
+    return packed
 
 
 def _boxes(boxes):
@@ -338,6 +355,15 @@ class Decoder:
 
     def __del__(self):
         self.close()
+
+    def pack_weights(self, device, stream=None):
+        """Allocate the packed-weight buffer (kept alive by the decoder) and pack into it."""
+        import torch
+        n = ctypes.c_size_t()
+        _check(LIB.vae_decoder_packed_weight_size(self._h, ctypes.byref(n)))
+        self._packed = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+        _check(LIB.vae_decoder_pack_weights(self._h, _ptr(self._packed), self._packed.numel(),
+                                            _stream(stream)))
 
     def workspace_size(self, desc):
         n = ctypes.c_size_t()

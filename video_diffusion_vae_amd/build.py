@@ -1,4 +1,4 @@
-"""Build libvae_mi355x.so (gfx950) in-tree: ``python -m video_diffusion_vae_amd.build``.
+"""Build libvae_mi355x.so (gfx950) in-tree: ``python video_diffusion_vae_amd/build.py``.
 
 Each HIP source under csrc/ is compiled to an object under _build/ in parallel, then all objects
 are linked into video_diffusion_vae_amd/libvae_mi355x.so. The build always recompiles.

@@ -237,7 +237,8 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
                                        const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream) {
     clear_error();
-    if (flags & ~VAE_CONV_SPLIT_FP32) return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
+    if (flags & ~(VAE_CONV_SPLIT_FP32 | VAE_CONV_PACKED_WEIGHTS))
+        return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
     VAE_TRY(check_tensor(x, "x"));
     VAE_TRY(check_tensor(y, "y"));
     if (!weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
@@ -254,8 +255,32 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
     }
     if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
     VAE_TRY(check_box(out_box, *y, "out_box"));
+    if ((flags & VAE_CONV_PACKED_WEIGHTS) && !conv_uses_mfma(*x, *y, weight_dtype))
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x->c,
+                    32);
     return launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, to_box(out_box, *y), flags,
                          as_stream(stream));
+}
+
+VAE_API vae_status_t vae_conv_weight_pack_size(int32_t cout, int32_t cin, size_t* bytes) {
+    clear_error();
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");
+    if (cout < 1 || cin < 1) return fail(VAE_ERR_INVALID_ARG, "cout and cin must be >= 1");
+    if (cin % 32) return fail(VAE_ERR_UNSUPPORTED, "packing needs Cin % 32 == 0", 4, cin, 32);
+    *bytes = (size_t)packed_weight_elems(cout, cin) * 2;
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_conv_weight_pack(const void* weight, int32_t cout, int32_t cin,
+                                          void* packed, vae_stream_t stream) {
+    clear_error();
+    if (!weight || !packed) return fail(VAE_ERR_INVALID_ARG, "weight or packed is NULL");
+    if (cout < 1 || cin < 1) return fail(VAE_ERR_INVALID_ARG, "cout and cin must be >= 1");
+    if (cin % 32) return fail(VAE_ERR_UNSUPPORTED, "packing needs Cin % 32 == 0", 4, cin, 32);
+    if (reinterpret_cast<uintptr_t>(packed) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+    return launch_pack_weights(weight, cout, cin, packed, as_stream(stream));
 }
 
 VAE_API vae_status_t vae_groupnorm_stats_workspace(const vae_tensor_t* x, const vae_box_t* boxes,

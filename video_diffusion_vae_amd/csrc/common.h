@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/vae.h"
+#include "vae.h"
 
 namespace vae {
 

@@ -2,25 +2,27 @@
 //
 // bf16 weights: implicit GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //  - GEMM view: M = output positions, N = Cout, K = 27 * Cin, ordered (channel chunk, tap).
-//  - One workgroup computes a 2 x 8 x 16 (T x H x W) block of 256 output positions for NT
-//    output channels.
-//  - For each 32-channel chunk it stages the block's input tile in LDS once: 4 x 10 x 18 positions
-//    x 32 channels, i.e. the block, its one-row halo on each spatial side, and the two earlier
-//    frames. All 27 taps then read their A operands from that tile at shifted offsets. The halo
-//    and the causal frame clamp are thus resolved while the tile is loaded: the halo is the
-//    neighbouring data of the same tensor, read in place; rows outside the image become zeros; a
-//    frame index below 0 reads frame 0. The pages motivate this: a halo built by concatenation
-//    cost 1.31x ("[TRTLLM-14123][feat] add ParallelVAE_TrtllmWan for native Wan VAE",
-//    Description).
+//  - One workgroup (8 waves) computes a block of 256 output positions for NT output channels.
+//    The block is TB x HB x WB positions (2x8x16, 4x8x8 or 4x4x16, whichever pads the box least).
+//    Each wave owns 32 output channels and 256 * 32 / NT positions (32x32 MFMA tiles). Its 64
+//    accumulator registers leave room for four waves per SIMD, enough to hide L2 latency.
+//  - Input (A operand). For each 32-channel chunk the block's input tile is staged in LDS once:
+//    (TB+2) x (HB+2) x (WB+2) positions x 32 channels, i.e. the block, a one-row halo on each
+//    spatial side, and the two earlier frames. All 27 taps read their A fragments from that tile
+//    at shifted offsets. The halo and the causal frame clamp are resolved while the tile is
+//    loaded: the halo is the neighbouring data of the same tensor, read in place; rows outside
+//    the image become zeros; a frame index below 0 reads frame 0. The pages motivate this: a halo
+//    built by concatenation cost 1.31x ("[TRTLLM-14123][feat] add ParallelVAE_TrtllmWan for native
+//    Wan VAE", Description). LDS rows are padded from 64 to 80 bytes, so the 16-byte reads of
+//    8 consecutive lanes hit 8 distinct 16-byte bank groups.
+//  - Weights (B operand). They go straight from global memory (L2-resident per XCD) into
+//    registers in MFMA fragment order, prefetched one tap ahead. The tap loop therefore has no
+//    barriers and LDS carries only A.
 //  - fp32 inputs are rounded to bf16 (nearest-even) as they are staged, because MFMA operands are
 //    bf16. Accumulation is fp32. With the split flag an fp32 input is applied as two bf16
 //    operands, hi = bf16(x) and lo = bf16(x - hi). The K loop visits every channel chunk twice,
 //    about 16 significant bits of x reach the matrix cores, and the MFMA work doubles.
-//  - The weights of the next tap are prefetched into registers while the current tap runs, and
-//    double-buffered in LDS.
-//  - LDS rows are padded from 64 to 80 bytes, so the 16-byte operand reads of 8 consecutive
-//    lanes hit 8 distinct 16-byte bank groups.
-//  - Epilogue: each wave parks one 32 x WN accumulator tile at a time in LDS (reusing the input
+//  - Epilogue: each wave parks one 32 x 32 accumulator tile at a time in LDS (reusing the input
 //    tile), then every lane writes four consecutive channels with one 16-byte (fp32) or 8-byte
 //    (bf16) store. Bias and residual are added on the way.
 //  - Workgroups are ordered output-channel tile slowest, and remapped so that each XCD (the
@@ -35,12 +37,10 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
-constexpr int kTB = 2, kHB = 8, kWB = 16;            // output block (T, H, W)
-constexpr int kHT = kTB + 2, kHH = kHB + 2, kHW = kWB + 2;
-constexpr int kHaloPos = kHT * kHH * kHW;            // 720 input positions per block
 constexpr int kCK = 32;                              // input channels per LDS chunk
 constexpr int kRow = kCK * 2 + 16;                   // padded LDS row, bytes
-constexpr int kThreads = 256;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaThreads = kMfmaWaves * 64;
 constexpr int kXcds = 8;
 
 struct MfmaArgs {
@@ -118,14 +118,38 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const 
     *reinterpret_cast<uint2*>(p) = a;
 }
 
-template <int NT, typename TI, typename TO, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t halo[kHaloPos * kRow];
-    __shared__ __attribute__((aligned(16))) uint8_t bbuf[2][NT * kRow];
+// Staged input tile: (TB+2) x (HB+2) rows of (WB+2) positions, 80 bytes per position. The row
+// pitch is chosen for conflict-free 16-byte A-fragment reads. A fragment read covers
+//  - 16 positions of one row plus 16 of the next (WB = 16), or
+//  - 8 positions of each of four rows (WB = 8).
+// Measured with the LDS bank-conflict counter on gfx950, such reads are conflict-free only when
+// the row pitch is 0 mod 256 bytes (WB = 16) or 128 mod 256 bytes (WB = 8). The pitch is 1536 or
+// 896 bytes.
+template <int TB, int HB, int WB>
+struct BlockShape {
+    static_assert(TB * HB * WB == 256, "a block is 256 output positions");
+    static constexpr int HT = TB + 2, HH = HB + 2, HW = WB + 2;
+    static constexpr int kPos = HT * HH * HW;       // input positions staged per chunk
+    static constexpr int kPitch = WB == 16 ? 1536 : 896;
+    static_assert(HW * kRow <= kPitch, "a row must fit its pitch");
+    static constexpr int kBytes = HT * HH * kPitch;
+};
 
-    constexpr int WN = NT / 2;        // output channels per wave
-    constexpr int NJ = WN / 32;       // 32-wide MFMA column tiles per wave
-    constexpr int BU = NT * 4 / kThreads;  // 16-byte weight units per thread per tap
+template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
+__global__ __launch_bounds__(kMfmaThreads, 4)
+void conv3d_mfma_kernel(MfmaArgs a) {
+    using S = BlockShape<TB, HB, WB>;
+    constexpr int HH = S::HH, HW = S::HW;
+    constexpr int RP = S::kPitch;
+    __shared__ __attribute__((aligned(16))) uint8_t halo[S::kBytes];
+
+    // 8 waves: WNN of them across the NT output channels (32 each), WM across the 256 positions.
+    constexpr int WNN = NT / 32;
+    constexpr int WM = kMfmaWaves / WNN;
+    constexpr int MW = 256 / WM;       // positions per wave
+    constexpr int MI = MW / 32;        // 32-row MFMA tiles per wave
+    constexpr int NB = 2;              // weight fragments are prefetched one tap ahead
+    static_assert(WNN * WM == kMfmaWaves && MI >= 1, "wave grid");
 
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = logical / a.n_mblocks;
@@ -136,141 +160,132 @@ __global__ __launch_bounds__(kThreads, 2) void conv3d_mfma_kernel(MfmaArgs a) {
     mb /= a.nbh;
     const int bt_i = mb % a.nbt;
     const int n = mb / a.nbt;
-    const int t_blk = a.box.t0 + bt_i * kTB;
-    const int h_blk = a.box.h0 + bh_i * kHB;
-    const int w_blk = a.box.w0 + bw_i * kWB;
+    const int t_blk = a.box.t0 + bt_i * TB;
+    const int h_blk = a.box.h0 + bh_i * HB;
+    const int w_blk = a.box.w0 + bw_i * WB;
     const int n_blk = nt * NT;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wave_m = wave >> 1;     // frame of the block this wave computes
-    const int wave_n = wave & 1;
+    const int wave_m = wave / WNN;    // which MW of the block's 256 positions
+    const int wave_n = wave % WNN;    // which 32 of the NT output channels
     const int lrow = lane & 31;
     const int khalf = lane >> 5;      // which 8 of the 16 k values this lane feeds
 
     const int64_t cin = a.cin;
     const TI* xn = static_cast<const TI*>(a.x) + (int64_t)n * a.T * a.H * a.W * cin;
 
-    f32x16_t acc[4][NJ];
+    f32x16_t acc[MI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
-    // halo position of this lane's output row for sub-tile 0, tap (0,0,0)
-    const int a_base = (wave_m * kHH + (lrow >> 4)) * kHW + (lrow & 15);
-
-    uint4 breg[BU];
-    auto load_b = [&](int tap, int c0) {
+    // LDS byte offset of this lane's A row (tap 0,0,0) in each of the MI sub-tiles
+    int a_off[MI];
 #pragma unroll
-        for (int k = 0; k < BU; ++k) {
-            int u = tid + k * kThreads;
-            int row = u >> 2, g = u & 3;
-            int co = n_blk + row;
+    for (int i = 0; i < MI; ++i) {
+        const int m = wave_m * MW + i * 32 + lrow;
+        const int tb = m / (HB * WB), hb = (m / WB) % HB, wb = m % WB;
+        a_off[i] = (tb * HH + hb) * RP + wb * kRow + khalf * 16;
+    }
+    // This lane's weights: B column lrow of the wave's 32-channel tile, k half `khalf`.
+    // Standard layout [Cout][27][Cin]: 16 bytes of one weight row per fragment.
+    // Packed layout (see pack_weights_kernel): the 64 lanes of a fragment read 1 KB contiguously.
+    const int nch = a.cin / kCK;
+    const int co_tile = n_blk + wave_n * 32;
+    const bool b_ok = PACKED ? co_tile < a.cout : co_tile + lrow < a.cout;
+    const uint16_t* b_ptr =
+        PACKED ? a.w + (int64_t)(b_ok ? co_tile >> 5 : 0) * 27 * nch * 1024 + lrow * 16 + khalf * 8
+               : a.w + (int64_t)(b_ok ? co_tile + lrow : 0) * 27 * cin + khalf * 8;
+    uint4 bq[NB][2];
+    auto load_b = [&](int buf, int tap, int c0) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (co < a.cout)
-                v = *reinterpret_cast<const uint4*>(a.w + ((int64_t)co * 27 + tap) * cin + c0 + g * 8);
-            breg[k] = v;
-        }
-    };
-    auto store_b = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < BU; ++k) {
-            int u = tid + k * kThreads;
-            int row = u >> 2, g = u & 3;
-            *reinterpret_cast<uint4*>(&bbuf[buf][row * kRow + g * 16]) = breg[k];
+            const int64_t off = PACKED ? ((int64_t)tap * nch + (c0 >> 5)) * 1024 + kk * 512
+                                       : (int64_t)tap * cin + c0 + kk * 16;
+            if (b_ok) v = *reinterpret_cast<const uint4*>(b_ptr + off);
+            bq[buf][kk] = v;
         }
     };
 
-    const int n_passes = (a.cin / kCK) * (SPLIT ? 2 : 1);
+    const int n_passes = nch * (SPLIT ? 2 : 1);
     for (int kc = 0; kc < n_passes; ++kc) {
         const int c0 = (SPLIT ? (kc >> 1) : kc) * kCK;
         const bool lo = SPLIT && (kc & 1);
-        __syncthreads();  // the previous chunk's LDS reads are done
-        for (int u = tid; u < kHaloPos * 4; u += kThreads) {
-            int pos = u >> 2, g = u & 3;
-            int f = pos / (kHH * kHW);
-            int rem = pos - f * (kHH * kHW);
-            int r = rem / kHW;
-            int c = rem - r * kHW;
+        load_b(0, 0, c0);             // in flight while the input tile is staged
+        __syncthreads();              // the previous chunk's LDS reads are done
+        for (int u = tid; u < S::kPos * 4; u += kMfmaThreads) {
+            const int pos = u >> 2, g = u & 3;
+            const int f = pos / (HH * HW);
+            const int rem = pos - f * (HH * HW);
+            const int r = rem / HW;
+            const int c = rem - r * HW;
             int tg = t_blk - 2 + f;
             tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
-            int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
+            const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
             uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
             if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
                 const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
                 v = lo ? load8_lo<TI>(src) : load8<TI>(src);
             }
-            *reinterpret_cast<uint4*>(&halo[pos * kRow + g * 16]) = v;
+            *reinterpret_cast<uint4*>(&halo[(f * HH + r) * RP + c * kRow + g * 16]) = v;
         }
-        load_b(0, c0);
-        store_b(0);
         __syncthreads();
 
+#pragma unroll
         for (int tap = 0; tap < 27; ++tap) {
-            if (tap + 1 < 27) load_b(tap + 1, c0);
+            if (tap + 1 < 27) load_b((tap + 1) % NB, tap + 1, c0);
             const int kt = tap / 9, kh = (tap / 3) % 3, kw = tap % 3;
-            const uint8_t* bb = bbuf[tap & 1];
-            const int a_tap = a_base + (kt * kHH + kh) * kHW + kw;
+            const int tap_off = (kt * HH + kh) * RP + kw * kRow;
+            const int buf = tap % NB;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const int goff = (kk * 2 + khalf) * 16;
-                bf16x8_t bf[NJ];
+                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[buf][kk]);
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    bf[j] = *reinterpret_cast<const bf16x8_t*>(
-                        bb + (wave_n * WN + j * 32 + lrow) * kRow + goff);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
-                        &halo[(a_tap + i * 2 * kHW) * kRow + goff]);
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j],
-                                                                            0, 0, 0);
+                for (int i = 0; i < MI; ++i) {
+                    const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
+                        &halo[a_off[i] + tap_off + kk * 32]);
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[i], 0, 0, 0);
                 }
             }
-            if (tap + 1 < 27) store_b((tap + 1) & 1);
-            __syncthreads();
         }
     }
+    __syncthreads();  // the input tile is reused for the epilogue
 
     // Epilogue. In a 32x32 accumulator tile, lane l holds column l % 32 and register r holds
-    // row (r / 4) * 8 + (l / 32) * 4 + r % 4. Each wave parks one 32 x WN sub-tile at a time in
-    // its own slice of the (now idle) input tile, then reads rows back four channels per lane.
-    constexpr int EP = WN + 4;                      // padded staging row, floats
-    constexpr int LPR = WN / 4;                     // lanes per staged row
+    // row (r / 4) * 8 + (l / 32) * 4 + r % 4. Each wave parks one 32 x 32 tile at a time in its
+    // own slice of the (now idle) input tile, then reads rows back four channels per lane.
+    constexpr int EP = 32 + 4;                      // padded staging row, floats
+    constexpr int LPR = 8;                          // lanes per staged row
     constexpr int RPP = 64 / LPR;                   // rows per pass
-    static_assert(4 * 32 * EP * 4 <= kHaloPos * kRow, "epilogue staging must fit the input tile");
+    static_assert(kMfmaWaves * 32 * EP * 4 <= S::kBytes, "epilogue staging must fit the tile");
     float* ep = reinterpret_cast<float*>(halo) + wave * (32 * EP);
     const TO* res = static_cast<const TO*>(a.res);
     TO* y = static_cast<TO*>(a.y);
-    const int t = t_blk + wave_m;
     const int c4 = (lane % LPR) * 4;
-    const int co = n_blk + wave_n * WN + c4;
+    const int co = co_tile + c4;
     float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (a.bias)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (co + k < a.cout) bv[k] = a.bias[co + k];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ep[((r >> 2) * 8 + khalf * 4 + (r & 3)) * EP + j * 32 + lrow] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r)
+            ep[((r >> 2) * 8 + khalf * 4 + (r & 3)) * EP + lrow] = acc[i][r];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int pass = 0; pass < 32 / RPP; ++pass) {
             const int row = pass * RPP + lane / LPR;
-            const int m = i * 32 + row;
-            const int h = h_blk + (m >> 4), w = w_blk + (m & 15);
+            const int m = wave_m * MW + i * 32 + row;
+            const int t = t_blk + m / (HB * WB);
+            const int h = h_blk + (m / WB) % HB, w = w_blk + m % WB;
             if (t < a.box.t1 && h < a.box.h1 && w < a.box.w1 && co < a.cout) {
                 float v[4];
 #pragma unroll
@@ -341,10 +356,28 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
     Elem<TO>::store(y + o, acc);
 }
 
-template <int NT, typename TI, typename TO, bool SPLIT>
-vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
-                      const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                      hipStream_t stream) {
+// Output-block shapes (T x H x W = 256 positions). The launch picks the one that wastes the
+// fewest MFMA rows on ragged block edges for the box: 16x22x40 takes 4x8x8 (9% waste instead of
+// 31%), 31x44x80 takes 4x4x16, and the larger stages take 2x8x16.
+enum BlockKind { kBlk2x8x16 = 0, kBlk4x8x8 = 1, kBlk4x4x16 = 2 };
+
+int64_t padded_volume(const Box& b, int tb, int hb, int wb) {
+    return ceil_div(b.bt(), tb) * tb * ceil_div(b.bh(), hb) * hb * ceil_div(b.bw(), wb) * wb;
+}
+
+BlockKind pick_block(const Box& b) {
+    const int64_t v0 = padded_volume(b, 2, 8, 16);
+    const int64_t v1 = padded_volume(b, 4, 8, 8);
+    const int64_t v2 = padded_volume(b, 4, 4, 16);
+    if (v1 < v0 && v1 <= v2) return kBlk4x8x8;
+    if (v2 < v0) return kBlk4x4x16;
+    return kBlk2x8x16;
+}
+
+template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
+vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
+                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                       hipStream_t stream) {
     MfmaArgs a;
     a.x = x.data;
     a.w = static_cast<const uint16_t*>(w);
@@ -357,36 +390,90 @@ vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
     a.cin = (int32_t)x.c;
     a.cout = (int32_t)y.c;
     a.box = box;
-    a.nbt = (int32_t)ceil_div(box.bt(), kTB);
-    a.nbh = (int32_t)ceil_div(box.bh(), kHB);
-    a.nbw = (int32_t)ceil_div(box.bw(), kWB);
+    a.nbt = (int32_t)ceil_div(box.bt(), TB);
+    a.nbh = (int32_t)ceil_div(box.bh(), HB);
+    a.nbw = (int32_t)ceil_div(box.bw(), WB);
     int64_t mblocks = x.n * (int64_t)a.nbt * a.nbh * a.nbw;
     int64_t total = mblocks * ceil_div(y.c, NT);
     if (total > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "conv3d: grid too large");
     a.n_mblocks = (int32_t)mblocks;
-    hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT>), dim3((unsigned)total),
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
+                       dim3((unsigned)total), dim3(kMfmaThreads), 0, stream, a);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
+}
+
+template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
+vae_status_t run_block(const vae_tensor_t& x, const void* w, const float* bias,
+                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                       hipStream_t stream) {
+    switch (pick_block(box)) {
+        case kBlk4x8x8:
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box,
+                                                                 stream);
+        case kBlk4x4x16:
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 4, 16>(x, w, bias, residual, y, box,
+                                                                  stream);
+        default:
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 2, 8, 16>(x, w, bias, residual, y, box,
+                                                                  stream);
+    }
+}
+
+template <int NT, typename TI, typename TO, bool SPLIT>
+vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
+                      const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                      bool packed, hipStream_t stream) {
+    if (packed) return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, stream);
+    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, stream);
 }
 
 template <int NT, typename TI, bool SPLIT>
 vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bias,
                           const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                          hipStream_t stream) {
+                          bool packed, hipStream_t stream) {
     if (y.dtype == VAE_DTYPE_F32)
-        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, stream);
-    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, stream);
+        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, stream);
+    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, stream);
 }
 
 template <int NT>
 vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                         bool split, hipStream_t stream) {
+                         bool split, bool packed, hipStream_t stream) {
     if (x.dtype == VAE_DTYPE_BF16)
-        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, stream);
-    if (split) return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, stream);
-    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, stream);
+        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, stream);
+    if (split) return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, packed, stream);
+    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, packed, stream);
+}
+
+// Fragment-packed weights: [Cout/32][27 taps][Cin/32 chunks][kk 2][32 co][khalf 2][8 ci] bf16,
+// Cout padded to a multiple of 32 with zeros. One 32 (co) x 32 (ci) block per (tap, chunk) is
+// 2 KB, ordered so that the 16-byte B fragment of lane l (column l % 32, k half l / 32) for
+// k step kk sits at byte kk * 1024 + (l % 32) * 32 + (l / 32) * 16: one contiguous 1 KB read per
+// fragment.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w,
+                                                           uint16_t* __restrict__ p, int32_t cout,
+                                                           int32_t cin, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int nch = cin / kCK;
+    int64_t q = i;
+    const int e = (int)(q % 8);
+    q /= 8;
+    const int khalf = (int)(q % 2);
+    q /= 2;
+    const int r = (int)(q % 32);
+    q /= 32;
+    const int kk = (int)(q % 2);
+    q /= 2;
+    const int chunk = (int)(q % nch);
+    q /= nch;
+    const int tap = (int)(q % 27);
+    const int cot = (int)(q / 27);
+    const int co = cot * 32 + r;
+    const int ci = chunk * kCK + kk * 16 + khalf * 8 + e;
+    p[i] = co < cout ? w[((int64_t)co * 27 + tap) * cin + ci] : (uint16_t)0;
 }
 
 template <typename TX, typename TW, typename TO>
@@ -420,16 +507,33 @@ bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight
     return weight_dtype == VAE_DTYPE_BF16 && x.c % kCK == 0 && y.c % 4 == 0;
 }
 
+int64_t packed_weight_elems(int64_t cout, int64_t cin) {
+    return ceil_div(cout, 32) * 32 * 27 * cin;
+}
+
+vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
+                                 hipStream_t stream) {
+    const int64_t total = packed_weight_elems(cout, cin);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(packed),
+                       cout, cin, total);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
                            const Box& box, int32_t flags, hipStream_t stream) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
     const bool xf = x.dtype == VAE_DTYPE_F32;
     const bool split = (flags & VAE_CONV_SPLIT_FP32) != 0;
+    const bool packed = (flags & VAE_CONV_PACKED_WEIGHTS) != 0;
     if (conv_uses_mfma(x, y, weight_dtype)) {
-        if (y.c >= 128) return run_mfma_in<128>(x, w, bias, residual, y, box, split, stream);
-        return run_mfma_in<64>(x, w, bias, residual, y, box, split, stream);
+        if (y.c >= 128)
+            return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, stream);
+        return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, stream);
     }
+    if (packed) return fail(VAE_ERR_UNSUPPORTED, "packed weights need the MFMA path");
     if (weight_dtype == VAE_DTYPE_F32)
         return xf ? run_direct_out<float, float>(x, w, bias, residual, y, box, stream)
                   : run_direct_out<uint16_t, float>(x, w, bias, residual, y, box, stream);

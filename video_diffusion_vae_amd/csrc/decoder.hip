@@ -22,6 +22,7 @@ struct vae_decoder {
     float eps = 0.0f;
     std::vector<vae_layer_desc_t> layers;
     std::vector<const void*> ptrs;
+    std::vector<const void*> packed;   // per entry of ptrs: packed copy of a conv weight or null
     bool timing = false;
     struct Rec {
         int32_t kind, layer, tile;
@@ -223,12 +224,17 @@ struct Runner {
         return mark(VAE_KIND_GN, layer, 0.0, 3.0 * b);
     }
 
-    vae_status_t conv(const vae_tensor_t& x, const void* w, const void* b,
-                      const vae_tensor_t* res, const vae_tensor_t& y, int layer) {
-        const int32_t cf =
-            (d->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) ? VAE_CONV_SPLIT_FP32 : 0;
-        VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(b), res, y, whole_box(y),
-                              cf, s));
+    // `wi` indexes d->ptrs: the conv's weight, followed by its bias.
+    vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
+                      const vae_tensor_t& y, int layer) {
+        int32_t cf = (d->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) ? VAE_CONV_SPLIT_FP32 : 0;
+        const void* w = d->ptrs[wi];
+        if (d->packed[wi]) {
+            w = d->packed[wi];
+            cf |= VAE_CONV_PACKED_WEIGHTS;
+        }
+        VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res, y,
+                              whole_box(y), cf, s));
         const double flops = 2.0 * 27.0 * (double)x.c * (double)y.c * (double)positions(y);
         const double bytes = (double)numel(x) * elem_size(x.dtype) +
                              (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
@@ -258,7 +264,7 @@ struct Runner {
             if (l.op == VAE_OP_CONV) {
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = last ? final_out : buf(nb, os);
-                VAE_TRY(conv(cur, d->ptrs[p], d->ptrs[p + 1], nullptr, y, layer));
+                VAE_TRY(conv(cur, p, nullptr, y, layer));
                 p += 2;
                 cur = y;
                 cur_buf = last ? -2 : nb;
@@ -272,10 +278,10 @@ struct Runner {
                 as.dtype = d->act_dtype;
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
-                VAE_TRY(conv(t1, d->ptrs[p + 2], d->ptrs[p + 3], nullptr, t2, layer));
+                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer));
                 VAE_TRY(gn(t2, t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
                 vae_tensor_t y = last ? final_out : t2;
-                VAE_TRY(conv(t1, d->ptrs[p + 6], d->ptrs[p + 7], &cur, y, layer));
+                VAE_TRY(conv(t1, p + 6, &cur, y, layer));
                 p += 8;
                 cur = y;
                 cur_buf = last ? -2 : b2;
@@ -357,6 +363,25 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
     }
     *L = layout_of(r);
     return VAE_OK;
+}
+
+// Visit every conv of the plan: fn(ptr index of its weight, cin, cout).
+template <typename F>
+void for_each_conv(const vae_decoder& d, F fn) {
+    size_t p = 0;
+    for (const vae_layer_desc_t& l : d.layers) {
+        if (l.op == VAE_OP_CONV) fn(p, l.cin, l.cout);
+        if (l.op == VAE_OP_RES) {
+            fn(p + 2, l.cin, l.cin);
+            fn(p + 6, l.cin, l.cin);
+        }
+        p += ptrs_for(l);
+    }
+}
+
+// Convs that run on the MFMA path (bf16 weights, Cin % 32 == 0, Cout % 4 == 0) are packable.
+bool packable(const vae_decoder& d, int32_t cin, int32_t cout) {
+    return d.dtype == VAE_DTYPE_BF16 && cin % 32 == 0 && cout % 4 == 0;
 }
 
 }  // namespace
@@ -452,6 +477,7 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
     d->eps = spec->eps;
     d->layers.assign(spec->layers, spec->layers + spec->n_layers);
     d->ptrs.assign(params, params + need);
+    d->packed.assign(need, nullptr);
     *out = d;
     return VAE_OK;
 }
@@ -460,6 +486,42 @@ VAE_API void vae_decoder_destroy(vae_decoder_t* dec) {
     if (!dec) return;
     for (hipEvent_t e : dec->events) (void)hipEventDestroy(e);
     delete dec;
+}
+
+VAE_API vae_status_t vae_decoder_packed_weight_size(const vae_decoder_t* dec, size_t* bytes) {
+    clear_error();
+    if (!dec || !bytes) return fail(VAE_ERR_INVALID_ARG, "NULL argument");
+    size_t total = 0;
+    for_each_conv(*dec, [&](size_t, int32_t cin, int32_t cout) {
+        if (packable(*dec, cin, cout)) total += align_up((size_t)packed_weight_elems(cout, cin) * 2, 256);
+    });
+    *bytes = total;
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, size_t bytes,
+                                              vae_stream_t stream) {
+    clear_error();
+    if (!dec) return fail(VAE_ERR_INVALID_ARG, "decoder is NULL");
+    size_t need = 0;
+    VAE_TRY(vae_decoder_packed_weight_size(dec, &need));
+    if (need > 0 && (!buf || bytes < need))
+        return fail(VAE_ERR_WORKSPACE, "packed weight buffer too small", -1, (int64_t)bytes, -1,
+                    (int64_t)need);
+    if (reinterpret_cast<uintptr_t>(buf) % 256 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "packed weight buffer must be 256-byte aligned");
+    uint8_t* out = static_cast<uint8_t*>(buf);
+    vae_status_t st = VAE_OK;
+    std::vector<const void*> packed(dec->ptrs.size(), nullptr);
+    for_each_conv(*dec, [&](size_t wi, int32_t cin, int32_t cout) {
+        if (st != VAE_OK || !packable(*dec, cin, cout)) return;
+        st = launch_pack_weights(dec->ptrs[wi], cout, cin, out, as_stream(stream));
+        packed[wi] = out;
+        out += align_up((size_t)packed_weight_elems(cout, cin) * 2, 256);
+    });
+    if (st != VAE_OK) return st;
+    dec->packed = packed;
+    return VAE_OK;
 }
 
 VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,

@@ -19,6 +19,10 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
                            const Box& box, int32_t flags, hipStream_t stream);
 bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype);
+// Fragment-packed bf16 weights (see conv3d.hip): element count and the packing kernel.
+int64_t packed_weight_elems(int64_t cout, int64_t cin);
+vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
+                                 hipStream_t stream);
 
 // ---- group norm ----
 // Workspace: per-block partials of every box, fp64 [blocks][N][G][3].

@@ -20,13 +20,15 @@ def conv_weight_layout(w, dtype, device):
     return t.to(device=device, dtype=dtype)
 
 
-def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", split=True):
+def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", split=True,
+                   packed=True):
     """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
 
     Each parameter dict is {"kind": "conv", "w", "b"} or {"kind": "gn", "gamma", "beta"} holding
     host arrays. ``act_dtype`` is the storage dtype of the activations between ops ("f32" or
     "bf16"). ``split`` applies fp32 conv inputs as hi + lo bf16 operands
-    (VAE_DECODE_SPLIT_FP32_OPERANDS). Returns the Decoder; it keeps the device tensors alive.
+    (VAE_DECODE_SPLIT_FP32_OPERANDS). ``packed`` gives the MFMA convs fragment-packed weight
+    copies. Returns the Decoder; it keeps the device tensors alive.
     """
     import torch
     tdt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
@@ -41,5 +43,8 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", spl
     code = VAE_DTYPE_BF16 if spec["dtype"] == "bf16" else VAE_DTYPE_F32
     act = VAE_DTYPE_BF16 if act_dtype == "bf16" else VAE_DTYPE_F32
     flags = VAE_DECODE_SPLIT_FP32_OPERANDS if (split and code == VAE_DTYPE_BF16) else 0
-    return Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat,
-                   act_dtype=act, flags=flags)
+    dec = Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat,
+                  act_dtype=act, flags=flags)
+    if packed:
+        dec.pack_weights(device)
+    return dec
