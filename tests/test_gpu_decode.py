@@ -141,6 +141,26 @@ def _golden(mode):
     return np.load(path)
 
 
+def _check_golden(g, out):
+    pos = g["positions"]
+    got = out[0, pos[:, 0], pos[:, 1], pos[:, 2], :].double().cpu().numpy()
+    ref = g["values"]
+    assert np.all(np.isfinite(got))
+    p = 10 * np.log10((float(g["out_max"]) - float(g["out_min"])) ** 2 /
+                      np.mean((got - ref) ** 2))
+    m = float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+    o = out.double()
+    assert abs(float(o.mean()) - float(g["out_mean"])) <= 1e-3 * float(g["out_std"])
+    assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
+
+
+def test_ltx2_720p_overlap_blend_against_golden(v):
+    """Full 720p overlap-blend decode: 2x3 tiles of 16x16 latents, stride 14 (512/448 px)."""
+    g = _golden("overlap")
+    _check_golden(g, gpu_decode(v, "ltx2_720p", "overlap"))
+
+
 def test_ltx2_720p_patch_halo_against_golden(v):
     """Full 720p decode (latent [1,128,16,22,40] -> [1,121,704,1280,3]), 1x4 width patches, at
     the pixels the oracle's full fp64 decode stored."""
