@@ -10,8 +10,18 @@ between two device synchronisations. HIP events recorded by the library on the d
 give each op's GPU time inside that same timed region, and the conv roofline comes from them.
 
 Output: one JSON line on stdout; progress goes to stderr.
+
+Two helper modes serve the HBM-traffic figure of the conv roofline:
+- ``--calibrate-copy MIB`` runs only a plain copy of known size (the library's upsample kernel at
+  factor 1), for reading what rocprofv3's FETCH_SIZE / WRITE_SIZE counters report per copied byte;
+- ``--traffic-record FETCH WRITE COPY_FETCH COPY_WRITE --out PATH`` turns the four
+  ``*_counter_collection.csv`` files of those ``--pmc`` runs into a small JSON record. The bench
+  reports the record's traffic only while the conv kernel sources still hash to the digest stored
+  in it; otherwise ``traffic`` is null.
 """
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +35,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "decoded Mpixel-frames/s (720p VAE decode, 1 GPU) + conv MFMA % of peak"
+CONV_SOURCES = ["video_diffusion_vae_amd/csrc/conv3d.hip", "video_diffusion_vae_amd/csrc/kernels.h",
+                "video_diffusion_vae_amd/csrc/common.h"]
+CONV_KERNEL = "conv3d_mfma_kernel"
+COPY_KERNEL = "upsample_kernel"
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "conv3d_mfma_ltx2_720p_patch_halo_1x4_traffic.json")
 
 
 def log(*a):
@@ -48,7 +63,85 @@ def conv_flops(spec, latent_shape):
     return total
 
 
-def cpu_baseline(spec, params, frames=1):
+def conv_source_digest():
+    h = hashlib.sha256()
+    for rel in CONV_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _pmc_sum(path, kernel_substr, counter):
+    """Sum of one counter over the dispatches whose kernel name contains `kernel_substr`."""
+    total, dispatches = 0.0, set()
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel_substr in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                total += float(row["Counter_Value"])
+                dispatches.add(row["Dispatch_Id"])
+    return total, len(dispatches)
+
+
+def write_traffic_record(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, decodes,
+                         workload, out):
+    """Conv HBM bytes per decode from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    (known copy bytes) / (what the same counter reads for the copy)."""
+    copy_bytes = copy_mib * 2**20
+    cf, ncf = _pmc_sum(copy_fetch_csv, COPY_KERNEL, "FETCH_SIZE")
+    cw, ncw = _pmc_sum(copy_write_csv, COPY_KERNEL, "WRITE_SIZE")
+    # the calibration program launches the copy `ncf` times, each moving copy_bytes each way
+    fetch_scale = copy_bytes * ncf / (cf * 1024.0)
+    write_scale = copy_bytes * ncw / (cw * 1024.0)
+    f, nf = _pmc_sum(fetch_csv, CONV_KERNEL, "FETCH_SIZE")
+    w, nw = _pmc_sum(write_csv, CONV_KERNEL, "WRITE_SIZE")
+    rec = {
+        "workload": workload, "kernel": CONV_KERNEL, "decodes": decodes,
+        "conv_dispatches_per_decode": nf / decodes,
+        "fetch_kib_per_decode_raw": f / decodes, "write_kib_per_decode_raw": w / decodes,
+        "copy_bytes": copy_bytes, "copy_dispatches": ncf,
+        "copy_fetch_kib_raw": cf / ncf, "copy_write_kib_raw": cw / ncw,
+        "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "hbm_bytes_per_decode": (f * fetch_scale + w * write_scale) * 1024.0 / decodes,
+        "source_sha256": conv_source_digest(),
+    }
+    assert nf == nw, (nf, nw)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def conv_traffic(workload):
+    """HBM bytes of the conv launches of one decode, while the record matches the sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no traffic record"
+    if rec.get("workload") != workload:
+        return None, "traffic record is for another workload"
+    if rec.get("source_sha256") != conv_source_digest():
+        return None, "conv sources changed since the counters were taken"
+    return rec["hbm_bytes_per_decode"], "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def calibrate_copy(mib, repeats=3):
+    """Plain device copy of `mib` MiB (fp32 rows through the library's upsample kernel at factor
+    1), `repeats` times; prints what it did as one JSON line."""
+    import torch
+    import video_diffusion_vae_amd as v
+    dev = torch.device("cuda:0")
+    n = mib * 2**20 // 4
+    rows = n // 1024
+    src = torch.ones((1, 1, rows, 1, 1024), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(repeats):
+        v.vae_upsample(src, None, v.VAE_UPSAMPLE_NEAREST, 1, 1, 1, dst)
+    torch.cuda.synchronize(dev)
+    assert bool((dst == 1).all())
+    print(json.dumps({"copy_mib": mib, "repeats": repeats, "kernel": COPY_KERNEL}), flush=True)
+
+
+def cpu_baseline(spec, params, frames=2):
     """The oracle, as it stands, on a bounded sample: the full 720p spatial plan on `frames`
     latent frames, scaled by conv flops to the 16-frame decode."""
     import threadpoolctl
@@ -80,12 +173,28 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", choices=["patch", "overlap"], default="patch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=1)
+    ap.add_argument("--cpu-frames", type=int, default=2)
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
+    ap.add_argument("--traffic-record", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--decodes", type=int, default=1)
+    ap.add_argument("--out")
     args = ap.parse_args()
+    if args.traffic_record:
+        workload = ("ltx2_720p_decode_patch_halo_1x4" if args.mode == "patch"
+                    else "ltx2_720p_decode_overlap_blend_2x3")
+        write_traffic_record(*args.traffic_record, args.copy_mib, args.decodes, workload,
+                             args.out or TRAFFIC_RECORD)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this decode has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     import vae_synth
@@ -116,12 +225,15 @@ def main():
     log(f"[bench] {args.warmup} warmup steps done")
 
     dec.set_timing(True)
-    per_op = []
+    per_op, step_s, enqueue_s = [], [], []
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
+        ts = time.perf_counter()
         dec.vae_decode_tiled(zd, desc, out, ws)
+        enqueue_s.append(time.perf_counter() - ts)
         per_op.append(dec.timing())          # waits for this step's last event
+        step_s.append(time.perf_counter() - ts)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     dec.set_timing(False)
@@ -157,9 +269,18 @@ def main():
 
     conv = kinds["conv"]
     achieved = conv["flops"] / (conv["ms"] / 1000.0) / 1e12
+    traffic, traffic_note = conv_traffic(workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": "conv3d_mfma_kernel (all conv launches of a decode)"}
+                "traffic": traffic, "traffic_unit": "bytes per decode (conv launches)",
+                "traffic_note": traffic_note,
+                "kernel": "conv3d_mfma_kernel (all conv launches of one decode)",
+                "conv_ms_per_step": round(conv["ms"] / args.steps, 3),
+                "conv_launches_per_step": conv["n"] // args.steps}
+    pct = lambda a, q: float(np.percentile(np.asarray(a) * 1000.0, q))
+    timing = {"step_ms_p10": round(pct(step_s, 10), 3), "step_ms_p50": round(pct(step_s, 50), 3),
+              "step_ms_p90": round(pct(step_s, 90), 3),
+              "host_enqueue_ms_p50": round(pct(enqueue_s, 50), 3)}
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -177,7 +298,7 @@ def main():
                    "operands": "bf16 weights; fp32 conv inputs as bf16 hi+lo; fp32 accumulate",
                    "activations": "fp32 between ops, bf16 GroupNorm outputs inside res blocks",
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
-        "roofline": roofline, "kernels": summary, "cpu_baseline": baseline,
+        "roofline": roofline, "kernels": summary, "timing": timing, "cpu_baseline": baseline,
     }
     print(json.dumps(line), flush=True)
 
