@@ -2,10 +2,12 @@
 //
 // bf16 weights: implicit GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //  - GEMM view: M = output positions, N = Cout, K = 27 * Cin, ordered (channel chunk, tap).
-//  - One workgroup (8 waves) computes a block of 256 output positions for NT output channels.
+//  - One workgroup (4 waves) computes a block of 256 output positions for NT output channels.
 //    The block is TB x HB x WB positions (2x8x16, 4x8x8 or 4x4x16, whichever pads the box least).
-//    Each wave owns 32 output channels and 256 * 32 / NT positions (32x32 MFMA tiles). Its 64
-//    accumulator registers leave room for four waves per SIMD, enough to hide L2 latency.
+//    Each wave owns 32 output channels and 256 * 32 / NT positions (32x32 MFMA tiles): at NT = 128
+//    a wave covers all 256 positions. Each weight fragment it loads then feeds eight MFMAs. Its
+//    128 accumulator registers allow two waves per SIMD, i.e. two workgroups per CU, so one
+//    workgroup's tile staging overlaps the other's MFMA work.
 //  - Input (A operand). For each 32-channel chunk the block's input tile is staged in LDS once:
 //    (TB+2) x (HB+2) x (WB+2) positions x 32 channels, i.e. the block, a one-row halo on each
 //    spatial side, and the two earlier frames. All 27 taps read their A fragments from that tile
@@ -20,8 +22,11 @@
 //    barriers and LDS carries only A.
 //  - fp32 inputs are rounded to bf16 (nearest-even) as they are staged, because MFMA operands are
 //    bf16. Accumulation is fp32. With the split flag an fp32 input is applied as two bf16
-//    operands, hi = bf16(x) and lo = bf16(x - hi). The K loop visits every channel chunk twice,
-//    about 16 significant bits of x reach the matrix cores, and the MFMA work doubles.
+//    operands, hi = bf16(x) and lo = bf16(x - hi), so about 16 significant bits of x reach the
+//    matrix cores and the MFMA work doubles. A chunk then holds 16 channels: its LDS row carries
+//    their hi halves in the first 32 bytes and their lo halves in the next 32. The two k steps of
+//    a tap read hi and lo against the same weight fragment. Each fp32 value is loaded once, and
+//    the weight loads per MFMA halve.
 //  - Epilogue: each wave parks one 32 x 32 accumulator tile at a time in LDS (reusing the input
 //    tile), then every lane writes four consecutive channels with one 16-byte (fp32) or 8-byte
 //    (bf16) store. Bias and residual are added on the way.
@@ -39,7 +44,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int kCK = 32;                              // input channels per LDS chunk
 constexpr int kRow = kCK * 2 + 16;                   // padded LDS row, bytes
-constexpr int kMfmaWaves = 8;
+constexpr int kMfmaWaves = 4;                        // waves per workgroup
 constexpr int kMfmaThreads = kMfmaWaves * 64;
 constexpr int kXcds = 8;
 
@@ -78,23 +83,28 @@ template <> __device__ __forceinline__ uint4 load8<float>(const float* p) {
     return r;
 }
 
-// The low half of the hi + lo bf16 split of 8 fp32 values: bf16(x - bf16(x)).
-__device__ __forceinline__ uint16_t lo_bf16(float x) {
-    return f32_to_bf16(x - bf16_to_f32(f32_to_bf16(x)));
+// The hi + lo bf16 split of 8 fp32 values: hi = bf16(x), lo = bf16(x - hi).
+template <typename TI> __device__ __forceinline__ void split8(const TI* p, uint4& hi, uint4& lo);
+template <> __device__ __forceinline__ void split8<uint16_t>(const uint16_t* p, uint4& hi,
+                                                             uint4& lo) {
+    hi = *reinterpret_cast<const uint4*>(p);
+    lo = make_uint4(0, 0, 0, 0);
 }
-template <typename TI> __device__ __forceinline__ uint4 load8_lo(const TI* p);
-template <> __device__ __forceinline__ uint4 load8_lo<uint16_t>(const uint16_t*) {
-    return make_uint4(0, 0, 0, 0);
-}
-template <> __device__ __forceinline__ uint4 load8_lo<float>(const float* p) {
+template <> __device__ __forceinline__ void split8<float>(const float* p, uint4& hi, uint4& lo) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    uint4 r;
-    r.x = (uint32_t)lo_bf16(a.x) | ((uint32_t)lo_bf16(a.y) << 16);
-    r.y = (uint32_t)lo_bf16(a.z) | ((uint32_t)lo_bf16(a.w) << 16);
-    r.z = (uint32_t)lo_bf16(b.x) | ((uint32_t)lo_bf16(b.y) << 16);
-    r.w = (uint32_t)lo_bf16(b.z) | ((uint32_t)lo_bf16(b.w) << 16);
-    return r;
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+        const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
+        h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 template <typename TO> __device__ __forceinline__ void load4(const TO* p, float* v);
@@ -136,14 +146,14 @@ struct BlockShape {
 };
 
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
-__global__ __launch_bounds__(kMfmaThreads, 4)
+__global__ __launch_bounds__(kMfmaThreads, 2)
 void conv3d_mfma_kernel(MfmaArgs a) {
     using S = BlockShape<TB, HB, WB>;
     constexpr int HH = S::HH, HW = S::HW;
     constexpr int RP = S::kPitch;
     __shared__ __attribute__((aligned(16))) uint8_t halo[S::kBytes];
 
-    // 8 waves: WNN of them across the NT output channels (32 each), WM across the 256 positions.
+    // WNN waves across the NT output channels (32 each), WM across the 256 positions.
     constexpr int WNN = NT / 32;
     constexpr int WM = kMfmaWaves / WNN;
     constexpr int MW = 256 / WM;       // positions per wave
@@ -199,26 +209,32 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     const uint16_t* b_ptr =
         PACKED ? a.w + (int64_t)(b_ok ? co_tile >> 5 : 0) * 27 * nch * 1024 + lrow * 16 + khalf * 8
                : a.w + (int64_t)(b_ok ? co_tile + lrow : 0) * 27 * cin + khalf * 8;
-    uint4 bq[NB][2];
+    // Weight fragments per tap: one per k step, or one for both (hi and lo) with the split.
+    constexpr int KB = SPLIT ? 1 : 2;
+    uint4 bq[NB][KB];
     auto load_b = [&](int buf, int tap, int c0) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            const int64_t off = PACKED ? ((int64_t)tap * nch + (c0 >> 5)) * 1024 + kk * 512
+        for (int kk = 0; kk < KB; ++kk) {
+            // split chunks are 16 channels: the k-step half of a packed 32-channel block
+            const int half = SPLIT ? (c0 >> 4) & 1 : kk;
+            const int64_t off = PACKED ? ((int64_t)tap * nch + (c0 >> 5)) * 1024 + half * 512
                                        : (int64_t)tap * cin + c0 + kk * 16;
-            if (b_ok) v = *reinterpret_cast<const uint4*>(b_ptr + off);
-            bq[buf][kk] = v;
+            // Unconditional: b_ptr points at valid weights even for columns past Cout, whose
+            // outputs are never stored. A branch here would split the tap loop into blocks the
+            // scheduler cannot overlap, and force a full wait on every prefetch.
+            bq[buf][kk] = *reinterpret_cast<const uint4*>(b_ptr + off);
         }
     };
 
-    const int n_passes = nch * (SPLIT ? 2 : 1);
-    for (int kc = 0; kc < n_passes; ++kc) {
-        const int c0 = (SPLIT ? (kc >> 1) : kc) * kCK;
-        const bool lo = SPLIT && (kc & 1);
+    constexpr int CK = SPLIT ? 16 : kCK;       // input channels per staged chunk
+    constexpr int UPP = SPLIT ? 2 : 4;         // staging units per position (8 channels each)
+    const int n_chunks = a.cin / CK;
+    for (int kc = 0; kc < n_chunks; ++kc) {
+        const int c0 = kc * CK;
         load_b(0, 0, c0);             // in flight while the input tile is staged
         __syncthreads();              // the previous chunk's LDS reads are done
-        for (int u = tid; u < S::kPos * 4; u += kMfmaThreads) {
-            const int pos = u >> 2, g = u & 3;
+        for (int u = tid; u < S::kPos * UPP; u += kMfmaThreads) {
+            const int pos = u / UPP, g = u % UPP;
             const int f = pos / (HH * HW);
             const int rem = pos - f * (HH * HW);
             const int r = rem / HW;
@@ -227,30 +243,52 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
             const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
             uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
+            uint4 vl = make_uint4(0, 0, 0, 0);
             if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
                 const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
-                v = lo ? load8_lo<TI>(src) : load8<TI>(src);
+                if constexpr (SPLIT) split8<TI>(src, v, vl);
+                else v = load8<TI>(src);
             }
-            *reinterpret_cast<uint4*>(&halo[(f * HH + r) * RP + c * kRow + g * 16]) = v;
+            uint8_t* dst = &halo[(f * HH + r) * RP + c * kRow + g * 16];
+            *reinterpret_cast<uint4*>(dst) = v;            // split: hi in bytes 0..31 of the row
+            if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = vl;  // lo in bytes 32..63
         }
         __syncthreads();
 
+        // 54 k steps (27 taps x 2). The A fragments of step s + 1 are read from LDS while the
+        // MFMAs of step s run; the weights of tap + 1 are fetched during tap.
+        bf16x8_t af[2][MI];
 #pragma unroll
-        for (int tap = 0; tap < 27; ++tap) {
-            if (tap + 1 < 27) load_b((tap + 1) % NB, tap + 1, c0);
-            const int kt = tap / 9, kh = (tap / 3) % 3, kw = tap % 3;
-            const int tap_off = (kt * HH + kh) * RP + kw * kRow;
-            const int buf = tap % NB;
+        for (int i = 0; i < MI; ++i)
+            af[0][i] = *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i]]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[buf][kk]);
+        for (int step = 0; step < 54; ++step) {
+            const int tap = step >> 1, kk = step & 1;
+            if (kk == 0 && tap + 1 < 27) load_b((tap + 1) % NB, tap + 1, c0);
+            if (step + 1 < 54) {
+                const int nt = (step + 1) >> 1, nk = (step + 1) & 1;
+                const int kt = nt / 9, kh = (nt / 3) % 3, kw = nt % 3;
+                const int off = (kt * HH + kh) * RP + kw * kRow + nk * 32;
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(
-                        &halo[a_off[i] + tap_off + kk * 32]);
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[i], 0, 0, 0);
-                }
+                for (int i = 0; i < MI; ++i)
+                    af[(step + 1) & 1][i] =
+                        *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i] + off]);
             }
+            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf, acc[i], 0,
+                                                                 0, 0);
+            // Each k step is its own scheduling island: the weight loads first, then the MFMAs
+            // alternating with the next step's LDS reads, so that neither waits on the other.
+            if (kk == 0 && tap + 1 < 27) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (step + 1 < 54) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();  // the input tile is reused for the epilogue
