@@ -276,9 +276,9 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * With bf16 weights, fp32 activations keep the bf16 rounding to the conv operands alone: about
  * 40 fewer roundings on the way through the LTX-2-shaped plan.
  * VAE_DECODE_SPLIT_FP32_OPERANDS goes further for convs that read an fp32 activation (the
- * upsampling convs read the fp32 residual stream). It makes a standalone GN_SILU write fp32 (the
- * output conv then reads fp32), and every such conv runs with VAE_CONV_SPLIT_FP32. The convs
- * inside residual blocks keep one rounding of their GroupNorm operand.
+ * upsampling convs read the fp32 residual stream): each such CONV runs with VAE_CONV_SPLIT_FP32
+ * unless its no_split is set. A standalone GN_SILU followed by a splitting CONV writes fp32 for
+ * it. The convs inside residual blocks keep one rounding of their GroupNorm operand.
  * The parameter pointers come in plan order, two per entry:
  *  conv -> (weight, bias);
  *  GN -> (gamma, beta);
@@ -292,6 +292,8 @@ typedef struct vae_layer_desc {
     int32_t cin, cout;
     int32_t st, sh, sw;
     int32_t f32_out;
+    int32_t no_split;  /* conv only: 1 = round an fp32 input to bf16 once even when the decoder
+                          splits fp32 operands (VAE_DECODE_SPLIT_FP32_OPERANDS) */
 } vae_layer_desc_t;
 
 enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1 };

@@ -126,6 +126,40 @@ def test_ltx2_shaped_overlap_blend(v, name):
     _bf16_bar(got, oracle_out(name, "overlap"))
 
 
+@pytest.mark.parametrize("mode,patches", [("patch", (1, 4)), ("overlap", (1, 1))])
+def test_ltx2_720p_one_frame_every_value(v, mode, patches):
+    """The full-width 720p plan on one latent frame ([1,128,1,22,40] -> [1,1,704,1280,3]): every
+    one of the 2.7M output values against the oracle, in both tiling modes."""
+    got = host(gpu_decode(v, "ltx2_720p_1f", mode, patches))
+    assert got.shape == (1, 1, 704, 1280, 3)
+    _bf16_bar(got, oracle_out("ltx2_720p_1f", "whole" if mode == "patch" else "overlap"))
+
+
+def test_no_split_on_every_conv_matches_unsplit_decoder(v):
+    """Per-conv no_split set on every conv of a splitting decoder gives, bit for bit, the decoder
+    without the split flag."""
+    import copy
+    import torch
+    spec = vae_synth.LTX2_TINY
+    ns = copy.deepcopy(spec)
+    for op in ns["layers"]:
+        if op["op"] == "conv":
+            op["no_split"] = True
+    z = ndhwc(vae_synth.latent(spec))
+    zd = dev(z, "bf16")
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 2))
+    outs = []
+    for sp, split in ((ns, True), (spec, False)):
+        dec = v.upload_decoder(sp, params_of("ltx2_tiny"), split=split)
+        ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
+        out = torch.empty(oracle.output_shape(spec, z.shape), dtype=torch.float32, device="cuda")
+        dec.vae_decode_tiled(zd, desc, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+        dec.close()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_decode_is_deterministic(v):
     import torch
     a, b = gpu_decode(v, "ltx2_small", "patch", (1, 2), repeat=2)

@@ -64,7 +64,8 @@ class vae_tile_t(ctypes.Structure):
 
 
 class vae_layer_desc_t(ctypes.Structure):
-    _fields_ = [(k, ctypes.c_int32) for k in ("op", "cin", "cout", "st", "sh", "sw", "f32_out")]
+    _fields_ = [(k, ctypes.c_int32)
+                for k in ("op", "cin", "cout", "st", "sh", "sw", "f32_out", "no_split")]
 
 
 class vae_decoder_spec_t(ctypes.Structure):
@@ -314,15 +315,16 @@ def layer_descs(plan):
         k = op["op"]
         if k == "conv":
             out.append(vae_layer_desc_t(VAE_OP_CONV, op["cin"], op["cout"], 1, 1, 1,
-                                        int(op.get("f32_out", False))))
+                                        int(op.get("f32_out", False)),
+                                        int(op.get("no_split", False))))
         elif k == "res":
-            out.append(vae_layer_desc_t(VAE_OP_RES, op["c"], op["c"], 1, 1, 1, 0))
+            out.append(vae_layer_desc_t(VAE_OP_RES, op["c"], op["c"], 1, 1, 1, 0, 0))
         elif k == "gn_silu":
-            out.append(vae_layer_desc_t(VAE_OP_GN_SILU, 0, 0, 1, 1, 1, 0))
+            out.append(vae_layer_desc_t(VAE_OP_GN_SILU, 0, 0, 1, 1, 1, 0, 0))
         elif k == "d2s":
-            out.append(vae_layer_desc_t(VAE_OP_D2S, 0, 0, op["st"], op["sh"], op["sw"], 0))
+            out.append(vae_layer_desc_t(VAE_OP_D2S, 0, 0, op["st"], op["sh"], op["sw"], 0, 0))
         elif k == "nearest":
-            out.append(vae_layer_desc_t(VAE_OP_NEAREST, 0, 0, 1, op["sh"], op["sw"], 0))
+            out.append(vae_layer_desc_t(VAE_OP_NEAREST, 0, 0, 1, op["sh"], op["sw"], 0, 0))
         else:
             raise ValueError(k)
     return out

@@ -41,10 +41,20 @@ struct Shape {
     int64_t bytes() const { return n * t * h * w * c * elem_size(dtype); }
 };
 
-// Output dtype of a standalone GN_SILU: the next conv's operand dtype, or the activation dtype
-// when that conv takes fp32 inputs as split operands.
-int32_t gn_silu_dtype(const vae_decoder& d) {
-    return (d.flags & VAE_DECODE_SPLIT_FP32_OPERANDS) ? d.act_dtype : d.dtype;
+// Whether layer i is a conv that applies an fp32 input as split hi + lo bf16 operands.
+bool conv_splits(int32_t flags, const vae_layer_desc_t* layers, int n, int i) {
+    return (flags & VAE_DECODE_SPLIT_FP32_OPERANDS) && i >= 0 && i < n &&
+           layers[i].op == VAE_OP_CONV && !layers[i].no_split;
+}
+
+// Output dtype of the standalone GN_SILU at layer i: the activation dtype when the next layer is
+// a conv that splits its fp32 input, else the conv operand dtype.
+int32_t gn_silu_dtype(int32_t dtype, int32_t act_dtype, int32_t flags,
+                      const vae_layer_desc_t* layers, int n, int i) {
+    return conv_splits(flags, layers, n, i + 1) ? act_dtype : dtype;
+}
+int32_t gn_silu_dtype(const vae_decoder& d, int i) {
+    return gn_silu_dtype(d.dtype, d.act_dtype, d.flags, d.layers.data(), (int)d.layers.size(), i);
 }
 
 // Number of device pointers each op consumes.
@@ -74,7 +84,7 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
                 s.dtype = d.act_dtype;
                 break;
             case VAE_OP_GN_SILU:
-                s.dtype = gn_silu_dtype(d);
+                s.dtype = gn_silu_dtype(d, (int)i);
                 break;
             case VAE_OP_D2S:
                 s.t = l.st * s.t - (l.st - 1);
@@ -150,7 +160,7 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         if (last && final_in_buffer) r->tile = std::max(r->tile, s.bytes());
         if (l.op == VAE_OP_RES || l.op == VAE_OP_GN_SILU) {
             Shape g = cur;
-            g.dtype = l.op == VAE_OP_RES ? d.dtype : gn_silu_dtype(d);
+            g.dtype = l.op == VAE_OP_RES ? d.dtype : gn_silu_dtype(d, (int)i);
             r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
             vae_tensor_t x = tensor_of(nullptr, cur);
             r->gn = std::max<int64_t>(
@@ -227,7 +237,9 @@ struct Runner {
     // `wi` indexes d->ptrs: the conv's weight, followed by its bias.
     vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
                       const vae_tensor_t& y, int layer) {
-        int32_t cf = (d->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) ? VAE_CONV_SPLIT_FP32 : 0;
+        int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
+                         ? VAE_CONV_SPLIT_FP32
+                         : 0;
         const void* w = d->ptrs[wi];
         if (d->packed[wi]) {
             w = d->packed[wi];
@@ -290,7 +302,7 @@ struct Runner {
                 vae_tensor_t y;
                 int nb = cur_buf;
                 Shape gs = shape_of(cur);
-                gs.dtype = gn_silu_dtype(*d);
+                gs.dtype = gn_silu_dtype(*d, layer);
                 if (last) {
                     y = final_out;
                     nb = -2;
@@ -405,7 +417,6 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
         return fail(VAE_ERR_UNSUPPORTED, "an fp32 plan keeps fp32 activations");
     if (spec->flags & ~VAE_DECODE_SPLIT_FP32_OPERANDS)
         return fail(VAE_ERR_INVALID_ARG, "unknown decoder flags");
-    const bool split = (spec->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) != 0;
     if (spec->latent_channels < 1 || spec->groups < 1 || !(spec->eps >= 0.0f))
         return fail(VAE_ERR_INVALID_ARG, "latent_channels and groups must be >= 1, eps >= 0");
     if (spec->n_layers < 1 || !spec->layers) return fail(VAE_ERR_INVALID_ARG, "empty layer plan");
@@ -434,7 +445,8 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
                 if (c % spec->groups)
                     return fail(VAE_ERR_UNSUPPORTED, "width not divisible by groups", 4, c,
                                 spec->groups);
-                act = split ? spec->act_dtype : spec->dtype;
+                act = gn_silu_dtype(spec->dtype, spec->act_dtype, spec->flags, spec->layers,
+                                    spec->n_layers, i);
                 break;
             case VAE_OP_D2S: {
                 if (l.st < 1 || l.sh < 1 || l.sw < 1)
