@@ -121,6 +121,37 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
                                        const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream);
 
+/* Causal Conv3d followed by the statistics of a GroupNorm over its output.
+ *
+ * The conv is the one vae_conv3d_causal computes, with the same arguments. In addition,
+ * mean_rstd receives [N][groups][2] fp32: the mean of each (sample, group) over out_box and
+ * 1/sqrt(var + eps). var is the biased variance about that global mean (divide by the count),
+ * which is the statistic a patch-parallel GroupNorm must reproduce (P4, PatchGroupNorm commit).
+ * The statistics are those of y as stored, e.g. after rounding to bf16, and include the residual.
+ *
+ * On the MFMA path, with 4, 8, 16 or 32 channels per group, the conv's epilogue forms the
+ * partials while the outputs are still in registers. They are (count, mean, M2) per output block
+ * and group, merged with Chan's update in a fixed order (fp32 within a block, fp64 across blocks).
+ * This saves a second read of y. Other shapes run a separate statistics pass over y, with the
+ * same result up to rounding.
+ *
+ * ws: device scratch of vae_conv3d_causal_gn_workspace() bytes, 16-byte aligned, owned by the
+ * caller. Its contents are undefined afterwards. mean_rstd: device, N * groups * 2 floats.
+ * Errors: those of vae_conv3d_causal; UNSUPPORTED when y's channels are not divisible by groups
+ * or the shape is one vae_groupnorm_stats refuses; INVALID_ARG for eps < 0, a NULL mean_rstd or
+ * an empty out_box; WORKSPACE for a short ws.
+ */
+VAE_API vae_status_t vae_conv3d_causal_gn_workspace(const vae_tensor_t* x, const vae_tensor_t* y,
+                                                    int32_t weight_dtype,
+                                                    const vae_box_t* out_box, int32_t groups,
+                                                    size_t* bytes);
+VAE_API vae_status_t vae_conv3d_causal_gn(const vae_tensor_t* x, const void* weight,
+                                          int32_t weight_dtype, const float* bias,
+                                          const vae_tensor_t* residual, vae_tensor_t* y,
+                                          const vae_box_t* out_box, int32_t flags, int32_t groups,
+                                          float eps, float* mean_rstd, void* ws, size_t ws_bytes,
+                                          vae_stream_t stream);
+
 /* Fragment-packed copy of bf16 conv weights, for the MFMA path. Layout:
  * [ceil(Cout/32)][27 taps][Cin/32][2][32][2][8], i.e. output channels in tiles of 32 and input
  * channels in chunks of 32, ordered so that each 16-byte matrix-core operand fragment of a

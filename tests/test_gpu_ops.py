@@ -83,6 +83,66 @@ def test_conv3d_mfma_matches_oracle(v, case):
         assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
 
 
+CONV_GN_CASES = [
+    # (N, T, H, W), Cin, Cout, groups, in dtype, out dtype, residual, box
+    ((1, 3, 9, 17), 32, 128, 32, "bf16", "f32", False, None),            # 4 channels per group
+    ((2, 4, 6, 20), 64, 256, 32, "bf16", "bf16", True, None),            # 8, two samples
+    ((1, 5, 10, 20), 32, 512, 32, "bf16", "f32", True, (1, 5, 2, 9, 3, 17)),  # 16, in a box
+    ((1, 2, 5, 9), 64, 1024, 32, "bf16", "f32", False, None),            # 32
+    ((1, 3, 9, 19), 64, 64, 8, "f32", "f32", False, None),               # 64-wide tiles
+    ((1, 3, 6, 9), 32, 64, 32, "bf16", "f32", False, None),              # 2: separate pass
+    ((1, 3, 6, 9), 16, 32, 8, "bf16", "f32", True, None),                # direct conv path
+]
+
+
+@pytest.mark.parametrize("case", CONV_GN_CASES)
+def test_conv3d_gn_statistics(v, case):
+    """Conv plus the GroupNorm statistics of its stored output over the box. The epilogue gathers
+    them on the MFMA path (4-32 channels per group). Other shapes take a separate pass.
+    Checks:
+     - y is bit-identical to vae_conv3d_causal's;
+     - mean/rstd match the oracle's two-pass statistics of the oracle conv;
+     - mean/rstd match the separate statistics pass run over the same y."""
+    import torch
+    (n, t, h, w), cin, cout, groups, idt, odt, use_res, bx = case
+    x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", 60 + CONV_GN_CASES.index(case))
+    if idt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [16, cin], scale=1e-3))
+        ref = oracle.causal_conv3d(vae_synth.round_bf16(x), wt, b)
+    else:
+        ref = oracle.causal_conv3d(x, wt, b)
+    if use_res:
+        ref = ref + r
+    tdt = torch.float32 if odt == "f32" else torch.bfloat16
+    xd = dev(x, idt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16 if cin % 32 == 0 else torch.float32, "cuda")
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, odt) if use_res else None
+    y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=tdt)
+    mr = torch.zeros((n, groups, 2), dtype=torch.float32, device="cuda")
+    v.vae_conv3d_causal_gn(xd, wd, bd, rd, y, groups, 1e-6, mr, bx)
+    y0 = torch.full_like(y, 7.0)
+    v.vae_conv3d_causal(xd, wd, bd, rd, y0, bx)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    bx = bx or (0, t, 0, h, 0, w)
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    rf = ref[sl] if odt == "f32" else vae_synth.round_bf16(ref[sl]).astype(np.float64)
+    cnt, mean, m2 = oracle.group_moments(rf, groups)
+    var = m2 / cnt
+    got = mr.cpu().numpy().astype(np.float64)
+    tol = 1e-4 if odt == "f32" else 1e-3
+    assert np.all(np.abs(got[..., 0] - mean) <= tol * np.sqrt(var) + 1e-6)
+    np.testing.assert_allclose(got[..., 1], 1 / np.sqrt(var + 1e-6), rtol=tol)
+    # the separate statistics pass over the same y
+    part = torch.zeros((1, n, groups, 3), dtype=torch.float64, device="cuda")
+    v.vae_groupnorm_stats(y, [bx], groups, part)
+    mr2 = torch.zeros_like(mr)
+    v.vae_groupnorm_combine(part, 1, n, groups, 1e-6, mr2)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(got, mr2.cpu().numpy(), rtol=2e-5, atol=1e-6)
+
+
 @pytest.mark.parametrize("shape,cin,cout,box", [((1, 3, 9, 19), 64, 256, None),
                                                  ((1, 5, 7, 33), 32, 48, (1, 5, 0, 7, 4, 30))])
 def test_conv3d_split_operands(v, shape, cin, cout, box):

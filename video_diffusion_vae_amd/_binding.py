@@ -24,7 +24,7 @@ VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
 # Every symbol include/vae.h declares.
 EXPORTS = (
     "vae_last_error", "vae_last_error_info", "vae_version", "vae_conv3d_causal",
-    "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_decoder_packed_weight_size",
+    "vae_conv3d_causal_gn_workspace", "vae_conv3d_causal_gn", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_decoder_packed_weight_size",
     "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_upsample",
@@ -94,6 +94,8 @@ def _load():
         "vae_last_error_info": ([ctypes.POINTER(vae_error_info_t)], I32),
         "vae_version": ([], I32),
         "vae_conv3d_causal": ([T, P, I32, P, T, T, B, I32, P], I32),
+        "vae_conv3d_causal_gn_workspace": ([T, T, I32, B, I32, ctypes.POINTER(SZ)], I32),
+        "vae_conv3d_causal_gn": ([T, P, I32, P, T, T, B, I32, I32, F, P, P, SZ, P], I32),
         "vae_conv_weight_pack_size": ([I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_conv_weight_pack": ([P, I32, I32, P, P], I32),
         "vae_decoder_packed_weight_size": ([P, ctypes.POINTER(SZ)], I32),
@@ -209,6 +211,30 @@ def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, strea
                                  _ref(rd), ctypes.byref(yd), _ref(box(out_box)), int(flags),
                                  _stream(stream)))
     return y
+
+
+def vae_conv3d_causal_gn_workspace(x, y, weight_dtype, out_box, groups):
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    n = ctypes.c_size_t(0)
+    _check(LIB.vae_conv3d_causal_gn_workspace(ctypes.byref(xd), ctypes.byref(yd), int(weight_dtype),
+                                              _ref(box(out_box)), int(groups), ctypes.byref(n)))
+    return n.value
+
+
+def vae_conv3d_causal_gn(x, weight, bias, residual, y, groups, eps, mean_rstd, out_box=None,
+                         flags=0, ws=None, stream=None):
+    """Causal Conv3d plus the GroupNorm statistics of y over out_box: mean_rstd [N, groups, 2]
+    fp32 (device) receives (mean, 1/sqrt(var + eps))."""
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    rd = tensor_desc(residual) if residual is not None else None
+    if ws is None:
+        ws = _workspace(vae_conv3d_causal_gn_workspace(x, y, _dtype_code(weight), out_box, groups),
+                        x.device)
+    _check(LIB.vae_conv3d_causal_gn(ctypes.byref(xd), _ptr(weight), _dtype_code(weight),
+                                    _ptr(bias), _ref(rd), ctypes.byref(yd), _ref(box(out_box)),
+                                    int(flags), int(groups), ctypes.c_float(eps), _ptr(mean_rstd),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return mean_rstd
 
 
 def vae_conv_weight_pack(weight, stream=None):

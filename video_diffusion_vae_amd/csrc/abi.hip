@@ -215,28 +215,9 @@ std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
     return tiles;
 }
 
-}  // namespace vae
-
-using namespace vae;
-
-extern "C" {
-
-VAE_API const char* vae_last_error(void) { return error_state().text.c_str(); }
-
-VAE_API vae_status_t vae_last_error_info(vae_error_info_t* info) {
-    if (!info) return VAE_ERR_INVALID_ARG;
-    *info = error_state().info;
-    return VAE_OK;
-}
-
-VAE_API int32_t vae_version(void) { return 100; }
-
-VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
-                                       int32_t weight_dtype, const float* bias,
-                                       const vae_tensor_t* residual, vae_tensor_t* y,
-                                       const vae_box_t* out_box, int32_t flags,
-                                       vae_stream_t stream) {
-    clear_error();
+vae_status_t check_conv(const vae_tensor_t* x, const void* weight, int32_t weight_dtype,
+                        const vae_tensor_t* residual, vae_tensor_t* y, const vae_box_t* out_box,
+                        int32_t flags) {
     if (flags & ~(VAE_CONV_SPLIT_FP32 | VAE_CONV_PACKED_WEIGHTS))
         return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
     VAE_TRY(check_tensor(x, "x"));
@@ -259,8 +240,94 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
         return fail(VAE_ERR_UNSUPPORTED,
                     "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x->c,
                     32);
+    return VAE_OK;
+}
+
+// Workspace of vae_conv3d_causal_gn: the fused partials, or the separate statistics pass's.
+size_t conv_gn_workspace(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype,
+                         const Box& box, int32_t groups, int64_t* slots) {
+    *slots = conv_gn_slots(x, y, weight_dtype, box, groups);
+    if (*slots > 0) return (size_t)(y.n * groups * *slots * 3) * sizeof(double);
+    BoxList bl;
+    bl.n = 1;
+    bl.b[0] = box;
+    return gn_stats_workspace(y, bl, groups);
+}
+
+}  // namespace vae
+
+using namespace vae;
+
+extern "C" {
+
+VAE_API const char* vae_last_error(void) { return error_state().text.c_str(); }
+
+VAE_API vae_status_t vae_last_error_info(vae_error_info_t* info) {
+    if (!info) return VAE_ERR_INVALID_ARG;
+    *info = error_state().info;
+    return VAE_OK;
+}
+
+VAE_API int32_t vae_version(void) { return 100; }
+
+
+VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
+                                       int32_t weight_dtype, const float* bias,
+                                       const vae_tensor_t* residual, vae_tensor_t* y,
+                                       const vae_box_t* out_box, int32_t flags,
+                                       vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_conv(x, weight, weight_dtype, residual, y, out_box, flags));
     return launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, to_box(out_box, *y), flags,
                          as_stream(stream));
+}
+
+VAE_API vae_status_t vae_conv3d_causal_gn_workspace(const vae_tensor_t* x, const vae_tensor_t* y,
+                                                    int32_t weight_dtype,
+                                                    const vae_box_t* out_box, int32_t groups,
+                                                    size_t* bytes) {
+    clear_error();
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");
+    VAE_TRY(check_tensor(x, "x"));
+    VAE_TRY(check_gn(y, groups));
+    VAE_TRY(check_box(out_box, *y, "out_box"));
+    int64_t slots = 0;
+    *bytes = conv_gn_workspace(*x, *y, weight_dtype, to_box(out_box, *y), groups, &slots);
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_conv3d_causal_gn(const vae_tensor_t* x, const void* weight,
+                                          int32_t weight_dtype, const float* bias,
+                                          const vae_tensor_t* residual, vae_tensor_t* y,
+                                          const vae_box_t* out_box, int32_t flags, int32_t groups,
+                                          float eps, float* mean_rstd, void* ws, size_t ws_bytes,
+                                          vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_conv(x, weight, weight_dtype, residual, y, out_box, flags));
+    VAE_TRY(check_gn(y, groups));
+    if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
+    if (!mean_rstd) return fail(VAE_ERR_INVALID_ARG, "mean_rstd is NULL");
+    const Box box = to_box(out_box, *y);
+    int64_t slots = 0;
+    const size_t need = conv_gn_workspace(*x, *y, weight_dtype, box, groups, &slots);
+    if (!ws || ws_bytes < need)
+        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
+                    (int64_t)need);
+    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    hipStream_t s = as_stream(stream);
+    double* part = static_cast<double*>(ws);
+    if (box.volume() == 0 || y->n == 0) return fail(VAE_ERR_INVALID_ARG, "empty out_box");
+    if (slots > 0) {
+        const ConvGn gn{part, groups};
+        VAE_TRY(launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, box, flags, s, &gn));
+        return launch_gn_finalize_slots(part, slots, (int32_t)y->n, groups, eps, mean_rstd, s);
+    }
+    BoxList bl;
+    bl.n = 1;
+    bl.b[0] = box;
+    VAE_TRY(launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, box, flags, s));
+    return launch_gn_stats(*y, bl, groups, part, nullptr, mean_rstd, eps, s);
 }
 
 VAE_API vae_status_t vae_conv_weight_pack_size(int32_t cout, int32_t cin, size_t* bytes) {

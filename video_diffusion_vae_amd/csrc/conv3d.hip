@@ -58,6 +58,10 @@ struct MfmaArgs {
     Box box;
     int32_t nbt, nbh, nbw;   // blocks along each box axis
     int32_t n_mblocks;       // N * nbt * nbh * nbw
+    // Optional GroupNorm partials of the output as stored: fp64 (count, mean, M2) per
+    // (sample, group, slot), slot = position block * WM + wave row; null when not wanted.
+    double* stats;
+    int32_t groups, nslots;
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -126,6 +130,28 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const 
     a.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
     a.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
     *reinterpret_cast<uint2*>(p) = a;
+}
+
+// The value an output element holds once stored.
+template <typename TO> __device__ __forceinline__ float stored(float v);
+template <> __device__ __forceinline__ float stored<float>(float v) { return v; }
+template <> __device__ __forceinline__ float stored<uint16_t>(float v) {
+    return bf16_to_f32(f32_to_bf16(v));
+}
+
+// Chan's pairwise update of (count, mean, M2) with another partial, in fp32.
+__device__ __forceinline__ void chan_merge_f32(float& n, float& mean, float& m2, float nb,
+                                               float mb, float m2b) {
+    const float t = n + nb;
+    if (nb > 0.0f && n > 0.0f) {
+        const float d = mb - mean;
+        mean += d * (nb / t);
+        m2 += m2b + d * d * (n * nb / t);
+    } else if (nb > 0.0f) {
+        mean = mb;
+        m2 = m2b;
+    }
+    n = t;
 }
 
 // Staged input tile: (TB+2) x (HB+2) rows of (WB+2) positions, 80 bytes per position. The row
@@ -310,6 +336,9 @@ void conv3d_mfma_kernel(MfmaArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (co + k < a.cout) bv[k] = a.bias[co + k];
+    // GroupNorm partials of this lane's four channels (one group): shifted sums, shift = the
+    // lane's first stored value.
+    float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -325,11 +354,12 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             const int t = t_blk + m / (HB * WB);
             const int h = h_blk + (m / WB) % HB, w = w_blk + m % WB;
             if (t < a.box.t1 && h < a.box.h1 && w < a.box.w1 && co < a.cout) {
+                const int nv = a.cout - co < 4 ? a.cout - co : 4;
                 float v[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) v[k] = ep[row * EP + c4 + k] + bv[k];
                 const int64_t o = ((((int64_t)n * a.T + t) * a.H + h) * a.W + w) * a.cout + co;
-                if (co + 4 <= a.cout) {
+                if (nv == 4) {
                     if (res) {
                         float rv[4];
                         load4<TO>(res + o, rv);
@@ -338,10 +368,22 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                     }
                     store4<TO>(y + o, v);
                 } else {
-                    for (int k = 0; co + k < a.cout; ++k) {
-                        float vk = v[k];
-                        if (res) vk += Elem<TO>::load(res + o + k);
-                        Elem<TO>::store(y + o + k, vk);
+                    for (int k = 0; k < nv; ++k) {
+                        if (res) v[k] += Elem<TO>::load(res + o + k);
+                        Elem<TO>::store(y + o + k, v[k]);
+                    }
+                }
+                if (a.stats) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        if (k < nv) {
+                            const float q = stored<TO>(v[k]);
+                            sk = sn == 0.0f ? q : sk;
+                            const float d = q - sk;
+                            s1 += d;
+                            s2 = fmaf(d, d, s2);
+                            sn += 1.0f;
+                        }
                     }
                 }
             }
@@ -349,6 +391,37 @@ void conv3d_mfma_kernel(MfmaArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (a.stats) {
+        // lane -> (count, mean, M2); then merge the 8 lanes that hold the same four channels
+        // (lane ^ 8, 16, 32) and the lanes of one group (cpg / 4 neighbours), in a fixed order.
+        float mean = 0.0f, m2 = 0.0f;
+        if (sn > 0.0f) {
+            const float mk = s1 / sn;
+            mean = sk + mk;
+            m2 = fmaxf(s2 - s1 * mk, 0.0f);
+        }
+        const int cpg = a.cout / a.groups;
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) {
+            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
+                        m2b = __shfl_xor(m2, off);
+            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
+        }
+        for (int off = 1; off < cpg / 4; off <<= 1) {
+            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
+                        m2b = __shfl_xor(m2, off);
+            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
+        }
+        if (lane < LPR && lane % (cpg / 4) == 0 && co < a.cout) {
+            const int g = co / cpg;
+            const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
+            double* o = a.stats +
+                        (((int64_t)n * a.groups + g) * a.nslots + (int64_t)mb_local * WM + wave_m) * 3;
+            o[0] = sn;
+            o[1] = mean;
+            o[2] = m2;
+        }
     }
 }
 
@@ -412,10 +485,15 @@ BlockKind pick_block(const Box& b) {
     return kBlk2x8x16;
 }
 
+template <int NT>
+constexpr int wave_rows() {
+    return kMfmaWaves / (NT / 32);
+}
+
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
 vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
                        const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       hipStream_t stream) {
+                       const ConvGn* gn, hipStream_t stream) {
     MfmaArgs a;
     a.x = x.data;
     a.w = static_cast<const uint16_t*>(w);
@@ -435,6 +513,9 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     int64_t total = mblocks * ceil_div(y.c, NT);
     if (total > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "conv3d: grid too large");
     a.n_mblocks = (int32_t)mblocks;
+    a.stats = gn ? gn->ws : nullptr;
+    a.groups = gn ? gn->groups : 1;
+    a.nslots = a.nbt * a.nbh * a.nbw * wave_rows<NT>();
     hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
                        dim3((unsigned)total), dim3(kMfmaThreads), 0, stream, a);
     VAE_HIP_CHECK(hipGetLastError());
@@ -444,45 +525,48 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
 vae_status_t run_block(const vae_tensor_t& x, const void* w, const float* bias,
                        const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       hipStream_t stream) {
+                       const ConvGn* gn, hipStream_t stream) {
     switch (pick_block(box)) {
         case kBlk4x8x8:
-            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box,
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box, gn,
                                                                  stream);
         case kBlk4x4x16:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 4, 16>(x, w, bias, residual, y, box,
-                                                                  stream);
+                                                                  gn, stream);
         default:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 2, 8, 16>(x, w, bias, residual, y, box,
-                                                                  stream);
+                                                                  gn, stream);
     }
 }
 
 template <int NT, typename TI, typename TO, bool SPLIT>
 vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                      bool packed, hipStream_t stream) {
-    if (packed) return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, stream);
-    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, stream);
+                      bool packed, const ConvGn* gn, hipStream_t stream) {
+    if (packed)
+        return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, gn, stream);
+    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, gn, stream);
 }
 
 template <int NT, typename TI, bool SPLIT>
 vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bias,
                           const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                          bool packed, hipStream_t stream) {
+                          bool packed, const ConvGn* gn, hipStream_t stream) {
     if (y.dtype == VAE_DTYPE_F32)
-        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, stream);
-    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, stream);
+        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, gn, stream);
+    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, gn, stream);
 }
 
 template <int NT>
 vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                         bool split, bool packed, hipStream_t stream) {
+                         bool split, bool packed, const ConvGn* gn, hipStream_t stream) {
     if (x.dtype == VAE_DTYPE_BF16)
-        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, stream);
-    if (split) return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, packed, stream);
-    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, packed, stream);
+        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, gn,
+                                                 stream);
+    if (split)
+        return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, packed, gn, stream);
+    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, packed, gn, stream);
 }
 
 // Fragment-packed weights: [Cout/32][27 taps][Cin/32 chunks][kk 2][32 co][khalf 2][8 ci] bf16,
@@ -545,6 +629,21 @@ bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight
     return weight_dtype == VAE_DTYPE_BF16 && x.c % kCK == 0 && y.c % 4 == 0;
 }
 
+int64_t conv_gn_slots(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype,
+                      const Box& box, int32_t groups) {
+    if (!conv_uses_mfma(x, y, weight_dtype) || groups < 1 || y.c % groups) return 0;
+    const int64_t cpg = y.c / groups;
+    if (cpg % 4 || 32 % cpg) return 0;   // a lane's four channels, a wave's 32, hold whole groups
+    int tb = 2, hb = 8, wb = 16;
+    switch (pick_block(box)) {
+        case kBlk4x8x8: tb = 4; hb = 8; wb = 8; break;
+        case kBlk4x4x16: tb = 4; hb = 4; wb = 16; break;
+        default: break;
+    }
+    const int wm = y.c >= 128 ? wave_rows<128>() : wave_rows<64>();
+    return ceil_div(box.bt(), tb) * ceil_div(box.bh(), hb) * ceil_div(box.bw(), wb) * wm;
+}
+
 int64_t packed_weight_elems(int64_t cout, int64_t cin) {
     return ceil_div(cout, 32) * 32 * 27 * cin;
 }
@@ -561,15 +660,18 @@ vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void*
 
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
-                           const Box& box, int32_t flags, hipStream_t stream) {
+                           const Box& box, int32_t flags, hipStream_t stream, const ConvGn* gn) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
     const bool xf = x.dtype == VAE_DTYPE_F32;
     const bool split = (flags & VAE_CONV_SPLIT_FP32) != 0;
     const bool packed = (flags & VAE_CONV_PACKED_WEIGHTS) != 0;
+    if (gn && conv_gn_slots(x, y, weight_dtype, box, gn->groups) == 0)
+        return fail(VAE_ERR_UNSUPPORTED, "conv3d: fused GroupNorm statistics need the MFMA path "
+                                         "and 4, 8, 16 or 32 channels per group");
     if (conv_uses_mfma(x, y, weight_dtype)) {
         if (y.c >= 128)
-            return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, stream);
-        return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, stream);
+            return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, gn, stream);
+        return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, gn, stream);
     }
     if (packed) return fail(VAE_ERR_UNSUPPORTED, "packed weights need the MFMA path");
     if (weight_dtype == VAE_DTYPE_F32)

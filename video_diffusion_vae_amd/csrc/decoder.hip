@@ -57,6 +57,13 @@ int32_t gn_silu_dtype(const vae_decoder& d, int i) {
     return gn_silu_dtype(d.dtype, d.act_dtype, d.flags, d.layers.data(), (int)d.layers.size(), i);
 }
 
+// Whether the op after layer i starts with a GroupNorm of layer i's output.
+bool gn_follows(const vae_decoder& d, size_t i) {
+    if (i + 1 >= d.layers.size()) return false;
+    const int32_t op = d.layers[i + 1].op;
+    return op == VAE_OP_RES || op == VAE_OP_GN_SILU;
+}
+
 // Number of device pointers each op consumes.
 int ptrs_for(const vae_layer_desc_t& l) {
     switch (l.op) {
@@ -167,6 +174,20 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
                 r->gn, (int64_t)gn_stats_workspace(x, scaled_boxes(boxes, cur.t, ch, cw), d.groups));
             r->mr = std::max<int64_t>(r->mr, cur.n * d.groups * 2 * (int64_t)sizeof(float));
         }
+        // partials of GroupNorm statistics gathered by conv epilogues
+        const bool next_gn = gn_follows(d, i);
+        auto fused = [&](const Shape& xs, const Shape& ys) {
+            const vae_tensor_t x = tensor_of(nullptr, xs), y = tensor_of(nullptr, ys);
+            const int64_t slots = conv_gn_slots(x, y, d.dtype, whole_box(y), d.groups);
+            r->gn = std::max<int64_t>(r->gn, ys.n * d.groups * slots * 3 * (int64_t)sizeof(double));
+        };
+        if (l.op == VAE_OP_CONV && next_gn) fused(cur, s);
+        if (l.op == VAE_OP_RES) {
+            Shape xs = cur, ys = cur;
+            xs.dtype = d.dtype;
+            ys.dtype = d.act_dtype;
+            fused(xs, ys);
+        }
         if (l.op == VAE_OP_D2S || l.op == VAE_OP_NEAREST) {
             ch *= l.sh;
             cw *= l.sw;
@@ -222,21 +243,27 @@ struct Runner {
         return VAE_OK;
     }
 
+    bool stats_ready = false;  // mean/rstd already hold the statistics of the next GN's input
+
     vae_status_t gn(const vae_tensor_t& x, const vae_tensor_t& y, const BoxList& bl,
                     const void* gamma, const void* beta, int layer) {
         double* stats = reinterpret_cast<double*>(ws + L.gn);
         float* mr = reinterpret_cast<float*>(ws + L.mr);
-        VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
+        const bool fused = stats_ready;
+        if (!fused) VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
+        stats_ready = false;
         // the patch boxes partition the tensor, so one apply launch covers them all
         VAE_TRY(launch_gn_apply(x, whole_box(x), d->groups, mr, static_cast<const float*>(gamma),
                                 static_cast<const float*>(beta), true, y, s));
-        const double b = (double)numel(x) * elem_size(x.dtype);
-        return mark(VAE_KIND_GN, layer, 0.0, 3.0 * b);
+        const double xb = (double)numel(x) * elem_size(x.dtype);
+        const double yb = (double)numel(y) * elem_size(y.dtype);
+        return mark(VAE_KIND_GN, layer, 0.0, (fused ? 1.0 : 2.0) * xb + yb);
     }
 
-    // `wi` indexes d->ptrs: the conv's weight, followed by its bias.
+    // `wi` indexes d->ptrs: the conv's weight, followed by its bias. With `gn_next` the conv's
+    // epilogue also gathers the statistics of the GroupNorm that reads y.
     vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
-                      const vae_tensor_t& y, int layer) {
+                      const vae_tensor_t& y, int layer, bool gn_next) {
         int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
                          ? VAE_CONV_SPLIT_FP32
                          : 0;
@@ -245,12 +272,22 @@ struct Runner {
             w = d->packed[wi];
             cf |= VAE_CONV_PACKED_WEIGHTS;
         }
+        const int64_t slots =
+            gn_next ? conv_gn_slots(x, y, d->dtype, whole_box(y), d->groups) : 0;
+        const ConvGn g{reinterpret_cast<double*>(ws + L.gn), d->groups};
         VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res, y,
-                              whole_box(y), cf, s));
+                              whole_box(y), cf, s, slots > 0 ? &g : nullptr));
         const double flops = 2.0 * 27.0 * (double)x.c * (double)y.c * (double)positions(y);
         const double bytes = (double)numel(x) * elem_size(x.dtype) +
                              (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
-        return mark(VAE_KIND_CONV, layer, flops, bytes);
+        VAE_TRY(mark(VAE_KIND_CONV, layer, flops, bytes));
+        if (slots > 0) {
+            // merged into mean/rstd here; the time counts towards the GroupNorm that follows
+            VAE_TRY(launch_gn_finalize_slots(g.ws, slots, (int32_t)y.n, d->groups, d->eps,
+                                             reinterpret_cast<float*>(ws + L.mr), s));
+            stats_ready = true;
+        }
+        return VAE_OK;
     }
 
     // Run the whole plan on `in`; the last op writes `final_out`.
@@ -258,6 +295,7 @@ struct Runner {
                      const vae_tensor_t& final_out) {
         std::vector<Shape> shapes;
         walk(*d, shape_of(in), &shapes, nullptr, nullptr, nullptr);
+        stats_ready = false;
         vae_tensor_t cur = in;
         int cur_buf = -1;  // -1: the caller's input, never written
         int ch = 1, cw = 1;
@@ -276,7 +314,7 @@ struct Runner {
             if (l.op == VAE_OP_CONV) {
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = last ? final_out : buf(nb, os);
-                VAE_TRY(conv(cur, p, nullptr, y, layer));
+                VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, li)));
                 p += 2;
                 cur = y;
                 cur_buf = last ? -2 : nb;
@@ -290,10 +328,10 @@ struct Runner {
                 as.dtype = d->act_dtype;
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
-                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer));
+                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, true));
                 VAE_TRY(gn(t2, t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
                 vae_tensor_t y = last ? final_out : t2;
-                VAE_TRY(conv(t1, p + 6, &cur, y, layer));
+                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li)));
                 p += 8;
                 cur = y;
                 cur_buf = last ? -2 : b2;

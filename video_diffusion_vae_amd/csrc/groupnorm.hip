@@ -271,6 +271,20 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(const double* __r
     }
 }
 
+// grid (groups, N). ws: [N][G][slots][3], the layout a fused conv epilogue writes.
+__global__ __launch_bounds__(kThreads) void gn_finalize_slots_kernel(const double* __restrict__ ws,
+                                                                     int64_t slots, int32_t groups,
+                                                                     float eps, float* mean_rstd) {
+    const int g = blockIdx.x, n = blockIdx.y;
+    const double* base = ws + ((int64_t)n * groups + g) * slots * 3;
+    const Moments m = block_merge(base, 3, 0, (int)slots);
+    if (threadIdx.x == 0) {
+        const double var = m.n > 0.0 ? m.m2 / m.n : 0.0;
+        mean_rstd[((int64_t)n * groups + g) * 2] = (float)m.mean;
+        mean_rstd[((int64_t)n * groups + g) * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+    }
+}
+
 // grid (groups, N). part: [n_parts][N][G][3].
 __global__ __launch_bounds__(64) void gn_combine_kernel(const double* __restrict__ part,
                                                         int32_t n_parts, int32_t groups, float eps,
@@ -390,6 +404,15 @@ vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, i
                                float eps, float* mean_rstd, hipStream_t stream) {
     hipLaunchKernelGGL(gn_combine_kernel, dim3((unsigned)groups, (unsigned)n), dim3(64), 0, stream,
                        part, n_parts, groups, eps, mean_rstd);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+vae_status_t launch_gn_finalize_slots(const double* ws, int64_t slots, int32_t n, int32_t groups,
+                                      float eps, float* mean_rstd, hipStream_t stream) {
+    if (slots > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "too many statistics slots");
+    hipLaunchKernelGGL(gn_finalize_slots_kernel, dim3((unsigned)groups, (unsigned)n),
+                       dim3(kThreads), 0, stream, ws, slots, groups, eps, mean_rstd);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }

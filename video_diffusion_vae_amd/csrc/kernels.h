@@ -15,10 +15,20 @@ struct BoxList {
 };
 
 // ---- convolution ----
+// GroupNorm partials gathered by the MFMA conv's epilogue: fp64 (count, mean, M2) per
+// [N][groups][slots], for the output box as stored. conv_gn_slots() gives the slot count, or 0
+// when the shapes need the separate statistics pass.
+struct ConvGn {
+    double* ws;
+    int32_t groups;
+};
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
-                           const Box& box, int32_t flags, hipStream_t stream);
+                           const Box& box, int32_t flags, hipStream_t stream,
+                           const ConvGn* gn = nullptr);
 bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype);
+int64_t conv_gn_slots(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype,
+                      const Box& box, int32_t groups);
 // Fragment-packed bf16 weights (see conv3d.hip): element count and the packing kernel.
 int64_t packed_weight_elems(int64_t cout, int64_t cin);
 vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
@@ -33,6 +43,9 @@ vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_
                              hipStream_t stream);
 vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, int32_t groups,
                                float eps, float* mean_rstd, hipStream_t stream);
+// Partials [N][groups][slots][3] (as a fused conv writes them) -> mean/rstd [N][groups][2].
+vae_status_t launch_gn_finalize_slots(const double* ws, int64_t slots, int32_t n, int32_t groups,
+                                      float eps, float* mean_rstd, hipStream_t stream);
 vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t groups,
                              const float* mean_rstd, const float* gamma, const float* beta,
                              bool silu, const vae_tensor_t& y, hipStream_t stream);
