@@ -121,36 +121,59 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
                                        const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream);
 
-/* Causal Conv3d followed by the statistics of a GroupNorm over its output.
+/* Causal Conv3d with work fused into its output stage: a depth-to-space of the result, and the
+ * statistics of a GroupNorm that will read the result.
  *
- * The conv is the one vae_conv3d_causal computes, with the same arguments. In addition,
- * mean_rstd receives [N][groups][2] fp32: the mean of each (sample, group) over out_box and
- * 1/sqrt(var + eps). var is the biased variance about that global mean (divide by the count),
- * which is the statistic a patch-parallel GroupNorm must reproduce (P4, PatchGroupNorm commit).
- * The statistics are those of y as stored, e.g. after rounding to bf16, and include the residual.
+ * The conv is the one vae_conv3d_causal computes over out_box (in x's grid, NULL = all), with
+ * Cout = y.c * st * sh * sw output channels.
  *
- * On the MFMA path, with 4, 8, 16 or 32 channels per group, the conv's epilogue forms the
- * partials while the outputs are still in registers. They are (count, mean, M2) per output block
- * and group, merged with Chan's update in a fixed order (fp32 within a block, fp64 across blocks).
- * This saves a second read of y. Other shapes run a separate statistics pass over y, with the
- * same result up to rounding.
+ * Depth-to-space (d2s_st, d2s_sh, d2s_sw; all 0 = none). Conv output channel
+ * ((dt*sh + dh)*sw + dw)*C + c at (t, h, w) is written to channel c of y at
+ * (st*t + dt - (st-1), sh*h + dh, sw*w + dw). Positions whose frame is below 0 are dropped (the
+ * causal upsampler's first st-1 frames). y is [N, st*T-(st-1), sh*H, sw*W, C]. This is exactly
+ * what vae_upsample(VAE_UPSAMPLE_D2S) does to the conv output, without writing and re-reading
+ * that output. The upsampler moves channels into space (P4, LTX-2 decoder adapter commit).
  *
- * ws: device scratch of vae_conv3d_causal_gn_workspace() bytes, 16-byte aligned, owned by the
- * caller. Its contents are undefined afterwards. mean_rstd: device, N * groups * 2 floats.
- * Errors: those of vae_conv3d_causal; UNSUPPORTED when y's channels are not divisible by groups
- * or the shape is one vae_groupnorm_stats refuses; INVALID_ARG for eps < 0, a NULL mean_rstd or
- * an empty out_box; WORKSPACE for a short ws.
+ * GroupNorm statistics (gn_groups > 0). gn_mean_rstd receives [N][gn_groups][2] fp32: the mean
+ * of each (sample, group) of y's channels over the part of y this call writes, and
+ * 1/sqrt(var + gn_eps). var is the biased variance about that global mean (divide by the count),
+ * the statistic a patch-parallel GroupNorm must reproduce (P4, PatchGroupNorm commit). The
+ * statistics are those of y as stored (after any rounding to bf16, after the residual).
+ *  - On the MFMA path, with 4, 8, 16 or 32 channels per group (and C % 32 == 0 with a
+ *    depth-to-space), the conv's epilogue forms (count, mean, M2) per output block and group
+ *    while the outputs are in registers. These are merged with Chan's update in a fixed order:
+ *    fp32 within a block, fp64 across blocks. y is not read again.
+ *  - Other shapes run a separate statistics pass over y, with the same result up to rounding.
+ *
+ * Arguments:
+ *  residual: y's shape and dtype, or NULL.
+ *  ws / ws_bytes: device scratch of vae_conv3d_causal_fused_workspace() bytes, 16-byte aligned,
+ *  owned by the caller (unused without statistics). Its contents are undefined afterwards.
+ *
+ * Errors: those of vae_conv3d_causal; INVALID_ARG when y's shape does not match the factors;
+ * UNSUPPORTED for a depth-to-space off the MFMA path, for a channel count not divisible by
+ * gn_groups, or for a shape vae_groupnorm_stats refuses; INVALID_ARG for gn_eps < 0, a NULL
+ * gn_mean_rstd or an empty box with statistics; WORKSPACE for a short ws.
  */
-VAE_API vae_status_t vae_conv3d_causal_gn_workspace(const vae_tensor_t* x, const vae_tensor_t* y,
-                                                    int32_t weight_dtype,
-                                                    const vae_box_t* out_box, int32_t groups,
-                                                    size_t* bytes);
-VAE_API vae_status_t vae_conv3d_causal_gn(const vae_tensor_t* x, const void* weight,
-                                          int32_t weight_dtype, const float* bias,
-                                          const vae_tensor_t* residual, vae_tensor_t* y,
-                                          const vae_box_t* out_box, int32_t flags, int32_t groups,
-                                          float eps, float* mean_rstd, void* ws, size_t ws_bytes,
-                                          vae_stream_t stream);
+typedef struct vae_conv_fused {
+    const vae_tensor_t* x;
+    const void* weight;             /* [Cout][3][3][3][Cin], device */
+    int32_t weight_dtype;
+    int32_t flags;                  /* as for vae_conv3d_causal */
+    const float* bias;              /* [Cout] fp32, device, or NULL */
+    const vae_tensor_t* residual;
+    vae_tensor_t* y;
+    const vae_box_t* out_box;
+    int32_t d2s_st, d2s_sh, d2s_sw;
+    int32_t gn_groups;              /* 0: no statistics */
+    float gn_eps;
+    float* gn_mean_rstd;            /* device, N * gn_groups * 2 floats */
+    void* ws;
+    size_t ws_bytes;
+} vae_conv_fused_t;
+VAE_API vae_status_t vae_conv3d_causal_fused_workspace(const vae_conv_fused_t* args,
+                                                       size_t* bytes);
+VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_stream_t stream);
 
 /* Fragment-packed copy of bf16 conv weights, for the MFMA path. Layout:
  * [ceil(Cout/32)][27 taps][Cin/32][2][32][2][8], i.e. output channels in tiles of 32 and input

@@ -147,3 +147,26 @@ def test_workspace_query_needs_no_gpu(v):
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
                                          (8, 16, 32), patches=(1, 4)))
     dec.close()
+
+
+def test_fused_conv_validation_needs_no_gpu(v):
+    """Argument checks and the workspace query of vae_conv3d_causal_fused run on the host only
+    (host tensors stand in for device buffers; nothing is launched)."""
+    import torch
+    x = torch.zeros((1, 2, 4, 8, 64), dtype=torch.bfloat16)
+    w = torch.zeros((256, 3, 3, 3, 64), dtype=torch.bfloat16)
+    y = torch.zeros((1, 3, 8, 16, 32), dtype=torch.float32)   # d2s (2, 2, 2): 2T-1, 2H, 2W
+    # one 256-position block, eight sub-positions, one wave row: 8 slots per (sample, group)
+    n = v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), gn_groups=8)
+    assert n == 1 * 8 * 8 * 3 * 8
+    assert v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2)) == 0
+    with pytest.raises(v.VaeError) as e:          # y does not match the factors
+        v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(1, 2, 2))
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:          # a fused depth-to-space needs the MFMA path
+        x16 = torch.zeros((1, 2, 4, 8, 16), dtype=torch.bfloat16)
+        v.vae_conv3d_causal_fused_workspace(x16, w[..., :16], y, d2s=(2, 2, 2))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:          # groups must divide the channels
+        v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), gn_groups=5)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED

@@ -120,7 +120,8 @@ def test_conv3d_gn_statistics(v, case):
     rd = dev(r, odt) if use_res else None
     y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=tdt)
     mr = torch.zeros((n, groups, 2), dtype=torch.float32, device="cuda")
-    v.vae_conv3d_causal_gn(xd, wd, bd, rd, y, groups, 1e-6, mr, bx)
+    v.vae_conv3d_causal_fused(xd, wd, bd, rd, y, bx, gn_groups=groups, gn_eps=1e-6,
+                              gn_mean_rstd=mr)
     y0 = torch.full_like(y, 7.0)
     v.vae_conv3d_causal(xd, wd, bd, rd, y0, bx)
     torch.cuda.synchronize()
@@ -141,6 +142,80 @@ def test_conv3d_gn_statistics(v, case):
     v.vae_groupnorm_combine(part, 1, n, groups, 1e-6, mr2)
     torch.cuda.synchronize()
     np.testing.assert_allclose(got, mr2.cpu().numpy(), rtol=2e-5, atol=1e-6)
+
+
+CONV_D2S_CASES = [
+    # (N, T, H, W), Cin, C (channels after d2s), (st, sh, sw), in dtype, out dtype, split,
+    # box, GroupNorm groups (0: none)
+    ((1, 3, 5, 9), 64, 32, (2, 2, 2), "bf16", "f32", False, None, 8),
+    ((1, 4, 6, 7), 32, 64, (2, 2, 2), "f32", "f32", True, (1, 4, 1, 6, 2, 7), 16),
+    ((2, 2, 4, 10), 64, 32, (1, 2, 2), "bf16", "bf16", False, None, 4),
+    ((1, 1, 3, 5), 32, 128, (2, 2, 2), "bf16", "f32", False, None, 32),
+    ((1, 3, 4, 6), 32, 3, (1, 4, 4), "f32", "f32", True, None, 0),      # unpatchify-like
+    ((1, 2, 3, 5), 32, 3, (1, 4, 1), "bf16", "f32", False, None, 0),    # channel-wise stores
+]
+
+
+@pytest.mark.parametrize("case", CONV_D2S_CASES)
+def test_conv3d_fused_depth_to_space(v, case):
+    """Conv whose epilogue writes the depth-to-space of its output (with the causal frame drop),
+    optionally with the GroupNorm statistics of that result.
+    Checks:
+     - it matches the oracle conv followed by the oracle depth-to-space;
+     - it is bit-identical to the GPU conv followed by vae_upsample;
+     - the statistics match the oracle's over the part of y written."""
+    import torch
+    (n, t, h, w), cin, c, (st, sh, sw), idt, odt, split, bx, groups = case
+    cout = c * st * sh * sw
+    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 80 + CONV_D2S_CASES.index(case))
+    if idt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [17, cin], scale=1e-3))
+    if split:
+        hi = vae_synth.round_bf16(x).astype(np.float64)
+        xin = hi + vae_synth.round_bf16(x - hi).astype(np.float64)
+    else:
+        xin = vae_synth.round_bf16(x).astype(np.float64)
+    full = oracle.causal_conv3d(xin, wt, b)
+    bx_ = bx or (0, t, 0, h, 0, w)
+    tdt = torch.float32 if odt == "f32" else torch.bfloat16
+    xd = dev(x, idt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    flags = v.VAE_CONV_SPLIT_FP32 if split else 0
+    yshape = (n, st * t - (st - 1), sh * h, sw * w, c)
+    y = torch.full(yshape, 7.0, device="cuda", dtype=tdt)
+    mr = torch.zeros((n, max(groups, 1), 2), dtype=torch.float32, device="cuda")
+    v.vae_conv3d_causal_fused(xd, wd, bd, None, y, bx, flags, d2s=(st, sh, sw),
+                              gn_groups=groups, gn_eps=1e-6, gn_mean_rstd=mr)
+    # the two-step GPU path: conv into a full tensor, then depth-to-space of the box
+    y1 = torch.full((n, t, h, w, cout), 0.0, device="cuda", dtype=tdt)
+    v.vae_conv3d_causal(xd, wd, bd, None, y1, bx, flags)
+    y2 = torch.full(yshape, 7.0, device="cuda", dtype=tdt)
+    v.vae_upsample(y1, bx, v.VAE_UPSAMPLE_D2S, st, sh, sw, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    # against the oracle, over the part of y this call writes
+    ref = oracle.depth_to_space(full, st, sh, sw)
+    t0 = max(0, st * bx_[0] - (st - 1))
+    sl = (slice(None), slice(t0, st * bx_[1] - (st - 1)), slice(sh * bx_[2], sh * bx_[3]),
+          slice(sw * bx_[4], sw * bx_[5]))
+    got = host(y)
+    mask = np.zeros(got.shape, bool)
+    mask[sl] = True
+    assert np.all(got[~mask] == 7.0), "wrote outside the box's image"
+    g, rf = got[sl], ref[sl]
+    if odt == "f32":
+        assert rel_max_abs(g, rf) <= 1e-4
+    else:
+        assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
+    if groups:
+        rs = rf if odt == "f32" else vae_synth.round_bf16(rf).astype(np.float64)
+        cnt, mean, m2 = oracle.group_moments(rs, groups)
+        var = m2 / cnt
+        gm = mr.cpu().numpy().astype(np.float64)
+        tol = 1e-4 if odt == "f32" else 1e-3
+        assert np.all(np.abs(gm[..., 0] - mean) <= tol * np.sqrt(var) + 1e-6)
+        np.testing.assert_allclose(gm[..., 1], 1 / np.sqrt(var + 1e-6), rtol=tol)
 
 
 @pytest.mark.parametrize("shape,cin,cout,box", [((1, 3, 9, 19), 64, 256, None),

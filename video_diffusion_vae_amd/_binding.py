@@ -24,7 +24,7 @@ VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
 # Every symbol include/vae.h declares.
 EXPORTS = (
     "vae_last_error", "vae_last_error_info", "vae_version", "vae_conv3d_causal",
-    "vae_conv3d_causal_gn_workspace", "vae_conv3d_causal_gn", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_decoder_packed_weight_size",
+    "vae_conv3d_causal_fused_workspace", "vae_conv3d_causal_fused", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_decoder_packed_weight_size",
     "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_upsample",
@@ -43,6 +43,17 @@ class vae_tensor_t(ctypes.Structure):
 class vae_box_t(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in ("t0", "t1", "h0", "h1", "w0", "w1")]
 
+
+
+class vae_conv_fused_t(ctypes.Structure):
+    _fields_ = [("x", ctypes.POINTER(vae_tensor_t)), ("weight", ctypes.c_void_p),
+                ("weight_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("bias", ctypes.c_void_p), ("residual", ctypes.POINTER(vae_tensor_t)),
+                ("y", ctypes.POINTER(vae_tensor_t)), ("out_box", ctypes.POINTER(vae_box_t)),
+                ("d2s_st", ctypes.c_int32), ("d2s_sh", ctypes.c_int32), ("d2s_sw", ctypes.c_int32),
+                ("gn_groups", ctypes.c_int32), ("gn_eps", ctypes.c_float),
+                ("gn_mean_rstd", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
 
 class vae_error_info_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_int32), ("axis", ctypes.c_int32), ("extent", ctypes.c_int64),
@@ -94,8 +105,9 @@ def _load():
         "vae_last_error_info": ([ctypes.POINTER(vae_error_info_t)], I32),
         "vae_version": ([], I32),
         "vae_conv3d_causal": ([T, P, I32, P, T, T, B, I32, P], I32),
-        "vae_conv3d_causal_gn_workspace": ([T, T, I32, B, I32, ctypes.POINTER(SZ)], I32),
-        "vae_conv3d_causal_gn": ([T, P, I32, P, T, T, B, I32, I32, F, P, P, SZ, P], I32),
+        "vae_conv3d_causal_fused_workspace": ([ctypes.POINTER(vae_conv_fused_t),
+                                               ctypes.POINTER(SZ)], I32),
+        "vae_conv3d_causal_fused": ([ctypes.POINTER(vae_conv_fused_t), P], I32),
         "vae_conv_weight_pack_size": ([I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_conv_weight_pack": ([P, I32, I32, P, P], I32),
         "vae_decoder_packed_weight_size": ([P, ctypes.POINTER(SZ)], I32),
@@ -213,28 +225,46 @@ def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, strea
     return y
 
 
-def vae_conv3d_causal_gn_workspace(x, y, weight_dtype, out_box, groups):
-    xd, yd = tensor_desc(x), tensor_desc(y)
+def _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
+                gn_mean_rstd, ws):
+    keep = [tensor_desc(x), tensor_desc(y),
+            tensor_desc(residual) if residual is not None else None, box(out_box)]
+    a = vae_conv_fused_t()
+    a.x = ctypes.pointer(keep[0])
+    a.weight = _ptr(weight)
+    a.weight_dtype = _dtype_code(weight)
+    a.flags = int(flags)
+    a.bias = _ptr(bias)
+    a.residual = ctypes.pointer(keep[2]) if keep[2] is not None else None
+    a.y = ctypes.pointer(keep[1])
+    a.out_box = ctypes.pointer(keep[3]) if keep[3] is not None else None
+    a.d2s_st, a.d2s_sh, a.d2s_sw = (int(f) for f in d2s)
+    a.gn_groups = int(gn_groups)
+    a.gn_eps = float(gn_eps)
+    a.gn_mean_rstd = _ptr(gn_mean_rstd)
+    a.ws = _ptr(ws)
+    a.ws_bytes = ws.numel() if ws is not None else 0
+    return a, keep
+
+
+def vae_conv3d_causal_fused_workspace(x, weight, y, out_box=None, d2s=(0, 0, 0), gn_groups=0):
+    a, keep = _fused_args(x, weight, None, None, y, out_box, 0, d2s, gn_groups, 0.0, None, None)
     n = ctypes.c_size_t(0)
-    _check(LIB.vae_conv3d_causal_gn_workspace(ctypes.byref(xd), ctypes.byref(yd), int(weight_dtype),
-                                              _ref(box(out_box)), int(groups), ctypes.byref(n)))
+    _check(LIB.vae_conv3d_causal_fused_workspace(ctypes.byref(a), ctypes.byref(n)))
     return n.value
 
 
-def vae_conv3d_causal_gn(x, weight, bias, residual, y, groups, eps, mean_rstd, out_box=None,
-                         flags=0, ws=None, stream=None):
-    """Causal Conv3d plus the GroupNorm statistics of y over out_box: mean_rstd [N, groups, 2]
-    fp32 (device) receives (mean, 1/sqrt(var + eps))."""
-    xd, yd = tensor_desc(x), tensor_desc(y)
-    rd = tensor_desc(residual) if residual is not None else None
-    if ws is None:
-        ws = _workspace(vae_conv3d_causal_gn_workspace(x, y, _dtype_code(weight), out_box, groups),
+def vae_conv3d_causal_fused(x, weight, bias, residual, y, out_box=None, flags=0, d2s=(0, 0, 0),
+                            gn_groups=0, gn_eps=1e-6, gn_mean_rstd=None, ws=None, stream=None):
+    """Causal Conv3d with a fused depth-to-space (d2s = (st, sh, sw), y is then the upsampled
+    tensor) and/or the statistics of a GroupNorm over y (gn_mean_rstd [N, gn_groups, 2] fp32)."""
+    if ws is None and gn_groups:
+        ws = _workspace(vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups),
                         x.device)
-    _check(LIB.vae_conv3d_causal_gn(ctypes.byref(xd), _ptr(weight), _dtype_code(weight),
-                                    _ptr(bias), _ref(rd), ctypes.byref(yd), _ref(box(out_box)),
-                                    int(flags), int(groups), ctypes.c_float(eps), _ptr(mean_rstd),
-                                    _ptr(ws), ws.numel(), _stream(stream)))
-    return mean_rstd
+    a, keep = _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
+                          gn_mean_rstd, ws)
+    _check(LIB.vae_conv3d_causal_fused(ctypes.byref(a), _stream(stream)))
+    return y
 
 
 def vae_conv_weight_pack(weight, stream=None):

@@ -1,5 +1,6 @@
 // Exported C entry points: argument validation, thread-local error reporting, the host-only tile
 // split, and dispatch to the kernel launchers. No exception crosses this boundary.
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -243,15 +244,78 @@ vae_status_t check_conv(const vae_tensor_t* x, const void* weight, int32_t weigh
     return VAE_OK;
 }
 
-// Workspace of vae_conv3d_causal_gn: the fused partials, or the separate statistics pass's.
-size_t conv_gn_workspace(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype,
-                         const Box& box, int32_t groups, int64_t* slots) {
-    *slots = conv_gn_slots(x, y, weight_dtype, box, groups);
-    if (*slots > 0) return (size_t)(y.n * groups * *slots * 3) * sizeof(double);
+// The fused call's depth-to-space factors (0, 0, 0 reads as 1, 1, 1) and the box of y that the
+// conv's out_box covers.
+struct FusedPlan {
+    int32_t st, sh, sw, k;
+    Box cbox, ybox;
+};
+
+// `run`: the call itself (the workspace query needs no output pointers).
+vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
+    if (!a) return fail(VAE_ERR_INVALID_ARG, "args is NULL");
+    if (a->flags & ~(VAE_CONV_SPLIT_FP32 | VAE_CONV_PACKED_WEIGHTS))
+        return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
+    VAE_TRY(check_tensor(a->x, "x"));
+    VAE_TRY(check_tensor(a->y, "y"));
+    const vae_tensor_t& x = *a->x;
+    const vae_tensor_t& y = *a->y;
+    if (!a->weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
+    if (a->weight_dtype != VAE_DTYPE_BF16 && a->weight_dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_INVALID_ARG, "unknown weight dtype");
+    if (reinterpret_cast<uintptr_t>(a->weight) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "weight must be 16-byte aligned");
+    const bool none = a->d2s_st == 0 && a->d2s_sh == 0 && a->d2s_sw == 0;
+    p->st = none ? 1 : a->d2s_st;
+    p->sh = none ? 1 : a->d2s_sh;
+    p->sw = none ? 1 : a->d2s_sw;
+    if (p->st < 1 || p->sh < 1 || p->sw < 1)
+        return fail(VAE_ERR_INVALID_ARG, "d2s factors must all be 0 or all be >= 1");
+    p->k = p->st * p->sh * p->sw;
+    if (y.n != x.n || y.t != p->st * x.t - (p->st - 1) || y.h != p->sh * x.h ||
+        y.w != p->sw * x.w)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "y must be [N, st*T-(st-1), sh*H, sw*W, Cout/(st*sh*sw)] of x's [N, T, H, W]");
+    if (a->residual) {
+        VAE_TRY(check_tensor(a->residual, "residual"));
+        const vae_tensor_t& r = *a->residual;
+        if (!same_grid(r, y) || r.c != y.c || r.dtype != y.dtype)
+            return fail(VAE_ERR_INVALID_ARG, "residual must match y in shape and dtype");
+        if (overlaps(r, x)) return fail(VAE_ERR_INVALID_ARG, "residual overlaps x");
+    }
+    if (overlaps(x, y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
+    VAE_TRY(check_box(a->out_box, x, "out_box"));
+    p->cbox = to_box(a->out_box, x);
+    const Box& b = p->cbox;
+    p->ybox = Box{std::max(0, p->st * b.t0 - (p->st - 1)), p->st * b.t1 - (p->st - 1),
+                  p->sh * b.h0, p->sh * b.h1, p->sw * b.w0, p->sw * b.w1};
+    const bool mfma = conv_uses_mfma_c(x, y.c * p->k, a->weight_dtype);
+    if ((a->flags & VAE_CONV_PACKED_WEIGHTS) && !mfma)
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x.c,
+                    32);
+    if (p->k > 1 && !mfma)
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "a fused depth-to-space needs bf16 weights, Cin % 32 == 0 and Cout % 4 == 0",
+                    4, x.c, 32);
+    if (a->gn_groups) {
+        VAE_TRY(check_gn(a->y, a->gn_groups));
+        if (!(a->gn_eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "gn_eps must be >= 0");
+        if (run && !a->gn_mean_rstd) return fail(VAE_ERR_INVALID_ARG, "gn_mean_rstd is NULL");
+    }
+    return VAE_OK;
+}
+
+// Workspace of the fused call: the epilogue's partials, or the separate statistics pass's.
+size_t fused_workspace(const vae_conv_fused_t* a, const FusedPlan& p, int64_t* slots) {
+    *slots = 0;
+    if (!a->gn_groups) return 0;
+    *slots = conv_gn_slots(*a->x, a->y->c, a->weight_dtype, p.cbox, a->gn_groups, p.k);
+    if (*slots > 0) return (size_t)(a->y->n * a->gn_groups * *slots * 3) * sizeof(double);
     BoxList bl;
     bl.n = 1;
-    bl.b[0] = box;
-    return gn_stats_workspace(y, bl, groups);
+    bl.b[0] = p.ybox;
+    return gn_stats_workspace(*a->y, bl, a->gn_groups);
 }
 
 }  // namespace vae
@@ -282,52 +346,48 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
                          as_stream(stream));
 }
 
-VAE_API vae_status_t vae_conv3d_causal_gn_workspace(const vae_tensor_t* x, const vae_tensor_t* y,
-                                                    int32_t weight_dtype,
-                                                    const vae_box_t* out_box, int32_t groups,
-                                                    size_t* bytes) {
+VAE_API vae_status_t vae_conv3d_causal_fused_workspace(const vae_conv_fused_t* args,
+                                                       size_t* bytes) {
     clear_error();
     if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");
-    VAE_TRY(check_tensor(x, "x"));
-    VAE_TRY(check_gn(y, groups));
-    VAE_TRY(check_box(out_box, *y, "out_box"));
+    FusedPlan p;
+    VAE_TRY(check_fused(args, &p, false));
     int64_t slots = 0;
-    *bytes = conv_gn_workspace(*x, *y, weight_dtype, to_box(out_box, *y), groups, &slots);
+    *bytes = fused_workspace(args, p, &slots);
     return VAE_OK;
 }
 
-VAE_API vae_status_t vae_conv3d_causal_gn(const vae_tensor_t* x, const void* weight,
-                                          int32_t weight_dtype, const float* bias,
-                                          const vae_tensor_t* residual, vae_tensor_t* y,
-                                          const vae_box_t* out_box, int32_t flags, int32_t groups,
-                                          float eps, float* mean_rstd, void* ws, size_t ws_bytes,
-                                          vae_stream_t stream) {
+VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_stream_t stream) {
     clear_error();
-    VAE_TRY(check_conv(x, weight, weight_dtype, residual, y, out_box, flags));
-    VAE_TRY(check_gn(y, groups));
-    if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
-    if (!mean_rstd) return fail(VAE_ERR_INVALID_ARG, "mean_rstd is NULL");
-    const Box box = to_box(out_box, *y);
+    FusedPlan p;
+    VAE_TRY(check_fused(args, &p, true));
+    const vae_conv_fused_t& a = *args;
+    const vae_tensor_t& x = *a.x;
+    const vae_tensor_t& y = *a.y;
     int64_t slots = 0;
-    const size_t need = conv_gn_workspace(*x, *y, weight_dtype, box, groups, &slots);
-    if (!ws || ws_bytes < need)
-        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
-                    (int64_t)need);
-    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
-        return fail(VAE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    hipStream_t s = as_stream(stream);
-    double* part = static_cast<double*>(ws);
-    if (box.volume() == 0 || y->n == 0) return fail(VAE_ERR_INVALID_ARG, "empty out_box");
-    if (slots > 0) {
-        const ConvGn gn{part, groups};
-        VAE_TRY(launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, box, flags, s, &gn));
-        return launch_gn_finalize_slots(part, slots, (int32_t)y->n, groups, eps, mean_rstd, s);
+    const size_t need = fused_workspace(args, p, &slots);
+    if (a.gn_groups) {
+        if (!a.ws || a.ws_bytes < need)
+            return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)a.ws_bytes, -1,
+                        (int64_t)need);
+        if (reinterpret_cast<uintptr_t>(a.ws) % 16 != 0)
+            return fail(VAE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        if (p.cbox.volume() == 0 || p.ybox.volume() == 0 || x.n == 0)
+            return fail(VAE_ERR_INVALID_ARG, "statistics of an empty box");
     }
+    hipStream_t s = as_stream(stream);
+    double* part = static_cast<double*>(a.ws);
+    ConvFuse fz{slots > 0 ? part : nullptr, a.gn_groups ? a.gn_groups : 1, p.st, p.sh, p.sw};
+    VAE_TRY(launch_conv3d(x, a.weight, a.weight_dtype, a.bias, a.residual, y, p.cbox, a.flags, s,
+                          &fz));
+    if (!a.gn_groups) return VAE_OK;
+    if (slots > 0)
+        return launch_gn_finalize_slots(part, slots, (int32_t)y.n, a.gn_groups, a.gn_eps,
+                                        a.gn_mean_rstd, s);
     BoxList bl;
     bl.n = 1;
-    bl.b[0] = box;
-    VAE_TRY(launch_conv3d(*x, weight, weight_dtype, bias, residual, *y, box, flags, s));
-    return launch_gn_stats(*y, bl, groups, part, nullptr, mean_rstd, eps, s);
+    bl.b[0] = p.ybox;
+    return launch_gn_stats(y, bl, a.gn_groups, part, nullptr, a.gn_mean_rstd, a.gn_eps, s);
 }
 
 VAE_API vae_status_t vae_conv_weight_pack_size(int32_t cout, int32_t cin, size_t* bytes) {

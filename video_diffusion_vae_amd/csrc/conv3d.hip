@@ -58,8 +58,13 @@ struct MfmaArgs {
     Box box;
     int32_t nbt, nbh, nbw;   // blocks along each box axis
     int32_t n_mblocks;       // N * nbt * nbh * nbw
-    // Optional GroupNorm partials of the output as stored: fp64 (count, mean, M2) per
-    // (sample, group, slot), slot = position block * WM + wave row; null when not wanted.
+    // Output mapping. y may be the depth-to-space (st, sh, sw) of the conv output: conv channel
+    // ((dt*sh + dh)*sw + dw)*zc + c at (t, h, w) lands at channel c of y position
+    // (st*t + dt - (st-1), sh*h + dh, sw*w + dw); frames below 0 are dropped. Identity:
+    // st = sh = sw = 1 and zc = cout. The residual, if any, has y's shape.
+    int32_t yT, yH, yW, zc, st, sh, sw;
+    // Optional GroupNorm partials of y as stored: fp64 (count, mean, M2) per (sample, group of
+    // y's channels, slot), slot = (sub-position * position blocks + block) * WM + wave row.
     double* stats;
     int32_t groups, nslots;
 };
@@ -336,6 +341,21 @@ void conv3d_mfma_kernel(MfmaArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (co + k < a.cout) bv[k] = a.bias[co + k];
+    // Where this lane's four channels go in y. The sw * zc conv channels of one (dt, dh) are
+    // consecutive elements of one y row (dw, then c). When that count is a multiple of 4, a
+    // lane's aligned four channels stay together and are stored as one vector; otherwise each
+    // channel is placed on its own.
+    const int rowc = a.sw * a.zc;
+    const bool vec = rowc % 4 == 0;
+    const int srow = co / rowc, rem = co - srow * rowc;
+    const int sdh = srow % a.sh, sdt = srow / a.sh;
+    const int sub = co / a.zc, cz = co - sub * a.zc;   // sub-position and channel of y
+    auto y_off = [&](int t, int h, int w, int s_dt, int s_dh, int r) -> int64_t {
+        const int to = a.st * t + s_dt - (a.st - 1);
+        if (to < 0) return -1;   // causal drop
+        return ((((int64_t)n * a.yT + to) * a.yH + a.sh * h + s_dh) * a.yW + (int64_t)a.sw * w) *
+                   a.zc + r;
+    };
     // GroupNorm partials of this lane's four channels (one group): shifted sums, shift = the
     // lane's first stored value.
     float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
@@ -358,32 +378,44 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 float v[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) v[k] = ep[row * EP + c4 + k] + bv[k];
-                const int64_t o = ((((int64_t)n * a.T + t) * a.H + h) * a.W + w) * a.cout + co;
-                if (nv == 4) {
-                    if (res) {
-                        float rv[4];
-                        load4<TO>(res + o, rv);
+                if (vec) {
+                    const int64_t o = y_off(t, h, w, sdt, sdh, rem);
+                    if (o >= 0) {
+                        if (nv == 4) {
+                            if (res) {
+                                float rv[4];
+                                load4<TO>(res + o, rv);
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) v[k] += rv[k];
+                                for (int k = 0; k < 4; ++k) v[k] += rv[k];
+                            }
+                            store4<TO>(y + o, v);
+                        } else {
+                            for (int k = 0; k < nv; ++k) {
+                                if (res) v[k] += Elem<TO>::load(res + o + k);
+                                Elem<TO>::store(y + o + k, v[k]);
+                            }
+                        }
+                        if (a.stats) {
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                if (k < nv) {
+                                    const float q = stored<TO>(v[k]);
+                                    sk = sn == 0.0f ? q : sk;
+                                    const float d = q - sk;
+                                    s1 += d;
+                                    s2 = fmaf(d, d, s2);
+                                    sn += 1.0f;
+                                }
+                            }
+                        }
                     }
-                    store4<TO>(y + o, v);
                 } else {
                     for (int k = 0; k < nv; ++k) {
-                        if (res) v[k] += Elem<TO>::load(res + o + k);
-                        Elem<TO>::store(y + o + k, v[k]);
-                    }
-                }
-                if (a.stats) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        if (k < nv) {
-                            const float q = stored<TO>(v[k]);
-                            sk = sn == 0.0f ? q : sk;
-                            const float d = q - sk;
-                            s1 += d;
-                            s2 = fmaf(d, d, s2);
-                            sn += 1.0f;
-                        }
+                        const int ck = co + k, rk = ck / rowc;
+                        const int64_t o = y_off(t, h, w, rk / a.sh, rk % a.sh, ck - rk * rowc);
+                        if (o < 0) continue;
+                        if (res) v[k] += Elem<TO>::load(res + o);
+                        Elem<TO>::store(y + o, v[k]);
                     }
                 }
             }
@@ -401,7 +433,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             mean = sk + mk;
             m2 = fmaxf(s2 - s1 * mk, 0.0f);
         }
-        const int cpg = a.cout / a.groups;
+        const int cpg = a.zc / a.groups;
 #pragma unroll
         for (int off = 8; off < 64; off <<= 1) {
             const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
@@ -414,10 +446,11 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             chan_merge_f32(sn, mean, m2, nb, mb, m2b);
         }
         if (lane < LPR && lane % (cpg / 4) == 0 && co < a.cout) {
-            const int g = co / cpg;
+            const int g = cz / cpg;
+            const int nblk = a.nbt * a.nbh * a.nbw;
             const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
-            double* o = a.stats +
-                        (((int64_t)n * a.groups + g) * a.nslots + (int64_t)mb_local * WM + wave_m) * 3;
+            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
+            double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
             o[0] = sn;
             o[1] = mean;
             o[2] = m2;
@@ -493,7 +526,7 @@ constexpr int wave_rows() {
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
 vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
                        const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       const ConvGn* gn, hipStream_t stream) {
+                       const ConvFuse* fz, hipStream_t stream) {
     MfmaArgs a;
     a.x = x.data;
     a.w = static_cast<const uint16_t*>(w);
@@ -504,18 +537,25 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.H = (int32_t)x.h;
     a.W = (int32_t)x.w;
     a.cin = (int32_t)x.c;
-    a.cout = (int32_t)y.c;
+    a.st = fz ? fz->st : 1;
+    a.sh = fz ? fz->sh : 1;
+    a.sw = fz ? fz->sw : 1;
+    a.zc = (int32_t)y.c;
+    a.cout = (int32_t)(y.c * a.st * a.sh * a.sw);
+    a.yT = (int32_t)y.t;
+    a.yH = (int32_t)y.h;
+    a.yW = (int32_t)y.w;
     a.box = box;
     a.nbt = (int32_t)ceil_div(box.bt(), TB);
     a.nbh = (int32_t)ceil_div(box.bh(), HB);
     a.nbw = (int32_t)ceil_div(box.bw(), WB);
     int64_t mblocks = x.n * (int64_t)a.nbt * a.nbh * a.nbw;
-    int64_t total = mblocks * ceil_div(y.c, NT);
+    int64_t total = mblocks * ceil_div(a.cout, NT);
     if (total > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "conv3d: grid too large");
     a.n_mblocks = (int32_t)mblocks;
-    a.stats = gn ? gn->ws : nullptr;
-    a.groups = gn ? gn->groups : 1;
-    a.nslots = a.nbt * a.nbh * a.nbw * wave_rows<NT>();
+    a.stats = fz ? fz->gn_ws : nullptr;
+    a.groups = fz && fz->gn_ws ? fz->groups : 1;
+    a.nslots = (a.cout / a.zc) * a.nbt * a.nbh * a.nbw * wave_rows<NT>();
     hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
                        dim3((unsigned)total), dim3(kMfmaThreads), 0, stream, a);
     VAE_HIP_CHECK(hipGetLastError());
@@ -525,48 +565,48 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
 vae_status_t run_block(const vae_tensor_t& x, const void* w, const float* bias,
                        const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       const ConvGn* gn, hipStream_t stream) {
+                       const ConvFuse* fz, hipStream_t stream) {
     switch (pick_block(box)) {
         case kBlk4x8x8:
-            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box, gn,
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box, fz,
                                                                  stream);
         case kBlk4x4x16:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 4, 16>(x, w, bias, residual, y, box,
-                                                                  gn, stream);
+                                                                  fz, stream);
         default:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 2, 8, 16>(x, w, bias, residual, y, box,
-                                                                  gn, stream);
+                                                                  fz, stream);
     }
 }
 
 template <int NT, typename TI, typename TO, bool SPLIT>
 vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                      bool packed, const ConvGn* gn, hipStream_t stream) {
+                      bool packed, const ConvFuse* fz, hipStream_t stream) {
     if (packed)
-        return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, gn, stream);
-    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, gn, stream);
+        return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, fz, stream);
+    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, fz, stream);
 }
 
 template <int NT, typename TI, bool SPLIT>
 vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bias,
                           const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                          bool packed, const ConvGn* gn, hipStream_t stream) {
+                          bool packed, const ConvFuse* fz, hipStream_t stream) {
     if (y.dtype == VAE_DTYPE_F32)
-        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, gn, stream);
-    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, gn, stream);
+        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
+    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
 }
 
 template <int NT>
 vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                         bool split, bool packed, const ConvGn* gn, hipStream_t stream) {
+                         bool split, bool packed, const ConvFuse* fz, hipStream_t stream) {
     if (x.dtype == VAE_DTYPE_BF16)
-        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, gn,
+        return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, fz,
                                                  stream);
     if (split)
-        return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, packed, gn, stream);
-    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, packed, gn, stream);
+        return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, packed, fz, stream);
+    return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, packed, fz, stream);
 }
 
 // Fragment-packed weights: [Cout/32][27 taps][Cin/32 chunks][kk 2][32 co][khalf 2][8 ci] bf16,
@@ -625,14 +665,17 @@ vae_status_t run_direct_out(const vae_tensor_t& x, const void* w, const float* b
 
 }  // namespace
 
-bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype) {
-    return weight_dtype == VAE_DTYPE_BF16 && x.c % kCK == 0 && y.c % 4 == 0;
+// Convs that run on the matrix cores: bf16 weights, Cin % 32 == 0, Cout % 4 == 0.
+bool conv_uses_mfma_c(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype) {
+    return weight_dtype == VAE_DTYPE_BF16 && x.c % kCK == 0 && cout % 4 == 0;
 }
 
-int64_t conv_gn_slots(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype,
-                      const Box& box, int32_t groups) {
-    if (!conv_uses_mfma(x, y, weight_dtype) || groups < 1 || y.c % groups) return 0;
-    const int64_t cpg = y.c / groups;
+int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, const Box& box,
+                      int32_t groups, int32_t k) {
+    const int64_t cout = yc * k;
+    if (!conv_uses_mfma_c(x, cout, weight_dtype) || groups < 1 || yc % groups) return 0;
+    if (k > 1 && yc % 32) return 0;      // a wave's 32 channels share one sub-position
+    const int64_t cpg = yc / groups;
     if (cpg % 4 || 32 % cpg) return 0;   // a lane's four channels, a wave's 32, hold whole groups
     int tb = 2, hb = 8, wb = 16;
     switch (pick_block(box)) {
@@ -640,8 +683,8 @@ int64_t conv_gn_slots(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weig
         case kBlk4x4x16: tb = 4; hb = 4; wb = 16; break;
         default: break;
     }
-    const int wm = y.c >= 128 ? wave_rows<128>() : wave_rows<64>();
-    return ceil_div(box.bt(), tb) * ceil_div(box.bh(), hb) * ceil_div(box.bw(), wb) * wm;
+    const int wm = cout >= 128 ? wave_rows<128>() : wave_rows<64>();
+    return k * ceil_div(box.bt(), tb) * ceil_div(box.bh(), hb) * ceil_div(box.bw(), wb) * wm;
 }
 
 int64_t packed_weight_elems(int64_t cout, int64_t cin) {
@@ -658,20 +701,28 @@ vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void*
     return VAE_OK;
 }
 
+bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype) {
+    return conv_uses_mfma_c(x, y.c, weight_dtype);
+}
+
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
-                           const Box& box, int32_t flags, hipStream_t stream, const ConvGn* gn) {
+                           const Box& box, int32_t flags, hipStream_t stream, const ConvFuse* fz) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
     const bool xf = x.dtype == VAE_DTYPE_F32;
     const bool split = (flags & VAE_CONV_SPLIT_FP32) != 0;
     const bool packed = (flags & VAE_CONV_PACKED_WEIGHTS) != 0;
-    if (gn && conv_gn_slots(x, y, weight_dtype, box, gn->groups) == 0)
+    const int32_t k = fz ? fz->st * fz->sh * fz->sw : 1;
+    const int64_t cout = y.c * k;
+    if (fz && k > 1 && !conv_uses_mfma_c(x, cout, weight_dtype))
+        return fail(VAE_ERR_UNSUPPORTED, "conv3d: a fused depth-to-space needs the MFMA path");
+    if (fz && fz->gn_ws && conv_gn_slots(x, y.c, weight_dtype, box, fz->groups, k) == 0)
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: fused GroupNorm statistics need the MFMA path "
                                          "and 4, 8, 16 or 32 channels per group");
-    if (conv_uses_mfma(x, y, weight_dtype)) {
-        if (y.c >= 128)
-            return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, gn, stream);
-        return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, gn, stream);
+    if (conv_uses_mfma_c(x, cout, weight_dtype)) {
+        if (cout >= 128)
+            return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, fz, stream);
+        return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, fz, stream);
     }
     if (packed) return fail(VAE_ERR_UNSUPPORTED, "packed weights need the MFMA path");
     if (weight_dtype == VAE_DTYPE_F32)

@@ -176,17 +176,22 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         }
         // partials of GroupNorm statistics gathered by conv epilogues
         const bool next_gn = gn_follows(d, i);
-        auto fused = [&](const Shape& xs, const Shape& ys) {
-            const vae_tensor_t x = tensor_of(nullptr, xs), y = tensor_of(nullptr, ys);
-            const int64_t slots = conv_gn_slots(x, y, d.dtype, whole_box(y), d.groups);
+        auto fused = [&](const Shape& xs, const Shape& ys, int32_t k) {
+            const vae_tensor_t x = tensor_of(nullptr, xs);
+            const int64_t slots = conv_gn_slots(x, ys.c, d.dtype, whole_box(x), d.groups, k);
             r->gn = std::max<int64_t>(r->gn, ys.n * d.groups * slots * 3 * (int64_t)sizeof(double));
         };
-        if (l.op == VAE_OP_CONV && next_gn) fused(cur, s);
+        if (l.op == VAE_OP_CONV && next_gn) fused(cur, s, 1);
+        if (l.op == VAE_OP_CONV && i + 1 < d.layers.size() && d.layers[i + 1].op == VAE_OP_D2S &&
+            gn_follows(d, i + 1)) {
+            const vae_layer_desc_t& u = d.layers[i + 1];
+            fused(cur, shapes[i + 1], u.st * u.sh * u.sw);
+        }
         if (l.op == VAE_OP_RES) {
             Shape xs = cur, ys = cur;
             xs.dtype = d.dtype;
             ys.dtype = d.act_dtype;
-            fused(xs, ys);
+            fused(xs, ys, 1);
         }
         if (l.op == VAE_OP_D2S || l.op == VAE_OP_NEAREST) {
             ch *= l.sh;
@@ -261,9 +266,11 @@ struct Runner {
     }
 
     // `wi` indexes d->ptrs: the conv's weight, followed by its bias. With `gn_next` the conv's
-    // epilogue also gathers the statistics of the GroupNorm that reads y.
+    // epilogue also gathers the statistics of the GroupNorm that reads y. `up` (a D2S layer or
+    // null) makes y the depth-to-space of the conv output, written by the conv's epilogue.
     vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
-                      const vae_tensor_t& y, int layer, bool gn_next) {
+                      const vae_tensor_t& y, int layer, bool gn_next,
+                      const vae_layer_desc_t* up = nullptr) {
         int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
                          ? VAE_CONV_SPLIT_FP32
                          : 0;
@@ -272,18 +279,22 @@ struct Runner {
             w = d->packed[wi];
             cf |= VAE_CONV_PACKED_WEIGHTS;
         }
+        const int32_t k = up ? up->st * up->sh * up->sw : 1;
+        const int64_t cout = y.c * k;
         const int64_t slots =
-            gn_next ? conv_gn_slots(x, y, d->dtype, whole_box(y), d->groups) : 0;
-        const ConvGn g{reinterpret_cast<double*>(ws + L.gn), d->groups};
+            gn_next ? conv_gn_slots(x, y.c, d->dtype, whole_box(x), d->groups, k) : 0;
+        double* part = reinterpret_cast<double*>(ws + L.gn);
+        const ConvFuse fz{slots > 0 ? part : nullptr, d->groups, up ? up->st : 1,
+                          up ? up->sh : 1, up ? up->sw : 1};
         VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res, y,
-                              whole_box(y), cf, s, slots > 0 ? &g : nullptr));
-        const double flops = 2.0 * 27.0 * (double)x.c * (double)y.c * (double)positions(y);
+                              whole_box(x), cf, s, &fz));
+        const double flops = 2.0 * 27.0 * (double)x.c * (double)cout * (double)positions(x);
         const double bytes = (double)numel(x) * elem_size(x.dtype) +
                              (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
         VAE_TRY(mark(VAE_KIND_CONV, layer, flops, bytes));
         if (slots > 0) {
             // merged into mean/rstd here; the time counts towards the GroupNorm that follows
-            VAE_TRY(launch_gn_finalize_slots(g.ws, slots, (int32_t)y.n, d->groups, d->eps,
+            VAE_TRY(launch_gn_finalize_slots(part, slots, (int32_t)y.n, d->groups, d->eps,
                                              reinterpret_cast<float*>(ws + L.mr), s));
             stats_ready = true;
         }
@@ -312,12 +323,24 @@ struct Runner {
             const Shape& os = shapes[li];
             const int layer = (int)li;
             if (l.op == VAE_OP_CONV) {
+                // a depth-to-space right after the conv is done by the conv's epilogue
+                const bool fuse_up = li + 1 < d->layers.size() &&
+                                     d->layers[li + 1].op == VAE_OP_D2S &&
+                                     conv_uses_mfma_c(cur, l.cout, d->dtype);
+                const size_t lo = fuse_up ? li + 1 : li;
+                const bool out_last = lo + 1 == d->layers.size();
                 const int nb = free_buf(cur_buf, -1);
-                vae_tensor_t y = last ? final_out : buf(nb, os);
-                VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, li)));
+                vae_tensor_t y = out_last ? final_out : buf(nb, shapes[lo]);
+                VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, lo),
+                             fuse_up ? &d->layers[li + 1] : nullptr));
                 p += 2;
                 cur = y;
-                cur_buf = last ? -2 : nb;
+                cur_buf = out_last ? -2 : nb;
+                if (fuse_up) {
+                    ch *= d->layers[li + 1].sh;
+                    cw *= d->layers[li + 1].sw;
+                    li = lo;
+                }
             } else if (l.op == VAE_OP_RES) {
                 // x -> GN1 -> t1 -> conv1 -> t2 -> GN2 -> t1 -> conv2 (+ x) -> t2
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);

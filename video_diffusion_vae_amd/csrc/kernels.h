@@ -15,20 +15,26 @@ struct BoxList {
 };
 
 // ---- convolution ----
-// GroupNorm partials gathered by the MFMA conv's epilogue: fp64 (count, mean, M2) per
-// [N][groups][slots], for the output box as stored. conv_gn_slots() gives the slot count, or 0
-// when the shapes need the separate statistics pass.
-struct ConvGn {
-    double* ws;
+// Optional work fused into the MFMA conv's epilogue:
+//  - depth-to-space (st, sh, sw), st = sh = sw = 1 for none: y is then the depth-to-space of the
+//    conv output (channels y.c * st * sh * sw), with the causal drop of the first st-1 frames;
+//  - GroupNorm partials of y as stored (gn_ws non-null): fp64 (count, mean, M2) per
+//    [N][groups][slots]; conv_gn_slots() gives the slot count, or 0 when the shapes need the
+//    separate statistics pass.
+struct ConvFuse {
+    double* gn_ws;
     int32_t groups;
+    int32_t st, sh, sw;
 };
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
                            const Box& box, int32_t flags, hipStream_t stream,
-                           const ConvGn* gn = nullptr);
+                           const ConvFuse* fz = nullptr);
 bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype);
-int64_t conv_gn_slots(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype,
-                      const Box& box, int32_t groups);
+bool conv_uses_mfma_c(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype);
+// yc: channels of y; k = st * sh * sw of the fused depth-to-space (1 for none).
+int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, const Box& box,
+                      int32_t groups, int32_t k);
 // Fragment-packed bf16 weights (see conv3d.hip): element count and the packing kernel.
 int64_t packed_weight_elems(int64_t cout, int64_t cin);
 vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
