@@ -1,463 +1,27 @@
-// Causal Conv3d (3x3x3, stride 1) on channels-last (NDHWC) activations.
-//
-// bf16 weights: implicit GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
-//  - GEMM view: M = output positions, N = Cout, K = 27 * Cin, ordered (channel chunk, tap).
-//  - One workgroup (4 waves) computes a block of 256 output positions for NT output channels.
-//    The block is TB x HB x WB positions (2x8x16, 4x8x8 or 4x4x16, whichever pads the box least).
-//    Each wave owns 32 output channels and 256 * 32 / NT positions (32x32 MFMA tiles): at NT = 128
-//    a wave covers all 256 positions. Each weight fragment it loads then feeds eight MFMAs. Its
-//    128 accumulator registers allow two waves per SIMD, i.e. two workgroups per CU, so one
-//    workgroup's tile staging overlaps the other's MFMA work.
-//  - Input (A operand). For each 32-channel chunk the block's input tile is staged in LDS once:
-//    (TB+2) x (HB+2) x (WB+2) positions x 32 channels, i.e. the block, a one-row halo on each
-//    spatial side, and the two earlier frames. All 27 taps read their A fragments from that tile
-//    at shifted offsets. The halo and the causal frame clamp are resolved while the tile is
-//    loaded: the halo is the neighbouring data of the same tensor, read in place; rows outside
-//    the image become zeros; a frame index below 0 reads frame 0. The pages motivate this: a halo
-//    built by concatenation cost 1.31x ("[TRTLLM-14123][feat] add ParallelVAE_TrtllmWan for native
-//    Wan VAE", Description). LDS rows are padded from 64 to 80 bytes, so the 16-byte reads of
-//    8 consecutive lanes hit 8 distinct 16-byte bank groups.
-//  - Weights (B operand). They go straight from global memory (L2-resident per XCD) into
-//    registers in MFMA fragment order, prefetched one tap ahead. The tap loop therefore has no
-//    barriers and LDS carries only A.
-//  - fp32 inputs are rounded to bf16 (nearest-even) as they are staged, because MFMA operands are
-//    bf16. Accumulation is fp32. With the split flag an fp32 input is applied as two bf16
-//    operands, hi = bf16(x) and lo = bf16(x - hi), so about 16 significant bits of x reach the
-//    matrix cores and the MFMA work doubles. A chunk then holds 16 channels: its LDS row carries
-//    their hi halves in the first 32 bytes and their lo halves in the next 32. The two k steps of
-//    a tap read hi and lo against the same weight fragment. Each fp32 value is loaded once, and
-//    the weight loads per MFMA halve.
-//  - Epilogue: each wave parks one 32 x 32 accumulator tile at a time in LDS (reusing the input
-//    tile), then every lane writes four consecutive channels with one 16-byte (fp32) or 8-byte
-//    (bf16) store. Bias and residual are added on the way.
-//  - Workgroups are ordered output-channel tile slowest, and remapped so that each XCD (the
-//    hardware deals workgroup i to XCD i % 8) runs a contiguous range of them. An XCD then keeps
-//    one weight slice in its own L2 while it streams input blocks.
-// fp32 weights, or Cin % 32 != 0, or Cout % 4 != 0: a direct kernel, one thread per output.
-#include "kernels.h"
+// Causal Conv3d (3x3x3, stride 1) on channels-last (NDHWC) activations: dispatch, weight packing
+// and the direct path.
+//  - bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (conv3d_mfma.h).
+//  - Otherwise a direct kernel computes one output per thread with fp32 accumulation.
+#include "conv3d_mfma.h"
 
 namespace vae {
+namespace mfma {
+// instantiated in conv3d_mfma_*.hip
+#define VAE_MFMA_EXTERN(NT, TI, SPLIT)                                                         \
+    extern template vae_status_t run_mfma_out<NT, TI, SPLIT>(                                 \
+        const vae_tensor_t&, const void*, const float*, const vae_tensor_t*, const vae_tensor_t&, \
+        const Box&, bool, const ConvFuse*, hipStream_t);
+VAE_MFMA_EXTERN(128, uint16_t, false)
+VAE_MFMA_EXTERN(128, float, false)
+VAE_MFMA_EXTERN(128, float, true)
+VAE_MFMA_EXTERN(64, uint16_t, false)
+VAE_MFMA_EXTERN(64, float, false)
+VAE_MFMA_EXTERN(64, float, true)
+#undef VAE_MFMA_EXTERN
+}  // namespace mfma
+
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-
-constexpr int kCK = 32;                              // input channels per LDS chunk
-constexpr int kRow = kCK * 2 + 16;                   // padded LDS row, bytes
-constexpr int kMfmaWaves = 4;                        // waves per workgroup
-constexpr int kMfmaThreads = kMfmaWaves * 64;
-constexpr int kXcds = 8;
-
-struct MfmaArgs {
-    const void* x;
-    const uint16_t* w;
-    const float* bias;
-    const void* res;
-    void* y;
-    int32_t T, H, W, cin, cout;
-    Box box;
-    int32_t nbt, nbh, nbw;   // blocks along each box axis
-    int32_t n_mblocks;       // N * nbt * nbh * nbw
-    // Output mapping. y may be the depth-to-space (st, sh, sw) of the conv output: conv channel
-    // ((dt*sh + dh)*sw + dw)*zc + c at (t, h, w) lands at channel c of y position
-    // (st*t + dt - (st-1), sh*h + dh, sw*w + dw); frames below 0 are dropped. Identity:
-    // st = sh = sw = 1 and zc = cout. The residual, if any, has y's shape.
-    int32_t yT, yH, yW, zc, st, sh, sw;
-    // Optional GroupNorm partials of y as stored: fp64 (count, mean, M2) per (sample, group of
-    // y's channels, slot), slot = (sub-position * position blocks + block) * WM + wave row.
-    double* stats;
-    int32_t groups, nslots;
-};
-
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-    int per = total / kXcds;
-    int full = per * kXcds;
-    if (bid >= full) return bid;
-    return (bid % kXcds) * per + bid / kXcds;
-}
-
-// 8 input channels starting at p, as 8 bf16 in one 16-byte word.
-template <typename TI> __device__ __forceinline__ uint4 load8(const TI* p);
-template <> __device__ __forceinline__ uint4 load8<uint16_t>(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-template <> __device__ __forceinline__ uint4 load8<float>(const float* p) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    uint4 r;
-    r.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
-    r.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
-    r.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
-    r.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
-    return r;
-}
-
-// The hi + lo bf16 split of 8 fp32 values: hi = bf16(x), lo = bf16(x - hi).
-template <typename TI> __device__ __forceinline__ void split8(const TI* p, uint4& hi, uint4& lo);
-template <> __device__ __forceinline__ void split8<uint16_t>(const uint16_t* p, uint4& hi,
-                                                             uint4& lo) {
-    hi = *reinterpret_cast<const uint4*>(p);
-    lo = make_uint4(0, 0, 0, 0);
-}
-template <> __device__ __forceinline__ void split8<float>(const float* p, uint4& hi, uint4& lo) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-        const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-        h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-    hi = make_uint4(h[0], h[1], h[2], h[3]);
-    lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-template <typename TO> __device__ __forceinline__ void load4(const TO* p, float* v);
-template <> __device__ __forceinline__ void load4<float>(const float* p, float* v) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-}
-template <> __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p);
-    v[0] = bf16_to_f32((uint16_t)(a.x & 0xffff)); v[1] = bf16_to_f32((uint16_t)(a.x >> 16));
-    v[2] = bf16_to_f32((uint16_t)(a.y & 0xffff)); v[3] = bf16_to_f32((uint16_t)(a.y >> 16));
-}
-template <typename TO> __device__ __forceinline__ void store4(TO* p, const float* v);
-template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float* v) {
-    uint2 a;
-    a.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    a.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = a;
-}
-
-// The value an output element holds once stored.
-template <typename TO> __device__ __forceinline__ float stored(float v);
-template <> __device__ __forceinline__ float stored<float>(float v) { return v; }
-template <> __device__ __forceinline__ float stored<uint16_t>(float v) {
-    return bf16_to_f32(f32_to_bf16(v));
-}
-
-// Chan's pairwise update of (count, mean, M2) with another partial, in fp32.
-__device__ __forceinline__ void chan_merge_f32(float& n, float& mean, float& m2, float nb,
-                                               float mb, float m2b) {
-    const float t = n + nb;
-    if (nb > 0.0f && n > 0.0f) {
-        const float d = mb - mean;
-        mean += d * (nb / t);
-        m2 += m2b + d * d * (n * nb / t);
-    } else if (nb > 0.0f) {
-        mean = mb;
-        m2 = m2b;
-    }
-    n = t;
-}
-
-// Staged input tile: (TB+2) x (HB+2) rows of (WB+2) positions, 80 bytes per position. The row
-// pitch is chosen for conflict-free 16-byte A-fragment reads. A fragment read covers
-//  - 16 positions of one row plus 16 of the next (WB = 16), or
-//  - 8 positions of each of four rows (WB = 8).
-// Measured with the LDS bank-conflict counter on gfx950, such reads are conflict-free only when
-// the row pitch is 0 mod 256 bytes (WB = 16) or 128 mod 256 bytes (WB = 8). The pitch is 1536 or
-// 896 bytes.
-template <int TB, int HB, int WB>
-struct BlockShape {
-    static_assert(TB * HB * WB == 256, "a block is 256 output positions");
-    static constexpr int HT = TB + 2, HH = HB + 2, HW = WB + 2;
-    static constexpr int kPos = HT * HH * HW;       // input positions staged per chunk
-    static constexpr int kPitch = WB == 16 ? 1536 : 896;
-    static_assert(HW * kRow <= kPitch, "a row must fit its pitch");
-    static constexpr int kBytes = HT * HH * kPitch;
-};
-
-template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
-__global__ __launch_bounds__(kMfmaThreads, 2)
-void conv3d_mfma_kernel(MfmaArgs a) {
-    using S = BlockShape<TB, HB, WB>;
-    constexpr int HH = S::HH, HW = S::HW;
-    constexpr int RP = S::kPitch;
-    __shared__ __attribute__((aligned(16))) uint8_t halo[S::kBytes];
-
-    // WNN waves across the NT output channels (32 each), WM across the 256 positions.
-    constexpr int WNN = NT / 32;
-    constexpr int WM = kMfmaWaves / WNN;
-    constexpr int MW = 256 / WM;       // positions per wave
-    constexpr int MI = MW / 32;        // 32-row MFMA tiles per wave
-    constexpr int NB = 2;              // weight fragments are prefetched one tap ahead
-    static_assert(WNN * WM == kMfmaWaves && MI >= 1, "wave grid");
-
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = logical / a.n_mblocks;
-    int mb = logical - nt * a.n_mblocks;
-    const int bw_i = mb % a.nbw;
-    mb /= a.nbw;
-    const int bh_i = mb % a.nbh;
-    mb /= a.nbh;
-    const int bt_i = mb % a.nbt;
-    const int n = mb / a.nbt;
-    const int t_blk = a.box.t0 + bt_i * TB;
-    const int h_blk = a.box.h0 + bh_i * HB;
-    const int w_blk = a.box.w0 + bw_i * WB;
-    const int n_blk = nt * NT;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wave_m = wave / WNN;    // which MW of the block's 256 positions
-    const int wave_n = wave % WNN;    // which 32 of the NT output channels
-    const int lrow = lane & 31;
-    const int khalf = lane >> 5;      // which 8 of the 16 k values this lane feeds
-
-    const int64_t cin = a.cin;
-    const TI* xn = static_cast<const TI*>(a.x) + (int64_t)n * a.T * a.H * a.W * cin;
-
-    f32x16_t acc[MI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-
-    // LDS byte offset of this lane's A row (tap 0,0,0) in each of the MI sub-tiles
-    int a_off[MI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int m = wave_m * MW + i * 32 + lrow;
-        const int tb = m / (HB * WB), hb = (m / WB) % HB, wb = m % WB;
-        a_off[i] = (tb * HH + hb) * RP + wb * kRow + khalf * 16;
-    }
-    // This lane's weights: B column lrow of the wave's 32-channel tile, k half `khalf`.
-    // Standard layout [Cout][27][Cin]: 16 bytes of one weight row per fragment.
-    // Packed layout (see pack_weights_kernel): the 64 lanes of a fragment read 1 KB contiguously.
-    const int nch = a.cin / kCK;
-    const int co_tile = n_blk + wave_n * 32;
-    const bool b_ok = PACKED ? co_tile < a.cout : co_tile + lrow < a.cout;
-    const uint16_t* b_ptr =
-        PACKED ? a.w + (int64_t)(b_ok ? co_tile >> 5 : 0) * 27 * nch * 1024 + lrow * 16 + khalf * 8
-               : a.w + (int64_t)(b_ok ? co_tile + lrow : 0) * 27 * cin + khalf * 8;
-    // Weight fragments per tap: one per k step, or one for both (hi and lo) with the split.
-    constexpr int KB = SPLIT ? 1 : 2;
-    uint4 bq[NB][KB];
-    auto load_b = [&](int buf, int tap, int c0) {
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-            // split chunks are 16 channels: the k-step half of a packed 32-channel block
-            const int half = SPLIT ? (c0 >> 4) & 1 : kk;
-            const int64_t off = PACKED ? ((int64_t)tap * nch + (c0 >> 5)) * 1024 + half * 512
-                                       : (int64_t)tap * cin + c0 + kk * 16;
-            // Unconditional: b_ptr points at valid weights even for columns past Cout, whose
-            // outputs are never stored. A branch here would split the tap loop into blocks the
-            // scheduler cannot overlap, and force a full wait on every prefetch.
-            bq[buf][kk] = *reinterpret_cast<const uint4*>(b_ptr + off);
-        }
-    };
-
-    constexpr int CK = SPLIT ? 16 : kCK;       // input channels per staged chunk
-    constexpr int UPP = SPLIT ? 2 : 4;         // staging units per position (8 channels each)
-    const int n_chunks = a.cin / CK;
-    for (int kc = 0; kc < n_chunks; ++kc) {
-        const int c0 = kc * CK;
-        load_b(0, 0, c0);             // in flight while the input tile is staged
-        __syncthreads();              // the previous chunk's LDS reads are done
-        for (int u = tid; u < S::kPos * UPP; u += kMfmaThreads) {
-            const int pos = u / UPP, g = u % UPP;
-            const int f = pos / (HH * HW);
-            const int rem = pos - f * (HH * HW);
-            const int r = rem / HW;
-            const int c = rem - r * HW;
-            int tg = t_blk - 2 + f;
-            tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
-            const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
-            uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
-            uint4 vl = make_uint4(0, 0, 0, 0);
-            if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
-                const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
-                if constexpr (SPLIT) split8<TI>(src, v, vl);
-                else v = load8<TI>(src);
-            }
-            uint8_t* dst = &halo[(f * HH + r) * RP + c * kRow + g * 16];
-            *reinterpret_cast<uint4*>(dst) = v;            // split: hi in bytes 0..31 of the row
-            if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = vl;  // lo in bytes 32..63
-        }
-        __syncthreads();
-
-        // 54 k steps (27 taps x 2). The A fragments of step s + 1 are read from LDS while the
-        // MFMAs of step s run; the weights of tap + 1 are fetched during tap.
-        bf16x8_t af[2][MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-            af[0][i] = *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i]]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int step = 0; step < 54; ++step) {
-            const int tap = step >> 1, kk = step & 1;
-            if (kk == 0 && tap + 1 < 27) load_b((tap + 1) % NB, tap + 1, c0);
-            if (step + 1 < 54) {
-                const int nt = (step + 1) >> 1, nk = (step + 1) & 1;
-                const int kt = nt / 9, kh = (nt / 3) % 3, kw = nt % 3;
-                const int off = (kt * HH + kh) * RP + kw * kRow + nk * 32;
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    af[(step + 1) & 1][i] =
-                        *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i] + off]);
-            }
-            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf, acc[i], 0,
-                                                                 0, 0);
-            // Each k step is its own scheduling island: the weight loads first, then the MFMAs
-            // alternating with the next step's LDS reads, so that neither waits on the other.
-            if (kk == 0 && tap + 1 < 27) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (step + 1 < 54) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    __syncthreads();  // the input tile is reused for the epilogue
-
-    // Epilogue. In a 32x32 accumulator tile, lane l holds column l % 32 and register r holds
-    // row (r / 4) * 8 + (l / 32) * 4 + r % 4. Each wave parks one 32 x 32 tile at a time in its
-    // own slice of the (now idle) input tile, then reads rows back four channels per lane.
-    constexpr int EP = 32 + 4;                      // padded staging row, floats
-    constexpr int LPR = 8;                          // lanes per staged row
-    constexpr int RPP = 64 / LPR;                   // rows per pass
-    static_assert(kMfmaWaves * 32 * EP * 4 <= S::kBytes, "epilogue staging must fit the tile");
-    float* ep = reinterpret_cast<float*>(halo) + wave * (32 * EP);
-    const TO* res = static_cast<const TO*>(a.res);
-    TO* y = static_cast<TO*>(a.y);
-    const int c4 = (lane % LPR) * 4;
-    const int co = co_tile + c4;
-    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (a.bias)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (co + k < a.cout) bv[k] = a.bias[co + k];
-    // Where this lane's four channels go in y. The sw * zc conv channels of one (dt, dh) are
-    // consecutive elements of one y row (dw, then c). When that count is a multiple of 4, a
-    // lane's aligned four channels stay together and are stored as one vector; otherwise each
-    // channel is placed on its own.
-    const int rowc = a.sw * a.zc;
-    const bool vec = rowc % 4 == 0;
-    const int srow = co / rowc, rem = co - srow * rowc;
-    const int sdh = srow % a.sh, sdt = srow / a.sh;
-    const int sub = co / a.zc, cz = co - sub * a.zc;   // sub-position and channel of y
-    auto y_off = [&](int t, int h, int w, int s_dt, int s_dh, int r) -> int64_t {
-        const int to = a.st * t + s_dt - (a.st - 1);
-        if (to < 0) return -1;   // causal drop
-        return ((((int64_t)n * a.yT + to) * a.yH + a.sh * h + s_dh) * a.yW + (int64_t)a.sw * w) *
-                   a.zc + r;
-    };
-    // GroupNorm partials of this lane's four channels (one group): shifted sums, shift = the
-    // lane's first stored value.
-    float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            ep[((r >> 2) * 8 + khalf * 4 + (r & 3)) * EP + lrow] = acc[i][r];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int pass = 0; pass < 32 / RPP; ++pass) {
-            const int row = pass * RPP + lane / LPR;
-            const int m = wave_m * MW + i * 32 + row;
-            const int t = t_blk + m / (HB * WB);
-            const int h = h_blk + (m / WB) % HB, w = w_blk + m % WB;
-            if (t < a.box.t1 && h < a.box.h1 && w < a.box.w1 && co < a.cout) {
-                const int nv = a.cout - co < 4 ? a.cout - co : 4;
-                float v[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) v[k] = ep[row * EP + c4 + k] + bv[k];
-                if (vec) {
-                    const int64_t o = y_off(t, h, w, sdt, sdh, rem);
-                    if (o >= 0) {
-                        if (nv == 4) {
-                            if (res) {
-                                float rv[4];
-                                load4<TO>(res + o, rv);
-#pragma unroll
-                                for (int k = 0; k < 4; ++k) v[k] += rv[k];
-                            }
-                            store4<TO>(y + o, v);
-                        } else {
-                            for (int k = 0; k < nv; ++k) {
-                                if (res) v[k] += Elem<TO>::load(res + o + k);
-                                Elem<TO>::store(y + o + k, v[k]);
-                            }
-                        }
-                        if (a.stats) {
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                if (k < nv) {
-                                    const float q = stored<TO>(v[k]);
-                                    sk = sn == 0.0f ? q : sk;
-                                    const float d = q - sk;
-                                    s1 += d;
-                                    s2 = fmaf(d, d, s2);
-                                    sn += 1.0f;
-                                }
-                            }
-                        }
-                    }
-                } else {
-                    for (int k = 0; k < nv; ++k) {
-                        const int ck = co + k, rk = ck / rowc;
-                        const int64_t o = y_off(t, h, w, rk / a.sh, rk % a.sh, ck - rk * rowc);
-                        if (o < 0) continue;
-                        if (res) v[k] += Elem<TO>::load(res + o);
-                        Elem<TO>::store(y + o, v[k]);
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    if (a.stats) {
-        // lane -> (count, mean, M2); then merge the 8 lanes that hold the same four channels
-        // (lane ^ 8, 16, 32) and the lanes of one group (cpg / 4 neighbours), in a fixed order.
-        float mean = 0.0f, m2 = 0.0f;
-        if (sn > 0.0f) {
-            const float mk = s1 / sn;
-            mean = sk + mk;
-            m2 = fmaxf(s2 - s1 * mk, 0.0f);
-        }
-        const int cpg = a.zc / a.groups;
-#pragma unroll
-        for (int off = 8; off < 64; off <<= 1) {
-            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
-                        m2b = __shfl_xor(m2, off);
-            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
-        }
-        for (int off = 1; off < cpg / 4; off <<= 1) {
-            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
-                        m2b = __shfl_xor(m2, off);
-            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
-        }
-        if (lane < LPR && lane % (cpg / 4) == 0 && co < a.cout) {
-            const int g = cz / cpg;
-            const int nblk = a.nbt * a.nbh * a.nbw;
-            const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
-            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
-            double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
-            o[0] = sn;
-            o[1] = mean;
-            o[2] = m2;
-        }
-    }
-}
-
+using namespace mfma;
 // ------------------------------------------------------------------------------------------------
 // Direct path: one thread per (output position, output channel).
 // ------------------------------------------------------------------------------------------------
@@ -503,100 +67,6 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
 // Output-block shapes (T x H x W = 256 positions). The launch picks the one that wastes the
 // fewest MFMA rows on ragged block edges for the box: 16x22x40 takes 4x8x8 (9% waste instead of
 // 31%), 31x44x80 takes 4x4x16, and the larger stages take 2x8x16.
-enum BlockKind { kBlk2x8x16 = 0, kBlk4x8x8 = 1, kBlk4x4x16 = 2 };
-
-int64_t padded_volume(const Box& b, int tb, int hb, int wb) {
-    return ceil_div(b.bt(), tb) * tb * ceil_div(b.bh(), hb) * hb * ceil_div(b.bw(), wb) * wb;
-}
-
-BlockKind pick_block(const Box& b) {
-    const int64_t v0 = padded_volume(b, 2, 8, 16);
-    const int64_t v1 = padded_volume(b, 4, 8, 8);
-    const int64_t v2 = padded_volume(b, 4, 4, 16);
-    if (v1 < v0 && v1 <= v2) return kBlk4x8x8;
-    if (v2 < v0) return kBlk4x4x16;
-    return kBlk2x8x16;
-}
-
-template <int NT>
-constexpr int wave_rows() {
-    return kMfmaWaves / (NT / 32);
-}
-
-template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
-vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
-                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       const ConvFuse* fz, hipStream_t stream) {
-    MfmaArgs a;
-    a.x = x.data;
-    a.w = static_cast<const uint16_t*>(w);
-    a.bias = bias;
-    a.res = residual ? residual->data : nullptr;
-    a.y = y.data;
-    a.T = (int32_t)x.t;
-    a.H = (int32_t)x.h;
-    a.W = (int32_t)x.w;
-    a.cin = (int32_t)x.c;
-    a.st = fz ? fz->st : 1;
-    a.sh = fz ? fz->sh : 1;
-    a.sw = fz ? fz->sw : 1;
-    a.zc = (int32_t)y.c;
-    a.cout = (int32_t)(y.c * a.st * a.sh * a.sw);
-    a.yT = (int32_t)y.t;
-    a.yH = (int32_t)y.h;
-    a.yW = (int32_t)y.w;
-    a.box = box;
-    a.nbt = (int32_t)ceil_div(box.bt(), TB);
-    a.nbh = (int32_t)ceil_div(box.bh(), HB);
-    a.nbw = (int32_t)ceil_div(box.bw(), WB);
-    int64_t mblocks = x.n * (int64_t)a.nbt * a.nbh * a.nbw;
-    int64_t total = mblocks * ceil_div(a.cout, NT);
-    if (total > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "conv3d: grid too large");
-    a.n_mblocks = (int32_t)mblocks;
-    a.stats = fz ? fz->gn_ws : nullptr;
-    a.groups = fz && fz->gn_ws ? fz->groups : 1;
-    a.nslots = (a.cout / a.zc) * a.nbt * a.nbh * a.nbw * wave_rows<NT>();
-    hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
-                       dim3((unsigned)total), dim3(kMfmaThreads), 0, stream, a);
-    VAE_HIP_CHECK(hipGetLastError());
-    return VAE_OK;
-}
-
-template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
-vae_status_t run_block(const vae_tensor_t& x, const void* w, const float* bias,
-                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       const ConvFuse* fz, hipStream_t stream) {
-    switch (pick_block(box)) {
-        case kBlk4x8x8:
-            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box, fz,
-                                                                 stream);
-        case kBlk4x4x16:
-            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 4, 16>(x, w, bias, residual, y, box,
-                                                                  fz, stream);
-        default:
-            return run_shape<NT, TI, TO, SPLIT, PACKED, 2, 8, 16>(x, w, bias, residual, y, box,
-                                                                  fz, stream);
-    }
-}
-
-template <int NT, typename TI, typename TO, bool SPLIT>
-vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
-                      const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                      bool packed, const ConvFuse* fz, hipStream_t stream) {
-    if (packed)
-        return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, fz, stream);
-    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, fz, stream);
-}
-
-template <int NT, typename TI, bool SPLIT>
-vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bias,
-                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                          bool packed, const ConvFuse* fz, hipStream_t stream) {
-    if (y.dtype == VAE_DTYPE_F32)
-        return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
-    return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
-}
-
 template <int NT>
 vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
