@@ -35,8 +35,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "decoded Mpixel-frames/s (720p VAE decode, 1 GPU) + conv MFMA % of peak"
-CONV_SOURCES = ["video_diffusion_vae_amd/csrc/conv3d.hip", "video_diffusion_vae_amd/csrc/kernels.h",
-                "video_diffusion_vae_amd/csrc/common.h"]
+CSRC = os.path.join(ROOT, "video_diffusion_vae_amd", "csrc")
+CONV_SOURCES = sorted(os.path.join("video_diffusion_vae_amd", "csrc", f) for f in os.listdir(CSRC)
+                      if f.startswith("conv3d") or f in ("kernels.h", "common.h"))
 CONV_KERNEL = "conv3d_mfma_kernel"
 COPY_KERNEL = "upsample_kernel"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "conv3d_mfma_ltx2_720p_patch_halo_1x4_traffic.json")

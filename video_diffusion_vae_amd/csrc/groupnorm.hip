@@ -332,8 +332,7 @@ __global__ __launch_bounds__(kThreads) void gn_apply_kernel(
         sc[k] = mr[2 * g + 1] * gm;
         sh[k] = bt - mr[2 * g] * sc[k];
     }
-    for (int e = threadIdx.x; e < seg; e += kThreads) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(xr + (int64_t)e * V);
+    auto apply = [&](int e, const uint4& raw) {
         const TI* v = reinterpret_cast<const TI*>(&raw);
         TO out[V];
 #pragma unroll
@@ -350,7 +349,18 @@ __global__ __launch_bounds__(kThreads) void gn_apply_kernel(
 #pragma unroll
             for (int k = 0; k < V; ++k) yr[(int64_t)e * V + k] = out[k];
         }
+    };
+    // four loads in flight per thread before any is used
+    int e = threadIdx.x;
+    for (; e + 3 * kThreads < seg; e += 4 * kThreads) {
+        uint4 raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            raw[u] = *reinterpret_cast<const uint4*>(xr + (int64_t)(e + u * kThreads) * V);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) apply(e + u * kThreads, raw[u]);
     }
+    for (; e < seg; e += kThreads) apply(e, *reinterpret_cast<const uint4*>(xr + (int64_t)e * V));
 }
 
 template <typename TI, typename TO>
