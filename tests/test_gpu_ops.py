@@ -432,23 +432,44 @@ def test_tile_merge_matches_oracle(v, grid):
     assert rel_max_abs(host(out), ref) <= 1e-5
 
 
-@pytest.mark.parametrize("case", [((1, 3, 9, 19), 64, 256, "bf16"), ((2, 2, 8, 16), 32, 48, "f32"),
-                                  ((1, 2, 8, 16), 128, 52, "f32"), ((1, 5, 10, 12), 96, 128, "bf16")])
+PACKED_CASES = [
+    # (N, T, H, W), Cin, Cout, input dtype, split fp32 operands
+    ((1, 3, 9, 19), 64, 256, "bf16", False),
+    ((2, 2, 8, 16), 32, 48, "f32", False),
+    ((1, 2, 8, 16), 128, 52, "f32", False),
+    ((1, 5, 10, 12), 96, 128, "bf16", False),
+    # 2x8x16 blocks: the packed path stages through the ring of frame slots
+    ((1, 4, 16, 32), 96, 128, "bf16", False),          # three chunks
+    ((1, 5, 16, 32), 64, 256, "bf16", False),          # a ragged last frame block, two Cout tiles
+    ((1, 4, 16, 32), 64, 128, "f32", True),            # split: four 16-channel chunks
+    ((2, 3, 8, 16), 32, 48, "f32", True),              # 64-wide tiles, two samples
+]
+
+
+@pytest.mark.parametrize("case", PACKED_CASES)
 def test_conv3d_packed_weights_bitwise_equal(v, case):
-    """Packed weights only change the load layout: the result must be bitwise identical to the
-    standard layout, and match the oracle."""
+    """Packed weights only change the load layout (and, for 2x8x16 blocks, the staging order):
+    the result must be bitwise identical to the standard layout, and match the oracle."""
     import torch
-    (n, t, h, w), cin, cout, idt = case
-    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 60 + cout)
+    (n, t, h, w), cin, cout, idt, split = case
+    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 60 + PACKED_CASES.index(case))
+    if idt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [18, cin], scale=1e-3))
     wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
     packed = v.vae_conv_weight_pack(wd)
     bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
     y0 = torch.empty((n, t, h, w, cout), device="cuda", dtype=torch.float32)
     y1 = torch.empty_like(y0)
     xd = dev(x, idt)
-    v.vae_conv3d_causal(xd, wd, bd, None, y0)
+    sf = v.VAE_CONV_SPLIT_FP32 if split else 0
+    v.vae_conv3d_causal(xd, wd, bd, None, y0, flags=sf)
     v.vae_conv3d_causal(xd, packed.view(torch.bfloat16), bd, None, y1,
-                        flags=v.VAE_CONV_PACKED_WEIGHTS)
+                        flags=v.VAE_CONV_PACKED_WEIGHTS | sf)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
-    assert rel_max_abs(host(y1), oracle.causal_conv3d(x, wt, b)) <= 1e-4
+    if split:
+        hi = vae_synth.round_bf16(x).astype(np.float64)
+        xin = hi + vae_synth.round_bf16(x - hi).astype(np.float64)
+    else:
+        xin = vae_synth.round_bf16(x).astype(np.float64)
+    assert rel_max_abs(host(y1), oracle.causal_conv3d(xin, wt, b)) <= 1e-4

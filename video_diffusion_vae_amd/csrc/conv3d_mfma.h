@@ -164,6 +164,55 @@ __device__ __forceinline__ void chan_merge_f32(float& n, float& mean, float& m2,
     n = t;
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1, each a separate instantiation.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Raw input of one staging unit: 8 input channels (16 bytes of bf16, 32 of fp32).
+template <typename TI> struct Raw8 {
+    uint4 v[sizeof(TI) / 2];
+};
+template <typename TI> __device__ __forceinline__ Raw8<TI> load_raw8(const TI* p) {
+    Raw8<TI> r;
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(TI) / 2); ++i) r.v[i] = q[i];
+    return r;
+}
+// Operand granule(s) of a unit: bf16 as is; fp32 rounded to bf16, or split into hi and lo.
+// A unit outside the image (in == false) is zero padding.
+template <typename TI, bool SPLIT>
+__device__ __forceinline__ void to_operand(const Raw8<TI>& r, bool in, uint4& hi, uint4& lo) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    lo = z;
+    if constexpr (sizeof(TI) == 2) {
+        hi = in ? r.v[0] : z;
+    } else {
+        float v[8] = {__uint_as_float(r.v[0].x), __uint_as_float(r.v[0].y),
+                      __uint_as_float(r.v[0].z), __uint_as_float(r.v[0].w),
+                      __uint_as_float(r.v[1].x), __uint_as_float(r.v[1].y),
+                      __uint_as_float(r.v[1].z), __uint_as_float(r.v[1].w)};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
+            h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            if constexpr (SPLIT) {
+                const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
+                const uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
+                l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+        }
+        hi = in ? make_uint4(h[0], h[1], h[2], h[3]) : z;
+        if constexpr (SPLIT) lo = in ? make_uint4(l[0], l[1], l[2], l[3]) : z;
+    }
+}
+
 // Staged input tile: (TB+2) x (HB+2) rows of (WB+2) positions, 80 bytes per position. The row
 // pitch is chosen for conflict-free 16-byte A-fragment reads. A fragment read covers
 //  - 16 positions of one row plus 16 of the next (WB = 16), or
@@ -187,7 +236,14 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     using S = BlockShape<TB, HB, WB>;
     constexpr int HH = S::HH, HW = S::HW;
     constexpr int RP = S::kPitch;
-    __shared__ __attribute__((aligned(16))) uint8_t halo[S::kBytes];
+    // Blocks two frames deep (TB = 2) stage through a ring of frame slots (see below); the others
+    // through one tile buffer. The ring's extra registers fit two waves per SIMD with packed
+    // weights and bf16 (or split) operands.
+    constexpr bool ROLL = TB == 2 && PACKED && (sizeof(TI) == 2 || SPLIT);
+    constexpr int NS = S::HT + 1;                  // frame slots of the ring
+    constexpr int FB = HH * RP;                    // bytes of one frame slot
+    constexpr int kSink = ROLL ? NS * FB : S::kBytes;   // 64 bytes absorbing padding units
+    __shared__ __attribute__((aligned(16))) uint8_t halo[kSink + (ROLL ? 64 : 0)];
 
     // WNN waves across the NT output channels (32 each), WM across the 256 positions.
     constexpr int WNN = NT / 32;
@@ -266,67 +322,208 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     constexpr int CK = SPLIT ? 16 : kCK;       // input channels per staged chunk
     constexpr int UPP = SPLIT ? 2 : 4;         // staging units per position (8 channels each)
     const int n_chunks = a.cin / CK;
-    for (int kc = 0; kc < n_chunks; ++kc) {
-        const int c0 = kc * CK;
+    if constexpr (ROLL) {
+        // Ring staging. The tile's 4 frames live in 4 of NS = 5 LDS frame slots: frame f of chunk
+        // c is slot (b_c + f) mod NS, and b decreases by one per chunk. Taps kt = 0, 1, 2 read
+        // frames {0, 1}, {1, 2} and {2, 3}, so a slot frees as soon as its frame's last phase is
+        // done. While chunk c runs, the next chunk's frames are loaded into registers and written
+        // into freed slots:
+        //   frame 0 -> the spare slot (anytime); frame 1 -> frame 0's slot (after phase 0);
+        //   frame 2 -> frame 1's slot (after phase 1); frame 3 -> written at the start of the
+        //   next chunk into frame 2's slot.
+        // One barrier per phase; no chunk waits for its own loads.
+        constexpr int FPOS = HH * HW;                     // positions per frame
+        constexpr int FUN = FPOS * UPP;                   // staging units per frame
+        constexpr int FST = (FUN + kMfmaThreads - 1) / kMfmaThreads;
+        int fu_pos[FST], fu_lds[FST];
 #pragma unroll
-        for (int t = 0; t < PD; ++t) load_b(t, t, c0);   // in flight while the tile is staged
-        __syncthreads();              // the previous chunk's LDS reads are done
-        for (int u = tid; u < S::kPos * UPP; u += kMfmaThreads) {
+        for (int i = 0; i < FST; ++i) {
+            int u = tid + i * kMfmaThreads;
+            const bool valid = u < FUN;
+            u = valid ? u : FUN - 1;
             const int pos = u / UPP, g = u % UPP;
-            const int f = pos / (HH * HW);
-            const int rem = pos - f * (HH * HW);
-            const int r = rem / HW;
-            const int c = rem - r * HW;
-            int tg = t_blk - 2 + f;
-            tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
-            const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
-            uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
-            uint4 vl = make_uint4(0, 0, 0, 0);
-            if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
-                const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
-                if constexpr (SPLIT) split8<TI>(src, v, vl);
-                else v = load8<TI>(src);
-            }
-            uint8_t* dst = &halo[(f * HH + r) * RP + c * kRow + g * 16];
-            *reinterpret_cast<uint4*>(dst) = v;            // split: hi in bytes 0..31 of the row
-            if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = vl;  // lo in bytes 32..63
+            const int r = pos / HW, c = pos % HW;
+            fu_pos[i] = r | (c << 8) | (g << 16) | (valid ? 0 : 1 << 30);
+            fu_lds[i] = r * RP + c * kRow + g * 16;
         }
+        Raw8<TI> fst[FST];
+        uint32_t fin = 0;                                 // bit i: unit i inside the image
+        auto frame_load = [&](int f, int c0) {
+            int tg = t_blk - 2 + f;
+            tg = tg < 0 ? 0 : (tg >= a.T ? a.T - 1 : tg);   // causal clamp; past T is not stored
+#pragma unroll
+            for (int i = 0; i < FST; ++i) {
+                const int q = fu_pos[i];
+                const int r = q & 255, c = (q >> 8) & 255, g = (q >> 16) & 3;
+                const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
+                const bool in = (unsigned)hg < (unsigned)a.H && (unsigned)wg < (unsigned)a.W;
+                const int hc = hg < 0 ? 0 : (hg >= a.H ? a.H - 1 : hg);
+                const int wc = wg < 0 ? 0 : (wg >= a.W ? a.W - 1 : wg);
+                fst[i] = load_raw8<TI>(xn + ((int64_t)(tg * a.H + hc) * a.W + wc) * cin + c0 +
+                                       g * 8);
+                fin = in ? (fin | (1u << i)) : (fin & ~(1u << i));
+            }
+        };
+        auto frame_write = [&](int slot) {
+#pragma unroll
+            for (int i = 0; i < FST; ++i) {
+                uint4 hi, lo;
+                to_operand<TI, SPLIT>(fst[i], (fin >> i) & 1u, hi, lo);
+                uint8_t* dst = (fu_pos[i] >> 30) ? halo + kSink : halo + slot * FB + fu_lds[i];
+                *reinterpret_cast<uint4*>(dst) = hi;              // split: hi in bytes 0..31
+                if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = lo;
+            }
+        };
+        // A rows of this lane inside a frame, and the tile frame each of its MI tiles starts at
+        int a_in[MI], tb_of[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int m = wave_m * MW + i * 32 + lrow;
+            const int hb = (m / WB) % HB, wb = m % WB;
+            a_in[i] = hb * RP + wb * kRow + khalf * 16;
+            tb_of[i] = (wave_m * MW + i * 32) / (HB * WB);
+        }
+
+        // prologue: chunk 0 into slots 0..3, the first weights in flight
+        int b = 0;
+#pragma unroll
+        for (int f = 0; f < S::HT; ++f) {
+            frame_load(f, 0);
+            frame_write(f);
+        }
+#pragma unroll
+        for (int t = 0; t < PD; ++t) load_b(t, t, 0);
         __syncthreads();
 
-        // 54 k steps (27 taps x 2). The A fragments of step s + 1 are read from LDS while the
-        // MFMAs of step s run; the weights of tap + 1 are fetched during tap.
-        bf16x8_t af[2][MI];
+        for (int kc = 0; kc < n_chunks; ++kc) {
+            const int c0 = kc * CK;
+            const int cn = (kc + 1 < n_chunks ? kc + 1 : kc) * CK;   // the last chunk restages
+            auto slot = [&](int f) { return (b + f + NS) % NS; };
+            int abase[MI];
+            auto set_phase = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-            af[0][i] = *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i]]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int step = 0; step < 54; ++step) {
-            const int tap = step >> 1, kk = step & 1;
-            if (kk == 0 && tap + PD < 27) load_b((tap + PD) % NB, tap + PD, c0);
-            if (step + 1 < 54) {
-                const int nt = (step + 1) >> 1, nk = (step + 1) & 1;
-                const int kt = nt / 9, kh = (nt / 3) % 3, kw = nt % 3;
-                const int off = (kt * HH + kh) * RP + kw * kRow + nk * 32;
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    af[(step + 1) & 1][i] =
-                        *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i] + off]);
-            }
-            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
+                for (int i = 0; i < MI; ++i) abase[i] = slot(tb_of[i] + kt) * FB + a_in[i];
+            };
+            set_phase(0);
+            bf16x8_t af[2][MI];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf, acc[i], 0,
-                                                                 0, 0);
-            // Each k step is its own scheduling island: the weight loads first, then the MFMAs
-            // alternating with the next step's LDS reads, so that neither waits on the other.
-            if (kk == 0 && tap + PD < 27) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (step + 1 < 54) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
+                af[0][i] = *reinterpret_cast<const bf16x8_t*>(&halo[abase[i]]);
             __builtin_amdgcn_sched_barrier(0);
+            static_for<0, 54>([&](auto step_c) {
+                constexpr int step = decltype(step_c)::value;
+                constexpr int tap = step >> 1, kk = step & 1;
+                // phase ends: every wave is done with the phase's first frame
+                if constexpr (step == 17 || step == 35) {
+                    __syncthreads();
+                    set_phase(step == 17 ? 1 : 2);
+                }
+                if constexpr (kk == 0) {
+                    if constexpr (tap + PD < 27) load_b((tap + PD) % NB, tap + PD, c0);
+                    else load_b((tap + PD) % NB, tap + PD - 27, cn);
+                }
+                constexpr bool ld = step == 2 || step == 20 || step == 38 || step == 50;
+                constexpr bool wr = step == 0 || step == 14 || step == 32 || step == 48;
+                if constexpr (step == 0) frame_write(slot(3));    // this chunk's frame 3 (held)
+                if constexpr (step == 2) frame_load(0, cn);
+                if constexpr (step == 14) frame_write(slot(-1));  // next frame 0 -> spare slot
+                if constexpr (step == 20) frame_load(1, cn);
+                if constexpr (step == 32) frame_write(slot(0));   // next frame 1
+                if constexpr (step == 38) frame_load(2, cn);
+                if constexpr (step == 48) frame_write(slot(1));   // next frame 2
+                if constexpr (step == 50) frame_load(3, cn);      // held into the next chunk
+                if constexpr (step + 1 < 54) {
+                    constexpr int nt = (step + 1) >> 1, nk = (step + 1) & 1;
+                    constexpr int kh = (nt / 3) % 3, kw = nt % 3;
+                    constexpr int off = kh * RP + kw * kRow + nk * 32;
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        af[(step + 1) & 1][i] =
+                            *reinterpret_cast<const bf16x8_t*>(&halo[abase[i] + off]);
+                }
+                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf,
+                                                                     acc[i], 0, 0, 0);
+                if constexpr (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
+                if constexpr (ld)
+                    __builtin_amdgcn_sched_group_barrier(0x020, FST * (int)(sizeof(TI) / 2), 0);
+                if constexpr (wr)
+                    __builtin_amdgcn_sched_group_barrier(0x200, FST * (SPLIT ? 2 : 1), 0);
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (step + 1 < 54) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            __syncthreads();   // chunk done: its frames 2, 3 are free, the next 0..2 are staged
+            b = (b + NS - 1) % NS;
+        }
+    } else {
+        for (int kc = 0; kc < n_chunks; ++kc) {
+            const int c0 = kc * CK;
+    #pragma unroll
+            for (int t = 0; t < PD; ++t) load_b(t, t, c0);   // in flight while the tile is staged
+            __syncthreads();              // the previous chunk's LDS reads are done
+            for (int u = tid; u < S::kPos * UPP; u += kMfmaThreads) {
+                const int pos = u / UPP, g = u % UPP;
+                const int f = pos / (HH * HW);
+                const int rem = pos - f * (HH * HW);
+                const int r = rem / HW;
+                const int c = rem - r * HW;
+                int tg = t_blk - 2 + f;
+                tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
+                const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
+                uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
+                uint4 vl = make_uint4(0, 0, 0, 0);
+                if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
+                    const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
+                    if constexpr (SPLIT) split8<TI>(src, v, vl);
+                    else v = load8<TI>(src);
+                }
+                uint8_t* dst = &halo[(f * HH + r) * RP + c * kRow + g * 16];
+                *reinterpret_cast<uint4*>(dst) = v;            // split: hi in bytes 0..31 of the row
+                if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = vl;  // lo in bytes 32..63
+            }
+            __syncthreads();
+
+            // 54 k steps (27 taps x 2). The A fragments of step s + 1 are read from LDS while the
+            // MFMAs of step s run; the weights of tap + 1 are fetched during tap.
+            bf16x8_t af[2][MI];
+    #pragma unroll
+            for (int i = 0; i < MI; ++i)
+                af[0][i] = *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i]]);
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int step = 0; step < 54; ++step) {
+                const int tap = step >> 1, kk = step & 1;
+                if (kk == 0 && tap + PD < 27) load_b((tap + PD) % NB, tap + PD, c0);
+                if (step + 1 < 54) {
+                    const int nt = (step + 1) >> 1, nk = (step + 1) & 1;
+                    const int kt = nt / 9, kh = (nt / 3) % 3, kw = nt % 3;
+                    const int off = (kt * HH + kh) * RP + kw * kRow + nk * 32;
+    #pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        af[(step + 1) & 1][i] =
+                            *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i] + off]);
+                }
+                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
+    #pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf, acc[i], 0,
+                                                                     0, 0);
+                // Each k step is its own scheduling island: the weight loads first, then the MFMAs
+                // alternating with the next step's LDS reads, so that neither waits on the other.
+                if (kk == 0 && tap + PD < 27) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
+    #pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (step + 1 < 54) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     __syncthreads();  // the input tile is reused for the epilogue
@@ -337,7 +534,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     constexpr int EP = 32 + 4;                      // padded staging row, floats
     constexpr int LPR = 8;                          // lanes per staged row
     constexpr int RPP = 64 / LPR;                   // rows per pass
-    static_assert(kMfmaWaves * 32 * EP * 4 <= S::kBytes, "epilogue staging must fit the tile");
+    static_assert(kMfmaWaves * 32 * EP * 4 <= kSink, "epilogue staging must fit the tile");
     float* ep = reinterpret_cast<float*>(halo) + wave * (32 * EP);
     const TO* res = static_cast<const TO*>(a.res);
     TO* y = static_cast<TO*>(a.y);
