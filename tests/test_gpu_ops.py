@@ -443,6 +443,10 @@ PACKED_CASES = [
     ((1, 5, 16, 32), 64, 256, "bf16", False),          # a ragged last frame block, two Cout tiles
     ((1, 4, 16, 32), 64, 128, "f32", True),            # split: four 16-channel chunks
     ((2, 3, 8, 16), 32, 48, "f32", True),              # 64-wide tiles, two samples
+    # 4x8x8 and 4x4x16 blocks: six-frame tiles in a ring of eight slots
+    ((1, 7, 8, 24), 96, 128, "bf16", False),           # 4x8x8, ragged last frame block
+    ((1, 8, 12, 32), 64, 256, "bf16", False),          # 4x4x16, ragged rows
+    ((1, 6, 16, 8), 32, 128, "f32", True),             # 4x8x8, split
 ]
 
 

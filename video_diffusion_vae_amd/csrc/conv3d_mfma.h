@@ -236,11 +236,12 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     using S = BlockShape<TB, HB, WB>;
     constexpr int HH = S::HH, HW = S::HW;
     constexpr int RP = S::kPitch;
-    // Blocks two frames deep (TB = 2) stage through a ring of frame slots (see below); the others
-    // through one tile buffer. The ring's extra registers fit two waves per SIMD with packed
-    // weights and bf16 (or split) operands.
-    constexpr bool ROLL = TB == 2 && PACKED && (sizeof(TI) == 2 || SPLIT);
-    constexpr int NS = S::HT + 1;                  // frame slots of the ring
+    // With packed weights and bf16 (or split) operands the tile is staged through a ring of frame
+    // slots (see below); otherwise through one tile buffer. The ring's extra registers fit two
+    // waves per SIMD in those cases.
+    constexpr bool ROLL = PACKED && (sizeof(TI) == 2 || SPLIT);
+    constexpr int NSP = TB == 2 ? 1 : 2;           // spare frame slots of the ring
+    constexpr int NS = S::HT + NSP;                // frame slots of the ring
     constexpr int FB = HH * RP;                    // bytes of one frame slot
     constexpr int kSink = ROLL ? NS * FB : S::kBytes;   // 64 bytes absorbing padding units
     __shared__ __attribute__((aligned(16))) uint8_t halo[kSink + (ROLL ? 64 : 0)];
@@ -323,15 +324,21 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     constexpr int UPP = SPLIT ? 2 : 4;         // staging units per position (8 channels each)
     const int n_chunks = a.cin / CK;
     if constexpr (ROLL) {
-        // Ring staging. The tile's 4 frames live in 4 of NS = 5 LDS frame slots: frame f of chunk
-        // c is slot (b_c + f) mod NS, and b decreases by one per chunk. Taps kt = 0, 1, 2 read
-        // frames {0, 1}, {1, 2} and {2, 3}, so a slot frees as soon as its frame's last phase is
-        // done. While chunk c runs, the next chunk's frames are loaded into registers and written
-        // into freed slots:
-        //   frame 0 -> the spare slot (anytime); frame 1 -> frame 0's slot (after phase 0);
-        //   frame 2 -> frame 1's slot (after phase 1); frame 3 -> written at the start of the
-        //   next chunk into frame 2's slot.
+        // Ring staging. The tile's HT = TB + 2 frames live in HT of NS = HT + NSP LDS frame
+        // slots: frame f of chunk c is slot (b_c + f) mod NS, and b moves back by NSP slots per
+        // chunk. Taps kt = 0, 1, 2 read frames kt .. kt + TB - 1, so frame 0's slot frees after
+        // phase 0 and frame 1's after phase 1. While chunk c runs, the next chunk's frames are
+        // loaded into registers and written into free slots:
+        //  - frames 0 .. NSP - 1 into the spare slots (anytime);
+        //  - frame NSP into frame 0's slot (after phase 0);
+        //  - frame NSP + 1 into frame 1's slot (after phase 1);
+        //  - the remaining NHOLD frames at the start of the next chunk, into slots its first phase
+        //    does not read; they become visible at its phase-0 barrier.
         // One barrier per phase; no chunk waits for its own loads.
+        constexpr int NIN = NSP + 2;                       // next frames written in the chunk
+        constexpr int NHOLD = S::HT - NIN;                 // next frames held into the chunk
+        static_assert(NHOLD == 1 || NHOLD == 2, "ring schedule");
+        static_assert(NIN >= TB, "the next chunk's first phase must be staged in time");
         constexpr int FPOS = HH * HW;                     // positions per frame
         constexpr int FUN = FPOS * UPP;                   // staging units per frame
         constexpr int FST = (FUN + kMfmaThreads - 1) / kMfmaThreads;
@@ -346,9 +353,9 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             fu_pos[i] = r | (c << 8) | (g << 16) | (valid ? 0 : 1 << 30);
             fu_lds[i] = r * RP + c * kRow + g * 16;
         }
-        Raw8<TI> fst[FST];
-        uint32_t fin = 0;                                 // bit i: unit i inside the image
-        auto frame_load = [&](int f, int c0) {
+        Raw8<TI> fst[2][FST];                             // [1] only for a second held frame
+        uint32_t fin[2] = {0, 0};                         // bit i: unit i inside the image
+        auto frame_load = [&](int f, int c0, int reg) {
             int tg = t_blk - 2 + f;
             tg = tg < 0 ? 0 : (tg >= a.T ? a.T - 1 : tg);   // causal clamp; past T is not stored
 #pragma unroll
@@ -359,16 +366,16 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 const bool in = (unsigned)hg < (unsigned)a.H && (unsigned)wg < (unsigned)a.W;
                 const int hc = hg < 0 ? 0 : (hg >= a.H ? a.H - 1 : hg);
                 const int wc = wg < 0 ? 0 : (wg >= a.W ? a.W - 1 : wg);
-                fst[i] = load_raw8<TI>(xn + ((int64_t)(tg * a.H + hc) * a.W + wc) * cin + c0 +
-                                       g * 8);
-                fin = in ? (fin | (1u << i)) : (fin & ~(1u << i));
+                fst[reg][i] = load_raw8<TI>(xn + ((int64_t)(tg * a.H + hc) * a.W + wc) * cin +
+                                            c0 + g * 8);
+                fin[reg] = in ? (fin[reg] | (1u << i)) : (fin[reg] & ~(1u << i));
             }
         };
-        auto frame_write = [&](int slot) {
+        auto frame_write = [&](int slot, int reg) {
 #pragma unroll
             for (int i = 0; i < FST; ++i) {
                 uint4 hi, lo;
-                to_operand<TI, SPLIT>(fst[i], (fin >> i) & 1u, hi, lo);
+                to_operand<TI, SPLIT>(fst[reg][i], (fin[reg] >> i) & 1u, hi, lo);
                 uint8_t* dst = (fu_pos[i] >> 30) ? halo + kSink : halo + slot * FB + fu_lds[i];
                 *reinterpret_cast<uint4*>(dst) = hi;              // split: hi in bytes 0..31
                 if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = lo;
@@ -384,21 +391,32 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             tb_of[i] = (wave_m * MW + i * 32) / (HB * WB);
         }
 
-        // prologue: chunk 0 into slots 0..3, the first weights in flight
+        // prologue: chunk 0 into slots 0 .. HT-1 (its held frames stay in registers too, so that
+        // the first chunk's step-0 rewrite is harmless), the first weights in flight
         int b = 0;
 #pragma unroll
-        for (int f = 0; f < S::HT; ++f) {
-            frame_load(f, 0);
-            frame_write(f);
+        for (int f = 0; f < NIN; ++f) {
+            frame_load(f, 0, 0);
+            frame_write(f, 0);
+        }
+#pragma unroll
+        for (int h = 0; h < NHOLD; ++h) {
+            frame_load(NIN + h, 0, h);
+            frame_write(NIN + h, h);
         }
 #pragma unroll
         for (int t = 0; t < PD; ++t) load_b(t, t, 0);
         __syncthreads();
 
+        // step schedule: in-chunk frame k is loaded at LDK[k] and written at WRK[k] into slot
+        // offset k - NSP; held frame h is loaded at HLD[h]
+        constexpr int LDK[4] = {2, TB == 2 ? 20 : 10, TB == 2 ? 38 : 20, 38};
+        constexpr int WRK[4] = {TB == 2 ? 14 : 8, TB == 2 ? 32 : 16, TB == 2 ? 48 : 30, 46};
+        constexpr int HLD[2] = {TB == 2 ? 50 : 48, 50};
         for (int kc = 0; kc < n_chunks; ++kc) {
             const int c0 = kc * CK;
             const int cn = (kc + 1 < n_chunks ? kc + 1 : kc) * CK;   // the last chunk restages
-            auto slot = [&](int f) { return (b + f + NS) % NS; };
+            auto slot = [&](int f) { return (b + f + 2 * NS) % NS; };
             int abase[MI];
             auto set_phase = [&](int kt) {
 #pragma unroll
@@ -422,16 +440,18 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                     if constexpr (tap + PD < 27) load_b((tap + PD) % NB, tap + PD, c0);
                     else load_b((tap + PD) % NB, tap + PD - 27, cn);
                 }
-                constexpr bool ld = step == 2 || step == 20 || step == 38 || step == 50;
-                constexpr bool wr = step == 0 || step == 14 || step == 32 || step == 48;
-                if constexpr (step == 0) frame_write(slot(3));    // this chunk's frame 3 (held)
-                if constexpr (step == 2) frame_load(0, cn);
-                if constexpr (step == 14) frame_write(slot(-1));  // next frame 0 -> spare slot
-                if constexpr (step == 20) frame_load(1, cn);
-                if constexpr (step == 32) frame_write(slot(0));   // next frame 1
-                if constexpr (step == 38) frame_load(2, cn);
-                if constexpr (step == 48) frame_write(slot(1));   // next frame 2
-                if constexpr (step == 50) frame_load(3, cn);      // held into the next chunk
+                constexpr int ldk = step == LDK[0] ? 0 : step == LDK[1] ? 1 : step == LDK[2] ? 2
+                                  : (NIN > 3 && step == LDK[3]) ? 3 : -1;
+                constexpr int wrk = step == WRK[0] ? 0 : step == WRK[1] ? 1 : step == WRK[2] ? 2
+                                  : (NIN > 3 && step == WRK[3]) ? 3 : -1;
+                constexpr int hld = step == HLD[0] ? 0 : (NHOLD > 1 && step == HLD[1]) ? 1 : -1;
+                if constexpr (step == 0) {
+#pragma unroll
+                    for (int h = 0; h < NHOLD; ++h) frame_write(slot(NIN + h), h);
+                }
+                if constexpr (ldk >= 0) frame_load(ldk, cn, 0);
+                if constexpr (wrk >= 0) frame_write(slot(wrk - NSP), 0);
+                if constexpr (hld >= 0) frame_load(NIN + hld, cn, hld);
                 if constexpr (step + 1 < 54) {
                     constexpr int nt = (step + 1) >> 1, nk = (step + 1) & 1;
                     constexpr int kh = (nt / 3) % 3, kw = nt % 3;
@@ -446,11 +466,14 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 for (int i = 0; i < MI; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf,
                                                                      acc[i], 0, 0, 0);
+                constexpr int n_ld = (ldk >= 0) + (hld >= 0);
+                constexpr int n_wr = (wrk >= 0) + (step == 0 ? NHOLD : 0);
                 if constexpr (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
-                if constexpr (ld)
-                    __builtin_amdgcn_sched_group_barrier(0x020, FST * (int)(sizeof(TI) / 2), 0);
-                if constexpr (wr)
-                    __builtin_amdgcn_sched_group_barrier(0x200, FST * (SPLIT ? 2 : 1), 0);
+                if constexpr (n_ld > 0)
+                    __builtin_amdgcn_sched_group_barrier(0x020, n_ld * FST * (int)(sizeof(TI) / 2),
+                                                         0);
+                if constexpr (n_wr > 0)
+                    __builtin_amdgcn_sched_group_barrier(0x200, n_wr * FST * (SPLIT ? 2 : 1), 0);
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -458,8 +481,8 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
-            __syncthreads();   // chunk done: its frames 2, 3 are free, the next 0..2 are staged
-            b = (b + NS - 1) % NS;
+            __syncthreads();   // chunk done: its later frames are free, the next chunk is staged
+            b = (b + NS - NSP) % NS;
         }
     } else {
         for (int kc = 0; kc < n_chunks; ++kc) {
