@@ -68,6 +68,7 @@ struct MfmaArgs {
     // (st*t + dt - (st-1), sh*h + dh, sw*w + dw); frames below 0 are dropped. Identity:
     // st = sh = sw = 1 and zc = cout. The residual, if any, has y's shape.
     int32_t yT, yH, yW, zc, st, sh, sw;
+    int32_t res_f32;         // the residual is fp32 while y is bf16 (a stream handed on in bf16)
     // Optional GroupNorm partials of y as stored: fp64 (count, mean, M2) per (sample, group of
     // y's channels, slot), slot = (sub-position * position blocks + block) * WM + wave row.
     double* stats;
@@ -560,6 +561,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     static_assert(kMfmaWaves * 32 * EP * 4 <= kSink, "epilogue staging must fit the tile");
     float* ep = reinterpret_cast<float*>(halo) + wave * (32 * EP);
     const TO* res = static_cast<const TO*>(a.res);
+    const float* res32 = static_cast<const float*>(a.res);   // when a.res_f32
     TO* y = static_cast<TO*>(a.y);
     const int c4 = (lane % LPR) * 4;
     const int co = co_tile + c4;
@@ -611,14 +613,16 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                         if (nv == 4) {
                             if (res) {
                                 float rv[4];
-                                load4<TO>(res + o, rv);
+                                if (a.res_f32) load4<float>(res32 + o, rv);
+                                else load4<TO>(res + o, rv);
 #pragma unroll
                                 for (int k = 0; k < 4; ++k) v[k] += rv[k];
                             }
                             store4<TO>(y + o, v);
                         } else {
                             for (int k = 0; k < nv; ++k) {
-                                if (res) v[k] += Elem<TO>::load(res + o + k);
+                                if (res)
+                                    v[k] += a.res_f32 ? res32[o + k] : Elem<TO>::load(res + o + k);
                                 Elem<TO>::store(y + o + k, v[k]);
                             }
                         }
@@ -641,7 +645,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                         const int ck = co + k, rk = ck / rowc;
                         const int64_t o = y_off(t, h, w, rk / a.sh, rk % a.sh, ck - rk * rowc);
                         if (o < 0) continue;
-                        if (res) v[k] += Elem<TO>::load(res + o);
+                        if (res) v[k] += a.res_f32 ? res32[o] : Elem<TO>::load(res + o);
                         Elem<TO>::store(y + o, v[k]);
                     }
                 }
@@ -714,6 +718,7 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.w = static_cast<const uint16_t*>(w);
     a.bias = bias;
     a.res = residual ? residual->data : nullptr;
+    a.res_f32 = residual && residual->dtype == VAE_DTYPE_F32 && y.dtype != VAE_DTYPE_F32;
     a.y = y.data;
     a.T = (int32_t)x.t;
     a.H = (int32_t)x.h;

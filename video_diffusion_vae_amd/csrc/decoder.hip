@@ -57,6 +57,20 @@ int32_t gn_silu_dtype(const vae_decoder& d, int i) {
     return gn_silu_dtype(d.dtype, d.act_dtype, d.flags, d.layers.data(), (int)d.layers.size(), i);
 }
 
+// Storage dtype of a residual block's output (layer i). When the next layer is a conv that rounds
+// its input to the bf16 operand dtype anyway (bf16 weights on the matrix cores, no split), the
+// block stores bf16 directly: the same rounding, done once at the store, with half the bytes.
+int32_t res_out_dtype(const vae_decoder& d, size_t i) {
+    if (i + 1 < d.layers.size() && d.dtype == VAE_DTYPE_BF16 && d.layers[i].cin % 32 == 0) {
+        const vae_layer_desc_t& n = d.layers[i + 1];
+        if (n.op == VAE_OP_CONV && !conv_splits(d.flags, d.layers.data(), (int)d.layers.size(),
+                                                (int)i + 1) &&
+            n.cin % 32 == 0 && n.cout % 4 == 0)
+            return VAE_DTYPE_BF16;
+    }
+    return d.act_dtype;
+}
+
 // Whether the op after layer i starts with a GroupNorm of layer i's output.
 bool gn_follows(const vae_decoder& d, size_t i) {
     if (i + 1 >= d.layers.size()) return false;
@@ -88,7 +102,7 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
                 s.dtype = l.f32_out ? VAE_DTYPE_F32 : d.act_dtype;
                 break;
             case VAE_OP_RES:
-                s.dtype = d.act_dtype;
+                s.dtype = res_out_dtype(d, i);
                 break;
             case VAE_OP_GN_SILU:
                 s.dtype = gn_silu_dtype(d, (int)i);
@@ -353,7 +367,9 @@ struct Runner {
                 VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
                 VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, true));
                 VAE_TRY(gn(t2, t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
-                vae_tensor_t y = last ? final_out : t2;
+                Shape ys = as;
+                ys.dtype = res_out_dtype(*d, li);   // conv1's output in b2 is dead by now
+                vae_tensor_t y = last ? final_out : buf(b2, ys);
                 VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li)));
                 p += 8;
                 cur = y;
