@@ -38,8 +38,13 @@ CONV_GN_PLAN = {
 
 
 def params_of(name, affine=None):
-    # the LTX-2-shaped workloads share one layer plan, hence one weight set
-    key = "ltx2_720p" if name.startswith("ltx2_") and name != "ltx2_tiny" else name
+    # the LTX-2-shaped workloads share one layer plan, hence one weight set (as do the tiny ones)
+    if name.startswith("ltx2_tiny"):
+        key = "ltx2_tiny"
+    elif name.startswith("ltx2_"):
+        key = "ltx2_720p"
+    else:
+        key = name
     return _params(key, affine)
 
 
@@ -218,6 +223,14 @@ def test_ltx2_tiny_both_modes(v):
     _bf16_bar(got, oracle_out("ltx2_tiny", "whole"))
     got = host(gpu_decode(v, "ltx2_tiny", "overlap"))
     _bf16_bar(got, oracle_out("ltx2_tiny", "overlap"))
+
+
+@pytest.mark.parametrize("mode,patches", [("patch", (1, 2)), ("overlap", (1, 1))])
+def test_ltx2_tiny_batch_of_two(v, mode, patches):
+    """N = 2: statistics, tiles and epilogue offsets per sample."""
+    got = host(gpu_decode(v, "ltx2_tiny_n2", mode, patches))
+    assert got.shape[0] == 2
+    _bf16_bar(got, oracle_out("ltx2_tiny_n2", "whole" if mode == "patch" else "overlap"))
 
 
 def test_bf16_activation_storage_variant(v):

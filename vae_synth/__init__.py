@@ -15,7 +15,8 @@ is built from its config.json with random weights):
 - ``LTX2_SMALL`` / ``LTX2_MID``: the same layer plan at small latents, for parity at oracle-friendly
   sizes;
 - ``LTX2_720P_1F``: the same plan on one latent frame at the full 720p extent [1,128,1,22,40];
-- ``LTX2_TINY``: the same structure at a quarter of the widths, for a quick smoke check.
+- ``LTX2_TINY``: the same structure at a quarter of the widths, for a quick smoke check;
+  ``LTX2_TINY_N2`` is that plan on a batch of two latents.
 
 Layer plan vocabulary (every op works on a channels-last activation):
 - ``conv``: causal Conv3d 3x3x3, stride 1, ``cin`` -> ``cout``; ``"f32_out": True`` keeps the result
@@ -43,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "LTX2_720P_1F", "LTX2_TINY",
-    "WORKLOADS",
+    "LTX2_TINY_N2", "WORKLOADS",
     "round_bf16", "bf16_bits", "normal", "uniform", "latent", "decoder_params", "conv_params",
     "walk_plan", "with_latent",
 ]
@@ -165,8 +166,11 @@ LTX2_TINY = {
     "overlap_tile": (3, 4), "overlap_stride": (2, 3),
 }
 
+# Two samples in one latent: every per-sample path (GroupNorm statistics, tile offsets) at N = 2.
+LTX2_TINY_N2 = with_latent(LTX2_TINY, (2, 128, 2, 4, 6), "ltx2_tiny_n2")
+
 WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
-                                    LTX2_720P_1F, LTX2_TINY)}
+                                    LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2)}
 
 
 # ----------------------------------------------------------------------------------------------

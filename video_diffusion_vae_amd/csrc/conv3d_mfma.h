@@ -231,6 +231,149 @@ struct BlockShape {
     static constexpr int kBytes = HT * HH * kPitch;
 };
 
+// Epilogue of one block. In a 32x32 accumulator tile, lane l holds column l % 32 and register r
+// holds row (r / 4) * 8 + (l / 32) * 4 + r % 4. Each wave parks one 32 x 32 tile at a time in its
+// LDS slice `ep` (32 rows of kEp floats), then reads rows back four channels per lane: bias,
+// residual, the store (optionally at its depth-to-space position) and GroupNorm partials.
+constexpr int kEp = 32 + 4;                         // padded staging row, floats
+template <typename TO, int HB, int WB, int MI, int MW, int WM>
+__device__ __forceinline__ void conv_epilogue(const MfmaArgs& a, const f32x16_t (&acc)[MI],
+                                              float* ep, int n, int t_blk, int h_blk, int w_blk,
+                                              int bt_i, int bh_i, int bw_i, int co_tile, int lane,
+                                              int wave_m) {
+    constexpr int EP = kEp;
+    constexpr int LPR = 8;                          // lanes per staged row
+    constexpr int RPP = 64 / LPR;                   // rows per pass
+    const int lrow = lane & 31, khalf = lane >> 5;
+    const TO* res = static_cast<const TO*>(a.res);
+    const float* res32 = static_cast<const float*>(a.res);   // when a.res_f32
+    TO* y = static_cast<TO*>(a.y);
+    const int c4 = (lane % LPR) * 4;
+    const int co = co_tile + c4;
+    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.bias)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (co + k < a.cout) bv[k] = a.bias[co + k];
+    // Where this lane's four channels go in y. The sw * zc conv channels of one (dt, dh) are
+    // consecutive elements of one y row (dw, then c). When that count is a multiple of 4, a
+    // lane's aligned four channels stay together and are stored as one vector; otherwise each
+    // channel is placed on its own.
+    const int rowc = a.sw * a.zc;
+    const bool vec = rowc % 4 == 0;
+    const int srow = co / rowc, rem = co - srow * rowc;
+    const int sdh = srow % a.sh, sdt = srow / a.sh;
+    const int sub = co / a.zc, cz = co - sub * a.zc;   // sub-position and channel of y
+    auto y_off = [&](int t, int h, int w, int s_dt, int s_dh, int r) -> int64_t {
+        const int to = a.st * t + s_dt - (a.st - 1);
+        if (to < 0) return -1;   // causal drop
+        return ((((int64_t)n * a.yT + to) * a.yH + a.sh * h + s_dh) * a.yW + (int64_t)a.sw * w) *
+                   a.zc + r;
+    };
+    // GroupNorm partials of this lane's four channels (one group): shifted sums, shift = the
+    // lane's first stored value.
+    float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            ep[((r >> 2) * 8 + khalf * 4 + (r & 3)) * EP + lrow] = acc[i][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int pass = 0; pass < 32 / RPP; ++pass) {
+            const int row = pass * RPP + lane / LPR;
+            const int m = wave_m * MW + i * 32 + row;
+            const int t = t_blk + m / (HB * WB);
+            const int h = h_blk + (m / WB) % HB, w = w_blk + m % WB;
+            if (t < a.box.t1 && h < a.box.h1 && w < a.box.w1 && co < a.cout) {
+                const int nv = a.cout - co < 4 ? a.cout - co : 4;
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = ep[row * EP + c4 + k] + bv[k];
+                if (vec) {
+                    const int64_t o = y_off(t, h, w, sdt, sdh, rem);
+                    if (o >= 0) {
+                        if (nv == 4) {
+                            if (res) {
+                                float rv[4];
+                                if (a.res_f32) load4<float>(res32 + o, rv);
+                                else load4<TO>(res + o, rv);
+#pragma unroll
+                                for (int k = 0; k < 4; ++k) v[k] += rv[k];
+                            }
+                            store4<TO>(y + o, v);
+                        } else {
+                            for (int k = 0; k < nv; ++k) {
+                                if (res)
+                                    v[k] += a.res_f32 ? res32[o + k] : Elem<TO>::load(res + o + k);
+                                Elem<TO>::store(y + o + k, v[k]);
+                            }
+                        }
+                        if (a.stats) {
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                if (k < nv) {
+                                    const float q = stored<TO>(v[k]);
+                                    sk = sn == 0.0f ? q : sk;
+                                    const float d = q - sk;
+                                    s1 += d;
+                                    s2 = fmaf(d, d, s2);
+                                    sn += 1.0f;
+                                }
+                            }
+                        }
+                    }
+                } else {
+                    for (int k = 0; k < nv; ++k) {
+                        const int ck = co + k, rk = ck / rowc;
+                        const int64_t o = y_off(t, h, w, rk / a.sh, rk % a.sh, ck - rk * rowc);
+                        if (o < 0) continue;
+                        if (res) v[k] += a.res_f32 ? res32[o] : Elem<TO>::load(res + o);
+                        Elem<TO>::store(y + o, v[k]);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (a.stats) {
+        // lane -> (count, mean, M2); then merge the 8 lanes that hold the same four channels
+        // (lane ^ 8, 16, 32) and the lanes of one group (cpg / 4 neighbours), in a fixed order.
+        float mean = 0.0f, m2 = 0.0f;
+        if (sn > 0.0f) {
+            const float mk = s1 / sn;
+            mean = sk + mk;
+            m2 = fmaxf(s2 - s1 * mk, 0.0f);
+        }
+        const int cpg = a.zc / a.groups;
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) {
+            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
+                        m2b = __shfl_xor(m2, off);
+            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
+        }
+        for (int off = 1; off < cpg / 4; off <<= 1) {
+            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
+                        m2b = __shfl_xor(m2, off);
+            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
+        }
+        if (lane < LPR && lane % (cpg / 4) == 0 && co < a.cout) {
+            const int g = cz / cpg;
+            const int nblk = a.nbt * a.nbh * a.nbw;
+            const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
+            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
+            double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
+            o[0] = sn;
+            o[1] = mean;
+            o[2] = m2;
+        }
+    }
+}
+
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
 __global__ __launch_bounds__(kMfmaThreads, 2)
 void conv3d_mfma_kernel(MfmaArgs a) {
@@ -552,141 +695,11 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     }
     __syncthreads();  // the input tile is reused for the epilogue
 
-    // Epilogue. In a 32x32 accumulator tile, lane l holds column l % 32 and register r holds
-    // row (r / 4) * 8 + (l / 32) * 4 + r % 4. Each wave parks one 32 x 32 tile at a time in its
-    // own slice of the (now idle) input tile, then reads rows back four channels per lane.
-    constexpr int EP = 32 + 4;                      // padded staging row, floats
-    constexpr int LPR = 8;                          // lanes per staged row
-    constexpr int RPP = 64 / LPR;                   // rows per pass
-    static_assert(kMfmaWaves * 32 * EP * 4 <= kSink, "epilogue staging must fit the tile");
-    float* ep = reinterpret_cast<float*>(halo) + wave * (32 * EP);
-    const TO* res = static_cast<const TO*>(a.res);
-    const float* res32 = static_cast<const float*>(a.res);   // when a.res_f32
-    TO* y = static_cast<TO*>(a.y);
-    const int c4 = (lane % LPR) * 4;
-    const int co = co_tile + c4;
-    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (a.bias)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (co + k < a.cout) bv[k] = a.bias[co + k];
-    // Where this lane's four channels go in y. The sw * zc conv channels of one (dt, dh) are
-    // consecutive elements of one y row (dw, then c). When that count is a multiple of 4, a
-    // lane's aligned four channels stay together and are stored as one vector; otherwise each
-    // channel is placed on its own.
-    const int rowc = a.sw * a.zc;
-    const bool vec = rowc % 4 == 0;
-    const int srow = co / rowc, rem = co - srow * rowc;
-    const int sdh = srow % a.sh, sdt = srow / a.sh;
-    const int sub = co / a.zc, cz = co - sub * a.zc;   // sub-position and channel of y
-    auto y_off = [&](int t, int h, int w, int s_dt, int s_dh, int r) -> int64_t {
-        const int to = a.st * t + s_dt - (a.st - 1);
-        if (to < 0) return -1;   // causal drop
-        return ((((int64_t)n * a.yT + to) * a.yH + a.sh * h + s_dh) * a.yW + (int64_t)a.sw * w) *
-                   a.zc + r;
-    };
-    // GroupNorm partials of this lane's four channels (one group): shifted sums, shift = the
-    // lane's first stored value.
-    float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            ep[((r >> 2) * 8 + khalf * 4 + (r & 3)) * EP + lrow] = acc[i][r];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int pass = 0; pass < 32 / RPP; ++pass) {
-            const int row = pass * RPP + lane / LPR;
-            const int m = wave_m * MW + i * 32 + row;
-            const int t = t_blk + m / (HB * WB);
-            const int h = h_blk + (m / WB) % HB, w = w_blk + m % WB;
-            if (t < a.box.t1 && h < a.box.h1 && w < a.box.w1 && co < a.cout) {
-                const int nv = a.cout - co < 4 ? a.cout - co : 4;
-                float v[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) v[k] = ep[row * EP + c4 + k] + bv[k];
-                if (vec) {
-                    const int64_t o = y_off(t, h, w, sdt, sdh, rem);
-                    if (o >= 0) {
-                        if (nv == 4) {
-                            if (res) {
-                                float rv[4];
-                                if (a.res_f32) load4<float>(res32 + o, rv);
-                                else load4<TO>(res + o, rv);
-#pragma unroll
-                                for (int k = 0; k < 4; ++k) v[k] += rv[k];
-                            }
-                            store4<TO>(y + o, v);
-                        } else {
-                            for (int k = 0; k < nv; ++k) {
-                                if (res)
-                                    v[k] += a.res_f32 ? res32[o + k] : Elem<TO>::load(res + o + k);
-                                Elem<TO>::store(y + o + k, v[k]);
-                            }
-                        }
-                        if (a.stats) {
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                if (k < nv) {
-                                    const float q = stored<TO>(v[k]);
-                                    sk = sn == 0.0f ? q : sk;
-                                    const float d = q - sk;
-                                    s1 += d;
-                                    s2 = fmaf(d, d, s2);
-                                    sn += 1.0f;
-                                }
-                            }
-                        }
-                    }
-                } else {
-                    for (int k = 0; k < nv; ++k) {
-                        const int ck = co + k, rk = ck / rowc;
-                        const int64_t o = y_off(t, h, w, rk / a.sh, rk % a.sh, ck - rk * rowc);
-                        if (o < 0) continue;
-                        if (res) v[k] += a.res_f32 ? res32[o] : Elem<TO>::load(res + o);
-                        Elem<TO>::store(y + o, v[k]);
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    if (a.stats) {
-        // lane -> (count, mean, M2); then merge the 8 lanes that hold the same four channels
-        // (lane ^ 8, 16, 32) and the lanes of one group (cpg / 4 neighbours), in a fixed order.
-        float mean = 0.0f, m2 = 0.0f;
-        if (sn > 0.0f) {
-            const float mk = s1 / sn;
-            mean = sk + mk;
-            m2 = fmaxf(s2 - s1 * mk, 0.0f);
-        }
-        const int cpg = a.zc / a.groups;
-#pragma unroll
-        for (int off = 8; off < 64; off <<= 1) {
-            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
-                        m2b = __shfl_xor(m2, off);
-            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
-        }
-        for (int off = 1; off < cpg / 4; off <<= 1) {
-            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
-                        m2b = __shfl_xor(m2, off);
-            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
-        }
-        if (lane < LPR && lane % (cpg / 4) == 0 && co < a.cout) {
-            const int g = cz / cpg;
-            const int nblk = a.nbt * a.nbh * a.nbw;
-            const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
-            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
-            double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
-            o[0] = sn;
-            o[1] = mean;
-            o[2] = m2;
-        }
-    }
+    // Epilogue: each wave stages through its own slice of the (now idle) input tile.
+    static_assert(kMfmaWaves * 32 * kEp * 4 <= S::kBytes, "epilogue staging must fit the tile");
+    conv_epilogue<TO, HB, WB, MI, MW, WM>(a, acc, reinterpret_cast<float*>(halo) + wave * 32 * kEp,
+                                          n, t_blk, h_blk, w_blk, bt_i, bh_i, bw_i, co_tile, lane,
+                                          wave_m);
 }
 
 enum BlockKind { kBlk2x8x16 = 0, kBlk4x8x8 = 1, kBlk4x4x16 = 2 };
