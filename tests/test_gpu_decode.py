@@ -165,11 +165,14 @@ def test_no_split_on_every_conv_matches_unsplit_decoder(v):
     assert torch.equal(outs[0], outs[1])
 
 
-def test_decode_is_deterministic(v):
+@pytest.mark.parametrize("name", ["ltx2_small", "ltx2_tiny"])
+def test_decode_is_deterministic(v, name):
+    """Two decodes through one workspace are bit-identical (ltx2_tiny's last stage is 32 channels
+    wide, so half of each 64-wide conv tile lies past Cout)."""
     import torch
-    a, b = gpu_decode(v, "ltx2_small", "patch", (1, 2), repeat=2)
+    a, b = gpu_decode(v, name, "patch", (1, 2), repeat=2)
     assert torch.equal(a, b)
-    a, b = gpu_decode(v, "ltx2_small", "overlap", repeat=2)
+    a, b = gpu_decode(v, name, "overlap", repeat=2)
     assert torch.equal(a, b)
 
 

@@ -92,6 +92,9 @@ CONV_GN_CASES = [
     ((1, 3, 9, 19), 64, 64, 8, "f32", "f32", False, None),               # 64-wide tiles
     ((1, 3, 6, 9), 32, 64, 32, "bf16", "f32", False, None),              # 2: separate pass
     ((1, 3, 6, 9), 16, 32, 8, "bf16", "f32", True, None),                # direct conv path
+    # Cout 32 in a 64-wide tile: one wave's channels all past Cout
+    ((1, 3, 8, 20), 64, 32, 8, "bf16", "f32", True, None),
+    ((1, 3, 8, 16), 32, 32, 4, "bf16", "bf16", False, (0, 3, 1, 8, 2, 15)),  # in a box
 ]
 
 
@@ -447,6 +450,11 @@ PACKED_CASES = [
     ((1, 7, 8, 24), 96, 128, "bf16", False),           # 4x8x8, ragged last frame block
     ((1, 8, 12, 32), 64, 256, "bf16", False),          # 4x4x16, ragged rows
     ((1, 6, 16, 8), 32, 128, "f32", True),             # 4x8x8, split
+    # Cout a multiple of 32 but not of the tile: waves whose 32 channels are all past Cout
+    ((1, 3, 8, 16), 64, 32, "bf16", False),            # 64-wide tile, one wave past Cout
+    ((1, 4, 8, 24), 32, 96, "bf16", False),            # second 64-wide tile half used
+    ((1, 3, 9, 16), 64, 160, "bf16", False),           # 128-wide tiles, three waves past Cout
+    ((1, 3, 8, 16), 32, 96, "f32", True),              # split, 64-wide tiles
 ]
 
 

@@ -374,6 +374,147 @@ __device__ __forceinline__ void conv_epilogue(const MfmaArgs& a, const f32x16_t 
     }
 }
 
+// Epilogue straight from the accumulator registers, for outputs where a wave tile's 32 channels
+// are 32 consecutive channels of one y position (zc and Cout multiples of 32): no LDS round trip.
+// Lane l stores channel co_tile + l % 32 of the 16 positions its registers hold, so one store
+// instruction writes two runs of 32 channels.
+//
+// The 16 rows of a lane's 32x32 tile, (r / 4) * 8 + (l / 32) * 4 + r % 4 past the tile's first
+// row, lie in one frame of the block: with WB = 16 they are columns +0..3 and +8..11 of two
+// consecutive rows, with WB = 8 columns +0..3 of four consecutive rows (the tile's first row is a
+// multiple of 32, so no offset carries into the next row or frame). A y offset is then a uniform
+// part (block, tile, register) plus a per-lane 32-bit part (channel, k half), which the stores
+// take as a scalar base and a vector offset. MASKED = false is the case of a block entirely
+// inside the box with no dropped frame: no per-position test.
+template <bool MASKED, typename TO, int HB, int WB, int MI, int MW, int WM>
+__device__ __forceinline__ void conv_epilogue_direct_tiles(
+    const MfmaArgs& a, const f32x16_t (&acc)[MI], int n, int t_blk, int h_blk, int w_blk,
+    int sub, int cz, float bv, int khalf, int wave_m, float& sn, float& sk, float& s1, float& s2) {
+    static_assert(WB == 16 || WB == 8, "direct epilogue row pattern");
+    static_assert(MW % 32 == 0, "tiles start at multiples of 32 rows");
+    const int sdw = sub % a.sw, sdh = (sub / a.sw) % a.sh, sdt = sub / (a.sw * a.sh);
+    const int64_t stride_t = (int64_t)a.st * a.yH * a.yW * a.zc;
+    const int64_t stride_h = (int64_t)a.sh * a.yW * a.zc;
+    const int64_t stride_w = (int64_t)a.sw * a.zc;
+    const int to_blk = a.st * t_blk + sdt - (a.st - 1);
+    // uniform offset of the block's first position (at sub-position `sub`, channel 0 of y)
+    const int64_t blk = ((((int64_t)n * a.yT + to_blk) * a.yH + (int64_t)a.sh * h_blk + sdh) *
+                             a.yW + (int64_t)a.sw * w_blk + sdw) * a.zc;
+    const uint32_t lane_b = (uint32_t)((khalf * 4 * stride_w + cz) * (int64_t)sizeof(TO));
+    char* yb = reinterpret_cast<char*>(a.y);
+    const char* rb = reinterpret_cast<const char*>(a.res);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int mi = wave_m * MW + i * 32;                 // uniform first row of the tile
+        const int tl = mi / (HB * WB), hl = (mi / WB) % HB, wl = mi % WB;
+        const int64_t di = blk + tl * stride_t + hl * stride_h + wl * stride_w;
+        int64_t d[16];                                        // uniform, elements
+        bool ok[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int dh = WB == 16 ? r >> 3 : r >> 2;
+            const int dw = WB == 16 ? ((r >> 2) & 1) * 8 + (r & 3) : r & 3;
+            d[r] = di + dh * stride_h + dw * stride_w;
+            ok[r] = !MASKED || (t_blk + tl < a.box.t1 && to_blk + a.st * tl >= 0 &&
+                                h_blk + hl + dh < a.box.h1 &&
+                                w_blk + wl + khalf * 4 + dw < a.box.w1);
+        }
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = acc[i][r] + bv;
+        if (rb) {
+            // all 16 loads in flight at once; masked positions read the tensor's first element
+            float rv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const char* q = rb + d[r] * (a.res_f32 ? 4 : (int64_t)sizeof(TO)) +
+                                (a.res_f32 ? lane_b / sizeof(TO) * 4 : lane_b);
+                if (MASKED && !ok[r]) q = rb;
+                rv[r] = a.res_f32 ? *reinterpret_cast<const float*>(q)
+                                  : Elem<TO>::load(reinterpret_cast<const TO*>(q));
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[r] += rv[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (ok[r])
+                Elem<TO>::store(reinterpret_cast<TO*>(yb + d[r] * (int64_t)sizeof(TO) + lane_b),
+                                v[r]);
+        if (a.stats) {
+            // shifted sums of the values as stored; shift = this lane's first stored value
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float q = stored<TO>(v[r]);
+                if (MASKED) {
+                    sk = (sn == 0.0f && ok[r]) ? q : sk;
+                    const float dq = ok[r] ? q - sk : 0.0f;
+                    s1 += dq;
+                    s2 = fmaf(dq, dq, s2);
+                    sn += ok[r] ? 1.0f : 0.0f;
+                } else {
+                    if (i == 0 && r == 0) sk = q;
+                    const float dq = q - sk;
+                    s1 += dq;
+                    s2 = fmaf(dq, dq, s2);
+                }
+            }
+            if (!MASKED) sn += 16.0f;
+        }
+    }
+}
+
+template <typename TO, int TB, int HB, int WB, int MI, int MW, int WM>
+__device__ __forceinline__ void conv_epilogue_direct(const MfmaArgs& a, const f32x16_t (&acc)[MI],
+                                                     int n, int t_blk, int h_blk, int w_blk,
+                                                     int bt_i, int bh_i, int bw_i, int co_tile,
+                                                     int lane, int wave_m) {
+    // Cout is a multiple of 32: a wave's 32 channels are all stored or all past Cout
+    if (co_tile >= a.cout) return;
+    const int lrow = lane & 31, khalf = lane >> 5;
+    const int co = co_tile + lrow;
+    const float bv = a.bias ? a.bias[co] : 0.0f;
+    // the wave's 32 channels share one sub-position of the depth-to-space mapping
+    const int sub = co_tile / a.zc, cz = co - sub * a.zc;
+    const int sdt = sub / (a.sw * a.sh);
+    float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    const bool inside = t_blk + TB <= a.box.t1 && h_blk + HB <= a.box.h1 &&
+                        w_blk + WB <= a.box.w1 && a.st * t_blk + sdt - (a.st - 1) >= 0;
+    if (inside)
+        conv_epilogue_direct_tiles<false, TO, HB, WB, MI, MW, WM>(
+            a, acc, n, t_blk, h_blk, w_blk, sub, cz, bv, khalf, wave_m, sn, sk, s1, s2);
+    else
+        conv_epilogue_direct_tiles<true, TO, HB, WB, MI, MW, WM>(
+            a, acc, n, t_blk, h_blk, w_blk, sub, cz, bv, khalf, wave_m, sn, sk, s1, s2);
+    if (a.stats) {
+        // lane -> (count, mean, M2); merge the two lanes of one channel (lane ^ 32), then the
+        // cpg lanes of one group, in a fixed order
+        float mean = 0.0f, m2 = 0.0f;
+        if (sn > 0.0f) {
+            const float mk = s1 / sn;
+            mean = sk + mk;
+            m2 = fmaxf(s2 - s1 * mk, 0.0f);
+        }
+        const int cpg = a.zc / a.groups;
+        for (int off = 32; off >= 1; off >>= 1) {
+            if (off < 32 && off >= cpg) continue;
+            const float nb = __shfl_xor(sn, off), mb = __shfl_xor(mean, off),
+                        m2b = __shfl_xor(m2, off);
+            chan_merge_f32(sn, mean, m2, nb, mb, m2b);
+        }
+        if (lane < 32 && lane % cpg == 0) {
+            const int g = cz / cpg;
+            const int nblk = a.nbt * a.nbh * a.nbw;
+            const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
+            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
+            double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
+            o[0] = sn;
+            o[1] = mean;
+            o[2] = m2;
+        }
+    }
+}
+
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
 __global__ __launch_bounds__(kMfmaThreads, 2)
 void conv3d_mfma_kernel(MfmaArgs a) {
@@ -692,6 +833,11 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    }
+    if (a.zc % 32 == 0 && a.cout % 32 == 0) {
+        conv_epilogue_direct<TO, TB, HB, WB, MI, MW, WM>(a, acc, n, t_blk, h_blk, w_blk, bt_i, bh_i,
+                                                     bw_i, co_tile, lane, wave_m);
+        return;
     }
     __syncthreads();  // the input tile is reused for the epilogue
 
