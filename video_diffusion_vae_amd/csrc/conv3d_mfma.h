@@ -698,9 +698,12 @@ void conv3d_mfma_kernel(MfmaArgs a) {
         constexpr int LDK[4] = {2, TB == 2 ? 20 : 10, TB == 2 ? 38 : 20, 38};
         constexpr int WRK[4] = {TB == 2 ? 14 : 8, TB == 2 ? 32 : 16, TB == 2 ? 48 : 30, 46};
         constexpr int HLD[2] = {TB == 2 ? 50 : 48, 50};
-        for (int kc = 0; kc < n_chunks; ++kc) {
+        // One chunk. NEXT: stage the next chunk's frames and fetch its first weights while this
+        // one computes. The last chunk is a copy without those loads and writes.
+        auto chunk = [&](int kc, auto next_c) {
+            constexpr bool NEXT = decltype(next_c)::value;
             const int c0 = kc * CK;
-            const int cn = (kc + 1 < n_chunks ? kc + 1 : kc) * CK;   // the last chunk restages
+            const int cn = (kc + 1) * CK;
             auto slot = [&](int f) { return (b + f + 2 * NS) % NS; };
             int abase[MI];
             auto set_phase = [&](int kt) {
@@ -721,15 +724,17 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                     __syncthreads();
                     set_phase(step == 17 ? 1 : 2);
                 }
-                if constexpr (kk == 0) {
+                constexpr bool ldb = kk == 0 && (tap + PD < 27 || NEXT);
+                if constexpr (ldb) {
                     if constexpr (tap + PD < 27) load_b((tap + PD) % NB, tap + PD, c0);
                     else load_b((tap + PD) % NB, tap + PD - 27, cn);
                 }
-                constexpr int ldk = step == LDK[0] ? 0 : step == LDK[1] ? 1 : step == LDK[2] ? 2
-                                  : (NIN > 3 && step == LDK[3]) ? 3 : -1;
-                constexpr int wrk = step == WRK[0] ? 0 : step == WRK[1] ? 1 : step == WRK[2] ? 2
-                                  : (NIN > 3 && step == WRK[3]) ? 3 : -1;
-                constexpr int hld = step == HLD[0] ? 0 : (NHOLD > 1 && step == HLD[1]) ? 1 : -1;
+                constexpr int ldk = !NEXT ? -1 : step == LDK[0] ? 0 : step == LDK[1] ? 1
+                                  : step == LDK[2] ? 2 : (NIN > 3 && step == LDK[3]) ? 3 : -1;
+                constexpr int wrk = !NEXT ? -1 : step == WRK[0] ? 0 : step == WRK[1] ? 1
+                                  : step == WRK[2] ? 2 : (NIN > 3 && step == WRK[3]) ? 3 : -1;
+                constexpr int hld = !NEXT ? -1 : step == HLD[0] ? 0
+                                  : (NHOLD > 1 && step == HLD[1]) ? 1 : -1;
                 if constexpr (step == 0) {
 #pragma unroll
                     for (int h = 0; h < NHOLD; ++h) frame_write(slot(NIN + h), h);
@@ -753,7 +758,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                                                                      acc[i], 0, 0, 0);
                 constexpr int n_ld = (ldk >= 0) + (hld >= 0);
                 constexpr int n_wr = (wrk >= 0) + (step == 0 ? NHOLD : 0);
-                if constexpr (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
+                if constexpr (ldb) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
                 if constexpr (n_ld > 0)
                     __builtin_amdgcn_sched_group_barrier(0x020, n_ld * FST * (int)(sizeof(TI) / 2),
                                                          0);
@@ -768,7 +773,9 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             });
             __syncthreads();   // chunk done: its later frames are free, the next chunk is staged
             b = (b + NS - NSP) % NS;
-        }
+        };
+        for (int kc = 0; kc + 1 < n_chunks; ++kc) chunk(kc, std::true_type{});
+        chunk(n_chunks - 1, std::false_type{});
     } else {
         for (int kc = 0; kc < n_chunks; ++kc) {
             const int c0 = kc * CK;
