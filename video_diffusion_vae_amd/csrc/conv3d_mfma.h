@@ -29,9 +29,12 @@
 //    their hi halves in the first 32 bytes and their lo halves in the next 32. The two k steps of
 //    a tap read hi and lo against the same weight fragment. Each fp32 value is loaded once, and
 //    the weight loads per MFMA halve.
-//  - Epilogue: each wave parks one 32 x 32 accumulator tile at a time in LDS (reusing the input
-//    tile), then every lane writes four consecutive channels with one 16-byte (fp32) or 8-byte
-//    (bf16) store. Bias and residual are added on the way.
+//  - Epilogue. Where a wave's 32 channels are 32 consecutive channels of y (Cout and y's channel
+//    count multiples of 32), each lane stores its accumulator registers directly: one channel at
+//    16 positions, two runs of 32 channels per store instruction. Otherwise each wave parks one
+//    32 x 32 tile at a time in LDS (reusing the input tile) and every lane writes four
+//    consecutive channels with one 16-byte (fp32) or 8-byte (bf16) store. Bias, residual,
+//    depth-to-space placement and GroupNorm partials are done on the way.
 //  - Workgroups are ordered output-channel tile slowest, and remapped so that each XCD (the
 //    hardware deals workgroup i to XCD i % 8) runs a contiguous range of them. An XCD then keeps
 //    one weight slice in its own L2 while it streams input blocks.
