@@ -40,6 +40,13 @@ CONV_SOURCES = sorted(os.path.join("video_diffusion_vae_amd", "csrc", f) for f i
                       if f.startswith("conv3d") or f in ("kernels.h", "common.h"))
 CONV_KERNEL = "conv3d_mfma_kernel"
 COPY_KERNEL = "upsample_kernel"
+OPERANDS = {
+    "f16": "bf16 weights and GroupNorm operands; the 3 upsampling convs and conv_out take fp16 "
+           "operands (fp16 hand-off of the fp32 stream, weights exact in fp16); fp32 accumulate",
+    "split": "bf16 weights; the upsampling convs up0/up1 and conv_out apply fp32 inputs as bf16 "
+             "hi+lo; fp32 accumulate",
+    "bf16": "bf16 weights and operands; fp32 accumulate",
+}
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "conv3d_mfma_ltx2_720p_patch_halo_1x4_traffic.json")
 
 
@@ -173,6 +180,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", choices=["patch", "overlap"], default="patch")
+    ap.add_argument("--operands", choices=["f16", "split", "bf16"], default="f16",
+                    help="operands of the convs that read an fp32 activation (up-convs, conv_out)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=2)
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
@@ -206,7 +215,7 @@ def main():
     z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))
     params = vae_synth.decoder_params(spec)
     dev = torch.device("cuda:0")
-    dec = v.upload_decoder(spec, params, dev)
+    dec = v.upload_decoder(spec, params, dev, operands=args.operands)
     zd = torch.as_tensor(z).to(device=dev, dtype=torch.bfloat16)
     if args.mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 4))
@@ -296,7 +305,7 @@ def main():
         "data": "synthetic (seeded latent, random-init weights)",
         "config": {"workload": workload, "latent": [1, 128, 16, 22, 40],
                    "output": [1, 3, 121, 704, 1280], "parallelism": "none (1 GPU)",
-                   "operands": "bf16 weights; fp32 conv inputs as bf16 hi+lo; fp32 accumulate",
+                   "operands": OPERANDS[args.operands],
                    "activations": "fp32 between ops, bf16 GroupNorm outputs inside res blocks",
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
         "roofline": roofline, "kernels": summary, "timing": timing, "cpu_baseline": baseline,

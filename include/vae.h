@@ -13,6 +13,10 @@
  *  - Layout: activations are dense NDHWC (channels fastest), addressed with 64-bit offsets.
  *    Conv weights are [Cout][kt=3][kh=3][kw=3][Cin]. Bias, gamma and beta are fp32 vectors.
  *  - Dtypes: VAE_DTYPE_BF16 (bfloat16 storage, fp32 arithmetic) or VAE_DTYPE_F32.
+ *    VAE_DTYPE_F16 (IEEE binary16 storage, 11 significant bits) is accepted only where a call
+ *    says so: as a conv input on the MFMA path, as the conv output of a bf16 input, as a
+ *    GroupNorm output, and by vae_upsample (a copy). It is the operand hand-off of convs whose
+ *    input needs more than bf16's 8 significant bits (see vae_conv3d_causal).
  *  - Ownership: the caller owns every buffer. Device buffers are passed as raw device pointers;
  *    the library never allocates or frees device memory and never synchronises the stream. It
  *    keeps no pointer after a call returns, except the weight pointers held by a decoder object,
@@ -51,7 +55,7 @@ typedef enum {
     VAE_ERR_WORKSPACE = 4     /* workspace missing or smaller than the size query returned */
 } vae_status_t;
 
-enum { VAE_DTYPE_BF16 = 1, VAE_DTYPE_F32 = 2 };
+enum { VAE_DTYPE_BF16 = 1, VAE_DTYPE_F32 = 2, VAE_DTYPE_F16 = 3 };
 
 typedef struct vae_tensor {
     void* data;       /* device pointer, NDHWC dense */
@@ -101,20 +105,29 @@ VAE_API int32_t vae_version(void);
  * the tensor. Such a box is one patch of a patch-halo decode.
  *
  * Arguments:
- *  x: [N,T,H,W,Cin] input (device), bf16 or fp32.
+ *  x: [N,T,H,W,Cin] input (device), bf16, fp32, or fp16 (MFMA path only).
  *  weight: [Cout][3][3][3][Cin] (device) of dtype weight_dtype.
  *  bias: [Cout] fp32 (device), or NULL.
- *  residual: tensor of y's shape and dtype added to the result, or NULL. It may alias y.
- *  y: [N,T,H,W,Cout] output, bf16 or fp32. It must not overlap x.
- *  flags: 0, or a combination of VAE_CONV_SPLIT_FP32 and VAE_CONV_PACKED_WEIGHTS (weight is then
- *         the fragment-packed copy written by vae_conv_weight_pack; MFMA path only).
+ *  residual: tensor of y's shape and dtype added to the result, or NULL. It may alias y. When y
+ *            is bf16 or fp16 the residual may also be fp32 (a residual stream kept in fp32; the
+ *            sum is rounded once, at the store).
+ *  y: [N,T,H,W,Cout] output, bf16 or fp32; fp16 when x is bf16 (MFMA path). It must not
+ *     overlap x.
+ *  flags: 0, or a combination of VAE_CONV_SPLIT_FP32 and one of
+ *         VAE_CONV_PACKED_WEIGHTS (weight is the fragment-packed copy written by
+ *         vae_conv_weight_pack; MFMA path, bf16 or fp32 x) or
+ *         VAE_CONV_PACKED_F16_WEIGHTS (weight is the fp16 copy written by
+ *         vae_conv_weight_pack_f16; fp16 x only).
  * bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (MFMA). Products
  * accumulate in fp32. An fp32 x is rounded to bf16 (nearest-even) as the operand, or, with
  * VAE_CONV_SPLIT_FP32, applied as two bf16 operands hi = bf16(x) and lo = bf16(x - hi). The split
- * keeps about 16 significant bits of x and costs twice the matrix-core work. Every other case runs
- * on a direct fp32-accumulating path, where the flag changes nothing.
+ * keeps about 16 significant bits of x and costs twice the matrix-core work. An fp16 x is applied
+ * as fp16 operands at the bf16 rate: the bf16 weights are converted exactly, scaled by 2^10 into
+ * fp16's normal range (|w| must stay below 64), and the fp32 sums are scaled back by 2^-10, which
+ * is exact. Every other case runs on a direct fp32-accumulating path, where the split flag changes
+ * nothing.
  */
-enum { VAE_CONV_SPLIT_FP32 = 1, VAE_CONV_PACKED_WEIGHTS = 2 };
+enum { VAE_CONV_SPLIT_FP32 = 1, VAE_CONV_PACKED_WEIGHTS = 2, VAE_CONV_PACKED_F16_WEIGHTS = 4 };
 VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
                                        int32_t weight_dtype, const float* bias,
                                        const vae_tensor_t* residual, vae_tensor_t* y,
@@ -146,7 +159,7 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
  *  - Other shapes run a separate statistics pass over y, with the same result up to rounding.
  *
  * Arguments:
- *  residual: y's shape and dtype, or NULL.
+ *  residual: as for vae_conv3d_causal (y's shape; y's dtype, or fp32), or NULL.
  *  ws / ws_bytes: device scratch of vae_conv3d_causal_fused_workspace() bytes, 16-byte aligned,
  *  owned by the caller (unused without statistics). Its contents are undefined afterwards.
  *
@@ -184,6 +197,11 @@ VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_s
 VAE_API vae_status_t vae_conv_weight_pack_size(int32_t cout, int32_t cin, size_t* bytes);
 VAE_API vae_status_t vae_conv_weight_pack(const void* weight, int32_t cout, int32_t cin,
                                           void* packed, vae_stream_t stream);
+/* The same layout with every bf16 weight converted to fp16 after scaling by 2^10 (exact for
+ * |w| < 64; magnitudes below 2^-24 lose bits as fp16 subnormals). It is the weight operand of an
+ * fp16 x (VAE_CONV_PACKED_F16_WEIGHTS). Same size as vae_conv_weight_pack_size. */
+VAE_API vae_status_t vae_conv_weight_pack_f16(const void* weight, int32_t cout, int32_t cin,
+                                              void* packed, vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* GroupNorm (+SiLU) with statistics merged across patches                                    */
@@ -203,8 +221,10 @@ VAE_API vae_status_t vae_conv_weight_pack(const void* weight, int32_t cout, int3
  *  boxes: the patches owning the statistics (n_boxes >= 1; NULL with n_boxes == 1 = whole tensor).
  *         The apply step writes y over every box.
  *  gamma, beta: [C] fp32 (device) or NULL (1 and 0).
- *  y: same shape as x; dtype bf16 or fp32 (it may differ from x: an fp32 activation normalised
- *     into the bf16 operand of the next convolution). It may alias x when the dtypes match.
+ *  x: bf16 or fp32.
+ *  y: same shape as x; dtype bf16, fp32 or fp16 (it may differ from x: an fp32 activation
+ *     normalised into the bf16 or fp16 operand of the next convolution). It may alias x when the
+ *     dtypes match.
  *  ws: device scratch of at least vae_groupnorm_silu_workspace() bytes.
  * Partials are combined in a fixed order: results are bitwise reproducible run to run.
  */
@@ -333,6 +353,11 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * upsampling convs read the fp32 residual stream): each such CONV runs with VAE_CONV_SPLIT_FP32
  * unless its no_split is set. A standalone GN_SILU followed by a splitting CONV writes fp32 for
  * it. The convs inside residual blocks keep one rounding of their GroupNorm operand.
+ * VAE_DECODE_F16_OPERANDS (bf16 plans with fp32 activations; not with the split flag) gives
+ * those same convs, i.e. every CONV that follows a RES or GN_SILU, fp16 operands instead: the producing op stores its
+ * output in fp16 (one rounding to 11 significant bits) and the conv runs at the bf16 rate
+ * (vae_conv3d_causal with an fp16 x). no_split does not apply to it. Activations must stay below
+ * 65504 in magnitude there.
  * The parameter pointers come in plan order, two per entry:
  *  conv -> (weight, bias);
  *  GN -> (gamma, beta);
@@ -350,11 +375,11 @@ typedef struct vae_layer_desc {
                           splits fp32 operands (VAE_DECODE_SPLIT_FP32_OPERANDS) */
 } vae_layer_desc_t;
 
-enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1 };
+enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1, VAE_DECODE_F16_OPERANDS = 2 };
 typedef struct vae_decoder_spec {
     int32_t dtype;              /* weights and convolution operands: VAE_DTYPE_* */
     int32_t act_dtype;          /* activations stored between ops (conv outputs, residual stream) */
-    int32_t flags;              /* VAE_DECODE_SPLIT_FP32_OPERANDS or 0 */
+    int32_t flags;              /* VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS or 0 */
     int32_t latent_channels;
     int32_t groups;
     float eps;

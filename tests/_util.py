@@ -7,11 +7,14 @@ def ndhwc(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64).transpose(0, 2, 3, 4, 1))
 
 
+TORCH_DTYPES = {"bf16": "bfloat16", "f32": "float32", "f16": "float16"}
+
+
 def dev(a, dtype="bf16"):
-    """Host NDHWC array (bf16-exact values for bf16) -> contiguous device tensor."""
+    """Host NDHWC array (values exact in ``dtype`` for bf16/f16) -> contiguous device tensor."""
     import torch
     t = torch.as_tensor(np.ascontiguousarray(np.asarray(a, dtype=np.float32)))
-    return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    return t.to(device="cuda", dtype=getattr(torch, TORCH_DTYPES[dtype]))
 
 
 def host(t):
@@ -34,3 +37,14 @@ def psnr(got, ref):
 def bf16_round_bound(ref):
     """Elementwise bound of one round-to-nearest-even bf16 store of ``ref``: half a bf16 ulp."""
     return np.abs(ref) * 2.0 ** -8
+
+
+def f16_round_bound(ref):
+    """Elementwise bound of one round-to-nearest-even fp16 store of ``ref`` (normal range): half
+    an fp16 ulp."""
+    return np.abs(ref) * 2.0 ** -11
+
+
+def round_f16(a):
+    """Nearest-even fp16 rounding (numpy's conversion), back in float64."""
+    return np.asarray(a, np.float64).astype(np.float16).astype(np.float64)

@@ -116,6 +116,10 @@ def test_decoder_plan_validation(v):
         v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, spec["layers"], fake[:0],
                   act_dtype=v.VAE_DTYPE_BF16)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:      # split and fp16 operands together
+        v.Decoder(v.VAE_DTYPE_BF16, 16, 32, 1e-6, spec["layers"], fake[:0],
+                  flags=v.VAE_DECODE_SPLIT_FP32_OPERANDS | v.VAE_DECODE_F16_OPERANDS)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
 
 
 def test_workspace_query_needs_no_gpu(v):
@@ -131,7 +135,8 @@ def test_workspace_query_needs_no_gpu(v):
 
         def data_ptr(self):
             return self.p.value
-    dec = v.Decoder(v.VAE_DTYPE_BF16, 128, 32, 1e-6, spec["layers"], [P(p) for p in ptrs])
+    dec = v.Decoder(v.VAE_DTYPE_BF16, 128, 32, 1e-6, spec["layers"], [P(p) for p in ptrs],
+                    flags=v.VAE_DECODE_F16_OPERANDS)
     a = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
                                          (8, 32, 32), patches=(1, 4)))
     b = dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 16, 22, 40, 128),

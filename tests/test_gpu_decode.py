@@ -69,11 +69,13 @@ def oracle_out(name, mode, affine=None):
                                        spec["scale"])
 
 
-def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32"):
+def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32", operands="f16"):
+    """Decode through vae_decode_tiled. ``operands``: how convs reading an fp32 activation get
+    their operands, "f16" (the default), "split" (bf16 hi + lo) or "bf16"."""
     import torch
     spec = spec_of(name)
     z = ndhwc(vae_synth.latent(spec))
-    dec = v.upload_decoder(spec, params_of(name, affine), act_dtype=act)
+    dec = v.upload_decoder(spec, params_of(name, affine), act_dtype=act, operands=operands)
     zd = dev(z, spec["dtype"])
     if mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
@@ -118,24 +120,28 @@ def _bf16_bar(got, ref):
     return p, m
 
 
+@pytest.mark.parametrize("operands", ["f16", "split"])
 @pytest.mark.parametrize("name,patches", [("ltx2_small", (1, 2)), ("ltx2_small", (1, 1)),
                                           ("ltx2_mid", (2, 3))])
-def test_ltx2_shaped_patch_halo(v, name, patches):
-    got = host(gpu_decode(v, name, "patch", patches))
+def test_ltx2_shaped_patch_halo(v, name, patches, operands):
+    got = host(gpu_decode(v, name, "patch", patches, operands=operands))
     _bf16_bar(got, oracle_out(name, "whole"))
 
 
+@pytest.mark.parametrize("operands", ["f16", "split"])
 @pytest.mark.parametrize("name", ["ltx2_small", "ltx2_mid"])
-def test_ltx2_shaped_overlap_blend(v, name):
-    got = host(gpu_decode(v, name, "overlap"))
+def test_ltx2_shaped_overlap_blend(v, name, operands):
+    got = host(gpu_decode(v, name, "overlap", operands=operands))
     _bf16_bar(got, oracle_out(name, "overlap"))
 
 
+@pytest.mark.parametrize("operands", ["f16", "split"])
 @pytest.mark.parametrize("mode,patches", [("patch", (1, 4)), ("overlap", (1, 1))])
-def test_ltx2_720p_one_frame_every_value(v, mode, patches):
+def test_ltx2_720p_one_frame_every_value(v, mode, patches, operands):
     """The full-width 720p plan on one latent frame ([1,128,1,22,40] -> [1,1,704,1280,3]): every
-    one of the 2.7M output values against the oracle, in both tiling modes."""
-    got = host(gpu_decode(v, "ltx2_720p_1f", mode, patches))
+    one of the 2.7M output values against the oracle, in both tiling modes and with fp16 or split
+    operands for the convs that read an fp32 activation."""
+    got = host(gpu_decode(v, "ltx2_720p_1f", mode, patches, operands=operands))
     assert got.shape == (1, 1, 704, 1280, 3)
     _bf16_bar(got, oracle_out("ltx2_720p_1f", "whole" if mode == "patch" else "overlap"))
 
@@ -154,8 +160,8 @@ def test_no_split_on_every_conv_matches_unsplit_decoder(v):
     zd = dev(z, "bf16")
     desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 2))
     outs = []
-    for sp, split in ((ns, True), (spec, False)):
-        dec = v.upload_decoder(sp, params_of("ltx2_tiny"), split=split)
+    for sp, operands in ((ns, "split"), (spec, "bf16")):
+        dec = v.upload_decoder(sp, params_of("ltx2_tiny"), operands=operands)
         ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
         out = torch.empty(oracle.output_shape(spec, z.shape), dtype=torch.float32, device="cuda")
         dec.vae_decode_tiled(zd, desc, out, ws)
@@ -165,14 +171,15 @@ def test_no_split_on_every_conv_matches_unsplit_decoder(v):
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("operands", ["f16", "split"])
 @pytest.mark.parametrize("name", ["ltx2_small", "ltx2_tiny"])
-def test_decode_is_deterministic(v, name):
+def test_decode_is_deterministic(v, name, operands):
     """Two decodes through one workspace are bit-identical (ltx2_tiny's last stage is 32 channels
     wide, so half of each 64-wide conv tile lies past Cout)."""
     import torch
-    a, b = gpu_decode(v, name, "patch", (1, 2), repeat=2)
+    a, b = gpu_decode(v, name, "patch", (1, 2), repeat=2, operands=operands)
     assert torch.equal(a, b)
-    a, b = gpu_decode(v, name, "overlap", repeat=2)
+    a, b = gpu_decode(v, name, "overlap", repeat=2, operands=operands)
     assert torch.equal(a, b)
 
 
@@ -197,17 +204,19 @@ def _check_golden(g, out):
     assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
 
 
-def test_ltx2_720p_overlap_blend_against_golden(v):
+@pytest.mark.parametrize("operands", ["f16", "split"])
+def test_ltx2_720p_overlap_blend_against_golden(v, operands):
     """Full 720p overlap-blend decode: 2x3 tiles of 16x16 latents, stride 14 (512/448 px)."""
     g = _golden("overlap")
-    _check_golden(g, gpu_decode(v, "ltx2_720p", "overlap"))
+    _check_golden(g, gpu_decode(v, "ltx2_720p", "overlap", operands=operands))
 
 
-def test_ltx2_720p_patch_halo_against_golden(v):
+@pytest.mark.parametrize("operands", ["f16", "split"])
+def test_ltx2_720p_patch_halo_against_golden(v, operands):
     """Full 720p decode (latent [1,128,16,22,40] -> [1,121,704,1280,3]), 1x4 width patches, at
     the pixels the oracle's full fp64 decode stored."""
     g = _golden("whole")
-    out = gpu_decode(v, "ltx2_720p", "patch", (1, 4))
+    out = gpu_decode(v, "ltx2_720p", "patch", (1, 4), operands=operands)
     pos = g["positions"]
     got = out[0, pos[:, 0], pos[:, 1], pos[:, 2], :].double().cpu().numpy()
     ref = g["values"]
@@ -240,12 +249,17 @@ def test_bf16_activation_storage_variant(v):
     """Storing every activation in bf16 (act_dtype=bf16) is the faster, less exact variant. About
     40 extra roundings keep it above 50 dB PSNR, but it is not held to the 2e-2 max-abs bar; the
     default (fp32 activations) is."""
-    got = host(gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16"))
+    import torch
+    got = gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16")
     ref = oracle_out("ltx2_tiny", "whole")
-    assert psnr(got, ref) >= 50.0
+    assert psnr(host(got), ref) >= 50.0
+    # a bf16 stream has nothing finer to hand on: the fp16 operand flag changes nothing
+    same = gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16", operands="bf16")
+    assert torch.equal(got, same)
 
 
-def test_packed_and_standard_weights_decode_identically(v):
+@pytest.mark.parametrize("operands", ["f16", "split"])
+def test_packed_and_standard_weights_decode_identically(v, operands):
     import torch
     spec = vae_synth.LTX2_TINY
     z = ndhwc(vae_synth.latent(spec))
@@ -253,7 +267,7 @@ def test_packed_and_standard_weights_decode_identically(v):
     desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 2))
     outs = []
     for packed in (False, True):
-        dec = v.upload_decoder(spec, params_of("ltx2_tiny"), packed=packed)
+        dec = v.upload_decoder(spec, params_of("ltx2_tiny"), packed=packed, operands=operands)
         ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
         out = torch.empty(oracle.output_shape(spec, z.shape), dtype=torch.float32, device="cuda")
         dec.vae_decode_tiled(zd, desc, out, ws)

@@ -4,6 +4,9 @@ Tolerances:
 - fp32 paths: relative max-abs <= 1e-4;
 - bf16 inputs with fp32 output: products are exact in fp32, so the same 1e-4;
 - bf16 outputs: half a bf16 ulp of the reference plus 1e-4 relative (one rounding per store);
+  fp16 outputs: half an fp16 ulp plus 1e-4 relative;
+- fp16 inputs: the operands are exact (fp16 x, bf16 weights scaled by 2^10 into fp16), so fp32
+  outputs are held to 1e-4 relative;
 - integer/permutation work (upsampling): bit-exact.
 """
 import numpy as np
@@ -11,7 +14,7 @@ import pytest
 
 import oracle
 import vae_synth
-from _util import ndhwc, dev, host, rel_max_abs, bf16_round_bound
+from _util import ndhwc, dev, host, rel_max_abs, bf16_round_bound, f16_round_bound, round_f16
 
 pytestmark = pytest.mark.gpu
 
@@ -288,6 +291,8 @@ GN_CASES = [
     ("f32>bf16", (1, 3, 11, 20, 128), 32, ([], [5, 10, 15])),
     ("f32>bf16", (1, 2, 8, 10, 1024), 32, ([4], [])),
     ("bf16>f32", (1, 2, 6, 7, 256), 32, ([3], [])),
+    ("f32>f16", (1, 3, 11, 20, 128), 32, ([], [5, 10, 15])),
+    ("bf16>f16", (1, 2, 8, 10, 256), 32, ([4], [])),
 ]
 
 
@@ -312,7 +317,7 @@ def test_groupnorm_silu_patch_stats(v, case):
     boxes = _boxes(shape, cuts)
     xd = dev(x, idt)
     y = torch.empty(xd.shape, device="cuda",
-                    dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
+                    dtype={"bf16": torch.bfloat16, "f16": torch.float16}.get(odt, torch.float32))
     g_d, b_d = torch.as_tensor(gamma, device="cuda"), torch.as_tensor(beta, device="cuda")
     v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, g_d, b_d, True, y)
     torch.cuda.synchronize()
@@ -320,7 +325,8 @@ def test_groupnorm_silu_patch_stats(v, case):
     if odt == "f32":
         assert rel_max_abs(got, ref) <= 1e-4
     else:
-        assert np.all(np.abs(got - ref) <= bf16_round_bound(ref) + 1e-4 * np.abs(ref).max())
+        bound = bf16_round_bound(ref) if odt == "bf16" else f16_round_bound(ref)
+        assert np.all(np.abs(got - ref) <= bound + 1e-4 * np.abs(ref).max())
     # determinism: the same call gives a bitwise identical result (in place when dtypes match)
     y2 = xd if idt == odt else torch.empty_like(y)
     v.vae_groupnorm_silu(xd, boxes, groups, 1e-6, g_d, b_d, True, y2)
@@ -376,6 +382,8 @@ UP_CASES = [
     ("f32", (1, 2, 5, 3, 12), "d2s", (2, 1, 1), None),
     ("bf16", (1, 2, 3, 4, 16), "nearest", (1, 2, 2), None),
     ("f32", (1, 1, 3, 3, 4), "nearest", (1, 2, 3), (0, 1, 1, 3, 0, 2)),
+    ("f16", (1, 3, 4, 5, 64), "d2s", (2, 2, 2), None),
+    ("f16", (1, 2, 3, 4, 16), "nearest", (1, 2, 2), (0, 2, 1, 3, 0, 4)),
 ]
 
 
@@ -385,6 +393,8 @@ def test_upsample_bit_exact(v, case):
     dtype, shape, mode, (st, sh, sw), bx = case
     n, t, h, w, c = shape
     x = ndhwc(vae_synth.normal((n, c, t, h, w), [25, c], dtype=dtype))
+    if dtype == "f16":
+        x = round_f16(x)
     if mode == "d2s":
         ref = oracle.depth_to_space(x, st, sh, sw)
         m = v.VAE_UPSAMPLE_D2S
@@ -485,3 +495,109 @@ def test_conv3d_packed_weights_bitwise_equal(v, case):
     else:
         xin = vae_synth.round_bf16(x).astype(np.float64)
     assert rel_max_abs(host(y1), oracle.causal_conv3d(xin, wt, b)) <= 1e-4
+
+
+F16_IN_CASES = [
+    # (N, T, H, W), Cin, Cout, out dtype, residual, box
+    ((1, 3, 9, 17), 32, 64, "f32", False, None),
+    ((1, 5, 10, 20), 64, 128, "f32", True, None),
+    ((2, 2, 8, 16), 32, 48, "f32", False, None),                    # staged epilogue
+    ((1, 4, 11, 23), 128, 256, "bf16", True, (1, 4, 2, 9, 5, 15)),
+    ((1, 2, 8, 16), 128, 52, "f32", True, None),
+    ((1, 1, 7, 5), 96, 128, "f32", False, None),
+]
+
+
+@pytest.mark.parametrize("case", F16_IN_CASES)
+def test_conv3d_f16_input(v, case):
+    """An fp16 input runs v_mfma_f32_32x32x16_f16 against the bf16 weights converted to fp16
+    (scaled by 2^10, then the sums by 2^-10): the operands are exact, so the result is the
+    oracle's conv of the fp16 values up to fp32 summation. Standard-layout and fp16-packed
+    weights give bitwise equal results."""
+    import torch
+    (n, t, h, w), cin, cout, odt, use_res, bx = case
+    x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", 80 + F16_IN_CASES.index(case))
+    # an fp32 activation with finer values than bf16, rounded once to fp16
+    x = round_f16(x + ndhwc(vae_synth.normal((n, cin, t, h, w), [15, cin], scale=1e-3)))
+    ref = oracle.causal_conv3d(x, wt, b)
+    if use_res:
+        ref = ref + r
+    xd = dev(x, "f16")
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, odt) if use_res else None
+    tdt = torch.float32 if odt == "f32" else torch.bfloat16
+    y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=tdt)
+    v.vae_conv3d_causal(xd, wd, bd, rd, y, bx)
+    yp = torch.full_like(y, 7.0)
+    wp = v.vae_conv_weight_pack_f16(wd).view(torch.bfloat16)
+    v.vae_conv3d_causal(xd, wp, bd, rd, yp, bx, flags=v.VAE_CONV_PACKED_F16_WEIGHTS)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+    got = host(y)
+    bx = bx or (0, t, 0, h, 0, w)
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    mask = np.zeros(got.shape, bool)
+    mask[sl] = True
+    assert np.all(got[~mask] == 7.0), "conv wrote outside its box"
+    g, rf = got[sl], ref[sl]
+    if odt == "f32":
+        assert rel_max_abs(g, rf) <= 1e-4
+    else:
+        assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
+
+
+F16_OUT_CASES = [
+    # (N, T, H, W), Cin, Cout, residual dtype (None = no residual)
+    ((1, 3, 9, 17), 64, 128, "f32"),        # direct epilogue, fp32 residual stream
+    ((1, 4, 8, 16), 32, 64, "f16"),
+    ((2, 2, 8, 16), 32, 48, "f32"),         # staged epilogue
+    ((1, 2, 5, 9), 128, 256, None),
+]
+
+
+@pytest.mark.parametrize("case", F16_OUT_CASES)
+def test_conv3d_f16_output_handoff(v, case):
+    """A bf16-input conv that stores fp16 (the operand hand-off to an fp16-input conv), with an
+    fp32 or fp16 residual: one nearest-even rounding of the fp32 sum."""
+    import torch
+    (n, t, h, w), cin, cout, rdt = case
+    x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", 90 + F16_OUT_CASES.index(case))
+    if rdt == "f16":
+        r = round_f16(r)
+    ref = oracle.causal_conv3d(x, wt, b) + (r if rdt else 0.0)
+    y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=torch.float16)
+    v.vae_conv3d_causal(dev(x, "bf16"), v.conv_weight_layout(wt, torch.bfloat16, "cuda"),
+                        torch.as_tensor(b, dtype=torch.float32, device="cuda"),
+                        dev(r, rdt) if rdt else None, y)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.all(np.abs(got - ref) <= f16_round_bound(ref) + 1e-4 * np.abs(ref).max())
+
+
+def test_conv3d_f16_argument_rules(v):
+    import torch
+    x16 = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.float16)
+    xb = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.bfloat16)
+    w = torch.zeros((32, 3, 3, 3, 32), device="cuda", dtype=torch.bfloat16)
+    y = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.float32)
+    y16 = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.float16)
+    with pytest.raises(v.VaeError) as e:        # bf16-packed weights with an fp16 input
+        v.vae_conv3d_causal(x16, v.vae_conv_weight_pack(w).view(torch.bfloat16), None, None, y,
+                            flags=v.VAE_CONV_PACKED_WEIGHTS)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:        # fp16-packed weights with a bf16 input
+        v.vae_conv3d_causal(xb, v.vae_conv_weight_pack_f16(w).view(torch.bfloat16), None, None, y,
+                            flags=v.VAE_CONV_PACKED_F16_WEIGHTS)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:        # an fp16 output needs a bf16 input
+        v.vae_conv3d_causal(x16, w, None, None, y16)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    x20 = torch.zeros((1, 2, 4, 4, 20), device="cuda", dtype=torch.float16)
+    with pytest.raises(v.VaeError) as e:        # fp16 needs the MFMA path (Cin % 32)
+        v.vae_conv3d_causal(x20, w[..., :20].contiguous(), None, None, y)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:        # GroupNorm does not read fp16
+        v.vae_groupnorm_silu(x16, None, 8, 1e-6, None, None, True, y)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+

@@ -12,19 +12,20 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvae_mi355x.so")
 
 VAE_OK, VAE_ERR_INVALID_ARG, VAE_ERR_UNSUPPORTED, VAE_ERR_HIP, VAE_ERR_WORKSPACE = range(5)
-VAE_DTYPE_BF16, VAE_DTYPE_F32 = 1, 2
+VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DTYPE_F16 = 1, 2, 3
 VAE_UPSAMPLE_NEAREST, VAE_UPSAMPLE_D2S = 1, 2
 VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
-VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS = 1, 2
-VAE_DECODE_SPLIT_FP32_OPERANDS = 1
+VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
+VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
 VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
 
 # Every symbol include/vae.h declares.
 EXPORTS = (
     "vae_last_error", "vae_last_error_info", "vae_version", "vae_conv3d_causal",
-    "vae_conv3d_causal_fused_workspace", "vae_conv3d_causal_fused", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_decoder_packed_weight_size",
+    "vae_conv3d_causal_fused_workspace", "vae_conv3d_causal_fused", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_conv_weight_pack_f16",
+    "vae_decoder_packed_weight_size",
     "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_upsample",
@@ -110,6 +111,7 @@ def _load():
         "vae_conv3d_causal_fused": ([ctypes.POINTER(vae_conv_fused_t), P], I32),
         "vae_conv_weight_pack_size": ([I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_conv_weight_pack": ([P, I32, I32, P, P], I32),
+        "vae_conv_weight_pack_f16": ([P, I32, I32, P, P], I32),
         "vae_decoder_packed_weight_size": ([P, ctypes.POINTER(SZ)], I32),
         "vae_decoder_pack_weights": ([P, P, SZ, P], I32),
         "vae_groupnorm_silu_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
@@ -170,6 +172,8 @@ def _dtype_code(t):
         return VAE_DTYPE_BF16
     if t.dtype == torch.float32:
         return VAE_DTYPE_F32
+    if t.dtype == torch.float16:
+        return VAE_DTYPE_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -269,12 +273,21 @@ def vae_conv3d_causal_fused(x, weight, bias, residual, y, out_box=None, flags=0,
 
 def vae_conv_weight_pack(weight, stream=None):
     """Fragment-packed copy of a bf16 [Cout, 3, 3, 3, Cin] device weight (a new uint8 tensor)."""
+    return _pack(LIB.vae_conv_weight_pack, weight, stream)
+
+
+def vae_conv_weight_pack_f16(weight, stream=None):
+    """The same packed layout holding fp16(w * 2^10): the weights of an fp16-input conv."""
+    return _pack(LIB.vae_conv_weight_pack_f16, weight, stream)
+
+
+def _pack(fn, weight, stream):
     import torch
     cout, cin = weight.shape[0], weight.shape[-1]
     n = ctypes.c_size_t()
     _check(LIB.vae_conv_weight_pack_size(cout, cin, ctypes.byref(n)))
     packed = torch.empty(n.value, dtype=torch.uint8, device=weight.device)
-    _check(LIB.vae_conv_weight_pack(_ptr(weight), cout, cin, _ptr(packed), _stream(stream)))
+    _check(fn(_ptr(weight), cout, cin, _ptr(packed), _stream(stream)))
     return packed
 
 

@@ -34,7 +34,7 @@ void clear_error() {
 // ------------------------------------------------------------------------------------------------
 vae_status_t check_tensor(const vae_tensor_t* t, const char* name) {
     if (!t) return fail(VAE_ERR_INVALID_ARG, std::string(name) + " is NULL");
-    if (t->dtype != VAE_DTYPE_BF16 && t->dtype != VAE_DTYPE_F32)
+    if (t->dtype != VAE_DTYPE_BF16 && t->dtype != VAE_DTYPE_F32 && t->dtype != VAE_DTYPE_F16)
         return fail(VAE_ERR_INVALID_ARG, std::string(name) + ": unknown dtype");
     const int64_t d[5] = {t->n, t->t, t->h, t->w, t->c};
     for (int i = 0; i < 5; ++i)
@@ -96,6 +96,8 @@ vae_status_t box_list(const vae_tensor_t& x, const vae_box_t* boxes, int32_t n_b
 
 vae_status_t check_gn(const vae_tensor_t* x, int32_t groups) {
     VAE_TRY(check_tensor(x, "x"));
+    if (x->dtype == VAE_DTYPE_F16)
+        return fail(VAE_ERR_UNSUPPORTED, "group norm reads bf16 or fp32 (fp16 is an output only)");
     if (groups < 1 || x->c % groups != 0)
         return fail(VAE_ERR_UNSUPPORTED, "channels must be divisible by groups", 4, x->c, groups);
     if (!gn_shape_supported(*x, groups))
@@ -216,11 +218,52 @@ std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
     return tiles;
 }
 
+// The residual has y's shape, and y's dtype or fp32 when y is bf16 or fp16.
+vae_status_t check_residual(const vae_tensor_t* r, const vae_tensor_t& x, const vae_tensor_t& y) {
+    VAE_TRY(check_tensor(r, "residual"));
+    const bool dtype_ok =
+        r->dtype == y.dtype || (r->dtype == VAE_DTYPE_F32 && y.dtype != VAE_DTYPE_F32);
+    if (!same_grid(*r, y) || r->c != y.c || !dtype_ok)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "residual must match y in shape, and in dtype or be fp32 (bf16/fp16 y)");
+    if (overlaps(*r, x)) return fail(VAE_ERR_INVALID_ARG, "residual overlaps x");
+    return VAE_OK;
+}
+
+// fp16 tensors and the packed-weight flags (shared by both conv calls).
+vae_status_t check_conv_dtypes(const vae_tensor_t& x, const vae_tensor_t& y,
+                               const vae_tensor_t* residual, int64_t cout, int32_t weight_dtype,
+                               int32_t flags) {
+    const int32_t packs = VAE_CONV_PACKED_WEIGHTS | VAE_CONV_PACKED_F16_WEIGHTS;
+    if (flags & ~(VAE_CONV_SPLIT_FP32 | packs))
+        return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
+    if ((flags & packs) == packs)
+        return fail(VAE_ERR_INVALID_ARG, "give one packed-weight flag");
+    const bool mfma = conv_uses_mfma_c(x, cout, weight_dtype);
+    if (x.dtype == VAE_DTYPE_F16 || y.dtype == VAE_DTYPE_F16) {
+        if (!mfma)
+            return fail(VAE_ERR_UNSUPPORTED,
+                        "fp16 tensors need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x.c,
+                        32);
+        if (y.dtype == VAE_DTYPE_F16 && x.dtype != VAE_DTYPE_BF16)
+            return fail(VAE_ERR_UNSUPPORTED, "an fp16 y needs a bf16 x");
+    }
+    if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && x.dtype != VAE_DTYPE_F16)
+        return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 x");
+    if ((flags & VAE_CONV_PACKED_WEIGHTS) && x.dtype == VAE_DTYPE_F16)
+        return fail(VAE_ERR_INVALID_ARG, "an fp16 x takes fp16-packed weights");
+    if ((flags & packs) && !mfma)
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x.c,
+                    32);
+    if (residual && residual->dtype != y.dtype && !mfma)
+        return fail(VAE_ERR_UNSUPPORTED, "an fp32 residual with a bf16 y needs the MFMA path");
+    return VAE_OK;
+}
+
 vae_status_t check_conv(const vae_tensor_t* x, const void* weight, int32_t weight_dtype,
                         const vae_tensor_t* residual, vae_tensor_t* y, const vae_box_t* out_box,
                         int32_t flags) {
-    if (flags & ~(VAE_CONV_SPLIT_FP32 | VAE_CONV_PACKED_WEIGHTS))
-        return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
     VAE_TRY(check_tensor(x, "x"));
     VAE_TRY(check_tensor(y, "y"));
     if (!weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
@@ -229,18 +272,10 @@ vae_status_t check_conv(const vae_tensor_t* x, const void* weight, int32_t weigh
     if (reinterpret_cast<uintptr_t>(weight) % 16 != 0)
         return fail(VAE_ERR_INVALID_ARG, "weight must be 16-byte aligned");
     if (!same_grid(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "x and y must share N, T, H, W");
-    if (residual) {
-        VAE_TRY(check_tensor(residual, "residual"));
-        if (!same_grid(*residual, *y) || residual->c != y->c || residual->dtype != y->dtype)
-            return fail(VAE_ERR_INVALID_ARG, "residual must match y in shape and dtype");
-        if (overlaps(*residual, *x)) return fail(VAE_ERR_INVALID_ARG, "residual overlaps x");
-    }
+    if (residual) VAE_TRY(check_residual(residual, *x, *y));
     if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
     VAE_TRY(check_box(out_box, *y, "out_box"));
-    if ((flags & VAE_CONV_PACKED_WEIGHTS) && !conv_uses_mfma(*x, *y, weight_dtype))
-        return fail(VAE_ERR_UNSUPPORTED,
-                    "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x->c,
-                    32);
+    VAE_TRY(check_conv_dtypes(*x, *y, residual, y->c, weight_dtype, flags));
     return VAE_OK;
 }
 
@@ -254,8 +289,6 @@ struct FusedPlan {
 // `run`: the call itself (the workspace query needs no output pointers).
 vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
     if (!a) return fail(VAE_ERR_INVALID_ARG, "args is NULL");
-    if (a->flags & ~(VAE_CONV_SPLIT_FP32 | VAE_CONV_PACKED_WEIGHTS))
-        return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
     VAE_TRY(check_tensor(a->x, "x"));
     VAE_TRY(check_tensor(a->y, "y"));
     const vae_tensor_t& x = *a->x;
@@ -276,13 +309,7 @@ vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
         y.w != p->sw * x.w)
         return fail(VAE_ERR_INVALID_ARG,
                     "y must be [N, st*T-(st-1), sh*H, sw*W, Cout/(st*sh*sw)] of x's [N, T, H, W]");
-    if (a->residual) {
-        VAE_TRY(check_tensor(a->residual, "residual"));
-        const vae_tensor_t& r = *a->residual;
-        if (!same_grid(r, y) || r.c != y.c || r.dtype != y.dtype)
-            return fail(VAE_ERR_INVALID_ARG, "residual must match y in shape and dtype");
-        if (overlaps(r, x)) return fail(VAE_ERR_INVALID_ARG, "residual overlaps x");
-    }
+    if (a->residual) VAE_TRY(check_residual(a->residual, x, y));
     if (overlaps(x, y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
     VAE_TRY(check_box(a->out_box, x, "out_box"));
     p->cbox = to_box(a->out_box, x);
@@ -290,15 +317,14 @@ vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
     p->ybox = Box{std::max(0, p->st * b.t0 - (p->st - 1)), p->st * b.t1 - (p->st - 1),
                   p->sh * b.h0, p->sh * b.h1, p->sw * b.w0, p->sw * b.w1};
     const bool mfma = conv_uses_mfma_c(x, y.c * p->k, a->weight_dtype);
-    if ((a->flags & VAE_CONV_PACKED_WEIGHTS) && !mfma)
-        return fail(VAE_ERR_UNSUPPORTED,
-                    "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x.c,
-                    32);
+    VAE_TRY(check_conv_dtypes(x, y, a->residual, y.c * p->k, a->weight_dtype, a->flags));
     if (p->k > 1 && !mfma)
         return fail(VAE_ERR_UNSUPPORTED,
                     "a fused depth-to-space needs bf16 weights, Cin % 32 == 0 and Cout % 4 == 0",
                     4, x.c, 32);
     if (a->gn_groups) {
+        if (y.dtype == VAE_DTYPE_F16)
+            return fail(VAE_ERR_UNSUPPORTED, "statistics of an fp16 y are not gathered");
         VAE_TRY(check_gn(a->y, a->gn_groups));
         if (!(a->gn_eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "gn_eps must be >= 0");
         if (run && !a->gn_mean_rstd) return fail(VAE_ERR_INVALID_ARG, "gn_mean_rstd is NULL");
@@ -408,6 +434,17 @@ VAE_API vae_status_t vae_conv_weight_pack(const void* weight, int32_t cout, int3
     if (reinterpret_cast<uintptr_t>(packed) % 16 != 0)
         return fail(VAE_ERR_INVALID_ARG, "packed must be 16-byte aligned");
     return launch_pack_weights(weight, cout, cin, packed, as_stream(stream));
+}
+
+VAE_API vae_status_t vae_conv_weight_pack_f16(const void* weight, int32_t cout, int32_t cin,
+                                              void* packed, vae_stream_t stream) {
+    clear_error();
+    if (!weight || !packed) return fail(VAE_ERR_INVALID_ARG, "weight or packed is NULL");
+    if (cout < 1 || cin < 1) return fail(VAE_ERR_INVALID_ARG, "cout and cin must be >= 1");
+    if (cin % 32) return fail(VAE_ERR_UNSUPPORTED, "packing needs Cin % 32 == 0", 4, cin, 32);
+    if (reinterpret_cast<uintptr_t>(packed) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+    return launch_pack_weights(weight, cout, cin, packed, as_stream(stream), true);
 }
 
 VAE_API vae_status_t vae_groupnorm_stats_workspace(const vae_tensor_t* x, const vae_box_t* boxes,

@@ -32,6 +32,12 @@ template <> struct Elem<uint16_t> {
     static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16(v); }
     static constexpr int kVec = 8;  // elements per 16-byte vector
 };
+// IEEE binary16 storage (the fp16 operand hand-off). Conversions round to nearest even.
+template <> struct Elem<_Float16> {
+    static __device__ __forceinline__ float load(const _Float16* p) { return (float)*p; }
+    static __device__ __forceinline__ void store(_Float16* p, float v) { *p = (_Float16)v; }
+    static constexpr int kVec = 8;
+};
 template <> struct Elem<float> {
     static __device__ __forceinline__ float load(const float* p) { return *p; }
     static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
@@ -81,7 +87,7 @@ inline Box whole_box(const vae_tensor_t& x) {
 inline Box to_box(const vae_box_t* b, const vae_tensor_t& x) {
     return b ? Box{b->t0, b->t1, b->h0, b->h1, b->w0, b->w1} : whole_box(x);
 }
-inline int64_t elem_size(int32_t dtype) { return dtype == VAE_DTYPE_BF16 ? 2 : 4; }
+inline int64_t elem_size(int32_t dtype) { return dtype == VAE_DTYPE_F32 ? 4 : 2; }
 inline int64_t positions(const vae_tensor_t& x) { return x.n * x.t * x.h * x.w; }
 inline int64_t numel(const vae_tensor_t& x) { return positions(x) * x.c; }
 

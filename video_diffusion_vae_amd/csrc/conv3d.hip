@@ -1,6 +1,7 @@
 // Causal Conv3d (3x3x3, stride 1) on channels-last (NDHWC) activations: dispatch, weight packing
 // and the direct path.
-//  - bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (conv3d_mfma.h).
+//  - bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (conv3d_mfma.h);
+//    fp16 inputs only run there.
 //  - Otherwise a direct kernel computes one output per thread with fp32 accumulation.
 #include "conv3d_mfma.h"
 
@@ -17,6 +18,8 @@ VAE_MFMA_EXTERN(128, float, true)
 VAE_MFMA_EXTERN(64, uint16_t, false)
 VAE_MFMA_EXTERN(64, float, false)
 VAE_MFMA_EXTERN(64, float, true)
+VAE_MFMA_EXTERN(128, _Float16, false)
+VAE_MFMA_EXTERN(64, _Float16, false)
 #undef VAE_MFMA_EXTERN
 }  // namespace mfma
 
@@ -74,6 +77,9 @@ vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias
     if (x.dtype == VAE_DTYPE_BF16)
         return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, fz,
                                                  stream);
+    if (x.dtype == VAE_DTYPE_F16)
+        return run_mfma_out<NT, _Float16, false>(x, w, bias, residual, y, box, packed, fz,
+                                                 stream);
     if (split)
         return run_mfma_out<NT, float, true>(x, w, bias, residual, y, box, packed, fz, stream);
     return run_mfma_out<NT, float, false>(x, w, bias, residual, y, box, packed, fz, stream);
@@ -83,10 +89,11 @@ vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias
 // Cout padded to a multiple of 32 with zeros. One 32 (co) x 32 (ci) block per (tap, chunk) is
 // 2 KB, ordered so that the 16-byte B fragment of lane l (column l % 32, k half l / 32) for
 // k step kk sits at byte kk * 1024 + (l % 32) * 32 + (l / 32) * 16: one contiguous 1 KB read per
-// fragment.
+// fragment. With to_f16 each weight is stored as fp16(w * 2^10) instead (exact for |w| < 64).
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w,
                                                            uint16_t* __restrict__ p, int32_t cout,
-                                                           int32_t cin, int64_t total) {
+                                                           int32_t cin, int64_t total,
+                                                           int32_t to_f16) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     const int nch = cin / kCK;
@@ -105,7 +112,8 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
     const int cot = (int)(q / 27);
     const int co = cot * 32 + r;
     const int ci = chunk * kCK + kk * 16 + khalf * 8 + e;
-    p[i] = co < cout ? w[((int64_t)co * 27 + tap) * cin + ci] : (uint16_t)0;
+    const uint16_t b = co < cout ? w[((int64_t)co * 27 + tap) * cin + ci] : (uint16_t)0;
+    p[i] = to_f16 ? f16_bits(bf16_to_f32(b) * kF16WeightScale) : b;
 }
 
 template <typename TX, typename TW, typename TO>
@@ -162,11 +170,11 @@ int64_t packed_weight_elems(int64_t cout, int64_t cin) {
 }
 
 vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool to_f16) {
     const int64_t total = packed_weight_elems(cout, cin);
     hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
                        stream, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(packed),
-                       cout, cin, total);
+                       cout, cin, total, (int32_t)to_f16);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
@@ -181,9 +189,16 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
     const bool xf = x.dtype == VAE_DTYPE_F32;
     const bool split = (flags & VAE_CONV_SPLIT_FP32) != 0;
-    const bool packed = (flags & VAE_CONV_PACKED_WEIGHTS) != 0;
+    const bool packed = (flags & (VAE_CONV_PACKED_WEIGHTS | VAE_CONV_PACKED_F16_WEIGHTS)) != 0;
+    const bool x16 = x.dtype == VAE_DTYPE_F16;
+    if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && !x16)
+        return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 input");
+    if ((flags & VAE_CONV_PACKED_WEIGHTS) && x16)
+        return fail(VAE_ERR_INVALID_ARG, "an fp16 input takes fp16-packed weights");
     const int32_t k = fz ? fz->st * fz->sh * fz->sw : 1;
     const int64_t cout = y.c * k;
+    if ((x16 || y.dtype == VAE_DTYPE_F16) && !conv_uses_mfma_c(x, cout, weight_dtype))
+        return fail(VAE_ERR_UNSUPPORTED, "conv3d: fp16 tensors need the MFMA path");
     if (fz && k > 1 && !conv_uses_mfma_c(x, cout, weight_dtype))
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: a fused depth-to-space needs the MFMA path");
     if (fz && fz->gn_ws && conv_gn_slots(x, y.c, weight_dtype, box, fz->groups, k) == 0)

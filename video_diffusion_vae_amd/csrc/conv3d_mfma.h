@@ -1,5 +1,5 @@
-// Causal Conv3d on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16): the kernel and its launch
-// templates. Each (NT, input type, split) combination is instantiated in a source file of its
+// Causal Conv3d on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, or _f16 for fp16 inputs):
+// the kernel and its launch templates. Each (NT, input type, split) combination is instantiated in a source file of its
 // own (conv3d_mfma_*.hip), so that they compile in parallel.
 //
 // Implicit GEMM:
@@ -29,6 +29,12 @@
 //    their hi halves in the first 32 bytes and their lo halves in the next 32. The two k steps of
 //    a tap read hi and lo against the same weight fragment. Each fp32 value is loaded once, and
 //    the weight loads per MFMA halve.
+//  - fp16 inputs (the operand hand-off of convs that read an fp32 stream) stage as they are and
+//    run v_mfma_f32_32x32x16_f16 at the bf16 rate: 11 significant bits of x reach the matrix
+//    cores, against 8 for bf16 and 16 for the split at twice the work. The bf16 weights become
+//    fp16 exactly after a 2^10 scale (packed that way ahead of time, or converted as each
+//    fragment is used with the standard layout); the sums are scaled back by 2^-10 before the
+//    epilogue, which is exact.
 //  - Epilogue. Where a wave's 32 channels are 32 consecutive channels of y (Cout and y's channel
 //    count multiples of 32), each lane stores its accumulator registers directly: one channel at
 //    16 positions, two runs of 32 channels per store instruction. Otherwise each wave parks one
@@ -48,7 +54,41 @@ namespace vae {
 namespace mfma {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// fp16 weight operands are the bf16 weights times 2^10 (exact for |w| < 64); the fp32 sums are
+// multiplied by 2^-10 before the epilogue.
+constexpr float kF16WeightScale = 1024.0f;
+constexpr float kF16WeightUnscale = 1.0f / 1024.0f;
+
+__host__ __device__ inline uint16_t f16_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// 8 bf16 weights (one B fragment of the standard layout) as 8 scaled fp16 weights.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8_scaled(const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(w[i] << 16) * kF16WeightScale;
+        const float hi = __uint_as_float(w[i] & 0xffff0000u) * kF16WeightScale;
+        o[i] = (uint32_t)f16_bits(lo) | ((uint32_t)f16_bits(hi) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// One 32x32x16 MFMA step; a and b carry 8 bf16 or 8 fp16 values.
+template <bool F16>
+__device__ __forceinline__ f32x16_t mfma_step(const bf16x8_t& a, const bf16x8_t& b,
+                                              const f32x16_t& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 constexpr int kCK = 32;                              // input channels per LDS chunk
 constexpr int kRow = kCK * 2 + 16;                   // padded LDS row, bytes
@@ -71,7 +111,7 @@ struct MfmaArgs {
     // (st*t + dt - (st-1), sh*h + dh, sw*w + dw); frames below 0 are dropped. Identity:
     // st = sh = sw = 1 and zc = cout. The residual, if any, has y's shape.
     int32_t yT, yH, yW, zc, st, sh, sw;
-    int32_t res_f32;         // the residual is fp32 while y is bf16 (a stream handed on in bf16)
+    int32_t res_f32;         // the residual is fp32 while y is bf16 or fp16 (a hand-off)
     // Optional GroupNorm partials of y as stored: fp64 (count, mean, M2) per (sample, group of
     // y's channels, slot), slot = (sub-position * position blocks + block) * WM + wave row.
     double* stats;
@@ -88,6 +128,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // 8 input channels starting at p, as 8 bf16 in one 16-byte word.
 template <typename TI> __device__ __forceinline__ uint4 load8(const TI* p);
 template <> __device__ __forceinline__ uint4 load8<uint16_t>(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+template <> __device__ __forceinline__ uint4 load8<_Float16>(const _Float16* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 template <> __device__ __forceinline__ uint4 load8<float>(const float* p) {
@@ -135,6 +178,10 @@ template <> __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, f
     v[0] = bf16_to_f32((uint16_t)(a.x & 0xffff)); v[1] = bf16_to_f32((uint16_t)(a.x >> 16));
     v[2] = bf16_to_f32((uint16_t)(a.y & 0xffff)); v[3] = bf16_to_f32((uint16_t)(a.y >> 16));
 }
+template <> __device__ __forceinline__ void load4<_Float16>(const _Float16* p, float* v) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (float)p[k];
+}
 template <typename TO> __device__ __forceinline__ void store4(TO* p, const float* v);
 template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -146,11 +193,21 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const 
     *reinterpret_cast<uint2*>(p) = a;
 }
 
+template <> __device__ __forceinline__ void store4<_Float16>(_Float16* p, const float* v) {
+    uint2 a;
+    a.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
+    a.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = a;
+}
+
 // The value an output element holds once stored.
 template <typename TO> __device__ __forceinline__ float stored(float v);
 template <> __device__ __forceinline__ float stored<float>(float v) { return v; }
 template <> __device__ __forceinline__ float stored<uint16_t>(float v) {
     return bf16_to_f32(f32_to_bf16(v));
+}
+template <> __device__ __forceinline__ float stored<_Float16>(float v) {
+    return (float)(_Float16)v;
 }
 
 // Chan's pairwise update of (count, mean, M2) with another partial, in fp32.
@@ -522,6 +579,8 @@ template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int
 __global__ __launch_bounds__(kMfmaThreads, 2)
 void conv3d_mfma_kernel(MfmaArgs a) {
     using S = BlockShape<TB, HB, WB>;
+    constexpr bool F16 = std::is_same<TI, _Float16>::value;   // fp16 operands
+    static_assert(!(F16 && SPLIT), "fp16 inputs are not split");
     constexpr int HH = S::HH, HW = S::HW;
     constexpr int RP = S::kPitch;
     // With packed weights and bf16 (or split) operands the tile is staged through a ring of frame
@@ -594,6 +653,12 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     // Weight fragments per tap: one per k step, or one for both (hi and lo) with the split.
     constexpr int KB = SPLIT ? 1 : 2;
     uint4 bq[NB][KB];
+    // The B operand as the MFMA takes it: packed fp16 weights are used as loaded; standard-layout
+    // bf16 weights become scaled fp16 here, after their load has landed.
+    auto b_operand = [&](const uint4& q) -> bf16x8_t {
+        if constexpr (F16 && !PACKED) return __builtin_bit_cast(bf16x8_t, bf16x8_to_f16x8_scaled(q));
+        else return __builtin_bit_cast(bf16x8_t, q);
+    };
     auto load_b = [&](int buf, int tap, int c0) {
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
@@ -754,11 +819,9 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                         af[(step + 1) & 1][i] =
                             *reinterpret_cast<const bf16x8_t*>(&halo[abase[i] + off]);
                 }
-                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
+                const bf16x8_t bf = b_operand(bq[tap % NB][SPLIT ? 0 : kk]);
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf,
-                                                                     acc[i], 0, 0, 0);
+                for (int i = 0; i < MI; ++i) acc[i] = mfma_step<F16>(af[step & 1][i], bf, acc[i]);
                 constexpr int n_ld = (ldk >= 0) + (hld >= 0);
                 constexpr int n_wr = (wrk >= 0) + (step == 0 ? NHOLD : 0);
                 if constexpr (ldb) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
@@ -827,11 +890,9 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                         af[(step + 1) & 1][i] =
                             *reinterpret_cast<const bf16x8_t*>(&halo[a_off[i] + off]);
                 }
-                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bq[tap % NB][SPLIT ? 0 : kk]);
+                const bf16x8_t bf = b_operand(bq[tap % NB][SPLIT ? 0 : kk]);
     #pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[step & 1][i], bf, acc[i], 0,
-                                                                     0, 0);
+                for (int i = 0; i < MI; ++i) acc[i] = mfma_step<F16>(af[step & 1][i], bf, acc[i]);
                 // Each k step is its own scheduling island: the weight loads first, then the MFMAs
                 // alternating with the next step's LDS reads, so that neither waits on the other.
                 if (kk == 0 && tap + PD < 27) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
@@ -843,6 +904,12 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    }
+    if constexpr (F16) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] *= kF16WeightUnscale;
     }
     if (a.zc % 32 == 0 && a.cout % 32 == 0) {
         conv_epilogue_direct<TO, TB, HB, WB, MI, MW, WM>(a, acc, n, t_blk, h_blk, w_blk, bt_i, bh_i,
@@ -950,6 +1017,14 @@ vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bia
                           bool packed, const ConvFuse* fz, hipStream_t stream) {
     if (y.dtype == VAE_DTYPE_F32)
         return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
+    if (y.dtype == VAE_DTYPE_F16) {
+        // fp16 outputs are the operand hand-off of a bf16-input conv
+        if constexpr (std::is_same<TI, uint16_t>::value)
+            return run_mfma<NT, TI, _Float16, SPLIT>(x, w, bias, residual, y, box, packed, fz,
+                                                     stream);
+        else
+            return fail(VAE_ERR_UNSUPPORTED, "conv3d: an fp16 output needs a bf16 input");
+    }
     return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
 }
 

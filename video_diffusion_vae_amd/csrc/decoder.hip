@@ -47,10 +47,29 @@ bool conv_splits(int32_t flags, const vae_layer_desc_t* layers, int n, int i) {
            layers[i].op == VAE_OP_CONV && !layers[i].no_split;
 }
 
-// Output dtype of the standalone GN_SILU at layer i: the activation dtype when the next layer is
-// a conv that splits its fp32 input, else the conv operand dtype.
+// Whether layer i is a conv that takes fp16 operands (VAE_DECODE_F16_OPERANDS): a CONV on the
+// matrix cores right after a RES whose convs also run there, or after a GN_SILU, in a plan that
+// keeps fp32 activations (a bf16 stream has nothing finer to hand on). Its producer stores fp16.
+bool conv_f16(int32_t dtype, int32_t act_dtype, int32_t flags, const vae_layer_desc_t* layers,
+              int n, int i) {
+    if (!(flags & VAE_DECODE_F16_OPERANDS) || dtype != VAE_DTYPE_BF16 ||
+        act_dtype != VAE_DTYPE_F32 || i < 1 || i >= n)
+        return false;
+    const vae_layer_desc_t& l = layers[i];
+    const vae_layer_desc_t& prev = layers[i - 1];
+    if (l.op != VAE_OP_CONV || l.cin % 32 || l.cout % 4) return false;
+    return (prev.op == VAE_OP_RES && prev.cin % 32 == 0) || prev.op == VAE_OP_GN_SILU;
+}
+bool conv_f16(const vae_decoder& d, int i) {
+    return conv_f16(d.dtype, d.act_dtype, d.flags, d.layers.data(), (int)d.layers.size(), i);
+}
+
+// Output dtype of the standalone GN_SILU at layer i: fp16 when the next layer is a conv with
+// fp16 operands, the activation dtype when it is a conv that splits its fp32 input, else the conv
+// operand dtype.
 int32_t gn_silu_dtype(int32_t dtype, int32_t act_dtype, int32_t flags,
                       const vae_layer_desc_t* layers, int n, int i) {
+    if (conv_f16(dtype, act_dtype, flags, layers, n, i + 1)) return VAE_DTYPE_F16;
     return conv_splits(flags, layers, n, i + 1) ? act_dtype : dtype;
 }
 int32_t gn_silu_dtype(const vae_decoder& d, int i) {
@@ -60,7 +79,10 @@ int32_t gn_silu_dtype(const vae_decoder& d, int i) {
 // Storage dtype of a residual block's output (layer i). When the next layer is a conv that rounds
 // its input to the bf16 operand dtype anyway (bf16 weights on the matrix cores, no split), the
 // block stores bf16 directly: the same rounding, done once at the store, with half the bytes.
+// With fp16 operands for the next conv, the block stores fp16 (the one rounding that conv's
+// operand gets).
 int32_t res_out_dtype(const vae_decoder& d, size_t i) {
+    if (conv_f16(d, (int)i + 1)) return VAE_DTYPE_F16;
     if (i + 1 < d.layers.size() && d.dtype == VAE_DTYPE_BF16 && d.layers[i].cin % 32 == 0) {
         const vae_layer_desc_t& n = d.layers[i + 1];
         if (n.op == VAE_OP_CONV && !conv_splits(d.flags, d.layers.data(), (int)d.layers.size(),
@@ -290,8 +312,9 @@ struct Runner {
                          : 0;
         const void* w = d->ptrs[wi];
         if (d->packed[wi]) {
+            // convs with fp16 operands were packed as fp16 (see vae_decoder_pack_weights)
             w = d->packed[wi];
-            cf |= VAE_CONV_PACKED_WEIGHTS;
+            cf |= x.dtype == VAE_DTYPE_F16 ? VAE_CONV_PACKED_F16_WEIGHTS : VAE_CONV_PACKED_WEIGHTS;
         }
         const int32_t k = up ? up->st * up->sh * up->sw : 1;
         const int64_t cout = y.c * k;
@@ -454,15 +477,16 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
     return VAE_OK;
 }
 
-// Visit every conv of the plan: fn(ptr index of its weight, cin, cout).
+// Visit every conv of the plan: fn(ptr index of its weight, cin, cout, fp16 operands).
 template <typename F>
 void for_each_conv(const vae_decoder& d, F fn) {
     size_t p = 0;
-    for (const vae_layer_desc_t& l : d.layers) {
-        if (l.op == VAE_OP_CONV) fn(p, l.cin, l.cout);
+    for (size_t i = 0; i < d.layers.size(); ++i) {
+        const vae_layer_desc_t& l = d.layers[i];
+        if (l.op == VAE_OP_CONV) fn(p, l.cin, l.cout, conv_f16(d, (int)i));
         if (l.op == VAE_OP_RES) {
-            fn(p + 2, l.cin, l.cin);
-            fn(p + 6, l.cin, l.cin);
+            fn(p + 2, l.cin, l.cin, false);
+            fn(p + 6, l.cin, l.cin, false);
         }
         p += ptrs_for(l);
     }
@@ -492,8 +516,10 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
         return fail(VAE_ERR_INVALID_ARG, "unknown activation dtype");
     if (spec->dtype == VAE_DTYPE_F32 && spec->act_dtype != VAE_DTYPE_F32)
         return fail(VAE_ERR_UNSUPPORTED, "an fp32 plan keeps fp32 activations");
-    if (spec->flags & ~VAE_DECODE_SPLIT_FP32_OPERANDS)
+    if (spec->flags & ~(VAE_DECODE_SPLIT_FP32_OPERANDS | VAE_DECODE_F16_OPERANDS))
         return fail(VAE_ERR_INVALID_ARG, "unknown decoder flags");
+    if ((spec->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) && (spec->flags & VAE_DECODE_F16_OPERANDS))
+        return fail(VAE_ERR_INVALID_ARG, "give one of the split and fp16 operand flags");
     if (spec->latent_channels < 1 || spec->groups < 1 || !(spec->eps >= 0.0f))
         return fail(VAE_ERR_INVALID_ARG, "latent_channels and groups must be >= 1, eps >= 0");
     if (spec->n_layers < 1 || !spec->layers) return fail(VAE_ERR_INVALID_ARG, "empty layer plan");
@@ -581,7 +607,7 @@ VAE_API vae_status_t vae_decoder_packed_weight_size(const vae_decoder_t* dec, si
     clear_error();
     if (!dec || !bytes) return fail(VAE_ERR_INVALID_ARG, "NULL argument");
     size_t total = 0;
-    for_each_conv(*dec, [&](size_t, int32_t cin, int32_t cout) {
+    for_each_conv(*dec, [&](size_t, int32_t cin, int32_t cout, bool) {
         if (packable(*dec, cin, cout)) total += align_up((size_t)packed_weight_elems(cout, cin) * 2, 256);
     });
     *bytes = total;
@@ -602,9 +628,9 @@ VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, siz
     uint8_t* out = static_cast<uint8_t*>(buf);
     vae_status_t st = VAE_OK;
     std::vector<const void*> packed(dec->ptrs.size(), nullptr);
-    for_each_conv(*dec, [&](size_t wi, int32_t cin, int32_t cout) {
+    for_each_conv(*dec, [&](size_t wi, int32_t cin, int32_t cout, bool f16) {
         if (st != VAE_OK || !packable(*dec, cin, cout)) return;
-        st = launch_pack_weights(dec->ptrs[wi], cout, cin, out, as_stream(stream));
+        st = launch_pack_weights(dec->ptrs[wi], cout, cin, out, as_stream(stream), f16);
         packed[wi] = out;
         out += align_up((size_t)packed_weight_elems(cout, cin) * 2, 256);
     });

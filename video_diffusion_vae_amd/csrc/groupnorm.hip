@@ -432,7 +432,13 @@ vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t grou
                              bool silu, const vae_tensor_t& y, hipStream_t stream) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
     const bool xb = x.dtype == VAE_DTYPE_BF16, yb = y.dtype == VAE_DTYPE_BF16;
-    if (xb && yb)
+    if (y.dtype == VAE_DTYPE_F16) {   // the fp16 operand of the next conv
+        if (xb)
+            apply_launch<uint16_t, _Float16>(x, box, groups, mean_rstd, gamma, beta, silu, y,
+                                             stream);
+        else
+            apply_launch<float, _Float16>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
+    } else if (xb && yb)
         apply_launch<uint16_t, uint16_t>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
     else if (xb)
         apply_launch<uint16_t, float>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);

@@ -37,8 +37,9 @@ int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, c
                       int32_t groups, int32_t k);
 // Fragment-packed bf16 weights (see conv3d.hip): element count and the packing kernel.
 int64_t packed_weight_elems(int64_t cout, int64_t cin);
+// to_f16: fp16(w * 2^10), the weight operand of fp16 inputs.
 vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool to_f16 = false);
 
 // ---- group norm ----
 // Workspace: per-block partials of every box, fp64 [blocks][N][G][3].

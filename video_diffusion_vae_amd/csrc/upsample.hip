@@ -76,7 +76,8 @@ vae_status_t run(const vae_tensor_t& x, const Box& b, int32_t mode, int32_t st, 
 vae_status_t launch_upsample(const vae_tensor_t& x, const Box& box, int32_t mode, int32_t st,
                              int32_t sh, int32_t sw, const vae_tensor_t& y, hipStream_t stream) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
-    if (x.dtype == VAE_DTYPE_BF16) return run<uint16_t>(x, box, mode, st, sh, sw, y, stream);
+    // a copy: bf16 and fp16 move as 16-bit words
+    if (x.dtype != VAE_DTYPE_F32) return run<uint16_t>(x, box, mode, st, sh, sw, y, stream);
     return run<float>(x, box, mode, st, sh, sw, y, stream);
 }
 

@@ -9,7 +9,13 @@ from __future__ import annotations
 
 import numpy as np
 
-from ._binding import Decoder, VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DECODE_SPLIT_FP32_OPERANDS
+from ._binding import (Decoder, VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DECODE_F16_OPERANDS,
+                       VAE_DECODE_SPLIT_FP32_OPERANDS)
+
+# How convs that read an fp32 activation (the upsampling convs, conv_out) get their operands:
+# "f16" (one rounding to fp16, bf16 rate), "split" (bf16 hi + lo, twice the work) or "bf16".
+OPERAND_FLAGS = {"f16": VAE_DECODE_F16_OPERANDS, "split": VAE_DECODE_SPLIT_FP32_OPERANDS,
+                 "bf16": 0}
 
 
 def conv_weight_layout(w, dtype, device):
@@ -20,14 +26,14 @@ def conv_weight_layout(w, dtype, device):
     return t.to(device=device, dtype=dtype)
 
 
-def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", split=True,
+def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", operands="f16",
                    packed=True):
     """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
 
     Each parameter dict is {"kind": "conv", "w", "b"} or {"kind": "gn", "gamma", "beta"} holding
     host arrays. ``act_dtype`` is the storage dtype of the activations between ops ("f32" or
-    "bf16"). ``split`` applies fp32 conv inputs as hi + lo bf16 operands
-    (VAE_DECODE_SPLIT_FP32_OPERANDS). ``packed`` gives the MFMA convs fragment-packed weight
+    "bf16"). ``operands`` picks how convs that read an fp32 activation get their operands
+    (OPERAND_FLAGS; bf16 plans only). ``packed`` gives the MFMA convs fragment-packed weight
     copies. Returns the Decoder; it keeps the device tensors alive.
     """
     import torch
@@ -42,7 +48,7 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", spl
             flat.append(torch.as_tensor(np.asarray(p["beta"], np.float32)).to(device))
     code = VAE_DTYPE_BF16 if spec["dtype"] == "bf16" else VAE_DTYPE_F32
     act = VAE_DTYPE_BF16 if act_dtype == "bf16" else VAE_DTYPE_F32
-    flags = VAE_DECODE_SPLIT_FP32_OPERANDS if (split and code == VAE_DTYPE_BF16) else 0
+    flags = OPERAND_FLAGS[operands] if code == VAE_DTYPE_BF16 else 0
     dec = Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat,
                   act_dtype=act, flags=flags)
     if packed:
