@@ -96,6 +96,10 @@ class vae_op_timing_t(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python video_diffusion_vae_amd/build.py`")
+    # torch first: it loads the HIP runtime that owns the device memory and streams handed to the
+    # library, and the library then binds to that same runtime (one libamdhip64 per process).
+    # Loaded the other way round, the device was not found on the GPU host.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     T = ctypes.POINTER(vae_tensor_t)
