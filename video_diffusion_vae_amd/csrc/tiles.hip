@@ -7,6 +7,8 @@
 //  - each kernel evaluates the separable ramps from the tile's overlaps while it streams;
 //  - the final divide evaluates the per-axis weight sums from the tile grid itself.
 // All passes go over contiguous rows (fixed n, t, h) of fp32 NDHWC data.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace vae {
@@ -50,6 +52,95 @@ __global__ __launch_bounds__(kThreads) void merge_finalize_kernel(float* __restr
     }
 }
 
+// The same two passes, each block streaming several rows. The per-column factor (the W ramp of
+// the tile, or the W weight sum of the output) is evaluated once per block into LDS instead of
+// once per element. With VEC, rows are read and written as float4: every row starts on a
+// 16-byte boundary, and element 4e + k lies in column (4e + k) / C. The arithmetic per element
+// is that of the kernels above.
+constexpr int kRowBlocks = 4096;           // at most this many blocks per sample
+constexpr int kMaxLdsColumns = 8192;       // per-column factors kept in LDS (32 KB)
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void merge_rows_kernel(const float* __restrict__ tile,
+                                                              float* __restrict__ out, int32_t oT,
+                                                              int32_t oH, int32_t oW, int32_t C,
+                                                              Box b, int32_t lead_h,
+                                                              int32_t trail_h, int32_t lead_w,
+                                                              int32_t trail_w) {
+    extern __shared__ float col[];          // ramp_w of each tile column
+    const int bw = (int)b.bw(), bh = (int)b.bh();
+    for (int i = threadIdx.x; i < bw; i += kThreads) col[i] = ramp_weight(i, bw, lead_w, trail_w);
+    __syncthreads();
+    const int n = blockIdx.y;
+    const int64_t rows = b.bt() * bh;
+    const int seg = bw * C;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const int tl = (int)(r / bh), hl = (int)(r % bh);
+        const float wh = ramp_weight(hl, bh, lead_h, trail_h);
+        const float* src = tile + (((int64_t)n * b.bt() + tl) * bh + hl) * (int64_t)seg;
+        float* dst = out + ((((int64_t)n * oT + b.t0 + tl) * oH + b.h0 + hl) * oW + b.w0) * C;
+        if constexpr (VEC) {
+            const float4* s4 = reinterpret_cast<const float4*>(src);
+            float4* d4 = reinterpret_cast<float4*>(dst);
+            for (int e4 = threadIdx.x; e4 < seg / 4; e4 += kThreads) {
+                int wl = (4 * e4) / C, rem = 4 * e4 - wl * C;
+                const float4 sv = s4[e4];
+                float4 dv = d4[e4];
+                float* dp = &dv.x;
+                const float* sp = &sv.x;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    dp[k] += wh * col[wl] * sp[k];
+                    if (++rem == C) {
+                        rem = 0;
+                        ++wl;
+                    }
+                }
+                d4[e4] = dv;
+            }
+        } else {
+            for (int e = threadIdx.x; e < seg; e += kThreads) dst[e] += wh * col[e / C] * src[e];
+        }
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void merge_finalize_rows_kernel(float* __restrict__ out,
+                                                                       int32_t oT, int32_t oH,
+                                                                       int32_t oW, int32_t C,
+                                                                       AxisTiling ah,
+                                                                       AxisTiling aw) {
+    extern __shared__ float col[];          // S_w of each output column
+    for (int i = threadIdx.x; i < oW; i += kThreads) col[i] = axis_weight_sum(aw, i);
+    __syncthreads();
+    const int n = blockIdx.y;
+    const int64_t rows = (int64_t)oT * oH;
+    const int seg = oW * C;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const float sh = axis_weight_sum(ah, (int)(r % oH));
+        float* row = out + ((int64_t)n * rows + r) * seg;
+        if constexpr (VEC) {
+            float4* r4 = reinterpret_cast<float4*>(row);
+            for (int e4 = threadIdx.x; e4 < seg / 4; e4 += kThreads) {
+                int wl = (4 * e4) / C, rem = 4 * e4 - wl * C;
+                float4 v = r4[e4];
+                float* vp = &v.x;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    vp[k] /= sh * col[wl];
+                    if (++rem == C) {
+                        rem = 0;
+                        ++wl;
+                    }
+                }
+                r4[e4] = v;
+            }
+        } else {
+            for (int e = threadIdx.x; e < seg; e += kThreads) row[e] /= sh * col[e / C];
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void zero_kernel(uint4* p, int64_t n16) {
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
          i += (int64_t)gridDim.x * kThreads)
@@ -86,6 +177,26 @@ vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& b, int32_t le
                           int32_t trail_h, int32_t lead_w, int32_t trail_w,
                           const vae_tensor_t& out, hipStream_t stream) {
     if (b.volume() == 0 || out.n == 0) return VAE_OK;
+    const float* tp = static_cast<const float*>(tile_out.data);
+    float* op = static_cast<float*>(out.data);
+    if (b.bw() <= kMaxLdsColumns) {
+        const int64_t rows = b.bt() * b.bh();
+        const dim3 grid((unsigned)std::min<int64_t>(rows, kRowBlocks), (unsigned)out.n);
+        const size_t lds = (size_t)b.bw() * sizeof(float);
+        const bool vec = (b.bw() * out.c) % 4 == 0 && (b.w0 * out.c) % 4 == 0 &&
+                         (out.w * out.c) % 4 == 0 && (uintptr_t)tp % 16 == 0 &&
+                         (uintptr_t)op % 16 == 0;
+        if (vec)
+            hipLaunchKernelGGL(merge_rows_kernel<true>, grid, dim3(kThreads), lds, stream, tp, op,
+                               (int32_t)out.t, (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, b,
+                               lead_h, trail_h, lead_w, trail_w);
+        else
+            hipLaunchKernelGGL(merge_rows_kernel<false>, grid, dim3(kThreads), lds, stream, tp, op,
+                               (int32_t)out.t, (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, b,
+                               lead_h, trail_h, lead_w, trail_w);
+        VAE_HIP_CHECK(hipGetLastError());
+        return VAE_OK;
+    }
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(b.bt() * b.bh()), (unsigned)out.n),
                        dim3(kThreads), 0, stream, static_cast<const float*>(tile_out.data),
                        static_cast<float*>(out.data), (int32_t)out.t, (int32_t)out.h,
@@ -97,6 +208,22 @@ vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& b, int32_t le
 vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& ah,
                                    const AxisTiling& aw, hipStream_t stream) {
     if (numel(out) == 0) return VAE_OK;
+    float* op = static_cast<float*>(out.data);
+    if (out.w <= kMaxLdsColumns) {
+        const int64_t rows = out.t * out.h;
+        const dim3 grid((unsigned)std::min<int64_t>(rows, kRowBlocks), (unsigned)out.n);
+        const size_t lds = (size_t)out.w * sizeof(float);
+        if ((out.w * out.c) % 4 == 0 && (uintptr_t)op % 16 == 0)
+            hipLaunchKernelGGL(merge_finalize_rows_kernel<true>, grid, dim3(kThreads), lds, stream,
+                               op, (int32_t)out.t, (int32_t)out.h, (int32_t)out.w, (int32_t)out.c,
+                               ah, aw);
+        else
+            hipLaunchKernelGGL(merge_finalize_rows_kernel<false>, grid, dim3(kThreads), lds,
+                               stream, op, (int32_t)out.t, (int32_t)out.h, (int32_t)out.w,
+                               (int32_t)out.c, ah, aw);
+        VAE_HIP_CHECK(hipGetLastError());
+        return VAE_OK;
+    }
     hipLaunchKernelGGL(merge_finalize_kernel, dim3((unsigned)(out.t * out.h), (unsigned)out.n),
                        dim3(kThreads), 0, stream, static_cast<float*>(out.data), (int32_t)out.t,
                        (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, ah, aw);
