@@ -22,18 +22,20 @@ Sources, cited by page title and the part of the page:
   thread).
 - "Add tiled VAE parallelism & extended model support" (DistVAE PR #14): patch sharding with halo
   rows, global-mean biased-variance GroupNorm across patches, band rule, padding at true borders
-  only, causal temporal padding by repeated frames, depth-to-space upsampler (commit messages).
+  only, causal temporal padding by repeated frames, depth-to-space upsampler, RMS norms that reduce
+  over channels and a mid-block attention that takes each frame whole (commit messages).
 
 Parity status of each function:
 - pinned by tests/test_oracle_*.py: conv (brute force, torch CPU, causality), GroupNorm (torch CPU,
   closed forms, Chan split invariance, negative control), SiLU identities, upsampling (repeat,
   inverse), tiling (page-printed grids, band rule), merge identities, mode A == whole decode,
-  mode B 1x1 == whole decode;
+  mode B 1x1 == whole decode; RMS norm (closed forms, torch CPU rms_norm), frame attention (torch
+  CPU scaled_dot_product_attention, uniform-attention and permutation invariants);
 - parity unpinned: the absolute output values of a full random-init decoder. The pages print no
   tensor values, so a decoder's output is pinned only through its parts and the invariants above.
 """
 from .layers import (causal_conv3d, conv3d_valid, causal_time_pad, group_norm, silu,
-                     nearest_upsample, depth_to_space)
+                     nearest_upsample, depth_to_space, rms_norm, softmax, frame_attention)
 from .stats import group_moments, chan_combine, normalize_with
 from .tiling import (bands, axis_tiles, patch_tiles, overlap_tiles, ramp_1d, axis_weight_sum)
 from .decoder import (decode, decode_patch_halo, decode_overlap_blend, merge_tiles,
@@ -41,7 +43,8 @@ from .decoder import (decode, decode_patch_halo, decode_overlap_blend, merge_til
 
 __all__ = [
     "causal_conv3d", "conv3d_valid", "causal_time_pad", "group_norm", "silu", "nearest_upsample",
-    "depth_to_space", "group_moments", "chan_combine", "normalize_with", "bands", "axis_tiles",
+    "depth_to_space", "rms_norm", "softmax", "frame_attention", "group_moments", "chan_combine",
+    "normalize_with", "bands", "axis_tiles",
     "patch_tiles", "overlap_tiles", "ramp_1d", "axis_weight_sum", "decode", "decode_patch_halo",
     "decode_overlap_blend", "merge_tiles", "output_shape",
 ]

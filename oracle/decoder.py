@@ -3,7 +3,9 @@
 Test infrastructure: only tests, the smoke check and the benchmark's CPU-baseline leg use it.
 
 The layer plan and parameters come from ``vae_synth``: a list of ops and a parameter list in plan
-order. A residual block is GN+SiLU, conv, GN+SiLU, conv, plus its input.
+order. A residual block is GN+SiLU, conv, GN+SiLU, conv, plus its input; ``res_rms`` is the same
+block with RMS norms, ``rms_silu`` an RMS norm followed by SiLU, and ``attn`` the single-head
+frame attention block (``layers.frame_attention``).
 
 ``decode_patch_halo`` deliberately does not call ``decode``. It is the patch-sharded computation of
 "Add tiled VAE parallelism & extended model support" (PatchConv3d / PatchGroupNorm commit messages):
@@ -23,7 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 from .layers import causal_conv3d, causal_time_pad, conv3d_valid, group_norm, silu, \
-    nearest_upsample, depth_to_space
+    nearest_upsample, depth_to_space, rms_norm, frame_attention
 from .stats import group_moments, chan_combine, normalize_with
 from .tiling import bands, overlap_tiles, ramp_1d
 
@@ -67,6 +69,20 @@ def decode(spec: dict, z: np.ndarray, params: list) -> np.ndarray:
         elif k == "gn_silu":
             g = next(it)
             h = silu(group_norm(h, groups, eps, g["gamma"], g["beta"]))
+        elif k == "res_rms":
+            g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+            t = silu(rms_norm(h, eps, g1["gamma"], g1["beta"]))
+            t = causal_conv3d(t, c1["w"], c1["b"])
+            t = silu(rms_norm(t, eps, g2["gamma"], g2["beta"]))
+            h = causal_conv3d(t, c2["w"], c2["b"]) + h
+            del t
+        elif k == "rms_silu":
+            g = next(it)
+            h = silu(rms_norm(h, eps, g["gamma"], g["beta"]))
+        elif k == "attn":
+            a = next(it)
+            h = frame_attention(h, eps, a["gamma"], a["beta"], a["w_qkv"], a["b_qkv"], a["w_out"],
+                                a["b_out"])
         elif k == "d2s":
             h = depth_to_space(h, op["st"], op["sh"], op["sw"])
         elif k == "nearest":
@@ -151,6 +167,29 @@ def decode_patch_halo(spec: dict, z: np.ndarray, params: list, grid) -> np.ndarr
         elif k == "gn_silu":
             g = next(it)
             patches = _gn_patches(patches, groups, eps, g["gamma"], g["beta"], True)
+        elif k == "res_rms":
+            # RMS norms reduce over channels: each patch normalises its own positions
+            g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+            t = [[silu(rms_norm(p, eps, g1["gamma"], g1["beta"])) for p in row] for row in patches]
+            t = _conv_patches(t, c1["w"], c1["b"])
+            t = [[silu(rms_norm(p, eps, g2["gamma"], g2["beta"])) for p in row] for row in t]
+            t = _conv_patches(t, c2["w"], c2["b"])
+            patches = [[a + bb for a, bb in zip(ra, rb)] for ra, rb in zip(t, patches)]
+        elif k == "rms_silu":
+            g = next(it)
+            patches = [[silu(rms_norm(p, eps, g["gamma"], g["beta"])) for p in row]
+                       for row in patches]
+        elif k == "attn":
+            # the frame is gathered whole around the attention, then cut back into the same bands
+            a = next(it)
+            rows = [row[0].shape[2] for row in patches]
+            cols = [p.shape[3] for p in patches[0]]
+            whole = np.concatenate([np.concatenate(row, axis=3) for row in patches], axis=2)
+            whole = frame_attention(whole, eps, a["gamma"], a["beta"], a["w_qkv"], a["b_qkv"],
+                                    a["w_out"], a["b_out"])
+            r_at, c_at = _starts(rows), _starts(cols)
+            patches = [[whole[:, :, r_at[i]:r_at[i] + rows[i], c_at[j]:c_at[j] + cols[j]]
+                        for j in range(len(cols))] for i in range(len(rows))]
         elif k == "d2s":
             patches = [[depth_to_space(p, op["st"], op["sh"], op["sw"]) for p in row]
                        for row in patches]

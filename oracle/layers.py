@@ -134,3 +134,53 @@ def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
     y = x.reshape(n, t, h, w, st, sh, sw, c)
     y = y.transpose(0, 1, 4, 2, 5, 3, 6, 7).reshape(n, t * st, h * sh, w * sw, c)
     return np.ascontiguousarray(y[:, st - 1:])
+
+
+def rms_norm(x: np.ndarray, eps: float, gamma=None, beta=None) -> np.ndarray:
+    """Per-position RMS normalisation over the channels: y = x / sqrt(mean_c(x^2) + eps) * gamma
+    + beta.
+
+    Wan-style decoders normalise with RMS norms that reduce over channels only, so a spatial split
+    needs no exchange of statistics ("Add tiled VAE parallelism & extended model support", commit
+    messages on the Qwen-Image / Wan adapters and on the HunyuanVideo 1.5 encoder). The pages give
+    no formula; this is the plainest reading: the root mean square of the position's channel vector,
+    eps inside the root, then the per-channel affine.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    y = x / np.sqrt(ms + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, dtype=np.float64)
+    return y
+
+
+def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
+    """exp(s - max) / sum(exp(s - max)) along ``axis``."""
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - s.max(axis=axis, keepdims=True))
+    return e / e.sum(axis=axis, keepdims=True)
+
+
+def frame_attention(x: np.ndarray, eps: float, gamma, beta, w_qkv, b_qkv, w_out, b_out) -> np.ndarray:
+    """Single-head self-attention over the positions of each frame, with its residual.
+
+    A Wan-style decoder's mid block holds one attention block that takes each frame whole: it
+    cannot be applied to a patch, so a patch-split decode gathers the frame around it ("Add tiled
+    VAE parallelism & extended model support", commit message on the HunyuanVideo adapters; the Wan
+    attention block of "[TRTLLM-14123][feat] add ParallelVAE_TrtllmWan for native Wan VAE",
+    Description). The pages give no formula; the plainest reading of a single-head spatial block:
+      xn = rms_norm(x); [q | k | v] = xn W_qkv^T + b_qkv  (W_qkv [3C, C]);
+      per sample and frame, A = softmax(q k^T / sqrt(C)) over the frame's H*W positions;
+      y = (A v) W_out^T + b_out + x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, t, h, w, c = x.shape
+    xn = rms_norm(x, eps, gamma, beta).reshape(n, t, h * w, c)
+    qkv = xn @ np.asarray(w_qkv, np.float64).T + np.asarray(b_qkv, np.float64)
+    q, k, v = qkv[..., :c], qkv[..., c:2 * c], qkv[..., 2 * c:]
+    a = softmax((q @ np.swapaxes(k, -1, -2)) / np.sqrt(c), axis=-1)
+    o = a @ v
+    y = o @ np.asarray(w_out, np.float64).T + np.asarray(b_out, np.float64)
+    return y.reshape(n, t, h, w, c) + x

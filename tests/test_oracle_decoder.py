@@ -129,3 +129,21 @@ def test_tiny_decoder_matches_torch_library_graph():
     ref = _torch_decode(spec, z, params)
     got = oracle.decode(spec, z, params)
     assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-11
+
+
+@pytest.mark.parametrize("name,grid", [("wan_tiny", (2, 2)), ("wan_small", (1, 2))])
+def test_wan_shaped_patch_halo_equals_whole(name, grid):
+    """RMS norms reduce over channels and the attention gathers whole frames, so the patch-halo
+    decode of the Wan-shaped plan equals the whole decode."""
+    spec = vae_synth.WORKLOADS[name]
+    z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1)).astype(np.float64)
+    p = vae_synth.decoder_params(spec, affine_seed=7)
+    whole = oracle.decode(spec, z, p)
+    assert whole.shape == oracle.output_shape(spec, z.shape)
+    patch = oracle.decode_patch_halo(spec, z, p, grid)
+    assert np.abs(patch - whole).max() <= 1e-9 * np.abs(whole).max()
+
+
+def test_wan_shaped_output_shape():
+    spec = vae_synth.WAN_720P
+    assert oracle.output_shape(spec, (1, 21, 44, 80, 48)) == (1, 81, 704, 1280, 3)

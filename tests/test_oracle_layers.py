@@ -220,3 +220,90 @@ def test_synth_bf16_rounding():
     assert r[3] == -2.5
     t = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(r, t)
+
+
+# ------------------------------------------------------------------------------------------------
+# RMS norm and frame attention (Wan-shaped decoder)
+# ------------------------------------------------------------------------------------------------
+
+def test_rms_norm_matches_torch_and_closed_form():
+    import torch
+    x = vae_synth.normal((2, 3, 4, 5, 64), [40, 1], scale=2.0, mean=0.5).astype(np.float64)
+    gamma = vae_synth.normal((64,), [40, 2], scale=0.2, mean=1.0).astype(np.float64)
+    beta = vae_synth.normal((64,), [40, 3], scale=0.1).astype(np.float64)
+    got = oracle.rms_norm(x, 1e-6, gamma, beta)
+    ref = torch.nn.functional.rms_norm(torch.as_tensor(x), (64,), torch.as_tensor(gamma),
+                                       eps=1e-6).numpy() + beta
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # closed form: without the affine, the mean square over channels is ms / (ms + eps)
+    y = oracle.rms_norm(x, 1e-3)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), ms / (ms + 1e-3), rtol=1e-12)
+    # positive scale invariance (eps = 0), and each position on its own
+    np.testing.assert_allclose(oracle.rms_norm(3.5 * x, 0.0), oracle.rms_norm(x, 0.0), rtol=1e-12)
+    np.testing.assert_allclose(oracle.rms_norm(x[:, :1], 1e-6), oracle.rms_norm(x, 1e-6)[:, :1],
+                               rtol=0, atol=0)
+
+
+def _attn_inputs(c, seed):
+    g = vae_synth.normal((c,), [41, seed, 0], scale=0.2, mean=1.0).astype(np.float64)
+    b = vae_synth.normal((c,), [41, seed, 1], scale=0.1).astype(np.float64)
+    wq = vae_synth.normal((3 * c, c), [41, seed, 2], scale=1 / np.sqrt(c)).astype(np.float64)
+    bq = vae_synth.normal((3 * c,), [41, seed, 3], scale=0.1).astype(np.float64)
+    wo = vae_synth.normal((c, c), [41, seed, 4], scale=1 / np.sqrt(c)).astype(np.float64)
+    bo = vae_synth.normal((c,), [41, seed, 5], scale=0.1).astype(np.float64)
+    return g, b, wq, bq, wo, bo
+
+
+def test_frame_attention_matches_torch_sdpa():
+    import torch
+    F = torch.nn.functional
+    c = 32
+    x = vae_synth.normal((2, 3, 4, 5, c), [42, 0]).astype(np.float64)
+    g, b, wq, bq, wo, bo = _attn_inputs(c, 0)
+    got = oracle.frame_attention(x, 1e-6, g, b, wq, bq, wo, bo)
+    t = torch.as_tensor
+    xt = t(x)
+    xn = F.rms_norm(xt, (c,), t(g), eps=1e-6) + t(b)
+    qkv = F.linear(xn.reshape(2, 3, 20, c), t(wq), t(bq))
+    q, k, v = qkv[..., :c], qkv[..., c:2 * c], qkv[..., 2 * c:]
+    o = F.scaled_dot_product_attention(q, k, v)            # softmax(q k^T / sqrt(c)) v
+    ref = (F.linear(o, t(wo), t(bo)).reshape(x.shape) + xt).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+
+
+def test_frame_attention_invariants():
+    c = 16
+    x = vae_synth.normal((1, 2, 3, 4, c), [43, 0]).astype(np.float64)
+    g, b, wq, bq, wo, bo = _attn_inputs(c, 1)
+    # zero queries: every position attends uniformly, so it receives the frame mean of v
+    wq0, bq0 = wq.copy(), bq.copy()
+    wq0[:c] = 0.0
+    bq0[:c] = 0.0
+    y = oracle.frame_attention(x, 1e-6, g, b, wq0, bq0, wo, bo)
+    xn = oracle.rms_norm(x, 1e-6, g, b)
+    v = xn @ wq[2 * c:].T + bq[2 * c:]
+    vmean = v.mean(axis=(2, 3), keepdims=True)
+    np.testing.assert_allclose(y, np.broadcast_to(vmean @ wo.T + bo, x.shape) + x, rtol=1e-12,
+                               atol=1e-12)
+    # permuting the positions of a frame permutes the output the same way
+    y = oracle.frame_attention(x, 1e-6, g, b, wq, bq, wo, bo)
+    perm = vae_synth.normal((12,), [43, 1]).argsort()
+    xp = x.reshape(1, 2, 12, c)[:, :, perm].reshape(x.shape)
+    yp = oracle.frame_attention(xp, 1e-6, g, b, wq, bq, wo, bo)
+    np.testing.assert_allclose(yp.reshape(1, 2, 12, c), y.reshape(1, 2, 12, c)[:, :, perm],
+                               rtol=1e-12, atol=1e-12)
+    # frames do not see each other
+    y1 = oracle.frame_attention(x[:, 1:], 1e-6, g, b, wq, bq, wo, bo)
+    np.testing.assert_allclose(y1, y[:, 1:], rtol=0, atol=1e-14)
+
+
+def test_attention_needs_the_whole_frame():
+    """Negative control: attention applied per width patch differs from whole-frame attention."""
+    c = 16
+    x = vae_synth.normal((1, 1, 4, 6, c), [44, 0]).astype(np.float64)
+    g, b, wq, bq, wo, bo = _attn_inputs(c, 2)
+    whole = oracle.frame_attention(x, 1e-6, g, b, wq, bq, wo, bo)
+    per_patch = np.concatenate([oracle.frame_attention(x[:, :, :, s], 1e-6, g, b, wq, bq, wo, bo)
+                                for s in (slice(0, 3), slice(3, 6))], axis=3)
+    assert np.abs(per_patch - whole).max() > 1e-2

@@ -17,6 +17,10 @@ is built from its config.json with random weights):
 - ``LTX2_720P_1F``: the same plan on one latent frame at the full 720p extent [1,128,1,22,40];
 - ``LTX2_TINY``: the same structure at a quarter of the widths, for a quick smoke check;
   ``LTX2_TINY_N2`` is that plan on a batch of two latents.
+- ``WAN_720P``: a Wan2.2-TI2V-5B-shaped bf16 decoder, latent [1,48,21,44,80] -> video
+  [1,3,81,704,1280]: RMS-norm residual blocks, a mid-block single-head frame attention, two
+  temporal and three spatial (nearest + conv) upsamplings, unpatchify 2x2. ``WAN_SMALL`` and
+  ``WAN_TINY`` are that plan at oracle-friendly sizes (full and quarter widths).
 
 Layer plan vocabulary (every op works on a channels-last activation):
 - ``conv``: causal Conv3d 3x3x3, stride 1, ``cin`` -> ``cout``; ``"f32_out": True`` keeps the result
@@ -27,14 +31,19 @@ Layer plan vocabulary (every op works on a channels-last activation):
   2e-2 max-abs of the oracle;
 - ``res``: residual block of width ``c``: GN+SiLU, conv, GN+SiLU, conv, plus the block input;
 - ``gn_silu``: GroupNorm followed by SiLU;
+- ``res_rms`` / ``rms_silu``: the same with per-position RMS norms over the channels;
+- ``attn``: single-head self-attention over each frame's positions, width ``c``, with its residual;
 - ``d2s``: depth-to-space by (st, sh, sw); with st > 1 the first st-1 output frames are dropped;
 - ``nearest``: nearest-neighbour spatial upsampling by (sh, sw).
 
 Parameters are drawn in plan order: each ``conv`` gives one weight [cout, cin, 3, 3, 3] and one bias
-[cout]; each ``res`` gives GN(c), conv(c, c), GN(c), conv(c, c); each ``gn_silu`` gives GN(c). Conv
-weight number k (0-based, counting every conv in plan order) is N(0, 1) * 1/sqrt(27 * cin) drawn from
-PCG64([1, k]). Biases are 0, GN gamma is 1 and beta is 0, unless ``affine_seed`` asks for random
-values (used by tests to exercise the bias, gamma and beta paths).
+[cout]; each ``res`` / ``res_rms`` gives norm(c), conv(c, c), norm(c), conv(c, c); each ``gn_silu`` /
+``rms_silu`` gives norm(c); each ``attn`` gives one dict with the norm's gamma/beta, w_qkv [3c, c],
+b_qkv [3c], w_out [c, c], b_out [c]. Conv weight number k (0-based, counting every conv in plan
+order) is N(0, 1) * 1/sqrt(27 * cin) drawn from PCG64([1, k]); attention block number k draws
+w_qkv and w_out as N(0, 1) * 1/sqrt(c) from PCG64([5, k, 0]) and PCG64([5, k, 1]). Biases are 0,
+norm gamma is 1 and beta is 0, unless ``affine_seed`` asks for random values (used by tests to
+exercise the bias, gamma and beta paths).
 """
 from __future__ import annotations
 
@@ -44,7 +53,7 @@ import numpy as np
 
 __all__ = [
     "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "LTX2_720P_1F", "LTX2_TINY",
-    "LTX2_TINY_N2", "WORKLOADS",
+    "LTX2_TINY_N2", "WAN_720P", "WAN_SMALL", "WAN_TINY", "WORKLOADS",
     "round_bf16", "bf16_bits", "normal", "uniform", "latent", "decoder_params", "conv_params",
     "walk_plan", "with_latent",
 ]
@@ -169,8 +178,56 @@ LTX2_TINY = {
 # Two samples in one latent: every per-sample path (GroupNorm statistics, tile offsets) at N = 2.
 LTX2_TINY_N2 = with_latent(LTX2_TINY, (2, 128, 2, 4, 6), "ltx2_tiny_n2")
 
+_WAN_LAYERS = [
+    {"op": "conv", "cin": 48, "cout": 1024},
+    {"op": "res_rms", "c": 1024},                                   # mid block
+    {"op": "attn", "c": 1024},
+    {"op": "res_rms", "c": 1024},
+    {"op": "res_rms", "c": 1024},                                   # stage 0
+    {"op": "conv", "cin": 1024, "cout": 2048},                       # temporal x2
+    {"op": "d2s", "st": 2, "sh": 1, "sw": 1},
+    {"op": "nearest", "sh": 2, "sw": 2},                            # spatial x2
+    {"op": "conv", "cin": 1024, "cout": 512},
+    {"op": "res_rms", "c": 512},                                    # stage 1
+    {"op": "conv", "cin": 512, "cout": 1024},                        # temporal x2
+    {"op": "d2s", "st": 2, "sh": 1, "sw": 1},
+    {"op": "nearest", "sh": 2, "sw": 2},                            # spatial x2
+    {"op": "conv", "cin": 512, "cout": 256},
+    {"op": "res_rms", "c": 256},                                    # stage 2
+    {"op": "nearest", "sh": 2, "sw": 2},                            # spatial x2
+    {"op": "conv", "cin": 256, "cout": 128},
+    {"op": "res_rms", "c": 128},                                    # stage 3
+    {"op": "rms_silu"},
+    {"op": "conv", "cin": 128, "cout": 12, "f32_out": True},
+    {"op": "d2s", "st": 1, "sh": 2, "sw": 2},                       # unpatchify 2x2
+]
+
+WAN_720P = {
+    "name": "wan_720p",
+    "dtype": "bf16",
+    "latent": (1, 48, 21, 44, 80),
+    "groups": 32, "eps": 1e-6,
+    "layers": _WAN_LAYERS,
+    "scale": (4, 16, 16),
+    "patch_grid": (1, 4),
+    "overlap_tile": (32, 32), "overlap_stride": (28, 28),
+}
+WAN_SMALL = with_latent(WAN_720P, (1, 48, 2, 3, 5), "wan_small",
+                        patch_grid=(1, 2), overlap_tile=(2, 4), overlap_stride=(1, 3))
+
+# The Wan plan at a quarter of the widths (256/128/64/32).
+WAN_TINY = with_latent(WAN_720P, (1, 48, 3, 4, 6), "wan_tiny",
+                       patch_grid=(2, 2), overlap_tile=(3, 4), overlap_stride=(2, 3))
+WAN_TINY["layers"] = [dict(op) for op in _WAN_LAYERS]
+for _op in WAN_TINY["layers"]:
+    for _k in ("cin", "cout", "c"):
+        if _k in _op and not (_k == "cin" and _op["cin"] == 48) and \
+                not (_k == "cout" and _op.get("f32_out")):
+            _op[_k] //= 4
+
 WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
-                                    LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2)}
+                                    LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2, WAN_720P, WAN_SMALL,
+                                    WAN_TINY)}
 
 
 # ----------------------------------------------------------------------------------------------
@@ -229,6 +286,19 @@ def gn_params(index: int, c: int, affine_seed=None) -> dict:
     return {"kind": "gn", "gamma": gamma, "beta": beta, "c": c}
 
 
+def attn_params(index: int, c: int, dtype: str, affine_seed=None) -> dict:
+    g = gn_params(1000 + index, c, affine_seed)
+    w_qkv = normal((3 * c, c), [5, index, 0], scale=1.0 / np.sqrt(c), dtype=dtype)
+    w_out = normal((c, c), [5, index, 1], scale=1.0 / np.sqrt(c), dtype=dtype)
+    if affine_seed is None:
+        b_qkv, b_out = np.zeros(3 * c, np.float32), np.zeros(c, np.float32)
+    else:
+        b_qkv = normal((3 * c,), [6, affine_seed, index, 0], scale=0.1)
+        b_out = normal((c,), [6, affine_seed, index, 1], scale=0.1)
+    return {"kind": "attn", "gamma": g["gamma"], "beta": g["beta"], "w_qkv": w_qkv,
+            "b_qkv": b_qkv, "w_out": w_out, "b_out": b_out, "c": c}
+
+
 def walk_plan(spec: dict):
     """Yield (op, channels_in, channels_out) along the plan, following the channel count only."""
     c = spec["latent"][1]
@@ -237,9 +307,9 @@ def walk_plan(spec: dict):
         if kind == "conv":
             yield op, op["cin"], op["cout"]
             c = op["cout"]
-        elif kind == "res":
+        elif kind in ("res", "res_rms", "attn"):
             yield op, op["c"], op["c"]
-        elif kind == "gn_silu":
+        elif kind in ("gn_silu", "rms_silu"):
             yield op, c, c
         elif kind == "d2s":
             k = op["st"] * op["sh"] * op["sw"]
@@ -253,17 +323,19 @@ def walk_plan(spec: dict):
 
 def decoder_params(spec: dict, affine_seed=None) -> list:
     """Parameter list of a decoder plan, in plan order (see the module docstring)."""
-    out, n_conv, n_gn = [], 0, 0
+    out, n_conv, n_gn, n_attn = [], 0, 0, 0
     dt = spec["dtype"]
     for op, cin, cout in walk_plan(spec):
         kind = op["op"]
         if kind == "conv":
             out.append(conv_params(n_conv, cin, cout, dt, affine_seed)); n_conv += 1
-        elif kind == "res":
+        elif kind == "attn":
+            out.append(attn_params(n_attn, cin, dt, affine_seed)); n_attn += 1
+        elif kind in ("res", "res_rms"):
             out.append(gn_params(n_gn, cin, affine_seed)); n_gn += 1
             out.append(conv_params(n_conv, cin, cin, dt, affine_seed)); n_conv += 1
             out.append(gn_params(n_gn, cin, affine_seed)); n_gn += 1
             out.append(conv_params(n_conv, cin, cin, dt, affine_seed)); n_conv += 1
-        elif kind == "gn_silu":
+        elif kind in ("gn_silu", "rms_silu"):
             out.append(gn_params(n_gn, cin, affine_seed)); n_gn += 1
     return out
