@@ -257,6 +257,45 @@ VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t*
                                          int32_t apply_silu, vae_tensor_t* y, vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* RMS norm and frame attention (Wan-style decoders)                                          */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * y = act(x / sqrt(mean_c(x^2) + eps) * gamma + beta) at every position, act = SiLU or the identity.
+ * The norm reduces over the channels of one position only, so a patch-split decode needs no
+ * statistics from other patches (P4, commit messages on the Qwen-Image / Wan adapters and on the
+ * HunyuanVideo 1.5 encoder: RMS norms that reduce over channels need nothing sharded). The pages
+ * give no formula; this is the root mean square of the channel vector with eps inside the root.
+ *  x: bf16 or fp32, C % 8 == 0 and C / 8 dividing 256 (else UNSUPPORTED with info).
+ *  gamma, beta: [C] fp32 (device) or NULL (1 and 0).
+ *  y: x's shape; bf16, fp16 or fp32. It may alias x when the dtypes match.
+ */
+VAE_API vae_status_t vae_rmsnorm_silu(const vae_tensor_t* x, float eps, const float* gamma,
+                                      const float* beta, int32_t apply_silu, vae_tensor_t* y,
+                                      vae_stream_t stream);
+
+/*
+ * Single-head self-attention over the H*W positions of each frame (each sample and T index), plus
+ * the residual: the mid-block attention of Wan-style decoders, which takes a frame whole, so a
+ * patch-split decode gathers the frame around it (P4, commit message on the HunyuanVideo adapters;
+ * P5, Description: the Wan attention block). The pages give no formula; the plainest reading:
+ *   xn = rms_norm(x) with gamma/beta (no SiLU);  [q | k | v] = xn W_qkv^T + b_qkv;
+ *   y = softmax(q k^T / sqrt(C)) v W_out^T + b_out + x   (softmax over the frame's positions).
+ * Arithmetic: xn and the projections' operands bf16; q, k, v and the softmax weights fp16; every
+ * product accumulates in fp32; the logits and y are fp32.
+ *  x, y: fp32 [N,T,H,W,C], C % 32 == 0 and C / 8 dividing 256; y may alias x.
+ *  w_qkv: bf16 [3C][C] (rows: q, then k, then v), b_qkv [3C] fp32 or NULL; w_out: bf16 [C][C],
+ *  b_out [C] fp32 or NULL; gamma, beta: [C] fp32 or NULL. All device.
+ *  ws: device scratch of vae_frame_attention_workspace() bytes (16-byte aligned); contents undefined
+ *  afterwards. It holds about (8C + 6 H*W) * N*T*H*W bytes.
+ */
+VAE_API vae_status_t vae_frame_attention_workspace(const vae_tensor_t* x, size_t* bytes);
+VAE_API vae_status_t vae_frame_attention(const vae_tensor_t* x, float eps, const float* gamma,
+                                         const float* beta, const void* w_qkv,
+                                         const float* b_qkv, const void* w_out,
+                                         const float* b_out, vae_tensor_t* y, void* ws,
+                                         size_t ws_bytes, vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Upsampling                                                                                 */
 /* ------------------------------------------------------------------------------------------ */
 /*
@@ -343,6 +382,9 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  *  VAE_OP_GN_SILU GroupNorm + SiLU
  *  VAE_OP_D2S     depth-to-space (st, sh, sw) with the causal frame drop
  *  VAE_OP_NEAREST nearest spatial upsampling (sh, sw)
+ *  VAE_OP_RES_RMS residual block of width cin with RMS norms (vae_rmsnorm_silu) for the GroupNorms
+ *  VAE_OP_RMS_SILU RMS norm + SiLU
+ *  VAE_OP_ATTN    single-head frame attention of width cin (vae_frame_attention), fp32 activations
  * Dtypes:
  *  - conv weights and GroupNorm outputs (the operands of the next conv) have the plan dtype;
  *  - conv outputs and the residual stream have act_dtype;
@@ -354,17 +396,20 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * unless its no_split is set. A standalone GN_SILU followed by a splitting CONV writes fp32 for
  * it. The convs inside residual blocks keep one rounding of their GroupNorm operand.
  * VAE_DECODE_F16_OPERANDS (bf16 plans with fp32 activations; not with the split flag) gives
- * those same convs, i.e. every CONV that follows a RES or GN_SILU, fp16 operands instead: the producing op stores its
- * output in fp16 (one rounding to 11 significant bits) and the conv runs at the bf16 rate
+ * those same convs, i.e. every CONV that follows a RES, RES_RMS, GN_SILU or RMS_SILU (possibly
+ * through NEAREST ops, which copy), fp16 operands instead: the producing op stores its output in
+ * fp16 (one rounding to 11 significant bits) and the conv runs at the bf16 rate
  * (vae_conv3d_causal with an fp16 x). no_split does not apply to it. Activations must stay below
  * 65504 in magnitude there.
- * The parameter pointers come in plan order, two per entry:
+ * The parameter pointers come in plan order:
  *  conv -> (weight, bias);
- *  GN -> (gamma, beta);
- *  res -> GN, conv, GN, conv.
+ *  GN or RMS -> (gamma, beta);
+ *  res, res_rms -> norm, conv, norm, conv;
+ *  attn -> (gamma, beta, w_qkv [3C][C] bf16, b_qkv [3C], w_out [C][C] bf16, b_out [C]).
  * bias, gamma and beta may be NULL.
  */
-enum { VAE_OP_CONV = 1, VAE_OP_RES = 2, VAE_OP_GN_SILU = 3, VAE_OP_D2S = 4, VAE_OP_NEAREST = 5 };
+enum { VAE_OP_CONV = 1, VAE_OP_RES = 2, VAE_OP_GN_SILU = 3, VAE_OP_D2S = 4, VAE_OP_NEAREST = 5,
+       VAE_OP_RES_RMS = 6, VAE_OP_RMS_SILU = 7, VAE_OP_ATTN = 8 };
 
 typedef struct vae_layer_desc {
     int32_t op;
@@ -430,7 +475,7 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec, const vae_tensor
 /* Per-op GPU timing of the most recent vae_decode_tiled call (events recorded on its stream).
  * Enabled with vae_decoder_set_timing(dec, 1); collecting waits for the last recorded event. */
 enum { VAE_KIND_CONV = 1, VAE_KIND_GN = 2, VAE_KIND_UPSAMPLE = 3, VAE_KIND_MERGE = 4,
-       VAE_KIND_OTHER = 5 };
+       VAE_KIND_OTHER = 5, VAE_KIND_RMS = 6, VAE_KIND_ATTN = 7 };
 typedef struct vae_op_timing {
     int32_t kind;       /* VAE_KIND_* */
     int32_t layer;      /* index in the plan */

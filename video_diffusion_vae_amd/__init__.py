@@ -7,4 +7,4 @@ built.
 from ._binding import *  # noqa: F401,F403
 from ._binding import (LIB, EXPORTS, Decoder, VaeError, tensor_desc, tiling_desc,  # noqa: F401
                        last_error_info, layer_descs)
-from .weights import upload_decoder, conv_weight_layout  # noqa: F401
+from .weights import upload_decoder, conv_weight_layout, latent_channels, pad_latent  # noqa: F401

@@ -19,7 +19,8 @@ VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
 VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
 VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
-VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other"}
+VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN = 6, 7, 8
+VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other", 6: "rms", 7: "attn"}
 
 # Every symbol include/vae.h declares.
 EXPORTS = (
@@ -28,7 +29,8 @@ EXPORTS = (
     "vae_decoder_packed_weight_size",
     "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
-    "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_upsample",
+    "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_rmsnorm_silu",
+    "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
     "vae_decode_workspace_size", "vae_decode_tiled", "vae_decoder_set_timing",
     "vae_decoder_get_timing",
@@ -124,6 +126,9 @@ def _load():
         "vae_groupnorm_stats": ([T, B, I32, I32, P, P, SZ, P], I32),
         "vae_groupnorm_combine": ([P, I32, I32, I32, F, P, P], I32),
         "vae_groupnorm_apply": ([T, B, I32, P, P, P, I32, T, P], I32),
+        "vae_rmsnorm_silu": ([T, F, P, P, I32, T, P], I32),
+        "vae_frame_attention_workspace": ([T, ctypes.POINTER(SZ)], I32),
+        "vae_frame_attention": ([T, F, P, P, P, P, P, P, T, P, SZ, P], I32),
         "vae_upsample": ([T, B, I32, I32, I32, I32, T, P], I32),
         "vae_tile_split": ([D, ctypes.POINTER(vae_tile_t), I32, ctypes.POINTER(I32)], I32),
         "vae_tile_merge": ([T, ctypes.POINTER(vae_tile_t), D, T, I32, P], I32),
@@ -348,6 +353,32 @@ def vae_groupnorm_apply(x, out_box, groups, mean_rstd, gamma, beta, apply_silu, 
     return y
 
 
+def vae_rmsnorm_silu(x, eps, gamma, beta, apply_silu, y, stream=None):
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    _check(LIB.vae_rmsnorm_silu(ctypes.byref(xd), eps, _ptr(gamma), _ptr(beta), int(apply_silu),
+                                ctypes.byref(yd), _stream(stream)))
+    return y
+
+
+def vae_frame_attention_workspace(x):
+    xd = tensor_desc(x)
+    n = ctypes.c_size_t()
+    _check(LIB.vae_frame_attention_workspace(ctypes.byref(xd), ctypes.byref(n)))
+    return n.value
+
+
+def vae_frame_attention(x, eps, gamma, beta, w_qkv, b_qkv, w_out, b_out, y, ws=None, stream=None):
+    """Single-head attention over each frame's positions, plus x (w_qkv [3C, C], w_out [C, C]
+    bf16 device tensors)."""
+    if ws is None:
+        ws = _workspace(vae_frame_attention_workspace(x), x.device)
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    _check(LIB.vae_frame_attention(ctypes.byref(xd), eps, _ptr(gamma), _ptr(beta), _ptr(w_qkv),
+                                   _ptr(b_qkv), _ptr(w_out), _ptr(b_out), ctypes.byref(yd),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
 def vae_upsample(x, in_box, mode, st, sh, sw, y, stream=None):
     xd, yd = tensor_desc(x), tensor_desc(y)
     _check(LIB.vae_upsample(ctypes.byref(xd), _ref(box(in_box)), mode, st, sh, sw,
@@ -379,7 +410,8 @@ def vae_tile_merge(tile_out, tile, desc, out, flags, stream=None):
 
 
 _OPS = {"conv": VAE_OP_CONV, "res": VAE_OP_RES, "gn_silu": VAE_OP_GN_SILU, "d2s": VAE_OP_D2S,
-        "nearest": VAE_OP_NEAREST}
+        "nearest": VAE_OP_NEAREST, "res_rms": VAE_OP_RES_RMS, "rms_silu": VAE_OP_RMS_SILU,
+        "attn": VAE_OP_ATTN}
 
 
 def layer_descs(plan):
@@ -394,6 +426,12 @@ def layer_descs(plan):
             out.append(vae_layer_desc_t(VAE_OP_RES, op["c"], op["c"], 1, 1, 1, 0, 0))
         elif k == "gn_silu":
             out.append(vae_layer_desc_t(VAE_OP_GN_SILU, 0, 0, 1, 1, 1, 0, 0))
+        elif k == "res_rms":
+            out.append(vae_layer_desc_t(VAE_OP_RES_RMS, op["c"], op["c"], 1, 1, 1, 0, 0))
+        elif k == "rms_silu":
+            out.append(vae_layer_desc_t(VAE_OP_RMS_SILU, 0, 0, 1, 1, 1, 0, 0))
+        elif k == "attn":
+            out.append(vae_layer_desc_t(VAE_OP_ATTN, op["c"], op["c"], 1, 1, 1, 0, 0))
         elif k == "d2s":
             out.append(vae_layer_desc_t(VAE_OP_D2S, 0, 0, op["st"], op["sh"], op["sw"], 0, 0))
         elif k == "nearest":
@@ -407,7 +445,8 @@ class Decoder:
     """vae_decoder_t over a layer plan and device parameter tensors (plan order, two per entry).
 
     ``params`` is a flat list of device tensors or None: conv -> (weight [Cout,3,3,3,Cin], bias),
-    GN -> (gamma, beta); the tensors must outlive the decoder.
+    GN / RMS -> (gamma, beta), attn -> (gamma, beta, w_qkv, b_qkv, w_out, b_out); the tensors must
+    outlive the decoder.
     """
 
     def __init__(self, dtype, latent_channels, groups, eps, plan, params, act_dtype=VAE_DTYPE_F32,

@@ -539,6 +539,65 @@ VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* 
     return VAE_OK;
 }
 
+VAE_API vae_status_t vae_rmsnorm_silu(const vae_tensor_t* x, float eps, const float* gamma,
+                                      const float* beta, int32_t apply_silu, vae_tensor_t* y,
+                                      vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_tensor(x, "x"));
+    VAE_TRY(check_tensor(y, "y"));
+    if (x->dtype == VAE_DTYPE_F16)
+        return fail(VAE_ERR_UNSUPPORTED, "rms norm reads bf16 or fp32 (fp16 is an output only)");
+    if (!rms_shape_supported(x->c))
+        return fail(VAE_ERR_UNSUPPORTED, "rms norm needs C % 8 == 0 and C / 8 dividing 256", 4,
+                    x->c, 8);
+    if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
+    VAE_TRY(check_gn_output(*x, *y));
+    return launch_rms_norm(*x, eps, gamma, beta, apply_silu != 0, *y, as_stream(stream));
+}
+
+vae_status_t check_attention(const vae_tensor_t* x) {
+    VAE_TRY(check_tensor(x, "x"));
+    if (x->dtype != VAE_DTYPE_F32) return fail(VAE_ERR_UNSUPPORTED, "attention reads fp32 x");
+    if (!attention_shape_supported(x->c))
+        return fail(VAE_ERR_UNSUPPORTED, "attention needs C % 32 == 0 and C / 8 dividing 256", 4,
+                    x->c, 32);
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_frame_attention_workspace(const vae_tensor_t* x, size_t* bytes) {
+    clear_error();
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");
+    VAE_TRY(check_attention(x));
+    *bytes = attention_workspace(*x);
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_frame_attention(const vae_tensor_t* x, float eps, const float* gamma,
+                                         const float* beta, const void* w_qkv,
+                                         const float* b_qkv, const void* w_out,
+                                         const float* b_out, vae_tensor_t* y, void* ws,
+                                         size_t ws_bytes, vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_attention(x));
+    VAE_TRY(check_tensor(y, "y"));
+    if (y->dtype != VAE_DTYPE_F32 || !same_grid(*x, *y) || y->c != x->c)
+        return fail(VAE_ERR_INVALID_ARG, "y must be fp32 with x's shape");
+    if (y->data != x->data && overlaps(*x, *y))
+        return fail(VAE_ERR_INVALID_ARG, "y must be x itself or not overlap it");
+    if (!w_qkv || !w_out) return fail(VAE_ERR_INVALID_ARG, "w_qkv or w_out is NULL");
+    if (reinterpret_cast<uintptr_t>(w_qkv) % 16 || reinterpret_cast<uintptr_t>(w_out) % 16)
+        return fail(VAE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+    if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
+    const size_t need = attention_workspace(*x);
+    if (numel(*x) > 0 && (!ws || ws_bytes < need))
+        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
+                    (int64_t)need);
+    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    return launch_frame_attention(*x, eps, gamma, beta, w_qkv, b_qkv, w_out, b_out, *y, ws,
+                                  as_stream(stream));
+}
+
 VAE_API vae_status_t vae_upsample(const vae_tensor_t* x, const vae_box_t* box, int32_t mode,
                                   int32_t st, int32_t sh, int32_t sw, vae_tensor_t* y,
                                   vae_stream_t stream) {

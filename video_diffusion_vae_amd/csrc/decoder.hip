@@ -50,15 +50,25 @@ bool conv_splits(int32_t flags, const vae_layer_desc_t* layers, int n, int i) {
 // Whether layer i is a conv that takes fp16 operands (VAE_DECODE_F16_OPERANDS): a CONV on the
 // matrix cores right after a RES whose convs also run there, or after a GN_SILU, in a plan that
 // keeps fp32 activations (a bf16 stream has nothing finer to hand on). Its producer stores fp16.
+// NEAREST ops between the producer and the conv only copy, so they pass fp16 values through.
 bool conv_f16(int32_t dtype, int32_t act_dtype, int32_t flags, const vae_layer_desc_t* layers,
               int n, int i) {
     if (!(flags & VAE_DECODE_F16_OPERANDS) || dtype != VAE_DTYPE_BF16 ||
         act_dtype != VAE_DTYPE_F32 || i < 1 || i >= n)
         return false;
     const vae_layer_desc_t& l = layers[i];
-    const vae_layer_desc_t& prev = layers[i - 1];
     if (l.op != VAE_OP_CONV || l.cin % 32 || l.cout % 4) return false;
-    return (prev.op == VAE_OP_RES && prev.cin % 32 == 0) || prev.op == VAE_OP_GN_SILU;
+    int j = i - 1;
+    while (j > 0 && layers[j].op == VAE_OP_NEAREST) --j;
+    const vae_layer_desc_t& prev = layers[j];
+    return ((prev.op == VAE_OP_RES || prev.op == VAE_OP_RES_RMS) && prev.cin % 32 == 0) ||
+           prev.op == VAE_OP_GN_SILU || prev.op == VAE_OP_RMS_SILU;
+}
+// The conv that layer i feeds, past any NEAREST ops, or -1.
+int fed_conv(const vae_layer_desc_t* layers, int n, int i) {
+    int j = i + 1;
+    while (j < n && layers[j].op == VAE_OP_NEAREST) ++j;
+    return j < n && layers[j].op == VAE_OP_CONV ? j : -1;
 }
 bool conv_f16(const vae_decoder& d, int i) {
     return conv_f16(d.dtype, d.act_dtype, d.flags, d.layers.data(), (int)d.layers.size(), i);
@@ -69,7 +79,8 @@ bool conv_f16(const vae_decoder& d, int i) {
 // operand dtype.
 int32_t gn_silu_dtype(int32_t dtype, int32_t act_dtype, int32_t flags,
                       const vae_layer_desc_t* layers, int n, int i) {
-    if (conv_f16(dtype, act_dtype, flags, layers, n, i + 1)) return VAE_DTYPE_F16;
+    const int j = fed_conv(layers, n, i);
+    if (j >= 0 && conv_f16(dtype, act_dtype, flags, layers, n, j)) return VAE_DTYPE_F16;
     return conv_splits(flags, layers, n, i + 1) ? act_dtype : dtype;
 }
 int32_t gn_silu_dtype(const vae_decoder& d, int i) {
@@ -82,7 +93,8 @@ int32_t gn_silu_dtype(const vae_decoder& d, int i) {
 // With fp16 operands for the next conv, the block stores fp16 (the one rounding that conv's
 // operand gets).
 int32_t res_out_dtype(const vae_decoder& d, size_t i) {
-    if (conv_f16(d, (int)i + 1)) return VAE_DTYPE_F16;
+    const int j = fed_conv(d.layers.data(), (int)d.layers.size(), (int)i);
+    if (j >= 0 && conv_f16(d, j)) return VAE_DTYPE_F16;
     if (i + 1 < d.layers.size() && d.dtype == VAE_DTYPE_BF16 && d.layers[i].cin % 32 == 0) {
         const vae_layer_desc_t& n = d.layers[i + 1];
         if (n.op == VAE_OP_CONV && !conv_splits(d.flags, d.layers.data(), (int)d.layers.size(),
@@ -106,6 +118,9 @@ int ptrs_for(const vae_layer_desc_t& l) {
         case VAE_OP_CONV: return 2;
         case VAE_OP_RES: return 8;
         case VAE_OP_GN_SILU: return 2;
+        case VAE_OP_RES_RMS: return 8;
+        case VAE_OP_RMS_SILU: return 2;
+        case VAE_OP_ATTN: return 6;
         default: return 0;
     }
 }
@@ -124,10 +139,15 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
                 s.dtype = l.f32_out ? VAE_DTYPE_F32 : d.act_dtype;
                 break;
             case VAE_OP_RES:
+            case VAE_OP_RES_RMS:
                 s.dtype = res_out_dtype(d, i);
                 break;
             case VAE_OP_GN_SILU:
+            case VAE_OP_RMS_SILU:
                 s.dtype = gn_silu_dtype(d, (int)i);
+                break;
+            case VAE_OP_ATTN:
+                s.dtype = VAE_DTYPE_F32;
                 break;
             case VAE_OP_D2S:
                 s.t = l.st * s.t - (l.st - 1);
@@ -186,6 +206,7 @@ struct Req {
     int64_t mr = 0;       // mean/rstd
     int64_t crop = 0;     // latent crop (mode B)
     int64_t tile = 0;     // one decoded tile, fp32 pixels (mode B)
+    int64_t attn = 0;     // frame attention scratch
 };
 
 // Requirements of one run of the plan on an input of shape `in` with patch boxes `boxes`.
@@ -201,6 +222,14 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         const bool last = i + 1 == d.layers.size();
         if (!last) r->act = std::max(r->act, s.bytes());
         if (last && final_in_buffer) r->tile = std::max(r->tile, s.bytes());
+        if (l.op == VAE_OP_RES_RMS || l.op == VAE_OP_RMS_SILU) {
+            Shape g = cur;
+            g.dtype = l.op == VAE_OP_RES_RMS ? d.dtype : gn_silu_dtype(d, (int)i);
+            r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
+        }
+        if (l.op == VAE_OP_ATTN)
+            r->attn = std::max<int64_t>(r->attn,
+                                        (int64_t)attention_workspace(tensor_of(nullptr, cur)));
         if (l.op == VAE_OP_RES || l.op == VAE_OP_GN_SILU) {
             Shape g = cur;
             g.dtype = l.op == VAE_OP_RES ? d.dtype : gn_silu_dtype(d, (int)i);
@@ -238,7 +267,7 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
 }
 
 struct Layout {
-    size_t buf[3], gn, mr, crop, tile, total;
+    size_t buf[3], gn, mr, crop, tile, attn, total;
     int64_t act_bytes;
 };
 
@@ -258,6 +287,8 @@ Layout layout_of(const Req& r) {
     off += align_up((size_t)r.crop, 256);
     L.tile = off;
     off += align_up((size_t)r.tile, 256);
+    L.attn = off;
+    off += align_up((size_t)r.attn, 256);
     L.total = off;
     L.act_bytes = (int64_t)act;
     return L;
@@ -299,6 +330,14 @@ struct Runner {
         const double xb = (double)numel(x) * elem_size(x.dtype);
         const double yb = (double)numel(y) * elem_size(y.dtype);
         return mark(VAE_KIND_GN, layer, 0.0, (fused ? 1.0 : 2.0) * xb + yb);
+    }
+
+    vae_status_t rms(const vae_tensor_t& x, const vae_tensor_t& y, const void* gamma,
+                     const void* beta, int layer) {
+        VAE_TRY(launch_rms_norm(x, d->eps, static_cast<const float*>(gamma),
+                                static_cast<const float*>(beta), true, y, s));
+        return mark(VAE_KIND_RMS, layer, 0.0,
+                    (double)numel(x) * elem_size(x.dtype) + (double)numel(y) * elem_size(y.dtype));
     }
 
     // `wi` indexes d->ptrs: the conv's weight, followed by its bias. With `gn_next` the conv's
@@ -397,6 +436,60 @@ struct Runner {
                 p += 8;
                 cur = y;
                 cur_buf = last ? -2 : b2;
+            } else if (l.op == VAE_OP_RES_RMS) {
+                // x -> RMS1 -> t1 -> conv1 -> t2 -> RMS2 -> t1 -> conv2 (+ x) -> t2
+                const int b1 = free_buf(cur_buf, -1);
+                const int b2 = free_buf(cur_buf, b1);
+                Shape gs = shape_of(cur), as = shape_of(cur);
+                gs.dtype = d->dtype;
+                as.dtype = d->act_dtype;
+                vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
+                stats_ready = false;
+                VAE_TRY(rms(cur, t1, d->ptrs[p], d->ptrs[p + 1], layer));
+                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, false));
+                VAE_TRY(rms(t2, t1, d->ptrs[p + 4], d->ptrs[p + 5], layer));
+                Shape ys = as;
+                ys.dtype = res_out_dtype(*d, li);
+                vae_tensor_t y = last ? final_out : buf(b2, ys);
+                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li)));
+                p += 8;
+                cur = y;
+                cur_buf = last ? -2 : b2;
+            } else if (l.op == VAE_OP_RMS_SILU) {
+                vae_tensor_t y;
+                int nb = cur_buf;
+                Shape gs = shape_of(cur);
+                gs.dtype = gn_silu_dtype(*d, layer);
+                if (last) {
+                    y = final_out;
+                    nb = -2;
+                } else if (cur_buf < 0 || cur.dtype != gs.dtype) {
+                    nb = free_buf(cur_buf, -1);
+                    y = buf(nb, gs);
+                } else {
+                    y = cur;  // in place
+                }
+                stats_ready = false;
+                VAE_TRY(rms(cur, y, d->ptrs[p], d->ptrs[p + 1], layer));
+                p += 2;
+                cur = y;
+                cur_buf = nb;
+            } else if (l.op == VAE_OP_ATTN) {
+                const int nb = free_buf(cur_buf, -1);
+                vae_tensor_t y = last ? final_out : buf(nb, os);
+                stats_ready = false;
+                VAE_TRY(launch_frame_attention(
+                    cur, d->eps, static_cast<const float*>(d->ptrs[p]),
+                    static_cast<const float*>(d->ptrs[p + 1]), d->ptrs[p + 2],
+                    static_cast<const float*>(d->ptrs[p + 3]), d->ptrs[p + 4],
+                    static_cast<const float*>(d->ptrs[p + 5]), y, ws + L.attn, s));
+                const double hw = (double)cur.h * cur.w, pos = (double)positions(cur);
+                const double c = (double)cur.c;
+                VAE_TRY(mark(VAE_KIND_ATTN, layer, 2.0 * pos * c * c * 4.0 + 4.0 * pos * hw * c,
+                             0.0));
+                p += 6;
+                cur = y;
+                cur_buf = last ? -2 : nb;
             } else if (l.op == VAE_OP_GN_SILU) {
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
                 vae_tensor_t y;
@@ -484,7 +577,7 @@ void for_each_conv(const vae_decoder& d, F fn) {
     for (size_t i = 0; i < d.layers.size(); ++i) {
         const vae_layer_desc_t& l = d.layers[i];
         if (l.op == VAE_OP_CONV) fn(p, l.cin, l.cout, conv_f16(d, (int)i));
-        if (l.op == VAE_OP_RES) {
+        if (l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) {
             fn(p + 2, l.cin, l.cin, false);
             fn(p + 6, l.cin, l.cin, false);
         }
@@ -551,6 +644,29 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
                 act = gn_silu_dtype(spec->dtype, spec->act_dtype, spec->flags, spec->layers,
                                     spec->n_layers, i);
                 break;
+            case VAE_OP_RES_RMS:
+                if (l.cin != c) return fail(VAE_ERR_INVALID_ARG, "res width does not chain");
+                if (act != spec->act_dtype)
+                    return fail(VAE_ERR_UNSUPPORTED,
+                                "a residual block input must have the activation dtype");
+                if (!rms_shape_supported(c))
+                    return fail(VAE_ERR_UNSUPPORTED, "rms norm width", 4, c, 8);
+                break;
+            case VAE_OP_RMS_SILU:
+                if (!rms_shape_supported(c))
+                    return fail(VAE_ERR_UNSUPPORTED, "rms norm width", 4, c, 8);
+                act = gn_silu_dtype(spec->dtype, spec->act_dtype, spec->flags, spec->layers,
+                                    spec->n_layers, i);
+                break;
+            case VAE_OP_ATTN:
+                if (l.cin != c) return fail(VAE_ERR_INVALID_ARG, "attention width does not chain");
+                if (spec->dtype != VAE_DTYPE_BF16 || spec->act_dtype != VAE_DTYPE_F32 ||
+                    act != VAE_DTYPE_F32)
+                    return fail(VAE_ERR_UNSUPPORTED,
+                                "attention needs bf16 weights and fp32 activations");
+                if (!attention_shape_supported(c))
+                    return fail(VAE_ERR_UNSUPPORTED, "attention width", 4, c, 32);
+                break;
             case VAE_OP_D2S: {
                 if (l.st < 1 || l.sh < 1 || l.sw < 1)
                     return fail(VAE_ERR_INVALID_ARG, "d2s factors must be >= 1");
@@ -578,8 +694,10 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
         const vae_layer_desc_t& l = spec->layers[i];
         if (l.op == VAE_OP_CONV && !params[p])
             return fail(VAE_ERR_INVALID_ARG, "conv weight pointer is NULL");
-        if (l.op == VAE_OP_RES && (!params[p + 2] || !params[p + 6]))
+        if ((l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) && (!params[p + 2] || !params[p + 6]))
             return fail(VAE_ERR_INVALID_ARG, "res conv weight pointer is NULL");
+        if (l.op == VAE_OP_ATTN && (!params[p + 2] || !params[p + 4]))
+            return fail(VAE_ERR_INVALID_ARG, "attention weight pointer is NULL");
         p += ptrs_for(l);
     }
     vae_decoder* d = new (std::nothrow) vae_decoder();

@@ -58,6 +58,21 @@ vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t grou
                              bool silu, const vae_tensor_t& y, hipStream_t stream);
 bool gn_shape_supported(const vae_tensor_t& x, int32_t groups);
 
+// ---- RMS norm and frame attention (Wan-style decoders) ----
+bool rms_shape_supported(int64_t c);
+// y = x / sqrt(mean_c(x^2) + eps) * gamma + beta (+ SiLU) per position; x bf16/fp32, y any dtype.
+vae_status_t launch_rms_norm(const vae_tensor_t& x, float eps, const float* gamma,
+                             const float* beta, bool silu, const vae_tensor_t& y,
+                             hipStream_t stream);
+bool attention_shape_supported(int64_t c);
+size_t attention_workspace(const vae_tensor_t& x);
+// Single-head attention over each frame's positions plus the residual; fp32 x and y (y may be
+// x); bf16 weights w_qkv [3C][C] and w_out [C][C]; ws of attention_workspace(x) bytes.
+vae_status_t launch_frame_attention(const vae_tensor_t& x, float eps, const float* gamma,
+                                    const float* beta, const void* w_qkv, const float* b_qkv,
+                                    const void* w_out, const float* b_out, const vae_tensor_t& y,
+                                    void* ws, hipStream_t stream);
+
 // ---- upsampling ----
 vae_status_t launch_upsample(const vae_tensor_t& x, const Box& box, int32_t mode, int32_t st,
                              int32_t sh, int32_t sw, const vae_tensor_t& y, hipStream_t stream);

@@ -1,0 +1,115 @@
+// RMS normalisation over the channels of each position (+ SiLU): the norm of Wan-style decoders.
+//
+// y = x / sqrt(mean_c(x^2) + eps) * gamma + beta, then optionally SiLU. The norm reduces over the
+// channels of one position only, so a patch-split decode needs no statistics exchange ("Add tiled
+// VAE parallelism & extended model support", commit messages on the Qwen-Image / Wan adapters and on
+// the HunyuanVideo 1.5 encoder: RMS norms that reduce over channels need nothing sharded).
+//
+// NDHWC puts a position's C channels in one contiguous run. Each thread owns 8 consecutive
+// channels of one position (one 16-byte load for bf16, two for fp32); the C / 8 threads of a
+// position sum their squares with lane shuffles, and through LDS when a position spans two waves
+// (C = 1024 or 2048). A block of 256 threads covers 256 / (C / 8) positions per step.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace vae {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBlocks = 8192;
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict__ x,
+                                                            TO* __restrict__ y, int64_t positions,
+                                                            int32_t C, float eps,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta,
+                                                            int32_t silu) {
+    __shared__ float part[kThreads / 64];                  // one partial per wave
+    const int tpp = C / 8;                                 // threads per position
+    const int ppb = kThreads / tpp;                        // positions per block step
+    const int tid = threadIdx.x;
+    const int slot = tid / tpp, c0 = (tid % tpp) * 8;
+    const int lane = tid & 63, wave = tid >> 6;
+    float sc[8], sh[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        sc[k] = gamma ? gamma[c0 + k] : 1.0f;
+        sh[k] = beta ? beta[c0 + k] : 0.0f;
+    }
+    for (int64_t p0 = (int64_t)blockIdx.x * ppb; p0 < positions; p0 += (int64_t)gridDim.x * ppb) {
+        const int64_t p = p0 + slot;
+        const bool valid = p < positions;
+        float v[8];
+        const TI* src = x + (valid ? p : 0) * C + c0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = Elem<TI>::load(src + k);
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss = fmaf(v[k], v[k], ss);
+        // sum over the position's threads: within the wave, then across the two waves of a
+        // position when tpp = 128 or 256
+        const int span = tpp < 64 ? tpp : 64;
+        for (int off = 1; off < span; off <<= 1) ss += __shfl_xor(ss, off);
+        if (tpp > 64) {
+            if (lane == 0) part[wave] = ss;
+            __syncthreads();
+            const int w0 = (tid / tpp) * (tpp / 64);
+            float t = 0.0f;
+            for (int w = 0; w < tpp / 64; ++w) t += part[w0 + w];
+            ss = t;
+            __syncthreads();
+        }
+        const float r = 1.0f / sqrtf(ss / (float)C + eps);
+        if (valid) {
+            TO* dst = y + p * C + c0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float z = fmaf(v[k] * r, sc[k], sh[k]);
+                if (silu) z = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+                Elem<TO>::store(dst + k, z);
+            }
+        }
+    }
+}
+
+template <typename TI, typename TO>
+void rms_launch(const vae_tensor_t& x, float eps, const float* gamma, const float* beta, bool silu,
+                const vae_tensor_t& y, hipStream_t stream) {
+    const int64_t positions = vae::positions(x);
+    const int ppb = kThreads / (int)(x.c / 8);
+    const int64_t blocks = std::min<int64_t>(ceil_div(positions, ppb), kMaxBlocks);
+    hipLaunchKernelGGL((rms_norm_kernel<TI, TO>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       static_cast<const TI*>(x.data), static_cast<TO*>(y.data), positions,
+                       (int32_t)x.c, eps, gamma, beta, (int32_t)silu);
+}
+
+template <typename TI>
+void rms_out(const vae_tensor_t& x, float eps, const float* gamma, const float* beta, bool silu,
+             const vae_tensor_t& y, hipStream_t stream) {
+    if (y.dtype == VAE_DTYPE_F32) rms_launch<TI, float>(x, eps, gamma, beta, silu, y, stream);
+    else if (y.dtype == VAE_DTYPE_F16) rms_launch<TI, _Float16>(x, eps, gamma, beta, silu, y, stream);
+    else rms_launch<TI, uint16_t>(x, eps, gamma, beta, silu, y, stream);
+}
+
+}  // namespace
+
+bool rms_shape_supported(int64_t c) {
+    return c >= 8 && c % 8 == 0 && c / 8 <= kThreads && kThreads % (c / 8) == 0;
+}
+
+vae_status_t launch_rms_norm(const vae_tensor_t& x, float eps, const float* gamma,
+                             const float* beta, bool silu, const vae_tensor_t& y,
+                             hipStream_t stream) {
+    if (numel(x) == 0) return VAE_OK;
+    if (!rms_shape_supported(x.c))
+        return fail(VAE_ERR_UNSUPPORTED, "rms norm needs C % 8 == 0 and C / 8 dividing 256", 4,
+                    x.c, 8);
+    if (x.dtype == VAE_DTYPE_F32) rms_out<float>(x, eps, gamma, beta, silu, y, stream);
+    else rms_out<uint16_t>(x, eps, gamma, beta, silu, y, stream);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+}  // namespace vae

@@ -26,6 +26,24 @@ def conv_weight_layout(w, dtype, device):
     return t.to(device=device, dtype=dtype)
 
 
+def latent_channels(spec: dict) -> int:
+    """Channels of the latent the GPU decoder takes: the plan's, rounded up to a multiple of 32
+    for a bf16 plan, so that the first conv runs on the matrix cores (48 -> 64 for the Wan-shaped
+    plan). The extra channels are zeros in the latent and in the first conv's weights, so the
+    result is the same sum."""
+    c = spec["latent"][1]
+    return (c + 31) // 32 * 32 if spec["dtype"] == "bf16" else c
+
+
+def pad_latent(z, spec: dict):
+    """NDHWC host latent padded with zero channels to latent_channels(spec)."""
+    c = latent_channels(spec)
+    if z.shape[-1] == c:
+        return z
+    pad = np.zeros(z.shape[:-1] + (c - z.shape[-1],), dtype=z.dtype)
+    return np.concatenate([z, pad], axis=-1)
+
+
 def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", operands="f16",
                    packed=True):
     """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
@@ -38,19 +56,33 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", ope
     """
     import torch
     tdt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+    f32 = lambda a: torch.as_tensor(np.asarray(a, np.float32)).to(device)
+    lc = latent_channels(spec)
+    layers = [dict(op) for op in spec["layers"]]
     flat = []
-    for p in params:
+    for k, p in enumerate(params):
         if p["kind"] == "conv":
-            flat.append(conv_weight_layout(p["w"], tdt, device))
-            flat.append(torch.as_tensor(np.asarray(p["b"], np.float32)).to(device))
+            w = np.asarray(p["w"], np.float32)
+            if k == 0 and w.shape[1] < lc:       # zero weights for the zero latent channels
+                w = np.concatenate([w, np.zeros((w.shape[0], lc - w.shape[1]) + w.shape[2:],
+                                                np.float32)], axis=1)
+                layers[0]["cin"] = lc
+            flat.append(conv_weight_layout(w, tdt, device))
+            flat.append(f32(p["b"]))
+        elif p["kind"] == "attn":
+            flat += [f32(p["gamma"]), f32(p["beta"]),
+                     torch.as_tensor(np.asarray(p["w_qkv"], np.float32)).to(device, tdt),
+                     f32(p["b_qkv"]),
+                     torch.as_tensor(np.asarray(p["w_out"], np.float32)).to(device, tdt),
+                     f32(p["b_out"])]
         else:
-            flat.append(torch.as_tensor(np.asarray(p["gamma"], np.float32)).to(device))
-            flat.append(torch.as_tensor(np.asarray(p["beta"], np.float32)).to(device))
+            flat.append(f32(p["gamma"]))
+            flat.append(f32(p["beta"]))
     code = VAE_DTYPE_BF16 if spec["dtype"] == "bf16" else VAE_DTYPE_F32
     act = VAE_DTYPE_BF16 if act_dtype == "bf16" else VAE_DTYPE_F32
     flags = OPERAND_FLAGS[operands] if code == VAE_DTYPE_BF16 else 0
-    dec = Decoder(code, spec["latent"][1], spec["groups"], spec["eps"], spec["layers"], flat,
-                  act_dtype=act, flags=flags)
+    dec = Decoder(code, lc, spec["groups"], spec["eps"], layers, flat, act_dtype=act,
+                  flags=flags)
     if packed:
         dec.pack_weights(device)
     return dec
