@@ -1,9 +1,12 @@
 """Benchmark: tiled causal-3D VAE decode at 720p on one MI355X.
 
-One step is one full decode of the LTX-2-shaped plan:
+One step is one full decode of the LTX-2-shaped plan (the default, ``--workload ltx2``):
 - input: seeded latent [1,128,16,22,40], random-init bf16 weights;
 - output: [1,3,121,704,1280] fp32 (109,035,520 pixel-frames);
 - default tiling: 1x4 patch-halo (mode A); ``--mode overlap`` times the 2x3 overlap-blend decode.
+``--workload wan`` times the Wan2.2-TI2V-5B-shaped plan instead: latent [1,48,21,44,80] (padded
+with zero channels to 64 for the matrix cores) -> [1,3,81,704,1280] (72,990,720 pixel-frames),
+with RMS-norm residual blocks and a mid-block frame attention.
 
 Inputs and weights are resident in HBM before the timed region. Exactly --steps decodes are timed
 between two device synchronisations. HIP events recorded by the library on the decode's own stream
@@ -62,13 +65,40 @@ def conv_flops(spec, latent_shape):
         k = op["op"]
         if k == "conv":
             total += 2 * 27 * op["cin"] * op["cout"] * n * t * h * w
-        elif k == "res":
+        elif k in ("res", "res_rms"):
             total += 2 * (2 * 27 * op["c"] * op["c"] * n * t * h * w)
         elif k == "d2s":
             t, h, w = op["st"] * t - (op["st"] - 1), h * op["sh"], w * op["sw"]
         elif k == "nearest":
             h, w = h * op["sh"], w * op["sw"]
     return total
+
+
+def output_shape(spec, latent_shape):
+    """[N, T, H, W, C] of the decoded video for an NDHWC latent shape, following the plan."""
+    n, t, h, w, c = latent_shape
+    for op in spec["layers"]:
+        k = op["op"]
+        if k == "conv":
+            c = op["cout"]
+        elif k == "d2s":
+            t, h, w = op["st"] * t - (op["st"] - 1), h * op["sh"], w * op["sw"]
+            c //= op["st"] * op["sh"] * op["sw"]
+        elif k == "nearest":
+            h, w = h * op["sh"], w * op["sw"]
+    return (n, t, h, w, c)
+
+
+WORKLOADS = {
+    # name: (plan, patch grid of the patch-halo mode, tile grid name of the overlap mode)
+    "ltx2": ("LTX2_720P", (1, 4), "2x3"),
+    "wan": ("WAN_720P", (1, 4), "2x3"),
+}
+
+
+def workload_name(kind, mode):
+    prefix = {"ltx2": "ltx2_720p", "wan": "wan2.2_ti2v_5b_720p"}[kind]
+    return prefix + ("_decode_patch_halo_1x4" if mode == "patch" else "_decode_overlap_blend_2x3")
 
 
 def conv_source_digest():
@@ -149,9 +179,49 @@ def calibrate_copy(mib, repeats=3):
     print(json.dumps({"copy_mib": mib, "repeats": repeats, "kernel": COPY_KERNEL}), flush=True)
 
 
+def standalone_passes(v, dev, reps=5):
+    """HBM rates of the streaming passes as standalone library calls at the 720p decode's shapes
+    (inside the decode the depth-to-space runs in the conv epilogue, and the merge only in the
+    overlap-blend mode). Timed with events on the stream the calls are enqueued on."""
+    import torch
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, nbytes):
+        fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        e.synchronize()
+        ms = s.elapsed_time(e) / reps
+        gbs = nbytes / (ms / 1000.0) / 1e9
+        return {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                "bytes": nbytes}
+
+    # depth-to-space of the largest upsampling conv's output: fp32 [1,61,88,160,1024] -> S3
+    x = torch.zeros((1, 61, 88, 160, 1024), dtype=torch.float32, device=dev)
+    y = torch.empty((1, 121, 176, 320, 128), dtype=torch.float32, device=dev)
+    out["upsample_d2s_f32_s2_to_s3"] = timed(
+        lambda: v.vae_upsample(x, None, v.VAE_UPSAMPLE_D2S, 2, 2, 2, y),
+        x.numel() * 4 + y.numel() * 4)
+    del x
+    # GroupNorm apply + SiLU at S3 (fp32 in, bf16 operand out), statistics given
+    mr = torch.zeros((1, 32, 2), dtype=torch.float32, device=dev)
+    mr[..., 1] = 1.0
+    yb = torch.empty(y.shape, dtype=torch.bfloat16, device=dev)
+    out["gn_apply_silu_f32_to_bf16_s3"] = timed(
+        lambda: v.vae_groupnorm_apply(y, None, 32, mr, None, None, True, yb),
+        y.numel() * 4 + yb.numel() * 2)
+    del y, yb
+    torch.cuda.synchronize(dev)
+    return out
+
+
 def cpu_baseline(spec, params, frames=2):
     """The oracle, as it stands, on a bounded sample: the full 720p spatial plan on `frames`
-    latent frames, scaled by conv flops to the 16-frame decode."""
+    latent frames, scaled by conv flops to the full decode."""
     import threadpoolctl
     import oracle
     import vae_synth
@@ -161,16 +231,19 @@ def cpu_baseline(spec, params, frames=2):
     t0 = time.perf_counter()
     out = oracle.decode(spec, z, params)
     sample_s = time.perf_counter() - t0
-    full_shape = (1, 16, 22, 40, 128)
+    n, c, t, h, w = spec["latent"]
+    full_shape = (n, t, h, w, c)
     scale = conv_flops(spec, full_shape) / conv_flops(spec, z.shape)
     est_full_s = sample_s * scale
-    px = 121 * 704 * 1280
+    _, to, ho, wo, _ = output_shape(spec, full_shape)
+    px = to * ho * wo
     return {
         "value": px / est_full_s / 1e6, "unit": "Mpx-frames/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle fp64 decode of latent [1,128,{frames},22,40] -> {list(out.shape)} "
-                   f"in {sample_s:.1f} s, scaled by conv flops x{scale:.1f} to the 16-frame "
-                   f"720p decode (est. {est_full_s:.0f} s); os.cpu_count()={os.cpu_count()}"),
+        "sample": (f"oracle fp64 decode of latent [{n},{c},{frames},{h},{w}] -> "
+                   f"{list(out.shape)} in {sample_s:.1f} s, scaled by conv flops x{scale:.1f} to "
+                   f"the {t}-frame 720p decode (est. {est_full_s:.0f} s); "
+                   f"os.cpu_count()={os.cpu_count()}"),
     }
 
 
@@ -180,10 +253,13 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--mode", choices=["patch", "overlap"], default="patch")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="ltx2",
+                    help="ltx2: the LTX-2-shaped decode (the headline); wan: the Wan2.2-shaped one")
     ap.add_argument("--operands", choices=["f16", "split", "bf16"], default="f16",
                     help="operands of the convs that read an fp32 activation (up-convs, conv_out)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=2)
+    ap.add_argument("--cpu-frames", type=int, default=0,
+                    help="latent frames of the oracle's sample (default 2 for ltx2, 1 for wan)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB")
     ap.add_argument("--traffic-record", nargs=4,
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"))
@@ -192,8 +268,7 @@ def main():
     ap.add_argument("--out")
     args = ap.parse_args()
     if args.traffic_record:
-        workload = ("ltx2_720p_decode_patch_halo_1x4" if args.mode == "patch"
-                    else "ltx2_720p_decode_overlap_blend_2x3")
+        workload = workload_name(args.workload, args.mode)
         write_traffic_record(*args.traffic_record, args.copy_mib, args.decodes, workload,
                              args.out or TRAFFIC_RECORD)
         return
@@ -210,22 +285,24 @@ def main():
     import vae_synth
     import video_diffusion_vae_amd as v
 
-    spec = vae_synth.LTX2_720P
+    plan_name, patch_grid, _ = WORKLOADS[args.workload]
+    spec = getattr(vae_synth, plan_name)
     t_setup = time.perf_counter()
     z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))
+    out_shape = output_shape(spec, z.shape)
     params = vae_synth.decoder_params(spec)
     dev = torch.device("cuda:0")
     dec = v.upload_decoder(spec, params, dev, operands=args.operands)
-    zd = torch.as_tensor(z).to(device=dev, dtype=torch.bfloat16)
+    zp = v.pad_latent(z, spec)            # zero channels up to a multiple of 32 (48 -> 64)
+    zd = torch.as_tensor(zp).to(device=dev, dtype=torch.bfloat16)
+    workload = workload_name(args.workload, args.mode)
     if args.mode == "patch":
-        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 4))
-        workload = "ltx2_720p_decode_patch_halo_1x4"
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, spec["scale"], patches=patch_grid)
     else:
-        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, z.shape, spec["scale"],
+        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, zp.shape, spec["scale"],
                              tile=spec["overlap_tile"], stride=spec["overlap_stride"])
-        workload = "ltx2_720p_decode_overlap_blend_2x3"
     ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device=dev)
-    out = torch.empty((1, 121, 704, 1280, 3), dtype=torch.float32, device=dev)
+    out = torch.empty(out_shape, dtype=torch.float32, device=dev)
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s, workspace "
         f"{ws.numel() / 2**30:.2f} GiB")
 
@@ -248,7 +325,7 @@ def main():
     elapsed = time.perf_counter() - t0
     dec.set_timing(False)
     ms = elapsed * 1000.0 / args.steps
-    px = 121 * 704 * 1280
+    px = out_shape[1] * out_shape[2] * out_shape[3]
     value = px / (ms / 1000.0) / 1e6
     log(f"[bench] {args.steps} timed steps: {ms:.2f} ms/step, {value:.1f} Mpx-frames/s")
 
@@ -292,10 +369,15 @@ def main():
               "step_ms_p90": round(pct(step_s, 90), 3),
               "host_enqueue_ms_p50": round(pct(enqueue_s, 50), 3)}
 
+    passes = standalone_passes(v, dev) if args.workload == "ltx2" else None
+    for name, p in (passes or {}).items():
+        log(f"  pass {name}: {json.dumps(p)}")
+
     baseline = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on its bounded sample ...")
-        baseline = cpu_baseline(spec, params, args.cpu_frames)
+        frames = args.cpu_frames or (2 if args.workload == "ltx2" else 1)
+        baseline = cpu_baseline(spec, params, frames)
         log(f"[bench] cpu baseline: {baseline}")
 
     line = {
@@ -303,12 +385,16 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded latent, random-init weights)",
-        "config": {"workload": workload, "latent": [1, 128, 16, 22, 40],
-                   "output": [1, 3, 121, 704, 1280], "parallelism": "none (1 GPU)",
+        "config": {"workload": workload, "latent": list(spec["latent"]),
+                   "output": [out_shape[0], out_shape[4]] + list(out_shape[1:4]),
+                   "parallelism": "none (1 GPU)",
                    "operands": OPERANDS[args.operands],
-                   "activations": "fp32 between ops, bf16 GroupNorm outputs inside res blocks",
+                   "activations": "fp32 between ops, bf16 norm outputs inside res blocks",
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
-        "roofline": roofline, "kernels": summary, "timing": timing, "cpu_baseline": baseline,
+        "roofline": roofline, "kernels": summary, "standalone_passes": passes, "timing": timing,
+        "attention_tflop_per_step": (round(kinds["attn"]["flops"] / args.steps / 1e12, 3)
+                                     if "attn" in kinds else None),
+        "cpu_baseline": baseline,
     }
     print(json.dumps(line), flush=True)
 
