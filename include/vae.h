@@ -14,7 +14,7 @@
  *    Conv weights are [Cout][kt=3][kh=3][kw=3][Cin]. Bias, gamma and beta are fp32 vectors.
  *  - Dtypes: VAE_DTYPE_BF16 (bfloat16 storage, fp32 arithmetic) or VAE_DTYPE_F32.
  *    VAE_DTYPE_F16 (IEEE binary16 storage, 11 significant bits) is accepted only where a call
- *    says so: as a conv input on the MFMA path, as the conv output of a bf16 input, as a
+ *    says so: as a conv input on the MFMA path, as the conv output of a 2-byte input, as a
  *    GroupNorm output, and by vae_upsample (a copy). It is the operand hand-off of convs whose
  *    input needs more than bf16's 8 significant bits (see vae_conv3d_causal).
  *  - Ownership: the caller owns every buffer. Device buffers are passed as raw device pointers;
@@ -111,8 +111,8 @@ VAE_API int32_t vae_version(void);
  *  residual: tensor of y's shape and dtype added to the result, or NULL. It may alias y. When y
  *            is bf16 or fp16 the residual may also be fp32 (a residual stream kept in fp32; the
  *            sum is rounded once, at the store).
- *  y: [N,T,H,W,Cout] output, bf16 or fp32; fp16 when x is bf16 (MFMA path). It must not
- *     overlap x.
+ *  y: [N,T,H,W,Cout] output, bf16 or fp32; fp16 when x is bf16 or fp16 (MFMA path). It must
+ *     not overlap x.
  *  flags: 0, or a combination of VAE_CONV_SPLIT_FP32 and one of
  *         VAE_CONV_PACKED_WEIGHTS (weight is the fragment-packed copy written by
  *         vae_conv_weight_pack; MFMA path, bf16 or fp32 x) or
@@ -396,8 +396,9 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * unless its no_split is set. A standalone GN_SILU followed by a splitting CONV writes fp32 for
  * it. The convs inside residual blocks keep one rounding of their GroupNorm operand.
  * VAE_DECODE_F16_OPERANDS (bf16 plans with fp32 activations; not with the split flag) gives
- * those same convs, i.e. every CONV that follows a RES, RES_RMS, GN_SILU or RMS_SILU (possibly
- * through NEAREST ops, which copy), fp16 operands instead: the producing op stores its output in
+ * those same convs, i.e. every CONV that follows a RES, RES_RMS, GN_SILU, RMS_SILU, or a CONV
+ * whose own input is bf16 or fp16 (possibly through its fused D2S and NEAREST ops, which copy),
+ * fp16 operands instead: the producing op stores its output in
  * fp16 (one rounding to 11 significant bits) and the conv runs at the bf16 rate
  * (vae_conv3d_causal with an fp16 x). no_split does not apply to it. Activations must stay below
  * 65504 in magnitude there.

@@ -548,26 +548,29 @@ def test_conv3d_f16_input(v, case):
 
 
 F16_OUT_CASES = [
-    # (N, T, H, W), Cin, Cout, residual dtype (None = no residual)
-    ((1, 3, 9, 17), 64, 128, "f32"),        # direct epilogue, fp32 residual stream
-    ((1, 4, 8, 16), 32, 64, "f16"),
-    ((2, 2, 8, 16), 32, 48, "f32"),         # staged epilogue
-    ((1, 2, 5, 9), 128, 256, None),
+    # (N, T, H, W), Cin, Cout, residual dtype (None = no residual), input dtype
+    ((1, 3, 9, 17), 64, 128, "f32", "bf16"),   # direct epilogue, fp32 residual stream
+    ((1, 4, 8, 16), 32, 64, "f16", "bf16"),
+    ((2, 2, 8, 16), 32, 48, "f32", "bf16"),    # staged epilogue
+    ((1, 2, 5, 9), 128, 256, None, "bf16"),
+    ((1, 3, 8, 16), 64, 128, None, "f16"),     # fp16 in, fp16 out (a conv feeding a conv)
 ]
 
 
 @pytest.mark.parametrize("case", F16_OUT_CASES)
 def test_conv3d_f16_output_handoff(v, case):
-    """A bf16-input conv that stores fp16 (the operand hand-off to an fp16-input conv), with an
-    fp32 or fp16 residual: one nearest-even rounding of the fp32 sum."""
+    """A conv that stores fp16 (the operand hand-off to an fp16-input conv), with an fp32 or fp16
+    residual: one nearest-even rounding of the fp32 sum."""
     import torch
-    (n, t, h, w), cin, cout, rdt = case
+    (n, t, h, w), cin, cout, rdt, idt = case
     x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", 90 + F16_OUT_CASES.index(case))
+    if idt == "f16":
+        x = round_f16(x + ndhwc(vae_synth.normal((n, cin, t, h, w), [17, cin], scale=1e-3)))
     if rdt == "f16":
         r = round_f16(r)
     ref = oracle.causal_conv3d(x, wt, b) + (r if rdt else 0.0)
     y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=torch.float16)
-    v.vae_conv3d_causal(dev(x, "bf16"), v.conv_weight_layout(wt, torch.bfloat16, "cuda"),
+    v.vae_conv3d_causal(dev(x, idt), v.conv_weight_layout(wt, torch.bfloat16, "cuda"),
                         torch.as_tensor(b, dtype=torch.float32, device="cuda"),
                         dev(r, rdt) if rdt else None, y)
     torch.cuda.synchronize()
@@ -590,8 +593,9 @@ def test_conv3d_f16_argument_rules(v):
         v.vae_conv3d_causal(xb, v.vae_conv_weight_pack_f16(w).view(torch.bfloat16), None, None, y,
                             flags=v.VAE_CONV_PACKED_F16_WEIGHTS)
     assert e.value.status == v.VAE_ERR_INVALID_ARG
-    with pytest.raises(v.VaeError) as e:        # an fp16 output needs a bf16 input
-        v.vae_conv3d_causal(x16, w, None, None, y16)
+    x32 = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.float32)
+    with pytest.raises(v.VaeError) as e:        # an fp16 output needs a 2-byte input
+        v.vae_conv3d_causal(x32, w, None, None, y16)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
     x20 = torch.zeros((1, 2, 4, 4, 20), device="cuda", dtype=torch.float16)
     with pytest.raises(v.VaeError) as e:        # fp16 needs the MFMA path (Cin % 32)

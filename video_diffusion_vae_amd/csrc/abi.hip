@@ -245,8 +245,8 @@ vae_status_t check_conv_dtypes(const vae_tensor_t& x, const vae_tensor_t& y,
             return fail(VAE_ERR_UNSUPPORTED,
                         "fp16 tensors need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x.c,
                         32);
-        if (y.dtype == VAE_DTYPE_F16 && x.dtype != VAE_DTYPE_BF16)
-            return fail(VAE_ERR_UNSUPPORTED, "an fp16 y needs a bf16 x");
+        if (y.dtype == VAE_DTYPE_F16 && x.dtype == VAE_DTYPE_F32)
+            return fail(VAE_ERR_UNSUPPORTED, "an fp16 y needs a bf16 or fp16 x");
     }
     if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && x.dtype != VAE_DTYPE_F16)
         return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 x");

@@ -17,7 +17,8 @@
 // Every product is one batched "NT" GEMM on the matrix cores: C[b][m][n] = alpha *
 // sum_k A[b][m][k] B[b][n][k] (+ bias, + residual), A and B both K-contiguous, which is what
 // channels-last activations and [out][in] weights already are. 128 x 128 tiles, 4 waves of 64 x 64
-// (2 x 2 MFMA 32x32x16 tiles each), K in steps of 32 through two LDS buffers. Rows past M or N
+// (2 x 2 MFMA 32x32x16 tiles each), K in steps of 64 through two LDS buffers: the next step's
+// global loads are in flight while the 16 MFMAs per wave of the current one run. Rows past M or N
 // read a valid row and are never stored; K elements past K are zero-filled in LDS.
 #include <algorithm>
 #include <cmath>
@@ -32,8 +33,10 @@ using mfma::f32x16_t;
 using mfma::mfma_step;
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kPitch = kBK + 8;     // halves per LDS row (80 bytes): conflict-free 16-byte reads
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kPitch = kBK + 8;     // halves per LDS row (144 bytes, an odd number of 16-byte
+                                    // units): conflict-free 16-byte fragment reads
+constexpr int kUnits = kBM * kBK / 8 / kThreads;   // 16-byte units per thread per operand
 
 struct GemmArgs {
     const uint16_t* a;   // 2-byte operands (bf16 or fp16 bits)
@@ -59,13 +62,13 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs g) {
     const uint16_t* A = g.a + (int64_t)bz * g.sa;
     const uint16_t* B = g.b + (int64_t)bz * g.sb;
 
-    // staging: each thread moves two 16-byte units of A and two of B per K step
-    uint4 ra[2], rb[2];
+    // staging: each thread moves kUnits 16-byte units of A and of B per K step
+    uint4 ra[kUnits], rb[kUnits];
     auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kUnits; ++i) {
             const int u = tid + i * kThreads;
-            const int row = u >> 2, kc = (u & 3) * 8;
+            const int row = u / (kBK / 8), kc = (u % (kBK / 8)) * 8;
             const int k = k0 + kc;
             const int ma = std::min(m0 + row, g.M - 1), nb = std::min(n0 + row, g.N - 1);
             uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
@@ -73,9 +76,15 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs g) {
                 va = *reinterpret_cast<const uint4*>(A + (int64_t)ma * g.lda + k);
                 vb = *reinterpret_cast<const uint4*>(B + (int64_t)nb * g.ldb + k);
                 if (k + 8 > g.K) {   // a partial unit at the end of K: zero the tail
-                    uint16_t* pa = reinterpret_cast<uint16_t*>(&va);
-                    uint16_t* pb = reinterpret_cast<uint16_t*>(&vb);
-                    for (int e = g.K - k; e < 8; ++e) pa[e] = pb[e] = 0;
+                    // per 32-bit word, keep the halves whose k is inside K (static indices only,
+                    // so the unit stays in registers)
+                    auto keep = [&](int e) {
+                        return (k + e < g.K ? 0xffffu : 0u) |
+                               (k + e + 1 < g.K ? 0xffff0000u : 0u);
+                    };
+                    const uint32_t m0 = keep(0), m1 = keep(2), m2 = keep(4), m3 = keep(6);
+                    va.x &= m0; va.y &= m1; va.z &= m2; va.w &= m3;
+                    vb.x &= m0; vb.y &= m1; vb.z &= m2; vb.w &= m3;
                 }
             }
             ra[i] = va;
@@ -84,9 +93,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs g) {
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kUnits; ++i) {
             const int u = tid + i * kThreads;
-            const int row = u >> 2, kc = (u & 3) * 8;
+            const int row = u / (kBK / 8), kc = (u % (kBK / 8)) * 8;
             *reinterpret_cast<uint4*>(&As[buf][row * kPitch + kc]) = ra[i];
             *reinterpret_cast<uint4*>(&Bs[buf][row * kPitch + kc]) = rb[i];
         }
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt_kernel(GemmArgs g) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load((kt + 1) * kBK);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < kBK / 16; ++kk) {
             bf16x8_t af[2], bfr[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {

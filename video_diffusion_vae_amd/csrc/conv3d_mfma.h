@@ -1018,12 +1018,12 @@ vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bia
     if (y.dtype == VAE_DTYPE_F32)
         return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
     if (y.dtype == VAE_DTYPE_F16) {
-        // fp16 outputs are the operand hand-off of a bf16-input conv
-        if constexpr (std::is_same<TI, uint16_t>::value)
+        // fp16 outputs are the operand hand-off to an fp16-input conv, from a 2-byte input
+        if constexpr (sizeof(TI) == 2)
             return run_mfma<NT, TI, _Float16, SPLIT>(x, w, bias, residual, y, box, packed, fz,
                                                      stream);
         else
-            return fail(VAE_ERR_UNSUPPORTED, "conv3d: an fp16 output needs a bf16 input");
+            return fail(VAE_ERR_UNSUPPORTED, "conv3d: an fp16 output needs a bf16 or fp16 input");
     }
     return run_mfma<NT, TI, uint16_t, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
 }

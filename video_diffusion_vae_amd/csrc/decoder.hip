@@ -60,9 +60,24 @@ bool conv_f16(int32_t dtype, int32_t act_dtype, int32_t flags, const vae_layer_d
     if (l.op != VAE_OP_CONV || l.cin % 32 || l.cout % 4) return false;
     int j = i - 1;
     while (j > 0 && layers[j].op == VAE_OP_NEAREST) --j;
+    if (j > 0 && layers[j].op == VAE_OP_D2S) --j;       // the d2s its producing conv writes
     const vae_layer_desc_t& prev = layers[j];
+    if (prev.op == VAE_OP_CONV)
+        // a conv stores fp16 from a 2-byte input: the latent (plan dtype) or fp16 operands
+        return !prev.f32_out && prev.cin % 32 == 0 && prev.cout % 4 == 0 &&
+               (j == 0 || conv_f16(dtype, act_dtype, flags, layers, n, j));
     return ((prev.op == VAE_OP_RES || prev.op == VAE_OP_RES_RMS) && prev.cin % 32 == 0) ||
            prev.op == VAE_OP_GN_SILU || prev.op == VAE_OP_RMS_SILU;
+}
+// Whether the CONV at layer i stores fp16 for an fp16-operand conv it feeds (through its d2s and
+// NEAREST copies).
+bool conv_out_f16(int32_t dtype, int32_t act_dtype, int32_t flags,
+                  const vae_layer_desc_t* layers, int n, int i) {
+    int j = i + 1;
+    if (j < n && layers[j].op == VAE_OP_D2S) ++j;
+    while (j < n && layers[j].op == VAE_OP_NEAREST) ++j;
+    return j < n && layers[j].op == VAE_OP_CONV &&
+           conv_f16(dtype, act_dtype, flags, layers, n, j);
 }
 // The conv that layer i feeds, past any NEAREST ops, or -1.
 int fed_conv(const vae_layer_desc_t* layers, int n, int i) {
@@ -136,7 +151,11 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
         switch (l.op) {
             case VAE_OP_CONV:
                 s.c = l.cout;
-                s.dtype = l.f32_out ? VAE_DTYPE_F32 : d.act_dtype;
+                s.dtype = l.f32_out ? VAE_DTYPE_F32
+                          : conv_out_f16(d.dtype, d.act_dtype, d.flags, d.layers.data(),
+                                         (int)d.layers.size(), (int)i)
+                              ? VAE_DTYPE_F16
+                              : d.act_dtype;
                 break;
             case VAE_OP_RES:
             case VAE_OP_RES_RMS:
