@@ -164,3 +164,15 @@ def test_wan_shaped_decode_is_deterministic(v):
     import torch
     a, b = _decode(v, "wan_tiny", "patch", (2, 2), repeat=2)
     assert torch.equal(a, b)
+
+
+def test_wan_720p_one_frame_every_value(v):
+    """The full-width Wan-shaped 720p plan on one latent frame ([1,48,1,44,80] ->
+    [1,1,704,1280,3]) in 1 x 4 width patches: the attention gathers all 3520 positions of the
+    frame, and every output value is compared with the oracle's whole decode (the overlap mode
+    is covered at the small sizes above; its oracle at this size takes over a minute)."""
+    got = host(_decode(v, "wan_720p_1f", "patch", (1, 4)))
+    ref = _oracle("wan_720p_1f", "patch")
+    assert got.shape == (1, 1, 704, 1280, 3)
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
