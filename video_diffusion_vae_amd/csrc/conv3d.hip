@@ -20,6 +20,10 @@ VAE_MFMA_EXTERN(64, float, false)
 VAE_MFMA_EXTERN(64, float, true)
 VAE_MFMA_EXTERN(128, _Float16, false)
 VAE_MFMA_EXTERN(64, _Float16, false)
+VAE_MFMA_EXTERN(32, uint16_t, false)
+VAE_MFMA_EXTERN(32, float, false)
+VAE_MFMA_EXTERN(32, float, true)
+VAE_MFMA_EXTERN(32, _Float16, false)
 #undef VAE_MFMA_EXTERN
 }  // namespace mfma
 
@@ -161,7 +165,7 @@ int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, c
         case kBlk4x4x16: tb = 4; hb = 4; wb = 16; break;
         default: break;
     }
-    const int wm = cout >= 128 ? wave_rows<128>() : wave_rows<64>();
+    const int wm = cout >= 128 ? wave_rows<128>() : cout > 32 ? wave_rows<64>() : wave_rows<32>();
     return k * ceil_div(box.bt(), tb) * ceil_div(box.bh(), hb) * ceil_div(box.bw(), wb) * wm;
 }
 
@@ -205,9 +209,12 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: fused GroupNorm statistics need the MFMA path "
                                          "and 4, 8, 16 or 32 channels per group");
     if (conv_uses_mfma_c(x, cout, weight_dtype)) {
+        // output-channel tile: 128 wide, or 64 / 32 for narrow outputs (conv_out's 48 or 12)
         if (cout >= 128)
             return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, fz, stream);
-        return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, fz, stream);
+        if (cout > 32)
+            return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, fz, stream);
+        return run_mfma_in<32>(x, w, bias, residual, y, box, split, packed, fz, stream);
     }
     if (packed) return fail(VAE_ERR_UNSUPPORTED, "packed weights need the MFMA path");
     if (weight_dtype == VAE_DTYPE_F32)

@@ -4,7 +4,8 @@
 //
 // Implicit GEMM:
 //  - GEMM view: M = output positions, N = Cout, K = 27 * Cin, ordered (channel chunk, tap).
-//  - One workgroup (4 waves) computes a block of 256 output positions for NT output channels.
+//  - One workgroup (4 waves) computes a block of 256 output positions for NT output channels
+//    (NT = 128; 64 or 32 for narrow outputs, whose waves then split the positions 2 or 4 ways).
 //    The block is TB x HB x WB positions (2x8x16, 4x8x8 or 4x4x16, whichever pads the box least).
 //    Each wave owns 32 output channels and 256 * 32 / NT positions (32x32 MFMA tiles): at NT = 128
 //    a wave covers all 256 positions. Each weight fragment it loads then feeds eight MFMAs. Its

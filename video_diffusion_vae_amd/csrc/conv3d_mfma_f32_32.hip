@@ -1,0 +1,10 @@
+// MFMA conv kernels for NT = 32, fp32 input (see conv3d_mfma.h).
+#include "conv3d_mfma.h"
+
+namespace vae {
+namespace mfma {
+template vae_status_t run_mfma_out<32, float, false>(const vae_tensor_t&, const void*, const float*,
+                                                   const vae_tensor_t*, const vae_tensor_t&,
+                                                   const Box&, bool, const ConvFuse*, hipStream_t);
+}  // namespace mfma
+}  // namespace vae
