@@ -134,11 +134,19 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
                                        const vae_box_t* out_box, int32_t flags,
                                        vae_stream_t stream);
 
-/* Causal Conv3d with work fused into its output stage: a depth-to-space of the result, and the
- * statistics of a GroupNorm that will read the result.
+/* Causal Conv3d with work fused into its input and output stages: a nearest upsampling of its
+ * input, a depth-to-space of the result, and the statistics of a GroupNorm that will read the
+ * result.
  *
- * The conv is the one vae_conv3d_causal computes over out_box (in x's grid, NULL = all), with
- * Cout = y.c * st * sh * sw output channels.
+ * Input upsampling (in_up_sh, in_up_sw; 0 or 1 = none; powers of two up to 16). The conv reads
+ * the nearest upsampling of x, u[t, h, w] = x[t, h / in_up_sh, w / in_up_sw], straight from x while
+ * its input tile is staged; u is never written. The input grid below is then u's
+ * [N, T, H * in_up_sh, W * in_up_sw], and zero padding applies at u's borders. This is exactly
+ * vae_upsample(VAE_UPSAMPLE_NEAREST) followed by the conv, without writing and re-reading u (the
+ * spatial upsampler of Wan-style decoders is a nearest upsampling followed by a conv).
+ *
+ * The conv is the one vae_conv3d_causal computes over out_box (in the input grid, NULL = all),
+ * with Cout = y.c * st * sh * sw output channels.
  *
  * Depth-to-space (d2s_st, d2s_sh, d2s_sw; all 0 = none). Conv output channel
  * ((dt*sh + dh)*sw + dw)*C + c at (t, h, w) is written to channel c of y at
@@ -164,8 +172,9 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
  *  owned by the caller (unused without statistics). Its contents are undefined afterwards.
  *
  * Errors: those of vae_conv3d_causal; INVALID_ARG when y's shape does not match the factors;
- * UNSUPPORTED for a depth-to-space off the MFMA path, for a channel count not divisible by
- * gn_groups, or for a shape vae_groupnorm_stats refuses; INVALID_ARG for gn_eps < 0, a NULL
+ * UNSUPPORTED for a depth-to-space or an input upsampling off the MFMA path, for an input
+ * upsampling factor that is not a power of two, for a channel count not divisible by gn_groups,
+ * or for a shape vae_groupnorm_stats refuses; INVALID_ARG for gn_eps < 0, a NULL
  * gn_mean_rstd or an empty box with statistics; WORKSPACE for a short ws.
  */
 typedef struct vae_conv_fused {
@@ -183,6 +192,7 @@ typedef struct vae_conv_fused {
     float* gn_mean_rstd;            /* device, N * gn_groups * 2 floats */
     void* ws;
     size_t ws_bytes;
+    int32_t in_up_sh, in_up_sw;     /* nearest upsampling of x read by the conv; 0 = none */
 } vae_conv_fused_t;
 VAE_API vae_status_t vae_conv3d_causal_fused_workspace(const vae_conv_fused_t* args,
                                                        size_t* bytes);

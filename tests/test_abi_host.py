@@ -175,3 +175,12 @@ def test_fused_conv_validation_needs_no_gpu(v):
     with pytest.raises(v.VaeError) as e:          # groups must divide the channels
         v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), gn_groups=5)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    # a nearest upsampling of x read by the conv: y follows the upsampled grid
+    yu = torch.zeros((1, 3, 16, 32, 32), dtype=torch.float32)   # d2s (2,2,2) of an 8x16 grid
+    assert v.vae_conv3d_causal_fused_workspace(x, w, yu, d2s=(2, 2, 2), in_up=(2, 2)) == 0
+    with pytest.raises(v.VaeError) as e:          # y does not follow the upsampled grid
+        v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), in_up=(2, 2))
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:          # factors must be powers of two
+        v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), in_up=(3, 1))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED

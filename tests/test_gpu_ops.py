@@ -605,3 +605,43 @@ def test_conv3d_f16_argument_rules(v):
         v.vae_groupnorm_silu(x16, None, 8, 1e-6, None, None, True, y)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
 
+
+
+IN_UP_CASES = [
+    # (N, T, h, w) of x before the upsampling, Cin, Cout, dtype, (sh, sw), box in the upsampled grid
+    ((1, 3, 5, 9), 64, 128, "bf16", (2, 2), None),
+    ((1, 2, 4, 6), 32, 64, "f16", (2, 2), (0, 2, 1, 7, 3, 12)),
+    ((2, 2, 3, 8), 64, 96, "f32", (2, 1), None),
+    ((1, 3, 4, 4), 32, 48, "bf16", (4, 4), None),
+    ((1, 4, 6, 10), 64, 32, "f16", (2, 2), (1, 4, 0, 12, 0, 20)),
+]
+
+
+@pytest.mark.parametrize("case", IN_UP_CASES)
+def test_conv3d_folded_nearest_upsampling(v, case):
+    """A conv reading the nearest upsampling of x while it stages its input equals
+    vae_upsample(NEAREST) followed by the conv, bit for bit (same operands, same order)."""
+    import torch
+    (n, t, h, w), cin, cout, dt, (sh, sw), bx = case
+    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 95 + IN_UP_CASES.index(case))
+    if dt == "f16":
+        x = round_f16(x + ndhwc(vae_synth.normal((n, cin, t, h, w), [18, cin], scale=1e-3)))
+    elif dt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [18, cin], scale=1e-3))
+    xd = dev(x, dt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    xu = torch.empty((n, t, h * sh, w * sw, cin), device="cuda", dtype=xd.dtype)
+    v.vae_upsample(xd, None, v.VAE_UPSAMPLE_NEAREST, 1, sh, sw, xu)
+    y0 = torch.full((n, t, h * sh, w * sw, cout), 7.0, device="cuda", dtype=torch.float32)
+    y1 = torch.full_like(y0, 7.0)
+    v.vae_conv3d_causal(xu, wd, bd, None, y0, bx)
+    v.vae_conv3d_causal_fused(xd, wd, bd, None, y1, bx, in_up=(sh, sw))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    # and both are the oracle's conv of the upsampled input
+    xin = vae_synth.round_bf16(x).astype(np.float64) if dt == "f32" else x
+    ref = oracle.causal_conv3d(oracle.nearest_upsample(xin, sh, sw), wt, b)
+    bx = bx or (0, t, 0, h * sh, 0, w * sw)
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    assert rel_max_abs(host(y1)[sl], ref[sl]) <= 1e-4

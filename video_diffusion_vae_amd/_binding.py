@@ -56,7 +56,8 @@ class vae_conv_fused_t(ctypes.Structure):
                 ("d2s_st", ctypes.c_int32), ("d2s_sh", ctypes.c_int32), ("d2s_sw", ctypes.c_int32),
                 ("gn_groups", ctypes.c_int32), ("gn_eps", ctypes.c_float),
                 ("gn_mean_rstd", ctypes.c_void_p), ("ws", ctypes.c_void_p),
-                ("ws_bytes", ctypes.c_size_t)]
+                ("ws_bytes", ctypes.c_size_t), ("in_up_sh", ctypes.c_int32),
+                ("in_up_sw", ctypes.c_int32)]
 
 class vae_error_info_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_int32), ("axis", ctypes.c_int32), ("extent", ctypes.c_int64),
@@ -239,7 +240,7 @@ def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, strea
 
 
 def _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
-                gn_mean_rstd, ws):
+                gn_mean_rstd, ws, in_up=(0, 0)):
     keep = [tensor_desc(x), tensor_desc(y),
             tensor_desc(residual) if residual is not None else None, box(out_box)]
     a = vae_conv_fused_t()
@@ -257,25 +258,30 @@ def _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn
     a.gn_mean_rstd = _ptr(gn_mean_rstd)
     a.ws = _ptr(ws)
     a.ws_bytes = ws.numel() if ws is not None else 0
+    a.in_up_sh, a.in_up_sw = (int(f) for f in in_up)
     return a, keep
 
 
-def vae_conv3d_causal_fused_workspace(x, weight, y, out_box=None, d2s=(0, 0, 0), gn_groups=0):
-    a, keep = _fused_args(x, weight, None, None, y, out_box, 0, d2s, gn_groups, 0.0, None, None)
+def vae_conv3d_causal_fused_workspace(x, weight, y, out_box=None, d2s=(0, 0, 0), gn_groups=0,
+                                      in_up=(0, 0)):
+    a, keep = _fused_args(x, weight, None, None, y, out_box, 0, d2s, gn_groups, 0.0, None, None,
+                          in_up)
     n = ctypes.c_size_t(0)
     _check(LIB.vae_conv3d_causal_fused_workspace(ctypes.byref(a), ctypes.byref(n)))
     return n.value
 
 
 def vae_conv3d_causal_fused(x, weight, bias, residual, y, out_box=None, flags=0, d2s=(0, 0, 0),
-                            gn_groups=0, gn_eps=1e-6, gn_mean_rstd=None, ws=None, stream=None):
-    """Causal Conv3d with a fused depth-to-space (d2s = (st, sh, sw), y is then the upsampled
-    tensor) and/or the statistics of a GroupNorm over y (gn_mean_rstd [N, gn_groups, 2] fp32)."""
+                            gn_groups=0, gn_eps=1e-6, gn_mean_rstd=None, ws=None, stream=None,
+                            in_up=(0, 0)):
+    """Causal Conv3d of the nearest upsampling of x by in_up = (sh, sw), with a fused
+    depth-to-space (d2s = (st, sh, sw), y is then the upsampled tensor) and/or the statistics of a
+    GroupNorm over y (gn_mean_rstd [N, gn_groups, 2] fp32)."""
     if ws is None and gn_groups:
-        ws = _workspace(vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups),
-                        x.device)
+        ws = _workspace(vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups,
+                                                          in_up), x.device)
     a, keep = _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
-                          gn_mean_rstd, ws)
+                          gn_mean_rstd, ws, in_up)
     _check(LIB.vae_conv3d_causal_fused(ctypes.byref(a), _stream(stream)))
     return y
 

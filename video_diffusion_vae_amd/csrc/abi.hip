@@ -283,8 +283,17 @@ vae_status_t check_conv(const vae_tensor_t* x, const void* weight, int32_t weigh
 // conv's out_box covers.
 struct FusedPlan {
     int32_t st, sh, sw, k;
+    int32_t lsh, lsw;     // log2 of the input's nearest upsampling (0 = none)
     Box cbox, ybox;
 };
+
+// log2 of a nearest factor: 0 reads as 1; factors must be powers of two up to 16.
+int32_t nearest_log2(int32_t f) {
+    if (f == 0 || f == 1) return 0;
+    for (int32_t l = 1; l <= 4; ++l)
+        if (f == (1 << l)) return l;
+    return -1;
+}
 
 // `run`: the call itself (the workspace query needs no output pointers).
 vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
@@ -296,6 +305,16 @@ vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
     if (!a->weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
     if (a->weight_dtype != VAE_DTYPE_BF16 && a->weight_dtype != VAE_DTYPE_F32)
         return fail(VAE_ERR_INVALID_ARG, "unknown weight dtype");
+    p->lsh = nearest_log2(a->in_up_sh);
+    p->lsw = nearest_log2(a->in_up_sw);
+    if (p->lsh < 0 || p->lsw < 0)
+        return fail(VAE_ERR_UNSUPPORTED, "input upsampling factors must be 0, 1, 2, 4, 8 or 16");
+    // the conv's input grid: x after the nearest upsampling
+    vae_tensor_t xl = x;
+    xl.h = x.h << p->lsh;
+    xl.w = x.w << p->lsw;
+    if (xl.h * xl.w > INT32_MAX)
+        return fail(VAE_ERR_UNSUPPORTED, "upsampled spatial extent too large");
     if (reinterpret_cast<uintptr_t>(a->weight) % 16 != 0)
         return fail(VAE_ERR_INVALID_ARG, "weight must be 16-byte aligned");
     const bool none = a->d2s_st == 0 && a->d2s_sh == 0 && a->d2s_sw == 0;
@@ -305,23 +324,24 @@ vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
     if (p->st < 1 || p->sh < 1 || p->sw < 1)
         return fail(VAE_ERR_INVALID_ARG, "d2s factors must all be 0 or all be >= 1");
     p->k = p->st * p->sh * p->sw;
-    if (y.n != x.n || y.t != p->st * x.t - (p->st - 1) || y.h != p->sh * x.h ||
-        y.w != p->sw * x.w)
+    if (y.n != xl.n || y.t != p->st * xl.t - (p->st - 1) || y.h != p->sh * xl.h ||
+        y.w != p->sw * xl.w)
         return fail(VAE_ERR_INVALID_ARG,
-                    "y must be [N, st*T-(st-1), sh*H, sw*W, Cout/(st*sh*sw)] of x's [N, T, H, W]");
+                    "y must be [N, st*T-(st-1), sh*H, sw*W, Cout/(st*sh*sw)] of the input grid "
+                    "[N, T, H, W] (x's, times the input upsampling)");
     if (a->residual) VAE_TRY(check_residual(a->residual, x, y));
     if (overlaps(x, y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
-    VAE_TRY(check_box(a->out_box, x, "out_box"));
-    p->cbox = to_box(a->out_box, x);
+    VAE_TRY(check_box(a->out_box, xl, "out_box"));
+    p->cbox = to_box(a->out_box, xl);
     const Box& b = p->cbox;
     p->ybox = Box{std::max(0, p->st * b.t0 - (p->st - 1)), p->st * b.t1 - (p->st - 1),
                   p->sh * b.h0, p->sh * b.h1, p->sw * b.w0, p->sw * b.w1};
     const bool mfma = conv_uses_mfma_c(x, y.c * p->k, a->weight_dtype);
     VAE_TRY(check_conv_dtypes(x, y, a->residual, y.c * p->k, a->weight_dtype, a->flags));
-    if (p->k > 1 && !mfma)
+    if ((p->k > 1 || p->lsh || p->lsw) && !mfma)
         return fail(VAE_ERR_UNSUPPORTED,
-                    "a fused depth-to-space needs bf16 weights, Cin % 32 == 0 and Cout % 4 == 0",
-                    4, x.c, 32);
+                    "a fused depth-to-space or input upsampling needs bf16 weights, Cin % 32 == 0 "
+                    "and Cout % 4 == 0", 4, x.c, 32);
     if (a->gn_groups) {
         if (y.dtype == VAE_DTYPE_F16)
             return fail(VAE_ERR_UNSUPPORTED, "statistics of an fp16 y are not gathered");
@@ -403,7 +423,8 @@ VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_s
     }
     hipStream_t s = as_stream(stream);
     double* part = static_cast<double*>(a.ws);
-    ConvFuse fz{slots > 0 ? part : nullptr, a.gn_groups ? a.gn_groups : 1, p.st, p.sh, p.sw};
+    ConvFuse fz{slots > 0 ? part : nullptr, a.gn_groups ? a.gn_groups : 1, p.st, p.sh, p.sw,
+                p.lsh, p.lsw};
     VAE_TRY(launch_conv3d(x, a.weight, a.weight_dtype, a.bias, a.residual, y, p.cbox, a.flags, s,
                           &fz));
     if (!a.gn_groups) return VAE_OK;

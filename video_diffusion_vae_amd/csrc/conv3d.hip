@@ -201,6 +201,8 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
         return fail(VAE_ERR_INVALID_ARG, "an fp16 input takes fp16-packed weights");
     const int32_t k = fz ? fz->st * fz->sh * fz->sw : 1;
     const int64_t cout = y.c * k;
+    if (fz && (fz->lsh || fz->lsw) && !conv_uses_mfma_c(x, cout, weight_dtype))
+        return fail(VAE_ERR_UNSUPPORTED, "conv3d: a folded nearest upsampling needs the MFMA path");
     if ((x16 || y.dtype == VAE_DTYPE_F16) && !conv_uses_mfma_c(x, cout, weight_dtype))
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: fp16 tensors need the MFMA path");
     if (fz && k > 1 && !conv_uses_mfma_c(x, cout, weight_dtype))

@@ -103,7 +103,11 @@ struct MfmaArgs {
     const float* bias;
     const void* res;
     void* y;
+    // The conv's input grid is T x H x W. With a nearest upsampling folded into the staging
+    // (lsh, lsw = log2 of its factors, 0 = none), x holds the T x (H >> lsh) x (W >> lsw) tensor
+    // and input position (h, w) reads x at (h >> lsh, w >> lsw).
     int32_t T, H, W, cin, cout;
+    int32_t lsh, lsw;
     Box box;
     int32_t nbt, nbh, nbw;   // blocks along each box axis
     int32_t n_mblocks;       // N * nbt * nbh * nbw
@@ -626,7 +630,8 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     const int khalf = lane >> 5;      // which 8 of the 16 k values this lane feeds
 
     const int64_t cin = a.cin;
-    const TI* xn = static_cast<const TI*>(a.x) + (int64_t)n * a.T * a.H * a.W * cin;
+    const int xH = a.H >> a.lsh, xW = a.W >> a.lsw;      // x's own extents
+    const TI* xn = static_cast<const TI*>(a.x) + (int64_t)n * a.T * xH * xW * cin;
 
     f32x16_t acc[MI];
 #pragma unroll
@@ -720,7 +725,8 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 const bool in = (unsigned)hg < (unsigned)a.H && (unsigned)wg < (unsigned)a.W;
                 const int hc = hg < 0 ? 0 : (hg >= a.H ? a.H - 1 : hg);
                 const int wc = wg < 0 ? 0 : (wg >= a.W ? a.W - 1 : wg);
-                fst[reg][i] = load_raw8<TI>(xn + ((int64_t)(tg * a.H + hc) * a.W + wc) * cin +
+                fst[reg][i] = load_raw8<TI>(xn + ((int64_t)(tg * xH + (hc >> a.lsh)) * xW +
+                                                  (wc >> a.lsw)) * cin +
                                             c0 + g * 8);
                 fin[reg] = in ? (fin[reg] | (1u << i)) : (fin[reg] & ~(1u << i));
             }
@@ -861,7 +867,8 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
                 uint4 vl = make_uint4(0, 0, 0, 0);
                 if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
-                    const TI* src = xn + ((int64_t)(tg * a.H + hg) * a.W + wg) * cin + c0 + g * 8;
+                    const TI* src = xn + ((int64_t)(tg * xH + (hg >> a.lsh)) * xW + (wg >> a.lsw)) *
+                                             cin + c0 + g * 8;
                     if constexpr (SPLIT) split8<TI>(src, v, vl);
                     else v = load8<TI>(src);
                 }
@@ -958,8 +965,10 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.res_f32 = residual && residual->dtype == VAE_DTYPE_F32 && y.dtype != VAE_DTYPE_F32;
     a.y = y.data;
     a.T = (int32_t)x.t;
-    a.H = (int32_t)x.h;
-    a.W = (int32_t)x.w;
+    a.lsh = fz ? fz->lsh : 0;
+    a.lsw = fz ? fz->lsw : 0;
+    a.H = (int32_t)(x.h << a.lsh);
+    a.W = (int32_t)(x.w << a.lsw);
     a.cin = (int32_t)x.c;
     a.st = fz ? fz->st : 1;
     a.sh = fz ? fz->sh : 1;

@@ -120,6 +120,13 @@ int32_t res_out_dtype(const vae_decoder& d, size_t i) {
     return d.act_dtype;
 }
 
+// log2 of a power-of-two factor up to 16, else -1.
+int32_t log2_of(int32_t f) {
+    for (int32_t l = 0; l <= 4; ++l)
+        if (f == (1 << l)) return l;
+    return -1;
+}
+
 // Whether the op after layer i starts with a GroupNorm of layer i's output.
 bool gn_follows(const vae_decoder& d, size_t i) {
     if (i + 1 >= d.layers.size()) return false;
@@ -362,9 +369,10 @@ struct Runner {
     // `wi` indexes d->ptrs: the conv's weight, followed by its bias. With `gn_next` the conv's
     // epilogue also gathers the statistics of the GroupNorm that reads y. `up` (a D2S layer or
     // null) makes y the depth-to-space of the conv output, written by the conv's epilogue.
+    // `lsh`, `lsw`: a nearest upsampling of x (log2 factors) that the conv reads while staging.
     vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
                       const vae_tensor_t& y, int layer, bool gn_next,
-                      const vae_layer_desc_t* up = nullptr) {
+                      const vae_layer_desc_t* up = nullptr, int32_t lsh = 0, int32_t lsw = 0) {
         int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
                          ? VAE_CONV_SPLIT_FP32
                          : 0;
@@ -376,14 +384,18 @@ struct Runner {
         }
         const int32_t k = up ? up->st * up->sh * up->sw : 1;
         const int64_t cout = y.c * k;
+        vae_tensor_t xl = x;                       // the conv's input grid
+        xl.h <<= lsh;
+        xl.w <<= lsw;
+        const Box box = whole_box(xl);
         const int64_t slots =
-            gn_next ? conv_gn_slots(x, y.c, d->dtype, whole_box(x), d->groups, k) : 0;
+            gn_next ? conv_gn_slots(x, y.c, d->dtype, box, d->groups, k) : 0;
         double* part = reinterpret_cast<double*>(ws + L.gn);
         const ConvFuse fz{slots > 0 ? part : nullptr, d->groups, up ? up->st : 1,
-                          up ? up->sh : 1, up ? up->sw : 1};
+                          up ? up->sh : 1, up ? up->sw : 1, lsh, lsw};
         VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res, y,
-                              whole_box(x), cf, s, &fz));
-        const double flops = 2.0 * 27.0 * (double)x.c * (double)cout * (double)positions(x);
+                              box, cf, s, &fz));
+        const double flops = 2.0 * 27.0 * (double)x.c * (double)cout * (double)positions(xl);
         const double bytes = (double)numel(x) * elem_size(x.dtype) +
                              (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
         VAE_TRY(mark(VAE_KIND_CONV, layer, flops, bytes));
@@ -405,6 +417,7 @@ struct Runner {
         vae_tensor_t cur = in;
         int cur_buf = -1;  // -1: the caller's input, never written
         int ch = 1, cw = 1;
+        int32_t near_lsh = 0, near_lsw = 0;   // a nearest upsampling the next conv reads
         size_t p = 0;
         auto buf = [&](int i, const Shape& sh) { return tensor_of(ws + L.buf[i], sh); };
         auto free_buf = [&](int avoid1, int avoid2) {
@@ -427,7 +440,8 @@ struct Runner {
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = out_last ? final_out : buf(nb, shapes[lo]);
                 VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, lo),
-                             fuse_up ? &d->layers[li + 1] : nullptr));
+                             fuse_up ? &d->layers[li + 1] : nullptr, near_lsh, near_lsw));
+                near_lsh = near_lsw = 0;
                 p += 2;
                 cur = y;
                 cur_buf = out_last ? -2 : nb;
@@ -528,6 +542,16 @@ struct Runner {
                 p += 2;
                 cur = y;
                 cur_buf = nb;
+            } else if (l.op == VAE_OP_NEAREST && !last && d->layers[li + 1].op == VAE_OP_CONV &&
+                       conv_uses_mfma_c(cur, d->layers[li + 1].cout, d->dtype) &&
+                       log2_of(l.sh) >= 0 && log2_of(l.sw) >= 0 &&
+                       near_lsh + log2_of(l.sh) <= 4 && near_lsw + log2_of(l.sw) <= 4) {
+                // a nearest upsampling feeding an MFMA conv: the conv reads it while staging its
+                // input tile, so the upsampled tensor is never written
+                near_lsh += log2_of(l.sh);
+                near_lsw += log2_of(l.sw);
+                ch *= l.sh;
+                cw *= l.sw;
             } else {  // D2S / NEAREST
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = last ? final_out : buf(nb, os);

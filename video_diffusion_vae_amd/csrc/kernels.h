@@ -21,10 +21,14 @@ struct BoxList {
 //  - GroupNorm partials of y as stored (gn_ws non-null): fp64 (count, mean, M2) per
 //    [N][groups][slots]; conv_gn_slots() gives the slot count, or 0 when the shapes need the
 //    separate statistics pass.
+//  - a nearest upsampling of the input by (1 << lsh, 1 << lsw), read while the input tile is
+//    staged: x is then the tensor before that upsampling, and every extent and box refers to the
+//    upsampled grid.
 struct ConvFuse {
     double* gn_ws;
     int32_t groups;
     int32_t st, sh, sw;
+    int32_t lsh = 0, lsw = 0;
 };
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
