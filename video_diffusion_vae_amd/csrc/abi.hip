@@ -364,6 +364,15 @@ size_t fused_workspace(const vae_conv_fused_t* a, const FusedPlan& p, int64_t* s
     return gn_stats_workspace(*a->y, bl, a->gn_groups);
 }
 
+vae_status_t check_attention(const vae_tensor_t* x) {
+    VAE_TRY(check_tensor(x, "x"));
+    if (x->dtype != VAE_DTYPE_F32) return fail(VAE_ERR_UNSUPPORTED, "attention reads fp32 x");
+    if (!attention_shape_supported(x->c))
+        return fail(VAE_ERR_UNSUPPORTED, "attention needs C % 32 == 0 and C / 8 dividing 256", 4,
+                    x->c, 32);
+    return VAE_OK;
+}
+
 }  // namespace vae
 
 using namespace vae;
@@ -574,15 +583,6 @@ VAE_API vae_status_t vae_rmsnorm_silu(const vae_tensor_t* x, float eps, const fl
     if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
     VAE_TRY(check_gn_output(*x, *y));
     return launch_rms_norm(*x, eps, gamma, beta, apply_silu != 0, *y, as_stream(stream));
-}
-
-vae_status_t check_attention(const vae_tensor_t* x) {
-    VAE_TRY(check_tensor(x, "x"));
-    if (x->dtype != VAE_DTYPE_F32) return fail(VAE_ERR_UNSUPPORTED, "attention reads fp32 x");
-    if (!attention_shape_supported(x->c))
-        return fail(VAE_ERR_UNSUPPORTED, "attention needs C % 32 == 0 and C / 8 dividing 256", 4,
-                    x->c, 32);
-    return VAE_OK;
 }
 
 VAE_API vae_status_t vae_frame_attention_workspace(const vae_tensor_t* x, size_t* bytes) {
