@@ -176,3 +176,28 @@ def test_wan_720p_one_frame_every_value(v):
     assert got.shape == (1, 1, 704, 1280, 3)
     p, m = psnr(got, ref), float(np.abs(got - ref).max())
     assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
+def test_wan_720p_six_frames_against_golden(v):
+    """The full-width Wan-shaped 720p plan on six latent frames ([1,48,6,44,80] ->
+    [1,21,704,1280,3]) in 1 x 4 width patches, at the pixels the oracle's fp64 decode stored
+    (tests/golden/make_wan_720p_samples.py): both temporal upsamplings and the causal temporal taps
+    at full spatial size."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "wan_720p_6f_whole_samples.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path)
+    out = _decode(v, "wan_720p_6f", "patch", (1, 4))
+    assert tuple(out.shape) == tuple(int(d) for d in g["shape"])
+    pos = g["positions"]
+    got = out[0, pos[:, 0], pos[:, 1], pos[:, 2], :].double().cpu().numpy()
+    ref = g["values"]
+    assert np.all(np.isfinite(got))
+    p = 10 * np.log10((float(g["out_max"]) - float(g["out_min"])) ** 2 / np.mean((got - ref) ** 2))
+    m = float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+    o = out.double()
+    assert abs(float(o.mean()) - float(g["out_mean"])) <= 1e-3 * float(g["out_std"])
+    assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3

@@ -53,7 +53,7 @@ import numpy as np
 
 __all__ = [
     "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "LTX2_720P_1F", "LTX2_TINY",
-    "LTX2_TINY_N2", "WAN_720P", "WAN_SMALL", "WAN_720P_1F", "WAN_TINY", "WORKLOADS",
+    "LTX2_TINY_N2", "WAN_720P", "WAN_SMALL", "WAN_720P_1F", "WAN_720P_6F", "WAN_TINY", "WORKLOADS",
     "round_bf16", "bf16_bits", "normal", "uniform", "latent", "decoder_params", "conv_params",
     "walk_plan", "with_latent",
 ]
@@ -216,6 +216,10 @@ WAN_SMALL = with_latent(WAN_720P, (1, 48, 2, 3, 5), "wan_small",
                         patch_grid=(1, 2), overlap_tile=(2, 4), overlap_stride=(1, 3))
 # One latent frame at the full 720p extent: the attention sees all 44 x 80 positions of the frame.
 WAN_720P_1F = with_latent(WAN_720P, (1, 48, 1, 44, 80), "wan_720p_1f")
+# Six latent frames at the full 720p extent (21 output frames): both temporal upsamplings and the
+# causal temporal taps at full spatial size, at a quarter of the full decode's work (the reference
+# for its golden samples).
+WAN_720P_6F = with_latent(WAN_720P, (1, 48, 6, 44, 80), "wan_720p_6f")
 
 # The Wan plan at a quarter of the widths (256/128/64/32).
 WAN_TINY = with_latent(WAN_720P, (1, 48, 3, 4, 6), "wan_tiny",
@@ -229,7 +233,7 @@ for _op in WAN_TINY["layers"]:
 
 WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
                                     LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2, WAN_720P, WAN_SMALL,
-                                    WAN_720P_1F, WAN_TINY)}
+                                    WAN_720P_1F, WAN_720P_6F, WAN_TINY)}
 
 
 # ----------------------------------------------------------------------------------------------
