@@ -220,16 +220,16 @@ def merge_tiles(tile_outputs, tiles, out_shape) -> np.ndarray:
 
 
 def decode_overlap_blend(spec: dict, z: np.ndarray, params: list, tile_hw, stride_hw,
-                         scale) -> np.ndarray:
-    """Serial overlap-blend tiled decode of the NDHWC latent ``z``."""
+                         scale, tile_t: int = 0, stride_t: int = 0) -> np.ndarray:
+    """Serial overlap-blend tiled decode of the NDHWC latent ``z`` (``tile_t`` > 0 also cuts T)."""
     z = np.asarray(z, dtype=np.float64)
     _, t, h, w, _ = z.shape
-    tiles = overlap_tiles(t, h, w, tile_hw, stride_hw, scale)
+    tiles = overlap_tiles(t, h, w, tile_hw, stride_hw, scale, tile_t, stride_t)
     out_shape = output_shape(spec, z.shape)
     outs = []
     for tl in tiles:
-        _, _, h0, h1, w0, w1 = tl["latent"]
-        y = decode(spec, z[:, :, h0:h1, w0:w1], params)    # own borders, own statistics
+        t0, t1, h0, h1, w0, w1 = tl["latent"]
+        y = decode(spec, z[:, t0:t1, h0:h1, w0:w1], params)    # own borders, own statistics
         o = tl["out"]
         assert y.shape[1:4] == (o[1] - o[0], o[3] - o[2], o[5] - o[4]), (y.shape, o)
         outs.append(y)

@@ -21,8 +21,18 @@ E output samples. Over the overlap, the later tile's leading weight is (j+1)/(E+
 tile's trailing weight is (E-j)/(E+1), for j = 0..E-1. Elsewhere the weight is 1, and a tile's
 weight is the product over axes.
 
-Output boxes: spatial output = latent x scale. The temporal axis is never split and maps T latent
-frames to 1 + (T-1) * scale_t output frames (causal).
+Output boxes. A spatial span of latent rows [s, s + n) maps to output rows [s * r, (s + n) * r).
+The temporal axis is causal: a clip of n latent frames decodes to 1 + (n - 1) * r frames, because
+its first latent frame yields a single frame. The pages cut overlap tiles in time as well as in
+space ("[TRTLLM-14029][feat] LTX-2 tile-parallel VAE decode", Approach: overlapping
+spatial/temporal tiles), but say nothing of how a temporal tile's frames line up with the whole
+video. The plainest reading that the causal decoder supports: a temporal tile of latent frames
+[s, s + n), decoded alone, gives output frames [s * r, (s + n - 1) * r + 1). Its single first
+frame takes the place of the last frame of latent frame s in the whole decode, and the frames of
+each later latent frame line up with the whole decode's. For that reason consecutive temporal
+tiles must share at least one latent frame when r > 1; otherwise the r - 1 frames before a
+tile's first frame would come from no tile. Overlaps are measured between the output spans of
+neighbouring tiles.
 """
 from __future__ import annotations
 
@@ -55,6 +65,13 @@ def _out_t(t: int, scale_t: int) -> int:
     return 1 + (t - 1) * scale_t
 
 
+def out_span(start: int, size: int, scale: int, causal: bool):
+    """Output span [lo, hi) of the latent span [start, start + size) along one axis."""
+    if causal:
+        return start * scale, (start + size - 1) * scale + 1
+    return start * scale, (start + size) * scale
+
+
 def patch_tiles(t: int, h: int, w: int, ph: int, pw: int, scale):
     """Patch list (row-major) with latent and output boxes; overlaps are all zero."""
     st, sh, sw = scale
@@ -70,39 +87,43 @@ def patch_tiles(t: int, h: int, w: int, ph: int, pw: int, scale):
     return tiles
 
 
-def _overlaps(spans, scale):
-    """Per tile along one axis: (lead, trail) overlap with the neighbours, in output samples."""
+def _overlaps(outs):
+    """Per tile along one axis: (lead, trail) overlap of its output span with the neighbours'."""
     lead, trail = [], []
-    for k, (s, n) in enumerate(spans):
-        if k > 0:
-            ps, pn = spans[k - 1]
-            lead.append(max(0, ps + pn - s) * scale)
-        else:
-            lead.append(0)
-        if k + 1 < len(spans):
-            ns, _ = spans[k + 1]
-            trail.append(max(0, s + n - ns) * scale)
-        else:
-            trail.append(0)
+    for k, (lo, hi) in enumerate(outs):
+        lead.append(max(0, outs[k - 1][1] - lo) if k > 0 else 0)
+        trail.append(max(0, hi - outs[k + 1][0]) if k + 1 < len(outs) else 0)
     return lead, trail
 
 
-def overlap_tiles(t: int, h: int, w: int, tile_hw, stride_hw, scale):
-    """Overlapping tile list (row-major over H then W) with latent/output boxes and overlaps."""
+def overlap_tiles(t: int, h: int, w: int, tile_hw, stride_hw, scale, tile_t: int = 0,
+                  stride_t: int = 0):
+    """Overlapping tile list (row-major over T, H, W) with latent/output boxes and overlaps.
+
+    ``tile_t`` <= 0 leaves the temporal axis whole."""
     st, sh, sw = scale
+    ts = axis_tiles(t, tile_t, stride_t)
+    if len(ts) > 1 and st > 1 and stride_t >= tile_t:
+        raise ValueError(f"temporal stride {stride_t} must be below the tile ({tile_t}): "
+                         "a causal tile's first frame leaves a gap otherwise")
     hs = axis_tiles(h, tile_hw[0], stride_hw[0])
     ws = axis_tiles(w, tile_hw[1], stride_hw[1])
-    lh, th = _overlaps(hs, sh)
-    lw, tw = _overlaps(ws, sw)
+    to = [out_span(s, n, st, True) for s, n in ts]
+    ho = [out_span(s, n, sh, False) for s, n in hs]
+    wo = [out_span(s, n, sw, False) for s, n in ws]
+    lt, tt = _overlaps(to)
+    lh, th = _overlaps(ho)
+    lw, tw = _overlaps(wo)
     tiles = []
-    for i, (h0, hn) in enumerate(hs):
-        for j, (w0, wn) in enumerate(ws):
-            tiles.append({
-                "row": i, "col": j,
-                "latent": (0, t, h0, h0 + hn, w0, w0 + wn),
-                "out": (0, _out_t(t, st), h0 * sh, (h0 + hn) * sh, w0 * sw, (w0 + wn) * sw),
-                "lead": (0, lh[i], lw[j]), "trail": (0, th[i], tw[j]),
-            })
+    for k, (t0, tn) in enumerate(ts):
+        for i, (h0, hn) in enumerate(hs):
+            for j, (w0, wn) in enumerate(ws):
+                tiles.append({
+                    "slab": k, "row": i, "col": j,
+                    "latent": (t0, t0 + tn, h0, h0 + hn, w0, w0 + wn),
+                    "out": to[k] + ho[i] + wo[j],
+                    "lead": (lt[k], lh[i], lw[j]), "trail": (tt[k], th[i], tw[j]),
+                })
     return tiles
 
 
@@ -120,7 +141,7 @@ def ramp_1d(size: int, lead: int, trail: int) -> np.ndarray:
 
 
 def axis_weight_sum(tiles, axis: int, length: int) -> np.ndarray:
-    """Sum over the distinct tiles along ``axis`` (1 = H, 2 = W) of their 1-D ramps."""
+    """Sum over the distinct tiles along ``axis`` (0 = T, 1 = H, 2 = W) of their 1-D ramps."""
     seen = {}
     for tl in tiles:
         lo, hi = tl["out"][2 * axis], tl["out"][2 * axis + 1]

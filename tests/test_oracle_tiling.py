@@ -107,3 +107,77 @@ def test_merge_preserves_constant_and_single_tile():
     assert len(one) == 1
     y = np.random.default_rng(1).standard_normal(shape)
     assert np.array_equal(oracle.merge_tiles([y], one, shape), y)
+
+
+# ------------------------------------------------------------------------------------------------
+# Temporal tiles (overlap-blend). A clip of latent frames [s, s + n) decodes to output frames
+# [s * r, (s + n - 1) * r + 1): its single first frame stands for the last frame of latent frame s.
+# ------------------------------------------------------------------------------------------------
+
+def test_temporal_grid_by_hand():
+    # 16 latent frames, tiles of 8 stepping by 6, r = 8: clips [0,8), [6,14), [12,16) decode to
+    # 57, 57 and 25 frames at output frames 0, 48 and 96; neighbours share 9 output frames.
+    tiles = oracle.overlap_tiles(16, 22, 40, (0, 0), (0, 0), (8, 32, 32), 8, 6)
+    assert [t["latent"][:2] for t in tiles] == [(0, 8), (6, 14), (12, 16)]
+    assert [t["out"][:2] for t in tiles] == [(0, 57), (48, 105), (96, 121)]
+    assert [t["lead"][0] for t in tiles] == [0, 9, 9]
+    assert [t["trail"][0] for t in tiles] == [9, 9, 0]
+    assert all(t["out"][2:] == (0, 704, 0, 1280) for t in tiles)
+    np.testing.assert_allclose(oracle.axis_weight_sum(tiles, 0, 121), 1.0, rtol=0, atol=1e-15)
+
+
+def test_temporal_tiles_are_t_major_and_cover_the_output():
+    tiles = oracle.overlap_tiles(7, 22, 40, (16, 16), (14, 14), (4, 2, 2), 3, 2)
+    assert len(tiles) == 4 * 2 * 3          # clip starts 0, 2, 4, 6
+    assert [t["slab"] for t in tiles] == sorted(t["slab"] for t in tiles)
+    covered = np.zeros(1 + 6 * 4, dtype=bool)
+    for t in tiles:
+        covered[t["out"][0]:t["out"][1]] = True
+        assert t["out"][1] - t["out"][0] == 1 + (t["latent"][1] - t["latent"][0] - 1) * 4
+    assert covered.all()
+    assert np.all(oracle.axis_weight_sum(tiles, 0, 25) > 0)
+
+
+def test_temporal_refusals():
+    with pytest.raises(ValueError):        # r > 1: tiles that share no latent frame leave a gap
+        oracle.overlap_tiles(16, 4, 4, (0, 0), (0, 0), (8, 1, 1), 8, 8)
+    # r = 1 has no single first frame, so abutting clips are fine
+    tiles = oracle.overlap_tiles(16, 4, 4, (0, 0), (0, 0), (1, 1, 1), 8, 8)
+    assert [t["out"][:2] for t in tiles] == [(0, 8), (8, 16)]
+
+
+@pytest.mark.parametrize("tt,stt", [(3, 2), (4, 2), (5, 1), (2, 1)])
+def test_temporal_merge_of_exact_crops_is_identity(tt, stt):
+    tiles = oracle.overlap_tiles(7, 9, 8, (5, 4), (3, 3), (4, 2, 2), tt, stt)
+    y = np.random.default_rng(2).standard_normal((1, 25, 18, 16, 2))
+    merged = oracle.merge_tiles(_crop_tiles(y, tiles), tiles, y.shape)
+    np.testing.assert_allclose(merged, y, rtol=1e-15, atol=1e-15)
+
+
+_LOCAL_PLAN = {
+    # no convolution and no norm: every output frame depends on one latent frame only
+    "groups": 1, "eps": 1e-6, "scale": (4, 2, 2),
+    "layers": [{"op": "d2s", "st": 2, "sh": 2, "sw": 1},
+               {"op": "d2s", "st": 2, "sh": 1, "sw": 2}],
+}
+
+
+def test_temporal_clip_lines_up_with_the_whole_decode():
+    """A temporally local plan pins the frame alignment: each clip decoded alone equals the whole
+    decode over the clip's output span, for every clip start."""
+    z = np.random.default_rng(3).standard_normal((1, 7, 3, 4, 16))
+    whole = oracle.decode(_LOCAL_PLAN, z, [])
+    assert whole.shape == (1, 25, 6, 8, 1)
+    for s in range(7):
+        for n in range(1, 8 - s):
+            lo, hi = oracle.tiling.out_span(s, n, 4, True)
+            clip = oracle.decode(_LOCAL_PLAN, z[:, s:s + n], [])
+            assert np.array_equal(clip, whole[:, lo:hi]), (s, n)
+
+
+@pytest.mark.parametrize("tt,stt", [(3, 2), (4, 2), (4, 3)])
+def test_temporal_overlap_blend_of_a_local_plan_is_the_whole_decode(tt, stt):
+    z = np.random.default_rng(4).standard_normal((1, 7, 3, 4, 16))
+    whole = oracle.decode(_LOCAL_PLAN, z, [])
+    tiled = oracle.decode_overlap_blend(_LOCAL_PLAN, z, [], (2, 3), (1, 2), (4, 2, 2), tt, stt)
+    np.testing.assert_allclose(tiled, whole, rtol=1e-14, atol=1e-14)
