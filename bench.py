@@ -96,9 +96,11 @@ WORKLOADS = {
 }
 
 
-def workload_name(kind, mode):
+def workload_name(kind, mode, tile_t=0, stride_t=0):
     prefix = {"ltx2": "ltx2_720p", "wan": "wan2.2_ti2v_5b_720p"}[kind]
-    return prefix + ("_decode_patch_halo_1x4" if mode == "patch" else "_decode_overlap_blend_2x3")
+    if mode == "patch":
+        return prefix + "_decode_patch_halo_1x4"
+    return prefix + "_decode_overlap_blend_2x3" + (f"_t{tile_t}s{stride_t}" if tile_t else "")
 
 
 def conv_source_digest():
@@ -257,6 +259,10 @@ def main():
                     help="ltx2: the LTX-2-shaped decode (the headline); wan: the Wan2.2-shaped one")
     ap.add_argument("--operands", choices=["f16", "split", "bf16"], default="f16",
                     help="operands of the convs that read an fp32 activation (up-convs, conv_out)")
+    ap.add_argument("--tile-t", type=int, default=0,
+                    help="overlap mode: also cut T into clips of this many latent frames")
+    ap.add_argument("--stride-t", type=int, default=0,
+                    help="overlap mode: latent frames between clip starts (below --tile-t)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames of the oracle's sample (default 2 for ltx2, 1 for wan)")
@@ -295,12 +301,13 @@ def main():
     dec = v.upload_decoder(spec, params, dev, operands=args.operands)
     zp = v.pad_latent(z, spec)            # zero channels up to a multiple of 32 (48 -> 64)
     zd = torch.as_tensor(zp).to(device=dev, dtype=torch.bfloat16)
-    workload = workload_name(args.workload, args.mode)
+    workload = workload_name(args.workload, args.mode, args.tile_t, args.stride_t)
     if args.mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, spec["scale"], patches=patch_grid)
     else:
         desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, zp.shape, spec["scale"],
-                             tile=spec["overlap_tile"], stride=spec["overlap_stride"])
+                             tile=spec["overlap_tile"], stride=spec["overlap_stride"],
+                             tile_t=args.tile_t, stride_t=args.stride_t)
     ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device=dev)
     out = torch.empty(out_shape, dtype=torch.float32, device=dev)
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s, workspace "

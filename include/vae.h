@@ -340,8 +340,14 @@ VAE_API vae_status_t vae_upsample(const vae_tensor_t* x, const vae_box_t* box, i
  *    per-axis parts, a weight buffer, a divide). Where consecutive tiles overlap by E output
  *    samples, the later tile rises as (j+1)/(E+1) and the earlier one falls as (E-j)/(E+1),
  *    j = 0..E-1.
- * Output boxes: spatial = latent box * scale. T is never cut and maps to 1 + (T-1)*scale_t frames
- * (causal decode).
+ *    Mode B also cuts T when tile_t > 0 (P1, Approach: the tiles overlap in space and in time).
+ * Output boxes: spatial = latent box * scale. T is causal: a clip of n latent frames decodes to
+ * 1 + (n-1)*scale_t frames, and the clip [t0, t1) lands on output frames
+ * [t0*scale_t, (t1-1)*scale_t + 1), its single first frame standing for the last frame of latent
+ * frame t0 in the whole decode (the pages do not say how temporal tiles line up; this is the
+ * reading the causal decoder supports). With scale_t > 1, consecutive temporal tiles must share a
+ * latent frame (stride_t < tile_t), or the scale_t - 1 frames before a tile's first frame would
+ * come from no tile. Overlaps E are measured between neighbouring tiles' output spans.
  */
 enum { VAE_TILING_PATCH_HALO = 1, VAE_TILING_OVERLAP_BLEND = 2 };
 
@@ -352,6 +358,7 @@ typedef struct vae_tiling_desc {
     int32_t patches_h, patches_w;        /* mode A grid */
     int32_t tile_h, tile_w;              /* mode B tile size, latent rows */
     int32_t stride_h, stride_w;          /* mode B tile stride, latent rows */
+    int32_t tile_t, stride_t;            /* mode B temporal tiles, latent frames (0: T whole) */
 } vae_tiling_desc_t;
 
 typedef struct vae_tile {
@@ -365,7 +372,9 @@ typedef struct vae_tile {
 /* Host-only. tiles == NULL: *n_tiles receives the count. Otherwise up to `capacity` tiles, in
  * row-major order, are written and *n_tiles is the count. Refused (VAE_ERR_UNSUPPORTED, info
  * filled): a band that would be empty (a patch narrower than the one-row halo, P4,
- * calc_bottom_halo_width commit); a stride outside 1..tile. */
+ * calc_bottom_halo_width commit); a stride outside 1..tile; a temporal stride that is not below
+ * the temporal tile while scale_t > 1 (info.axis = 1). Tiles come T-major, then H, then W; `row`
+ * and `col` index the H and W tiles. */
 VAE_API vae_status_t vae_tile_split(const vae_tiling_desc_t* desc, vae_tile_t* tiles,
                                     int32_t capacity, int32_t* n_tiles);
 

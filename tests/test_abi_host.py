@@ -52,6 +52,17 @@ OVERLAP_CASES = [
     (9, 13, 29, (7, 6), (7, 1), (1, 4, 4)), (1, 1, 1, (1, 1), (1, 1), (1, 1, 1)),
 ]
 
+# with temporal tiles: (T, H, W, tile_hw, stride_hw, scale, tile_t, stride_t)
+TEMPORAL_CASES = [
+    (16, 22, 40, (16, 16), (14, 14), (8, 32, 32), 8, 6),      # 3 clips, 9 shared output frames
+    (16, 22, 40, (0, 0), (0, 0), (8, 32, 32), 4, 1),          # contained clips at the end
+    (15, 44, 80, (32, 32), (28, 28), (4, 16, 16), 8, 7),      # a one-frame last clip [14, 15)
+    (7, 9, 8, (5, 4), (3, 3), (4, 2, 2), 3, 2),
+    (16, 4, 4, (0, 0), (0, 0), (1, 1, 1), 8, 8),              # scale 1: abutting clips allowed
+    (3, 16, 16, (8, 8), (6, 6), (2, 4, 4), 2, 1),
+    (5, 3, 3, (0, 0), (0, 0), (2, 1, 1), 9, 1),               # tile longer than T: T whole
+]
+
 
 @pytest.mark.parametrize("case", PATCH_CASES)
 def test_patch_split_bit_exact(v, case):
@@ -79,6 +90,32 @@ def test_overlap_split_bit_exact(v, case):
         f = _fields(g)
         for k in ("latent", "out", "lead", "trail"):
             assert f[k] == r[k], (k, f[k], r[k])
+
+
+@pytest.mark.parametrize("case", TEMPORAL_CASES)
+def test_temporal_overlap_split_bit_exact(v, case):
+    t, h, w, tile, stride, scale, tt, stt = case
+    got = v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, t, h, w, 8), scale,
+                                         tile=tile, stride=stride, tile_t=tt, stride_t=stt))
+    ref = oracle.overlap_tiles(t, h, w, tile, stride, scale, tt, stt)
+    assert len(got) == len(ref)
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert g.index == i
+        f = _fields(g)
+        for k in ("latent", "out", "lead", "trail", "row", "col"):
+            assert f[k] == r[k], (k, f[k], r[k])
+
+
+def test_temporal_gap_is_refused_with_numbers(v):
+    with pytest.raises(v.VaeError) as e:
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 16, 4, 4, 8), (8, 1, 1),
+                                       tile_t=8, stride_t=8))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    assert e.value.info["axis"] == 1 and e.value.info["extent"] == 8
+    with pytest.raises(v.VaeError) as e:
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 16, 4, 4, 8), (1, 1, 1),
+                                       tile_t=4, stride_t=5))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 1
 
 
 def test_refusals_carry_numbers(v):

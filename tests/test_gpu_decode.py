@@ -59,19 +59,21 @@ def spec_of(name):
 
 
 @functools.lru_cache(maxsize=None)
-def oracle_out(name, mode, affine=None):
+def oracle_out(name, mode, affine=None, tt=(0, 0)):
     spec = spec_of(name)
     z = ndhwc(vae_synth.latent(spec))
     p = params_of(name, affine)
     if mode == "whole":
         return oracle.decode(spec, z, p)
     return oracle.decode_overlap_blend(spec, z, p, spec["overlap_tile"], spec["overlap_stride"],
-                                       spec["scale"])
+                                       spec["scale"], tt[0], tt[1])
 
 
-def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32", operands="f16"):
+def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32", operands="f16",
+               tt=(0, 0)):
     """Decode through vae_decode_tiled. ``operands``: how convs reading an fp32 activation get
-    their operands, "f16" (the default), "split" (bf16 hi + lo) or "bf16"."""
+    their operands, "f16" (the default), "split" (bf16 hi + lo) or "bf16". ``tt``: temporal tile
+    and stride of an overlap-blend decode (0: T whole)."""
     import torch
     spec = spec_of(name)
     z = ndhwc(vae_synth.latent(spec))
@@ -81,7 +83,8 @@ def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32", 
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
     else:
         desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, z.shape, spec["scale"],
-                             tile=spec["overlap_tile"], stride=spec["overlap_stride"])
+                             tile=spec["overlap_tile"], stride=spec["overlap_stride"],
+                             tile_t=tt[0], stride_t=tt[1])
     ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
     out_shape = oracle.output_shape(spec, z.shape)
     outs = []
@@ -112,6 +115,18 @@ def test_tiny_decoder_patch_halo(v, patches):
 def test_tiny_decoder_overlap_blend(v):
     got = host(gpu_decode(v, "tiny_decoder", "overlap", affine=3))
     assert rel_max_abs(got, oracle_out("tiny_decoder", "overlap", 3)) <= 1e-4
+
+
+@pytest.mark.parametrize("tt", [(2, 1), (3, 2)])
+def test_tiny_decoder_overlap_blend_temporal_tiles(v, tt):
+    """Tiles in T as well: (2, 1) cuts the 3 latent frames into clips [0,2) [1,3) [2,3), the last
+    a single frame; (3, 2) leaves T whole (no longer than the tile)."""
+    got = host(gpu_decode(v, "tiny_decoder", "overlap", affine=3, tt=tt))
+    ref = oracle_out("tiny_decoder", "overlap", 3, tt)
+    assert got.shape == ref.shape == (1, 5, 64, 64, 3)
+    assert rel_max_abs(got, ref) <= 1e-4
+    if tt == (3, 2):
+        assert rel_max_abs(got, oracle_out("tiny_decoder", "overlap", 3)) <= 1e-4
 
 
 def _bf16_bar(got, ref):

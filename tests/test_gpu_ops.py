@@ -419,17 +419,21 @@ def test_upsample_bit_exact(v, case):
         assert np.all(got[~mask] == -3.0)
 
 
-@pytest.mark.parametrize("grid", [((16, 16), (14, 14), (22, 40), (2, 4, 4)),
-                                  ((4, 5), (3, 2), (9, 11), (1, 3, 2)),
-                                  ((8, 8), (8, 8), (8, 8), (1, 2, 2))])
+@pytest.mark.parametrize("grid", [((16, 16), (14, 14), (22, 40), (2, 4, 4), 2, (0, 0)),
+                                  ((4, 5), (3, 2), (9, 11), (1, 3, 2), 2, (0, 0)),
+                                  ((8, 8), (8, 8), (8, 8), (1, 2, 2), 2, (0, 0)),
+                                  # temporal tiles: clips [0,3) [2,5) [4,5); 3 shared frames
+                                  ((4, 5), (3, 2), (9, 11), (2, 3, 2), 5, (3, 2)),
+                                  ((0, 0), (0, 0), (5, 7), (4, 1, 1), 7, (4, 1))])
 def test_tile_merge_matches_oracle(v, grid):
     import torch
-    tile, stride, (lh, lw), scale = grid
-    desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 2, lh, lw, 3), scale, tile=tile,
-                         stride=stride)
+    tile, stride, (lh, lw), scale, lt, (tt, stt) = grid
+    desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, lt, lh, lw, 3), scale, tile=tile,
+                         stride=stride, tile_t=tt, stride_t=stt)
     tiles = v.vae_tile_split(desc)
-    ref_tiles = oracle.overlap_tiles(2, lh, lw, tile, stride, scale)
-    out_shape = (1, 1 + (2 - 1) * scale[0], lh * scale[1], lw * scale[2], 3)
+    ref_tiles = oracle.overlap_tiles(lt, lh, lw, tile, stride, scale, tt, stt)
+    assert len(tiles) == len(ref_tiles)
+    out_shape = (1, 1 + (lt - 1) * scale[0], lh * scale[1], lw * scale[2], 3)
     outs = []
     for k, tl in enumerate(ref_tiles):
         o = tl["out"]

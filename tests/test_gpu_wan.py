@@ -114,16 +114,16 @@ def _params(name):
 
 
 @functools.lru_cache(maxsize=None)
-def _oracle(name, mode):
+def _oracle(name, mode, tt=(0, 0)):
     spec = vae_synth.WORKLOADS[name]
     z = ndhwc(vae_synth.latent(spec))
     if mode == "patch":
         return oracle.decode(spec, z, _params(name))
     return oracle.decode_overlap_blend(spec, z, _params(name), spec["overlap_tile"],
-                                       spec["overlap_stride"], spec["scale"])
+                                       spec["overlap_stride"], spec["scale"], tt[0], tt[1])
 
 
-def _decode(v, name, mode, patches=(1, 1), operands="f16", repeat=1):
+def _decode(v, name, mode, patches=(1, 1), operands="f16", repeat=1, tt=(0, 0)):
     import torch
     spec = vae_synth.WORKLOADS[name]
     z = v.pad_latent(ndhwc(vae_synth.latent(spec)), spec)
@@ -133,7 +133,8 @@ def _decode(v, name, mode, patches=(1, 1), operands="f16", repeat=1):
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
     else:
         desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, z.shape, spec["scale"],
-                             tile=spec["overlap_tile"], stride=spec["overlap_stride"])
+                             tile=spec["overlap_tile"], stride=spec["overlap_stride"],
+                             tile_t=tt[0], stride_t=tt[1])
     ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(repeat):
@@ -156,6 +157,17 @@ def test_wan_shaped_decode(v, name, mode, patches, operands):
     got = host(_decode(v, name, mode, patches, operands))
     ref = _oracle(name, mode)
     assert got.shape == ref.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
+def test_wan_shaped_decode_temporal_tiles(v):
+    """Overlap-blend tiles in T as well as in space: the 3 latent frames of wan_tiny as clips
+    [0,2) [1,3) [2,3) (output frames [0,5) [4,9) [8,9)), each decoded alone with its own causal
+    start, per-frame attention and RMS norms, then blended."""
+    got = host(_decode(v, "wan_tiny", "overlap", tt=(2, 1)))
+    ref = _oracle("wan_tiny", "overlap", (2, 1))
+    assert got.shape == ref.shape == (1, 9, 64, 96, 3)
     p, m = psnr(got, ref), float(np.abs(got - ref).max())
     assert p >= 50.0 and m <= 2e-2, (p, m)
 

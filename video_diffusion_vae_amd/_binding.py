@@ -67,7 +67,7 @@ class vae_error_info_t(ctypes.Structure):
 class vae_tiling_desc_t(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in (
         "mode", "n", "t", "h", "w", "scale_t", "scale_h", "scale_w", "patches_h", "patches_w",
-        "tile_h", "tile_w", "stride_h", "stride_w")]
+        "tile_h", "tile_w", "stride_h", "stride_w", "tile_t", "stride_t")]
 
 
 class vae_tile_t(ctypes.Structure):
@@ -392,11 +392,13 @@ def vae_upsample(x, in_box, mode, st, sh, sw, y, stream=None):
     return y
 
 
-def tiling_desc(mode, latent_shape, scale, patches=(1, 1), tile=(0, 0), stride=(0, 0)):
-    """vae_tiling_desc_t from an NDHWC latent shape [N, T, H, W, C]."""
+def tiling_desc(mode, latent_shape, scale, patches=(1, 1), tile=(0, 0), stride=(0, 0), tile_t=0,
+                stride_t=0):
+    """vae_tiling_desc_t from an NDHWC latent shape [N, T, H, W, C]. ``tile`` and ``stride`` are
+    (H, W); ``tile_t`` > 0 also cuts T (overlap-blend only)."""
     n, t, h, w = latent_shape[:4]
     return vae_tiling_desc_t(mode, n, t, h, w, scale[0], scale[1], scale[2], patches[0],
-                             patches[1], tile[0], tile[1], stride[0], stride[1])
+                             patches[1], tile[0], tile[1], stride[0], stride[1], tile_t, stride_t)
 
 
 def vae_tile_split(desc):

@@ -158,13 +158,18 @@ vae_status_t check_tiling(const vae_tiling_desc_t* d) {
         VAE_TRY(bands(d->h, d->patches_h, 2, &b));
         VAE_TRY(bands(d->w, d->patches_w, 3, &b));
     } else if (d->mode == VAE_TILING_OVERLAP_BLEND) {
-        const AxisTiling ax[2] = {{d->h, d->tile_h, d->stride_h, d->scale_h},
-                                  {d->w, d->tile_w, d->stride_w, d->scale_w}};
-        for (int i = 0; i < 2; ++i) {
+        AxisTiling ax[3];
+        overlap_axes(*d, ax);
+        for (int i = 0; i < 3; ++i) {
             if (axis_is_cut(ax[i]) && (ax[i].stride < 1 || ax[i].stride > ax[i].tile))
                 return fail(VAE_ERR_UNSUPPORTED, "tile stride must be in 1..tile (no gaps)",
-                            2 + i, ax[i].stride, -1, 1);
+                            1 + i, ax[i].stride, -1, 1);
         }
+        if (axis_is_cut(ax[0]) && ax[0].scale > 1 && ax[0].stride >= ax[0].tile)
+            return fail(VAE_ERR_UNSUPPORTED,
+                        "temporal tiles must share a latent frame (stride_t < tile_t): a causal "
+                        "tile's first frame would leave a gap",
+                        1, ax[0].stride, -1, 1);
     } else {
         return fail(VAE_ERR_INVALID_ARG, "unknown tiling mode");
     }
@@ -172,6 +177,12 @@ vae_status_t check_tiling(const vae_tiling_desc_t* d) {
 }
 
 int32_t out_frames(int32_t t, int32_t scale_t) { return 1 + (t - 1) * scale_t; }
+
+void overlap_axes(const vae_tiling_desc_t& d, AxisTiling ax[3]) {
+    ax[0] = AxisTiling{d.t, d.tile_t, d.stride_t, d.scale_t, 1};
+    ax[1] = AxisTiling{d.h, d.tile_h, d.stride_h, d.scale_h, 0};
+    ax[2] = AxisTiling{d.w, d.tile_w, d.stride_w, d.scale_w, 0};
+}
 
 std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
     std::vector<vae_tile_t> tiles;
@@ -194,26 +205,33 @@ std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
                 tiles.push_back(t);
             }
     } else {
-        const AxisTiling ah{d.h, d.tile_h, d.stride_h, d.scale_h};
-        const AxisTiling aw{d.w, d.tile_w, d.stride_w, d.scale_w};
-        for (int32_t i = 0; i < axis_count(ah); ++i)
-            for (int32_t j = 0; j < axis_count(aw); ++j) {
-                int32_t hs, hn, ws, wn;
-                axis_span(ah, i, &hs, &hn);
-                axis_span(aw, j, &ws, &wn);
-                vae_tile_t t{};
-                t.index = (int32_t)tiles.size();
-                t.row = i;
-                t.col = j;
-                t.latent = vae_box_t{0, d.t, hs, hs + hn, ws, ws + wn};
-                t.out = vae_box_t{0, to, hs * d.scale_h, (hs + hn) * d.scale_h, ws * d.scale_w,
-                                  (ws + wn) * d.scale_w};
-                t.lead_h = axis_lead(ah, i);
-                t.trail_h = axis_trail(ah, i);
-                t.lead_w = axis_lead(aw, j);
-                t.trail_w = axis_trail(aw, j);
-                tiles.push_back(t);
-            }
+        AxisTiling ax[3];
+        overlap_axes(d, ax);
+        const AxisTiling &at = ax[0], &ah = ax[1], &aw = ax[2];
+        for (int32_t k = 0; k < axis_count(at); ++k)
+            for (int32_t i = 0; i < axis_count(ah); ++i)
+                for (int32_t j = 0; j < axis_count(aw); ++j) {
+                    int32_t ts, tn, hs, hn, ws, wn, ot, otn, oh, ohn, ow, own;
+                    axis_span(at, k, &ts, &tn);
+                    axis_span(ah, i, &hs, &hn);
+                    axis_span(aw, j, &ws, &wn);
+                    axis_out_span(at, k, &ot, &otn);
+                    axis_out_span(ah, i, &oh, &ohn);
+                    axis_out_span(aw, j, &ow, &own);
+                    vae_tile_t t{};
+                    t.index = (int32_t)tiles.size();
+                    t.row = i;
+                    t.col = j;
+                    t.latent = vae_box_t{ts, ts + tn, hs, hs + hn, ws, ws + wn};
+                    t.out = vae_box_t{ot, ot + otn, oh, oh + ohn, ow, ow + own};
+                    t.lead_t = axis_lead(at, k);
+                    t.trail_t = axis_trail(at, k);
+                    t.lead_h = axis_lead(ah, i);
+                    t.trail_h = axis_trail(ah, i);
+                    t.lead_w = axis_lead(aw, j);
+                    t.trail_w = axis_trail(aw, j);
+                    tiles.push_back(t);
+                }
     }
     return tiles;
 }
@@ -692,12 +710,11 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
         return fail(VAE_ERR_INVALID_ARG, "unknown merge flags");
     hipStream_t s = as_stream(stream);
     if (flags & VAE_MERGE_ZERO) VAE_TRY(launch_zero(out->data, numel(*out) * 4, s));
-    VAE_TRY(launch_merge(*tile_out, to_box(&ob, *out), tile->lead_h, tile->trail_h, tile->lead_w,
-                         tile->trail_w, *out, s));
+    VAE_TRY(launch_merge(*tile_out, to_box(&ob, *out), MergeRamps{*tile}, *out, s));
     if (flags & VAE_MERGE_FINALIZE) {
-        const AxisTiling ah{desc->h, desc->tile_h, desc->stride_h, desc->scale_h};
-        const AxisTiling aw{desc->w, desc->tile_w, desc->stride_w, desc->scale_w};
-        VAE_TRY(launch_merge_finalize(*out, ah, aw, s));
+        AxisTiling ax[3];
+        overlap_axes(*desc, ax);
+        VAE_TRY(launch_merge_finalize(*out, ax[0], ax[1], ax[2], s));
     }
     return VAE_OK;
 }

@@ -857,8 +857,8 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tens
                                 t.latent.w1});
         VAE_TRY(r.run(*latent, boxes, *out));
     } else {
-        const AxisTiling ah{desc->h, desc->tile_h, desc->stride_h, desc->scale_h};
-        const AxisTiling aw{desc->w, desc->tile_w, desc->stride_w, desc->scale_w};
+        AxisTiling ax[3];
+        overlap_axes(*desc, ax);
         for (size_t i = 0; i < tiles.size(); ++i) {
             const vae_tile_t& t = tiles[i];
             r.tile = (int32_t)i;
@@ -875,10 +875,10 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tens
             VAE_TRY(r.run(crop, one, tile_out));
             const Box ob{t.out.t0, t.out.t1, t.out.h0, t.out.h1, t.out.w0, t.out.w1};
             if (i == 0) VAE_TRY(launch_zero(out->data, numel(*out) * 4, r.s));
-            VAE_TRY(launch_merge(tile_out, ob, t.lead_h, t.trail_h, t.lead_w, t.trail_w, *out, r.s));
+            VAE_TRY(launch_merge(tile_out, ob, MergeRamps{t}, *out, r.s));
             double mb = 3.0 * (double)ts.bytes() + (i == 0 ? (double)numel(*out) * 4 : 0.0);
             if (i + 1 == tiles.size()) {
-                VAE_TRY(launch_merge_finalize(*out, ah, aw, r.s));
+                VAE_TRY(launch_merge_finalize(*out, ax[0], ax[1], ax[2], r.s));
                 mb += 2.0 * (double)numel(*out) * 4;
             }
             VAE_TRY(r.mark(VAE_KIND_MERGE, -1, 0, mb));

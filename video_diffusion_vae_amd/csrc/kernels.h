@@ -82,11 +82,19 @@ vae_status_t launch_upsample(const vae_tensor_t& x, const Box& box, int32_t mode
                              int32_t sh, int32_t sw, const vae_tensor_t& y, hipStream_t stream);
 
 // ---- tiles ----
-vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& out_box, int32_t lead_h,
-                          int32_t trail_h, int32_t lead_w, int32_t trail_w,
+// A tile's overlaps with its neighbours along T, H and W (output samples).
+struct MergeRamps {
+    int32_t lead_t, trail_t, lead_h, trail_h, lead_w, trail_w;
+    MergeRamps() = default;
+    explicit MergeRamps(const vae_tile_t& t)
+        : lead_t(t.lead_t), trail_t(t.trail_t), lead_h(t.lead_h), trail_h(t.trail_h),
+          lead_w(t.lead_w), trail_w(t.trail_w) {}
+};
+vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& out_box, const MergeRamps& r,
                           const vae_tensor_t& out, hipStream_t stream);
-vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& ah,
-                                   const AxisTiling& aw, hipStream_t stream);
+vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& at,
+                                   const AxisTiling& ah, const AxisTiling& aw,
+                                   hipStream_t stream);
 vae_status_t launch_zero(void* p, int64_t bytes, hipStream_t stream);
 // Copy x[:, box] (latent grid) into the dense tensor y (shape of the box).
 vae_status_t launch_crop(const vae_tensor_t& x, const Box& box, const vae_tensor_t& y,

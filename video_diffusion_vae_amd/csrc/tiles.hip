@@ -16,34 +16,39 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// grid (tile rows bt*bh, N). out[box] += w * tile; w = ramp_h(h) * ramp_w(w) (T is never cut).
+// Weight of tile row (tl, hl): ramp_t(tl) * ramp_h(hl).
+__device__ inline float row_weight(const MergeRamps& m, const Box& b, int tl, int hl) {
+    return ramp_weight(tl, (int)b.bt(), m.lead_t, m.trail_t) *
+           ramp_weight(hl, (int)b.bh(), m.lead_h, m.trail_h);
+}
+
+// grid (tile rows bt*bh, N). out[box] += w * tile; w = ramp_t(t) * ramp_h(h) * ramp_w(w).
 __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ tile,
                                                          float* __restrict__ out, int32_t oT,
                                                          int32_t oH, int32_t oW, int32_t C, Box b,
-                                                         int32_t lead_h, int32_t trail_h,
-                                                         int32_t lead_w, int32_t trail_w) {
+                                                         MergeRamps m) {
     const int n = blockIdx.y;
     const int64_t r = blockIdx.x;
     const int tl = (int)(r / b.bh()), hl = (int)(r % b.bh());
-    const float wh = ramp_weight(hl, (int)b.bh(), lead_h, trail_h);
+    const float wh = row_weight(m, b, tl, hl);
     const float* src = tile + (((int64_t)n * b.bt() + tl) * b.bh() + hl) * b.bw() * C;
     float* dst = out + ((((int64_t)n * oT + b.t0 + tl) * oH + b.h0 + hl) * oW + b.w0) * C;
     const int seg = (int)b.bw() * C;
     for (int e = threadIdx.x; e < seg; e += kThreads) {
         const int wl = e / C;
-        dst[e] += wh * ramp_weight(wl, (int)b.bw(), lead_w, trail_w) * src[e];
+        dst[e] += wh * ramp_weight(wl, (int)b.bw(), m.lead_w, m.trail_w) * src[e];
     }
 }
 
-// grid (rows oT*oH, N). out /= S_h(h) * S_w(w).
+// grid (rows oT*oH, N). out /= S_t(t) * S_h(h) * S_w(w).
 __global__ __launch_bounds__(kThreads) void merge_finalize_kernel(float* __restrict__ out,
                                                                   int32_t oT, int32_t oH,
                                                                   int32_t oW, int32_t C,
-                                                                  AxisTiling ah, AxisTiling aw) {
+                                                                  AxisTiling at, AxisTiling ah,
+                                                                  AxisTiling aw) {
     const int n = blockIdx.y;
     const int64_t r = blockIdx.x;
-    const int h = (int)(r % oH);
-    const float sh = axis_weight_sum(ah, h);
+    const float sh = axis_weight_sum(at, (int)(r / oH)) * axis_weight_sum(ah, (int)(r % oH));
     float* row = out + ((int64_t)n * oT * oH + r) * oW * C;
     const int seg = oW * C;
     for (int e = threadIdx.x; e < seg; e += kThreads) {
@@ -64,19 +69,17 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void merge_rows_kernel(const float* __restrict__ tile,
                                                               float* __restrict__ out, int32_t oT,
                                                               int32_t oH, int32_t oW, int32_t C,
-                                                              Box b, int32_t lead_h,
-                                                              int32_t trail_h, int32_t lead_w,
-                                                              int32_t trail_w) {
+                                                              Box b, MergeRamps m) {
     extern __shared__ float col[];          // ramp_w of each tile column
     const int bw = (int)b.bw(), bh = (int)b.bh();
-    for (int i = threadIdx.x; i < bw; i += kThreads) col[i] = ramp_weight(i, bw, lead_w, trail_w);
+    for (int i = threadIdx.x; i < bw; i += kThreads) col[i] = ramp_weight(i, bw, m.lead_w, m.trail_w);
     __syncthreads();
     const int n = blockIdx.y;
     const int64_t rows = b.bt() * bh;
     const int seg = bw * C;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         const int tl = (int)(r / bh), hl = (int)(r % bh);
-        const float wh = ramp_weight(hl, bh, lead_h, trail_h);
+        const float wh = row_weight(m, b, tl, hl);
         const float* src = tile + (((int64_t)n * b.bt() + tl) * bh + hl) * (int64_t)seg;
         float* dst = out + ((((int64_t)n * oT + b.t0 + tl) * oH + b.h0 + hl) * oW + b.w0) * C;
         if constexpr (VEC) {
@@ -108,6 +111,7 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void merge_finalize_rows_kernel(float* __restrict__ out,
                                                                        int32_t oT, int32_t oH,
                                                                        int32_t oW, int32_t C,
+                                                                       AxisTiling at,
                                                                        AxisTiling ah,
                                                                        AxisTiling aw) {
     extern __shared__ float col[];          // S_w of each output column
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void merge_finalize_rows_kernel(float* __
     const int64_t rows = (int64_t)oT * oH;
     const int seg = oW * C;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const float sh = axis_weight_sum(ah, (int)(r % oH));
+        const float sh = axis_weight_sum(at, (int)(r / oH)) * axis_weight_sum(ah, (int)(r % oH));
         float* row = out + ((int64_t)n * rows + r) * seg;
         if constexpr (VEC) {
             float4* r4 = reinterpret_cast<float4*>(row);
@@ -173,8 +177,7 @@ __global__ __launch_bounds__(kThreads) void crop_kernel(const uint8_t* __restric
 
 }  // namespace
 
-vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& b, int32_t lead_h,
-                          int32_t trail_h, int32_t lead_w, int32_t trail_w,
+vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& b, const MergeRamps& m,
                           const vae_tensor_t& out, hipStream_t stream) {
     if (b.volume() == 0 || out.n == 0) return VAE_OK;
     const float* tp = static_cast<const float*>(tile_out.data);
@@ -189,24 +192,25 @@ vae_status_t launch_merge(const vae_tensor_t& tile_out, const Box& b, int32_t le
         if (vec)
             hipLaunchKernelGGL(merge_rows_kernel<true>, grid, dim3(kThreads), lds, stream, tp, op,
                                (int32_t)out.t, (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, b,
-                               lead_h, trail_h, lead_w, trail_w);
+                               m);
         else
             hipLaunchKernelGGL(merge_rows_kernel<false>, grid, dim3(kThreads), lds, stream, tp, op,
                                (int32_t)out.t, (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, b,
-                               lead_h, trail_h, lead_w, trail_w);
+                               m);
         VAE_HIP_CHECK(hipGetLastError());
         return VAE_OK;
     }
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(b.bt() * b.bh()), (unsigned)out.n),
                        dim3(kThreads), 0, stream, static_cast<const float*>(tile_out.data),
                        static_cast<float*>(out.data), (int32_t)out.t, (int32_t)out.h,
-                       (int32_t)out.w, (int32_t)out.c, b, lead_h, trail_h, lead_w, trail_w);
+                       (int32_t)out.w, (int32_t)out.c, b, m);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
 
-vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& ah,
-                                   const AxisTiling& aw, hipStream_t stream) {
+vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& at,
+                                   const AxisTiling& ah, const AxisTiling& aw,
+                                   hipStream_t stream) {
     if (numel(out) == 0) return VAE_OK;
     float* op = static_cast<float*>(out.data);
     if (out.w <= kMaxLdsColumns) {
@@ -216,17 +220,17 @@ vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& ah
         if ((out.w * out.c) % 4 == 0 && (uintptr_t)op % 16 == 0)
             hipLaunchKernelGGL(merge_finalize_rows_kernel<true>, grid, dim3(kThreads), lds, stream,
                                op, (int32_t)out.t, (int32_t)out.h, (int32_t)out.w, (int32_t)out.c,
-                               ah, aw);
+                               at, ah, aw);
         else
             hipLaunchKernelGGL(merge_finalize_rows_kernel<false>, grid, dim3(kThreads), lds,
                                stream, op, (int32_t)out.t, (int32_t)out.h, (int32_t)out.w,
-                               (int32_t)out.c, ah, aw);
+                               (int32_t)out.c, at, ah, aw);
         VAE_HIP_CHECK(hipGetLastError());
         return VAE_OK;
     }
     hipLaunchKernelGGL(merge_finalize_kernel, dim3((unsigned)(out.t * out.h), (unsigned)out.n),
                        dim3(kThreads), 0, stream, static_cast<float*>(out.data), (int32_t)out.t,
-                       (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, ah, aw);
+                       (int32_t)out.h, (int32_t)out.w, (int32_t)out.c, at, ah, aw);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
