@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "decoded Mpixel-frames/s (720p VAE decode, 1 GPU) + conv MFMA % of peak"
 CSRC = os.path.join(ROOT, "video_diffusion_vae_amd", "csrc")
 CONV_SOURCES = sorted(os.path.join("video_diffusion_vae_amd", "csrc", f) for f in os.listdir(CSRC)
-                      if f.startswith("conv3d") or f in ("kernels.h", "common.h"))
+                      if f.startswith("conv3d") or f in ("kernels.h", "common.h", "decoder.hip"))
 CONV_KERNEL = "conv3d_mfma_kernel"
 COPY_KERNEL = "upsample_kernel"
 OPERANDS = {
@@ -94,6 +94,13 @@ WORKLOADS = {
     "ltx2": ("LTX2_720P", (1, 4), "2x3"),
     "wan": ("WAN_720P", (1, 4), "2x3"),
 }
+
+
+def activations_note(operands):
+    if operands == "f16":
+        return ("fp32 residual stream; res-block conv1 outputs fp16; norm outputs bf16, or fp16 "
+                "where an fp16-operand conv reads them")
+    return "fp32 between ops, bf16 norm outputs inside res blocks"
 
 
 def workload_name(kind, mode, tile_t=0, stride_t=0):
@@ -396,7 +403,7 @@ def main():
                    "output": [out_shape[0], out_shape[4]] + list(out_shape[1:4]),
                    "parallelism": "none (1 GPU)",
                    "operands": OPERANDS[args.operands],
-                   "activations": "fp32 between ops, bf16 norm outputs inside res blocks",
+                   "activations": activations_note(args.operands),
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
         "roofline": roofline, "kernels": summary, "standalone_passes": passes, "timing": timing,
         "attention_tflop_per_step": (round(kinds["attn"]["flops"] / args.steps / 1e12, 3)

@@ -231,7 +231,7 @@ VAE_API vae_status_t vae_conv_weight_pack_f16(const void* weight, int32_t cout, 
  *  boxes: the patches owning the statistics (n_boxes >= 1; NULL with n_boxes == 1 = whole tensor).
  *         The apply step writes y over every box.
  *  gamma, beta: [C] fp32 (device) or NULL (1 and 0).
- *  x: bf16 or fp32.
+ *  x: bf16, fp16 or fp32 (fp16: a conv output stored at half width inside a residual block).
  *  y: same shape as x; dtype bf16, fp32 or fp16 (it may differ from x: an fp32 activation
  *     normalised into the bf16 or fp16 operand of the next convolution). It may alias x when the
  *     dtypes match.
@@ -275,7 +275,7 @@ VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t*
  * statistics from other patches (P4, commit messages on the Qwen-Image / Wan adapters and on the
  * HunyuanVideo 1.5 encoder: RMS norms that reduce over channels need nothing sharded). The pages
  * give no formula; this is the root mean square of the channel vector with eps inside the root.
- *  x: bf16 or fp32, C % 8 == 0 and C / 8 dividing 256 (else UNSUPPORTED with info).
+ *  x: bf16, fp16 or fp32, C % 8 == 0 and C / 8 dividing 256 (else UNSUPPORTED with info).
  *  gamma, beta: [C] fp32 (device) or NULL (1 and 0).
  *  y: x's shape; bf16, fp16 or fp32. It may alias x when the dtypes match.
  */
@@ -419,8 +419,10 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * whose own input is bf16 or fp16 (possibly through its fused D2S and NEAREST ops, which copy),
  * fp16 operands instead: the producing op stores its output in
  * fp16 (one rounding to 11 significant bits) and the conv runs at the bf16 rate
- * (vae_conv3d_causal with an fp16 x). no_split does not apply to it. Activations must stay below
- * 65504 in magnitude there.
+ * (vae_conv3d_causal with an fp16 x). no_split does not apply to it. The flag also stores the
+ * output of the first conv of each RES and RES_RMS block, which only its block's second norm
+ * reads, in fp16 instead of fp32 (half the bytes written and read back). Activations must stay
+ * below 65504 in magnitude in both places.
  * The parameter pointers come in plan order:
  *  conv -> (weight, bias);
  *  GN or RMS -> (gamma, beta);

@@ -293,6 +293,10 @@ GN_CASES = [
     ("bf16>f32", (1, 2, 6, 7, 256), 32, ([3], [])),
     ("f32>f16", (1, 3, 11, 20, 128), 32, ([], [5, 10, 15])),
     ("bf16>f16", (1, 2, 8, 10, 256), 32, ([4], [])),
+    # fp16 inputs: the first conv of a residual block stores its output in fp16
+    ("f16>bf16", (1, 3, 12, 20, 128), 32, ([5], [10])),
+    ("f16>f16", (1, 2, 8, 10, 1024), 32, ([], [1, 5, 9])),
+    ("f16>f32", (1, 2, 6, 7, 256), 32, ([3], [])),
 ]
 
 
@@ -311,6 +315,8 @@ def test_groupnorm_silu_patch_stats(v, case):
     idt, odt = dts.split(">")
     n, t, h, w, c = shape
     x = ndhwc(vae_synth.normal((n, c, t, h, w), [20, c, h], scale=1.5, mean=0.3, dtype=idt))
+    if idt == "f16":
+        x = round_f16(x)             # the oracle sees exactly the values the GPU reads
     gamma = vae_synth.normal((c,), [21, c], scale=0.2, mean=1.0)
     beta = vae_synth.normal((c,), [22, c], scale=0.1)
     ref = oracle.silu(oracle.group_norm(x, groups, 1e-6, gamma, beta))
@@ -604,9 +610,6 @@ def test_conv3d_f16_argument_rules(v):
     x20 = torch.zeros((1, 2, 4, 4, 20), device="cuda", dtype=torch.float16)
     with pytest.raises(v.VaeError) as e:        # fp16 needs the MFMA path (Cin % 32)
         v.vae_conv3d_causal(x20, w[..., :20].contiguous(), None, None, y)
-    assert e.value.status == v.VAE_ERR_UNSUPPORTED
-    with pytest.raises(v.VaeError) as e:        # GroupNorm does not read fp16
-        v.vae_groupnorm_silu(x16, None, 8, 1e-6, None, None, True, y)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
 
 

@@ -16,7 +16,8 @@ import pytest
 
 import oracle
 import vae_synth
-from _util import ndhwc, dev, host, rel_max_abs, psnr, bf16_round_bound, f16_round_bound
+from _util import (ndhwc, dev, host, rel_max_abs, psnr, bf16_round_bound, f16_round_bound,
+                   round_f16)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +38,9 @@ RMS_CASES = [
     ((1, 1, 7, 9, 32), "f32", "f32", True),
     ((1, 2, 4, 4, 2048), "f32", "bf16", False),
     ((1, 3, 3, 3, 512), "bf16", "bf16", True),
+    # fp16 inputs: the first conv of a residual block stores its output in fp16
+    ((1, 3, 5, 7, 128), "f16", "bf16", True),
+    ((1, 2, 3, 5, 1024), "f16", "f16", True),
 ]
 
 
@@ -46,6 +50,8 @@ def test_rmsnorm_matches_oracle(v, case):
     shape, idt, odt, act = case
     n, t, h, w, c = shape
     x = ndhwc(vae_synth.normal((n, c, t, h, w), [50, c], scale=1.7, mean=0.2, dtype=idt))
+    if idt == "f16":
+        x = round_f16(x)             # the oracle sees exactly the values the GPU reads
     gamma = vae_synth.normal((c,), [51, c], scale=0.2, mean=1.0)
     beta = vae_synth.normal((c,), [52, c], scale=0.1)
     ref = oracle.rms_norm(x, 1e-6, gamma, beta)

@@ -96,14 +96,12 @@ vae_status_t box_list(const vae_tensor_t& x, const vae_box_t* boxes, int32_t n_b
 
 vae_status_t check_gn(const vae_tensor_t* x, int32_t groups) {
     VAE_TRY(check_tensor(x, "x"));
-    if (x->dtype == VAE_DTYPE_F16)
-        return fail(VAE_ERR_UNSUPPORTED, "group norm reads bf16 or fp32 (fp16 is an output only)");
     if (groups < 1 || x->c % groups != 0)
         return fail(VAE_ERR_UNSUPPORTED, "channels must be divisible by groups", 4, x->c, groups);
     if (!gn_shape_supported(*x, groups))
         return fail(VAE_ERR_UNSUPPORTED,
                     "group norm needs C/vec to divide 256 and groups aligned to 16-byte vectors",
-                    4, x->c, x->dtype == VAE_DTYPE_BF16 ? 8 : 4);
+                    4, x->c, elem_size(x->dtype) == 2 ? 8 : 4);
     return VAE_OK;
 }
 
@@ -593,8 +591,6 @@ VAE_API vae_status_t vae_rmsnorm_silu(const vae_tensor_t* x, float eps, const fl
     clear_error();
     VAE_TRY(check_tensor(x, "x"));
     VAE_TRY(check_tensor(y, "y"));
-    if (x->dtype == VAE_DTYPE_F16)
-        return fail(VAE_ERR_UNSUPPORTED, "rms norm reads bf16 or fp32 (fp16 is an output only)");
     if (!rms_shape_supported(x->c))
         return fail(VAE_ERR_UNSUPPORTED, "rms norm needs C % 8 == 0 and C / 8 dividing 256", 4,
                     x->c, 8);

@@ -107,6 +107,17 @@ int32_t gn_silu_dtype(const vae_decoder& d, int i) {
 // block stores bf16 directly: the same rounding, done once at the store, with half the bytes.
 // With fp16 operands for the next conv, the block stores fp16 (the one rounding that conv's
 // operand gets).
+// The first conv of a RES or RES_RMS block writes the tensor that only the block's second norm
+// reads. With fp16 operands it is stored in fp16: the norm reads 2 bytes a value instead of 4,
+// and the conv writes half as much.
+// (The conv must run on the matrix cores, which hold the fp16 output path: Cin % 32 == 0.)
+int32_t res_mid_dtype(const vae_decoder& d, int32_t width) {
+    return (d.flags & VAE_DECODE_F16_OPERANDS) && d.dtype == VAE_DTYPE_BF16 &&
+                   d.act_dtype == VAE_DTYPE_F32 && width % 32 == 0
+               ? VAE_DTYPE_F16
+               : d.act_dtype;
+}
+
 int32_t res_out_dtype(const vae_decoder& d, size_t i) {
     const int j = fed_conv(d.layers.data(), (int)d.layers.size(), (int)i);
     if (j >= 0 && conv_f16(d, j)) return VAE_DTYPE_F16;
@@ -281,7 +292,7 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         if (l.op == VAE_OP_RES) {
             Shape xs = cur, ys = cur;
             xs.dtype = d.dtype;
-            ys.dtype = d.act_dtype;
+            ys.dtype = res_mid_dtype(d, l.cin);
             fused(xs, ys, 1);
         }
         if (l.op == VAE_OP_D2S || l.op == VAE_OP_NEAREST) {
@@ -457,7 +468,7 @@ struct Runner {
                 const int b2 = free_buf(cur_buf, b1);
                 Shape gs = shape_of(cur), as = shape_of(cur);
                 gs.dtype = d->dtype;
-                as.dtype = d->act_dtype;
+                as.dtype = res_mid_dtype(*d, l.cin);
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
                 VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, true));
@@ -475,7 +486,7 @@ struct Runner {
                 const int b2 = free_buf(cur_buf, b1);
                 Shape gs = shape_of(cur), as = shape_of(cur);
                 gs.dtype = d->dtype;
-                as.dtype = d->act_dtype;
+                as.dtype = res_mid_dtype(*d, l.cin);
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 stats_ready = false;
                 VAE_TRY(rms(cur, t1, d->ptrs[p], d->ptrs[p + 1], layer));

@@ -377,7 +377,7 @@ void apply_launch(const vae_tensor_t& x, const Box& box, int32_t groups, const f
 }  // namespace
 
 bool gn_shape_supported(const vae_tensor_t& x, int32_t groups) {
-    const int64_t V = x.dtype == VAE_DTYPE_BF16 ? 8 : 4;
+    const int64_t V = elem_size(x.dtype) == 2 ? 8 : 4;
     if (groups <= 0 || x.c % groups != 0 || x.c % V != 0) return false;
     const int64_t cv = x.c / V;
     if (cv > kThreads || kThreads % cv != 0) return false;
@@ -398,6 +398,10 @@ vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_
     if (x.dtype == VAE_DTYPE_BF16)
         hipLaunchKernelGGL(gn_stats_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(x.data), (int32_t)x.t, (int32_t)x.h,
+                           (int32_t)x.w, (int32_t)x.c, groups, g, ws);
+    else if (x.dtype == VAE_DTYPE_F16)
+        hipLaunchKernelGGL(gn_stats_kernel<_Float16>, grid, dim3(kThreads), 0, stream,
+                           static_cast<const _Float16*>(x.data), (int32_t)x.t, (int32_t)x.h,
                            (int32_t)x.w, (int32_t)x.c, groups, g, ws);
     else
         hipLaunchKernelGGL(gn_stats_kernel<float>, grid, dim3(kThreads), 0, stream,
@@ -432,7 +436,16 @@ vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t grou
                              bool silu, const vae_tensor_t& y, hipStream_t stream) {
     if (box.volume() == 0 || x.n == 0) return VAE_OK;
     const bool xb = x.dtype == VAE_DTYPE_BF16, yb = y.dtype == VAE_DTYPE_BF16;
-    if (y.dtype == VAE_DTYPE_F16) {   // the fp16 operand of the next conv
+    if (x.dtype == VAE_DTYPE_F16) {   // an fp16 conv output (the middle of a residual block)
+        if (y.dtype == VAE_DTYPE_F16)
+            apply_launch<_Float16, _Float16>(x, box, groups, mean_rstd, gamma, beta, silu, y,
+                                             stream);
+        else if (yb)
+            apply_launch<_Float16, uint16_t>(x, box, groups, mean_rstd, gamma, beta, silu, y,
+                                             stream);
+        else
+            apply_launch<_Float16, float>(x, box, groups, mean_rstd, gamma, beta, silu, y, stream);
+    } else if (y.dtype == VAE_DTYPE_F16) {   // the fp16 operand of the next conv
         if (xb)
             apply_launch<uint16_t, _Float16>(x, box, groups, mean_rstd, gamma, beta, silu, y,
                                              stream);

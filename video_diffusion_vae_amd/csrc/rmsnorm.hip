@@ -107,6 +107,7 @@ vae_status_t launch_rms_norm(const vae_tensor_t& x, float eps, const float* gamm
         return fail(VAE_ERR_UNSUPPORTED, "rms norm needs C % 8 == 0 and C / 8 dividing 256", 4,
                     x.c, 8);
     if (x.dtype == VAE_DTYPE_F32) rms_out<float>(x, eps, gamma, beta, silu, y, stream);
+    else if (x.dtype == VAE_DTYPE_F16) rms_out<_Float16>(x, eps, gamma, beta, silu, y, stream);
     else rms_out<uint16_t>(x, eps, gamma, beta, silu, y, stream);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
