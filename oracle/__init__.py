@@ -35,15 +35,17 @@ Parity status of each function:
   tensor values, so a decoder's output is pinned only through its parts and the invariants above.
 """
 from .layers import (causal_conv3d, conv3d_valid, causal_time_pad, group_norm, silu,
-                     nearest_upsample, depth_to_space, rms_norm, softmax, frame_attention)
+                     nearest_upsample, depth_to_space, space_to_depth, rms_norm, softmax,
+                     frame_attention)
 from .stats import group_moments, chan_combine, normalize_with
 from .tiling import (bands, axis_tiles, patch_tiles, overlap_tiles, ramp_1d, axis_weight_sum)
 from .decoder import (decode, decode_patch_halo, decode_overlap_blend, merge_tiles,
-                      output_shape)
+                      output_shape, encode, encode_patch_halo, encode_overlap_blend)
 
 __all__ = [
     "causal_conv3d", "conv3d_valid", "causal_time_pad", "group_norm", "silu", "nearest_upsample",
-    "depth_to_space", "rms_norm", "softmax", "frame_attention", "group_moments", "chan_combine",
+    "depth_to_space", "space_to_depth", "rms_norm", "softmax", "frame_attention",
+    "group_moments", "chan_combine", "encode", "encode_patch_halo", "encode_overlap_blend",
     "normalize_with", "bands", "axis_tiles",
     "patch_tiles", "overlap_tiles", "ramp_1d", "axis_weight_sum", "decode", "decode_patch_halo",
     "decode_overlap_blend", "merge_tiles", "output_shape",

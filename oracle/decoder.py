@@ -25,7 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 from .layers import causal_conv3d, causal_time_pad, conv3d_valid, group_norm, silu, \
-    nearest_upsample, depth_to_space, rms_norm, frame_attention
+    nearest_upsample, depth_to_space, space_to_depth, rms_norm, frame_attention
 from .stats import group_moments, chan_combine, normalize_with
 from .tiling import bands, overlap_tiles, ramp_1d
 
@@ -42,6 +42,9 @@ def output_shape(spec: dict, latent_shape):
             t, h, w, c = st * t - (st - 1), h * sh, w * sw, c // (st * sh * sw)
         elif k == "nearest":
             h, w = h * op["sh"], w * op["sw"]
+        elif k == "s2d":
+            st, sh, sw = op["st"], op["sh"], op["sw"]
+            t, h, w, c = (t + st - 1) // st, h // sh, w // sw, c * st * sh * sw
     return (n, t, h, w, c)
 
 
@@ -87,9 +90,17 @@ def decode(spec: dict, z: np.ndarray, params: list) -> np.ndarray:
             h = depth_to_space(h, op["st"], op["sh"], op["sw"])
         elif k == "nearest":
             h = nearest_upsample(h, op["sh"], op["sw"])
+        elif k == "s2d":
+            h = space_to_depth(h, op["st"], op["sh"], op["sw"])
         else:
             raise ValueError(k)
     return h
+
+
+def encode(spec: dict, x: np.ndarray, params: list) -> np.ndarray:
+    """Untiled encode of the NDHWC video ``x``: the same plan executor as ``decode``; an encoder
+    plan narrows with ``s2d`` folds where a decoder widens with ``d2s``."""
+    return decode(spec, x, params)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -143,13 +154,20 @@ def _gn_patches(patches, groups, eps, gamma, beta, act):
     return out
 
 
-def decode_patch_halo(spec: dict, z: np.ndarray, params: list, grid) -> np.ndarray:
-    """Decode with the latent cut into ph x pw patches (bands along H and W)."""
+def decode_patch_halo(spec: dict, z: np.ndarray, params: list, grid, unit=(1, 1)) -> np.ndarray:
+    """Decode with the latent cut into ph x pw patches (bands along H and W).
+
+    ``unit``: the bands are cut in whole multiples of it (rows, columns). An encoder plan folds
+    space into channels, so its bands must be multiples of the total fold ("Add tiled VAE
+    parallelism & extended model support", encoder commit: bands in whole multiples of what the
+    VAE narrows the axis by, the first ranks taking one band more)."""
     ph, pw = grid
     groups, eps = spec["groups"], spec["eps"]
     z = np.asarray(z, dtype=np.float64)
-    hb = bands(z.shape[2], ph)
-    wb = bands(z.shape[3], pw)
+    uh, uw = unit
+    assert z.shape[2] % uh == 0 and z.shape[3] % uw == 0, (z.shape, unit)
+    hb = [(s * uh, n * uh) for s, n in bands(z.shape[2] // uh, ph)]
+    wb = [(s * uw, n * uw) for s, n in bands(z.shape[3] // uw, pw)]
     patches = [[z[:, :, h0:h0 + hs, w0:w0 + ws] for (w0, ws) in wb] for (h0, hs) in hb]
     it = iter(params)
     for op in spec["layers"]:
@@ -195,6 +213,10 @@ def decode_patch_halo(spec: dict, z: np.ndarray, params: list, grid) -> np.ndarr
                        for row in patches]
         elif k == "nearest":
             patches = [[nearest_upsample(p, op["sh"], op["sw"]) for p in row] for row in patches]
+        elif k == "s2d":
+            # bands are cut in whole multiples of the fold, so every patch folds on its own
+            patches = [[space_to_depth(p, op["st"], op["sh"], op["sw"]) for p in row]
+                       for row in patches]
         else:
             raise ValueError(k)
     return np.concatenate([np.concatenate(row, axis=3) for row in patches], axis=2)
@@ -232,5 +254,38 @@ def decode_overlap_blend(spec: dict, z: np.ndarray, params: list, tile_hw, strid
         y = decode(spec, z[:, t0:t1, h0:h1, w0:w1], params)    # own borders, own statistics
         o = tl["out"]
         assert y.shape[1:4] == (o[1] - o[0], o[3] - o[2], o[5] - o[4]), (y.shape, o)
+        outs.append(y)
+    return merge_tiles(outs, tiles, out_shape)
+
+
+# ------------------------------------------------------------------------------------------------
+# Encode
+# ------------------------------------------------------------------------------------------------
+
+def encode_patch_halo(spec: dict, x: np.ndarray, params: list, grid) -> np.ndarray:
+    """Patch-halo encode: bands in whole multiples of the plan's spatial fold (spec["down"])."""
+    return decode_patch_halo(spec, x, params, grid, unit=tuple(spec["down"][1:]))
+
+
+def encode_overlap_blend(spec: dict, x: np.ndarray, params: list, tile_hw, stride_hw) -> np.ndarray:
+    """Serial overlap-blend tiled encode of the NDHWC video ``x``.
+
+    The tile grid is cut on the latent grid (``tile_hw``, ``stride_hw`` in latent rows: 16 / 14 are
+    512 / 448 pixels at a fold of 32, i.e. 64 pixels of overlap). Each tile encodes its pixel crop
+    alone, with its own borders and statistics, T whole, and the latent tiles are blended with the
+    same separable ramps as decoded tiles, in latent space ("[Feature] Support VAE tiling parallel
+    encode for LTX-2", Purpose and review thread: sample tiles 512 with stride 448, per-tile latent
+    shapes, a blend of the latents)."""
+    x = np.asarray(x, dtype=np.float64)
+    dt, dh, dw = spec["down"]
+    out_shape = output_shape(spec, x.shape)
+    _, lt, lh, lw, _ = out_shape
+    assert x.shape[2] == lh * dh and x.shape[3] == lw * dw, (x.shape, out_shape)
+    tiles = overlap_tiles(lt, lh, lw, tile_hw, stride_hw, (1, 1, 1))
+    outs = []
+    for tl in tiles:
+        _, _, h0, h1, w0, w1 = tl["latent"]
+        y = decode(spec, x[:, :, h0 * dh:h1 * dh, w0 * dw:w1 * dw], params)
+        assert y.shape[1:4] == (lt, h1 - h0, w1 - w0), (y.shape, tl)
         outs.append(y)
     return merge_tiles(outs, tiles, out_shape)

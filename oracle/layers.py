@@ -136,6 +136,27 @@ def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
     return np.ascontiguousarray(y[:, st - 1:])
 
 
+def space_to_depth(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
+    """Space-to-depth downsampling with a causal front pad: the fold of the encoder.
+
+    Most LTX-2 encoder downsamplers fold space into channels after a stride-1 convolution
+    ("Add tiled VAE parallelism & extended model support", LTX-2 encoder commit message; the same
+    page: a downsampler that folds reads one input position per output one). The pages give
+    neither the channel order nor the frame rule. Here, the mirror of ``depth_to_space``: st-1
+    copies of frame 0 go in front (T frames become (T + st - 1) / st, so 121 -> 61 -> 31 -> 16),
+    and input (st*t + dt, sh*h + dh, sw*w + dw, c) of the padded clip lands in output channel
+    ((dt*sh + dh)*sw + dw)*C + c at (t, h, w). ``depth_to_space`` of the result gives ``x`` back.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, t, h, w, c = x.shape
+    assert (t + st - 1) % st == 0 and h % sh == 0 and w % sw == 0, (x.shape, st, sh, sw)
+    xp = np.concatenate([np.repeat(x[:, :1], st - 1, axis=1), x], axis=1) if st > 1 else x
+    to = xp.shape[1] // st
+    y = xp.reshape(n, to, st, h // sh, sh, w // sw, sw, c)
+    y = y.transpose(0, 1, 3, 5, 2, 4, 6, 7).reshape(n, to, h // sh, w // sw, st * sh * sw * c)
+    return np.ascontiguousarray(y)
+
+
 def rms_norm(x: np.ndarray, eps: float, gamma=None, beta=None) -> np.ndarray:
     """Per-position RMS normalisation over the channels: y = x / sqrt(mean_c(x^2) + eps) * gamma
     + beta.

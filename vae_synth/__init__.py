@@ -231,9 +231,63 @@ for _op in WAN_TINY["layers"]:
                 not (_k == "cout" and _op.get("f32_out")):
             _op[_k] //= 4
 
+# LTX-2-shaped encoder: video [1,3,121,704,1280] -> latent [1,256,16,22,40] (mean and log-variance,
+# 128 channels each), widths 128/256/512/1024. Each downsampler is a stride-1 causal conv to
+# C_next / 8 channels, then a (2,2,2) space-to-depth fold with the causal front pad (121 -> 61 -> 31
+# -> 16 frames); the input is patchified by a (1,4,4) fold first.
+_LTX2_ENC_LAYERS = [
+    {"op": "s2d", "st": 1, "sh": 4, "sw": 4},                       # patchify: 3 -> 48 channels
+    {"op": "conv", "cin": 48, "cout": 128},
+    {"op": "res", "c": 128},
+    {"op": "res", "c": 128},
+    {"op": "conv", "cin": 128, "cout": 32},
+    {"op": "s2d", "st": 2, "sh": 2, "sw": 2},
+    {"op": "res", "c": 256},
+    {"op": "res", "c": 256},
+    {"op": "conv", "cin": 256, "cout": 64},
+    {"op": "s2d", "st": 2, "sh": 2, "sw": 2},
+    {"op": "res", "c": 512},
+    {"op": "res", "c": 512},
+    {"op": "conv", "cin": 512, "cout": 128},
+    {"op": "s2d", "st": 2, "sh": 2, "sw": 2},
+    {"op": "res", "c": 1024},
+    {"op": "res", "c": 1024},
+    {"op": "gn_silu"},
+    {"op": "conv", "cin": 1024, "cout": 256, "f32_out": True},
+]
+
+LTX2_ENC_720P = {
+    "name": "ltx2_enc_720p",
+    "kind": "encoder",
+    "dtype": "bf16",
+    "input": (1, 3, 121, 704, 1280),
+    "groups": 32, "eps": 1e-6,
+    "layers": _LTX2_ENC_LAYERS,
+    "down": (8, 32, 32),                  # video -> latent: T = (T_in + 7) / 8, H / 32, W / 32
+    "patch_grid": (1, 4),
+    # tiles on the latent grid: 16 / 14 latent rows are 512 / 448 pixels (64 pixels of overlap)
+    "overlap_tile": (16, 16), "overlap_stride": (14, 14),
+}
+
+
+def with_input(spec: dict, input_shape, name: str, **extra) -> dict:
+    """A copy of an encoder ``spec`` with another input shape (and other tiling fields)."""
+    out = copy.deepcopy(spec)
+    out["input"] = tuple(input_shape)
+    out["name"] = name
+    out.update(extra)
+    return out
+
+
+LTX2_ENC_TINY = with_input(LTX2_ENC_720P, (1, 3, 9, 64, 96), "ltx2_enc_tiny", patch_grid=(1, 3),
+                           overlap_tile=(2, 2), overlap_stride=(1, 1))
+LTX2_ENC_SMALL = with_input(LTX2_ENC_720P, (1, 3, 9, 64, 160), "ltx2_enc_small",
+                            patch_grid=(2, 2), overlap_tile=(2, 3), overlap_stride=(2, 2))
+
 WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
                                     LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2, WAN_720P, WAN_SMALL,
-                                    WAN_720P_1F, WAN_720P_6F, WAN_TINY)}
+                                    WAN_720P_1F, WAN_720P_6F, WAN_TINY, LTX2_ENC_720P,
+                                    LTX2_ENC_TINY, LTX2_ENC_SMALL)}
 
 
 # ----------------------------------------------------------------------------------------------
@@ -269,7 +323,10 @@ def uniform(shape, seed, lo: float = -1.0, hi: float = 1.0, dtype: str = "f32") 
 
 
 def latent(spec: dict, seed=0) -> np.ndarray:
-    """The decoder input, NCDHW float32 (bf16-exact for bf16 workloads)."""
+    """The plan's input, NCDHW float32 (bf16-exact for bf16 workloads): a N(0, 1) latent for a
+    decoder, a U(-1, 1) video for an encoder."""
+    if spec.get("kind") == "encoder":
+        return uniform(spec["input"], seed, dtype=spec["dtype"])
     shape = spec["latent"] if "latent" in spec else spec["input"]
     return normal(shape, seed, dtype=spec["dtype"])
 
@@ -307,7 +364,7 @@ def attn_params(index: int, c: int, dtype: str, affine_seed=None) -> dict:
 
 def walk_plan(spec: dict):
     """Yield (op, channels_in, channels_out) along the plan, following the channel count only."""
-    c = spec["latent"][1]
+    c = (spec["latent"] if "latent" in spec else spec["input"])[1]
     for op in spec["layers"]:
         kind = op["op"]
         if kind == "conv":
@@ -323,6 +380,10 @@ def walk_plan(spec: dict):
             c //= k
         elif kind == "nearest":
             yield op, c, c
+        elif kind == "s2d":
+            k = op["st"] * op["sh"] * op["sw"]
+            yield op, c, c * k
+            c *= k
         else:
             raise ValueError(f"unknown op {kind!r}")
 
