@@ -325,6 +325,23 @@ VAE_API vae_status_t vae_upsample(const vae_tensor_t* x, const vae_box_t* box, i
                                   vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Space-to-depth (the encoder's fold)                                                        */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * The encoder's downsampling fold, the mirror of VAE_UPSAMPLE_D2S (P4, encoder commits: most
+ * LTX-2 downsamplers fold space into channels after a stride-1 convolution, one input position
+ * per output): st-1 copies of frame 0 go in front (causal), then
+ *   y[t, h, w, ((dt*sh+dh)*sw+dw)*C + c] = x[max(st*t+dt-(st-1), 0), sh*h+dh, sw*w+dw, c].
+ * T frames become (T + st - 1) / st; vae_upsample with VAE_UPSAMPLE_D2S and the same factors
+ * gives x back.
+ *  x: [N,T,H,W,C] with (T + st - 1) % st == 0, H % sh == 0, W % sw == 0 (else UNSUPPORTED with
+ *     info); any dtype.
+ *  y: [N, (T+st-1)/st, H/sh, W/sw, C*st*sh*sw], x's dtype; must not overlap x.
+ */
+VAE_API vae_status_t vae_space_to_depth(const vae_tensor_t* x, int32_t st, int32_t sh, int32_t sw,
+                                        vae_tensor_t* y, vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Tile split / merge                                                                         */
 /* ------------------------------------------------------------------------------------------ */
 /*
@@ -404,6 +421,9 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  *  VAE_OP_RES_RMS residual block of width cin with RMS norms (vae_rmsnorm_silu) for the GroupNorms
  *  VAE_OP_RMS_SILU RMS norm + SiLU
  *  VAE_OP_ATTN    single-head frame attention of width cin (vae_frame_attention), fp32 activations
+ *  VAE_OP_S2D     space-to-depth fold (st, sh, sw) with the causal front copies of frame 0
+ *                 (vae_space_to_depth): an encoder plan. Such a plan runs untiled (patch-halo
+ *                 mode, 1 x 1 grid, scales 1); its input extents must fold evenly.
  * Dtypes:
  *  - conv weights and GroupNorm outputs (the operands of the next conv) have the plan dtype;
  *  - conv outputs and the residual stream have act_dtype;
@@ -431,7 +451,7 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * bias, gamma and beta may be NULL.
  */
 enum { VAE_OP_CONV = 1, VAE_OP_RES = 2, VAE_OP_GN_SILU = 3, VAE_OP_D2S = 4, VAE_OP_NEAREST = 5,
-       VAE_OP_RES_RMS = 6, VAE_OP_RMS_SILU = 7, VAE_OP_ATTN = 8 };
+       VAE_OP_RES_RMS = 6, VAE_OP_RMS_SILU = 7, VAE_OP_ATTN = 8, VAE_OP_S2D = 9 };
 
 typedef struct vae_layer_desc {
     int32_t op;

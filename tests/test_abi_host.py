@@ -191,6 +191,48 @@ def test_workspace_query_needs_no_gpu(v):
     dec.close()
 
 
+def test_encoder_plan_runs_untiled_only(v):
+    """An encoder plan (space-to-depth folds) takes the 4-channel padded video, sizes its
+    workspace for an untiled run, and refuses tilings and extents its folds do not divide."""
+    import vae_synth
+    spec = vae_synth.LTX2_ENC_720P
+    assert v.latent_channels(spec) == 4                # 3 -> 4: the 4x4 patchify gives 64
+    layers = [dict(op) for op in spec["layers"]]
+    layers[1]["cin"] = 64
+    n_ptr = sum({"conv": 2, "res": 8, "gn_silu": 2}.get(op["op"], 0) for op in layers)
+    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(n_ptr)]
+
+    class P:
+        def __init__(self, p):
+            self.p = p
+
+        def data_ptr(self):
+            return self.p.value
+    dec = v.Decoder(v.VAE_DTYPE_BF16, 4, 32, 1e-6, layers, [P(p) for p in ptrs],
+                    flags=v.VAE_DECODE_F16_OPERANDS)
+    shape = (1, 121, 704, 1280, 4)
+    a = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1)))
+    # the largest activation: the 128-channel fp32 stage-0 tensor, 121 x 176 x 320
+    assert a >= 3 * 121 * 176 * 320 * 128 * 4
+    with pytest.raises(v.VaeError) as e:          # patches: not yet for a folding plan
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1),
+                                         patches=(1, 2)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:          # overlap tiles: not yet for a folding plan
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, shape, (1, 1, 1),
+                                         tile=(16, 16), stride=(14, 14)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:          # 120 frames do not fold causally by 2
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 120, 704, 1280, 4),
+                                         (1, 1, 1)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 1
+    with pytest.raises(v.VaeError) as e:          # 700 rows do not fold by 4 then 2, 2, 2
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 121, 700, 1280, 4),
+                                         (1, 1, 1)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 2
+    dec.close()
+
+
 def test_fused_conv_validation_needs_no_gpu(v):
     """Argument checks and the workspace query of vae_conv3d_causal_fused run on the host only
     (host tensors stand in for device buffers; nothing is launched)."""

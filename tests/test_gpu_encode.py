@@ -1,0 +1,117 @@
+"""GPU parity of the encode path against the CPU oracle, through the C ABI.
+
+- vae_space_to_depth: a permutation, so bit-exact against oracle.space_to_depth for every dtype
+  and vector width (16-byte, 8-byte and scalar rows);
+- the LTX-2-shaped encoder plan, untiled (vae_decode_tiled with a 1 x 1 patch grid), against
+  oracle.encode at the bf16 bar: PSNR >= 50 dB and max-abs <= 2e-2 on the latent, in both operand
+  modes. The 3-channel video is padded with a zero channel on upload (4 x 16 = 64 channels after
+  the patchify fold) and conv_in gets zero weights there, so the sums are the same.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import vae_synth
+from _util import ndhwc, dev, host, psnr, round_f16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def v():
+    import torch
+    import video_diffusion_vae_amd as v
+    assert torch.cuda.is_available()
+    return v
+
+
+S2D_CASES = [
+    # (N, T, H, W, C), dtype, (st, sh, sw)
+    ((1, 9, 16, 24, 4), "bf16", (1, 4, 4)),      # the patchify of a padded video: 8-byte rows
+    ((1, 5, 8, 12, 32), "f32", (2, 2, 2)),       # 16-byte vectors, causal front copy
+    ((2, 3, 4, 6, 64), "bf16", (2, 2, 2)),
+    ((1, 9, 6, 10, 3), "f32", (4, 2, 1)),        # scalar rows, three front copies
+    ((1, 4, 6, 6, 8), "f16", (1, 3, 2)),
+    ((1, 1, 2, 2, 16), "bf16", (1, 1, 1)),       # identity fold
+]
+
+
+@pytest.mark.parametrize("case", S2D_CASES)
+def test_space_to_depth_bit_exact(v, case):
+    import torch
+    shape, dt, fold = case
+    st, sh, sw = fold
+    x = vae_synth.normal(shape, [60, shape[-1]], dtype=dt)
+    if dt == "f16":
+        x = round_f16(x)
+    ref = oracle.space_to_depth(x, st, sh, sw)
+    xd = dev(x, dt)
+    y = torch.full(ref.shape, -7.0, device="cuda", dtype=xd.dtype)
+    v.vae_space_to_depth(xd, st, sh, sw, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), ref)
+
+
+def test_space_to_depth_argument_rules(v):
+    import torch
+    x = torch.zeros((1, 4, 8, 8, 4), device="cuda", dtype=torch.bfloat16)
+    y = torch.zeros((1, 2, 4, 4, 32), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(v.VaeError) as e:         # 4 frames do not fold causally by 2
+        v.vae_space_to_depth(x, 2, 2, 2, y)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 1
+    with pytest.raises(v.VaeError) as e:         # y of the wrong shape (16 channels, not 32)
+        v.vae_space_to_depth(x[:, :3], 2, 2, 2, y[..., :16].contiguous())
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    v.vae_space_to_depth(x[:, :3], 2, 2, 2, y)   # 3 frames fold to 2: accepted
+    with pytest.raises(v.VaeError) as e:         # dtype mismatch
+        v.vae_space_to_depth(x[:, :3], 2, 2, 2, y.float())
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+
+
+@functools.lru_cache(maxsize=None)
+def _params(name):
+    return vae_synth.decoder_params(vae_synth.WORKLOADS[name], affine_seed=9)
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle(name):
+    spec = vae_synth.WORKLOADS[name]
+    return oracle.encode(spec, ndhwc(vae_synth.latent(spec)), _params(name))
+
+
+def _encode(v, name, operands="f16", repeat=1):
+    import torch
+    spec = vae_synth.WORKLOADS[name]
+    x = ndhwc(vae_synth.latent(spec))
+    xp = v.pad_latent(x, spec)
+    enc = v.upload_decoder(spec, _params(name), operands=operands)
+    xd = dev(xp, "bf16")
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xp.shape, (1, 1, 1))
+    ws = torch.empty(enc.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(repeat):
+        out = torch.full(oracle.output_shape(spec, x.shape), float("nan"), device="cuda",
+                         dtype=torch.float32)
+        enc.vae_decode_tiled(xd, desc, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    enc.close()
+    return outs if repeat > 1 else outs[0]
+
+
+@pytest.mark.parametrize("operands", ["f16", "split"])
+@pytest.mark.parametrize("name", ["ltx2_enc_tiny", "ltx2_enc_small"])
+def test_encode_untiled_matches_oracle(v, name, operands):
+    got = host(_encode(v, name, operands))
+    ref = _oracle(name)
+    assert got.shape == ref.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
+def test_encode_is_deterministic(v):
+    import torch
+    a, b = _encode(v, "ltx2_enc_tiny", repeat=2)
+    assert torch.equal(a, b)

@@ -19,7 +19,7 @@ VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
 VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
 VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
-VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN = 6, 7, 8
+VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN, VAE_OP_S2D = 6, 7, 8, 9
 VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other", 6: "rms", 7: "attn"}
 
 # Every symbol include/vae.h declares.
@@ -30,7 +30,7 @@ EXPORTS = (
     "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_rmsnorm_silu",
-    "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample",
+    "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample", "vae_space_to_depth",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
     "vae_decode_workspace_size", "vae_decode_tiled", "vae_decoder_set_timing",
     "vae_decoder_get_timing",
@@ -131,6 +131,7 @@ def _load():
         "vae_frame_attention_workspace": ([T, ctypes.POINTER(SZ)], I32),
         "vae_frame_attention": ([T, F, P, P, P, P, P, P, T, P, SZ, P], I32),
         "vae_upsample": ([T, B, I32, I32, I32, I32, T, P], I32),
+        "vae_space_to_depth": ([T, I32, I32, I32, T, P], I32),
         "vae_tile_split": ([D, ctypes.POINTER(vae_tile_t), I32, ctypes.POINTER(I32)], I32),
         "vae_tile_merge": ([T, ctypes.POINTER(vae_tile_t), D, T, I32, P], I32),
         "vae_decoder_create": ([ctypes.POINTER(vae_decoder_spec_t), ctypes.POINTER(P), I32,
@@ -392,6 +393,13 @@ def vae_upsample(x, in_box, mode, st, sh, sw, y, stream=None):
     return y
 
 
+def vae_space_to_depth(x, st, sh, sw, y, stream=None):
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    _check(LIB.vae_space_to_depth(ctypes.byref(xd), st, sh, sw, ctypes.byref(yd),
+                                  _stream(stream)))
+    return y
+
+
 def tiling_desc(mode, latent_shape, scale, patches=(1, 1), tile=(0, 0), stride=(0, 0), tile_t=0,
                 stride_t=0):
     """vae_tiling_desc_t from an NDHWC latent shape [N, T, H, W, C]. ``tile`` and ``stride`` are
@@ -419,7 +427,7 @@ def vae_tile_merge(tile_out, tile, desc, out, flags, stream=None):
 
 _OPS = {"conv": VAE_OP_CONV, "res": VAE_OP_RES, "gn_silu": VAE_OP_GN_SILU, "d2s": VAE_OP_D2S,
         "nearest": VAE_OP_NEAREST, "res_rms": VAE_OP_RES_RMS, "rms_silu": VAE_OP_RMS_SILU,
-        "attn": VAE_OP_ATTN}
+        "attn": VAE_OP_ATTN, "s2d": VAE_OP_S2D}
 
 
 def layer_descs(plan):
@@ -440,6 +448,8 @@ def layer_descs(plan):
             out.append(vae_layer_desc_t(VAE_OP_RMS_SILU, 0, 0, 1, 1, 1, 0, 0))
         elif k == "attn":
             out.append(vae_layer_desc_t(VAE_OP_ATTN, op["c"], op["c"], 1, 1, 1, 0, 0))
+        elif k == "s2d":
+            out.append(vae_layer_desc_t(VAE_OP_S2D, 0, 0, op["st"], op["sh"], op["sw"], 0, 0))
         elif k == "d2s":
             out.append(vae_layer_desc_t(VAE_OP_D2S, 0, 0, op["st"], op["sh"], op["sw"], 0, 0))
         elif k == "nearest":

@@ -176,6 +176,15 @@ vae_status_t check_tiling(const vae_tiling_desc_t* d) {
 
 int32_t out_frames(int32_t t, int32_t scale_t) { return 1 + (t - 1) * scale_t; }
 
+vae_status_t check_fold(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw) {
+    if (st < 1 || sh < 1 || sw < 1) return fail(VAE_ERR_INVALID_ARG, "fold factors must be >= 1");
+    if ((x.t + st - 1) % st)
+        return fail(VAE_ERR_UNSUPPORTED, "s2d: T + st - 1 must be a multiple of st", 1, x.t, st);
+    if (x.h % sh) return fail(VAE_ERR_UNSUPPORTED, "s2d: H must be a multiple of sh", 2, x.h, sh);
+    if (x.w % sw) return fail(VAE_ERR_UNSUPPORTED, "s2d: W must be a multiple of sw", 3, x.w, sw);
+    return VAE_OK;
+}
+
 void overlap_axes(const vae_tiling_desc_t& d, AxisTiling ax[3]) {
     ax[0] = AxisTiling{d.t, d.tile_t, d.stride_t, d.scale_t, 1};
     ax[1] = AxisTiling{d.h, d.tile_h, d.stride_h, d.scale_h, 0};
@@ -659,6 +668,22 @@ VAE_API vae_status_t vae_upsample(const vae_tensor_t* x, const vae_box_t* box, i
     if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
     VAE_TRY(check_box(box, *x, "box"));
     return launch_upsample(*x, to_box(box, *x), mode, st, sh, sw, *y, as_stream(stream));
+}
+
+VAE_API vae_status_t vae_space_to_depth(const vae_tensor_t* x, int32_t st, int32_t sh, int32_t sw,
+                                        vae_tensor_t* y, vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_tensor(x, "x"));
+    VAE_TRY(check_tensor(y, "y"));
+    VAE_TRY(check_fold(*x, st, sh, sw));
+    const int64_t k = (int64_t)st * sh * sw;
+    if (x->dtype != y->dtype) return fail(VAE_ERR_INVALID_ARG, "x and y dtypes differ");
+    if (y->n != x->n || y->t != (x->t + st - 1) / st || y->h != x->h / sh ||
+        y->w != x->w / sw || y->c != x->c * k)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "s2d: y shape must be ((T+st-1)/st, H/sh, W/sw, C*st*sh*sw)");
+    if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
+    return launch_space_to_depth(*x, st, sh, sw, *y, as_stream(stream));
 }
 
 VAE_API vae_status_t vae_tile_split(const vae_tiling_desc_t* desc, vae_tile_t* tiles,

@@ -201,6 +201,21 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
                 sh *= l.sh;
                 sw *= l.sw;
                 break;
+            case VAE_OP_S2D:
+                {
+                    vae_tensor_t g{};
+                    g.n = s.n;
+                    g.t = s.t;
+                    g.h = s.h;
+                    g.w = s.w;
+                    g.c = s.c;
+                    VAE_TRY(check_fold(g, l.st, l.sh, l.sw));
+                }
+                s.t = (s.t + l.st - 1) / l.st;
+                s.h /= l.sh;
+                s.w /= l.sw;
+                s.c *= (int64_t)l.st * l.sh * l.sw;
+                break;
             default:
                 break;
         }
@@ -226,15 +241,26 @@ vae_tensor_t tensor_of(void* p, const Shape& s) {
 
 Shape shape_of(const vae_tensor_t& t) { return Shape{t.n, t.t, t.h, t.w, t.c, t.dtype}; }
 
-// Latent-grid patch boxes scaled to an activation with cumulative spatial scale (ch, cw).
-BoxList scaled_boxes(const std::vector<Box>& latent_boxes, int64_t t, int ch, int cw) {
+// Input-grid patch boxes scaled to an activation with cumulative spatial scale (ch, cw) and
+// cumulative fold (fh, fw): rows b.h0 * ch / fh and so on. Patch grids of plans that fold are
+// 1 x 1, so the division is exact.
+BoxList scaled_boxes(const std::vector<Box>& latent_boxes, int64_t t, int ch, int cw, int fh = 1,
+                     int fw = 1) {
     BoxList bl;
     bl.n = (int32_t)latent_boxes.size();
     for (size_t i = 0; i < latent_boxes.size(); ++i) {
         const Box& b = latent_boxes[i];
-        bl.b[i] = Box{0, (int32_t)t, b.h0 * ch, b.h1 * ch, b.w0 * cw, b.w1 * cw};
+        bl.b[i] = Box{0, (int32_t)t, b.h0 * ch / fh, b.h1 * ch / fh, b.w0 * cw / fw,
+                      b.w1 * cw / fw};
     }
     return bl;
+}
+
+// Whether the plan has a space-to-depth fold (an encoder plan).
+bool plan_folds(const vae_decoder& d) {
+    for (const vae_layer_desc_t& l : d.layers)
+        if (l.op == VAE_OP_S2D) return true;
+    return false;
 }
 
 struct Req {
@@ -252,7 +278,7 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
     std::vector<Shape> shapes;
     walk(d, in, &shapes, nullptr, nullptr, nullptr);
     Shape cur = in;
-    int ch = 1, cw = 1;
+    int ch = 1, cw = 1, fh = 1, fw = 1;
     for (size_t i = 0; i < d.layers.size(); ++i) {
         const vae_layer_desc_t& l = d.layers[i];
         const Shape& s = shapes[i];
@@ -273,7 +299,8 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
             r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
             vae_tensor_t x = tensor_of(nullptr, cur);
             r->gn = std::max<int64_t>(
-                r->gn, (int64_t)gn_stats_workspace(x, scaled_boxes(boxes, cur.t, ch, cw), d.groups));
+                r->gn, (int64_t)gn_stats_workspace(x, scaled_boxes(boxes, cur.t, ch, cw, fh, fw),
+                                                   d.groups));
             r->mr = std::max<int64_t>(r->mr, cur.n * d.groups * 2 * (int64_t)sizeof(float));
         }
         // partials of GroupNorm statistics gathered by conv epilogues
@@ -298,6 +325,10 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         if (l.op == VAE_OP_D2S || l.op == VAE_OP_NEAREST) {
             ch *= l.sh;
             cw *= l.sw;
+        }
+        if (l.op == VAE_OP_S2D) {
+            fh *= l.sh;
+            fw *= l.sw;
         }
         cur = s;
     }
@@ -358,6 +389,12 @@ struct Runner {
                     const void* gamma, const void* beta, int layer) {
         double* stats = reinterpret_cast<double*>(ws + L.gn);
         float* mr = reinterpret_cast<float*>(ws + L.mr);
+        for (int i = 0; i < bl.n; ++i) {
+            const Box& b = bl.b[i];
+            if (b.t0 < 0 || b.h0 < 0 || b.w0 < 0 || b.t1 > x.t || b.h1 > x.h || b.w1 > x.w ||
+                b.volume() <= 0)
+                return fail(VAE_ERR_INVALID_ARG, "GroupNorm patch box outside the activation");
+        }
         const bool fused = stats_ready;
         if (!fused) VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
         stats_ready = false;
@@ -427,7 +464,7 @@ struct Runner {
         stats_ready = false;
         vae_tensor_t cur = in;
         int cur_buf = -1;  // -1: the caller's input, never written
-        int ch = 1, cw = 1;
+        int ch = 1, cw = 1, fh = 1, fw = 1;
         int32_t near_lsh = 0, near_lsw = 0;   // a nearest upsampling the next conv reads
         size_t p = 0;
         auto buf = [&](int i, const Shape& sh) { return tensor_of(ws + L.buf[i], sh); };
@@ -463,7 +500,7 @@ struct Runner {
                 }
             } else if (l.op == VAE_OP_RES) {
                 // x -> GN1 -> t1 -> conv1 -> t2 -> GN2 -> t1 -> conv2 (+ x) -> t2
-                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
+                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
                 const int b1 = free_buf(cur_buf, -1);
                 const int b2 = free_buf(cur_buf, b1);
                 Shape gs = shape_of(cur), as = shape_of(cur);
@@ -535,7 +572,7 @@ struct Runner {
                 cur = y;
                 cur_buf = last ? -2 : nb;
             } else if (l.op == VAE_OP_GN_SILU) {
-                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw);
+                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
                 vae_tensor_t y;
                 int nb = cur_buf;
                 Shape gs = shape_of(cur);
@@ -563,6 +600,17 @@ struct Runner {
                 near_lsw += log2_of(l.sw);
                 ch *= l.sh;
                 cw *= l.sw;
+            } else if (l.op == VAE_OP_S2D) {
+                const int nb = free_buf(cur_buf, -1);
+                vae_tensor_t y = last ? final_out : buf(nb, os);
+                VAE_TRY(launch_space_to_depth(cur, l.st, l.sh, l.sw, y, s));
+                VAE_TRY(mark(VAE_KIND_UPSAMPLE, layer, 0.0,
+                             (double)numel(cur) * elem_size(cur.dtype) +
+                                 (double)numel(y) * elem_size(y.dtype)));
+                fh *= l.sh;
+                fw *= l.sw;
+                cur = y;
+                cur_buf = last ? -2 : nb;
             } else {  // D2S / NEAREST
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = last ? final_out : buf(nb, os);
@@ -586,7 +634,7 @@ vae_status_t plan_output(const vae_decoder& d, const vae_tiling_desc_t& desc, Sh
                          int* st, int* sh, int* sw) {
     Shape in{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype};
     std::vector<Shape> shapes;
-    walk(d, in, &shapes, st, sh, sw);
+    VAE_TRY(walk(d, in, &shapes, st, sh, sw));
     *out = shapes.back();
     return VAE_OK;
 }
@@ -596,9 +644,14 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
     VAE_TRY(check_tiling(&desc));
     int st, sh, sw;
     Shape out;
-    plan_output(d, desc, &out, &st, &sh, &sw);
+    VAE_TRY(plan_output(d, desc, &out, &st, &sh, &sw));
     if (st != desc.scale_t || sh != desc.scale_h || sw != desc.scale_w)
         return fail(VAE_ERR_INVALID_ARG, "tiling scales do not match the decoder plan");
+    if (plan_folds(d) &&
+        (desc.mode != VAE_TILING_PATCH_HALO || desc.patches_h != 1 || desc.patches_w != 1))
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "a plan with space-to-depth folds (an encoder) runs untiled: patch-halo mode "
+                    "with a 1 x 1 grid");
     if (desc.mode == VAE_TILING_PATCH_HALO && (int64_t)desc.patches_h * desc.patches_w > kMaxBoxes)
         return fail(VAE_ERR_UNSUPPORTED, "the decoder takes at most 16 patches", -1,
                     (int64_t)desc.patches_h * desc.patches_w, -1, 1);
@@ -732,6 +785,11 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
             case VAE_OP_NEAREST:
                 if (l.sh < 1 || l.sw < 1)
                     return fail(VAE_ERR_INVALID_ARG, "nearest factors must be >= 1");
+                break;
+            case VAE_OP_S2D:
+                if (l.st < 1 || l.sh < 1 || l.sw < 1)
+                    return fail(VAE_ERR_INVALID_ARG, "s2d factors must be >= 1");
+                c *= (int64_t)l.st * l.sh * l.sw;
                 break;
             default:
                 return fail(VAE_ERR_INVALID_ARG, "unknown op in layer plan");

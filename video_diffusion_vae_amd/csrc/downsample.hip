@@ -1,0 +1,84 @@
+// Space-to-depth downsampling of channels-last activations: the fold of an encoder.
+//
+// Encoder downsamplers that fold space into channels after a stride-1 convolution read one input
+// position per output one ("Add tiled VAE parallelism & extended model support", encoder commit
+// messages). The fold mirrors the decoder's depth-to-space: st-1 copies of frame 0 go in front
+// (causal), and input (st*t + dt - (st-1), sh*h + dh, sw*w + dw, c) lands in output channel
+// ((dt*sh + dh)*sw + dw)*C + c at (t, h, w); input frames below 0 read frame 0.
+//
+// One block handles one (output row t,h; sub-row dt,dh) pair: it reads the contiguous input row
+// (st*t + dt - (st-1), sh*h + dh) and writes, for every output column, sw consecutive C-channel
+// slices of the output row. Reads are fully contiguous; writes are contiguous runs of sw*C values.
+#include "kernels.h"
+
+namespace vae {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T, int V>
+__global__ __launch_bounds__(kThreads) void space_to_depth_kernel(
+    const T* __restrict__ x, T* __restrict__ y, int32_t xT, int32_t xH, int32_t xW, int32_t C,
+    int32_t yT, int32_t yH, int32_t yW, int32_t st, int32_t sh, int32_t sw) {
+    const int n = blockIdx.z;
+    const int64_t row = blockIdx.x;                  // output row t * yH + h
+    const int sub = blockIdx.y;                      // dt * sh + dh
+    const int t = (int)(row / yH), h = (int)(row % yH);
+    const int dt = sub / sh, dh = sub % sh;
+    int ti = st * t + dt - (st - 1);
+    ti = ti < 0 ? 0 : ti;                            // the causal front copies of frame 0
+    const int hi = sh * h + dh;
+    const int64_t yC = (int64_t)C * st * sh * sw;
+    const T* xr = x + (((int64_t)n * xT + ti) * xH + hi) * (int64_t)xW * C;
+    T* yr = y + (((int64_t)n * yT + t) * yH + h) * (int64_t)yW * yC + (int64_t)sub * sw * C;
+    const int CV = C / V;
+    const int seg = xW * CV;                         // input vectors in the row
+    for (int e = threadIdx.x; e < seg; e += kThreads) {
+        const int cv = e % CV;
+        const int wi = e / CV;                       // input column
+        const int wo = wi / sw, dw = wi % sw;
+        const T* src = xr + (int64_t)e * V;
+        T* dst = yr + (int64_t)wo * yC + (int64_t)dw * C + cv * V;
+        if constexpr (V * sizeof(T) == 16) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else if constexpr (V * sizeof(T) == 8) {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) dst[k] = src[k];
+        }
+    }
+}
+
+template <typename T, int V>
+void launch(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw, const vae_tensor_t& y,
+            hipStream_t stream) {
+    const dim3 grid((unsigned)(y.t * y.h), (unsigned)(st * sh), (unsigned)x.n);
+    hipLaunchKernelGGL((space_to_depth_kernel<T, V>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const T*>(x.data), static_cast<T*>(y.data), (int32_t)x.t,
+                       (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, (int32_t)y.t, (int32_t)y.h,
+                       (int32_t)y.w, st, sh, sw);
+}
+
+template <typename T>
+void run(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw, const vae_tensor_t& y,
+         hipStream_t stream) {
+    constexpr int V16 = 16 / sizeof(T), V8 = 8 / sizeof(T);
+    if (x.c % V16 == 0) launch<T, V16>(x, st, sh, sw, y, stream);
+    else if (x.c % V8 == 0) launch<T, V8>(x, st, sh, sw, y, stream);
+    else launch<T, 1>(x, st, sh, sw, y, stream);
+}
+
+}  // namespace
+
+vae_status_t launch_space_to_depth(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw,
+                                   const vae_tensor_t& y, hipStream_t stream) {
+    if (numel(y) == 0) return VAE_OK;
+    // a copy: bf16 and fp16 move as 16-bit words
+    if (x.dtype != VAE_DTYPE_F32) run<uint16_t>(x, st, sh, sw, y, stream);
+    else run<float>(x, st, sh, sw, y, stream);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+}  // namespace vae

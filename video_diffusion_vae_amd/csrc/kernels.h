@@ -81,6 +81,10 @@ vae_status_t launch_frame_attention(const vae_tensor_t& x, float eps, const floa
 vae_status_t launch_upsample(const vae_tensor_t& x, const Box& box, int32_t mode, int32_t st,
                              int32_t sh, int32_t sw, const vae_tensor_t& y, hipStream_t stream);
 
+// ---- space-to-depth (encoder fold, causal front pad) ----
+vae_status_t launch_space_to_depth(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw,
+                                   const vae_tensor_t& y, hipStream_t stream);
+
 // ---- tiles ----
 // A tile's overlaps with its neighbours along T, H and W (output samples).
 struct MergeRamps {

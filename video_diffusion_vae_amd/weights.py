@@ -26,13 +26,28 @@ def conv_weight_layout(w, dtype, device):
     return t.to(device=device, dtype=dtype)
 
 
+def _lead_fold(spec: dict) -> int:
+    """Channel factor of the space-to-depth folds before the first conv (an encoder's patchify)."""
+    k = 1
+    for op in spec["layers"]:
+        if op["op"] != "s2d":
+            break
+        k *= op["st"] * op["sh"] * op["sw"]
+    return k
+
+
 def latent_channels(spec: dict) -> int:
-    """Channels of the latent the GPU decoder takes: the plan's, rounded up to a multiple of 32
-    for a bf16 plan, so that the first conv runs on the matrix cores (48 -> 64 for the Wan-shaped
-    plan). The extra channels are zeros in the latent and in the first conv's weights, so the
-    result is the same sum."""
-    c = spec["latent"][1]
-    return (c + 31) // 32 * 32 if spec["dtype"] == "bf16" else c
+    """Channels of the input the GPU plan takes: the plan's, padded for a bf16 plan so that the
+    first conv reads a multiple of 32 channels and runs on the matrix cores (a 48-channel latent
+    -> 64; a 3-channel video -> 4, which the 4x4 patchify turns into 64). The extra channels are
+    zeros in the input and in the first conv's weights, so the result is the same sum."""
+    c = (spec["latent"] if "latent" in spec else spec["input"])[1]
+    if spec["dtype"] != "bf16":
+        return c
+    k = _lead_fold(spec)
+    while (c * k) % 32:
+        c += 1
+    return c
 
 
 def pad_latent(z, spec: dict):
@@ -58,15 +73,22 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", ope
     tdt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
     f32 = lambda a: torch.as_tensor(np.asarray(a, np.float32)).to(device)
     lc = latent_channels(spec)
+    c0 = (spec["latent"] if "latent" in spec else spec["input"])[1]
+    fold = _lead_fold(spec)
     layers = [dict(op) for op in spec["layers"]]
+    first_conv = next(i for i, op in enumerate(layers) if op["op"] == "conv")
     flat = []
     for k, p in enumerate(params):
         if p["kind"] == "conv":
             w = np.asarray(p["w"], np.float32)
-            if k == 0 and w.shape[1] < lc:       # zero weights for the zero latent channels
-                w = np.concatenate([w, np.zeros((w.shape[0], lc - w.shape[1]) + w.shape[2:],
-                                                np.float32)], axis=1)
-                layers[0]["cin"] = lc
+            if k == 0 and lc > c0:
+                # zero weights for the zero input channels: input channel f * c0 + j of the
+                # (folded) plan input is channel f * lc + j of the padded one
+                cout = w.shape[0]
+                wp = np.zeros((cout, fold, lc) + w.shape[2:], np.float32)
+                wp[:, :, :c0] = w.reshape((cout, fold, c0) + w.shape[2:])
+                w = wp.reshape((cout, fold * lc) + w.shape[2:])
+                layers[first_conv]["cin"] = fold * lc
             flat.append(conv_weight_layout(w, tdt, device))
             flat.append(f32(p["b"]))
         elif p["kind"] == "attn":
