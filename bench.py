@@ -71,11 +71,14 @@ def conv_flops(spec, latent_shape):
             t, h, w = op["st"] * t - (op["st"] - 1), h * op["sh"], w * op["sw"]
         elif k == "nearest":
             h, w = h * op["sh"], w * op["sw"]
+        elif k == "s2d":
+            t, h, w = (t + op["st"] - 1) // op["st"], h // op["sh"], w // op["sw"]
     return total
 
 
 def output_shape(spec, latent_shape):
-    """[N, T, H, W, C] of the decoded video for an NDHWC latent shape, following the plan."""
+    """[N, T, H, W, C] of the plan's output for an NDHWC input shape (a decoder's video, an
+    encoder's latent)."""
     n, t, h, w, c = latent_shape
     for op in spec["layers"]:
         k = op["op"]
@@ -86,6 +89,9 @@ def output_shape(spec, latent_shape):
             c //= op["st"] * op["sh"] * op["sw"]
         elif k == "nearest":
             h, w = h * op["sh"], w * op["sw"]
+        elif k == "s2d":
+            t, h, w = (t + op["st"] - 1) // op["st"], h // op["sh"], w // op["sw"]
+            c *= op["st"] * op["sh"] * op["sw"]
     return (n, t, h, w, c)
 
 
@@ -93,7 +99,9 @@ WORKLOADS = {
     # name: (plan, patch grid of the patch-halo mode, tile grid name of the overlap mode)
     "ltx2": ("LTX2_720P", (1, 4), "2x3"),
     "wan": ("WAN_720P", (1, 4), "2x3"),
+    "ltx2_enc": ("LTX2_ENC_720P", (1, 1), None),     # encode, untiled
 }
+ENCODE_METRIC = "encoded Mpixel-frames/s (720p VAE encode, 1 GPU) + conv MFMA % of peak"
 
 
 def activations_note(operands):
@@ -104,6 +112,8 @@ def activations_note(operands):
 
 
 def workload_name(kind, mode, tile_t=0, stride_t=0):
+    if kind == "ltx2_enc":
+        return "ltx2_720p_encode_untiled"
     prefix = {"ltx2": "ltx2_720p", "wan": "wan2.2_ti2v_5b_720p"}[kind]
     if mode == "patch":
         return prefix + "_decode_patch_halo_1x4"
@@ -234,25 +244,28 @@ def cpu_baseline(spec, params, frames=2):
     import threadpoolctl
     import oracle
     import vae_synth
-    z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))[:, :frames]
+    encoder = spec.get("kind") == "encoder"
+    take = 8 * frames - 7 if encoder else frames       # an encoder's sample: whole latent frames
+    z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))[:, :take]
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
     out = oracle.decode(spec, z, params)
     sample_s = time.perf_counter() - t0
-    n, c, t, h, w = spec["latent"]
+    n, c, t, h, w = spec["input"] if encoder else spec["latent"]
     full_shape = (n, t, h, w, c)
     scale = conv_flops(spec, full_shape) / conv_flops(spec, z.shape)
     est_full_s = sample_s * scale
-    _, to, ho, wo, _ = output_shape(spec, full_shape)
+    _, to, ho, wo, _ = full_shape if encoder else output_shape(spec, full_shape)
     px = to * ho * wo
+    what = "encode of video" if encoder else "decode of latent"
     return {
         "value": px / est_full_s / 1e6, "unit": "Mpx-frames/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle fp64 decode of latent [{n},{c},{frames},{h},{w}] -> "
+        "sample": (f"oracle fp64 {what} [{n},{c},{take},{h},{w}] -> "
                    f"{list(out.shape)} in {sample_s:.1f} s, scaled by conv flops x{scale:.1f} to "
-                   f"the {t}-frame 720p decode (est. {est_full_s:.0f} s); "
-                   f"os.cpu_count()={os.cpu_count()}"),
+                   f"the {t}-frame 720p {'encode' if encoder else 'decode'} "
+                   f"(est. {est_full_s:.0f} s); os.cpu_count()={os.cpu_count()}"),
     }
 
 
@@ -298,8 +311,12 @@ def main():
     import vae_synth
     import video_diffusion_vae_amd as v
 
-    plan_name, patch_grid, _ = WORKLOADS[args.workload]
+    plan_name, patch_grid, tiles = WORKLOADS[args.workload]
     spec = getattr(vae_synth, plan_name)
+    encoder = spec.get("kind") == "encoder"
+    if args.mode == "overlap" and tiles is None:
+        print(f"--workload {args.workload} runs untiled only (--mode patch)", file=sys.stderr)
+        sys.exit(2)
     t_setup = time.perf_counter()
     z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))
     out_shape = output_shape(spec, z.shape)
@@ -310,7 +327,8 @@ def main():
     zd = torch.as_tensor(zp).to(device=dev, dtype=torch.bfloat16)
     workload = workload_name(args.workload, args.mode, args.tile_t, args.stride_t)
     if args.mode == "patch":
-        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, spec["scale"], patches=patch_grid)
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, spec.get("scale", (1, 1, 1)),
+                             patches=patch_grid)
     else:
         desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, zp.shape, spec["scale"],
                              tile=spec["overlap_tile"], stride=spec["overlap_stride"],
@@ -339,7 +357,8 @@ def main():
     elapsed = time.perf_counter() - t0
     dec.set_timing(False)
     ms = elapsed * 1000.0 / args.steps
-    px = out_shape[1] * out_shape[2] * out_shape[3]
+    video = z.shape if encoder else out_shape          # pixel-frames of the video side
+    px = video[1] * video[2] * video[3]
     value = px / (ms / 1000.0) / 1e6
     log(f"[bench] {args.steps} timed steps: {ms:.2f} ms/step, {value:.1f} Mpx-frames/s")
 
@@ -395,11 +414,14 @@ def main():
         log(f"[bench] cpu baseline: {baseline}")
 
     line = {
-        "metric": METRIC, "value": round(value, 3), "unit": "Mpx-frames/s", "n_gpus": 1,
+        "metric": ENCODE_METRIC if encoder else METRIC, "value": round(value, 3),
+        "unit": "Mpx-frames/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded latent, random-init weights)",
-        "config": {"workload": workload, "latent": list(spec["latent"]),
+        "data": ("synthetic (seeded U(-1,1) video, random-init weights)" if encoder
+                 else "synthetic (seeded latent, random-init weights)"),
+        "config": {"workload": workload,
+                   ("input" if encoder else "latent"): list(spec["input" if encoder else "latent"]),
                    "output": [out_shape[0], out_shape[4]] + list(out_shape[1:4]),
                    "parallelism": "none (1 GPU)",
                    "operands": OPERANDS[args.operands],

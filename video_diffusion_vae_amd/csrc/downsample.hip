@@ -6,9 +6,11 @@
 // (causal), and input (st*t + dt - (st-1), sh*h + dh, sw*w + dw, c) lands in output channel
 // ((dt*sh + dh)*sw + dw)*C + c at (t, h, w); input frames below 0 read frame 0.
 //
-// One block handles one (output row t,h; sub-row dt,dh) pair: it reads the contiguous input row
-// (st*t + dt - (st-1), sh*h + dh) and writes, for every output column, sw consecutive C-channel
-// slices of the output row. Reads are fully contiguous; writes are contiguous runs of sw*C values.
+// One block handles one output row (t, h) and walks it in order: thread e writes output vector e
+// of the row (V channels of one sub-position) and reads it from input row (st*t + dt - (st-1),
+// sh*h + dh). Writes are fully contiguous. A wave's reads cover, for each sub-row, consecutive
+// input columns, i.e. whole input lines spread over the wave (with 4 bf16 channels, the patchify
+// of a padded video: 16 pieces of 8 bytes per output position, each line read once).
 #include "kernels.h"
 
 namespace vae {
@@ -20,25 +22,25 @@ template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void space_to_depth_kernel(
     const T* __restrict__ x, T* __restrict__ y, int32_t xT, int32_t xH, int32_t xW, int32_t C,
     int32_t yT, int32_t yH, int32_t yW, int32_t st, int32_t sh, int32_t sw) {
-    const int n = blockIdx.z;
+    const int n = blockIdx.y;
     const int64_t row = blockIdx.x;                  // output row t * yH + h
-    const int sub = blockIdx.y;                      // dt * sh + dh
     const int t = (int)(row / yH), h = (int)(row % yH);
-    const int dt = sub / sh, dh = sub % sh;
-    int ti = st * t + dt - (st - 1);
-    ti = ti < 0 ? 0 : ti;                            // the causal front copies of frame 0
-    const int hi = sh * h + dh;
-    const int64_t yC = (int64_t)C * st * sh * sw;
-    const T* xr = x + (((int64_t)n * xT + ti) * xH + hi) * (int64_t)xW * C;
-    T* yr = y + (((int64_t)n * yT + t) * yH + h) * (int64_t)yW * yC + (int64_t)sub * sw * C;
-    const int CV = C / V;
-    const int seg = xW * CV;                         // input vectors in the row
+    const int CV = C / V;                            // vectors per sub-position
+    const int kv = st * sh * sw * CV;                // vectors per output position
+    const int seg = yW * kv;                         // vectors in the output row
+    const int64_t xrow = (int64_t)xW * C;
+    const T* xn = x + (int64_t)n * xT * xH * xrow;
+    T* yr = y + ((int64_t)n * yT + t) * yH * (int64_t)yW * kv * V + (int64_t)h * yW * kv * V;
     for (int e = threadIdx.x; e < seg; e += kThreads) {
-        const int cv = e % CV;
-        const int wi = e / CV;                       // input column
-        const int wo = wi / sw, dw = wi % sw;
-        const T* src = xr + (int64_t)e * V;
-        T* dst = yr + (int64_t)wo * yC + (int64_t)dw * C + cv * V;
+        const int wo = e / kv;
+        const int j = e - wo * kv;
+        const int p = j / CV, cv = j - p * CV;       // sub-position ((dt*sh + dh)*sw + dw)
+        const int dw = p % sw, dh = (p / sw) % sh, dt = p / (sw * sh);
+        int ti = st * t + dt - (st - 1);
+        ti = ti < 0 ? 0 : ti;                        // the causal front copies of frame 0
+        const T* src = xn + ((int64_t)ti * xH + sh * h + dh) * xrow +
+                       (int64_t)(sw * wo + dw) * C + cv * V;
+        T* dst = yr + (int64_t)e * V;
         if constexpr (V * sizeof(T) == 16) {
             *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
         } else if constexpr (V * sizeof(T) == 8) {
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void space_to_depth_kernel(
 template <typename T, int V>
 void launch(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw, const vae_tensor_t& y,
             hipStream_t stream) {
-    const dim3 grid((unsigned)(y.t * y.h), (unsigned)(st * sh), (unsigned)x.n);
+    const dim3 grid((unsigned)(y.t * y.h), (unsigned)x.n);
     hipLaunchKernelGGL((space_to_depth_kernel<T, V>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(x.data), static_cast<T*>(y.data), (int32_t)x.t,
                        (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, (int32_t)y.t, (int32_t)y.h,
