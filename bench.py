@@ -99,7 +99,7 @@ WORKLOADS = {
     # name: (plan, patch grid of the patch-halo mode, tile grid name of the overlap mode)
     "ltx2": ("LTX2_720P", (1, 4), "2x3"),
     "wan": ("WAN_720P", (1, 4), "2x3"),
-    "ltx2_enc": ("LTX2_ENC_720P", (1, 1), None),     # encode, untiled
+    "ltx2_enc": ("LTX2_ENC_720P", (1, 1), "2x3"),    # encode: untiled, or latent-grid tiles
 }
 ENCODE_METRIC = "encoded Mpixel-frames/s (720p VAE encode, 1 GPU) + conv MFMA % of peak"
 
@@ -113,7 +113,7 @@ def activations_note(operands):
 
 def workload_name(kind, mode, tile_t=0, stride_t=0):
     if kind == "ltx2_enc":
-        return "ltx2_720p_encode_untiled"
+        return "ltx2_720p_encode_" + ("untiled" if mode == "patch" else "overlap_blend_2x3")
     prefix = {"ltx2": "ltx2_720p", "wan": "wan2.2_ti2v_5b_720p"}[kind]
     if mode == "patch":
         return prefix + "_decode_patch_halo_1x4"
@@ -330,9 +330,10 @@ def main():
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, spec.get("scale", (1, 1, 1)),
                              patches=patch_grid)
     else:
-        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, zp.shape, spec["scale"],
+        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, zp.shape, spec.get("scale", (1, 1, 1)),
                              tile=spec["overlap_tile"], stride=spec["overlap_stride"],
-                             tile_t=args.tile_t, stride_t=args.stride_t)
+                             tile_t=args.tile_t, stride_t=args.stride_t,
+                             down=spec.get("down", (0, 0, 0)))
     ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device=dev)
     out = torch.empty(out_shape, dtype=torch.float32, device=dev)
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s, workspace "

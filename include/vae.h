@@ -365,6 +365,12 @@ VAE_API vae_status_t vae_space_to_depth(const vae_tensor_t* x, int32_t st, int32
  * reading the causal decoder supports). With scale_t > 1, consecutive temporal tiles must share a
  * latent frame (stride_t < tile_t), or the scale_t - 1 frames before a tile's first frame would
  * come from no tile. Overlaps E are measured between neighbouring tiles' output spans.
+ * Encoders (down_* > 1, scales 1, mode B only, T whole): n, t, h, w are the input video's extents,
+ * and the tile grid (tile_*, stride_*) is cut on the output latent grid of
+ * (t + down_t - 1) / down_t frames, h / down_h rows and w / down_w columns (P2: sample tiles 512
+ * with stride 448 are 16 / 14 latent rows at a fold of 32, with per-tile latent shapes and a
+ * latent-space blend). Each tile's `latent` box is then its input-video box (latent rows times
+ * the fold, all frames) and `out` its latent box; the ramps run over the latent overlaps.
  */
 enum { VAE_TILING_PATCH_HALO = 1, VAE_TILING_OVERLAP_BLEND = 2 };
 
@@ -376,6 +382,7 @@ typedef struct vae_tiling_desc {
     int32_t tile_h, tile_w;              /* mode B tile size, latent rows */
     int32_t stride_h, stride_w;          /* mode B tile stride, latent rows */
     int32_t tile_t, stride_t;            /* mode B temporal tiles, latent frames (0: T whole) */
+    int32_t down_t, down_h, down_w;      /* an encoder's folds (0 or 1: none); see below */
 } vae_tiling_desc_t;
 
 typedef struct vae_tile {

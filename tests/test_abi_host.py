@@ -191,9 +191,47 @@ def test_workspace_query_needs_no_gpu(v):
     dec.close()
 
 
-def test_encoder_plan_runs_untiled_only(v):
+@pytest.mark.parametrize("case", [((121, 704, 1280), (16, 16), (14, 14)),
+                                  ((9, 64, 160), (2, 3), (2, 2)),
+                                  ((9, 64, 96), (2, 2), (1, 1))])
+def test_encoder_overlap_split_on_the_latent_grid(v, case):
+    """An encoder desc (down = 8, 32, 32) cuts its tiles on the latent grid: `out` is the latent
+    box (all latent frames), `latent` the input-video box (rows and columns times 32, all input
+    frames); overlaps are latent samples."""
+    (t, h, w), tile, stride = case
+    lt, lh, lw = (t + 7) // 8, h // 32, w // 32
+    got = v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, t, h, w, 4), (1, 1, 1),
+                                         tile=tile, stride=stride, down=(8, 32, 32)))
+    ref = oracle.overlap_tiles(lt, lh, lw, tile, stride, (1, 1, 1))
+    assert len(got) == len(ref)
+    for g, r in zip(got, ref):
+        f = _fields(g)
+        assert f["out"] == r["out"] == r["latent"]
+        _, _, h0, h1, w0, w1 = r["latent"]
+        assert f["latent"] == (0, t, 32 * h0, 32 * h1, 32 * w0, 32 * w1)
+        assert f["lead"] == r["lead"] and f["trail"] == r["trail"]
+
+
+def test_encoder_tiling_refusals(v):
+    with pytest.raises(v.VaeError) as e:          # folds in a patch-halo desc
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 9, 64, 96, 4), (1, 1, 1),
+                                       down=(8, 32, 32)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:          # temporal tiles with folds
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 9, 64, 96, 4), (1, 1, 1),
+                                       tile=(2, 2), stride=(1, 1), tile_t=2, stride_t=1,
+                                       down=(8, 32, 32)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:          # 100 rows do not fold by 32
+        v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 9, 100, 96, 4), (1, 1, 1),
+                                       tile=(2, 2), stride=(1, 1), down=(8, 32, 32)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 2
+
+
+def test_encoder_plan_tilings(v):
     """An encoder plan (space-to-depth folds) takes the 4-channel padded video, sizes its
-    workspace for an untiled run, and refuses tilings and extents its folds do not divide."""
+    workspace untiled and in latent-grid overlap tiles, and refuses patch grids, folds that are
+    not the plan's, and extents its folds do not divide."""
     import vae_synth
     spec = vae_synth.LTX2_ENC_720P
     assert v.latent_channels(spec) == 4                # 3 -> 4: the 4x4 patchify gives 64
@@ -218,10 +256,17 @@ def test_encoder_plan_runs_untiled_only(v):
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1),
                                          patches=(1, 2)))
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
-    with pytest.raises(v.VaeError) as e:          # overlap tiles: not yet for a folding plan
+    with pytest.raises(v.VaeError) as e:          # overlap tiles need the plan's folds in down
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, shape, (1, 1, 1),
                                          tile=(16, 16), stride=(14, 14)))
-    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:          # folds that are not the plan's
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, shape, (1, 1, 1),
+                                         tile=(16, 16), stride=(14, 14), down=(8, 16, 16)))
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    b = dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, shape, (1, 1, 1),
+                                         tile=(16, 16), stride=(14, 14), down=(8, 32, 32)))
+    assert 0 < b < a                              # a 512 x 512 pixel tile at a time
     with pytest.raises(v.VaeError) as e:          # 120 frames do not fold causally by 2
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 120, 704, 1280, 4),
                                          (1, 1, 1)))

@@ -3,8 +3,8 @@
 - vae_space_to_depth: a permutation, so bit-exact against oracle.space_to_depth for every dtype
   and vector width (16-byte, 8-byte and scalar rows);
 - the LTX-2-shaped encoder plan, untiled (vae_decode_tiled with a 1 x 1 patch grid), against
-  oracle.encode at the bf16 bar: PSNR >= 50 dB and max-abs <= 2e-2 on the latent, in both operand
-  modes. The 3-channel video is padded with a zero channel on upload (4 x 16 = 64 channels after
+  oracle.encode, and in overlap tiles cut on the latent grid (down = the plan's folds) against
+  oracle.encode_overlap_blend, at the bf16 bar: PSNR >= 50 dB and max-abs <= 2e-2 on the latent. The 3-channel video is padded with a zero channel on upload (4 x 16 = 64 channels after
   the patchify fold) and conv_in gets zero weights there, so the sums are the same.
 """
 import functools
@@ -76,19 +76,26 @@ def _params(name):
 
 
 @functools.lru_cache(maxsize=None)
-def _oracle(name):
+def _oracle(name, tiles=None):
     spec = vae_synth.WORKLOADS[name]
-    return oracle.encode(spec, ndhwc(vae_synth.latent(spec)), _params(name))
+    x = ndhwc(vae_synth.latent(spec))
+    if tiles is None:
+        return oracle.encode(spec, x, _params(name))
+    return oracle.encode_overlap_blend(spec, x, _params(name), tiles[0], tiles[1])
 
 
-def _encode(v, name, operands="f16", repeat=1):
+def _encode(v, name, operands="f16", repeat=1, tiles=None):
     import torch
     spec = vae_synth.WORKLOADS[name]
     x = ndhwc(vae_synth.latent(spec))
     xp = v.pad_latent(x, spec)
     enc = v.upload_decoder(spec, _params(name), operands=operands)
     xd = dev(xp, "bf16")
-    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xp.shape, (1, 1, 1))
+    if tiles is None:
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xp.shape, (1, 1, 1))
+    else:
+        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, xp.shape, (1, 1, 1), tile=tiles[0],
+                             stride=tiles[1], down=spec["down"])
     ws = torch.empty(enc.workspace_size(desc), dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(repeat):
@@ -109,6 +116,26 @@ def test_encode_untiled_matches_oracle(v, name, operands):
     assert got.shape == ref.shape
     p, m = psnr(got, ref), float(np.abs(got - ref).max())
     assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
+@pytest.mark.parametrize("name,tiles", [("ltx2_enc_small", ((2, 3), (2, 2))),
+                                        ("ltx2_enc_tiny", ((2, 2), (1, 1))),
+                                        ("ltx2_enc_tiny", ((1, 2), (1, 1)))])
+def test_encode_overlap_blend_matches_oracle(v, name, tiles):
+    """Tiles cut on the latent grid, each encoding its pixel crop alone (own borders, own
+    GroupNorm statistics), blended in latent space: against oracle.encode_overlap_blend."""
+    got = host(_encode(v, name, tiles=tiles))
+    ref = _oracle(name, tiles)
+    assert got.shape == ref.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
+def test_encode_one_overlap_tile_is_the_untiled_encode(v):
+    import torch
+    whole = _encode(v, "ltx2_enc_small")
+    one = _encode(v, "ltx2_enc_small", tiles=((8, 8), (8, 8)))
+    assert torch.equal(whole, one)
 
 
 def test_encode_is_deterministic(v):

@@ -67,7 +67,8 @@ class vae_error_info_t(ctypes.Structure):
 class vae_tiling_desc_t(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in (
         "mode", "n", "t", "h", "w", "scale_t", "scale_h", "scale_w", "patches_h", "patches_w",
-        "tile_h", "tile_w", "stride_h", "stride_w", "tile_t", "stride_t")]
+        "tile_h", "tile_w", "stride_h", "stride_w", "tile_t", "stride_t", "down_t", "down_h",
+        "down_w")]
 
 
 class vae_tile_t(ctypes.Structure):
@@ -401,12 +402,15 @@ def vae_space_to_depth(x, st, sh, sw, y, stream=None):
 
 
 def tiling_desc(mode, latent_shape, scale, patches=(1, 1), tile=(0, 0), stride=(0, 0), tile_t=0,
-                stride_t=0):
-    """vae_tiling_desc_t from an NDHWC latent shape [N, T, H, W, C]. ``tile`` and ``stride`` are
-    (H, W); ``tile_t`` > 0 also cuts T (overlap-blend only)."""
+                stride_t=0, down=(0, 0, 0)):
+    """vae_tiling_desc_t from the NDHWC input shape [N, T, H, W, C] (a decoder's latent, an
+    encoder's video). ``tile`` and ``stride`` are (H, W); ``tile_t`` > 0 also cuts T
+    (overlap-blend only). ``down``: an encoder's folds (T, H, W); its tile grid is then cut on the
+    output latent grid."""
     n, t, h, w = latent_shape[:4]
     return vae_tiling_desc_t(mode, n, t, h, w, scale[0], scale[1], scale[2], patches[0],
-                             patches[1], tile[0], tile[1], stride[0], stride[1], tile_t, stride_t)
+                             patches[1], tile[0], tile[1], stride[0], stride[1], tile_t, stride_t,
+                             down[0], down[1], down[2])
 
 
 def vae_tile_split(desc):

@@ -151,6 +151,22 @@ vae_status_t check_tiling(const vae_tiling_desc_t* d) {
         return fail(VAE_ERR_INVALID_ARG, "latent extents must be >= 1");
     if (d->scale_t < 1 || d->scale_h < 1 || d->scale_w < 1)
         return fail(VAE_ERR_INVALID_ARG, "scales must be >= 1");
+    if (d->down_t < 0 || d->down_h < 0 || d->down_w < 0)
+        return fail(VAE_ERR_INVALID_ARG, "folds must be >= 0");
+    if (encodes(*d)) {
+        if (d->mode != VAE_TILING_OVERLAP_BLEND)
+            return fail(VAE_ERR_UNSUPPORTED, "an encoder tiling (down_*) is overlap-blend only");
+        if (d->scale_t != 1 || d->scale_h != 1 || d->scale_w != 1 || d->tile_t > 0)
+            return fail(VAE_ERR_UNSUPPORTED,
+                        "an encoder tiling takes scales 1 and keeps T whole (tile_t = 0)");
+        const int32_t ft = d->down_t > 1 ? d->down_t : 1, fh = d->down_h > 1 ? d->down_h : 1,
+                      fw = d->down_w > 1 ? d->down_w : 1;
+        if ((d->t + ft - 1) % ft)
+            return fail(VAE_ERR_UNSUPPORTED, "T + down_t - 1 must be a multiple of down_t", 1,
+                        d->t, ft);
+        if (d->h % fh) return fail(VAE_ERR_UNSUPPORTED, "H must be a multiple of down_h", 2, d->h, fh);
+        if (d->w % fw) return fail(VAE_ERR_UNSUPPORTED, "W must be a multiple of down_w", 3, d->w, fw);
+    }
     if (d->mode == VAE_TILING_PATCH_HALO) {
         std::vector<Band> b;
         VAE_TRY(bands(d->h, d->patches_h, 2, &b));
@@ -185,7 +201,32 @@ vae_status_t check_fold(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t s
     return VAE_OK;
 }
 
+bool encodes(const vae_tiling_desc_t& d) {
+    return d.down_t > 1 || d.down_h > 1 || d.down_w > 1;
+}
+
+void desc_out_extents(const vae_tiling_desc_t& d, int32_t* t, int32_t* h, int32_t* w) {
+    if (encodes(d)) {
+        const int32_t ft = d.down_t > 1 ? d.down_t : 1;
+        *t = (d.t + ft - 1) / ft;
+        *h = d.h / (d.down_h > 1 ? d.down_h : 1);
+        *w = d.w / (d.down_w > 1 ? d.down_w : 1);
+        return;
+    }
+    *t = out_frames(d.t, d.scale_t);
+    *h = d.h * d.scale_h;
+    *w = d.w * d.scale_w;
+}
+
 void overlap_axes(const vae_tiling_desc_t& d, AxisTiling ax[3]) {
+    if (encodes(d)) {   // cut on the output latent grid; T whole
+        int32_t t, h, w;
+        desc_out_extents(d, &t, &h, &w);
+        ax[0] = AxisTiling{t, 0, 0, 1, 1};
+        ax[1] = AxisTiling{h, d.tile_h, d.stride_h, 1, 0};
+        ax[2] = AxisTiling{w, d.tile_w, d.stride_w, 1, 0};
+        return;
+    }
     ax[0] = AxisTiling{d.t, d.tile_t, d.stride_t, d.scale_t, 1};
     ax[1] = AxisTiling{d.h, d.tile_h, d.stride_h, d.scale_h, 0};
     ax[2] = AxisTiling{d.w, d.tile_w, d.stride_w, d.scale_w, 0};
@@ -231,6 +272,12 @@ std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
                     t.col = j;
                     t.latent = vae_box_t{ts, ts + tn, hs, hs + hn, ws, ws + wn};
                     t.out = vae_box_t{ot, ot + otn, oh, oh + ohn, ow, ow + own};
+                    if (encodes(d)) {   // the input-video box of the latent tile
+                        const int32_t fh = d.down_h > 1 ? d.down_h : 1;
+                        const int32_t fw = d.down_w > 1 ? d.down_w : 1;
+                        t.latent = vae_box_t{0, d.t, hs * fh, (hs + hn) * fh, ws * fw,
+                                             (ws + wn) * fw};
+                    }
                     t.lead_t = axis_lead(at, k);
                     t.trail_t = axis_trail(at, k);
                     t.lead_h = axis_lead(ah, i);
@@ -718,8 +765,9 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
         return fail(VAE_ERR_INVALID_ARG, "merge takes an overlap-blend tiling");
     if (tile_out->dtype != VAE_DTYPE_F32 || out->dtype != VAE_DTYPE_F32)
         return fail(VAE_ERR_UNSUPPORTED, "merge accumulates fp32 tensors");
-    if (out->n != desc->n || out->t != out_frames(desc->t, desc->scale_t) ||
-        out->h != (int64_t)desc->h * desc->scale_h || out->w != (int64_t)desc->w * desc->scale_w)
+    int32_t ot, oh, ow;
+    desc_out_extents(*desc, &ot, &oh, &ow);
+    if (out->n != desc->n || out->t != ot || out->h != oh || out->w != ow)
         return fail(VAE_ERR_INVALID_ARG, "out shape does not match the tiling");
     const vae_box_t& ob = tile->out;
     VAE_TRY(check_box(&ob, *out, "tile->out"));

@@ -256,11 +256,22 @@ BoxList scaled_boxes(const std::vector<Box>& latent_boxes, int64_t t, int ch, in
     return bl;
 }
 
-// Whether the plan has a space-to-depth fold (an encoder plan).
-bool plan_folds(const vae_decoder& d) {
+// Whether the plan has a space-to-depth fold (an encoder plan), and its total folds.
+bool plan_folds(const vae_decoder& d, int32_t* ft = nullptr, int32_t* fh = nullptr,
+                int32_t* fw = nullptr) {
+    int32_t t = 1, h = 1, w = 1;
+    bool any = false;
     for (const vae_layer_desc_t& l : d.layers)
-        if (l.op == VAE_OP_S2D) return true;
-    return false;
+        if (l.op == VAE_OP_S2D) {
+            any = true;
+            t *= l.st;
+            h *= l.sh;
+            w *= l.sw;
+        }
+    if (ft) *ft = t;
+    if (fh) *fh = h;
+    if (fw) *fw = w;
+    return any;
 }
 
 struct Req {
@@ -647,11 +658,18 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
     VAE_TRY(plan_output(d, desc, &out, &st, &sh, &sw));
     if (st != desc.scale_t || sh != desc.scale_h || sw != desc.scale_w)
         return fail(VAE_ERR_INVALID_ARG, "tiling scales do not match the decoder plan");
-    if (plan_folds(d) &&
-        (desc.mode != VAE_TILING_PATCH_HALO || desc.patches_h != 1 || desc.patches_w != 1))
+    int32_t ft, fh, fw;
+    const bool folds = plan_folds(d, &ft, &fh, &fw);
+    if (folds && desc.mode == VAE_TILING_PATCH_HALO && (desc.patches_h != 1 || desc.patches_w != 1))
         return fail(VAE_ERR_UNSUPPORTED,
-                    "a plan with space-to-depth folds (an encoder) runs untiled: patch-halo mode "
-                    "with a 1 x 1 grid");
+                    "a plan with space-to-depth folds (an encoder) runs patch-halo with a 1 x 1 "
+                    "grid, or overlap-blend with the plan's folds in down_*");
+    if (folds && desc.mode == VAE_TILING_OVERLAP_BLEND &&
+        (!encodes(desc) || std::max(desc.down_t, 1) != ft || std::max(desc.down_h, 1) != fh ||
+         std::max(desc.down_w, 1) != fw))
+        return fail(VAE_ERR_INVALID_ARG, "an encoder's overlap tiling needs down_* = its folds");
+    if (!folds && encodes(desc))
+        return fail(VAE_ERR_INVALID_ARG, "down_* is for plans with space-to-depth folds");
     if (desc.mode == VAE_TILING_PATCH_HALO && (int64_t)desc.patches_h * desc.patches_w > kMaxBoxes)
         return fail(VAE_ERR_UNSUPPORTED, "the decoder takes at most 16 patches", -1,
                     (int64_t)desc.patches_h * desc.patches_w, -1, 1);
