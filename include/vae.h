@@ -365,12 +365,15 @@ VAE_API vae_status_t vae_space_to_depth(const vae_tensor_t* x, int32_t st, int32
  * reading the causal decoder supports). With scale_t > 1, consecutive temporal tiles must share a
  * latent frame (stride_t < tile_t), or the scale_t - 1 frames before a tile's first frame would
  * come from no tile. Overlaps E are measured between neighbouring tiles' output spans.
- * Encoders (down_* > 1, scales 1, mode B only, T whole): n, t, h, w are the input video's extents,
- * and the tile grid (tile_*, stride_*) is cut on the output latent grid of
- * (t + down_t - 1) / down_t frames, h / down_h rows and w / down_w columns (P2: sample tiles 512
- * with stride 448 are 16 / 14 latent rows at a fold of 32, with per-tile latent shapes and a
- * latent-space blend). Each tile's `latent` box is then its input-video box (latent rows times
- * the fold, all frames) and `out` its latent box; the ramps run over the latent overlaps.
+ * Encoders (down_* > 1 = the plan's folds, scales 1, T whole): n, t, h, w are the input video's
+ * extents, and tiles are cut on the output latent grid of (t + down_t - 1) / down_t frames,
+ * h / down_h rows and w / down_w columns. Each tile's `latent` box is then its input-video box
+ * (latent rows times the fold, all frames) and `out` its latent box.
+ *  mode A: the bands are whole multiples of the fold (P4, encoder commit), i.e. the band rule over
+ *    latent rows; the result equals the untiled encode.
+ *  mode B: (P2: sample tiles 512 with stride 448 are 16 / 14 latent rows at a fold of 32, with
+ *    per-tile latent shapes and a latent-space blend) the ramps run over the latent overlaps.
+ * An encoder plan also runs untiled with patches 1 x 1 and no down_*.
  */
 enum { VAE_TILING_PATCH_HALO = 1, VAE_TILING_OVERLAP_BLEND = 2 };
 
@@ -429,8 +432,8 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  *  VAE_OP_RMS_SILU RMS norm + SiLU
  *  VAE_OP_ATTN    single-head frame attention of width cin (vae_frame_attention), fp32 activations
  *  VAE_OP_S2D     space-to-depth fold (st, sh, sw) with the causal front copies of frame 0
- *                 (vae_space_to_depth): an encoder plan. Such a plan runs untiled (patch-halo
- *                 mode, 1 x 1 grid, scales 1); its input extents must fold evenly.
+ *                 (vae_space_to_depth): an encoder plan. Such a plan runs untiled, or tiled with
+ *                 the tiling desc's down_* set to its folds; its input extents must fold evenly.
  * Dtypes:
  *  - conv weights and GroupNorm outputs (the operands of the next conv) have the plan dtype;
  *  - conv outputs and the residual stream have act_dtype;

@@ -212,11 +212,25 @@ def test_encoder_overlap_split_on_the_latent_grid(v, case):
         assert f["lead"] == r["lead"] and f["trail"] == r["trail"]
 
 
-def test_encoder_tiling_refusals(v):
-    with pytest.raises(v.VaeError) as e:          # folds in a patch-halo desc
+def test_encoder_patch_split_in_fold_units(v):
+    """Patch-halo bands of an encoder are whole multiples of its fold (the band rule over latent
+    rows): 2 latent rows -> 1 + 1, 5 latent columns -> 3 + 2; `latent` holds the pixel box."""
+    got = v.vae_tile_split(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 9, 64, 160, 4), (1, 1, 1),
+                                         patches=(2, 2), down=(8, 32, 32)))
+    ref = oracle.patch_tiles(2, 2, 5, 2, 2, (1, 1, 1))
+    assert len(got) == len(ref) == 4
+    for g, r in zip(got, ref):
+        f = _fields(g)
+        assert f["out"] == r["latent"]
+        _, _, h0, h1, w0, w1 = r["latent"]
+        assert f["latent"] == (0, 9, 32 * h0, 32 * h1, 32 * w0, 32 * w1)
+    with pytest.raises(v.VaeError) as e:          # 3 latent columns cannot take 4 bands
         v.vae_tile_split(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 9, 64, 96, 4), (1, 1, 1),
-                                       down=(8, 32, 32)))
-    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+                                       patches=(1, 4), down=(8, 32, 32)))
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 3
+
+
+def test_encoder_tiling_refusals(v):
     with pytest.raises(v.VaeError) as e:          # temporal tiles with folds
         v.vae_tile_split(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 9, 64, 96, 4), (1, 1, 1),
                                        tile=(2, 2), stride=(1, 1), tile_t=2, stride_t=1,
@@ -230,8 +244,8 @@ def test_encoder_tiling_refusals(v):
 
 def test_encoder_plan_tilings(v):
     """An encoder plan (space-to-depth folds) takes the 4-channel padded video, sizes its
-    workspace untiled and in latent-grid overlap tiles, and refuses patch grids, folds that are
-    not the plan's, and extents its folds do not divide."""
+    workspace untiled, in fold-unit patches and in latent-grid overlap tiles, and refuses tilings
+    without the plan's folds and extents its folds do not divide."""
     import vae_synth
     spec = vae_synth.LTX2_ENC_720P
     assert v.latent_channels(spec) == 4                # 3 -> 4: the 4x4 patchify gives 64
@@ -252,10 +266,13 @@ def test_encoder_plan_tilings(v):
     a = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1)))
     # the largest activation: the 128-channel fp32 stage-0 tensor, 121 x 176 x 320
     assert a >= 3 * 121 * 176 * 320 * 128 * 4
-    with pytest.raises(v.VaeError) as e:          # patches: not yet for a folding plan
+    with pytest.raises(v.VaeError) as e:          # patches need the plan's folds in down
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1),
                                          patches=(1, 2)))
-    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    c = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1),
+                                         patches=(1, 4), down=(8, 32, 32)))
+    assert c >= a
     with pytest.raises(v.VaeError) as e:          # overlap tiles need the plan's folds in down
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, shape, (1, 1, 1),
                                          tile=(16, 16), stride=(14, 14)))

@@ -84,14 +84,17 @@ def _oracle(name, tiles=None):
     return oracle.encode_overlap_blend(spec, x, _params(name), tiles[0], tiles[1])
 
 
-def _encode(v, name, operands="f16", repeat=1, tiles=None):
+def _encode(v, name, operands="f16", repeat=1, tiles=None, patches=None):
     import torch
     spec = vae_synth.WORKLOADS[name]
     x = ndhwc(vae_synth.latent(spec))
     xp = v.pad_latent(x, spec)
     enc = v.upload_decoder(spec, _params(name), operands=operands)
     xd = dev(xp, "bf16")
-    if tiles is None:
+    if patches is not None:
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xp.shape, (1, 1, 1), patches=patches,
+                             down=spec["down"])
+    elif tiles is None:
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xp.shape, (1, 1, 1))
     else:
         desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, xp.shape, (1, 1, 1), tile=tiles[0],
@@ -127,6 +130,16 @@ def test_encode_overlap_blend_matches_oracle(v, name, tiles):
     got = host(_encode(v, name, tiles=tiles))
     ref = _oracle(name, tiles)
     assert got.shape == ref.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
+@pytest.mark.parametrize("name,patches", [("ltx2_enc_small", (2, 2)), ("ltx2_enc_tiny", (1, 3))])
+def test_encode_patch_halo_matches_untiled_oracle(v, name, patches):
+    """Bands in whole multiples of the 32-pixel fold; halos read in place and GroupNorm statistics
+    merged across patches: the untiled encode."""
+    got = host(_encode(v, name, patches=patches))
+    ref = _oracle(name)
     p, m = psnr(got, ref), float(np.abs(got - ref).max())
     assert p >= 50.0 and m <= 2e-2, (p, m)
 

@@ -154,8 +154,6 @@ vae_status_t check_tiling(const vae_tiling_desc_t* d) {
     if (d->down_t < 0 || d->down_h < 0 || d->down_w < 0)
         return fail(VAE_ERR_INVALID_ARG, "folds must be >= 0");
     if (encodes(*d)) {
-        if (d->mode != VAE_TILING_OVERLAP_BLEND)
-            return fail(VAE_ERR_UNSUPPORTED, "an encoder tiling (down_*) is overlap-blend only");
         if (d->scale_t != 1 || d->scale_h != 1 || d->scale_w != 1 || d->tile_t > 0)
             return fail(VAE_ERR_UNSUPPORTED,
                         "an encoder tiling takes scales 1 and keeps T whole (tile_t = 0)");
@@ -168,9 +166,10 @@ vae_status_t check_tiling(const vae_tiling_desc_t* d) {
         if (d->w % fw) return fail(VAE_ERR_UNSUPPORTED, "W must be a multiple of down_w", 3, d->w, fw);
     }
     if (d->mode == VAE_TILING_PATCH_HALO) {
+        // an encoder's bands are whole multiples of its folds (P4, encoder commit)
         std::vector<Band> b;
-        VAE_TRY(bands(d->h, d->patches_h, 2, &b));
-        VAE_TRY(bands(d->w, d->patches_w, 3, &b));
+        VAE_TRY(bands(d->h / std::max(d->down_h, 1), d->patches_h, 2, &b));
+        VAE_TRY(bands(d->w / std::max(d->down_w, 1), d->patches_w, 3, &b));
     } else if (d->mode == VAE_TILING_OVERLAP_BLEND) {
         AxisTiling ax[3];
         overlap_axes(*d, ax);
@@ -235,7 +234,27 @@ void overlap_axes(const vae_tiling_desc_t& d, AxisTiling ax[3]) {
 std::vector<vae_tile_t> make_tiles(const vae_tiling_desc_t& d) {
     std::vector<vae_tile_t> tiles;
     const int32_t to = out_frames(d.t, d.scale_t);
-    if (d.mode == VAE_TILING_PATCH_HALO) {
+    if (d.mode == VAE_TILING_PATCH_HALO && encodes(d)) {
+        // bands in units of the fold: `latent` is the input-video box, `out` the latent box
+        const int32_t fh = std::max(d.down_h, 1), fw = std::max(d.down_w, 1);
+        int32_t ot, oh, ow;
+        desc_out_extents(d, &ot, &oh, &ow);
+        std::vector<Band> hb, wb;
+        bands(oh, d.patches_h, 2, &hb);
+        bands(ow, d.patches_w, 3, &wb);
+        for (size_t i = 0; i < hb.size(); ++i)
+            for (size_t j = 0; j < wb.size(); ++j) {
+                vae_tile_t t{};
+                t.index = (int32_t)tiles.size();
+                t.row = (int32_t)i;
+                t.col = (int32_t)j;
+                t.latent = vae_box_t{0, d.t, hb[i].start * fh, (hb[i].start + hb[i].size) * fh,
+                                     wb[j].start * fw, (wb[j].start + wb[j].size) * fw};
+                t.out = vae_box_t{0, ot, hb[i].start, hb[i].start + hb[i].size, wb[j].start,
+                                  wb[j].start + wb[j].size};
+                tiles.push_back(t);
+            }
+    } else if (d.mode == VAE_TILING_PATCH_HALO) {
         std::vector<Band> hb, wb;
         bands(d.h, d.patches_h, 2, &hb);
         bands(d.w, d.patches_w, 3, &wb);

@@ -660,14 +660,14 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
         return fail(VAE_ERR_INVALID_ARG, "tiling scales do not match the decoder plan");
     int32_t ft, fh, fw;
     const bool folds = plan_folds(d, &ft, &fh, &fw);
-    if (folds && desc.mode == VAE_TILING_PATCH_HALO && (desc.patches_h != 1 || desc.patches_w != 1))
-        return fail(VAE_ERR_UNSUPPORTED,
-                    "a plan with space-to-depth folds (an encoder) runs patch-halo with a 1 x 1 "
-                    "grid, or overlap-blend with the plan's folds in down_*");
-    if (folds && desc.mode == VAE_TILING_OVERLAP_BLEND &&
+    const bool untiled = desc.mode == VAE_TILING_PATCH_HALO && desc.patches_h == 1 &&
+                         desc.patches_w == 1 && !encodes(desc);
+    if (folds && !untiled &&
         (!encodes(desc) || std::max(desc.down_t, 1) != ft || std::max(desc.down_h, 1) != fh ||
          std::max(desc.down_w, 1) != fw))
-        return fail(VAE_ERR_INVALID_ARG, "an encoder's overlap tiling needs down_* = its folds");
+        return fail(VAE_ERR_INVALID_ARG,
+                    "an encoder (a plan with space-to-depth folds) is tiled with down_* = its "
+                    "folds, or runs untiled (1 x 1 patches, no down_*)");
     if (!folds && encodes(desc))
         return fail(VAE_ERR_INVALID_ARG, "down_* is for plans with space-to-depth folds");
     if (desc.mode == VAE_TILING_PATCH_HALO && (int64_t)desc.patches_h * desc.patches_w > kMaxBoxes)
