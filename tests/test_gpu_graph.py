@@ -1,4 +1,4 @@
-"""The decode captured in a HIP graph and replayed.
+"""The decode (and the encode) captured in a HIP graph and replayed.
 
 vae_decode_tiled enqueues kernels only: no allocation, copy, memset, event or synchronisation
 (with op timing off). A caller can therefore capture a whole decode, every layer of every
@@ -23,18 +23,31 @@ def v():
     return v
 
 
-@pytest.mark.parametrize("mode", ["patch", "overlap"])
-def test_decode_replays_from_a_hip_graph(v, mode):
+CASES = [
+    # (plan, tiling, tiling arguments)
+    ("ltx2_tiny", "patch", dict(patches=(1, 2))),
+    ("ltx2_tiny", "overlap", {}),
+    ("ltx2_mid", "overlap", dict(tile_t=2, stride_t=1)),           # temporal tiles as well
+    ("ltx2_enc_small", "patch", dict(patches=(1, 1))),             # the encoder, untiled
+    ("ltx2_enc_small", "patch", dict(patches=(2, 2), down=(8, 32, 32))),
+    ("ltx2_enc_small", "overlap", dict(down=(8, 32, 32))),         # latent-grid tiles
+]
+
+
+@pytest.mark.parametrize("name,mode,kw", CASES)
+def test_decode_replays_from_a_hip_graph(v, name, mode, kw):
     import torch
-    spec = vae_synth.LTX2_TINY
+    spec = vae_synth.WORKLOADS[name]
     z = ndhwc(vae_synth.latent(spec))
-    zd = dev(z, spec["dtype"])
+    zp = v.pad_latent(z, spec)
+    zd = dev(zp, spec["dtype"])
     dec = v.upload_decoder(spec, vae_synth.decoder_params(spec))
+    scale = spec.get("scale", (1, 1, 1))
     if mode == "patch":
-        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 2))
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, scale, **kw)
     else:
-        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, z.shape, spec["scale"],
-                             tile=spec["overlap_tile"], stride=spec["overlap_stride"])
+        desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, zp.shape, scale,
+                             tile=spec["overlap_tile"], stride=spec["overlap_stride"], **kw)
     ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
     shape = oracle.output_shape(spec, z.shape)
     eager = torch.empty(shape, dtype=torch.float32, device="cuda")
