@@ -155,3 +155,24 @@ def test_encode_is_deterministic(v):
     import torch
     a, b = _encode(v, "ltx2_enc_tiny", repeat=2)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("tile,stride", [((2, 3), (1, 2)), ((3, 2), (2, 2))])
+def test_tile_merge_with_an_encoder_desc(v, tile, stride):
+    """vae_tile_merge under an encoder desc (down = 8, 32, 32): the tiles are latent boxes, the
+    weight sums come from the latent grid, so blending exact crops of a latent gives it back."""
+    import torch
+    t, h, w = 17, 4 * 32, 5 * 32                      # latent [3, 4, 5]
+    desc = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, t, h, w, 4), (1, 1, 1), tile=tile,
+                         stride=stride, down=(8, 32, 32))
+    tiles = v.vae_tile_split(desc)
+    lat = vae_synth.normal((1, 3, 4, 5, 6), [61]).astype(np.float64)
+    out = torch.full(lat.shape, 3.0, device="cuda", dtype=torch.float32)
+    for k, tl in enumerate(tiles):
+        o = tl.out
+        crop = lat[:, o.t0:o.t1, o.h0:o.h1, o.w0:o.w1]
+        flags = (v.VAE_MERGE_ZERO if k == 0 else 0) | \
+                (v.VAE_MERGE_FINALIZE if k == len(tiles) - 1 else 0)
+        v.vae_tile_merge(dev(crop, "f32"), tl, desc, out, flags)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host(out), lat, rtol=1e-6, atol=1e-6)
