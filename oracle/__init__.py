@@ -30,11 +30,14 @@ Parity status of each function:
   closed forms, Chan split invariance, negative control), SiLU identities, upsampling (repeat,
   inverse), tiling (page-printed grids, band rule), merge identities, mode A == whole decode,
   mode B 1x1 == whole decode; RMS norm (closed forms, torch CPU rms_norm), frame attention (torch
-  CPU scaled_dot_product_attention, uniform-attention and permutation invariants);
+  CPU scaled_dot_product_attention, uniform-attention and permutation invariants); the encode
+  path (space_to_depth by brute force and its inverse, patch-halo encode == whole, fold-only
+  tiled encodes == whole, the strided causal conv against torch CPU conv3d and brute force);
 - parity unpinned: the absolute output values of a full random-init decoder. The pages print no
   tensor values, so a decoder's output is pinned only through its parts and the invariants above.
 """
-from .layers import (causal_conv3d, conv3d_valid, causal_time_pad, group_norm, silu,
+from .layers import (causal_conv3d, strided_causal_conv3d, conv3d_valid, causal_time_pad,
+                     group_norm, silu,
                      nearest_upsample, depth_to_space, space_to_depth, rms_norm, softmax,
                      frame_attention)
 from .stats import group_moments, chan_combine, normalize_with
@@ -43,7 +46,8 @@ from .decoder import (decode, decode_patch_halo, decode_overlap_blend, merge_til
                       output_shape, encode, encode_patch_halo, encode_overlap_blend)
 
 __all__ = [
-    "causal_conv3d", "conv3d_valid", "causal_time_pad", "group_norm", "silu", "nearest_upsample",
+    "causal_conv3d", "strided_causal_conv3d", "conv3d_valid", "causal_time_pad", "group_norm",
+    "silu", "nearest_upsample",
     "depth_to_space", "space_to_depth", "rms_norm", "softmax", "frame_attention",
     "group_moments", "chan_combine", "encode", "encode_patch_halo", "encode_overlap_blend",
     "normalize_with", "bands", "axis_tiles",

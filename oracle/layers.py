@@ -75,6 +75,28 @@ def causal_conv3d(x: np.ndarray, w: np.ndarray, b=None) -> np.ndarray:
     return conv3d_valid(xp, w, b)
 
 
+def strided_causal_conv3d(x: np.ndarray, w: np.ndarray, b=None, stride=(2, 2, 2),
+                          pad_hw=((1, 1), (1, 1))) -> np.ndarray:
+    """Strided causal Conv3d: the bare strided downsampler of an encoder.
+
+    One of the four LTX-2 encoder downsample kinds is a bare strided conv, and Wan's downsampler
+    pads (0, 1, 0, 1) and then strides 2 over the result ("Add tiled VAE parallelism & extended
+    model support", LTX-2 and Qwen-Image/Wan encoder commit messages). Temporal: kt-1 copies of
+    frame 0 in front, then output frame t reads padded frames st*t .. st*t + kt - 1 (input frames
+    st*t - (kt-1) .. st*t, clamped at 0), so T frames become (T - 1) // st + 1 (121 -> 61).
+    Spatial: zero rows/columns ``pad_hw`` = ((top, bottom), (left, right)), then stride.
+    Evaluated as the stride-1 valid correlation of the padded input, kept at every stride-th
+    position: y[o] = y1[stride * o].
+    """
+    w = np.asarray(w)
+    _, _, kt, kh, kw = w.shape
+    st, sh, sw = stride
+    xp = causal_time_pad(x, kt)
+    xp = np.pad(xp, ((0, 0), (0, 0), tuple(pad_hw[0]), tuple(pad_hw[1]), (0, 0)))
+    y1 = conv3d_valid(xp, w, b)
+    return np.ascontiguousarray(y1[:, ::st, ::sh, ::sw])
+
+
 def group_norm(x: np.ndarray, groups: int, eps: float, gamma=None, beta=None) -> np.ndarray:
     """torch.nn.GroupNorm's definition: per (sample, group), over the group's channels and T, H, W.
 

@@ -105,3 +105,47 @@ def test_encode_overlap_blend_differs_from_whole_only_by_tiling():
     tiled = oracle.encode_overlap_blend(spec, x, p, spec["overlap_tile"], spec["overlap_stride"])
     assert tiled.shape == whole.shape and np.all(np.isfinite(tiled))
     assert 1e-6 < np.abs(tiled - whole).max() < 10 * np.abs(whole).max()
+
+
+# ------------------------------------------------------------------------------------------------
+# The bare strided downsampler conv (oracle side; the GPU kernel is not built yet)
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("stride,pad,t", [((2, 2, 2), ((1, 1), (1, 1)), 5),   # LTX-2 kind
+                                          ((1, 2, 2), ((0, 1), (0, 1)), 3),   # Wan: pad, stride
+                                          ((2, 1, 2), ((1, 1), (0, 1)), 4)])
+def test_strided_causal_conv_against_torch(stride, pad, t):
+    """Against torch's own strided conv3d (CPU, float64) on the causally padded input."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((1, t, 6, 8, 3))
+    w = rng.standard_normal((4, 3, 3, 3, 3))
+    b = rng.standard_normal(4)
+    got = oracle.strided_causal_conv3d(x, w, b, stride, pad)
+    xp = np.concatenate([x[:, :1]] * 2 + [x], axis=1)                 # causal front copies
+    xt = torch.from_numpy(np.ascontiguousarray(xp.transpose(0, 4, 1, 2, 3)))
+    xt = torch.nn.functional.pad(xt, (pad[1][0], pad[1][1], pad[0][0], pad[0][1], 0, 0))
+    ref = torch.nn.functional.conv3d(xt, torch.from_numpy(w), torch.from_numpy(b), stride=stride)
+    ref = ref.numpy().transpose(0, 2, 3, 4, 1)
+    assert got.shape == ref.shape
+    assert got.shape[1] == (t - 1) // stride[0] + 1
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_strided_causal_conv_by_brute_force():
+    """Every output by explicit loops: frame st*t + a - 2 clamped at 0, row sh*h + p - top,
+    column sw*w + q - left, zeros outside the image."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((1, 3, 4, 5, 2))
+    w = rng.standard_normal((2, 2, 3, 3, 3))
+    stride, pad = (2, 2, 2), ((1, 1), (1, 1))
+    y = oracle.strided_causal_conv3d(x, w, None, stride, pad)
+    assert y.shape == (1, 2, 2, 3, 2)
+    for t, h, ww, o in itertools.product(range(2), range(2), range(3), range(2)):
+        acc = 0.0
+        for c, a, p, q in itertools.product(range(2), range(3), range(3), range(3)):
+            ti = max(2 * t + a - 2, 0)
+            hi, wi = 2 * h + p - 1, 2 * ww + q - 1
+            if 0 <= hi < 4 and 0 <= wi < 5:
+                acc += w[o, c, a, p, q] * x[0, ti, hi, wi, c]
+        assert abs(y[0, t, h, ww, o] - acc) < 1e-12
