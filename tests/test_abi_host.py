@@ -325,3 +325,27 @@ def test_fused_conv_validation_needs_no_gpu(v):
     with pytest.raises(v.VaeError) as e:          # factors must be powers of two
         v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), in_up=(3, 1))
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
+
+
+def test_space_to_depth_validation_needs_no_gpu(v):
+    """vae_space_to_depth's argument checks run on the host (host tensors stand in for device
+    buffers and the null stream handle; every call below is refused before anything is
+    launched)."""
+    import torch
+    x = torch.zeros((1, 5, 8, 12, 4), dtype=torch.bfloat16)
+    with pytest.raises(v.VaeError) as e:          # 5 frames fold causally by 2 -> 3, not 2
+        v.vae_space_to_depth(x, 2, 2, 2, torch.zeros((1, 2, 4, 6, 32), dtype=torch.bfloat16),
+                             stream=0)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:          # 12 columns do not fold by 5
+        v.vae_space_to_depth(x, 1, 2, 5, torch.zeros((1, 5, 4, 2, 40), dtype=torch.bfloat16),
+                             stream=0)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["axis"] == 3
+    assert e.value.info["required_multiple"] == 5
+    with pytest.raises(v.VaeError) as e:          # factors below 1
+        v.vae_space_to_depth(x, 0, 2, 2, torch.zeros((1, 3, 4, 6, 32), dtype=torch.bfloat16),
+                             stream=0)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:          # y aliasing x
+        v.vae_space_to_depth(x, 1, 1, 1, x, stream=0)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
