@@ -271,13 +271,38 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(const double* __r
     }
 }
 
-// grid (groups, N). ws: [N][G][slots][3], the layout a fused conv epilogue writes.
+// Slot counts above this are merged in two passes: chunks of kSlotChunk slots, one block each, in
+// place, then the chunk results. A conv epilogue leaves up to ~50k slots per (sample, group) at
+// the 720p shapes; one block per group merging them all took ~27 us per GroupNorm.
+constexpr int64_t kSlotChunk = 1024;
+
+// grid (chunks, groups, N). Chunk c merges slots [c * L, min((c + 1) * L, slots)) of ws
+// [N][G][slots][3] in a fixed order and writes the result over its first slot (only this block
+// reads or writes the chunk).
+__global__ __launch_bounds__(kThreads) void gn_slots_chunk_kernel(double* __restrict__ ws,
+                                                                  int64_t slots, int32_t groups,
+                                                                  int32_t L) {
+    const int c = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
+    double* base = ws + ((int64_t)n * groups + g) * slots * 3;
+    const int64_t lo = (int64_t)c * L;
+    const int64_t hi = lo + L < slots ? lo + L : slots;
+    const Moments m = block_merge(base, 3, (int)lo, (int)hi);
+    if (threadIdx.x == 0) {
+        base[lo * 3] = m.n;
+        base[lo * 3 + 1] = m.mean;
+        base[lo * 3 + 2] = m.m2;
+    }
+}
+
+// grid (groups, N). ws: [N][G][slots][3], the layout a fused conv epilogue writes; merges `count`
+// triples `stride` slots apart (every slot, or the first slot of every chunk).
 __global__ __launch_bounds__(kThreads) void gn_finalize_slots_kernel(const double* __restrict__ ws,
-                                                                     int64_t slots, int32_t groups,
+                                                                     int64_t slots, int64_t stride,
+                                                                     int32_t count, int32_t groups,
                                                                      float eps, float* mean_rstd) {
     const int g = blockIdx.x, n = blockIdx.y;
     const double* base = ws + ((int64_t)n * groups + g) * slots * 3;
-    const Moments m = block_merge(base, 3, 0, (int)slots);
+    const Moments m = block_merge(base, 3 * stride, 0, count);
     if (threadIdx.x == 0) {
         const double var = m.n > 0.0 ? m.m2 / m.n : 0.0;
         mean_rstd[((int64_t)n * groups + g) * 2] = (float)m.mean;
@@ -422,11 +447,23 @@ vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, i
     return VAE_OK;
 }
 
-vae_status_t launch_gn_finalize_slots(const double* ws, int64_t slots, int32_t n, int32_t groups,
+vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int32_t groups,
                                       float eps, float* mean_rstd, hipStream_t stream) {
     if (slots > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "too many statistics slots");
+    if (slots <= kSlotChunk) {
+        hipLaunchKernelGGL(gn_finalize_slots_kernel, dim3((unsigned)groups, (unsigned)n),
+                           dim3(kThreads), 0, stream, ws, slots, (int64_t)1, (int32_t)slots,
+                           groups, eps, mean_rstd);
+        VAE_HIP_CHECK(hipGetLastError());
+        return VAE_OK;
+    }
+    const int64_t chunks = ceil_div(slots, kSlotChunk);
+    hipLaunchKernelGGL(gn_slots_chunk_kernel, dim3((unsigned)chunks, (unsigned)groups, (unsigned)n),
+                       dim3(kThreads), 0, stream, ws, slots, groups, (int32_t)kSlotChunk);
+    VAE_HIP_CHECK(hipGetLastError());
     hipLaunchKernelGGL(gn_finalize_slots_kernel, dim3((unsigned)groups, (unsigned)n),
-                       dim3(kThreads), 0, stream, ws, slots, groups, eps, mean_rstd);
+                       dim3(kThreads), 0, stream, ws, slots, kSlotChunk, (int32_t)chunks, groups,
+                       eps, mean_rstd);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }

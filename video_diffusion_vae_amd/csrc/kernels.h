@@ -55,7 +55,9 @@ vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_
 vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, int32_t groups,
                                float eps, float* mean_rstd, hipStream_t stream);
 // Partials [N][groups][slots][3] (as a fused conv writes them) -> mean/rstd [N][groups][2].
-vae_status_t launch_gn_finalize_slots(const double* ws, int64_t slots, int32_t n, int32_t groups,
+// Large slot counts are merged in two passes, the first in place over ws (whose contents are
+// then spent).
+vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int32_t groups,
                                       float eps, float* mean_rstd, hipStream_t stream);
 vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t groups,
                              const float* mean_rstd, const float* gamma, const float* beta,
