@@ -176,3 +176,45 @@ def test_tile_merge_with_an_encoder_desc(v, tile, stride):
         v.vae_tile_merge(dev(crop, "f32"), tl, desc, out, flags)
     torch.cuda.synchronize()
     np.testing.assert_allclose(host(out), lat, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("patches", [None, (1, 4)])
+def test_ltx2_720p_encode_against_golden(v, patches):
+    """The full LTX-2-shaped 720p encode ([1,3,121,704,1280] -> [1,16,22,40,256]), untiled and in
+    1 x 4 patch-halo bands, at the latent positions the oracle's fp64 encode stored
+    (tests/golden/make_ltx2_enc_720p_samples.py), all 256 channels each."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "ltx2_enc_720p_samples.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path)
+    spec = vae_synth.LTX2_ENC_720P
+    import torch
+    x = ndhwc(vae_synth.latent(spec))
+    xp = v.pad_latent(x, spec)
+    enc = v.upload_decoder(spec, vae_synth.decoder_params(spec, affine_seed=9))
+    xd = dev(xp, "bf16")
+    del x, xp
+    if patches is None:
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xd.shape, (1, 1, 1))
+    else:
+        desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xd.shape, (1, 1, 1), patches=patches,
+                             down=spec["down"])
+    ws = torch.empty(enc.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out = torch.full(tuple(int(d) for d in g["shape"]), float("nan"), device="cuda",
+                     dtype=torch.float32)
+    enc.vae_decode_tiled(xd, desc, out, ws)
+    torch.cuda.synchronize()
+    enc.close()
+    del ws, xd
+    pos = g["positions"]
+    got = out[0, pos[:, 0], pos[:, 1], pos[:, 2], :].double().cpu().numpy()
+    ref = g["values"].astype(np.float64)
+    assert np.all(np.isfinite(got))
+    p = 10 * np.log10((float(g["out_max"]) - float(g["out_min"])) ** 2 / np.mean((got - ref) ** 2))
+    m = float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+    o = out.double()
+    assert abs(float(o.mean()) - float(g["out_mean"])) <= 1e-3 * float(g["out_std"])
+    assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
