@@ -436,10 +436,11 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  *                 the tiling desc's down_* set to its folds; its input extents must fold evenly.
  * Dtypes:
  *  - conv weights and GroupNorm outputs (the operands of the next conv) have the plan dtype;
- *  - conv outputs and the residual stream have act_dtype;
+ *  - conv outputs and the residual stream have act_dtype, which must be VAE_DTYPE_F32 (anything
+ *    else is refused with VAE_ERR_UNSUPPORTED): with bf16 weights this keeps the bf16 rounding
+ *    to the conv operands alone. Storing the activations in bf16 adds about 40 roundings on the
+ *    way through the LTX-2-shaped plan and misses the 2e-2 max-abs bound of a bf16 decode;
  *  - the latent has the plan dtype, and the decoded output is fp32.
- * With bf16 weights, fp32 activations keep the bf16 rounding to the conv operands alone: about
- * 40 fewer roundings on the way through the LTX-2-shaped plan.
  * VAE_DECODE_SPLIT_FP32_OPERANDS goes further for convs that read an fp32 activation (the
  * upsampling convs read the fp32 residual stream): each such CONV runs with VAE_CONV_SPLIT_FP32
  * unless its no_split is set. A standalone GN_SILU followed by a splitting CONV writes fp32 for
@@ -475,7 +476,8 @@ typedef struct vae_layer_desc {
 enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1, VAE_DECODE_F16_OPERANDS = 2 };
 typedef struct vae_decoder_spec {
     int32_t dtype;              /* weights and convolution operands: VAE_DTYPE_* */
-    int32_t act_dtype;          /* activations stored between ops (conv outputs, residual stream) */
+    int32_t act_dtype;          /* activations stored between ops (conv outputs, residual
+                                   stream): VAE_DTYPE_F32 */
     int32_t flags;              /* VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS or 0 */
     int32_t latent_channels;
     int32_t groups;

@@ -145,10 +145,11 @@ def test_decoder_plan_validation(v):
     bad[0] = {"op": "conv", "cin": 8, "cout": 128}
     with pytest.raises(v.VaeError):           # channels do not chain
         v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, bad, fake[:0])
-    with pytest.raises(v.VaeError) as e:      # bf16 activations: the last conv must be fp32
+    with pytest.raises(v.VaeError) as e:      # bf16 activation storage misses the bf16 bar
         v.Decoder(v.VAE_DTYPE_BF16, 16, 32, 1e-6, spec["layers"], fake[:0],
                   act_dtype=v.VAE_DTYPE_BF16)
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    assert "fp32" in str(e.value)
     with pytest.raises(v.VaeError) as e:      # an fp32 plan cannot store bf16 activations
         v.Decoder(v.VAE_DTYPE_F32, 16, 32, 1e-6, spec["layers"], fake[:0],
                   act_dtype=v.VAE_DTYPE_BF16)
@@ -189,6 +190,48 @@ def test_workspace_query_needs_no_gpu(v):
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
                                          (8, 16, 32), patches=(1, 4)))
     dec.close()
+
+
+class _FakePtr:
+    """A non-null device-pointer stand-in: creating a decoder never dereferences it."""
+
+    def __init__(self, i):
+        self.p = 0x1000 * (i + 1)
+
+    def data_ptr(self):
+        return self.p
+
+
+def _mixed_plan(block):
+    return [{"op": "conv", "cin": 32, "cout": 128}, {"op": block, "c": 128}, {"op": "gn_silu"},
+            {"op": "conv", "cin": 128, "cout": 32, "f32_out": True}]
+
+
+@pytest.mark.parametrize("flags", ["f16", "none"])
+def test_mixed_rms_gn_plan_workspace_holds_fused_partials(v, flags):
+    """The second conv of a RES_RMS block gathers the statistics of a GroupNorm that follows it in
+    its epilogue: the decode workspace must hold those partials. Sized like a RES block's (whose
+    first conv gathers partials of the same shape), and at least three activation buffers plus
+    the partials that vae_conv3d_causal_fused_workspace reports for that conv."""
+    import torch
+    shape = (1, 5, 64, 64, 32)
+    fl = v.VAE_DECODE_F16_OPERANDS if flags == "f16" else 0
+    sizes = {}
+    for block in ("res", "res_rms"):
+        layers = _mixed_plan(block)
+        n_ptr = sum({"conv": 2, "res": 8, "res_rms": 8, "gn_silu": 2}[op["op"]] for op in layers)
+        dec = v.Decoder(v.VAE_DTYPE_BF16, 32, 32, 1e-6, layers,
+                        [_FakePtr(i) for i in range(n_ptr)], flags=fl)
+        sizes[block] = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, (1, 1, 1)))
+        dec.close()
+    x = torch.zeros((1, 5, 64, 64, 128), dtype=torch.bfloat16)
+    w = torch.zeros((128, 3, 3, 3, 128), dtype=torch.bfloat16)
+    y = torch.zeros((1, 5, 64, 64, 128), dtype=torch.float32)
+    part = v.vae_conv3d_causal_fused_workspace(x, w, y, gn_groups=32)
+    assert part > 0
+    act = 5 * 64 * 64 * 128 * 4                   # the largest activation: fp32, 128 channels
+    assert sizes["res_rms"] >= 3 * act + part
+    assert sizes["res_rms"] == sizes["res"]
 
 
 @pytest.mark.parametrize("case", [((121, 704, 1280), (16, 16), (14, 14)),

@@ -260,19 +260,6 @@ def test_ltx2_tiny_batch_of_two(v, mode, patches):
     _bf16_bar(got, oracle_out("ltx2_tiny_n2", "whole" if mode == "patch" else "overlap"))
 
 
-def test_bf16_activation_storage_variant(v):
-    """Storing every activation in bf16 (act_dtype=bf16) is the faster, less exact variant. About
-    40 extra roundings keep it above 50 dB PSNR, but it is not held to the 2e-2 max-abs bar; the
-    default (fp32 activations) is."""
-    import torch
-    got = gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16")
-    ref = oracle_out("ltx2_tiny", "whole")
-    assert psnr(host(got), ref) >= 50.0
-    # a bf16 stream has nothing finer to hand on: the fp16 operand flag changes nothing
-    same = gpu_decode(v, "ltx2_tiny", "patch", (1, 2), act="bf16", operands="bf16")
-    assert torch.equal(got, same)
-
-
 @pytest.mark.parametrize("operands", ["f16", "split"])
 def test_packed_and_standard_weights_decode_identically(v, operands):
     import torch

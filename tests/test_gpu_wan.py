@@ -158,7 +158,11 @@ def _decode(v, name, mode, patches=(1, 1), operands="f16", repeat=1, tt=(0, 0)):
                                                ("wan_tiny", "overlap", (1, 1)),
                                                ("wan_small", "patch", (1, 2)),
                                                ("wan_small", "patch", (1, 1)),
-                                               ("wan_small", "overlap", (1, 1))])
+                                               ("wan_small", "overlap", (1, 1)),
+                                               # an RMS residual block feeding a GroupNorm
+                                               ("mixed_rms_gn", "patch", (1, 2)),
+                                               ("mixed_rms_gn", "patch", (1, 1)),
+                                               ("mixed_rms_gn", "overlap", (1, 1))])
 def test_wan_shaped_decode(v, name, mode, patches, operands):
     got = host(_decode(v, name, mode, patches, operands))
     ref = _oracle(name, mode)

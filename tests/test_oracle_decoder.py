@@ -101,6 +101,22 @@ def _torch_decode(spec, z, params):
         return F.silu(F.group_norm(h, g, torch.from_numpy(p["gamma"]).double(),
                                    torch.from_numpy(p["beta"]).double(), eps))
 
+    def rms(h, p):
+        # torch's rms_norm normalises the trailing dims: move channels last, then back
+        y = F.rms_norm(h.permute(0, 2, 3, 4, 1), (h.shape[1],),
+                       torch.from_numpy(p["gamma"]).double(), eps)
+        return (y + torch.from_numpy(p["beta"]).double()).permute(0, 4, 1, 2, 3)
+
+    def attn(h, p):
+        n, c, t, hh, ww = h.shape
+        xn = rms(h, p).permute(0, 2, 3, 4, 1).reshape(n * t, 1, hh * ww, c)
+        qkv = F.linear(xn, torch.from_numpy(p["w_qkv"]).double(),
+                       torch.from_numpy(p["b_qkv"]).double())
+        q, k, v = qkv.split(c, dim=-1)
+        o = F.scaled_dot_product_attention(q, k, v)           # softmax(q k^T / sqrt(c)) v
+        y = F.linear(o, torch.from_numpy(p["w_out"]).double(), torch.from_numpy(p["b_out"]).double())
+        return y.reshape(n, t, hh, ww, c).permute(0, 4, 1, 2, 3) + h
+
     h = torch.from_numpy(z).double().permute(0, 4, 1, 2, 3)
     for op in spec["layers"]:
         k = op["op"]
@@ -109,8 +125,23 @@ def _torch_decode(spec, z, params):
         elif k == "res":
             g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
             h = conv(gn(conv(gn(h, g1), c1), g2), c2) + h
+        elif k == "res_rms":
+            g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+            h = conv(F.silu(rms(conv(F.silu(rms(h, g1)), c1), g2)), c2) + h
         elif k == "gn_silu":
             h = gn(h, next(it))
+        elif k == "rms_silu":
+            h = F.silu(rms(h, next(it)))
+        elif k == "attn":
+            h = attn(h, next(it))
+        elif k == "s2d":
+            # causal front pad of st-1 copies of frame 0, then fold (dt, dh, dw) slowest into C
+            st, sh, sw = op["st"], op["sh"], op["sw"]
+            h = torch.cat([h[:, :, :1]] * (st - 1) + [h], dim=2)
+            n, c, t, hh, ww = h.shape
+            h = h.reshape(n, c, t // st, st, hh // sh, sh, ww // sw, sw)
+            h = h.permute(0, 3, 5, 7, 1, 2, 4, 6).reshape(n, st * sh * sw * c, t // st,
+                                                          hh // sh, ww // sw)
         elif k == "nearest":
             h = F.interpolate(h, scale_factor=(1, op["sh"], op["sw"]), mode="nearest")
         elif k == "d2s":
@@ -129,6 +160,39 @@ def test_tiny_decoder_matches_torch_library_graph():
     ref = _torch_decode(spec, z, params)
     got = oracle.decode(spec, z, params)
     assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-11
+
+
+@pytest.mark.parametrize("name", ["wan_tiny", "ltx2_enc_tiny"])
+def test_plan_matches_torch_library_graph(name):
+    """The RMS-norm residual blocks, the frame attention (torch's rms_norm, linear and
+    scaled_dot_product_attention) and the space-to-depth folds (a reshape) of the Wan-shaped
+    decoder and the LTX-2-shaped encoder, rebuilt from torch CPU library ops, with random
+    biases, gammas and betas."""
+    spec = vae_synth.WORKLOADS[name]
+    z = ndhwc(vae_synth.latent(spec)).astype(np.float64)
+    params = vae_synth.decoder_params(spec, affine_seed=11)
+    ref = _torch_decode(spec, z, params)
+    got = oracle.decode(spec, z, params)
+    assert got.shape == ref.shape == oracle.output_shape(spec, z.shape)
+    assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-11
+
+
+def test_torch_library_graph_detects_a_planted_error():
+    """Negative control: an oracle attention with its query projection's bias dropped must differ
+    from the library graph by far more than the pin's tolerance. (A key bias would not do: it
+    adds the same logit to every key of a query, which the softmax cancels.)"""
+    spec = vae_synth.WAN_TINY
+    z = ndhwc(vae_synth.latent(spec)).astype(np.float64)
+    params = vae_synth.decoder_params(spec, affine_seed=11)
+    ref = _torch_decode(spec, z, params)
+    c = next(p for p in params if p["kind"] == "attn")["c"]
+    bad = [dict(p) for p in params]
+    for p in bad:
+        if p["kind"] == "attn":
+            p["b_qkv"] = np.asarray(p["b_qkv"]).copy()
+            p["b_qkv"][:c] = 0.0
+    got = oracle.decode(spec, z, bad)
+    assert np.abs(got - ref).max() / np.abs(ref).max() > 1e-6
 
 
 @pytest.mark.parametrize("name,grid", [("wan_tiny", (2, 2)), ("wan_small", (1, 2))])

@@ -53,7 +53,8 @@ import numpy as np
 
 __all__ = [
     "CONV_GN", "TINY_DECODER", "LTX2_720P", "LTX2_SMALL", "LTX2_MID", "LTX2_720P_1F", "LTX2_TINY",
-    "LTX2_TINY_N2", "WAN_720P", "WAN_SMALL", "WAN_720P_1F", "WAN_720P_6F", "WAN_TINY", "WORKLOADS",
+    "LTX2_TINY_N2", "WAN_720P", "WAN_SMALL", "WAN_720P_1F", "WAN_720P_6F", "WAN_TINY",
+    "MIXED_RMS_GN", "WORKLOADS",
     "round_bf16", "bf16_bits", "normal", "uniform", "latent", "decoder_params", "conv_params",
     "walk_plan", "with_latent",
 ]
@@ -231,6 +232,25 @@ for _op in WAN_TINY["layers"]:
                 not (_k == "cout" and _op.get("f32_out")):
             _op[_k] //= 4
 
+# The Wan-shaped decoder is described with both RMS-style norms and GroupNorm variants: an RMS
+# residual block whose output feeds a GroupNorm (its second conv then gathers the GroupNorm's
+# statistics), at a size the oracle decodes in a second.
+MIXED_RMS_GN = {
+    "name": "mixed_rms_gn",
+    "dtype": "bf16",
+    "latent": (1, 32, 3, 12, 20),
+    "groups": 32, "eps": 1e-6,
+    "layers": [
+        {"op": "conv", "cin": 32, "cout": 128},
+        {"op": "res_rms", "c": 128},
+        {"op": "gn_silu"},
+        {"op": "conv", "cin": 128, "cout": 32, "f32_out": True},
+    ],
+    "scale": (1, 1, 1),
+    "patch_grid": (1, 2),
+    "overlap_tile": (6, 8), "overlap_stride": (4, 6),
+}
+
 # LTX-2-shaped encoder: video [1,3,121,704,1280] -> latent [1,256,16,22,40] (mean and log-variance,
 # 128 channels each), widths 128/256/512/1024. Each downsampler is a stride-1 causal conv to
 # C_next / 8 channels, then a (2,2,2) space-to-depth fold with the causal front pad (121 -> 61 -> 31
@@ -286,8 +306,8 @@ LTX2_ENC_SMALL = with_input(LTX2_ENC_720P, (1, 3, 9, 64, 160), "ltx2_enc_small",
 
 WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
                                     LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2, WAN_720P, WAN_SMALL,
-                                    WAN_720P_1F, WAN_720P_6F, WAN_TINY, LTX2_ENC_720P,
-                                    LTX2_ENC_TINY, LTX2_ENC_SMALL)}
+                                    WAN_720P_1F, WAN_720P_6F, WAN_TINY, MIXED_RMS_GN,
+                                    LTX2_ENC_720P, LTX2_ENC_TINY, LTX2_ENC_SMALL)}
 
 
 # ----------------------------------------------------------------------------------------------

@@ -242,14 +242,19 @@ vae_tensor_t tensor_of(void* p, const Shape& s) {
 Shape shape_of(const vae_tensor_t& t) { return Shape{t.n, t.t, t.h, t.w, t.c, t.dtype}; }
 
 // Input-grid patch boxes scaled to an activation with cumulative spatial scale (ch, cw) and
-// cumulative fold (fh, fw): rows b.h0 * ch / fh and so on. Patch grids of plans that fold are
-// 1 x 1, so the division is exact.
+// cumulative fold (fh, fw): rows b.h0 * ch / fh and so on. The division is exact: an encoder's
+// patch bands are cut in whole multiples of its total fold (check_tiling refuses other bands),
+// and a partial fold (fh, fw) divides the total one. `ok`, when given, is cleared if a division
+// would not be exact.
 BoxList scaled_boxes(const std::vector<Box>& latent_boxes, int64_t t, int ch, int cw, int fh = 1,
-                     int fw = 1) {
+                     int fw = 1, bool* ok = nullptr) {
     BoxList bl;
     bl.n = (int32_t)latent_boxes.size();
     for (size_t i = 0; i < latent_boxes.size(); ++i) {
         const Box& b = latent_boxes[i];
+        if (ok && ((int64_t)b.h0 * ch % fh || (int64_t)b.h1 * ch % fh ||
+                   (int64_t)b.w0 * cw % fw || (int64_t)b.w1 * cw % fw))
+            *ok = false;
         bl.b[i] = Box{0, (int32_t)t, b.h0 * ch / fh, b.h1 * ch / fh, b.w0 * cw / fw,
                       b.w1 * cw / fw};
     }
@@ -284,8 +289,9 @@ struct Req {
 };
 
 // Requirements of one run of the plan on an input of shape `in` with patch boxes `boxes`.
-void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>& boxes,
-                  bool final_in_buffer, Req* r) {
+vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>& boxes,
+                          bool final_in_buffer, Req* r) {
+    bool exact = true;   // every patch box scales to whole rows and columns of each activation
     std::vector<Shape> shapes;
     walk(d, in, &shapes, nullptr, nullptr, nullptr);
     Shape cur = in;
@@ -310,8 +316,8 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
             r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
             vae_tensor_t x = tensor_of(nullptr, cur);
             r->gn = std::max<int64_t>(
-                r->gn, (int64_t)gn_stats_workspace(x, scaled_boxes(boxes, cur.t, ch, cw, fh, fw),
-                                                   d.groups));
+                r->gn, (int64_t)gn_stats_workspace(
+                           x, scaled_boxes(boxes, cur.t, ch, cw, fh, fw, &exact), d.groups));
             r->mr = std::max<int64_t>(r->mr, cur.n * d.groups * 2 * (int64_t)sizeof(float));
         }
         // partials of GroupNorm statistics gathered by conv epilogues
@@ -328,10 +334,17 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
             fused(cur, shapes[i + 1], u.st * u.sh * u.sw);
         }
         if (l.op == VAE_OP_RES) {
+            // conv1 gathers the statistics of the block's second GroupNorm
             Shape xs = cur, ys = cur;
             xs.dtype = d.dtype;
             ys.dtype = res_mid_dtype(d, l.cin);
             fused(xs, ys, 1);
+        }
+        if ((l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) && next_gn) {
+            // conv2 gathers the statistics of the GroupNorm that reads the block's output
+            Shape xs = cur;
+            xs.dtype = d.dtype;
+            fused(xs, s, 1);
         }
         if (l.op == VAE_OP_D2S || l.op == VAE_OP_NEAREST) {
             ch *= l.sh;
@@ -343,6 +356,10 @@ void requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>&
         }
         cur = s;
     }
+    if (!exact)
+        return fail(VAE_ERR_INVALID_ARG, "patch bands do not fall on whole rows of every "
+                                         "activation (an encoder's bands must be whole folds)");
+    return VAE_OK;
 }
 
 struct Layout {
@@ -680,14 +697,14 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
         for (const vae_tile_t& t : *tiles)
             boxes.push_back(Box{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
                                 t.latent.w1});
-        requirements(d, Shape{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype}, boxes, false,
-                     &r);
+        VAE_TRY(requirements(d, Shape{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype}, boxes,
+                             false, &r));
     } else {
         for (const vae_tile_t& t : *tiles) {
             Shape in{desc.n, t.latent.t1 - t.latent.t0, t.latent.h1 - t.latent.h0,
                      t.latent.w1 - t.latent.w0, d.latent_c, d.dtype};
             std::vector<Box> one{Box{0, (int32_t)in.t, 0, (int32_t)in.h, 0, (int32_t)in.w}};
-            requirements(d, in, one, true, &r);
+            VAE_TRY(requirements(d, in, one, true, &r));
             r.crop = std::max(r.crop, in.bytes());
         }
     }
@@ -732,8 +749,11 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
         return fail(VAE_ERR_INVALID_ARG, "unknown plan dtype");
     if (spec->act_dtype != VAE_DTYPE_BF16 && spec->act_dtype != VAE_DTYPE_F32)
         return fail(VAE_ERR_INVALID_ARG, "unknown activation dtype");
-    if (spec->dtype == VAE_DTYPE_F32 && spec->act_dtype != VAE_DTYPE_F32)
-        return fail(VAE_ERR_UNSUPPORTED, "an fp32 plan keeps fp32 activations");
+    // bf16 activation storage rounds every op's output once more (about 40 extra roundings in
+    // the LTX-2-shaped plan) and misses the 2e-2 max-abs bar of a bf16 decode: refused.
+    if (spec->act_dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_UNSUPPORTED, "activations between ops are stored in fp32 "
+                                         "(act_dtype must be VAE_DTYPE_F32)");
     if (spec->flags & ~(VAE_DECODE_SPLIT_FP32_OPERANDS | VAE_DECODE_F16_OPERANDS))
         return fail(VAE_ERR_INVALID_ARG, "unknown decoder flags");
     if ((spec->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) && (spec->flags & VAE_DECODE_F16_OPERANDS))

@@ -64,9 +64,10 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", ope
     """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
 
     Each parameter dict is {"kind": "conv", "w", "b"} or {"kind": "gn", "gamma", "beta"} holding
-    host arrays. ``act_dtype`` is the storage dtype of the activations between ops ("f32" or
-    "bf16"). ``operands`` picks how convs that read an fp32 activation get their operands
-    (OPERAND_FLAGS; bf16 plans only). ``packed`` gives the MFMA convs fragment-packed weight
+    host arrays. ``act_dtype`` is the storage dtype of the activations between ops; the library
+    takes "f32" only (it refuses bf16 storage, which misses the bf16 decode's accuracy bound).
+    ``operands`` picks how convs that read an fp32 activation get their operands (OPERAND_FLAGS;
+    bf16 plans only). ``packed`` gives the MFMA convs fragment-packed weight
     copies. Returns the Decoder; it keeps the device tensors alive.
     """
     import torch
