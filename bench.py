@@ -116,8 +116,95 @@ def workload_name(kind, mode, tile_t=0, stride_t=0):
         return "ltx2_720p_encode_" + ("untiled" if mode == "patch" else "overlap_blend_2x3")
     prefix = {"ltx2": "ltx2_720p", "wan": "wan2.2_ti2v_5b_720p"}[kind]
     if mode == "patch":
-        return prefix + "_decode_patch_halo_1x4"
+        # the 1x4 patch-halo split with one launch per layer over all four patch boxes: on one
+        # GPU this computes the untiled decode's tensors
+        return prefix + "_decode_1x4_patch_halo_merged_launches"
+    if mode == "per_patch":
+        return prefix + "_decode_1x4_patch_halo_per_patch_launches"
     return prefix + "_decode_overlap_blend_2x3" + (f"_t{tile_t}s{stride_t}" if tile_t else "")
+
+
+LAUNCH_NOTE = {
+    "patch": "merged: one launch per layer covers the four patch boxes (halos read in place); "
+             "equals the untiled decode",
+    "per_patch": "per patch: every conv, GroupNorm pass and upsampling launched once per patch "
+                 "box, statistics merged across the boxes (four ranks' work, one after another)",
+    "overlap": "one overlap tile in flight",
+}
+
+
+def _band(length, parts, i):
+    """[start, end) of band i when `length` rows are cut into `parts` bands, the first
+    length % parts bands one row longer (the split vae_tile_split makes)."""
+    q, r = divmod(length, parts)
+    start = i * q + min(i, r)
+    return start, start + q + (1 if i < r else 0)
+
+
+def patch_summary(per_op, steps, patch, latent_box, out_px):
+    """Work of one patch of a per-patch decode: its own launches (records with tile == patch) and
+    the merges of GroupNorm statistics that every rank would also run (tile == -1)."""
+    own = [r for step in per_op for r in step if r["tile"] == patch]
+    shared = [r for step in per_op for r in step if r["tile"] == -1]
+    own_ms = sum(r["ms"] for r in own) / steps
+    shared_ms = sum(r["ms"] for r in shared) / steps
+    conv = [r for r in own if r["kind"] == "conv"]
+    conv_ms = sum(r["ms"] for r in conv) / steps
+    conv_flops = sum(r["flops"] for r in conv) / steps
+    tflops = conv_flops / (conv_ms / 1000.0) / 1e12
+    layers = {}
+    for r in conv:
+        L = layers.setdefault(r["layer"], {"ms": 0.0, "flops": 0.0, "n": 0})
+        L["ms"] += r["ms"]
+        L["flops"] += r["flops"]
+        L["n"] += 1
+    per_layer = []
+    for layer in sorted(layers):
+        L = layers[layer]
+        tf = L["flops"] / (L["ms"] / 1000.0) / 1e12
+        per_layer.append({"layer": layer, "launches_per_step": L["n"] // steps,
+                          "ms_per_step": round(L["ms"] / steps, 4), "tflops": round(tf, 1),
+                          "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    gn = [r for r in own if r["kind"] == "gn"]
+    gn_ms = sum(r["ms"] for r in gn) / steps
+    gn_bytes = sum(r["bytes"] for r in gn) / steps
+    total = own_ms + shared_ms
+    return {
+        "patch": patch, "latent_box": latent_box,
+        "ms_per_step": round(total, 3), "own_launches_ms": round(own_ms, 3),
+        "shared_stat_merges_ms": round(shared_ms, 3),
+        "value": round(out_px / (total / 1000.0) / 1e6, 3), "unit": "Mpx-frames/s",
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "conv3d_mfma_kernel (this patch's conv launches)",
+                     "conv_ms_per_step": round(conv_ms, 3),
+                     "conv_tflop_per_step": round(conv_flops / 1e12, 3)},
+        "gn": {"ms_per_step": round(gn_ms, 3),
+               "gbs": round(gn_bytes / (gn_ms / 1000.0) / 1e9, 1) if gn_ms else None},
+        "conv_layers": per_layer,
+    }
+
+
+def run_per_patch(v, dev, spec, params, operands, zd, desc, out, steps, warmup, patch):
+    """Times the per-patch decode and returns (per-step op records, wall ms per step)."""
+    import torch
+    dec = v.upload_decoder(spec, params, dev, operands=operands)
+    dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
+    ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        dec.vae_decode_tiled(zd, desc, out, ws)
+    torch.cuda.synchronize(dev)
+    dec.set_timing(True)
+    per_op = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dec.vae_decode_tiled(zd, desc, out, ws)
+        per_op.append(dec.timing())
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    dec.close()
+    del ws
+    return per_op, ms
 
 
 def conv_source_digest():
@@ -240,7 +327,10 @@ def standalone_passes(v, dev, reps=5):
 
 def cpu_baseline(spec, params, frames=2):
     """The oracle, as it stands, on a bounded sample: the full 720p spatial plan on `frames`
-    latent frames, scaled by conv flops to the full decode."""
+    latent frames (an encoder: the input frames that fold into that many latent frames). `value`
+    is the sample's own throughput, the video pixel-frames it produced (or consumed) per second:
+    measured, not extrapolated. Per output frame the sample does slightly more conv work than the
+    full decode (the first latent frame decodes to one frame), so the figure leans high."""
     import threadpoolctl
     import oracle
     import vae_synth
@@ -253,19 +343,21 @@ def cpu_baseline(spec, params, frames=2):
     out = oracle.decode(spec, z, params)
     sample_s = time.perf_counter() - t0
     n, c, t, h, w = spec["input"] if encoder else spec["latent"]
-    full_shape = (n, t, h, w, c)
-    scale = conv_flops(spec, full_shape) / conv_flops(spec, z.shape)
-    est_full_s = sample_s * scale
-    _, to, ho, wo, _ = full_shape if encoder else output_shape(spec, full_shape)
-    px = to * ho * wo
+    video = z.shape if encoder else out.shape
+    px = video[1] * video[2] * video[3]
+    full = (n, t, h, w, c)
+    work = conv_flops(spec, z.shape) / px
+    work_full = conv_flops(spec, full) / np.prod((output_shape(spec, full) if not encoder
+                                                  else full)[1:4])
     what = "encode of video" if encoder else "decode of latent"
     return {
-        "value": px / est_full_s / 1e6, "unit": "Mpx-frames/s", "cores": threads,
+        "value": px / sample_s / 1e6, "unit": "Mpx-frames/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle fp64 {what} [{n},{c},{take},{h},{w}] -> "
-                   f"{list(out.shape)} in {sample_s:.1f} s, scaled by conv flops x{scale:.1f} to "
-                   f"the {t}-frame 720p {'encode' if encoder else 'decode'} "
-                   f"(est. {est_full_s:.0f} s); os.cpu_count()={os.cpu_count()}"),
+        "sample": (f"oracle fp64 {what} [{n},{c},{take},{h},{w}] -> {list(out.shape)} "
+                   f"({px / 1e6:.2f} M px-frames) in {sample_s:.1f} s; value = sample "
+                   f"px-frames / sample time, not extrapolated (conv work per px-frame "
+                   f"{work / work_full:.2f}x the full {t}-frame 720p "
+                   f"{'encode' if encoder else 'decode'}'s); os.cpu_count()={os.cpu_count()}"),
     }
 
 
@@ -274,7 +366,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--mode", choices=["patch", "overlap"], default="patch")
+    ap.add_argument("--mode", choices=["patch", "per_patch", "overlap"], default="patch",
+                    help="patch: 1x4 patch-halo, one launch per layer; per_patch: the same split "
+                         "launched patch by patch; overlap: 2x3 overlap-blend tiles")
+    ap.add_argument("--no-quarter", action="store_true",
+                    help="skip the per-patch run that measures the interior quarter patch")
+    ap.add_argument("--quarter-steps", type=int, default=5)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="ltx2",
                     help="ltx2: the LTX-2-shaped decode (the headline); wan: the Wan2.2-shaped one")
     ap.add_argument("--operands", choices=["f16", "split", "bf16"], default="f16",
@@ -323,10 +420,15 @@ def main():
     params = vae_synth.decoder_params(spec)
     dev = torch.device("cuda:0")
     dec = v.upload_decoder(spec, params, dev, operands=args.operands)
+    if args.mode == "per_patch":
+        dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
     zp = v.pad_latent(z, spec)            # zero channels up to a multiple of 32 (48 -> 64)
     zd = torch.as_tensor(zp).to(device=dev, dtype=torch.bfloat16)
     workload = workload_name(args.workload, args.mode, args.tile_t, args.stride_t)
-    if args.mode == "patch":
+    if args.mode in ("patch", "per_patch"):
+        if encoder and args.mode == "per_patch":
+            print("--workload ltx2_enc runs untiled or overlap-tiled", file=sys.stderr)
+            sys.exit(2)
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, spec.get("scale", (1, 1, 1)),
                              patches=patch_grid)
     else:
@@ -407,6 +509,29 @@ def main():
     for name, p in (passes or {}).items():
         log(f"  pass {name}: {json.dumps(p)}")
 
+    # The interior quarter patch (patch 1 of the 1x4 split: latent columns [10, 20)) at its real
+    # shape: the launches one rank of the split runs, timed inside a per-patch decode.
+    quarter = None
+    if args.workload in ("ltx2", "wan") and args.mode in ("patch", "per_patch") and \
+            not args.no_quarter:
+        if args.mode == "per_patch":
+            q_ops, q_steps = per_op, args.steps
+        else:
+            log("[bench] per-patch decode for the quarter-patch figures ...")
+            q_ops, q_ms = run_per_patch(v, dev, spec, params, args.operands, zd, desc, out,
+                                        args.quarter_steps, 1, 1)
+            q_steps = args.quarter_steps
+            log(f"[bench] per-patch decode: {q_ms:.2f} ms/step")
+        lw = zp.shape[3]
+        b0, b1 = _band(lw, 4, 1)
+        out_px = out_shape[1] * out_shape[2] * (b1 - b0) * (out_shape[3] // lw)
+        quarter = patch_summary(q_ops, q_steps, 1,
+                                {"t": [0, zp.shape[1]], "h": [0, zp.shape[2]], "w": [b0, b1]},
+                                out_px)
+        if args.mode == "patch":
+            quarter["per_patch_decode_ms_per_step"] = round(q_ms, 3)
+        log(f"[bench] quarter patch: {json.dumps(quarter)}")
+
     baseline = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on its bounded sample ...")
@@ -425,10 +550,12 @@ def main():
                    ("input" if encoder else "latent"): list(spec["input" if encoder else "latent"]),
                    "output": [out_shape[0], out_shape[4]] + list(out_shape[1:4]),
                    "parallelism": "none (1 GPU)",
+                   "launch": LAUNCH_NOTE[args.mode],
                    "operands": OPERANDS[args.operands],
                    "activations": activations_note(args.operands),
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},
-        "roofline": roofline, "kernels": summary, "standalone_passes": passes, "timing": timing,
+        "roofline": roofline, "quarter_patch": quarter, "kernels": summary,
+        "standalone_passes": passes, "timing": timing,
         "attention_tflop_per_step": (round(kinds["attn"]["flops"] / args.steps / 1e12, 3)
                                      if "attn" in kinds else None),
         "cpu_baseline": baseline,

@@ -503,6 +503,24 @@ VAE_API vae_status_t vae_decoder_packed_weight_size(const vae_decoder_t* dec, si
 VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, size_t bytes,
                                               vae_stream_t stream);
 
+/* How a patch-halo decode (mode A with more than one patch) launches its work on one GPU.
+ *  VAE_LAUNCH_MERGED (the default): one launch per layer covers every patch box at once; each
+ *    patch's halo is its neighbour's data read in place, and a GroupNorm's statistics come from
+ *    the blocks of that one launch. The fastest way to run the whole decode on one device.
+ *  VAE_LAUNCH_PER_PATCH: every conv, GroupNorm pass and upsampling is launched once per patch
+ *    box, over that box only (its out_box), reading its halo in place: the work of one rank of a
+ *    patch split (P4, commits on PatchConv3d, Patchify and PatchGroupNorm). A GroupNorm's
+ *    statistics are formed per patch box as (count, mean, M2) and merged across the boxes with
+ *    Chan's update in patch order before any box is normalised. The per-position RMS norm, the
+ *    whole-frame attention and the space-to-depth fold stay one launch each. With timing on,
+ *    each launch is recorded with its patch index in vae_op_timing_t.tile (-1: the merge of the
+ *    statistics, shared by all patches).
+ * Both give the untiled decode up to the rounding order of the statistics. The workspace size
+ * depends on the setting: query it after setting it. Mode B ignores it.
+ * Returns VAE_ERR_INVALID_ARG for another value. */
+enum { VAE_LAUNCH_MERGED = 0, VAE_LAUNCH_PER_PATCH = 1 };
+VAE_API vae_status_t vae_decoder_set_launch(vae_decoder_t* dec, int32_t launch);
+
 /* Device scratch needed by vae_decode_tiled for this tiling (latent extents come from desc). */
 VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,
                                                const vae_tiling_desc_t* desc, size_t* bytes);
@@ -510,9 +528,11 @@ VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,
 /*
  * Decodes `latent` ([N,T,H,W,latent_channels], the plan's dtype) into `out` (fp32, NDHWC).
  * mode A (patch-halo):
- *  - convs, upsampling and the final placement run over the whole activation, and each patch's
- *    halo is its neighbour's data read in place;
- *  - GroupNorm statistics are formed per patch and merged across patches.
+ *  - convs, upsampling and the final placement cover the patch boxes, and each patch's halo is
+ *    its neighbour's data read in place; launched per layer or per patch box
+ *    (vae_decoder_set_launch);
+ *  - GroupNorm statistics are those of the whole tensor (the global mean and the biased
+ *    variance), merged across patches per box with the per-patch launches.
  *  The result equals the untiled decode.
  * mode B (overlap-blend):
  *  - each tile is decoded alone, one tile in flight, with its own borders and statistics;
@@ -533,7 +553,7 @@ enum { VAE_KIND_CONV = 1, VAE_KIND_GN = 2, VAE_KIND_UPSAMPLE = 3, VAE_KIND_MERGE
 typedef struct vae_op_timing {
     int32_t kind;       /* VAE_KIND_* */
     int32_t layer;      /* index in the plan */
-    int32_t tile;       /* tile index (mode B) or -1 */
+    int32_t tile;       /* tile index (mode B), patch index (per-patch launches) or -1 */
     int32_t reserved;
     double ms;          /* GPU time between the events around the op */
     double flops;       /* algorithmic flops (convs: 2 * 27 * Cin * Cout * positions) */

@@ -189,6 +189,17 @@ def test_workspace_query_needs_no_gpu(v):
     with pytest.raises(v.VaeError):               # scales that do not match the plan
         dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
                                          (8, 16, 32), patches=(1, 4)))
+    # per-patch launches keep every patch box's GroupNorm slots and moments: never smaller
+    dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
+    c = dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 16, 22, 40, 128),
+                                         (8, 32, 32), patches=(1, 4)))
+    assert c >= a
+    # the overlap-blend mode decodes one tile at a time and ignores the setting
+    assert dec.workspace_size(v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, (1, 16, 22, 40, 128),
+                                            (8, 32, 32), tile=(16, 16), stride=(14, 14))) == b
+    with pytest.raises(v.VaeError) as e:
+        dec.set_launch(2)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
     dec.close()
 
 

@@ -70,14 +70,19 @@ def oracle_out(name, mode, affine=None, tt=(0, 0)):
 
 
 def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32", operands="f16",
-               tt=(0, 0)):
+               tt=(0, 0), launch="merged", timing=None):
     """Decode through vae_decode_tiled. ``operands``: how convs reading an fp32 activation get
     their operands, "f16" (the default), "split" (bf16 hi + lo) or "bf16". ``tt``: temporal tile
-    and stride of an overlap-blend decode (0: T whole)."""
+    and stride of an overlap-blend decode (0: T whole). ``launch``: "merged" (one launch per
+    layer) or "per_patch" (every conv, GroupNorm pass and upsampling once per patch box).
+    ``timing``: a list that receives the per-op records of the last decode."""
     import torch
     spec = spec_of(name)
     z = ndhwc(vae_synth.latent(spec))
     dec = v.upload_decoder(spec, params_of(name, affine), act_dtype=act, operands=operands)
+    dec.set_launch(v.VAE_LAUNCH_PER_PATCH if launch == "per_patch" else v.VAE_LAUNCH_MERGED)
+    if timing is not None:
+        dec.set_timing(True)
     zd = dev(z, spec["dtype"])
     if mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
@@ -93,6 +98,8 @@ def gpu_decode(v, name, mode, patches=(1, 1), affine=None, repeat=1, act="f32", 
         dec.vae_decode_tiled(zd, desc, out, ws)
         outs.append(out)
     torch.cuda.synchronize()
+    if timing is not None:
+        timing.extend(dec.timing())
     dec.close()
     return outs if repeat > 1 else outs[0]
 
@@ -277,3 +284,89 @@ def test_packed_and_standard_weights_decode_identically(v, operands):
         outs.append(out)
         dec.close()
     assert torch.equal(outs[0], outs[1])
+
+
+# ------------------------------------------------------------------------------------------------
+# Per-patch launches: every conv, GroupNorm pass and upsampling once per patch box, over that box
+# only, with the GroupNorm statistics merged across the boxes (one rank's share of a patch split).
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("patches", [(1, 2), (2, 1), (2, 2)])
+def test_conv_gn_workload_per_patch(v, patches):
+    got = host(gpu_decode(v, "conv_gn_32", "patch", patches, 4, launch="per_patch"))
+    assert rel_max_abs(got, oracle_out("conv_gn_32", "whole", 4)) <= 1e-4
+
+
+@pytest.mark.parametrize("patches", [(2, 2), (1, 3), (3, 1)])
+def test_tiny_decoder_per_patch(v, patches):
+    """fp32: the per-patch decode equals the oracle's whole decode (rel 1e-4) and the merged
+    launches up to the rounding order of the statistics."""
+    got = host(gpu_decode(v, "tiny_decoder", "patch", patches, affine=3, launch="per_patch"))
+    assert rel_max_abs(got, oracle_out("tiny_decoder", "whole", 3)) <= 1e-4
+    merged = host(gpu_decode(v, "tiny_decoder", "patch", patches, affine=3))
+    assert rel_max_abs(got, merged) <= 1e-5
+
+
+@pytest.mark.parametrize("operands", ["f16", "split"])
+@pytest.mark.parametrize("name,patches", [("ltx2_small", (1, 2)), ("ltx2_mid", (2, 3)),
+                                          ("ltx2_tiny", (1, 2)), ("ltx2_tiny_n2", (1, 2))])
+def test_ltx2_shaped_per_patch(v, name, patches, operands):
+    got = host(gpu_decode(v, name, "patch", patches, operands=operands, launch="per_patch"))
+    _bf16_bar(got, oracle_out(name, "whole"))
+
+
+@pytest.mark.parametrize("operands", ["f16", "split"])
+def test_ltx2_720p_one_frame_per_patch_every_value(v, operands):
+    """The full-width 720p plan on one latent frame, each conv and GroupNorm launched per width
+    quarter (10 latent columns and their halo, scaled at every stage): every output value."""
+    got = host(gpu_decode(v, "ltx2_720p_1f", "patch", (1, 4), operands=operands,
+                          launch="per_patch"))
+    _bf16_bar(got, oracle_out("ltx2_720p_1f", "whole"))
+
+
+def test_ltx2_720p_per_patch_against_golden(v):
+    """The full 720p decode in four width quarters launched one by one, at the pixels the oracle's
+    fp64 decode stored (seams of the quarters included)."""
+    g = _golden("whole")
+    _check_golden(g, gpu_decode(v, "ltx2_720p", "patch", (1, 4), launch="per_patch"))
+
+
+@pytest.mark.parametrize("name,patches", [("mixed_rms_gn", (1, 2)), ("wan_tiny", (2, 2))])
+def test_rms_plans_per_patch(v, name, patches):
+    """Plans with RMS norms and the frame attention (one launch each) around per-patch convs, and
+    a GroupNorm fed by an RMS block's second conv, per patch."""
+    import torch
+    spec = vae_synth.WORKLOADS[name]
+    z = v.pad_latent(ndhwc(vae_synth.latent(spec)), spec)
+    p = vae_synth.decoder_params(spec, affine_seed=5)
+    dec = v.upload_decoder(spec, p)
+    dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
+    ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out = torch.full(oracle.output_shape(spec, ndhwc(vae_synth.latent(spec)).shape),
+                     float("nan"), device="cuda", dtype=torch.float32)
+    dec.vae_decode_tiled(dev(z, "bf16"), desc, out, ws)
+    torch.cuda.synchronize()
+    dec.close()
+    _bf16_bar(host(out), oracle.decode(spec, ndhwc(vae_synth.latent(spec)), p))
+
+
+def test_per_patch_decode_is_deterministic(v):
+    import torch
+    a, b = gpu_decode(v, "ltx2_small", "patch", (1, 2), repeat=2, launch="per_patch")
+    assert torch.equal(a, b)
+
+
+def test_per_patch_timing_records(v):
+    """Each per-patch launch is recorded with its patch index; the patches' conv work adds up to
+    the whole decode's, and the statistics merges are recorded as shared work (-1)."""
+    recs, merged = [], []
+    gpu_decode(v, "ltx2_tiny", "patch", (1, 2), launch="per_patch", timing=recs)
+    gpu_decode(v, "ltx2_tiny", "patch", (1, 2), timing=merged)
+    conv = [r for r in recs if r["kind"] == "conv"]
+    assert {r["tile"] for r in conv} == {0, 1}
+    assert any(r["tile"] == -1 and r["kind"] == "gn" for r in recs)
+    whole = sum(r["flops"] for r in merged if r["kind"] == "conv")
+    assert abs(sum(r["flops"] for r in conv) - whole) <= 1e-9 * whole
+    per = [sum(r["flops"] for r in conv if r["tile"] == t) for t in (0, 1)]
+    assert per[0] == per[1]                        # two equal bands of 3 latent columns

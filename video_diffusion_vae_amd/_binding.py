@@ -15,6 +15,7 @@ VAE_OK, VAE_ERR_INVALID_ARG, VAE_ERR_UNSUPPORTED, VAE_ERR_HIP, VAE_ERR_WORKSPACE
 VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DTYPE_F16 = 1, 2, 3
 VAE_UPSAMPLE_NEAREST, VAE_UPSAMPLE_D2S = 1, 2
 VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
+VAE_LAUNCH_MERGED, VAE_LAUNCH_PER_PATCH = 0, 1
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
 VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
 VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
@@ -32,7 +33,8 @@ EXPORTS = (
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_rmsnorm_silu",
     "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample", "vae_space_to_depth",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
-    "vae_decode_workspace_size", "vae_decode_tiled", "vae_decoder_set_timing",
+    "vae_decoder_set_launch", "vae_decode_workspace_size", "vae_decode_tiled",
+    "vae_decoder_set_timing",
     "vae_decoder_get_timing",
 )
 
@@ -138,6 +140,7 @@ def _load():
         "vae_decoder_create": ([ctypes.POINTER(vae_decoder_spec_t), ctypes.POINTER(P), I32,
                                 ctypes.POINTER(P)], I32),
         "vae_decoder_destroy": ([P], None),
+        "vae_decoder_set_launch": ([P, I32], I32),
         "vae_decode_workspace_size": ([P, D, ctypes.POINTER(SZ)], I32),
         "vae_decode_tiled": ([P, T, D, T, P, SZ, P], I32),
         "vae_decoder_set_timing": ([P, I32], I32),
@@ -500,6 +503,11 @@ class Decoder:
         self._packed = torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
         _check(LIB.vae_decoder_pack_weights(self._h, _ptr(self._packed), self._packed.numel(),
                                             _stream(stream)))
+
+    def set_launch(self, launch):
+        """VAE_LAUNCH_MERGED or VAE_LAUNCH_PER_PATCH (patch-halo decodes); query the workspace
+        size afterwards."""
+        _check(LIB.vae_decoder_set_launch(self._h, int(launch)))
 
     def workspace_size(self, desc):
         n = ctypes.c_size_t()

@@ -118,9 +118,11 @@ struct MfmaArgs {
     int32_t yT, yH, yW, zc, st, sh, sw;
     int32_t res_f32;         // the residual is fp32 while y is bf16 or fp16 (a hand-off)
     // Optional GroupNorm partials of y as stored: fp64 (count, mean, M2) per (sample, group of
-    // y's channels, slot), slot = (sub-position * position blocks + block) * WM + wave row.
+    // y's channels, slot), slot = slot0 + (sub-position * position blocks + block) * WM + wave
+    // row, in rows of nslots slots per (sample, group). slot0 > 0 and nslots above this launch's
+    // own count let several launches (one per patch box) fill one array.
     double* stats;
-    int32_t groups, nslots;
+    int32_t groups, nslots, slot0;
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -430,7 +432,7 @@ __device__ __forceinline__ void conv_epilogue(const MfmaArgs& a, const f32x16_t 
             const int g = cz / cpg;
             const int nblk = a.nbt * a.nbh * a.nbw;
             const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
-            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
+            const int64_t slot = a.slot0 + ((int64_t)sub * nblk + mb_local) * WM + wave_m;
             double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
             o[0] = sn;
             o[1] = mean;
@@ -571,7 +573,7 @@ __device__ __forceinline__ void conv_epilogue_direct(const MfmaArgs& a, const f3
             const int g = cz / cpg;
             const int nblk = a.nbt * a.nbh * a.nbw;
             const int mb_local = (bt_i * a.nbh + bh_i) * a.nbw + bw_i;
-            const int64_t slot = ((int64_t)sub * nblk + mb_local) * WM + wave_m;
+            const int64_t slot = a.slot0 + ((int64_t)sub * nblk + mb_local) * WM + wave_m;
             double* o = a.stats + (((int64_t)n * a.groups + g) * a.nslots + slot) * 3;
             o[0] = sn;
             o[1] = mean;
@@ -988,7 +990,12 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.n_mblocks = (int32_t)mblocks;
     a.stats = fz ? fz->gn_ws : nullptr;
     a.groups = fz && fz->gn_ws ? fz->groups : 1;
-    a.nslots = (a.cout / a.zc) * a.nbt * a.nbh * a.nbw * wave_rows<NT>();
+    const int64_t own = (int64_t)(a.cout / a.zc) * a.nbt * a.nbh * a.nbw * wave_rows<NT>();
+    const int64_t stride = fz && fz->slot_stride ? fz->slot_stride : own;
+    if (a.stats && (fz->slot0 < 0 || fz->slot0 + own > stride || stride > INT32_MAX))
+        return fail(VAE_ERR_INVALID_ARG, "conv3d: GroupNorm slot range outside its row");
+    a.nslots = (int32_t)stride;
+    a.slot0 = fz ? (int32_t)fz->slot0 : 0;
     hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
                        dim3((unsigned)total), dim3(kMfmaThreads), 0, stream, a);
     VAE_HIP_CHECK(hipGetLastError());

@@ -1,11 +1,16 @@
 // Decode executor: a layer plan over caller-owned device weights and workspace.
 //
-// Mode A (patch-halo). On one GPU all patches share one activation tensor per layer:
-//  - a conv launch covers every patch box at once, and each patch's halo is simply its
-//    neighbour's data in that tensor;
-//  - GroupNorm statistics are still formed per patch box and merged across patches with Chan's
-//    update ("Add tiled VAE parallelism & extended model support", PatchGroupNorm commit message);
-//  - the final unpatchify places every patch's pixels disjointly, straight into `out`.
+// Mode A (patch-halo). On one GPU all patches share one activation tensor per layer, and each
+// patch's halo is simply its neighbour's data in that tensor. Two ways to launch it:
+//  - merged (VAE_LAUNCH_MERGED, the default): one launch per layer covers every patch box at once;
+//    a GroupNorm's statistics come from that launch's blocks, which is the whole-tensor result;
+//  - per patch (VAE_LAUNCH_PER_PATCH): every conv, GroupNorm pass and upsampling is launched once
+//    per patch box, over that box only, as one rank of a patch split runs it. A GroupNorm's
+//    statistics are formed per patch box (count, mean, M2) and merged across the patches with
+//    Chan's update before any patch is normalised ("Add tiled VAE parallelism & extended model
+//    support", PatchConv3d and PatchGroupNorm commit messages). Ops that need no box (the
+//    per-position RMS norm, the whole-frame attention, the space-to-depth fold) stay one launch.
+// Either way the final unpatchify places every patch's pixels disjointly, straight into `out`.
 // Mode B (overlap-blend). The serial tiled decode of "[TRTLLM-14029][feat] LTX-2 tile-parallel VAE
 // decode" (Description): one tile in flight. Each tile's latent box is cropped, decoded with its own
 // borders and statistics, and blended into `out`, which is normalised after the last tile.
@@ -19,6 +24,7 @@
 
 struct vae_decoder {
     int32_t dtype = 0, act_dtype = 0, flags = 0, latent_c = 0, groups = 0;
+    int32_t launch = VAE_LAUNCH_MERGED;   // patch-halo launches: merged or one per patch box
     float eps = 0.0f;
     std::vector<vae_layer_desc_t> layers;
     std::vector<const void*> ptrs;
@@ -282,6 +288,7 @@ bool plan_folds(const vae_decoder& d, int32_t* ft = nullptr, int32_t* fh = nullp
 struct Req {
     int64_t act = 0;      // bytes of the largest activation kept in a rotating buffer
     int64_t gn = 0;       // GroupNorm stats workspace
+    int64_t parts = 0;    // per-patch GroupNorm moments (per-patch launches)
     int64_t mr = 0;       // mean/rstd
     int64_t crop = 0;     // latent crop (mode B)
     int64_t tile = 0;     // one decoded tile, fp32 pixels (mode B)
@@ -292,6 +299,7 @@ struct Req {
 vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>& boxes,
                           bool final_in_buffer, Req* r) {
     bool exact = true;   // every patch box scales to whole rows and columns of each activation
+    const bool per_patch = d.launch == VAE_LAUNCH_PER_PATCH && boxes.size() > 1;
     std::vector<Shape> shapes;
     walk(d, in, &shapes, nullptr, nullptr, nullptr);
     Shape cur = in;
@@ -315,16 +323,33 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
             g.dtype = l.op == VAE_OP_RES ? d.dtype : gn_silu_dtype(d, (int)i);
             r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
             vae_tensor_t x = tensor_of(nullptr, cur);
-            r->gn = std::max<int64_t>(
-                r->gn, (int64_t)gn_stats_workspace(
-                           x, scaled_boxes(boxes, cur.t, ch, cw, fh, fw, &exact), d.groups));
+            const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw, &exact);
+            r->gn = std::max<int64_t>(r->gn, (int64_t)gn_stats_workspace(x, bl, d.groups));
+            if (per_patch)
+                for (int b = 0; b < bl.n; ++b) {
+                    BoxList one;
+                    one.n = 1;
+                    one.b[0] = bl.b[b];
+                    r->gn = std::max<int64_t>(r->gn, (int64_t)gn_stats_workspace(x, one, d.groups));
+                }
+            r->parts = std::max<int64_t>(r->parts, (int64_t)bl.n * cur.n * d.groups * 3 *
+                                                       (int64_t)sizeof(double));
             r->mr = std::max<int64_t>(r->mr, cur.n * d.groups * 2 * (int64_t)sizeof(float));
         }
-        // partials of GroupNorm statistics gathered by conv epilogues
+        // partials of GroupNorm statistics gathered by conv epilogues: over the whole grid, or
+        // per patch box in rows holding every box's slots
         const bool next_gn = gn_follows(d, i);
         auto fused = [&](const Shape& xs, const Shape& ys, int32_t k) {
             const vae_tensor_t x = tensor_of(nullptr, xs);
-            const int64_t slots = conv_gn_slots(x, ys.c, d.dtype, whole_box(x), d.groups, k);
+            int64_t slots = 0;
+            if (per_patch) {
+                // xs is the conv's input grid; the boxes scale with it (nearest folds included)
+                const BoxList bl = scaled_boxes(boxes, xs.t, ch, cw, fh, fw, &exact);
+                for (int b = 0; b < bl.n; ++b)
+                    slots += conv_gn_slots(x, ys.c, d.dtype, bl.b[b], d.groups, k);
+            } else {
+                slots = conv_gn_slots(x, ys.c, d.dtype, whole_box(x), d.groups, k);
+            }
             r->gn = std::max<int64_t>(r->gn, ys.n * d.groups * slots * 3 * (int64_t)sizeof(double));
         };
         if (l.op == VAE_OP_CONV && next_gn) fused(cur, s, 1);
@@ -363,7 +388,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
 }
 
 struct Layout {
-    size_t buf[3], gn, mr, crop, tile, attn, total;
+    size_t buf[3], gn, parts, mr, crop, tile, attn, total;
     int64_t act_bytes;
 };
 
@@ -377,6 +402,8 @@ Layout layout_of(const Req& r) {
     }
     L.gn = off;
     off += align_up((size_t)r.gn, 256);
+    L.parts = off;
+    off += align_up((size_t)r.parts, 256);
     L.mr = off;
     off += align_up((size_t)r.mr, 256);
     L.crop = off;
@@ -412,10 +439,23 @@ struct Runner {
     }
 
     bool stats_ready = false;  // mean/rstd already hold the statistics of the next GN's input
+    bool per_patch = false;    // launch every conv, GroupNorm pass and upsampling per patch box
+
+    // Records an op of patch `patch` (-1: work shared by all patches, such as a merge of
+    // statistics) in the timing.
+    vae_status_t mark_patch(int32_t patch, int32_t kind, int32_t layer, double flops,
+                            double bytes) {
+        const int32_t keep = tile;
+        if (per_patch) tile = patch;
+        const vae_status_t st = mark(kind, layer, flops, bytes);
+        tile = keep;
+        return st;
+    }
 
     vae_status_t gn(const vae_tensor_t& x, const vae_tensor_t& y, const BoxList& bl,
                     const void* gamma, const void* beta, int layer) {
         double* stats = reinterpret_cast<double*>(ws + L.gn);
+        double* parts = reinterpret_cast<double*>(ws + L.parts);
         float* mr = reinterpret_cast<float*>(ws + L.mr);
         for (int i = 0; i < bl.n; ++i) {
             const Box& b = bl.b[i];
@@ -424,14 +464,38 @@ struct Runner {
                 return fail(VAE_ERR_INVALID_ARG, "GroupNorm patch box outside the activation");
         }
         const bool fused = stats_ready;
-        if (!fused) VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
         stats_ready = false;
-        // the patch boxes partition the tensor, so one apply launch covers them all
-        VAE_TRY(launch_gn_apply(x, whole_box(x), d->groups, mr, static_cast<const float*>(gamma),
-                                static_cast<const float*>(beta), true, y, s));
-        const double xb = (double)numel(x) * elem_size(x.dtype);
-        const double yb = (double)numel(y) * elem_size(y.dtype);
-        return mark(VAE_KIND_GN, layer, 0.0, (fused ? 1.0 : 2.0) * xb + yb);
+        const double xe = (double)elem_size(x.dtype) * x.n * x.c;   // bytes per position
+        const double ye = (double)elem_size(y.dtype) * y.n * y.c;
+        if (!per_patch) {
+            if (!fused) VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
+            // the patch boxes partition the tensor, so one apply launch covers them all
+            VAE_TRY(launch_gn_apply(x, whole_box(x), d->groups, mr,
+                                    static_cast<const float*>(gamma),
+                                    static_cast<const float*>(beta), true, y, s));
+            const double pos = (double)(x.t * x.h * x.w);
+            return mark(VAE_KIND_GN, layer, 0.0, pos * ((fused ? 1.0 : 2.0) * xe + ye));
+        }
+        if (!fused) {
+            // per-box (count, mean, M2), then one fixed-order Chan merge across the boxes
+            for (int i = 0; i < bl.n; ++i) {
+                BoxList one;
+                one.n = 1;
+                one.b[0] = bl.b[i];
+                VAE_TRY(launch_gn_stats(x, one, d->groups, stats,
+                                        parts + (int64_t)i * x.n * d->groups * 3, nullptr, d->eps,
+                                        s));
+                VAE_TRY(mark_patch(i, VAE_KIND_GN, layer, 0.0, (double)bl.b[i].volume() * xe));
+            }
+            VAE_TRY(launch_gn_combine(parts, bl.n, (int32_t)x.n, d->groups, d->eps, mr, s));
+            VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
+        }
+        for (int i = 0; i < bl.n; ++i) {
+            VAE_TRY(launch_gn_apply(x, bl.b[i], d->groups, mr, static_cast<const float*>(gamma),
+                                    static_cast<const float*>(beta), true, y, s));
+            VAE_TRY(mark_patch(i, VAE_KIND_GN, layer, 0.0, (double)bl.b[i].volume() * (xe + ye)));
+        }
+        return VAE_OK;
     }
 
     vae_status_t rms(const vae_tensor_t& x, const vae_tensor_t& y, const void* gamma,
@@ -446,8 +510,10 @@ struct Runner {
     // epilogue also gathers the statistics of the GroupNorm that reads y. `up` (a D2S layer or
     // null) makes y the depth-to-space of the conv output, written by the conv's epilogue.
     // `lsh`, `lsw`: a nearest upsampling of x (log2 factors) that the conv reads while staging.
+    // `bl`: the patch boxes in the conv's input grid; with per-patch launches the conv runs once
+    // per box, and the statistics of all boxes land in one array that is merged once.
     vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
-                      const vae_tensor_t& y, int layer, bool gn_next,
+                      const vae_tensor_t& y, int layer, bool gn_next, const BoxList& bl,
                       const vae_layer_desc_t* up = nullptr, int32_t lsh = 0, int32_t lsw = 0) {
         int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
                          ? VAE_CONV_SPLIT_FP32
@@ -463,23 +529,68 @@ struct Runner {
         vae_tensor_t xl = x;                       // the conv's input grid
         xl.h <<= lsh;
         xl.w <<= lsw;
-        const Box box = whole_box(xl);
-        const int64_t slots =
-            gn_next ? conv_gn_slots(x, y.c, d->dtype, box, d->groups, k) : 0;
+        BoxList launches;                          // one launch per entry
+        if (per_patch) {
+            launches = bl;
+        } else {
+            launches.n = 1;
+            launches.b[0] = whole_box(xl);
+        }
+        int64_t slots[kMaxBoxes], total = 0;
+        for (int i = 0; i < launches.n; ++i) {
+            const Box& b = launches.b[i];
+            if (b.t0 < 0 || b.h0 < 0 || b.w0 < 0 || b.t1 > xl.t || b.h1 > xl.h || b.w1 > xl.w ||
+                b.volume() <= 0)
+                return fail(VAE_ERR_INVALID_ARG, "conv patch box outside the activation");
+            slots[i] = gn_next ? conv_gn_slots(x, y.c, d->dtype, b, d->groups, k) : 0;
+            total += slots[i];
+        }
         double* part = reinterpret_cast<double*>(ws + L.gn);
-        const ConvFuse fz{slots > 0 ? part : nullptr, d->groups, up ? up->st : 1,
-                          up ? up->sh : 1, up ? up->sw : 1, lsh, lsw};
-        VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res, y,
-                              box, cf, s, &fz));
-        const double flops = 2.0 * 27.0 * (double)x.c * (double)cout * (double)positions(xl);
-        const double bytes = (double)numel(x) * elem_size(x.dtype) +
-                             (double)numel(y) * elem_size(y.dtype) * (res ? 2.0 : 1.0);
-        VAE_TRY(mark(VAE_KIND_CONV, layer, flops, bytes));
-        if (slots > 0) {
-            // merged into mean/rstd here; the time counts towards the GroupNorm that follows
-            VAE_TRY(launch_gn_finalize_slots(part, slots, (int32_t)y.n, d->groups, d->eps,
+        const double in_pos = (double)elem_size(x.dtype) * x.c * x.n;     // bytes per position
+        const double out_pos = (double)elem_size(y.dtype) * y.c * k * y.n * (res ? 2.0 : 1.0);
+        int64_t slot0 = 0;
+        for (int i = 0; i < launches.n; ++i) {
+            const Box& b = launches.b[i];
+            ConvFuse fz{total > 0 ? part : nullptr, d->groups, up ? up->st : 1, up ? up->sh : 1,
+                        up ? up->sw : 1, lsh, lsw};
+            fz.slot0 = slot0;
+            fz.slot_stride = total;
+            slot0 += slots[i];
+            VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res,
+                                  y, b, cf, s, &fz));
+            const double pos = (double)b.volume() * x.n;
+            const double flops = 2.0 * 27.0 * (double)x.c * (double)cout * pos;
+            // input read once (at its own resolution), output (and residual) once
+            const double bytes = pos / x.n / (double)(1 << (lsh + lsw)) * in_pos +
+                                 (double)b.volume() * out_pos;
+            VAE_TRY(mark_patch(i, VAE_KIND_CONV, layer, flops, bytes));
+        }
+        if (total > 0) {
+            // merged into mean/rstd here (all patches, in a fixed order); timed as shared work
+            VAE_TRY(launch_gn_finalize_slots(part, total, (int32_t)y.n, d->groups, d->eps,
                                              reinterpret_cast<float*>(ws + L.mr), s));
+            if (per_patch) VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
             stats_ready = true;
+        }
+        return VAE_OK;
+    }
+
+    // A standalone depth-to-space or nearest upsampling: over the whole tensor, or per patch box
+    // (boxes in x's grid).
+    vae_status_t upsample(const vae_tensor_t& x, const BoxList& bl, int mode, int32_t st,
+                          int32_t sh, int32_t sw, const vae_tensor_t& y, int layer) {
+        const double e = (double)elem_size(x.dtype) * x.c * x.n;
+        const double k = (double)sh * sw * (mode == VAE_UPSAMPLE_D2S ? 1.0 / (sh * sw) : 1.0);
+        if (!per_patch) {
+            VAE_TRY(launch_upsample(x, whole_box(x), mode, st, sh, sw, y, s));
+            return mark(VAE_KIND_UPSAMPLE, layer, 0.0,
+                        (double)numel(x) * elem_size(x.dtype) +
+                            (double)numel(y) * elem_size(y.dtype));
+        }
+        for (int i = 0; i < bl.n; ++i) {
+            VAE_TRY(launch_upsample(x, bl.b[i], mode, st, sh, sw, y, s));
+            VAE_TRY(mark_patch(i, VAE_KIND_UPSAMPLE, layer, 0.0,
+                               (double)bl.b[i].volume() * e * (1.0 + k)));
         }
         return VAE_OK;
     }
@@ -515,7 +626,9 @@ struct Runner {
                 const bool out_last = lo + 1 == d->layers.size();
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = out_last ? final_out : buf(nb, shapes[lo]);
-                VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, lo),
+                // ch, cw already hold a folded nearest upsampling: boxes in the conv's grid
+                const BoxList cb = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
+                VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, lo), cb,
                              fuse_up ? &d->layers[li + 1] : nullptr, near_lsh, near_lsw));
                 near_lsh = near_lsw = 0;
                 p += 2;
@@ -536,17 +649,18 @@ struct Runner {
                 as.dtype = res_mid_dtype(*d, l.cin);
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
-                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, true));
+                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, true, bl));
                 VAE_TRY(gn(t2, t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
                 Shape ys = as;
                 ys.dtype = res_out_dtype(*d, li);   // conv1's output in b2 is dead by now
                 vae_tensor_t y = last ? final_out : buf(b2, ys);
-                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li)));
+                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li), bl));
                 p += 8;
                 cur = y;
                 cur_buf = last ? -2 : b2;
             } else if (l.op == VAE_OP_RES_RMS) {
                 // x -> RMS1 -> t1 -> conv1 -> t2 -> RMS2 -> t1 -> conv2 (+ x) -> t2
+                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
                 const int b1 = free_buf(cur_buf, -1);
                 const int b2 = free_buf(cur_buf, b1);
                 Shape gs = shape_of(cur), as = shape_of(cur);
@@ -555,12 +669,12 @@ struct Runner {
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
                 stats_ready = false;
                 VAE_TRY(rms(cur, t1, d->ptrs[p], d->ptrs[p + 1], layer));
-                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, false));
+                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, false, bl));
                 VAE_TRY(rms(t2, t1, d->ptrs[p + 4], d->ptrs[p + 5], layer));
                 Shape ys = as;
                 ys.dtype = res_out_dtype(*d, li);
                 vae_tensor_t y = last ? final_out : buf(b2, ys);
-                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li)));
+                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li), bl));
                 p += 8;
                 cur = y;
                 cur_buf = last ? -2 : b2;
@@ -644,10 +758,8 @@ struct Runner {
                 vae_tensor_t y = last ? final_out : buf(nb, os);
                 const int mode = l.op == VAE_OP_D2S ? VAE_UPSAMPLE_D2S : VAE_UPSAMPLE_NEAREST;
                 const int st = l.op == VAE_OP_D2S ? l.st : 1;
-                VAE_TRY(launch_upsample(cur, whole_box(cur), mode, st, l.sh, l.sw, y, s));
-                VAE_TRY(mark(VAE_KIND_UPSAMPLE, layer, 0.0,
-                             (double)numel(cur) * elem_size(cur.dtype) +
-                                 (double)numel(y) * elem_size(y.dtype)));
+                VAE_TRY(upsample(cur, scaled_boxes(boxes, cur.t, ch, cw, fh, fw), mode, st, l.sh,
+                                 l.sw, y, layer));
                 ch *= l.sh;
                 cw *= l.sw;
                 cur = y;
@@ -962,6 +1074,7 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tens
         for (const vae_tile_t& t : tiles)
             boxes.push_back(Box{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
                                 t.latent.w1});
+        r.per_patch = dec->launch == VAE_LAUNCH_PER_PATCH && boxes.size() > 1;
         VAE_TRY(r.run(*latent, boxes, *out));
     } else {
         AxisTiling ax[3];
@@ -991,6 +1104,15 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tens
             VAE_TRY(r.mark(VAE_KIND_MERGE, -1, 0, mb));
         }
     }
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decoder_set_launch(vae_decoder_t* dec, int32_t launch) {
+    clear_error();
+    if (!dec) return fail(VAE_ERR_INVALID_ARG, "decoder is NULL");
+    if (launch != VAE_LAUNCH_MERGED && launch != VAE_LAUNCH_PER_PATCH)
+        return fail(VAE_ERR_INVALID_ARG, "launch must be VAE_LAUNCH_MERGED or VAE_LAUNCH_PER_PATCH");
+    dec->launch = launch;
     return VAE_OK;
 }
 

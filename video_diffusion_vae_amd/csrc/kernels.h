@@ -24,11 +24,15 @@ struct BoxList {
 //  - a nearest upsampling of the input by (1 << lsh, 1 << lsw), read while the input tile is
 //    staged: x is then the tensor before that upsampling, and every extent and box refers to the
 //    upsampled grid.
+// The partials of one launch fill slots [slot0, slot0 + conv_gn_slots(box)) of rows that are
+// slot_stride slots long (0: the launch's own count), so that the launches of several patch
+// boxes can share one array and be merged together.
 struct ConvFuse {
     double* gn_ws;
     int32_t groups;
     int32_t st, sh, sw;
     int32_t lsh = 0, lsw = 0;
+    int64_t slot0 = 0, slot_stride = 0;
 };
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
