@@ -127,7 +127,8 @@ VAE_API int32_t vae_version(void);
  * is exact. Every other case runs on a direct fp32-accumulating path, where the split flag changes
  * nothing.
  */
-enum { VAE_CONV_SPLIT_FP32 = 1, VAE_CONV_PACKED_WEIGHTS = 2, VAE_CONV_PACKED_F16_WEIGHTS = 4 };
+enum { VAE_CONV_SPLIT_FP32 = 1, VAE_CONV_PACKED_WEIGHTS = 2, VAE_CONV_PACKED_F16_WEIGHTS = 4,
+       VAE_CONV_SPLIT_K = 8 };
 VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight,
                                        int32_t weight_dtype, const float* bias,
                                        const vae_tensor_t* residual, vae_tensor_t* y,
@@ -169,7 +170,16 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
  * Arguments:
  *  residual: as for vae_conv3d_causal (y's shape; y's dtype, or fp32), or NULL.
  *  ws / ws_bytes: device scratch of vae_conv3d_causal_fused_workspace() bytes, 16-byte aligned,
- *  owned by the caller (unused without statistics). Its contents are undefined afterwards.
+ *  owned by the caller (unused without statistics or a split over K). Its contents are
+ *  undefined afterwards.
+ *
+ * VAE_CONV_SPLIT_K (this call only; flags of vae_conv3d_causal must not hold it): when the MFMA
+ * launch over out_box would fill fewer than the chip's 256 compute units (a small box, such as
+ * one patch of the first decoder stages), the conv splits its K dimension (the input-channel
+ * chunks) up to 4 ways. One launch stores each split's fp32 partial sums in ws, after the
+ * statistics partials; a second adds them in split order and runs the epilogue. The result is
+ * deterministic and differs from the unsplit conv only in the order of the fp32 additions. The
+ * workspace query includes those bytes when the flag is given.
  *
  * Errors: those of vae_conv3d_causal; INVALID_ARG when y's shape does not match the factors;
  * UNSUPPORTED for a depth-to-space or an input upsampling off the MFMA path, for an input
@@ -181,7 +191,7 @@ typedef struct vae_conv_fused {
     const vae_tensor_t* x;
     const void* weight;             /* [Cout][3][3][3][Cin], device */
     int32_t weight_dtype;
-    int32_t flags;                  /* as for vae_conv3d_causal */
+    int32_t flags;                  /* as for vae_conv3d_causal, plus VAE_CONV_SPLIT_K */
     const float* bias;              /* [Cout] fp32, device, or NULL */
     const vae_tensor_t* residual;
     vae_tensor_t* y;

@@ -86,6 +86,132 @@ def test_conv3d_mfma_matches_oracle(v, case):
         assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
 
 
+# Boxes 10, 12 or 20 positions wide, deep in T (one width quarter of the first decoder stages):
+# the extents make the launch pick a narrow block shape, which stages through one tile buffer
+# and stores through the LDS epilogue. (N, T, H, W), Cin, Cout, in, out, residual, box; the
+# comment names the block shape the extents select.
+NARROW_CASES = [
+    ((1, 16, 22, 10), 64, 128, "bf16", "f32", True, None),              # 16 x 8 x 2
+    ((1, 16, 12, 12), 64, 128, "bf16", "bf16", False, None),            # 16 x 4 x 4
+    ((1, 4, 16, 12), 64, 128, "bf16", "f32", True, None),               # 4 x 16 x 4
+    ((2, 16, 9, 10), 32, 64, "bf16", "bf16", True, None),               # 16 x 8 x 2, N = 2
+    ((1, 17, 13, 30), 64, 128, "bf16", "f32", True, (1, 17, 2, 13, 10, 20)),   # 16 x 8 x 2 box
+    ((1, 16, 12, 12), 64, 48, "f32", "f32", False, None),               # 16 x 4 x 4, Cout 48
+]
+
+
+@pytest.mark.parametrize("case", NARROW_CASES)
+def test_conv3d_narrow_blocks(v, case):
+    """The narrow block shapes against the oracle, with standard and packed weights (which must
+    agree bit for bit); nothing outside the box is written."""
+    import torch
+    (n, t, h, w), cin, cout, idt, odt, use_res, bx = case
+    x, wt, b, r = _conv_inputs((n, t, h, w), cin, cout, "bf16", 40 + NARROW_CASES.index(case))
+    if idt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [15, cin], scale=1e-3))
+        ref = oracle.causal_conv3d(vae_synth.round_bf16(x), wt, b)
+    else:
+        ref = oracle.causal_conv3d(x, wt, b)
+    if use_res:
+        ref = ref + r
+    xd = dev(x, idt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, odt) if use_res else None
+    tdt = torch.float32 if odt == "f32" else torch.bfloat16
+    y = torch.full((n, t, h, w, cout), 7.0, device="cuda", dtype=tdt)
+    v.vae_conv3d_causal(xd, wd, bd, rd, y, bx)
+    yp = torch.full_like(y, 7.0)
+    v.vae_conv3d_causal(xd, v.vae_conv_weight_pack(wd).view(torch.bfloat16), bd, rd, yp, bx,
+                        v.VAE_CONV_PACKED_WEIGHTS)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+    got = host(y)
+    bx = bx or (0, t, 0, h, 0, w)
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    mask = np.zeros(got.shape, bool)
+    mask[sl] = True
+    assert np.all(got[~mask] == 7.0), "conv wrote outside its box"
+    g, rf = got[sl], ref[sl]
+    if odt == "f32":
+        assert rel_max_abs(g, rf) <= 1e-4
+    else:
+        assert np.all(np.abs(g - rf) <= bf16_round_bound(rf) + 1e-4 * np.abs(rf).max())
+
+
+# Split over K (VAE_CONV_SPLIT_K): launches too small to fill the chip. (N, T, H, W), Cin,
+# C (after the depth-to-space), d2s factors, in, out, GroupNorm groups (0: none), residual
+SPLIT_K_CASES = [
+    ((1, 16, 22, 10), 256, 256, (1, 1, 1), "bf16", "f32", 32, True),    # S0-quarter-like, 4 splits
+    ((1, 16, 22, 10), 128, 64, (2, 2, 2), "f16", "f16", 0, False),      # up-conv-like, d2s
+    ((1, 4, 6, 10), 128, 32, (2, 2, 2), "bf16", "f32", 8, False),       # d2s + statistics
+    ((1, 3, 9, 17), 256, 48, (1, 1, 1), "f32", "f32", 0, True),         # fp32 in, Cout 48
+    ((2, 16, 9, 10), 128, 128, (1, 1, 1), "bf16", "bf16", 32, False),   # N = 2, 2 splits
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_K_CASES)
+def test_conv3d_split_k(v, case):
+    """A conv split over its input-channel chunks (one launch of partial sums, one that adds them
+    in split order and runs the epilogue): matches the oracle like the unsplit conv, differs
+    from it only by fp32 summation order, gathers the same statistics, and is deterministic."""
+    import torch
+    (n, t, h, w), cin, c, (st, sh, sw), idt, odt, groups, use_res = case
+    cout = c * st * sh * sw
+    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 70 + SPLIT_K_CASES.index(case))
+    if idt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [18, cin], scale=1e-3))
+        xin = vae_synth.round_bf16(x).astype(np.float64)
+    elif idt == "f16":
+        x = round_f16(x + ndhwc(vae_synth.normal((n, cin, t, h, w), [18, cin], scale=1e-3)))
+        xin = x
+    else:
+        xin = x
+    yshape = (n, st * t - (st - 1), sh * h, sw * w, c)
+    r = ndhwc(vae_synth.normal((yshape[0], c) + yshape[1:4], [19, cin], dtype="bf16")) \
+        if use_res else None
+    ref = oracle.depth_to_space(oracle.causal_conv3d(xin, wt, b), st, sh, sw)
+    if use_res:
+        ref = ref + r
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[odt]
+    xd = dev(x, idt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    flags = 0
+    if idt == "f16":
+        wd = v.vae_conv_weight_pack_f16(wd).view(torch.bfloat16)
+        flags = v.VAE_CONV_PACKED_F16_WEIGHTS
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, odt) if use_res else None
+    outs, stats = [], []
+    for fl in (flags | v.VAE_CONV_SPLIT_K, flags | v.VAE_CONV_SPLIT_K, flags):
+        y = torch.full(yshape, 7.0, device="cuda", dtype=tdt)
+        mr = torch.zeros((n, max(groups, 1), 2), dtype=torch.float32, device="cuda")
+        v.vae_conv3d_causal_fused(xd, wd, bd, rd, y, None, fl, d2s=(st, sh, sw),
+                                  gn_groups=groups, gn_eps=1e-6, gn_mean_rstd=mr)
+        outs.append(y)
+        stats.append(mr)
+    torch.cuda.synchronize()
+    # the split needs scratch beyond the statistics: the query grows with the flag
+    assert v.vae_conv3d_causal_fused_workspace(xd, wd, outs[0], None, (st, sh, sw), groups,
+                                               flags=flags) < \
+        v.vae_conv3d_causal_fused_workspace(xd, wd, outs[0], None, (st, sh, sw), groups,
+                                            flags=flags | v.VAE_CONV_SPLIT_K)
+    assert torch.equal(outs[0], outs[1]), "split conv is not deterministic"
+    got, unsplit = host(outs[0]), host(outs[2])
+    if odt == "f32":
+        assert rel_max_abs(got, ref) <= 1e-4
+        assert rel_max_abs(got, unsplit) <= 1e-5
+    else:
+        bound = bf16_round_bound(ref) if odt == "bf16" else f16_round_bound(ref)
+        assert np.all(np.abs(got - ref) <= bound + 1e-4 * np.abs(ref).max())
+        assert np.all(np.abs(got - unsplit) <= 2 * bound + 1e-5 * np.abs(ref).max())
+    if groups:
+        cnt, mean, m2 = oracle.group_moments(got, groups)      # of y as stored
+        gm = stats[0].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(gm[..., 0], mean, rtol=0, atol=1e-5 * np.sqrt(m2 / cnt).max())
+        np.testing.assert_allclose(gm[..., 1], 1 / np.sqrt(m2 / cnt + 1e-6), rtol=1e-5)
+
+
 CONV_GN_CASES = [
     # (N, T, H, W), Cin, Cout, groups, in dtype, out dtype, residual, box
     ((1, 3, 9, 17), 32, 128, 32, "bf16", "f32", False, None),            # 4 channels per group

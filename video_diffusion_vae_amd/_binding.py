@@ -18,6 +18,7 @@ VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
 VAE_LAUNCH_MERGED, VAE_LAUNCH_PER_PATCH = 0, 1
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
 VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
+VAE_CONV_SPLIT_K = 8
 VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
 VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN, VAE_OP_S2D = 6, 7, 8, 9
@@ -268,9 +269,9 @@ def _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn
 
 
 def vae_conv3d_causal_fused_workspace(x, weight, y, out_box=None, d2s=(0, 0, 0), gn_groups=0,
-                                      in_up=(0, 0)):
-    a, keep = _fused_args(x, weight, None, None, y, out_box, 0, d2s, gn_groups, 0.0, None, None,
-                          in_up)
+                                      in_up=(0, 0), flags=0):
+    a, keep = _fused_args(x, weight, None, None, y, out_box, flags, d2s, gn_groups, 0.0, None,
+                          None, in_up)
     n = ctypes.c_size_t(0)
     _check(LIB.vae_conv3d_causal_fused_workspace(ctypes.byref(a), ctypes.byref(n)))
     return n.value
@@ -282,9 +283,9 @@ def vae_conv3d_causal_fused(x, weight, bias, residual, y, out_box=None, flags=0,
     """Causal Conv3d of the nearest upsampling of x by in_up = (sh, sw), with a fused
     depth-to-space (d2s = (st, sh, sw), y is then the upsampled tensor) and/or the statistics of a
     GroupNorm over y (gn_mean_rstd [N, gn_groups, 2] fp32)."""
-    if ws is None and gn_groups:
-        ws = _workspace(vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups,
-                                                          in_up), x.device)
+    if ws is None:
+        n = vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups, in_up, flags)
+        ws = _workspace(n, x.device) if n else None
     a, keep = _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
                           gn_mean_rstd, ws, in_up)
     _check(LIB.vae_conv3d_causal_fused(ctypes.byref(a), _stream(stream)))

@@ -326,7 +326,7 @@ vae_status_t check_conv_dtypes(const vae_tensor_t& x, const vae_tensor_t& y,
                                const vae_tensor_t* residual, int64_t cout, int32_t weight_dtype,
                                int32_t flags) {
     const int32_t packs = VAE_CONV_PACKED_WEIGHTS | VAE_CONV_PACKED_F16_WEIGHTS;
-    if (flags & ~(VAE_CONV_SPLIT_FP32 | packs))
+    if (flags & ~(VAE_CONV_SPLIT_FP32 | packs | VAE_CONV_SPLIT_K))
         return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
     if ((flags & packs) == packs)
         return fail(VAE_ERR_INVALID_ARG, "give one packed-weight flag");
@@ -366,6 +366,9 @@ vae_status_t check_conv(const vae_tensor_t* x, const void* weight, int32_t weigh
     if (residual) VAE_TRY(check_residual(residual, *x, *y));
     if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
     VAE_TRY(check_box(out_box, *y, "out_box"));
+    if (flags & VAE_CONV_SPLIT_K)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "VAE_CONV_SPLIT_K needs a workspace: use vae_conv3d_causal_fused");
     VAE_TRY(check_conv_dtypes(*x, *y, residual, y->c, weight_dtype, flags));
     return VAE_OK;
 }
@@ -443,16 +446,34 @@ vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
     return VAE_OK;
 }
 
-// Workspace of the fused call: the epilogue's partials, or the separate statistics pass's.
-size_t fused_workspace(const vae_conv_fused_t* a, const FusedPlan& p, int64_t* slots) {
+// Workspace of the fused call: the epilogue's partials, or the separate statistics pass's; then,
+// 256-byte aligned at `split_off`, the partial sums of a split over K (`splits` > 1).
+size_t fused_workspace(const vae_conv_fused_t* a, const FusedPlan& p, int64_t* slots,
+                       int32_t* splits, size_t* split_off) {
     *slots = 0;
-    if (!a->gn_groups) return 0;
-    *slots = conv_gn_slots(*a->x, a->y->c, a->weight_dtype, p.cbox, a->gn_groups, p.k);
-    if (*slots > 0) return (size_t)(a->y->n * a->gn_groups * *slots * 3) * sizeof(double);
-    BoxList bl;
-    bl.n = 1;
-    bl.b[0] = p.ybox;
-    return gn_stats_workspace(*a->y, bl, a->gn_groups);
+    size_t gn = 0;
+    if (a->gn_groups) {
+        *slots = conv_gn_slots(*a->x, a->y->c, a->weight_dtype, p.cbox, a->gn_groups, p.k);
+        if (*slots > 0) {
+            gn = (size_t)(a->y->n * a->gn_groups * *slots * 3) * sizeof(double);
+        } else {
+            BoxList bl;
+            bl.n = 1;
+            bl.b[0] = p.ybox;
+            gn = gn_stats_workspace(*a->y, bl, a->gn_groups);
+        }
+    }
+    vae_tensor_t xl = *a->x;                 // the conv's input grid
+    xl.h <<= p.lsh;
+    xl.w <<= p.lsw;
+    const int64_t cout = a->y->c * p.k;
+    *splits = (a->flags & VAE_CONV_SPLIT_K)
+                  ? conv_split_count(xl, cout, a->weight_dtype, p.cbox,
+                                     (a->flags & VAE_CONV_SPLIT_FP32) != 0)
+                  : 1;
+    *split_off = align_up(gn, 256);
+    const size_t sb = conv_split_bytes(xl, cout, p.cbox, *splits);
+    return sb ? *split_off + sb : gn;
 }
 
 vae_status_t check_attention(const vae_tensor_t* x) {
@@ -499,7 +520,9 @@ VAE_API vae_status_t vae_conv3d_causal_fused_workspace(const vae_conv_fused_t* a
     FusedPlan p;
     VAE_TRY(check_fused(args, &p, false));
     int64_t slots = 0;
-    *bytes = fused_workspace(args, p, &slots);
+    int32_t splits = 1;
+    size_t split_off = 0;
+    *bytes = fused_workspace(args, p, &slots, &splits, &split_off);
     return VAE_OK;
 }
 
@@ -511,20 +534,26 @@ VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_s
     const vae_tensor_t& x = *a.x;
     const vae_tensor_t& y = *a.y;
     int64_t slots = 0;
-    const size_t need = fused_workspace(args, p, &slots);
-    if (a.gn_groups) {
+    int32_t splits = 1;
+    size_t split_off = 0;
+    const size_t need = fused_workspace(args, p, &slots, &splits, &split_off);
+    if (a.gn_groups || splits > 1) {
         if (!a.ws || a.ws_bytes < need)
             return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)a.ws_bytes, -1,
                         (int64_t)need);
         if (reinterpret_cast<uintptr_t>(a.ws) % 16 != 0)
             return fail(VAE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-        if (p.cbox.volume() == 0 || p.ybox.volume() == 0 || x.n == 0)
-            return fail(VAE_ERR_INVALID_ARG, "statistics of an empty box");
     }
+    if (a.gn_groups && (p.cbox.volume() == 0 || p.ybox.volume() == 0 || x.n == 0))
+        return fail(VAE_ERR_INVALID_ARG, "statistics of an empty box");
     hipStream_t s = as_stream(stream);
     double* part = static_cast<double*>(a.ws);
     ConvFuse fz{slots > 0 ? part : nullptr, a.gn_groups ? a.gn_groups : 1, p.st, p.sh, p.sw,
                 p.lsh, p.lsw};
+    if (splits > 1) {
+        fz.part = reinterpret_cast<float*>(static_cast<uint8_t*>(a.ws) + split_off);
+        fz.splits = splits;
+    }
     VAE_TRY(launch_conv3d(x, a.weight, a.weight_dtype, a.bias, a.residual, y, p.cbox, a.flags, s,
                           &fz));
     if (!a.gn_groups) return VAE_OK;

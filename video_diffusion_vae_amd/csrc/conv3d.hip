@@ -3,6 +3,8 @@
 //  - bf16 weights with Cin % 32 == 0 and Cout % 4 == 0 run on the matrix cores (conv3d_mfma.h);
 //    fp16 inputs only run there.
 //  - Otherwise a direct kernel computes one output per thread with fp32 accumulation.
+#include <algorithm>
+
 #include "conv3d_mfma.h"
 
 namespace vae {
@@ -71,9 +73,10 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
     Elem<TO>::store(y + o, acc);
 }
 
-// Output-block shapes (T x H x W = 256 positions). The launch picks the one that wastes the
-// fewest MFMA rows on ragged block edges for the box: 16x22x40 takes 4x8x8 (9% waste instead of
-// 31%), 31x44x80 takes 4x4x16, and the larger stages take 2x8x16.
+// Output-block shapes (T x H x W = 256 positions; pick_block in conv3d_mfma.h). The launch picks
+// the one that wastes the fewest MFMA rows on ragged block edges for the box: 16x22x40 takes
+// 4x8x8 (9% waste instead of 31%), 31x44x80 takes 4x4x16, the larger stages take 2x8x16, and one
+// width quarter of the first stages (10 or 20 columns) takes a narrow shape.
 template <int NT>
 vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
@@ -159,14 +162,29 @@ int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, c
     if (k > 1 && yc % 32) return 0;      // a wave's 32 channels share one sub-position
     const int64_t cpg = yc / groups;
     if (cpg % 4 || 32 % cpg) return 0;   // a lane's four channels, a wave's 32, hold whole groups
-    int tb = 2, hb = 8, wb = 16;
-    switch (pick_block(box)) {
-        case kBlk4x8x8: tb = 4; hb = 8; wb = 8; break;
-        case kBlk4x4x16: tb = 4; hb = 4; wb = 16; break;
-        default: break;
-    }
+    const BlockDims& d = kBlockDims[pick_block(box)];
     const int wm = cout >= 128 ? wave_rows<128>() : cout > 32 ? wave_rows<64>() : wave_rows<32>();
-    return k * ceil_div(box.bt(), tb) * ceil_div(box.bh(), hb) * ceil_div(box.bw(), wb) * wm;
+    return k * ceil_div(box.bt(), d.tb) * ceil_div(box.bh(), d.hb) * ceil_div(box.bw(), d.wb) * wm;
+}
+
+// A launch of fewer than 256 workgroups leaves CUs idle (256 CUs, two workgroups each when
+// busy). Splitting K s ways multiplies the workgroups by s: s is the largest count (up to 4) that
+// keeps the launch within one round of 512 workgroups, with at least two channel chunks per split.
+int32_t conv_split_count(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype, const Box& box,
+                         bool split_fp32) {
+    if (!conv_uses_mfma_c(x, cout, weight_dtype) || box.volume() == 0 || x.n == 0) return 1;
+    const int64_t wgs = conv_workgroups(x.n, cout, box);
+    const int64_t chunks = x.c / ((split_fp32 && x.dtype == VAE_DTYPE_F32) ? 16 : kCK);
+    if (wgs >= 256) return 1;
+    int64_t s = std::min<int64_t>({512 / wgs, chunks / 2, 4});
+    return s >= 2 ? (int32_t)s : 1;
+}
+
+size_t conv_split_bytes(const vae_tensor_t& x, int64_t cout, const Box& box, int32_t splits) {
+    if (splits <= 1) return 0;
+    // one fp32 accumulator per (position of a 256-position block, channel of the tile)
+    return (size_t)splits * (size_t)conv_workgroups(x.n, cout, box) * 256 *
+           (size_t)conv_nt(cout) * sizeof(float);
 }
 
 int64_t packed_weight_elems(int64_t cout, int64_t cin) {
@@ -210,13 +228,18 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
     if (fz && fz->gn_ws && conv_gn_slots(x, y.c, weight_dtype, box, fz->groups, k) == 0)
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: fused GroupNorm statistics need the MFMA path "
                                          "and 4, 8, 16 or 32 channels per group");
+    if (fz && fz->part && fz->splits > 1 && !conv_uses_mfma_c(x, cout, weight_dtype))
+        return fail(VAE_ERR_UNSUPPORTED, "conv3d: a split over K needs the MFMA path");
     if (conv_uses_mfma_c(x, cout, weight_dtype)) {
         // output-channel tile: 128 wide, or 64 / 32 for narrow outputs (conv_out's 48 or 12)
-        if (cout >= 128)
-            return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, fz, stream);
-        if (cout > 32)
-            return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, fz, stream);
-        return run_mfma_in<32>(x, w, bias, residual, y, box, split, packed, fz, stream);
+        switch (conv_nt(cout)) {
+            case 128:
+                return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, fz, stream);
+            case 64:
+                return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, fz, stream);
+            default:
+                return run_mfma_in<32>(x, w, bias, residual, y, box, split, packed, fz, stream);
+        }
     }
     if (packed) return fail(VAE_ERR_UNSUPPORTED, "packed weights need the MFMA path");
     if (weight_dtype == VAE_DTYPE_F32)

@@ -123,6 +123,14 @@ struct MfmaArgs {
     // own count let several launches (one per patch box) fill one array.
     double* stats;
     int32_t groups, nslots, slot0;
+    // Split over K. With splits > 1 the grid holds `splits` copies of the (channel tile, block)
+    // grid, split s taking the input-channel chunks [s * chunks / splits, (s + 1) * chunks /
+    // splits); each workgroup stores its raw fp32 accumulators to `part` and stops. Then
+    // conv3d_reduce_kernel, with `reduce` = that array, adds the splits' accumulators in split
+    // order and runs the epilogue. Layout: [split][tile][wave][MFMA tile][lane][16].
+    int32_t splits;
+    float* part;
+    const float* reduce;
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -286,14 +294,18 @@ __device__ __forceinline__ void to_operand(const Raw8<TI>& r, bool in, uint4& hi
 //  - 16 positions of one row plus 16 of the next (WB = 16), or
 //  - 8 positions of each of four rows (WB = 8).
 // Measured with the LDS bank-conflict counter on gfx950, such reads are conflict-free only when
-// the row pitch is 0 mod 256 bytes (WB = 16) or 128 mod 256 bytes (WB = 8). The pitch is 1536 or
-// 896 bytes.
+// the row pitch is 0 mod 256 bytes (WB = 16) or 128 mod 256 bytes (WB = 8): the 16-byte reads of
+// 8 consecutive lanes must land in 8 distinct 16-byte groups of a 256-byte line. The pitch is
+// 1536 or 896 bytes. The same rule gives the narrow blocks theirs: 8 lanes read 4 positions of
+// 2 rows (WB = 4; columns land in groups 0, 5, 10, 15, so the next row must shift them by 8:
+// pitch 128 mod 256, 640 bytes) or 2 positions of 4 rows (WB = 2; groups 0, 5, shifted by 4 per
+// row: pitch 64 mod 256, 320 bytes).
 template <int TB, int HB, int WB>
 struct BlockShape {
     static_assert(TB * HB * WB == 256, "a block is 256 output positions");
     static constexpr int HT = TB + 2, HH = HB + 2, HW = WB + 2;
     static constexpr int kPos = HT * HH * HW;       // input positions staged per chunk
-    static constexpr int kPitch = WB == 16 ? 1536 : 896;
+    static constexpr int kPitch = WB == 16 ? 1536 : WB == 8 ? 896 : WB == 4 ? 640 : 320;
     static_assert(HW * kRow <= kPitch, "a row must fit its pitch");
     static constexpr int kBytes = HT * HH * kPitch;
 };
@@ -592,8 +604,10 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     constexpr int RP = S::kPitch;
     // With packed weights and bf16 (or split) operands the tile is staged through a ring of frame
     // slots (see below); otherwise through one tile buffer. The ring's extra registers fit two
-    // waves per SIMD in those cases.
-    constexpr bool ROLL = PACKED && (sizeof(TI) == 2 || SPLIT);
+    // waves per SIMD in those cases. Its schedule is written for blocks of 2 or 4 frames, and on
+    // a narrow block (4 x 16 x 4) it needs more than half the registers of a SIMD: the narrow
+    // blocks stage through the tile buffer.
+    constexpr bool ROLL = PACKED && (sizeof(TI) == 2 || SPLIT) && TB <= 4 && WB >= 8;
     constexpr int NSP = TB == 2 ? 1 : 2;           // spare frame slots of the ring
     constexpr int NS = S::HT + NSP;                // frame slots of the ring
     constexpr int FB = HH * RP;                    // bytes of one frame slot
@@ -609,9 +623,15 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     constexpr int NB = PD + 1;
     static_assert(WNN * WM == kMfmaWaves && MI >= 1, "wave grid");
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = logical / a.n_mblocks;
-    int mb = logical - nt * a.n_mblocks;
+    // Uniform block indices, kept in scalar registers (readfirstlane): the vector registers are
+    // all taken by the accumulators, fragments and staging.
+    const int logical = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    // a split launch holds `splits` copies of the (channel tile, block) grid, split slowest
+    const int per_split = (int)gridDim.x / a.splits;
+    const int split = __builtin_amdgcn_readfirstlane(logical / per_split);
+    const int tile = __builtin_amdgcn_readfirstlane(logical - split * per_split);
+    const int nt = __builtin_amdgcn_readfirstlane(tile / a.n_mblocks);
+    int mb = tile - nt * a.n_mblocks;
     const int bw_i = mb % a.nbw;
     mb /= a.nbw;
     const int bh_i = mb % a.nbh;
@@ -684,6 +704,10 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     constexpr int CK = SPLIT ? 16 : kCK;       // input channels per staged chunk
     constexpr int UPP = SPLIT ? 2 : 4;         // staging units per position (8 channels each)
     const int n_chunks = a.cin / CK;
+    // this workgroup's chunks [kc0, kc1): all of them, or its split's share
+    const int kc0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * n_chunks / a.splits));
+    const int kc1 =
+        __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * n_chunks / a.splits));
     if constexpr (ROLL) {
         // Ring staging. The tile's HT = TB + 2 frames live in HT of NS = HT + NSP LDS frame
         // slots: frame f of chunk c is slot (b_c + f) mod NS, and b moves back by NSP slots per
@@ -758,16 +782,16 @@ void conv3d_mfma_kernel(MfmaArgs a) {
         int b = 0;
 #pragma unroll
         for (int f = 0; f < NIN; ++f) {
-            frame_load(f, 0, 0);
+            frame_load(f, kc0 * CK, 0);
             frame_write(f, 0);
         }
 #pragma unroll
         for (int h = 0; h < NHOLD; ++h) {
-            frame_load(NIN + h, 0, h);
+            frame_load(NIN + h, kc0 * CK, h);
             frame_write(NIN + h, h);
         }
 #pragma unroll
-        for (int t = 0; t < PD; ++t) load_b(t, t, 0);
+        for (int t = 0; t < PD; ++t) load_b(t, t, kc0 * CK);
         __syncthreads();
 
         // step schedule: in-chunk frame k is loaded at LDK[k] and written at WRK[k] into slot
@@ -849,10 +873,10 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             __syncthreads();   // chunk done: its later frames are free, the next chunk is staged
             b = (b + NS - NSP) % NS;
         };
-        for (int kc = 0; kc + 1 < n_chunks; ++kc) chunk(kc, std::true_type{});
-        chunk(n_chunks - 1, std::false_type{});
+        for (int kc = kc0; kc + 1 < kc1; ++kc) chunk(kc, std::true_type{});
+        chunk(kc1 - 1, std::false_type{});
     } else {
-        for (int kc = 0; kc < n_chunks; ++kc) {
+        for (int kc = kc0; kc < kc1; ++kc) {
             const int c0 = kc * CK;
     #pragma unroll
             for (int t = 0; t < PD; ++t) load_b(t, t, c0);   // in flight while the tile is staged
@@ -915,16 +939,34 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             }
         }
     }
+    if (a.part) {
+        // one split of a split conv: store the raw sums for the reduce launch
+        float* dst = a.part + (((int64_t)split * per_split + tile) * kMfmaWaves + wave) * MI * 1024 +
+                     lane * 16;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            float4* q = reinterpret_cast<float4*>(dst + i * 1024);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                q[k] = make_float4(acc[i][4 * k], acc[i][4 * k + 1], acc[i][4 * k + 2],
+                                   acc[i][4 * k + 3]);
+        }
+        return;
+    }
     if constexpr (F16) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][r] *= kF16WeightUnscale;
     }
-    if (a.zc % 32 == 0 && a.cout % 32 == 0) {
-        conv_epilogue_direct<TO, TB, HB, WB, MI, MW, WM>(a, acc, n, t_blk, h_blk, w_blk, bt_i, bh_i,
-                                                     bw_i, co_tile, lane, wave_m);
-        return;
+    // The narrow blocks (WB < 8) always take the staged epilogue: the direct one's register rows
+    // follow the 8- and 16-wide patterns, and with them it would not fit beside the staging.
+    if constexpr (WB >= 8) {
+        if (a.zc % 32 == 0 && a.cout % 32 == 0) {
+            conv_epilogue_direct<TO, TB, HB, WB, MI, MW, WM>(a, acc, n, t_blk, h_blk, w_blk, bt_i,
+                                                             bh_i, bw_i, co_tile, lane, wave_m);
+            return;
+        }
     }
     __syncthreads();  // the input tile is reused for the epilogue
 
@@ -935,24 +977,123 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                                           wave_m);
 }
 
-enum BlockKind { kBlk2x8x16 = 0, kBlk4x8x8 = 1, kBlk4x4x16 = 2 };
+// The second launch of a conv split over K: one workgroup per (channel tile, block) pair, with
+// the wave roles of conv3d_mfma_kernel. It adds the splits' accumulators in split order, then
+// runs the same epilogue. A kernel of its own, so that the main kernel's registers stay as they
+// are.
+template <int NT, typename TI, typename TO, int TB, int HB, int WB>
+__global__ __launch_bounds__(kMfmaThreads, 2)
+void conv3d_reduce_kernel(MfmaArgs a) {
+    constexpr bool F16 = std::is_same<TI, _Float16>::value;
+    constexpr int WNN = NT / 32;
+    constexpr int WM = kMfmaWaves / WNN;
+    constexpr int MW = 256 / WM;
+    constexpr int MI = MW / 32;
+    __shared__ __attribute__((aligned(16))) float ep[kMfmaWaves * 32 * kEp];
+    const int tile = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+    const int nt = __builtin_amdgcn_readfirstlane(tile / a.n_mblocks);
+    int mb = tile - nt * a.n_mblocks;
+    const int bw_i = mb % a.nbw;
+    mb /= a.nbw;
+    const int bh_i = mb % a.nbh;
+    mb /= a.nbh;
+    const int bt_i = mb % a.nbt;
+    const int n = mb / a.nbt;
+    const int t_blk = a.box.t0 + bt_i * TB;
+    const int h_blk = a.box.h0 + bh_i * HB;
+    const int w_blk = a.box.w0 + bw_i * WB;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_m = wave / WNN;
+    const int co_tile = nt * NT + (wave % WNN) * 32;
+    f32x16_t acc[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+    const int64_t per_split = gridDim.x;
+    for (int sp = 0; sp < a.splits; ++sp) {
+        const float* src =
+            a.reduce + (((int64_t)sp * per_split + tile) * kMfmaWaves + wave) * MI * 1024 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const float4* q = reinterpret_cast<const float4*>(src + i * 1024);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 v = q[k];
+                acc[i][4 * k] += v.x;
+                acc[i][4 * k + 1] += v.y;
+                acc[i][4 * k + 2] += v.z;
+                acc[i][4 * k + 3] += v.w;
+            }
+        }
+    }
+    if constexpr (F16) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][r] *= kF16WeightUnscale;
+    }
+    if constexpr (WB >= 8) {
+        if (a.zc % 32 == 0 && a.cout % 32 == 0) {
+            conv_epilogue_direct<TO, TB, HB, WB, MI, MW, WM>(a, acc, n, t_blk, h_blk, w_blk, bt_i,
+                                                             bh_i, bw_i, co_tile, lane, wave_m);
+            return;
+        }
+    }
+    conv_epilogue<TO, HB, WB, MI, MW, WM>(a, acc, ep + wave * 32 * kEp, n, t_blk, h_blk, w_blk,
+                                          bt_i, bh_i, bw_i, co_tile, lane, wave_m);
+}
+
+// Output-block shapes (T x H x W = 256 positions). The wide ones suit big boxes; the narrow ones
+// (WB = 4 or 2, deep in T) fit boxes 10 or 20 positions wide, such as one width quarter of the
+// 720p decode's first stages, where an 8- or 16-wide block wastes up to 43% of its rows.
+enum BlockKind {
+    kBlk2x8x16 = 0, kBlk4x8x8 = 1, kBlk4x4x16 = 2, kBlk4x16x4 = 3, kBlk16x4x4 = 4, kBlk16x8x2 = 5,
+    kBlockKinds = 6
+};
+
+struct BlockDims {
+    int tb, hb, wb;
+};
+
+constexpr BlockDims kBlockDims[kBlockKinds] = {{2, 8, 16}, {4, 8, 8}, {4, 4, 16},
+                                               {4, 16, 4}, {16, 4, 4}, {16, 8, 2}};
 
 inline int64_t padded_volume(const Box& b, int tb, int hb, int wb) {
     return ceil_div(b.bt(), tb) * tb * ceil_div(b.bh(), hb) * hb * ceil_div(b.bw(), wb) * wb;
 }
 
+// The shape that pads the box least. The narrow shapes, which stage without the ring, are
+// charged 10% more, about what the ring gains. Ties keep the earlier shape.
 inline BlockKind pick_block(const Box& b) {
-    const int64_t v0 = padded_volume(b, 2, 8, 16);
-    const int64_t v1 = padded_volume(b, 4, 8, 8);
-    const int64_t v2 = padded_volume(b, 4, 4, 16);
-    if (v1 < v0 && v1 <= v2) return kBlk4x8x8;
-    if (v2 < v0) return kBlk4x4x16;
-    return kBlk2x8x16;
+    int best = 0;
+    int64_t best_cost = INT64_MAX;
+    for (int k = 0; k < kBlockKinds; ++k) {
+        const BlockDims& d = kBlockDims[k];
+        const int64_t cost = padded_volume(b, d.tb, d.hb, d.wb) * (d.wb >= 8 ? 10 : 11);
+        if (cost < best_cost) {
+            best = k;
+            best_cost = cost;
+        }
+    }
+    return (BlockKind)best;
 }
 
 template <int NT>
 constexpr int wave_rows() {
     return kMfmaWaves / (NT / 32);
+}
+
+// Output-channel tile of a conv: 128 wide, or 64 / 32 for narrow outputs (conv_out's 48 or 12).
+inline int conv_nt(int64_t cout) { return cout >= 128 ? 128 : cout > 32 ? 64 : 32; }
+
+// Workgroups of one conv launch over `box` (all samples), before any split over K.
+inline int64_t conv_workgroups(int64_t n, int64_t cout, const Box& box) {
+    const BlockDims& d = kBlockDims[pick_block(box)];
+    return n * ceil_div(box.bt(), d.tb) * ceil_div(box.bh(), d.hb) * ceil_div(box.bw(), d.wb) *
+           ceil_div(cout, conv_nt(cout));
 }
 
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
@@ -996,26 +1137,87 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
         return fail(VAE_ERR_INVALID_ARG, "conv3d: GroupNorm slot range outside its row");
     a.nslots = (int32_t)stride;
     a.slot0 = fz ? (int32_t)fz->slot0 : 0;
+    a.splits = 1;
+    a.part = nullptr;
+    a.reduce = nullptr;
+    const int32_t splits = fz && fz->part ? fz->splits : 1;
+    if (splits > 1) {
+        // split over K: `splits` times the grid store partial sums, then one launch adds them
+        // and runs the epilogue
+        if (splits > a.cin / (SPLIT ? 16 : kCK) || total * splits > INT32_MAX)
+            return fail(VAE_ERR_INVALID_ARG, "conv3d: more K splits than channel chunks");
+        a.splits = splits;
+        a.part = fz->part;
+        hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
+                           dim3((unsigned)(total * splits)), dim3(kMfmaThreads), 0, stream, a);
+        VAE_HIP_CHECK(hipGetLastError());
+        a.part = nullptr;
+        a.reduce = fz->part;
+        hipLaunchKernelGGL((conv3d_reduce_kernel<NT, TI, TO, TB, HB, WB>), dim3((unsigned)total),
+                           dim3(kMfmaThreads), 0, stream, a);
+        VAE_HIP_CHECK(hipGetLastError());
+        return VAE_OK;
+    }
     hipLaunchKernelGGL((conv3d_mfma_kernel<NT, TI, TO, SPLIT, PACKED, TB, HB, WB>),
                        dim3((unsigned)total), dim3(kMfmaThreads), 0, stream, a);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
 
+// The narrow block shapes, instantiated in translation units of their own
+// (conv3d_mfma_*_narrow.hip) to keep the build parallel.
+template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
+vae_status_t run_narrow(BlockKind kind, const vae_tensor_t& x, const void* w, const float* bias,
+                        const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                        const ConvFuse* fz, hipStream_t stream) {
+    switch (kind) {
+        case kBlk4x16x4:
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 16, 4>(x, w, bias, residual, y, box,
+                                                                  fz, stream);
+        case kBlk16x4x4:
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 16, 4, 4>(x, w, bias, residual, y, box,
+                                                                  fz, stream);
+        default:
+            return run_shape<NT, TI, TO, SPLIT, PACKED, 16, 8, 2>(x, w, bias, residual, y, box,
+                                                                  fz, stream);
+    }
+}
+
+// Explicit instantiations of run_narrow for one (NT, input type, split): `extern` in the file that
+// instantiates run_mfma_out, empty in the file that holds the narrow kernels.
+#define VAE_NARROW_SIG(NT, TI, TO, SPLIT, PACKED)                                               \
+    vae_status_t run_narrow<NT, TI, TO, SPLIT, PACKED>(                                        \
+        BlockKind, const vae_tensor_t&, const void*, const float*, const vae_tensor_t*,        \
+        const vae_tensor_t&, const Box&, const ConvFuse*, hipStream_t)
+#define VAE_NARROW_INST(PREFIX, NT, TI, SPLIT)                                                  \
+    PREFIX template VAE_NARROW_SIG(NT, TI, float, SPLIT, true);                                 \
+    PREFIX template VAE_NARROW_SIG(NT, TI, float, SPLIT, false);                                \
+    PREFIX template VAE_NARROW_SIG(NT, TI, uint16_t, SPLIT, true);                              \
+    PREFIX template VAE_NARROW_SIG(NT, TI, uint16_t, SPLIT, false);
+// fp16 outputs exist for 2-byte inputs only
+#define VAE_NARROW_INST_F16(PREFIX, NT, TI, SPLIT)                                              \
+    VAE_NARROW_INST(PREFIX, NT, TI, SPLIT)                                                      \
+    PREFIX template VAE_NARROW_SIG(NT, TI, _Float16, SPLIT, true);                              \
+    PREFIX template VAE_NARROW_SIG(NT, TI, _Float16, SPLIT, false);
+
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
 vae_status_t run_block(const vae_tensor_t& x, const void* w, const float* bias,
                        const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
                        const ConvFuse* fz, hipStream_t stream) {
-    switch (pick_block(box)) {
+    const BlockKind kind = pick_block(box);
+    switch (kind) {
         case kBlk4x8x8:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 8, 8>(x, w, bias, residual, y, box, fz,
                                                                  stream);
         case kBlk4x4x16:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 4, 4, 16>(x, w, bias, residual, y, box,
                                                                   fz, stream);
-        default:
+        case kBlk2x8x16:
             return run_shape<NT, TI, TO, SPLIT, PACKED, 2, 8, 16>(x, w, bias, residual, y, box,
                                                                   fz, stream);
+        default:
+            return run_narrow<NT, TI, TO, SPLIT, PACKED>(kind, x, w, bias, residual, y, box, fz,
+                                                         stream);
     }
 }
 

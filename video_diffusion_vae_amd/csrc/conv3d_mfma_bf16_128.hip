@@ -3,6 +3,7 @@
 
 namespace vae {
 namespace mfma {
+VAE_NARROW_INST_F16(extern, 128, uint16_t, false)
 template vae_status_t run_mfma_out<128, uint16_t, false>(const vae_tensor_t&, const void*, const float*,
                                                    const vae_tensor_t*, const vae_tensor_t&,
                                                    const Box&, bool, const ConvFuse*, hipStream_t);

@@ -1,0 +1,8 @@
+// MFMA conv kernels with the narrow block shapes for NT = 64, bf16 input (see conv3d_mfma.h).
+#include "conv3d_mfma.h"
+
+namespace vae {
+namespace mfma {
+VAE_NARROW_INST_F16(, 64, uint16_t, false)
+}  // namespace mfma
+}  // namespace vae

@@ -3,6 +3,7 @@
 
 namespace vae {
 namespace mfma {
+VAE_NARROW_INST(extern, 32, float, false)
 template vae_status_t run_mfma_out<32, float, false>(const vae_tensor_t&, const void*, const float*,
                                                    const vae_tensor_t*, const vae_tensor_t&,
                                                    const Box&, bool, const ConvFuse*, hipStream_t);

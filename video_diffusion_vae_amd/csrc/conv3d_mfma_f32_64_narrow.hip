@@ -1,0 +1,8 @@
+// MFMA conv kernels with the narrow block shapes for NT = 64, fp32 input (see conv3d_mfma.h).
+#include "conv3d_mfma.h"
+
+namespace vae {
+namespace mfma {
+VAE_NARROW_INST(, 64, float, false)
+}  // namespace mfma
+}  // namespace vae

@@ -1,0 +1,9 @@
+// MFMA conv kernels with the narrow block shapes for NT = 32,
+// fp32 input split into bf16 hi + lo (see conv3d_mfma.h).
+#include "conv3d_mfma.h"
+
+namespace vae {
+namespace mfma {
+VAE_NARROW_INST(, 32, float, true)
+}  // namespace mfma
+}  // namespace vae

@@ -289,6 +289,7 @@ struct Req {
     int64_t act = 0;      // bytes of the largest activation kept in a rotating buffer
     int64_t gn = 0;       // GroupNorm stats workspace
     int64_t parts = 0;    // per-patch GroupNorm moments (per-patch launches)
+    int64_t splitk = 0;   // partial sums of a conv split over K (small launches)
     int64_t mr = 0;       // mean/rstd
     int64_t crop = 0;     // latent crop (mode B)
     int64_t tile = 0;     // one decoded tile, fp32 pixels (mode B)
@@ -352,6 +353,30 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
             }
             r->gn = std::max<int64_t>(r->gn, ys.n * d.groups * slots * 3 * (int64_t)sizeof(double));
         };
+        // scratch of convs split over K: the largest of the plan's launches, which run one at a
+        // time
+        auto split = [&](const Shape& xs, int64_t cout, bool split_fp32) {
+            const vae_tensor_t x = tensor_of(nullptr, xs);
+            BoxList bl;
+            if (per_patch) {
+                bl = scaled_boxes(boxes, xs.t, ch, cw, fh, fw, &exact);
+            } else {
+                bl.n = 1;
+                bl.b[0] = whole_box(x);
+            }
+            for (int b = 0; b < bl.n; ++b) {
+                const int32_t n = conv_split_count(x, cout, d.dtype, bl.b[b], split_fp32);
+                r->splitk = std::max<int64_t>(
+                    r->splitk, (int64_t)conv_split_bytes(x, cout, bl.b[b], n));
+            }
+        };
+        if (l.op == VAE_OP_CONV)
+            split(cur, l.cout, conv_splits(d.flags, d.layers.data(), (int)d.layers.size(), (int)i));
+        if (l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) {
+            Shape xs = cur;
+            xs.dtype = d.dtype;
+            split(xs, l.cin, false);
+        }
         if (l.op == VAE_OP_CONV && next_gn) fused(cur, s, 1);
         if (l.op == VAE_OP_CONV && i + 1 < d.layers.size() && d.layers[i + 1].op == VAE_OP_D2S &&
             gn_follows(d, i + 1)) {
@@ -388,7 +413,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
 }
 
 struct Layout {
-    size_t buf[3], gn, parts, mr, crop, tile, attn, total;
+    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, total;
     int64_t act_bytes;
 };
 
@@ -404,6 +429,8 @@ Layout layout_of(const Req& r) {
     off += align_up((size_t)r.gn, 256);
     L.parts = off;
     off += align_up((size_t)r.parts, 256);
+    L.splitk = off;
+    off += align_up((size_t)r.splitk, 256);
     L.mr = off;
     off += align_up((size_t)r.mr, 256);
     L.crop = off;
@@ -555,6 +582,9 @@ struct Runner {
                         up ? up->sw : 1, lsh, lsw};
             fz.slot0 = slot0;
             fz.slot_stride = total;
+            // a launch too small to fill the chip splits its K dimension over the scratch
+            fz.splits = conv_split_count(xl, cout, d->dtype, b, (cf & VAE_CONV_SPLIT_FP32) != 0);
+            if (fz.splits > 1) fz.part = reinterpret_cast<float*>(ws + L.splitk);
             slot0 += slots[i];
             VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res,
                                   y, b, cf, s, &fz));

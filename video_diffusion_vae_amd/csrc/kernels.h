@@ -27,12 +27,18 @@ struct BoxList {
 // The partials of one launch fill slots [slot0, slot0 + conv_gn_slots(box)) of rows that are
 // slot_stride slots long (0: the launch's own count), so that the launches of several patch
 // boxes can share one array and be merged together.
+// With `part` (conv_split_bytes(...) bytes of fp32 scratch) and splits > 1 the MFMA conv splits
+// its K dimension `splits` ways: one launch stores each split's partial sums, a second adds them
+// in split order and runs the epilogue (deterministic; the sums differ from the unsplit conv's
+// only by the order of their fp32 additions).
 struct ConvFuse {
     double* gn_ws;
     int32_t groups;
     int32_t st, sh, sw;
     int32_t lsh = 0, lsw = 0;
     int64_t slot0 = 0, slot_stride = 0;
+    float* part = nullptr;
+    int32_t splits = 1;
 };
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
@@ -43,6 +49,12 @@ bool conv_uses_mfma_c(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype)
 // yc: channels of y; k = st * sh * sw of the fused depth-to-space (1 for none).
 int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, const Box& box,
                       int32_t groups, int32_t k);
+// Split over K for launches that would leave most of the chip idle: the number of splits worth
+// making for a conv of x (its input grid) to `cout` channels over `box` (1: none), and the
+// scratch bytes of that many splits. `split_fp32`: the conv applies an fp32 x as hi + lo.
+int32_t conv_split_count(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype, const Box& box,
+                         bool split_fp32);
+size_t conv_split_bytes(const vae_tensor_t& x, int64_t cout, const Box& box, int32_t splits);
 // Fragment-packed bf16 weights (see conv3d.hip): element count and the packing kernel.
 int64_t packed_weight_elems(int64_t cout, int64_t cin);
 // to_f16: fp16(w * 2^10), the weight operand of fp16 inputs.
