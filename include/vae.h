@@ -256,6 +256,23 @@ VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* 
                                         vae_tensor_t* y, void* ws, size_t ws_bytes,
                                         vae_stream_t stream);
 
+/* vae_groupnorm_silu without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture into a graph, tight serving loops, harnesses that forbid
+ * allocation). Same arguments and result: it runs the same kernels, bit for bit. Its scratch (the
+ * partials and mean/rstd) is a fixed 8 MiB array in the library's device memory, one per GPU,
+ * held until the process ends; its address is looked up on the first call on each device. A call
+ * needing more (vae_groupnorm_silu_workspace() > 8 MiB: about N * groups * 3 * 8 bytes per
+ * statistics block, at most 4096 blocks) is refused with VAE_ERR_UNSUPPORTED, info.extent = the
+ * bytes needed and info.min_width = the bytes held. It allocates nothing and never
+ * synchronises. Calls that overlap on one GPU (other streams, other host threads) share that
+ * array and race; serialise them. Nothing in it needs clearing between calls: the statistics pass
+ * writes every partial the merge reads. */
+VAE_API vae_status_t vae_groupnorm_silu_noalloc(const vae_tensor_t* x, const vae_box_t* boxes,
+                                                int32_t n_boxes, int32_t groups, float eps,
+                                                const float* gamma, const float* beta,
+                                                int32_t apply_silu, vae_tensor_t* y,
+                                                vae_stream_t stream);
+
 /* The same operation in three steps, for callers that move the per-box partials themselves.
  * vae_groupnorm_stats: per box, (count, mean, M2) as fp64 into part[n_boxes][N][groups][3]
  *   (device). ws is sized by vae_groupnorm_stats_workspace().

@@ -403,3 +403,19 @@ def test_space_to_depth_validation_needs_no_gpu(v):
     with pytest.raises(v.VaeError) as e:          # y aliasing x
         v.vae_space_to_depth(x, 1, 1, 1, x, stream=0)
     assert e.value.status == v.VAE_ERR_INVALID_ARG
+
+
+def test_groupnorm_noalloc_refuses_beyond_its_scratch(v):
+    """vae_groupnorm_silu_noalloc holds 8 MiB of scratch per GPU: a call that needs more is
+    refused on the host, before any device work, with the byte counts in the error info. The
+    tensor descriptors are never dereferenced."""
+    # 16 samples of [16, 256, 256, 256]: 1024 statistics blocks x 16 x 32 groups x 24 bytes; two
+    # far-apart stand-in addresses, so that the tensors do not overlap
+    big = v.vae_tensor_t(1 << 40, v.VAE_DTYPE_BF16, 0, 16, 16, 256, 256, 256)
+    y = v.vae_tensor_t(1 << 41, v.VAE_DTYPE_BF16, 0, 16, 16, 256, 256, 256)
+    st = v.LIB.vae_groupnorm_silu_noalloc(ctypes.byref(big), None, 1, 32, 1e-6, None, None, 1,
+                                          ctypes.byref(y), None)
+    assert st == v.VAE_ERR_UNSUPPORTED
+    info = v.last_error_info()
+    assert info["min_width"] == 8 << 20 and info["extent"] > 8 << 20
+    assert b"noalloc" in v.LIB.vae_last_error()

@@ -30,7 +30,8 @@ EXPORTS = (
     "vae_conv3d_causal_fused_workspace", "vae_conv3d_causal_fused", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_conv_weight_pack_f16",
     "vae_decoder_packed_weight_size",
     "vae_decoder_pack_weights",
-    "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_stats_workspace",
+    "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_silu_noalloc",
+    "vae_groupnorm_stats_workspace",
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_rmsnorm_silu",
     "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample", "vae_space_to_depth",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
@@ -127,6 +128,7 @@ def _load():
         "vae_decoder_pack_weights": ([P, P, SZ, P], I32),
         "vae_groupnorm_silu_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_groupnorm_silu": ([T, B, I32, I32, F, P, P, I32, T, P, SZ, P], I32),
+        "vae_groupnorm_silu_noalloc": ([T, B, I32, I32, F, P, P, I32, T, P], I32),
         "vae_groupnorm_stats_workspace": ([T, B, I32, I32, ctypes.POINTER(SZ)], I32),
         "vae_groupnorm_stats": ([T, B, I32, I32, P, P, SZ, P], I32),
         "vae_groupnorm_combine": ([P, I32, I32, I32, F, P, P], I32),
@@ -325,6 +327,16 @@ def vae_groupnorm_silu_workspace(x, boxes, groups):
     n = ctypes.c_size_t()
     _check(LIB.vae_groupnorm_silu_workspace(ctypes.byref(xd), arr, nb, groups, ctypes.byref(n)))
     return n.value
+
+
+def vae_groupnorm_silu_noalloc(x, boxes, groups, eps, gamma, beta, apply_silu, y, stream=None):
+    """vae_groupnorm_silu on the library's own fixed scratch: allocates nothing."""
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    arr, nb = _boxes(boxes)
+    _check(LIB.vae_groupnorm_silu_noalloc(ctypes.byref(xd), arr, nb, groups, eps, _ptr(gamma),
+                                          _ptr(beta), int(apply_silu), ctypes.byref(yd),
+                                          _stream(stream)))
+    return y
 
 
 def vae_groupnorm_silu(x, boxes, groups, eps, gamma, beta, apply_silu, y, ws=None, stream=None):

@@ -2,6 +2,7 @@
 // split, and dispatch to the kernel launchers. No exception crosses this boundary.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -682,6 +683,75 @@ VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* 
     double* stats = static_cast<double*>(ws);
     float* mr = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                          align_up(gn_stats_workspace(*x, bl, groups), 256));
+    hipStream_t s = as_stream(stream);
+    VAE_TRY(launch_gn_stats(*x, bl, groups, stats, nullptr, mr, eps, s));
+    for (int i = 0; i < bl.n; ++i)
+        VAE_TRY(launch_gn_apply(*x, bl.b[i], groups, mr, gamma, beta, apply_silu != 0, *y, s));
+    return VAE_OK;
+}
+
+}  // extern "C"
+
+namespace vae {
+namespace {
+
+// Scratch of vae_groupnorm_silu_noalloc: one copy per GPU, held from the library's load until the
+// process ends. In host code `gn_scratch` stands for the array, not its device address: kernels
+// get the address hipGetSymbolAddress returns on that device.
+constexpr size_t kGnScratchBytes = size_t(8) << 20;
+__device__ __align__(256) uint8_t gn_scratch[kGnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex gn_scratch_mutex;
+uint8_t* gn_scratch_ptr[kMaxDevices];   // per device, null until its first call
+
+// The current device's scratch address, looked up once per device (with that device current).
+vae_status_t gn_scratch_address(uint8_t** out) {
+    int dev = -1;
+    VAE_HIP_CHECK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(VAE_ERR_UNSUPPORTED, "device index beyond the library's table");
+    std::lock_guard<std::mutex> lock(gn_scratch_mutex);
+    if (!gn_scratch_ptr[dev]) {
+        void* p = nullptr;
+        VAE_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(gn_scratch)));
+        if (!p) return fail(VAE_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch");
+        gn_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = gn_scratch_ptr[dev];
+    return VAE_OK;
+}
+
+}  // namespace
+}  // namespace vae
+
+extern "C" {
+
+VAE_API vae_status_t vae_groupnorm_silu_noalloc(const vae_tensor_t* x, const vae_box_t* boxes,
+                                                int32_t n_boxes, int32_t groups, float eps,
+                                                const float* gamma, const float* beta,
+                                                int32_t apply_silu, vae_tensor_t* y,
+                                                vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_gn(x, groups));
+    VAE_TRY(check_tensor(y, "y"));
+    VAE_TRY(check_gn_output(*x, *y));
+    if (!(eps >= 0.0f)) return fail(VAE_ERR_INVALID_ARG, "eps must be >= 0");
+    BoxList bl;
+    VAE_TRY(box_list(*x, boxes, n_boxes, &bl));
+    const size_t need = gn_full_workspace(*x, bl, groups);
+    if (need > kGnScratchBytes)
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "vae_groupnorm_silu_noalloc: this call needs " + std::to_string(need) +
+                        " bytes of scratch, above the library's " +
+                        std::to_string(kGnScratchBytes) + " (use vae_groupnorm_silu)",
+                    -1, (int64_t)need, -1, (int64_t)kGnScratchBytes);
+    uint8_t* ws = nullptr;
+    VAE_TRY(gn_scratch_address(&ws));
+    // the same launches as vae_groupnorm_silu: every partial slot the merge reads is written
+    // first by the statistics pass, so nothing needs clearing between calls
+    double* stats = reinterpret_cast<double*>(ws);
+    float* mr = reinterpret_cast<float*>(ws + align_up(gn_stats_workspace(*x, bl, groups), 256));
     hipStream_t s = as_stream(stream);
     VAE_TRY(launch_gn_stats(*x, bl, groups, stats, nullptr, mr, eps, s));
     for (int i = 0; i < bl.n; ++i)
