@@ -25,7 +25,14 @@ from __future__ import annotations
 import numpy as np
 
 from .layers import causal_conv3d, causal_time_pad, conv3d_valid, group_norm, silu, \
-    nearest_upsample, depth_to_space, space_to_depth, rms_norm, frame_attention
+    nearest_upsample, depth_to_space, space_to_depth, rms_norm, frame_attention, \
+    strided_causal_conv3d
+
+# Spatial zero padding of a strided downsampling conv ("conv_down"), ((top, bottom), (left,
+# right)): one row and column on every side (LTX-2's bare strided conv), or none before and one
+# after (Wan's downsampler pads (0, 1, 0, 1) before striding). "Add tiled VAE parallelism &
+# extended model support", LTX-2 and Qwen-Image/Wan encoder commit messages.
+DOWN_PADS = {"around": ((1, 1), (1, 1)), "after": ((0, 1), (0, 1))}
 from .stats import group_moments, chan_combine, normalize_with
 from .tiling import bands, overlap_tiles, ramp_1d
 
@@ -45,6 +52,12 @@ def output_shape(spec: dict, latent_shape):
         elif k == "s2d":
             st, sh, sw = op["st"], op["sh"], op["sw"]
             t, h, w, c = (t + st - 1) // st, h // sh, w // sw, c * st * sh * sw
+        elif k == "conv_down":
+            (pt, pb), (pl, pr) = DOWN_PADS[op["pad"]]
+            t = (t - 1) // op["st"] + 1
+            h = (h + pt + pb - 3) // op["sh"] + 1
+            w = (w + pl + pr - 3) // op["sw"] + 1
+            c = op["cout"]
     return (n, t, h, w, c)
 
 
@@ -92,6 +105,10 @@ def decode(spec: dict, z: np.ndarray, params: list) -> np.ndarray:
             h = nearest_upsample(h, op["sh"], op["sw"])
         elif k == "s2d":
             h = space_to_depth(h, op["st"], op["sh"], op["sw"])
+        elif k == "conv_down":
+            p = next(it)
+            h = strided_causal_conv3d(h, p["w"], p["b"], (op["st"], op["sh"], op["sw"]),
+                                      DOWN_PADS[op["pad"]])
         else:
             raise ValueError(k)
     return h
@@ -138,6 +155,42 @@ def _conv_patches(patches, w, b):
             y = conv3d_valid(causal_time_pad(ext, 3), w, b)
             # a convolved patch keeps the size of the patch it came from
             assert y.shape[2:4] == (rows[i], cols[j]), (y.shape, rows[i], cols[j])
+            out_row.append(y)
+        out.append(out_row)
+    return out
+
+
+def _conv_down_patches(patches, w, b, stride, pads):
+    """Strided conv of every patch. A patch's output rows [a / s, (a + n) / s) read input rows
+    s * o - top + (0, 1, 2): its own band plus `top` rows gathered before it and `bottom` after
+    (for a band of whole strides); zeros only beyond the true image border. The gathered region is
+    then convolved without further padding."""
+    (pt, pb), (pl, pr) = pads
+    rows = [row[0].shape[2] for row in patches]
+    cols = [p.shape[3] for p in patches[0]]
+    r_at, c_at = _starts(rows), _starts(cols)
+    n, t, _, _, c = patches[0][0].shape
+    out = []
+    for i in range(len(rows)):
+        out_row = []
+        for j in range(len(cols)):
+            assert rows[i] % stride[1] == 0 and cols[j] % stride[2] == 0, (rows, cols, stride)
+            r0, r1 = r_at[i] - pt, r_at[i] + rows[i] + pb
+            c0, c1 = c_at[j] - pl, c_at[j] + cols[j] + pr
+            ext = np.zeros((n, t, r1 - r0, c1 - c0, c))
+            for a in range(len(rows)):
+                lo_r, hi_r = max(r0, r_at[a]), min(r1, r_at[a] + rows[a])
+                if lo_r >= hi_r:
+                    continue
+                for bb in range(len(cols)):
+                    lo_c, hi_c = max(c0, c_at[bb]), min(c1, c_at[bb] + cols[bb])
+                    if lo_c >= hi_c:
+                        continue
+                    ext[:, :, lo_r - r0:hi_r - r0, lo_c - c0:hi_c - c0] = \
+                        patches[a][bb][:, :, lo_r - r_at[a]:hi_r - r_at[a],
+                                       lo_c - c_at[bb]:hi_c - c_at[bb]]
+            y = strided_causal_conv3d(ext, w, b, stride, ((0, 0), (0, 0)))
+            assert y.shape[2:4] == (rows[i] // stride[1], cols[j] // stride[2]), y.shape
             out_row.append(y)
         out.append(out_row)
     return out
@@ -217,6 +270,10 @@ def decode_patch_halo(spec: dict, z: np.ndarray, params: list, grid, unit=(1, 1)
             # bands are cut in whole multiples of the fold, so every patch folds on its own
             patches = [[space_to_depth(p, op["st"], op["sh"], op["sw"]) for p in row]
                        for row in patches]
+        elif k == "conv_down":
+            p = next(it)
+            patches = _conv_down_patches(patches, p["w"], p["b"], (op["st"], op["sh"], op["sw"]),
+                                         DOWN_PADS[op["pad"]])
         else:
             raise ValueError(k)
     return np.concatenate([np.concatenate(row, axis=3) for row in patches], axis=2)

@@ -134,6 +134,13 @@ def _torch_decode(spec, z, params):
             h = F.silu(rms(h, next(it)))
         elif k == "attn":
             h = attn(h, next(it))
+        elif k == "conv_down":
+            # two causal front copies of frame 0, the spatial zero pads, then a strided conv3d
+            p = next(it)
+            (pt, pb), (pl, pr) = {"around": ((1, 1), (1, 1)), "after": ((0, 1), (0, 1))}[op["pad"]]
+            hp = F.pad(torch.cat([h[:, :, :1], h[:, :, :1], h], dim=2), (pl, pr, pt, pb, 0, 0))
+            h = F.conv3d(hp, torch.from_numpy(p["w"]).double(), torch.from_numpy(p["b"]).double(),
+                         stride=(op["st"], op["sh"], op["sw"]))
         elif k == "s2d":
             # causal front pad of st-1 copies of frame 0, then fold (dt, dh, dw) slowest into C
             st, sh, sw = op["st"], op["sh"], op["sw"]
@@ -162,12 +169,14 @@ def test_tiny_decoder_matches_torch_library_graph():
     assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-11
 
 
-@pytest.mark.parametrize("name", ["wan_tiny", "ltx2_enc_tiny"])
+@pytest.mark.parametrize("name", ["wan_tiny", "ltx2_enc_tiny", "ltx2_enc_strided_tiny",
+                                  "wan_enc_tiny"])
 def test_plan_matches_torch_library_graph(name):
     """The RMS-norm residual blocks, the frame attention (torch's rms_norm, linear and
-    scaled_dot_product_attention) and the space-to-depth folds (a reshape) of the Wan-shaped
-    decoder and the LTX-2-shaped encoder, rebuilt from torch CPU library ops, with random
-    biases, gammas and betas."""
+    scaled_dot_product_attention), the space-to-depth folds (a reshape) and the strided
+    downsampling convs (torch's strided conv3d) of the Wan-shaped decoder and the LTX-2- and
+    Wan-style encoders, rebuilt from torch CPU library ops, with random biases, gammas and
+    betas."""
     spec = vae_synth.WORKLOADS[name]
     z = ndhwc(vae_synth.latent(spec)).astype(np.float64)
     params = vae_synth.decoder_params(spec, affine_seed=11)

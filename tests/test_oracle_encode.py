@@ -108,7 +108,7 @@ def test_encode_overlap_blend_differs_from_whole_only_by_tiling():
 
 
 # ------------------------------------------------------------------------------------------------
-# The bare strided downsampler conv (oracle side; the GPU kernel is not built yet)
+# The bare strided downsampler conv and the encoders built on it
 # ------------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("stride,pad,t", [((2, 2, 2), ((1, 1), (1, 1)), 5),   # LTX-2 kind
@@ -149,3 +149,29 @@ def test_strided_causal_conv_by_brute_force():
             if 0 <= hi < 4 and 0 <= wi < 5:
                 acc += w[o, c, a, p, q] * x[0, ti, hi, wi, c]
         assert abs(y[0, t, h, ww, o] - acc) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["ltx2_enc_strided_tiny", "wan_enc_tiny"])
+def test_strided_encoder_patch_halo_equals_whole(name):
+    """Patch bands in whole multiples of the plan's fold: each strided conv gathers its halo rows
+    (one before the band for padding around, one after for padding after) from the neighbours
+    and must reproduce the whole encode."""
+    spec = vae_synth.WORKLOADS[name]
+    x = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1)).astype(np.float64)
+    p = vae_synth.decoder_params(spec, affine_seed=4)
+    whole = oracle.encode(spec, x, p)
+    assert whole.shape == oracle.output_shape(spec, x.shape)
+    split = oracle.encode_patch_halo(spec, x, p, spec["patch_grid"])
+    assert np.abs(split - whole).max() <= 1e-12 * np.abs(whole).max()
+
+
+def test_strided_encoder_720p_shapes():
+    """Three stride-2 downsamplers after the 4x4 patchify: [1,3,121,704,1280] ->
+    [1,256,16,22,40], the frames 121 -> 61 -> 31 -> 16 by the causal rule."""
+    spec = vae_synth.LTX2_ENC_STRIDED_720P
+    assert oracle.output_shape(spec, (1, 121, 704, 1280, 3)) == (1, 16, 22, 40, 256)
+    ts = [121]
+    for op in spec["layers"]:
+        if op["op"] == "conv_down":
+            ts.append((ts[-1] - 1) // op["st"] + 1)
+    assert ts == [121, 61, 31, 16]

@@ -35,6 +35,9 @@ Layer plan vocabulary (every op works on a channels-last activation):
 - ``attn``: single-head self-attention over each frame's positions, width ``c``, with its residual;
 - ``d2s``: depth-to-space by (st, sh, sw); with st > 1 the first st-1 output frames are dropped;
 - ``nearest``: nearest-neighbour spatial upsampling by (sh, sw).
+- ``conv_down``: strided causal Conv3d 3x3x3, ``cin`` -> ``cout``, strides (st, sh, sw), zero
+  padding ``pad`` = "around" (one row/column on every side) or "after" (one after the image
+  only); T frames become (T - 1) // st + 1.
 
 Parameters are drawn in plan order: each ``conv`` gives one weight [cout, cin, 3, 3, 3] and one bias
 [cout]; each ``res`` / ``res_rms`` gives norm(c), conv(c, c), norm(c), conv(c, c); each ``gn_silu`` /
@@ -304,10 +307,60 @@ LTX2_ENC_TINY = with_input(LTX2_ENC_720P, (1, 3, 9, 64, 96), "ltx2_enc_tiny", pa
 LTX2_ENC_SMALL = with_input(LTX2_ENC_720P, (1, 3, 9, 64, 160), "ltx2_enc_small",
                             patch_grid=(2, 2), overlap_tile=(2, 3), overlap_stride=(2, 2))
 
+# The same encoder with bare strided downsamplers: each downsampler is one causal Conv3d C ->
+# C_next with stride (2, 2, 2) (LTX-2's fourth downsample kind), zero padding one row and column
+# around; the frame counts follow the causal rule (T - 1) // 2 + 1: 121 -> 61 -> 31 -> 16.
+_LTX2_ENC_STRIDED_LAYERS = [
+    {"op": "s2d", "st": 1, "sh": 4, "sw": 4},
+    {"op": "conv", "cin": 48, "cout": 128},
+    {"op": "res", "c": 128},
+    {"op": "res", "c": 128},
+    {"op": "conv_down", "cin": 128, "cout": 256, "st": 2, "sh": 2, "sw": 2, "pad": "around"},
+    {"op": "res", "c": 256},
+    {"op": "res", "c": 256},
+    {"op": "conv_down", "cin": 256, "cout": 512, "st": 2, "sh": 2, "sw": 2, "pad": "around"},
+    {"op": "res", "c": 512},
+    {"op": "res", "c": 512},
+    {"op": "conv_down", "cin": 512, "cout": 1024, "st": 2, "sh": 2, "sw": 2, "pad": "around"},
+    {"op": "res", "c": 1024},
+    {"op": "res", "c": 1024},
+    {"op": "gn_silu"},
+    {"op": "conv", "cin": 1024, "cout": 256, "f32_out": True},
+]
+LTX2_ENC_STRIDED_720P = with_input(LTX2_ENC_720P, LTX2_ENC_720P["input"], "ltx2_enc_strided_720p")
+LTX2_ENC_STRIDED_720P["layers"] = _LTX2_ENC_STRIDED_LAYERS
+LTX2_ENC_STRIDED_TINY = with_input(LTX2_ENC_STRIDED_720P, (1, 3, 9, 64, 96),
+                                   "ltx2_enc_strided_tiny", patch_grid=(1, 3),
+                                   overlap_tile=(2, 2), overlap_stride=(1, 1))
+# A Wan-style downsampler: zero padding only after the image (0, 1, 0, 1), then stride 2 in space
+# (and 1 in time), at a quarter of the widths.
+WAN_ENC_TINY = {
+    "name": "wan_enc_tiny",
+    "kind": "encoder",
+    "dtype": "bf16",
+    "input": (1, 3, 5, 32, 48),
+    "groups": 32, "eps": 1e-6,
+    "layers": [
+        {"op": "s2d", "st": 1, "sh": 2, "sw": 2},
+        {"op": "conv", "cin": 12, "cout": 64},
+        {"op": "res_rms", "c": 64},
+        {"op": "conv_down", "cin": 64, "cout": 128, "st": 1, "sh": 2, "sw": 2, "pad": "after"},
+        {"op": "res_rms", "c": 128},
+        {"op": "conv_down", "cin": 128, "cout": 128, "st": 2, "sh": 2, "sw": 2, "pad": "after"},
+        {"op": "res", "c": 128},
+        {"op": "gn_silu"},
+        {"op": "conv", "cin": 128, "cout": 32, "f32_out": True},
+    ],
+    "down": (2, 8, 8),
+    "patch_grid": (2, 2),
+    "overlap_tile": (3, 3), "overlap_stride": (2, 2),
+}
+
 WORKLOADS = {s["name"]: s for s in (CONV_GN, TINY_DECODER, LTX2_720P, LTX2_SMALL, LTX2_MID,
                                     LTX2_720P_1F, LTX2_TINY, LTX2_TINY_N2, WAN_720P, WAN_SMALL,
                                     WAN_720P_1F, WAN_720P_6F, WAN_TINY, MIXED_RMS_GN,
-                                    LTX2_ENC_720P, LTX2_ENC_TINY, LTX2_ENC_SMALL)}
+                                    LTX2_ENC_720P, LTX2_ENC_TINY, LTX2_ENC_SMALL,
+                                    LTX2_ENC_STRIDED_720P, LTX2_ENC_STRIDED_TINY, WAN_ENC_TINY)}
 
 
 # ----------------------------------------------------------------------------------------------
@@ -404,6 +457,9 @@ def walk_plan(spec: dict):
             k = op["st"] * op["sh"] * op["sw"]
             yield op, c, c * k
             c *= k
+        elif kind == "conv_down":
+            yield op, op["cin"], op["cout"]
+            c = op["cout"]
         else:
             raise ValueError(f"unknown op {kind!r}")
 
@@ -414,7 +470,7 @@ def decoder_params(spec: dict, affine_seed=None) -> list:
     dt = spec["dtype"]
     for op, cin, cout in walk_plan(spec):
         kind = op["op"]
-        if kind == "conv":
+        if kind in ("conv", "conv_down"):
             out.append(conv_params(n_conv, cin, cout, dt, affine_seed)); n_conv += 1
         elif kind == "attn":
             out.append(attn_params(n_attn, cin, dt, affine_seed)); n_attn += 1
