@@ -73,6 +73,9 @@ def conv_flops(spec, latent_shape):
             h, w = h * op["sh"], w * op["sw"]
         elif k == "s2d":
             t, h, w = (t + op["st"] - 1) // op["st"], h // op["sh"], w // op["sw"]
+        elif k == "conv_down":
+            t, h, w = (t - 1) // op["st"] + 1, h // op["sh"], w // op["sw"]
+            total += 2 * 27 * op["cin"] * op["cout"] * n * t * h * w
     return total
 
 
@@ -92,6 +95,8 @@ def output_shape(spec, latent_shape):
         elif k == "s2d":
             t, h, w = (t + op["st"] - 1) // op["st"], h // op["sh"], w // op["sw"]
             c *= op["st"] * op["sh"] * op["sw"]
+        elif k == "conv_down":
+            t, h, w, c = (t - 1) // op["st"] + 1, h // op["sh"], w // op["sw"], op["cout"]
     return (n, t, h, w, c)
 
 
@@ -100,6 +105,8 @@ WORKLOADS = {
     "ltx2": ("LTX2_720P", (1, 4), "2x3"),
     "wan": ("WAN_720P", (1, 4), "2x3"),
     "ltx2_enc": ("LTX2_ENC_720P", (1, 1), "2x3"),    # encode: untiled, or latent-grid tiles
+    # the same encoder with bare stride-2 causal convs as its downsamplers
+    "ltx2_enc_strided": ("LTX2_ENC_STRIDED_720P", (1, 1), "2x3"),
 }
 ENCODE_METRIC = "encoded Mpixel-frames/s (720p VAE encode, 1 GPU) + conv MFMA % of peak"
 
@@ -112,8 +119,9 @@ def activations_note(operands):
 
 
 def workload_name(kind, mode, tile_t=0, stride_t=0):
-    if kind == "ltx2_enc":
-        return "ltx2_720p_encode_" + ("untiled" if mode == "patch" else "overlap_blend_2x3")
+    if kind in ("ltx2_enc", "ltx2_enc_strided"):
+        prefix = "ltx2_720p_encode_" + ("strided_" if kind == "ltx2_enc_strided" else "")
+        return prefix + ("untiled" if mode == "patch" else "overlap_blend_2x3")
     prefix = {"ltx2": "ltx2_720p", "wan": "wan2.2_ti2v_5b_720p"}[kind]
     if mode == "patch":
         # the 1x4 patch-halo split with one launch per layer over all four patch boxes: on one

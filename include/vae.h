@@ -224,6 +224,42 @@ VAE_API vae_status_t vae_conv_weight_pack_f16(const void* weight, int32_t cout, 
                                               void* packed, vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Strided causal Conv3d (an encoder's bare downsampler)                                     */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * y[n,t,h,w,o] = bias[o] + residual[n,t,h,w,o]
+ *              + sum_{c,a,p,q} W[o,a,p,q,c] * x[n, max(st*t+a-2, 0), sh*h+p-pt, sw*w+q-pl, c]
+ * with zeros where a row or column leaves the image. Kernel 3x3x3; strides st, sh, sw >= 1.
+ * pad = VAE_PAD_AROUND: one zero row and column on every side (pt = pl = 1; LTX-2's bare strided
+ * conv); VAE_PAD_AFTER: none before the image, one after (pt = pl = 0; the Wan / Qwen-Image
+ * downsampler pads (0, 1, 0, 1) and strides 2). P4, LTX-2 and Qwen-Image/Wan encoder commit
+ * messages. The temporal axis is causal, as for vae_conv3d_causal: T frames become
+ * (T - 1) / st + 1.
+ *
+ * Arguments:
+ *  x: [N,T,H,W,Cin] (device), bf16, fp32 or fp16.
+ *  weight: [Cout][3][3][3][Cin] of weight_dtype, or with VAE_CONV_PACKED_WEIGHTS (bf16 x) /
+ *          VAE_CONV_PACKED_F16_WEIGHTS (fp16 x) the packed copy of vae_conv_weight_pack(_f16).
+ *  y: [N, (T-1)/st+1, (H+pt+pb-3)/sh+1, (W+pl+pr-3)/sw+1, Cout] (device), bf16, fp32 or fp16
+ *     (fp16 only on the matrix-core path); it must not overlap x. residual (or NULL) has y's
+ *     shape, y's dtype or fp32.
+ *  out_box: the positions of y computed (NULL = all); its input footprint is read in place, so a
+ *           box is one patch of a patch-halo encode.
+ * Packed weights with a bf16 or fp16 x, Cin % 32 == 0, Cout % 4 == 0, st and sh = sw in {1, 2}
+ * run on the matrix cores (fp32 accumulation; an fp16 x with fp16 weights scaled by 2^10, as for
+ * vae_conv3d_causal). Standard-layout weights run on a direct fp32-accumulating path.
+ * Errors: INVALID_ARG for shapes that do not match, strides < 1, an unknown pad or flags;
+ * UNSUPPORTED for packed weights or fp16 tensors off the matrix-core conditions.
+ */
+enum { VAE_PAD_AROUND = 0, VAE_PAD_AFTER = 1 };
+VAE_API vae_status_t vae_conv3d_causal_strided(const vae_tensor_t* x, const void* weight,
+                                               int32_t weight_dtype, const float* bias,
+                                               const vae_tensor_t* residual, vae_tensor_t* y,
+                                               const vae_box_t* out_box, int32_t st, int32_t sh,
+                                               int32_t sw, int32_t pad, int32_t flags,
+                                               vae_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* GroupNorm (+SiLU) with statistics merged across patches                                    */
 /* ------------------------------------------------------------------------------------------ */
 /*
@@ -461,6 +497,9 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  *  VAE_OP_S2D     space-to-depth fold (st, sh, sw) with the causal front copies of frame 0
  *                 (vae_space_to_depth): an encoder plan. Such a plan runs untiled, or tiled with
  *                 the tiling desc's down_* set to its folds; its input extents must fold evenly.
+ *  VAE_OP_CONV_DOWN strided causal conv cin -> cout, strides (st, sh, sw), zero padding `pad`
+ *                 (vae_conv3d_causal_strided): an encoder's downsampler. Its strides count as
+ *                 folds of the plan (down_*), and its input's H and W must be whole strides.
  * Dtypes:
  *  - conv weights and GroupNorm outputs (the operands of the next conv) have the plan dtype;
  *  - conv outputs and the residual stream have act_dtype, which must be VAE_DTYPE_F32 (anything
@@ -482,14 +521,15 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * reads, in fp16 instead of fp32 (half the bytes written and read back). Activations must stay
  * below 65504 in magnitude in both places.
  * The parameter pointers come in plan order:
- *  conv -> (weight, bias);
+ *  conv, conv_down -> (weight, bias);
  *  GN or RMS -> (gamma, beta);
  *  res, res_rms -> norm, conv, norm, conv;
  *  attn -> (gamma, beta, w_qkv [3C][C] bf16, b_qkv [3C], w_out [C][C] bf16, b_out [C]).
  * bias, gamma and beta may be NULL.
  */
 enum { VAE_OP_CONV = 1, VAE_OP_RES = 2, VAE_OP_GN_SILU = 3, VAE_OP_D2S = 4, VAE_OP_NEAREST = 5,
-       VAE_OP_RES_RMS = 6, VAE_OP_RMS_SILU = 7, VAE_OP_ATTN = 8, VAE_OP_S2D = 9 };
+       VAE_OP_RES_RMS = 6, VAE_OP_RMS_SILU = 7, VAE_OP_ATTN = 8, VAE_OP_S2D = 9,
+       VAE_OP_CONV_DOWN = 10 };
 
 typedef struct vae_layer_desc {
     int32_t op;
@@ -498,6 +538,7 @@ typedef struct vae_layer_desc {
     int32_t f32_out;
     int32_t no_split;  /* conv only: 1 = round an fp32 input to bf16 once even when the decoder
                           splits fp32 operands (VAE_DECODE_SPLIT_FP32_OPERANDS) */
+    int32_t pad;       /* VAE_OP_CONV_DOWN: VAE_PAD_AROUND or VAE_PAD_AFTER; 0 otherwise */
 } vae_layer_desc_t;
 
 enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1, VAE_DECODE_F16_OPERANDS = 2 };

@@ -419,3 +419,27 @@ def test_groupnorm_noalloc_refuses_beyond_its_scratch(v):
     info = v.last_error_info()
     assert info["min_width"] == 8 << 20 and info["extent"] > 8 << 20
     assert b"noalloc" in v.LIB.vae_last_error()
+
+
+def test_strided_conv_plan_rules(v):
+    """A plan's strided downsampler (VAE_OP_CONV_DOWN): strides of 1 or 2 with sh == sw, padding
+    after the image only with stride 2, and input extents of whole strides."""
+    def plan(**kw):
+        op = {"op": "conv_down", "cin": 32, "cout": 64, "st": 2, "sh": 2, "sw": 2, "pad": "around"}
+        op.update(kw)
+        return [op, {"op": "gn_silu"}, {"op": "conv", "cin": 64, "cout": 32, "f32_out": True}]
+    ptrs = [_FakePtr(i) for i in range(6)]
+    dec = v.Decoder(v.VAE_DTYPE_BF16, 32, 32, 1e-6, plan(), ptrs)
+    assert dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 5, 8, 8, 32),
+                                            (1, 1, 1))) > 0
+    with pytest.raises(v.VaeError) as e:          # 7 rows are not whole strides of 2
+        dec.workspace_size(v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 5, 7, 8, 32), (1, 1, 1)))
+    assert e.value.status == v.VAE_ERR_INVALID_ARG and e.value.info["axis"] == 2
+    dec.close()
+    for bad, status in [(dict(sh=3, sw=3), v.VAE_ERR_UNSUPPORTED),
+                        (dict(sh=2, sw=1), v.VAE_ERR_UNSUPPORTED),
+                        (dict(st=1, sh=1, sw=1, pad="after"), v.VAE_ERR_UNSUPPORTED),
+                        (dict(cin=16), v.VAE_ERR_INVALID_ARG)]:
+        with pytest.raises(v.VaeError) as e:
+            v.Decoder(v.VAE_DTYPE_BF16, 32, 32, 1e-6, plan(**bad), ptrs)
+        assert e.value.status == status, bad

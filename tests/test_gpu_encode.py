@@ -84,12 +84,13 @@ def _oracle(name, tiles=None):
     return oracle.encode_overlap_blend(spec, x, _params(name), tiles[0], tiles[1])
 
 
-def _encode(v, name, operands="f16", repeat=1, tiles=None, patches=None):
+def _encode(v, name, operands="f16", repeat=1, tiles=None, patches=None, launch="merged"):
     import torch
     spec = vae_synth.WORKLOADS[name]
     x = ndhwc(vae_synth.latent(spec))
     xp = v.pad_latent(x, spec)
     enc = v.upload_decoder(spec, _params(name), operands=operands)
+    enc.set_launch(v.VAE_LAUNCH_PER_PATCH if launch == "per_patch" else v.VAE_LAUNCH_MERGED)
     xd = dev(xp, "bf16")
     if patches is not None:
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, xp.shape, (1, 1, 1), patches=patches,
@@ -218,3 +219,32 @@ def test_ltx2_720p_encode_against_golden(v, patches):
     o = out.double()
     assert abs(float(o.mean()) - float(g["out_mean"])) <= 1e-3 * float(g["out_std"])
     assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
+
+
+@pytest.mark.parametrize("operands", ["f16", "split"])
+@pytest.mark.parametrize("name,mode", [("ltx2_enc_strided_tiny", "untiled"),
+                                       ("ltx2_enc_strided_tiny", "patch"),
+                                       ("ltx2_enc_strided_tiny", "per_patch"),
+                                       ("ltx2_enc_strided_tiny", "overlap"),
+                                       ("wan_enc_tiny", "untiled"),
+                                       ("wan_enc_tiny", "patch"),
+                                       ("wan_enc_tiny", "per_patch"),
+                                       ("wan_enc_tiny", "overlap")])
+def test_strided_encoders_match_oracle(v, name, mode, operands):
+    """Encoders whose downsamplers are strided causal convs (stride 2 with zero padding around,
+    LTX-2's bare kind; padding after the image, the Wan kind), untiled, in patch bands of whole
+    folds (one launch per layer, or one per patch), and in latent-grid overlap tiles, against the
+    oracle at the bf16 bar."""
+    spec = vae_synth.WORKLOADS[name]
+    if mode == "overlap":
+        tiles = (spec["overlap_tile"], spec["overlap_stride"])
+        got = host(_encode(v, name, operands, tiles=tiles))
+        ref = _oracle(name, tiles)
+    else:
+        patches = None if mode == "untiled" else spec["patch_grid"]
+        got = host(_encode(v, name, operands, patches=patches,
+                           launch="per_patch" if mode == "per_patch" else "merged"))
+        ref = _oracle(name)
+    assert got.shape == ref.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)

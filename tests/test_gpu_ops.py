@@ -212,6 +212,92 @@ def test_conv3d_split_k(v, case):
         np.testing.assert_allclose(gm[..., 1], 1 / np.sqrt(m2 / cnt + 1e-6), rtol=1e-5)
 
 
+# Strided causal convs: (N, T, H, W), Cin, Cout, strides, pad, in dtype, out dtype, weights
+# ("packed": the matrix-core kernel, "std": the direct kernel), residual dtype (None: none), box
+STRIDED_CASES = [
+    ((1, 5, 16, 24), 64, 128, (2, 2, 2), "around", "bf16", "f32", "packed", "f32", None),
+    ((1, 4, 18, 14), 32, 64, (1, 2, 2), "after", "bf16", "bf16", "packed", None, None),
+    ((2, 3, 9, 11), 64, 32, (2, 1, 1), "around", "f16", "f16", "packed", None, None),
+    ((1, 7, 20, 20), 128, 256, (2, 2, 2), "around", "bf16", "f32", "packed", None,
+     (1, 4, 2, 10, 0, 6)),
+    ((1, 6, 16, 16), 64, 128, (2, 2, 2), "after", "bf16", "bf16", "packed", "f32", None),
+    ((1, 4, 12, 12), 32, 48, (1, 1, 1), "around", "bf16", "f32", "packed", None, None),
+    ((1, 3, 8, 10), 48, 20, (2, 2, 2), "after", "f32", "f32", "std", None, None),
+    ((1, 4, 7, 9), 16, 24, (2, 2, 2), "around", "bf16", "bf16", "std", "bf16", None),
+]
+
+
+@pytest.mark.parametrize("case", STRIDED_CASES)
+def test_conv3d_strided_matches_oracle(v, case):
+    """vae_conv3d_causal_strided against oracle.strided_causal_conv3d (an fp32 x is compared
+    after its rounding to the bf16 operand on the matrix cores, unrounded on the direct path);
+    nothing outside the box is written, and the result is deterministic."""
+    import torch
+    (n, t, h, w), cin, cout, stride, pad, idt, odt, wk, rdt, bx = case
+    seed = 50 + STRIDED_CASES.index(case)
+    x, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", seed)
+    if idt == "f32":
+        x = x + ndhwc(vae_synth.normal((n, cin, t, h, w), [15, cin], scale=1e-3))
+    elif idt == "f16":
+        x = round_f16(x + ndhwc(vae_synth.normal((n, cin, t, h, w), [15, cin], scale=1e-3)))
+    pads = {"around": ((1, 1), (1, 1)), "after": ((0, 1), (0, 1))}[pad]
+    ref = oracle.strided_causal_conv3d(x, wt, b, stride, pads)
+    yshape = ref.shape
+    r = None
+    if rdt:
+        r = ndhwc(vae_synth.normal((yshape[0], cout) + yshape[1:4], [16, seed], dtype="bf16"))
+        ref = ref + r
+    xd = dev(x, idt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    flags = 0
+    if wk == "packed":
+        if idt == "f16":
+            wd, flags = v.vae_conv_weight_pack_f16(wd), v.VAE_CONV_PACKED_F16_WEIGHTS
+        else:
+            wd, flags = v.vae_conv_weight_pack(wd), v.VAE_CONV_PACKED_WEIGHTS
+        wd = wd.view(torch.bfloat16)
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, rdt) if rdt else None
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[odt]
+    ys = []
+    for _ in range(2):
+        y = torch.full(yshape, 7.0, device="cuda", dtype=tdt)
+        v.vae_conv3d_causal_strided(xd, wd, bd, rd, y, stride, pad, bx, flags)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    got = host(ys[0])
+    bx = bx or (0, yshape[1], 0, yshape[2], 0, yshape[3])
+    sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
+    mask = np.zeros(got.shape, bool)
+    mask[sl] = True
+    assert np.all(got[~mask] == 7.0), "wrote outside the box"
+    g, rf = got[sl], ref[sl]
+    if odt == "f32":
+        assert rel_max_abs(g, rf) <= 1e-4
+    else:
+        bound = bf16_round_bound(rf) if odt == "bf16" else f16_round_bound(rf)
+        assert np.all(np.abs(g - rf) <= bound + 1e-4 * np.abs(rf).max())
+
+
+def test_conv3d_strided_argument_rules(v):
+    import torch
+    x = torch.zeros((1, 5, 8, 8, 32), device="cuda", dtype=torch.bfloat16)
+    w = torch.zeros((64, 3, 3, 3, 32), device="cuda", dtype=torch.bfloat16)
+    y = torch.zeros((1, 3, 4, 4, 64), device="cuda", dtype=torch.bfloat16)
+    v.vae_conv3d_causal_strided(x, w, None, None, y, (2, 2, 2), "around")
+    with pytest.raises(v.VaeError) as e:           # wrong output extent
+        v.vae_conv3d_causal_strided(x, w, None, None, y[:, :2].contiguous(), (2, 2, 2), "around")
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    with pytest.raises(v.VaeError) as e:           # packed weights off the matrix-core rules
+        v.vae_conv3d_causal_strided(x.float(), w, None, None, y.float(), (2, 2, 2), "around",
+                                    flags=v.VAE_CONV_PACKED_WEIGHTS)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    with pytest.raises(v.VaeError) as e:           # stride 0
+        v.vae_conv3d_causal_strided(x, w, None, None, y, (0, 2, 2), "around")
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+
+
 CONV_GN_CASES = [
     # (N, T, H, W), Cin, Cout, groups, in dtype, out dtype, residual, box
     ((1, 3, 9, 17), 32, 128, 32, "bf16", "f32", False, None),            # 4 channels per group

@@ -21,12 +21,15 @@ VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2
 VAE_CONV_SPLIT_K = 8
 VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
-VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN, VAE_OP_S2D = 6, 7, 8, 9
+VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN, VAE_OP_S2D, VAE_OP_CONV_DOWN = 6, 7, 8, 9, 10
+VAE_PAD_AROUND, VAE_PAD_AFTER = 0, 1
+PAD_CODES = {"around": VAE_PAD_AROUND, "after": VAE_PAD_AFTER}
 VAE_KIND_NAMES = {1: "conv", 2: "gn", 3: "upsample", 4: "merge", 5: "other", 6: "rms", 7: "attn"}
 
 # Every symbol include/vae.h declares.
 EXPORTS = (
     "vae_last_error", "vae_last_error_info", "vae_version", "vae_conv3d_causal",
+    "vae_conv3d_causal_strided",
     "vae_conv3d_causal_fused_workspace", "vae_conv3d_causal_fused", "vae_conv_weight_pack_size", "vae_conv_weight_pack", "vae_conv_weight_pack_f16",
     "vae_decoder_packed_weight_size",
     "vae_decoder_pack_weights",
@@ -85,7 +88,7 @@ class vae_tile_t(ctypes.Structure):
 
 class vae_layer_desc_t(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32)
-                for k in ("op", "cin", "cout", "st", "sh", "sw", "f32_out", "no_split")]
+                for k in ("op", "cin", "cout", "st", "sh", "sw", "f32_out", "no_split", "pad")]
 
 
 class vae_decoder_spec_t(ctypes.Structure):
@@ -118,6 +121,7 @@ def _load():
         "vae_last_error_info": ([ctypes.POINTER(vae_error_info_t)], I32),
         "vae_version": ([], I32),
         "vae_conv3d_causal": ([T, P, I32, P, T, T, B, I32, P], I32),
+        "vae_conv3d_causal_strided": ([T, P, I32, P, T, T, B, I32, I32, I32, I32, I32, P], I32),
         "vae_conv3d_causal_fused_workspace": ([ctypes.POINTER(vae_conv_fused_t),
                                                ctypes.POINTER(SZ)], I32),
         "vae_conv3d_causal_fused": ([ctypes.POINTER(vae_conv_fused_t), P], I32),
@@ -236,6 +240,22 @@ def _workspace(nbytes, device):
 # ------------------------------------------------------------------------------------------------
 # Entry points (names as in include/vae.h)
 # ------------------------------------------------------------------------------------------------
+
+def vae_conv3d_causal_strided(x, weight, bias, residual, y, stride, pad="around", out_box=None,
+                              flags=0, weight_dtype=None, stream=None):
+    """Strided causal Conv3d; weight is [Cout, 3, 3, 3, Cin] (bf16 or fp32), or a packed copy
+    (uint8 buffer, with flags VAE_CONV_PACKED_WEIGHTS / VAE_CONV_PACKED_F16_WEIGHTS; its dtype is
+    then bf16). pad: "around" or "after"."""
+    xd, yd = tensor_desc(x), tensor_desc(y)
+    rd = tensor_desc(residual) if residual is not None else None
+    wdt = weight_dtype if weight_dtype is not None else (
+        VAE_DTYPE_BF16 if flags else _dtype_code(weight))
+    st, sh, sw = (int(s) for s in stride)
+    _check(LIB.vae_conv3d_causal_strided(ctypes.byref(xd), _ptr(weight), wdt, _ptr(bias),
+                                         _ref(rd), ctypes.byref(yd), _ref(box(out_box)), st, sh,
+                                         sw, PAD_CODES[pad], int(flags), _stream(stream)))
+    return y
+
 
 def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, stream=None):
     """Causal Conv3d; weight is a [Cout, 3, 3, 3, Cin] device tensor (bf16 or fp32)."""
@@ -474,6 +494,10 @@ def layer_descs(plan):
             out.append(vae_layer_desc_t(VAE_OP_D2S, 0, 0, op["st"], op["sh"], op["sw"], 0, 0))
         elif k == "nearest":
             out.append(vae_layer_desc_t(VAE_OP_NEAREST, 0, 0, 1, op["sh"], op["sw"], 0, 0))
+        elif k == "conv_down":
+            out.append(vae_layer_desc_t(VAE_OP_CONV_DOWN, op["cin"], op["cout"], op["st"],
+                                        op["sh"], op["sw"], int(op.get("f32_out", False)), 0,
+                                        PAD_CODES[op["pad"]]))
         else:
             raise ValueError(k)
     return out

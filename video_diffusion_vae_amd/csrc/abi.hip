@@ -567,6 +567,60 @@ VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_s
     return launch_gn_stats(y, bl, a.gn_groups, part, nullptr, a.gn_mean_rstd, a.gn_eps, s);
 }
 
+VAE_API vae_status_t vae_conv3d_causal_strided(const vae_tensor_t* x, const void* weight,
+                                               int32_t weight_dtype, const float* bias,
+                                               const vae_tensor_t* residual, vae_tensor_t* y,
+                                               const vae_box_t* out_box, int32_t st, int32_t sh,
+                                               int32_t sw, int32_t pad, int32_t flags,
+                                               vae_stream_t stream) {
+    clear_error();
+    VAE_TRY(check_tensor(x, "x"));
+    VAE_TRY(check_tensor(y, "y"));
+    if (!weight) return fail(VAE_ERR_INVALID_ARG, "weight is NULL");
+    if (weight_dtype != VAE_DTYPE_BF16 && weight_dtype != VAE_DTYPE_F32)
+        return fail(VAE_ERR_INVALID_ARG, "unknown weight dtype");
+    if (reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+        return fail(VAE_ERR_INVALID_ARG, "weight must be 16-byte aligned");
+    if (st < 1 || sh < 1 || sw < 1) return fail(VAE_ERR_INVALID_ARG, "strides must be >= 1");
+    if (pad != VAE_PAD_AROUND && pad != VAE_PAD_AFTER)
+        return fail(VAE_ERR_INVALID_ARG, "pad must be VAE_PAD_AROUND or VAE_PAD_AFTER");
+    const int32_t packs = VAE_CONV_PACKED_WEIGHTS | VAE_CONV_PACKED_F16_WEIGHTS;
+    if (flags & ~packs) return fail(VAE_ERR_INVALID_ARG, "unknown flags for a strided conv");
+    if ((flags & packs) == packs) return fail(VAE_ERR_INVALID_ARG, "give one packed-weight flag");
+    const int32_t before = pad == VAE_PAD_AROUND ? 1 : 0;
+    const int64_t ot = (x->t - 1) / st + 1;
+    const int64_t oh = (x->h + before + 1 - 3) / sh + 1;
+    const int64_t ow = (x->w + before + 1 - 3) / sw + 1;
+    if (x->h + before + 1 < 3 || x->w + before + 1 < 3)
+        return fail(VAE_ERR_INVALID_ARG, "strided conv: the padded image is narrower than 3");
+    if (y->n != x->n || y->t != ot || y->h != oh || y->w != ow)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "y must be [N, (T-1)/st+1, (H+pt+pb-3)/sh+1, (W+pl+pr-3)/sw+1, Cout]");
+    if (residual) {
+        VAE_TRY(check_tensor(residual, "residual"));
+        if (residual->n != y->n || residual->t != y->t || residual->h != y->h ||
+            residual->w != y->w || residual->c != y->c ||
+            (residual->dtype != y->dtype && residual->dtype != VAE_DTYPE_F32))
+            return fail(VAE_ERR_INVALID_ARG, "residual must have y's shape, y's dtype or fp32");
+        if (overlaps(*residual, *x)) return fail(VAE_ERR_INVALID_ARG, "residual overlaps x");
+    }
+    if (overlaps(*x, *y)) return fail(VAE_ERR_INVALID_ARG, "y must not overlap x");
+    VAE_TRY(check_box(out_box, *y, "out_box"));
+    const StrideGeom g{st, sh, sw, before, before};
+    const bool mfma = conv_strided_uses_mfma(*x, y->c, weight_dtype, flags, g);
+    if ((flags & packs) && !mfma)
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "strided conv: packed weights need a bf16 or fp16 x, Cin % 32 == 0, "
+                    "Cout % 4 == 0, st and sh = sw in {1, 2}", 4, x->c, 32);
+    if (!mfma && (x->dtype == VAE_DTYPE_F16 || y->dtype == VAE_DTYPE_F16))
+        return fail(VAE_ERR_UNSUPPORTED, "strided conv: fp16 tensors need packed weights");
+    if (residual && residual->dtype != y->dtype && !mfma)
+        return fail(VAE_ERR_UNSUPPORTED, "strided conv: an fp32 residual with a 2-byte y needs "
+                                         "the matrix-core path");
+    return launch_conv3d_strided(*x, weight, weight_dtype, bias, residual, *y, to_box(out_box, *y),
+                                 g, flags, as_stream(stream));
+}
+
 VAE_API vae_status_t vae_conv_weight_pack_size(int32_t cout, int32_t cin, size_t* bytes) {
     clear_error();
     if (!bytes) return fail(VAE_ERR_INVALID_ARG, "bytes is NULL");

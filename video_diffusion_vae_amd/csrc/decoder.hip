@@ -63,7 +63,8 @@ bool conv_f16(int32_t dtype, int32_t act_dtype, int32_t flags, const vae_layer_d
         act_dtype != VAE_DTYPE_F32 || i < 1 || i >= n)
         return false;
     const vae_layer_desc_t& l = layers[i];
-    if (l.op != VAE_OP_CONV || l.cin % 32 || l.cout % 4) return false;
+    if ((l.op != VAE_OP_CONV && l.op != VAE_OP_CONV_DOWN) || l.cin % 32 || l.cout % 4)
+        return false;
     int j = i - 1;
     while (j > 0 && layers[j].op == VAE_OP_NEAREST) --j;
     if (j > 0 && layers[j].op == VAE_OP_D2S) --j;       // the d2s its producing conv writes
@@ -82,14 +83,14 @@ bool conv_out_f16(int32_t dtype, int32_t act_dtype, int32_t flags,
     int j = i + 1;
     if (j < n && layers[j].op == VAE_OP_D2S) ++j;
     while (j < n && layers[j].op == VAE_OP_NEAREST) ++j;
-    return j < n && layers[j].op == VAE_OP_CONV &&
+    return j < n && (layers[j].op == VAE_OP_CONV || layers[j].op == VAE_OP_CONV_DOWN) &&
            conv_f16(dtype, act_dtype, flags, layers, n, j);
 }
-// The conv that layer i feeds, past any NEAREST ops, or -1.
+// The conv (stride 1 or strided) that layer i feeds, past any NEAREST ops, or -1.
 int fed_conv(const vae_layer_desc_t* layers, int n, int i) {
     int j = i + 1;
     while (j < n && layers[j].op == VAE_OP_NEAREST) ++j;
-    return j < n && layers[j].op == VAE_OP_CONV ? j : -1;
+    return j < n && (layers[j].op == VAE_OP_CONV || layers[j].op == VAE_OP_CONV_DOWN) ? j : -1;
 }
 bool conv_f16(const vae_decoder& d, int i) {
     return conv_f16(d.dtype, d.act_dtype, d.flags, d.layers.data(), (int)d.layers.size(), i);
@@ -129,8 +130,8 @@ int32_t res_out_dtype(const vae_decoder& d, size_t i) {
     if (j >= 0 && conv_f16(d, j)) return VAE_DTYPE_F16;
     if (i + 1 < d.layers.size() && d.dtype == VAE_DTYPE_BF16 && d.layers[i].cin % 32 == 0) {
         const vae_layer_desc_t& n = d.layers[i + 1];
-        if (n.op == VAE_OP_CONV && !conv_splits(d.flags, d.layers.data(), (int)d.layers.size(),
-                                                (int)i + 1) &&
+        if ((n.op == VAE_OP_CONV || n.op == VAE_OP_CONV_DOWN) &&
+            !conv_splits(d.flags, d.layers.data(), (int)d.layers.size(), (int)i + 1) &&
             n.cin % 32 == 0 && n.cout % 4 == 0)
             return VAE_DTYPE_BF16;
     }
@@ -155,6 +156,7 @@ bool gn_follows(const vae_decoder& d, size_t i) {
 int ptrs_for(const vae_layer_desc_t& l) {
     switch (l.op) {
         case VAE_OP_CONV: return 2;
+        case VAE_OP_CONV_DOWN: return 2;
         case VAE_OP_RES: return 8;
         case VAE_OP_GN_SILU: return 2;
         case VAE_OP_RES_RMS: return 8;
@@ -206,6 +208,17 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
                 s.w *= l.sw;
                 sh *= l.sh;
                 sw *= l.sw;
+                break;
+            case VAE_OP_CONV_DOWN:
+                if (s.h % l.sh || s.w % l.sw)
+                    return fail(VAE_ERR_INVALID_ARG,
+                                "a strided conv's input rows and columns must be whole strides",
+                                s.h % l.sh ? 2 : 3, s.h % l.sh ? s.h : s.w, s.h % l.sh ? l.sh : l.sw);
+                s.c = l.cout;
+                s.dtype = l.f32_out ? VAE_DTYPE_F32 : d.act_dtype;
+                s.t = (s.t - 1) / l.st + 1;
+                s.h /= l.sh;   // (H + pt + pb - 3) / sh + 1 for whole strides and one row of padding
+                s.w /= l.sw;
                 break;
             case VAE_OP_S2D:
                 {
@@ -273,7 +286,7 @@ bool plan_folds(const vae_decoder& d, int32_t* ft = nullptr, int32_t* fh = nullp
     int32_t t = 1, h = 1, w = 1;
     bool any = false;
     for (const vae_layer_desc_t& l : d.layers)
-        if (l.op == VAE_OP_S2D) {
+        if (l.op == VAE_OP_S2D || l.op == VAE_OP_CONV_DOWN) {
             any = true;
             t *= l.st;
             h *= l.sh;
@@ -400,7 +413,22 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
             ch *= l.sh;
             cw *= l.sw;
         }
-        if (l.op == VAE_OP_S2D) {
+        if (l.op == VAE_OP_CONV_DOWN) {
+            // y's grid folds by the strides; its epilogue may gather the next norm's statistics
+            const vae_tensor_t y = tensor_of(nullptr, s);
+            BoxList bl;
+            if (per_patch) {
+                bl = scaled_boxes(boxes, s.t, ch, cw, fh * l.sh, fw * l.sw, &exact);
+            } else {
+                bl.n = 1;
+                bl.b[0] = whole_box(y);
+            }
+            int64_t slots = 0;
+            if (next_gn)
+                for (int b = 0; b < bl.n; ++b) slots += conv_strided_gn_slots(y, bl.b[b], d.groups);
+            r->gn = std::max<int64_t>(r->gn, s.n * d.groups * slots * 3 * (int64_t)sizeof(double));
+        }
+        if (l.op == VAE_OP_S2D || l.op == VAE_OP_CONV_DOWN) {
             fh *= l.sh;
             fw *= l.sw;
         }
@@ -605,6 +633,60 @@ struct Runner {
         return VAE_OK;
     }
 
+    // A strided conv (an encoder's downsampler) into y, over y's whole grid or per patch box (`bl`,
+    // boxes of y); with `gn_next` its epilogue gathers the next GroupNorm's statistics.
+    vae_status_t conv_down(const vae_tensor_t& x, size_t wi, const vae_tensor_t& y, int layer,
+                           const vae_layer_desc_t& l, bool gn_next, const BoxList& bl) {
+        const void* w = d->ptrs[wi];
+        int32_t cf = 0;
+        if (d->packed[wi]) {
+            w = d->packed[wi];
+            cf = x.dtype == VAE_DTYPE_F16 ? VAE_CONV_PACKED_F16_WEIGHTS : VAE_CONV_PACKED_WEIGHTS;
+        }
+        const int32_t before = l.pad == VAE_PAD_AROUND ? 1 : 0;
+        const StrideGeom g{l.st, l.sh, l.sw, before, before};
+        BoxList launches;
+        if (per_patch) {
+            launches = bl;
+        } else {
+            launches.n = 1;
+            launches.b[0] = whole_box(y);
+        }
+        const bool fuse = gn_next && conv_strided_uses_mfma(x, y.c, d->dtype, cf, g);
+        int64_t slots[kMaxBoxes], total = 0;
+        for (int i = 0; i < launches.n; ++i) {
+            const Box& b = launches.b[i];
+            if (b.t0 < 0 || b.h0 < 0 || b.w0 < 0 || b.t1 > y.t || b.h1 > y.h || b.w1 > y.w ||
+                b.volume() <= 0)
+                return fail(VAE_ERR_INVALID_ARG, "strided conv patch box outside the activation");
+            slots[i] = fuse ? conv_strided_gn_slots(y, b, d->groups) : 0;
+            total += slots[i];
+        }
+        double* part = reinterpret_cast<double*>(ws + L.gn);
+        int64_t slot0 = 0;
+        for (int i = 0; i < launches.n; ++i) {
+            const Box& b = launches.b[i];
+            ConvFuse fz{total > 0 ? part : nullptr, d->groups, 1, 1, 1};
+            fz.slot0 = slot0;
+            fz.slot_stride = total;
+            slot0 += slots[i];
+            VAE_TRY(launch_conv3d_strided(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]),
+                                          nullptr, y, b, g, cf, s, &fz));
+            const double pos = (double)b.volume() * y.n;
+            const double flops = 2.0 * 27.0 * (double)x.c * (double)y.c * pos;
+            const double bytes = pos * (double)l.st * l.sh * l.sw * x.c * elem_size(x.dtype) +
+                                 pos * (double)y.c * elem_size(y.dtype);
+            VAE_TRY(mark_patch(i, VAE_KIND_CONV, layer, flops, bytes));
+        }
+        if (total > 0) {
+            VAE_TRY(launch_gn_finalize_slots(part, total, (int32_t)y.n, d->groups, d->eps,
+                                             reinterpret_cast<float*>(ws + L.mr), s));
+            if (per_patch) VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
+            stats_ready = true;
+        }
+        return VAE_OK;
+    }
+
     // A standalone depth-to-space or nearest upsampling: over the whole tensor, or per patch box
     // (boxes in x's grid).
     vae_status_t upsample(const vae_tensor_t& x, const BoxList& bl, int mode, int32_t st,
@@ -772,6 +854,16 @@ struct Runner {
                 near_lsw += log2_of(l.sw);
                 ch *= l.sh;
                 cw *= l.sw;
+            } else if (l.op == VAE_OP_CONV_DOWN) {
+                const int nb = free_buf(cur_buf, -1);
+                vae_tensor_t y = last ? final_out : buf(nb, os);
+                fh *= l.sh;   // y's grid
+                fw *= l.sw;
+                VAE_TRY(conv_down(cur, p, y, layer, l, gn_follows(*d, li),
+                                  scaled_boxes(boxes, y.t, ch, cw, fh, fw)));
+                p += 2;
+                cur = y;
+                cur_buf = last ? -2 : nb;
             } else if (l.op == VAE_OP_S2D) {
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = last ? final_out : buf(nb, os);
@@ -860,7 +952,8 @@ void for_each_conv(const vae_decoder& d, F fn) {
     size_t p = 0;
     for (size_t i = 0; i < d.layers.size(); ++i) {
         const vae_layer_desc_t& l = d.layers[i];
-        if (l.op == VAE_OP_CONV) fn(p, l.cin, l.cout, conv_f16(d, (int)i));
+        if (l.op == VAE_OP_CONV || l.op == VAE_OP_CONV_DOWN)
+            fn(p, l.cin, l.cout, conv_f16(d, (int)i));
         if (l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) {
             fn(p + 2, l.cin, l.cin, false);
             fn(p + 6, l.cin, l.cin, false);
@@ -966,6 +1059,20 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
                 if (l.sh < 1 || l.sw < 1)
                     return fail(VAE_ERR_INVALID_ARG, "nearest factors must be >= 1");
                 break;
+            case VAE_OP_CONV_DOWN:
+                if (l.cin != c || l.cout < 1)
+                    return fail(VAE_ERR_INVALID_ARG, "conv channels do not chain", 4, l.cin, -1, c);
+                if (l.st < 1 || l.st > 2 || l.sh < 1 || l.sh > 2 || l.sh != l.sw)
+                    return fail(VAE_ERR_UNSUPPORTED, "a strided conv in a plan takes strides "
+                                                     "st, sh = sw of 1 or 2");
+                if (l.pad != VAE_PAD_AROUND && l.pad != VAE_PAD_AFTER)
+                    return fail(VAE_ERR_INVALID_ARG, "unknown strided conv padding");
+                if (l.pad == VAE_PAD_AFTER && l.sh != 2)
+                    return fail(VAE_ERR_UNSUPPORTED, "padding after the image goes with stride 2 "
+                                                     "(it would shrink a stride-1 axis)");
+                c = l.cout;
+                act = l.f32_out ? VAE_DTYPE_F32 : spec->act_dtype;
+                break;
             case VAE_OP_S2D:
                 if (l.st < 1 || l.sh < 1 || l.sw < 1)
                     return fail(VAE_ERR_INVALID_ARG, "s2d factors must be >= 1");
@@ -984,7 +1091,7 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
     int p = 0;
     for (int i = 0; i < spec->n_layers; ++i) {
         const vae_layer_desc_t& l = spec->layers[i];
-        if (l.op == VAE_OP_CONV && !params[p])
+        if ((l.op == VAE_OP_CONV || l.op == VAE_OP_CONV_DOWN) && !params[p])
             return fail(VAE_ERR_INVALID_ARG, "conv weight pointer is NULL");
         if ((l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) && (!params[p + 2] || !params[p + 6]))
             return fail(VAE_ERR_INVALID_ARG, "res conv weight pointer is NULL");

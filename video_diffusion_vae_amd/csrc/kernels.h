@@ -61,6 +61,27 @@ int64_t packed_weight_elems(int64_t cout, int64_t cin);
 vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
                                  hipStream_t stream, bool to_f16 = false);
 
+// ---- strided conv (an encoder's bare downsampler) ----
+// Strides (st, sh, sw) and the zero rows / columns before the image (pt top, pl left); the ones
+// after it follow from y's extents.
+struct StrideGeom {
+    int32_t st, sh, sw, pt, pl;
+};
+// Whether the strided conv runs on the matrix cores: bf16 weights fragment-packed (bf16 or, for
+// an fp16 x, fp16), a 2-byte x, Cin % 32 == 0, Cout % 4 == 0, strides 1 or 2 with sh == sw.
+bool conv_strided_uses_mfma(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype,
+                            int32_t flags, const StrideGeom& g);
+// Slots of the GroupNorm partials its epilogue gathers over `box` (of y), per (sample, group);
+// 0 when the channel grouping does not allow it.
+int64_t conv_strided_gn_slots(const vae_tensor_t& y, const Box& box, int32_t groups);
+// `fz` may carry gn_ws (statistics of y as stored; matrix-core path only); its other fields are
+// ignored.
+vae_status_t launch_conv3d_strided(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
+                                   const float* bias, const vae_tensor_t* residual,
+                                   const vae_tensor_t& y, const Box& box, const StrideGeom& g,
+                                   int32_t flags, hipStream_t stream,
+                                   const ConvFuse* fz = nullptr);
+
 // ---- group norm ----
 // Workspace: per-block partials of every box, fp64 [blocks][N][G][3].
 size_t gn_stats_workspace(const vae_tensor_t& x, const BoxList& boxes, int32_t groups);
