@@ -18,9 +18,11 @@
  *    GroupNorm output, and by vae_upsample (a copy). It is the operand hand-off of convs whose
  *    input needs more than bf16's 8 significant bits (see vae_conv3d_causal).
  *  - Ownership: the caller owns every buffer. Device buffers are passed as raw device pointers;
- *    the library never allocates or frees device memory and never synchronises the stream. It
- *    keeps no pointer after a call returns, except the weight pointers held by a decoder object,
- *    which must outlive that object.
+ *    the library never allocates or frees device memory. It never synchronises the stream,
+ *    except in the setup calls that read a result back (fp16 weight packing checks its range;
+ *    vae_decode_status and vae_decoder_get_timing read results), each saying so. It keeps no
+ *    pointer after a call returns, except the weight pointers held by a decoder object, which
+ *    must outlive that object.
  *  - Streams: every device call is asynchronous and enqueued on `stream` (a hipStream_t passed as
  *    void*, NULL = the default stream). vae_tile_split is host-only and synchronous.
  *  - Errors: every call returns a vae_status_t. On failure nothing is enqueued, and
@@ -219,7 +221,11 @@ VAE_API vae_status_t vae_conv_weight_pack(const void* weight, int32_t cout, int3
                                           void* packed, vae_stream_t stream);
 /* The same layout with every bf16 weight converted to fp16 after scaling by 2^10 (exact for
  * |w| < 64; magnitudes below 2^-24 lose bits as fp16 subnormals). It is the weight operand of an
- * fp16 x (VAE_CONV_PACKED_F16_WEIGHTS). Same size as vae_conv_weight_pack_size. */
+ * fp16 x (VAE_CONV_PACKED_F16_WEIGHTS). Same size as vae_conv_weight_pack_size. The call checks
+ * the range: a weight of magnitude 64 or more (or not finite) would overflow fp16, and the call
+ * returns VAE_ERR_UNSUPPORTED (the packed buffer is then not to be used). The check reads a
+ * device flag back, so this setup call synchronises `stream`; concurrent checked packs in one
+ * process are serialised. */
 VAE_API vae_status_t vae_conv_weight_pack_f16(const void* weight, int32_t cout, int32_t cin,
                                               void* packed, vae_stream_t stream);
 
@@ -566,7 +572,11 @@ VAE_API void vae_decoder_destroy(vae_decoder_t* dec);
 /* Optional fragment-packed weights for the decoder's MFMA convs. The caller supplies a device
  * buffer of vae_decoder_packed_weight_size bytes, which must outlive the decoder. The pack is
  * enqueued on `stream`, and later decodes read the packed copies instead of the standard ones.
- * The results are identical; the packed copies are faster to load. */
+ * The results are identical; the packed copies are faster to load. The convs that take fp16
+ * operands (VAE_DECODE_F16_OPERANDS) are packed as vae_conv_weight_pack_f16 does, with its range
+ * check: a weight of magnitude 64 or more there is refused with VAE_ERR_UNSUPPORTED,
+ * info.extent = the conv's index in plan order (counting every conv, residual blocks' two each),
+ * and the decoder keeps its standard weights. With such convs the call synchronises `stream`. */
 VAE_API vae_status_t vae_decoder_packed_weight_size(const vae_decoder_t* dec, size_t* bytes);
 VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, size_t bytes,
                                               vae_stream_t stream);
@@ -613,6 +623,17 @@ VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,
 VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec, const vae_tensor_t* latent,
                                       const vae_tiling_desc_t* desc, vae_tensor_t* out, void* ws,
                                       size_t ws_bytes, vae_stream_t stream);
+
+/* Status of the most recent vae_decode_tiled call that used `ws` (same decoder and tiling desc):
+ * *flags = VAE_STATUS_NONFINITE when a GroupNorm's or RMS norm's statistics were not finite,
+ * i.e. an activation became inf or NaN. The usual cause is a value past fp16's 65504 at an fp16
+ * operand hand-off (VAE_DECODE_F16_OPERANDS): the output is then not to be trusted. 0 otherwise.
+ * Each decode clears the word it sets (with a kernel, so a captured decode keeps the behaviour);
+ * this call synchronises `stream` and reads the word back. */
+enum { VAE_STATUS_NONFINITE = 1 };
+VAE_API vae_status_t vae_decode_status(const vae_decoder_t* dec, const vae_tiling_desc_t* desc,
+                                       const void* ws, size_t ws_bytes, int32_t* flags,
+                                       vae_stream_t stream);
 
 /* Per-op GPU timing of the most recent vae_decode_tiled call (events recorded on its stream).
  * Enabled with vae_decoder_set_timing(dec, 1); collecting waits for the last recorded event. */

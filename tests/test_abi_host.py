@@ -443,3 +443,22 @@ def test_strided_conv_plan_rules(v):
         with pytest.raises(v.VaeError) as e:
             v.Decoder(v.VAE_DTYPE_BF16, 32, 32, 1e-6, plan(**bad), ptrs)
         assert e.value.status == status, bad
+
+
+def test_decode_status_argument_checks(v):
+    """vae_decode_status checks its arguments on the host before touching the device."""
+    import vae_synth
+    spec = vae_synth.LTX2_TINY
+    n_ptr = sum({"conv": 2, "res": 8, "gn_silu": 2}.get(op["op"], 0) for op in spec["layers"])
+    dec = v.Decoder(v.VAE_DTYPE_BF16, 128, 32, 1e-6, spec["layers"],
+                    [_FakePtr(i) for i in range(n_ptr)])
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, (1, 2, 4, 6, 128), spec["scale"])
+    need = dec.workspace_size(desc)
+    flags = ctypes.c_int32()
+    assert v.LIB.vae_decode_status(dec._h, ctypes.byref(desc), None, need, ctypes.byref(flags),
+                                   None) == v.VAE_ERR_INVALID_ARG
+    assert v.LIB.vae_decode_status(dec._h, ctypes.byref(desc), ctypes.c_void_p(1 << 40),
+                                   need - 1, ctypes.byref(flags), None) == v.VAE_ERR_WORKSPACE
+    assert v.LIB.vae_decode_status(dec._h, ctypes.byref(desc), ctypes.c_void_p(1 << 40), need,
+                                   None, None) == v.VAE_ERR_INVALID_ARG
+    dec.close()

@@ -370,3 +370,66 @@ def test_per_patch_timing_records(v):
     assert abs(sum(r["flops"] for r in conv) - whole) <= 1e-9 * whole
     per = [sum(r["flops"] for r in conv if r["tile"] == t) for t in (0, 1)]
     assert per[0] == per[1]                        # two equal bands of 3 latent columns
+
+
+# ------------------------------------------------------------------------------------------------
+# The fp16 operand hand-off's range guards
+# ------------------------------------------------------------------------------------------------
+
+def test_f16_weight_pack_refuses_weights_past_the_scale(v):
+    """fp16-packed weights are w * 2^10: a weight of magnitude 64 would overflow fp16 and is
+    refused; 63.75 (65280 after the scale) packs, exactly; the bf16 packing takes both."""
+    import torch
+    w = torch.zeros((32, 3, 3, 3, 32), dtype=torch.bfloat16, device="cuda")
+    w[3, 1, 2, 0, 7] = 63.75
+    p = v.vae_conv_weight_pack_f16(w)
+    torch.cuda.synchronize()
+    assert float(p.view(torch.float16).abs().max()) == 63.75 * 1024
+    w[5, 0, 0, 1, 9] = -64.0
+    with pytest.raises(v.VaeError) as e:
+        v.vae_conv_weight_pack_f16(w)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    v.vae_conv_weight_pack(w)                     # bf16 operands have no such limit
+    w[5, 0, 0, 1, 9] = float("inf")
+    with pytest.raises(v.VaeError):
+        v.vae_conv_weight_pack_f16(w)
+
+
+def test_decoder_pack_names_the_conv_past_the_fp16_range(v):
+    """A large weight in a conv with fp16 operands (the first upsampling conv, conv 3 in plan
+    order) is refused at packing with that conv's index; the same weight in conv_in (bf16
+    operands) is accepted."""
+    import copy
+    params = copy.deepcopy(params_of("ltx2_tiny"))
+    conv_params = [p for p in params if p["kind"] == "conv"]
+    conv_params[0]["w"][0, 0, 0, 0, 0] = 100.0
+    dec = v.upload_decoder(vae_synth.LTX2_TINY, params)   # packs: accepted
+    dec.close()
+    conv_params[3]["w"][1, 2, 1, 1, 0] = 100.0
+    with pytest.raises(v.VaeError) as e:
+        v.upload_decoder(vae_synth.LTX2_TINY, params)
+    assert e.value.status == v.VAE_ERR_UNSUPPORTED and e.value.info["extent"] == 3
+
+
+@pytest.mark.parametrize("name", ["ltx2_tiny", "wan_tiny"])
+def test_decode_reports_activations_past_fp16(v, name):
+    """A latent scaled by 1e6 drives the residual stream past 65504, where it is handed to an
+    fp16-operand conv: the decode runs to the end (no fault), its output holds non-finite
+    values, and vae_decode_status reports it. The unscaled decode reports nothing."""
+    import torch
+    spec = vae_synth.WORKLOADS[name]
+    z = v.pad_latent(ndhwc(vae_synth.latent(spec)), spec)
+    p = vae_synth.decoder_params(spec)
+    dec = v.upload_decoder(spec, p)
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=(1, 2))
+    ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(oracle.output_shape(spec, ndhwc(vae_synth.latent(spec)).shape),
+                      dtype=torch.float32, device="cuda")
+    flags = []
+    for scale in (1.0, 1e6, 1.0):
+        dec.vae_decode_tiled(dev(z * scale, "bf16"), desc, out, ws)
+        flags.append(dec.status(desc, ws))
+        finite = bool(torch.isfinite(out).all())
+        assert finite == (scale == 1.0), (scale, finite)
+    dec.close()
+    assert flags == [0, v.VAE_STATUS_NONFINITE, 0]

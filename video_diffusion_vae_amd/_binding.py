@@ -16,6 +16,7 @@ VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DTYPE_F16 = 1, 2, 3
 VAE_UPSAMPLE_NEAREST, VAE_UPSAMPLE_D2S = 1, 2
 VAE_TILING_PATCH_HALO, VAE_TILING_OVERLAP_BLEND = 1, 2
 VAE_LAUNCH_MERGED, VAE_LAUNCH_PER_PATCH = 0, 1
+VAE_STATUS_NONFINITE = 1
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
 VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
 VAE_CONV_SPLIT_K = 8
@@ -39,6 +40,7 @@ EXPORTS = (
     "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample", "vae_space_to_depth",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
     "vae_decoder_set_launch", "vae_decode_workspace_size", "vae_decode_tiled",
+    "vae_decode_status",
     "vae_decoder_set_timing",
     "vae_decoder_get_timing",
 )
@@ -150,6 +152,7 @@ def _load():
         "vae_decoder_set_launch": ([P, I32], I32),
         "vae_decode_workspace_size": ([P, D, ctypes.POINTER(SZ)], I32),
         "vae_decode_tiled": ([P, T, D, T, P, SZ, P], I32),
+        "vae_decode_status": ([P, D, P, SZ, ctypes.POINTER(I32), P], I32),
         "vae_decoder_set_timing": ([P, I32], I32),
         "vae_decoder_get_timing": ([P, ctypes.POINTER(vae_op_timing_t), I32,
                                     ctypes.POINTER(I32)], I32),
@@ -556,6 +559,13 @@ class Decoder:
         _check(LIB.vae_decode_tiled(self._h, ctypes.byref(ld), ctypes.byref(desc),
                                     ctypes.byref(od), _ptr(ws), ws.numel(), _stream(stream)))
         return out
+
+    def status(self, desc, ws, stream=None):
+        """Flags of the last decode through `ws` (VAE_STATUS_NONFINITE); synchronises."""
+        f = ctypes.c_int32()
+        _check(LIB.vae_decode_status(self._h, ctypes.byref(desc), _ptr(ws), ws.numel(),
+                                     ctypes.byref(f), _stream(stream)))
+        return f.value
 
     def set_timing(self, enable):
         _check(LIB.vae_decoder_set_timing(self._h, int(enable)))

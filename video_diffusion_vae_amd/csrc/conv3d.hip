@@ -4,6 +4,7 @@
 //    fp16 inputs only run there.
 //  - Otherwise a direct kernel computes one output per thread with fp32 accumulation.
 #include <algorithm>
+#include <mutex>
 
 #include "conv3d_mfma.h"
 
@@ -100,7 +101,7 @@ vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w,
                                                            uint16_t* __restrict__ p, int32_t cout,
                                                            int32_t cin, int64_t total,
-                                                           int32_t to_f16) {
+                                                           int32_t to_f16, uint32_t* status) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     const int nch = cin / kCK;
@@ -120,8 +121,25 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __res
     const int co = cot * 32 + r;
     const int ci = chunk * kCK + kk * 16 + khalf * 8 + e;
     const uint16_t b = co < cout ? w[((int64_t)co * 27 + tap) * cin + ci] : (uint16_t)0;
-    p[i] = to_f16 ? f16_bits(bf16_to_f32(b) * kF16WeightScale) : b;
+    if (to_f16) {
+        // |w| * 2^10 must stay within fp16's 65504 (|w| < 64), and w must be finite
+        const float sw = bf16_to_f32(b) * kF16WeightScale;
+        if (status && !(fabsf(sw) <= 65504.0f)) *status = 1u;
+        p[i] = f16_bits(sw);
+    } else {
+        p[i] = b;
+    }
 }
+
+__global__ void clear_word_kernel(uint32_t* word) { *word = 0u; }
+
+// The range flag of the fp16 packing, one per GPU (held until the process ends). In host code
+// `pack_range_flag` stands for the variable, not its device address: kernels get the address
+// hipGetSymbolAddress returns on that device.
+__device__ __align__(16) uint32_t pack_range_flag[4];
+constexpr int kMaxDevices = 64;
+std::mutex pack_flag_mutex;                  // also serialises the checked packs of a process
+uint32_t* pack_flag_ptr[kMaxDevices];
 
 template <typename TX, typename TW, typename TO>
 vae_status_t run_direct(const vae_tensor_t& x, const void* w, const float* bias,
@@ -194,10 +212,39 @@ int64_t packed_weight_elems(int64_t cout, int64_t cin) {
 vae_status_t launch_pack_weights(const void* w, int32_t cout, int32_t cin, void* packed,
                                  hipStream_t stream, bool to_f16) {
     const int64_t total = packed_weight_elems(cout, cin);
+    if (!to_f16) {
+        hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                           stream, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(packed),
+                           cout, cin, total, 0, (uint32_t*)nullptr);
+        VAE_HIP_CHECK(hipGetLastError());
+        return VAE_OK;
+    }
+    // fp16 packing checks the range: clear this device's flag, pack, read the flag back
+    int dev = -1;
+    VAE_HIP_CHECK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(VAE_ERR_UNSUPPORTED, "device index beyond the library's table");
+    std::lock_guard<std::mutex> lock(pack_flag_mutex);
+    if (!pack_flag_ptr[dev]) {
+        void* p = nullptr;
+        VAE_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(pack_range_flag)));
+        if (!p) return fail(VAE_ERR_HIP, "hipGetSymbolAddress returned NULL for the range flag");
+        pack_flag_ptr[dev] = static_cast<uint32_t*>(p);
+    }
+    uint32_t* flag = pack_flag_ptr[dev];
+    hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, stream, flag);
+    VAE_HIP_CHECK(hipGetLastError());
     hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
                        stream, static_cast<const uint16_t*>(w), static_cast<uint16_t*>(packed),
-                       cout, cin, total, (int32_t)to_f16);
+                       cout, cin, total, 1, flag);
     VAE_HIP_CHECK(hipGetLastError());
+    uint32_t h = 0;
+    VAE_HIP_CHECK(hipStreamSynchronize(stream));
+    VAE_HIP_CHECK(hipMemcpy(&h, flag, sizeof(h), hipMemcpyDeviceToHost));
+    if (h)
+        return fail(VAE_ERR_UNSUPPORTED,
+                    "fp16 weights: a weight of magnitude 64 or more (or not finite) overflows "
+                    "fp16 at the 2^10 scale; use bf16 operands for this conv");
     return VAE_OK;
 }
 

@@ -441,7 +441,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
 }
 
 struct Layout {
-    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, total;
+    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, status, total;
     int64_t act_bytes;
 };
 
@@ -467,6 +467,8 @@ Layout layout_of(const Req& r) {
     off += align_up((size_t)r.tile, 256);
     L.attn = off;
     off += align_up((size_t)r.attn, 256);
+    L.status = off;          // the decode's status word (vae_decode_status)
+    off += 256;
     L.total = off;
     L.act_bytes = (int64_t)act;
     return L;
@@ -494,6 +496,8 @@ struct Runner {
     }
 
     bool stats_ready = false;  // mean/rstd already hold the statistics of the next GN's input
+    // The decode's status word in the workspace: set when a norm's statistics are not finite.
+    uint32_t* status() { return reinterpret_cast<uint32_t*>(ws + L.status); }
     bool per_patch = false;    // launch every conv, GroupNorm pass and upsampling per patch box
 
     // Records an op of patch `patch` (-1: work shared by all patches, such as a merge of
@@ -520,10 +524,12 @@ struct Runner {
         }
         const bool fused = stats_ready;
         stats_ready = false;
+        uint32_t* st = status();
         const double xe = (double)elem_size(x.dtype) * x.n * x.c;   // bytes per position
         const double ye = (double)elem_size(y.dtype) * y.n * y.c;
         if (!per_patch) {
-            if (!fused) VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s));
+            if (!fused)
+                VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s, st));
             // the patch boxes partition the tensor, so one apply launch covers them all
             VAE_TRY(launch_gn_apply(x, whole_box(x), d->groups, mr,
                                     static_cast<const float*>(gamma),
@@ -539,10 +545,10 @@ struct Runner {
                 one.b[0] = bl.b[i];
                 VAE_TRY(launch_gn_stats(x, one, d->groups, stats,
                                         parts + (int64_t)i * x.n * d->groups * 3, nullptr, d->eps,
-                                        s));
+                                        s, st));
                 VAE_TRY(mark_patch(i, VAE_KIND_GN, layer, 0.0, (double)bl.b[i].volume() * xe));
             }
-            VAE_TRY(launch_gn_combine(parts, bl.n, (int32_t)x.n, d->groups, d->eps, mr, s));
+            VAE_TRY(launch_gn_combine(parts, bl.n, (int32_t)x.n, d->groups, d->eps, mr, s, st));
             VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
         }
         for (int i = 0; i < bl.n; ++i) {
@@ -556,7 +562,7 @@ struct Runner {
     vae_status_t rms(const vae_tensor_t& x, const vae_tensor_t& y, const void* gamma,
                      const void* beta, int layer) {
         VAE_TRY(launch_rms_norm(x, d->eps, static_cast<const float*>(gamma),
-                                static_cast<const float*>(beta), true, y, s));
+                                static_cast<const float*>(beta), true, y, s, status()));
         return mark(VAE_KIND_RMS, layer, 0.0,
                     (double)numel(x) * elem_size(x.dtype) + (double)numel(y) * elem_size(y.dtype));
     }
@@ -626,7 +632,7 @@ struct Runner {
         if (total > 0) {
             // merged into mean/rstd here (all patches, in a fixed order); timed as shared work
             VAE_TRY(launch_gn_finalize_slots(part, total, (int32_t)y.n, d->groups, d->eps,
-                                             reinterpret_cast<float*>(ws + L.mr), s));
+                                             reinterpret_cast<float*>(ws + L.mr), s, status()));
             if (per_patch) VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
             stats_ready = true;
         }
@@ -680,7 +686,7 @@ struct Runner {
         }
         if (total > 0) {
             VAE_TRY(launch_gn_finalize_slots(part, total, (int32_t)y.n, d->groups, d->eps,
-                                             reinterpret_cast<float*>(ws + L.mr), s));
+                                             reinterpret_cast<float*>(ws + L.mr), s, status()));
             if (per_patch) VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
             stats_ready = true;
         }
@@ -1145,13 +1151,22 @@ VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, siz
     uint8_t* out = static_cast<uint8_t*>(buf);
     vae_status_t st = VAE_OK;
     std::vector<const void*> packed(dec->ptrs.size(), nullptr);
+    int conv_index = 0, bad = -1;
     for_each_conv(*dec, [&](size_t wi, int32_t cin, int32_t cout, bool f16) {
-        if (st != VAE_OK || !packable(*dec, cin, cout)) return;
-        st = launch_pack_weights(dec->ptrs[wi], cout, cin, out, as_stream(stream), f16);
-        packed[wi] = out;
-        out += align_up((size_t)packed_weight_elems(cout, cin) * 2, 256);
+        if (st == VAE_OK && packable(*dec, cin, cout)) {
+            st = launch_pack_weights(dec->ptrs[wi], cout, cin, out, as_stream(stream), f16);
+            if (st != VAE_OK) bad = conv_index;
+            packed[wi] = out;
+            out += align_up((size_t)packed_weight_elems(cout, cin) * 2, 256);
+        }
+        ++conv_index;
     });
-    if (st != VAE_OK) return st;
+    if (st != VAE_OK) {
+        if (st == VAE_ERR_UNSUPPORTED)   // a weight outside the fp16 range: name the conv
+            return fail(st, "conv " + std::to_string(bad) + " (plan order): " + vae_last_error(),
+                        -1, bad);
+        return st;
+    }
     dec->packed = packed;
     return VAE_OK;
 }
@@ -1205,6 +1220,8 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tens
 
     dec->recs.clear();
     Runner r{dec, as_stream(stream), static_cast<uint8_t*>(ws), L, -1, 0};
+    // clear the status word with a kernel (no memset node, so a captured decode replays right)
+    VAE_TRY(launch_zero(r.ws + L.status, 16, r.s));
     VAE_TRY(r.mark(VAE_KIND_OTHER, -1, 0, 0));
     if (desc->mode == VAE_TILING_PATCH_HALO) {
         std::vector<Box> boxes;
@@ -1250,6 +1267,25 @@ VAE_API vae_status_t vae_decoder_set_launch(vae_decoder_t* dec, int32_t launch) 
     if (launch != VAE_LAUNCH_MERGED && launch != VAE_LAUNCH_PER_PATCH)
         return fail(VAE_ERR_INVALID_ARG, "launch must be VAE_LAUNCH_MERGED or VAE_LAUNCH_PER_PATCH");
     dec->launch = launch;
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decode_status(const vae_decoder_t* dec, const vae_tiling_desc_t* desc,
+                                       const void* ws, size_t ws_bytes, int32_t* flags,
+                                       vae_stream_t stream) {
+    clear_error();
+    if (!dec || !desc || !ws || !flags) return fail(VAE_ERR_INVALID_ARG, "NULL argument");
+    Layout L;
+    std::vector<vae_tile_t> tiles;
+    VAE_TRY(size_for(*dec, *desc, &L, &tiles));
+    if (ws_bytes < L.total)
+        return fail(VAE_ERR_WORKSPACE, "workspace too small", -1, (int64_t)ws_bytes, -1,
+                    (int64_t)L.total);
+    uint32_t word = 0;
+    VAE_HIP_CHECK(hipStreamSynchronize(as_stream(stream)));
+    VAE_HIP_CHECK(hipMemcpy(&word, static_cast<const uint8_t*>(ws) + L.status, sizeof(word),
+                            hipMemcpyDeviceToHost));
+    *flags = (int32_t)(word ? VAE_STATUS_NONFINITE : 0);
     return VAE_OK;
 }
 

@@ -52,6 +52,12 @@ __device__ __forceinline__ void chan_merge(Moments& a, double nb, double mb, dou
     a.n = n;
 }
 
+// Sets *status (when given) if a group's statistics are not finite: an input value was inf or
+// NaN, e.g. an activation past fp16's 65504 stored at an fp16 operand hand-off.
+__device__ __forceinline__ void flag_nonfinite(uint32_t* status, double mean, double var) {
+    if (status && !(isfinite(mean) && isfinite(var))) *status = 1u;
+}
+
 // Number of stats blocks per box for a given tensor.
 int32_t blocks_for_box(const Box& b, int64_t c, int32_t n_boxes) {
     int64_t rows = b.bt() * b.bh();
@@ -247,7 +253,8 @@ __device__ Moments block_merge(const double* src, int64_t stride, int lo, int hi
 __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(const double* __restrict__ ws,
                                                                GnBoxes boxes, int32_t groups,
                                                                float eps, double* part_out,
-                                                               float* mean_rstd) {
+                                                               float* mean_rstd,
+                                                               uint32_t* status) {
     const int g = blockIdx.x, n = blockIdx.y, N = gridDim.y;
     const int64_t stride = (int64_t)N * groups * 3;
     const double* base = ws + ((int64_t)n * groups + g) * 3;
@@ -268,6 +275,7 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_kernel(const double* __r
         const double var = total.n > 0.0 ? total.m2 / total.n : 0.0;
         mean_rstd[((int64_t)n * groups + g) * 2] = (float)total.mean;
         mean_rstd[((int64_t)n * groups + g) * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+        flag_nonfinite(status, total.mean, var);
     }
 }
 
@@ -299,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void gn_slots_chunk_kernel(double* __rest
 __global__ __launch_bounds__(kThreads) void gn_finalize_slots_kernel(const double* __restrict__ ws,
                                                                      int64_t slots, int64_t stride,
                                                                      int32_t count, int32_t groups,
-                                                                     float eps, float* mean_rstd) {
+                                                                     float eps, float* mean_rstd,
+                                                                     uint32_t* status) {
     const int g = blockIdx.x, n = blockIdx.y;
     const double* base = ws + ((int64_t)n * groups + g) * slots * 3;
     const Moments m = block_merge(base, 3 * stride, 0, count);
@@ -307,13 +316,14 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_slots_kernel(const doubl
         const double var = m.n > 0.0 ? m.m2 / m.n : 0.0;
         mean_rstd[((int64_t)n * groups + g) * 2] = (float)m.mean;
         mean_rstd[((int64_t)n * groups + g) * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+        flag_nonfinite(status, m.mean, var);
     }
 }
 
 // grid (groups, N). part: [n_parts][N][G][3].
 __global__ __launch_bounds__(64) void gn_combine_kernel(const double* __restrict__ part,
                                                         int32_t n_parts, int32_t groups, float eps,
-                                                        float* mean_rstd) {
+                                                        float* mean_rstd, uint32_t* status) {
     const int g = blockIdx.x, n = blockIdx.y, N = gridDim.y;
     Moments m{0.0, 0.0, 0.0};
     if (threadIdx.x == 0) {
@@ -324,6 +334,7 @@ __global__ __launch_bounds__(64) void gn_combine_kernel(const double* __restrict
         const double var = m.n > 0.0 ? m.m2 / m.n : 0.0;
         mean_rstd[((int64_t)n * groups + g) * 2] = (float)m.mean;
         mean_rstd[((int64_t)n * groups + g) * 2 + 1] = (float)(1.0 / sqrt(var + (double)eps));
+        flag_nonfinite(status, m.mean, var);
     }
 }
 
@@ -417,7 +428,7 @@ size_t gn_stats_workspace(const vae_tensor_t& x, const BoxList& boxes, int32_t g
 
 vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_t groups,
                              double* ws, double* part_out, float* mean_rstd, float eps,
-                             hipStream_t stream) {
+                             hipStream_t stream, uint32_t* status) {
     GnBoxes g = make_boxes(x, boxes);
     dim3 grid((unsigned)g.start[g.n], (unsigned)x.n);
     if (x.dtype == VAE_DTYPE_BF16)
@@ -434,26 +445,28 @@ vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_
                            (int32_t)x.w, (int32_t)x.c, groups, g, ws);
     VAE_HIP_CHECK(hipGetLastError());
     hipLaunchKernelGGL(gn_finalize_kernel, dim3((unsigned)groups, (unsigned)x.n), dim3(kThreads),
-                       0, stream, ws, g, groups, eps, part_out, mean_rstd);
+                       0, stream, ws, g, groups, eps, part_out, mean_rstd, status);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
 
 vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, int32_t groups,
-                               float eps, float* mean_rstd, hipStream_t stream) {
+                               float eps, float* mean_rstd, hipStream_t stream,
+                               uint32_t* status) {
     hipLaunchKernelGGL(gn_combine_kernel, dim3((unsigned)groups, (unsigned)n), dim3(64), 0, stream,
-                       part, n_parts, groups, eps, mean_rstd);
+                       part, n_parts, groups, eps, mean_rstd, status);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
 
 vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int32_t groups,
-                                      float eps, float* mean_rstd, hipStream_t stream) {
+                                      float eps, float* mean_rstd, hipStream_t stream,
+                                      uint32_t* status) {
     if (slots > INT32_MAX) return fail(VAE_ERR_UNSUPPORTED, "too many statistics slots");
     if (slots <= kSlotChunk) {
         hipLaunchKernelGGL(gn_finalize_slots_kernel, dim3((unsigned)groups, (unsigned)n),
                            dim3(kThreads), 0, stream, ws, slots, (int64_t)1, (int32_t)slots,
-                           groups, eps, mean_rstd);
+                           groups, eps, mean_rstd, status);
         VAE_HIP_CHECK(hipGetLastError());
         return VAE_OK;
     }
@@ -463,7 +476,7 @@ vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int3
     VAE_HIP_CHECK(hipGetLastError());
     hipLaunchKernelGGL(gn_finalize_slots_kernel, dim3((unsigned)groups, (unsigned)n),
                        dim3(kThreads), 0, stream, ws, slots, kSlotChunk, (int32_t)chunks, groups,
-                       eps, mean_rstd);
+                       eps, mean_rstd, status);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }

@@ -86,16 +86,19 @@ vae_status_t launch_conv3d_strided(const vae_tensor_t& x, const void* w, int32_t
 // Workspace: per-block partials of every box, fp64 [blocks][N][G][3].
 size_t gn_stats_workspace(const vae_tensor_t& x, const BoxList& boxes, int32_t groups);
 // Per-block partials -> per-box partials (part_out, optional) and mean/rstd (optional).
+// `status` (optional, device): set to 1 when a group's statistics are not finite.
 vae_status_t launch_gn_stats(const vae_tensor_t& x, const BoxList& boxes, int32_t groups,
                              double* ws, double* part_out, float* mean_rstd, float eps,
-                             hipStream_t stream);
+                             hipStream_t stream, uint32_t* status = nullptr);
 vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, int32_t groups,
-                               float eps, float* mean_rstd, hipStream_t stream);
+                               float eps, float* mean_rstd, hipStream_t stream,
+                               uint32_t* status = nullptr);
 // Partials [N][groups][slots][3] (as a fused conv writes them) -> mean/rstd [N][groups][2].
 // Large slot counts are merged in two passes, the first in place over ws (whose contents are
 // then spent).
 vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int32_t groups,
-                                      float eps, float* mean_rstd, hipStream_t stream);
+                                      float eps, float* mean_rstd, hipStream_t stream,
+                                      uint32_t* status = nullptr);
 vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t groups,
                              const float* mean_rstd, const float* gamma, const float* beta,
                              bool silu, const vae_tensor_t& y, hipStream_t stream);
@@ -104,9 +107,10 @@ bool gn_shape_supported(const vae_tensor_t& x, int32_t groups);
 // ---- RMS norm and frame attention (Wan-style decoders) ----
 bool rms_shape_supported(int64_t c);
 // y = x / sqrt(mean_c(x^2) + eps) * gamma + beta (+ SiLU) per position; x bf16/fp32, y any dtype.
+// `status` (optional, device): set to 1 when a position's sum of squares is not finite.
 vae_status_t launch_rms_norm(const vae_tensor_t& x, float eps, const float* gamma,
                              const float* beta, bool silu, const vae_tensor_t& y,
-                             hipStream_t stream);
+                             hipStream_t stream, uint32_t* status = nullptr);
 bool attention_shape_supported(int64_t c);
 size_t attention_workspace(const vae_tensor_t& x);
 // Single-head attention over each frame's positions plus the residual; fp32 x and y (y may be

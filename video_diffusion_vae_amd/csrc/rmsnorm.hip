@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict
                                                             int32_t C, float eps,
                                                             const float* __restrict__ gamma,
                                                             const float* __restrict__ beta,
-                                                            int32_t silu) {
+                                                            int32_t silu, uint32_t* status) {
     __shared__ float part[kThreads / 64];                  // one partial per wave
     const int tpp = C / 8;                                 // threads per position
     const int ppb = kThreads / tpp;                        // positions per block step
@@ -61,6 +61,9 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict
             ss = t;
             __syncthreads();
         }
+        // a non-finite sum of squares: an input value was inf or NaN (e.g. an activation past
+        // fp16's 65504 at an fp16 operand hand-off)
+        if (status && valid && !isfinite(ss)) *status = 1u;
         const float r = 1.0f / sqrtf(ss / (float)C + eps);
         if (valid) {
             TO* dst = y + p * C + c0;
@@ -76,21 +79,24 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict
 
 template <typename TI, typename TO>
 void rms_launch(const vae_tensor_t& x, float eps, const float* gamma, const float* beta, bool silu,
-                const vae_tensor_t& y, hipStream_t stream) {
+                const vae_tensor_t& y, hipStream_t stream, uint32_t* status) {
     const int64_t positions = vae::positions(x);
     const int ppb = kThreads / (int)(x.c / 8);
     const int64_t blocks = std::min<int64_t>(ceil_div(positions, ppb), kMaxBlocks);
     hipLaunchKernelGGL((rms_norm_kernel<TI, TO>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        static_cast<const TI*>(x.data), static_cast<TO*>(y.data), positions,
-                       (int32_t)x.c, eps, gamma, beta, (int32_t)silu);
+                       (int32_t)x.c, eps, gamma, beta, (int32_t)silu, status);
 }
 
 template <typename TI>
 void rms_out(const vae_tensor_t& x, float eps, const float* gamma, const float* beta, bool silu,
-             const vae_tensor_t& y, hipStream_t stream) {
-    if (y.dtype == VAE_DTYPE_F32) rms_launch<TI, float>(x, eps, gamma, beta, silu, y, stream);
-    else if (y.dtype == VAE_DTYPE_F16) rms_launch<TI, _Float16>(x, eps, gamma, beta, silu, y, stream);
-    else rms_launch<TI, uint16_t>(x, eps, gamma, beta, silu, y, stream);
+             const vae_tensor_t& y, hipStream_t stream, uint32_t* status) {
+    if (y.dtype == VAE_DTYPE_F32)
+        rms_launch<TI, float>(x, eps, gamma, beta, silu, y, stream, status);
+    else if (y.dtype == VAE_DTYPE_F16)
+        rms_launch<TI, _Float16>(x, eps, gamma, beta, silu, y, stream, status);
+    else
+        rms_launch<TI, uint16_t>(x, eps, gamma, beta, silu, y, stream, status);
 }
 
 }  // namespace
@@ -101,14 +107,15 @@ bool rms_shape_supported(int64_t c) {
 
 vae_status_t launch_rms_norm(const vae_tensor_t& x, float eps, const float* gamma,
                              const float* beta, bool silu, const vae_tensor_t& y,
-                             hipStream_t stream) {
+                             hipStream_t stream, uint32_t* status) {
     if (numel(x) == 0) return VAE_OK;
     if (!rms_shape_supported(x.c))
         return fail(VAE_ERR_UNSUPPORTED, "rms norm needs C % 8 == 0 and C / 8 dividing 256", 4,
                     x.c, 8);
-    if (x.dtype == VAE_DTYPE_F32) rms_out<float>(x, eps, gamma, beta, silu, y, stream);
-    else if (x.dtype == VAE_DTYPE_F16) rms_out<_Float16>(x, eps, gamma, beta, silu, y, stream);
-    else rms_out<uint16_t>(x, eps, gamma, beta, silu, y, stream);
+    if (x.dtype == VAE_DTYPE_F32) rms_out<float>(x, eps, gamma, beta, silu, y, stream, status);
+    else if (x.dtype == VAE_DTYPE_F16)
+        rms_out<_Float16>(x, eps, gamma, beta, silu, y, stream, status);
+    else rms_out<uint16_t>(x, eps, gamma, beta, silu, y, stream, status);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
