@@ -43,7 +43,8 @@ from .layers import (causal_conv3d, strided_causal_conv3d, conv3d_valid, causal_
 from .stats import group_moments, chan_combine, normalize_with
 from .tiling import (bands, axis_tiles, patch_tiles, overlap_tiles, ramp_1d, axis_weight_sum)
 from .decoder import (decode, decode_patch_halo, decode_overlap_blend, merge_tiles,
-                      output_shape, encode, encode_patch_halo, encode_overlap_blend)
+                      output_shape, encode, encode_patch_halo, encode_overlap_blend,
+                      decode_causal_clips)
 
 __all__ = [
     "causal_conv3d", "strided_causal_conv3d", "conv3d_valid", "causal_time_pad", "group_norm",
@@ -52,5 +53,5 @@ __all__ = [
     "group_moments", "chan_combine", "encode", "encode_patch_halo", "encode_overlap_blend",
     "normalize_with", "bands", "axis_tiles",
     "patch_tiles", "overlap_tiles", "ramp_1d", "axis_weight_sum", "decode", "decode_patch_halo",
-    "decode_overlap_blend", "merge_tiles", "output_shape",
+    "decode_overlap_blend", "merge_tiles", "output_shape", "decode_causal_clips",
 ]

@@ -114,6 +114,65 @@ def decode(spec: dict, z: np.ndarray, params: list) -> np.ndarray:
     return h
 
 
+def decode_causal_clips(spec: dict, z: np.ndarray, params: list, clip: int) -> np.ndarray:
+    """Decode clip by clip: latent frames [0, clip), [clip, 2 clip), ... one after another, each
+    clip seeing only its own frames plus what the clips before it left behind.
+
+    Every causal conv keeps the last two frames of its input (its temporal receptive field beyond
+    the current frame) and puts them in front of the next clip's input instead of the causal copies
+    of frame 0, which only the first clip gets. A causal depth-to-space drops its leading frames
+    in the first clip only. This is the plainest reading of the tile-parallel decode's temporal
+    tiles with the causal context carried ("[TRTLLM-14029][feat] LTX-2 tile-parallel VAE decode",
+    Description: overlapping spatial/temporal tiles of a causal decoder): carried, not
+    overlapped, the clips rebuild the whole decode exactly. That holds only for plans whose every
+    op is local in time; a GroupNorm's statistics span all frames, so such plans are refused.
+    """
+    kinds = {op["op"] for op in spec["layers"]}
+    assert not kinds & {"res", "gn_silu", "s2d", "conv_down"}, \
+        f"clip-by-clip decode needs ops local in time, not {sorted(kinds)}"
+    z = np.asarray(z, dtype=np.float64)
+    eps = spec["eps"]
+    caches = {}
+
+    def conv(h, p, key):
+        prev = caches.get(key)
+        if prev is None:
+            prev = np.concatenate([h[:, :1]] * 2, axis=1)       # causal copies of frame 0
+        ext = np.concatenate([prev, h], axis=1)
+        caches[key] = ext[:, -2:]
+        ext = np.pad(ext, ((0, 0), (0, 0), (1, 1), (1, 1), (0, 0)))
+        return conv3d_valid(ext, p["w"], p["b"])
+
+    outs = []
+    for c0 in range(0, z.shape[1], clip):
+        h = z[:, c0:c0 + clip]
+        it = iter(params)
+        for i, op in enumerate(spec["layers"]):
+            k = op["op"]
+            if k == "conv":
+                h = conv(h, next(it), (i, 0))
+            elif k == "res_rms":
+                g1, c1, g2, c2 = next(it), next(it), next(it), next(it)
+                t = conv(silu(rms_norm(h, eps, g1["gamma"], g1["beta"])), c1, (i, 1))
+                t = silu(rms_norm(t, eps, g2["gamma"], g2["beta"]))
+                h = conv(t, c2, (i, 2)) + h
+            elif k == "rms_silu":
+                g = next(it)
+                h = silu(rms_norm(h, eps, g["gamma"], g["beta"]))
+            elif k == "attn":
+                a = next(it)
+                h = frame_attention(h, eps, a["gamma"], a["beta"], a["w_qkv"], a["b_qkv"],
+                                    a["w_out"], a["b_out"])
+            elif k == "d2s":
+                h = depth_to_space(h, op["st"], op["sh"], op["sw"], drop=c0 == 0)
+            elif k == "nearest":
+                h = nearest_upsample(h, op["sh"], op["sw"])
+            else:
+                raise ValueError(k)
+        outs.append(h)
+    return np.concatenate(outs, axis=1)
+
+
 def encode(spec: dict, x: np.ndarray, params: list) -> np.ndarray:
     """Untiled encode of the NDHWC video ``x``: the same plan executor as ``decode``; an encoder
     plan narrows with ``s2d`` folds where a decoder widens with ``d2s``."""

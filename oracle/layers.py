@@ -138,7 +138,7 @@ def nearest_upsample(x: np.ndarray, sh: int, sw: int) -> np.ndarray:
     return np.repeat(np.repeat(x, sh, axis=2), sw, axis=3)
 
 
-def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
+def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int, drop: bool = True) -> np.ndarray:
     """Depth-to-space upsampling, then causal drop of the first st-1 frames.
 
     The upsampler moves channels into space, one input position per output ("Add tiled VAE
@@ -146,7 +146,8 @@ def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
     the channel order. Here input channel ((dt*sh + dh)*sw + dw)*C + c feeds output channel c at
     (st*t + dt, sh*h + dh, sw*w + dw): the sub-position is slowest and the channel fastest. With
     st > 1 the first st-1 frames are dropped, so T frames become st*T - (st-1) (16 -> 31 -> 61 -> 121
-    for the LTX-2-shaped workload).
+    for the LTX-2-shaped workload). ``drop=False`` keeps them: a later clip of a clip-by-clip
+    decode continues the sequence, and only the very first frame of the video is dropped.
     """
     x = np.asarray(x, dtype=np.float64)
     n, t, h, w, ck = x.shape
@@ -155,7 +156,7 @@ def depth_to_space(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:
     c = ck // k
     y = x.reshape(n, t, h, w, st, sh, sw, c)
     y = y.transpose(0, 1, 4, 2, 5, 3, 6, 7).reshape(n, t * st, h * sh, w * sw, c)
-    return np.ascontiguousarray(y[:, st - 1:])
+    return np.ascontiguousarray(y[:, st - 1:] if drop else y)
 
 
 def space_to_depth(x: np.ndarray, st: int, sh: int, sw: int) -> np.ndarray:

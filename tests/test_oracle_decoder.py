@@ -220,3 +220,44 @@ def test_wan_shaped_patch_halo_equals_whole(name, grid):
 def test_wan_shaped_output_shape():
     spec = vae_synth.WAN_720P
     assert oracle.output_shape(spec, (1, 21, 44, 80, 48)) == (1, 81, 704, 1280, 3)
+
+
+@pytest.mark.parametrize("name,clip", [("wan_tiny", 1), ("wan_tiny", 2), ("wan_small", 1)])
+def test_causal_clips_equal_whole_decode(name, clip):
+    """Clip by clip with each causal conv's last two input frames carried to the next clip: the
+    whole decode, frame for frame."""
+    spec = vae_synth.WORKLOADS[name]
+    z = ndhwc(vae_synth.latent(spec)).astype(np.float64)
+    p = vae_synth.decoder_params(spec, affine_seed=6)
+    whole = oracle.decode(spec, z, p)
+    clips = oracle.decode_causal_clips(spec, z, p, clip)
+    assert clips.shape == whole.shape
+    assert np.abs(clips - whole).max() <= 1e-12 * np.abs(whole).max()
+
+
+def test_causal_clips_carry_information_across_the_boundary():
+    """The carried frames matter: changing the last latent frame of the first clip changes the
+    second clip's output (through the carry), and changing the second clip's first frame leaves
+    every output frame of the first clip as it was (causality)."""
+    spec = vae_synth.WAN_TINY
+    z = ndhwc(vae_synth.latent(spec)).astype(np.float64)
+    p = vae_synth.decoder_params(spec, affine_seed=6)
+    base = oracle.decode_causal_clips(spec, z, p, 2)
+    first = 1 + (2 - 1) * 4                       # output frames of latent frames [0, 2)
+    z1 = z.copy()
+    z1[:, 1] += 0.5
+    a = oracle.decode_causal_clips(spec, z1, p, 2)
+    assert np.abs(a[:, first:] - base[:, first:]).max() > 1e-3
+    z2 = z.copy()
+    z2[:, 2] += 0.5
+    b = oracle.decode_causal_clips(spec, z2, p, 2)
+    assert np.array_equal(b[:, :first], base[:, :first])
+    assert np.abs(b[:, first:] - base[:, first:]).max() > 1e-3
+
+
+def test_causal_clips_refuse_groupnorm_plans():
+    """A GroupNorm's statistics span every frame: no clip-by-clip decode can reproduce it."""
+    spec = vae_synth.LTX2_TINY
+    z = ndhwc(vae_synth.latent(spec))
+    with pytest.raises(AssertionError):
+        oracle.decode_causal_clips(spec, z, vae_synth.decoder_params(spec), 1)
