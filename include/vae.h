@@ -599,6 +599,23 @@ VAE_API vae_status_t vae_decoder_pack_weights(vae_decoder_t* dec, void* buf, siz
 enum { VAE_LAUNCH_MERGED = 0, VAE_LAUNCH_PER_PATCH = 1 };
 VAE_API vae_status_t vae_decoder_set_launch(vae_decoder_t* dec, int32_t launch);
 
+/* Clip-by-clip decode ("[TRTLLM-14029][feat] LTX-2 tile-parallel VAE decode", Description: the
+ * decode's overlapping spatial/temporal tiles of a causal decoder). With frames > 0 a mode A
+ * decode of more than `frames` latent frames runs clip by clip: latent frames [0, frames),
+ * [frames, 2 frames), ... (the last clip may be shorter), each through the whole plan, writing
+ * its own output frames. Every causal conv keeps the last two frames of its input in the
+ * workspace and reads them in front of the next clip's first frame, where the first clip reads
+ * copies of its frame 0; a causal depth-to-space drops its leading frames in the first clip only.
+ * The result is the whole decode's up to rounding order (the same arithmetic, frame for frame),
+ * while every activation holds one clip: the workspace shrinks with the clip.
+ * frames = 0 (the default) decodes all frames at once.
+ * Refused (VAE_ERR_UNSUPPORTED) unless the plan is bf16 and every op is local in time: convs,
+ * RMS norms, frame attention and upsamplings (a GroupNorm's statistics span every frame; a fold
+ * that narrows time has no carry defined). At decode time a clip-by-clip decode takes N = 1 and
+ * refuses a temporal depth-to-space not fused into a matrix-core conv (VAE_ERR_UNSUPPORTED).
+ * Query the workspace after setting it. Mode B ignores it. */
+VAE_API vae_status_t vae_decoder_set_clip_frames(vae_decoder_t* dec, int32_t frames);
+
 /* Device scratch needed by vae_decode_tiled for this tiling (latent extents come from desc). */
 VAE_API vae_status_t vae_decode_workspace_size(const vae_decoder_t* dec,
                                                const vae_tiling_desc_t* desc, size_t* bytes);

@@ -462,3 +462,55 @@ def test_decode_status_argument_checks(v):
     assert v.LIB.vae_decode_status(dec._h, ctypes.byref(desc), ctypes.c_void_p(1 << 40), need,
                                    None, None) == v.VAE_ERR_INVALID_ARG
     dec.close()
+
+
+def _plan_decoder(v, spec, flags=0):
+    n_ptr = sum({"conv": 2, "res": 8, "res_rms": 8, "gn_silu": 2, "rms_silu": 2, "attn": 6}
+                .get(op["op"], 0) for op in spec["layers"])
+    lc = v.latent_channels(spec)
+    layers = [dict(op) for op in spec["layers"]]
+    first = next(op for op in layers if op["op"] == "conv")
+    first["cin"] = lc
+    return v.Decoder(v.VAE_DTYPE_BF16, lc, spec["groups"], spec["eps"], layers,
+                     [_FakePtr(i) for i in range(n_ptr)], flags=flags)
+
+
+def test_clip_frames_rules_and_workspace(v):
+    """A clip-by-clip decode takes plans whose every op is local in time (convs, RMS norms, frame
+    attention, upsamplings); a GroupNorm plan is refused. Its workspace holds one clip's
+    activations plus headroom and the carried frames: at the Wan 720p plan (21 latent frames) a
+    clip of 2 needs far less than the whole decode, and a clip at least as long as the latent
+    decodes at once, with the whole decode's workspace."""
+    import vae_synth
+    spec = vae_synth.WAN_720P
+    dec = _plan_decoder(v, spec, flags=v.VAE_DECODE_F16_OPERANDS)
+    shape = (1, 21, 44, 80, v.latent_channels(spec))
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, shape, spec["scale"], patches=(1, 4))
+    whole = dec.workspace_size(desc)
+    dec.set_clip_frames(2)
+    clip2 = dec.workspace_size(desc)
+    assert clip2 < whole / 4
+    # each of the three buffers holds at least a later clip's 8 frames of the 256-channel
+    # activation at 352 x 640 (2 bytes a value at least)
+    assert clip2 >= 3 * 8 * 352 * 640 * 256 * 2
+    dec.set_clip_frames(21)
+    assert dec.workspace_size(desc) == whole
+    dec.set_clip_frames(0)
+    assert dec.workspace_size(desc) == whole
+    # the overlap-blend mode ignores the setting
+    ob = v.tiling_desc(v.VAE_TILING_OVERLAP_BLEND, shape, spec["scale"], tile=(32, 32),
+                       stride=(28, 28))
+    b = dec.workspace_size(ob)
+    dec.set_clip_frames(2)
+    assert dec.workspace_size(ob) == b
+    with pytest.raises(v.VaeError) as e:
+        dec.set_clip_frames(-1)
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    dec.close()
+    for name in ("ltx2_tiny", "mixed_rms_gn"):
+        g = _plan_decoder(v, vae_synth.WORKLOADS[name])
+        with pytest.raises(v.VaeError) as e:       # GroupNorm statistics span every frame
+            g.set_clip_frames(1)
+        assert e.value.status == v.VAE_ERR_UNSUPPORTED
+        g.set_clip_frames(0)
+        g.close()

@@ -129,11 +129,16 @@ def _oracle(name, mode, tt=(0, 0)):
                                        spec["overlap_stride"], spec["scale"], tt[0], tt[1])
 
 
-def _decode(v, name, mode, patches=(1, 1), operands="f16", repeat=1, tt=(0, 0)):
+def _decode(v, name, mode, patches=(1, 1), operands="f16", repeat=1, tt=(0, 0), clip=0,
+            launch=None):
     import torch
     spec = vae_synth.WORKLOADS[name]
     z = v.pad_latent(ndhwc(vae_synth.latent(spec)), spec)
     dec = v.upload_decoder(spec, _params(name), operands=operands)
+    if clip:
+        dec.set_clip_frames(clip)
+    if launch is not None:
+        dec.set_launch(launch)
     zd = dev(z, "bf16")
     if mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
@@ -182,6 +187,24 @@ def test_wan_shaped_decode_temporal_tiles(v):
     assert p >= 50.0 and m <= 2e-2, (p, m)
 
 
+@pytest.mark.parametrize("name,clip,patches,per_patch", [("wan_tiny", 1, (1, 1), False),
+                                                          ("wan_tiny", 2, (2, 2), False),
+                                                          ("wan_tiny", 2, (2, 2), True),
+                                                          ("wan_tiny", 1, (2, 2), True),
+                                                          ("wan_small", 1, (1, 2), False)])
+def test_wan_shaped_decode_clip_by_clip(v, name, clip, patches, per_patch):
+    """The patch-halo decode in causal clips of `clip` latent frames, every causal conv carrying
+    its last two input frames into the next clip: the whole decode of the oracle, at the bf16
+    bar (wan_tiny's 3 frames as [0,1) [1,2) [2,3) or [0,2) [2,3); wan_small's 2 as one-frame
+    clips)."""
+    got = host(_decode(v, name, "patch", patches, clip=clip,
+                       launch=v.VAE_LAUNCH_PER_PATCH if per_patch else None))
+    ref = _oracle(name, "patch")
+    assert got.shape == ref.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
 def test_wan_shaped_decode_is_deterministic(v):
     import torch
     a, b = _decode(v, "wan_tiny", "patch", (2, 2), repeat=2)
@@ -200,18 +223,20 @@ def test_wan_720p_one_frame_every_value(v):
     assert p >= 50.0 and m <= 2e-2, (p, m)
 
 
-def test_wan_720p_six_frames_against_golden(v):
+@pytest.mark.parametrize("clip", [0, 2])
+def test_wan_720p_six_frames_against_golden(v, clip):
     """The full-width Wan-shaped 720p plan on six latent frames ([1,48,6,44,80] ->
     [1,21,704,1280,3]) in 1 x 4 width patches, at the pixels the oracle's fp64 decode stored
     (tests/golden/make_wan_720p_samples.py): both temporal upsamplings and the causal temporal taps
-    at full spatial size."""
+    at full spatial size. With clip = 2 the same decode runs as three causal clips of two latent
+    frames (output frames [0,5) [5,13) [13,21)), the frames carried at full size."""
     import os
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                         "wan_720p_6f_whole_samples.npz")
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated")
     g = np.load(path)
-    out = _decode(v, "wan_720p_6f", "patch", (1, 4))
+    out = _decode(v, "wan_720p_6f", "patch", (1, 4), clip=clip)
     assert tuple(out.shape) == tuple(int(d) for d in g["shape"])
     pos = g["positions"]
     got = out[0, pos[:, 0], pos[:, 1], pos[:, 2], :].double().cpu().numpy()

@@ -39,7 +39,8 @@ EXPORTS = (
     "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_rmsnorm_silu",
     "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample", "vae_space_to_depth",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
-    "vae_decoder_set_launch", "vae_decode_workspace_size", "vae_decode_tiled",
+    "vae_decoder_set_launch", "vae_decoder_set_clip_frames", "vae_decode_workspace_size",
+    "vae_decode_tiled",
     "vae_decode_status",
     "vae_decoder_set_timing",
     "vae_decoder_get_timing",
@@ -150,6 +151,7 @@ def _load():
                                 ctypes.POINTER(P)], I32),
         "vae_decoder_destroy": ([P], None),
         "vae_decoder_set_launch": ([P, I32], I32),
+        "vae_decoder_set_clip_frames": ([P, I32], I32),
         "vae_decode_workspace_size": ([P, D, ctypes.POINTER(SZ)], I32),
         "vae_decode_tiled": ([P, T, D, T, P, SZ, P], I32),
         "vae_decode_status": ([P, D, P, SZ, ctypes.POINTER(I32), P], I32),
@@ -548,6 +550,12 @@ class Decoder:
         """VAE_LAUNCH_MERGED or VAE_LAUNCH_PER_PATCH (patch-halo decodes); query the workspace
         size afterwards."""
         _check(LIB.vae_decoder_set_launch(self._h, int(launch)))
+
+    def set_clip_frames(self, frames):
+        """Decode patch-halo tilings clip by clip, `frames` latent frames at a time, carrying each
+        causal conv's last two input frames (0: all frames at once); query the workspace size
+        afterwards."""
+        _check(LIB.vae_decoder_set_clip_frames(self._h, int(frames)))
 
     def workspace_size(self, desc):
         n = ctypes.c_size_t()

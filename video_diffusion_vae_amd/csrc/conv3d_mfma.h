@@ -113,9 +113,11 @@ struct MfmaArgs {
     int32_t n_mblocks;       // N * nbt * nbh * nbw
     // Output mapping. y may be the depth-to-space (st, sh, sw) of the conv output: conv channel
     // ((dt*sh + dh)*sw + dw)*zc + c at (t, h, w) lands at channel c of y position
-    // (st*t + dt - (st-1), sh*h + dh, sw*w + dw); frames below 0 are dropped. Identity:
-    // st = sh = sw = 1 and zc = cout. The residual, if any, has y's shape.
-    int32_t yT, yH, yW, zc, st, sh, sw;
+    // (st*t + dt - tdrop, sh*h + dh, sw*w + dw); frames below 0 are dropped. tdrop is st - 1 (the
+    // causal drop of the first frames), plus st times the leading frames of an input whose
+    // first frames are only causal context (a clip's carried frames). Identity: st = sh = sw = 1,
+    // tdrop = 0 and zc = cout. The residual, if any, has y's shape.
+    int32_t yT, yH, yW, zc, st, sh, sw, tdrop;
     int32_t res_f32;         // the residual is fp32 while y is bf16 or fp16 (a hand-off)
     // Optional GroupNorm partials of y as stored: fp64 (count, mean, M2) per (sample, group of
     // y's channels, slot), slot = slot0 + (sub-position * position blocks + block) * WM + wave
@@ -344,7 +346,7 @@ __device__ __forceinline__ void conv_epilogue(const MfmaArgs& a, const f32x16_t 
     const int sdh = srow % a.sh, sdt = srow / a.sh;
     const int sub = co / a.zc, cz = co - sub * a.zc;   // sub-position and channel of y
     auto y_off = [&](int t, int h, int w, int s_dt, int s_dh, int r) -> int64_t {
-        const int to = a.st * t + s_dt - (a.st - 1);
+        const int to = a.st * t + s_dt - a.tdrop;
         if (to < 0) return -1;   // causal drop
         return ((((int64_t)n * a.yT + to) * a.yH + a.sh * h + s_dh) * a.yW + (int64_t)a.sw * w) *
                    a.zc + r;
@@ -475,7 +477,7 @@ __device__ __forceinline__ void conv_epilogue_direct_tiles(
     const int64_t stride_t = (int64_t)a.st * a.yH * a.yW * a.zc;
     const int64_t stride_h = (int64_t)a.sh * a.yW * a.zc;
     const int64_t stride_w = (int64_t)a.sw * a.zc;
-    const int to_blk = a.st * t_blk + sdt - (a.st - 1);
+    const int to_blk = a.st * t_blk + sdt - a.tdrop;
     // uniform offset of the block's first position (at sub-position `sub`, channel 0 of y)
     const int64_t blk = ((((int64_t)n * a.yT + to_blk) * a.yH + (int64_t)a.sh * h_blk + sdh) *
                              a.yW + (int64_t)a.sw * w_blk + sdw) * a.zc;
@@ -558,7 +560,7 @@ __device__ __forceinline__ void conv_epilogue_direct(const MfmaArgs& a, const f3
     const int sdt = sub / (a.sw * a.sh);
     float sn = 0.0f, sk = 0.0f, s1 = 0.0f, s2 = 0.0f;
     const bool inside = t_blk + TB <= a.box.t1 && h_blk + HB <= a.box.h1 &&
-                        w_blk + WB <= a.box.w1 && a.st * t_blk + sdt - (a.st - 1) >= 0;
+                        w_blk + WB <= a.box.w1 && a.st * t_blk + sdt - a.tdrop >= 0;
     if (inside)
         conv_epilogue_direct_tiles<false, TO, HB, WB, MI, MW, WM>(
             a, acc, n, t_blk, h_blk, w_blk, sub, cz, bv, khalf, wave_m, sn, sk, s1, s2);
@@ -1116,12 +1118,21 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.st = fz ? fz->st : 1;
     a.sh = fz ? fz->sh : 1;
     a.sw = fz ? fz->sw : 1;
+    a.tdrop = fz && fz->tdrop >= 0 ? fz->tdrop : a.st - 1;
     a.zc = (int32_t)y.c;
     a.cout = (int32_t)(y.c * a.st * a.sh * a.sw);
     a.yT = (int32_t)y.t;
     a.yH = (int32_t)y.h;
     a.yW = (int32_t)y.w;
     a.box = box;
+    // every position the grid stages lies in x, every value it stores lies in y (and in the
+    // residual, which has y's shape)
+    if (box.t0 < 0 || box.h0 < 0 || box.w0 < 0 || box.t1 > a.T || box.h1 > a.H ||
+        box.w1 > a.W || (int64_t)a.st * box.t1 - a.tdrop > a.yT ||
+        (int64_t)a.sh * box.h1 > a.yH || (int64_t)a.sw * box.w1 > a.yW || y.n != x.n ||
+        (residual && (residual->n != y.n || residual->t != y.t || residual->h != y.h ||
+                      residual->w != y.w || residual->c != y.c)))
+        return fail(VAE_ERR_INVALID_ARG, "conv3d: box outside the input, or outputs outside y");
     a.nbt = (int32_t)ceil_div(box.bt(), TB);
     a.nbh = (int32_t)ceil_div(box.bh(), HB);
     a.nbw = (int32_t)ceil_div(box.bw(), WB);

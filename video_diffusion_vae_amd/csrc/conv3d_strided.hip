@@ -279,6 +279,7 @@ vae_status_t run_strided_mfma(const vae_tensor_t& x, const void* w, const float*
     a.cout = (int32_t)y.c;
     a.zc = (int32_t)y.c;
     a.st = a.sh = a.sw = 1;
+    a.tdrop = 0;
     a.yT = (int32_t)y.t;
     a.yH = (int32_t)y.h;
     a.yW = (int32_t)y.w;

@@ -25,6 +25,7 @@
 struct vae_decoder {
     int32_t dtype = 0, act_dtype = 0, flags = 0, latent_c = 0, groups = 0;
     int32_t launch = VAE_LAUNCH_MERGED;   // patch-halo launches: merged or one per patch box
+    int32_t clip = 0;    // patch-halo decodes in causal clips of this many latent frames (0: whole)
     float eps = 0.0f;
     std::vector<vae_layer_desc_t> layers;
     std::vector<const void*> ptrs;
@@ -45,7 +46,12 @@ struct Shape {
     int64_t n, t, h, w, c;
     int32_t dtype;
     int64_t bytes() const { return n * t * h * w * c * elem_size(dtype); }
+    int64_t frame_bytes() const { return n * h * w * c * elem_size(dtype); }
 };
+
+// Frames of headroom before every activation of a clip-by-clip decode: a causal conv's carried
+// input frames go there.
+constexpr int64_t kCarry = 2;
 
 // Whether layer i is a conv that applies an fp32 input as split hi + lo bf16 operands.
 bool conv_splits(int32_t flags, const vae_layer_desc_t* layers, int n, int i) {
@@ -167,8 +173,10 @@ int ptrs_for(const vae_layer_desc_t& l) {
 }
 
 // Shape after each op, starting from the latent extents.
+// `drop`: a causal depth-to-space drops its first st - 1 frames (false for the later clips of a
+// clip-by-clip decode, which continue the sequence).
 vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, int* total_st,
-                  int* total_sh, int* total_sw) {
+                  int* total_sh, int* total_sw, bool drop = true) {
     Shape s = in;
     int st = 1, sh = 1, sw = 1;
     if (shapes) shapes->clear();
@@ -195,7 +203,7 @@ vae_status_t walk(const vae_decoder& d, Shape in, std::vector<Shape>* shapes, in
                 s.dtype = VAE_DTYPE_F32;
                 break;
             case VAE_OP_D2S:
-                s.t = l.st * s.t - (l.st - 1);
+                s.t = l.st * s.t - (drop ? l.st - 1 : 0);
                 s.h *= l.sh;
                 s.w *= l.sw;
                 s.c /= (int64_t)l.st * l.sh * l.sw;
@@ -307,27 +315,40 @@ struct Req {
     int64_t crop = 0;     // latent crop (mode B)
     int64_t tile = 0;     // one decoded tile, fp32 pixels (mode B)
     int64_t attn = 0;     // frame attention scratch
+    int64_t carry = 0;    // carried input frames of every causal conv (clip-by-clip decodes)
 };
 
 // Requirements of one run of the plan on an input of shape `in` with patch boxes `boxes`.
+// `headroom`: frames kept free before every activation held in a rotating buffer, and the
+// carried frames of every causal conv (clip-by-clip decodes).
 vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vector<Box>& boxes,
-                          bool final_in_buffer, Req* r) {
+                          bool final_in_buffer, Req* r, int64_t headroom = 0) {
+    auto held = [&](const Shape& x) { return x.bytes() + headroom * x.frame_bytes(); };
+    auto carry = [&](const Shape& x) {   // a conv's two carried input frames (x: its input)
+        if (headroom) r->carry += (int64_t)align_up((size_t)(kCarry * x.frame_bytes()), 256);
+    };
     bool exact = true;   // every patch box scales to whole rows and columns of each activation
     const bool per_patch = d.launch == VAE_LAUNCH_PER_PATCH && boxes.size() > 1;
     std::vector<Shape> shapes;
-    walk(d, in, &shapes, nullptr, nullptr, nullptr);
+    // a later clip keeps every frame of its depth-to-spaces: the larger shapes
+    walk(d, in, &shapes, nullptr, nullptr, nullptr, headroom == 0);
+    if (headroom) r->act = std::max(r->act, held(in));   // the clip's latent, copied in
     Shape cur = in;
     int ch = 1, cw = 1, fh = 1, fw = 1;
     for (size_t i = 0; i < d.layers.size(); ++i) {
         const vae_layer_desc_t& l = d.layers[i];
         const Shape& s = shapes[i];
         const bool last = i + 1 == d.layers.size();
-        if (!last) r->act = std::max(r->act, s.bytes());
+        if (!last) r->act = std::max(r->act, held(s));
         if (last && final_in_buffer) r->tile = std::max(r->tile, s.bytes());
         if (l.op == VAE_OP_RES_RMS || l.op == VAE_OP_RMS_SILU) {
             Shape g = cur;
             g.dtype = l.op == VAE_OP_RES_RMS ? d.dtype : gn_silu_dtype(d, (int)i);
-            r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
+            r->act = std::max(r->act, std::max(held(cur), held(g)));
+            if (l.op == VAE_OP_RES_RMS) {
+                carry(g);    // conv1 and conv2 read bf16 norm outputs of cur's grid
+                carry(g);
+            }
         }
         if (l.op == VAE_OP_ATTN)
             r->attn = std::max<int64_t>(r->attn,
@@ -335,7 +356,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
         if (l.op == VAE_OP_RES || l.op == VAE_OP_GN_SILU) {
             Shape g = cur;
             g.dtype = l.op == VAE_OP_RES ? d.dtype : gn_silu_dtype(d, (int)i);
-            r->act = std::max(r->act, std::max(cur.bytes(), g.bytes()));
+            r->act = std::max(r->act, std::max(held(cur), held(g)));
             vae_tensor_t x = tensor_of(nullptr, cur);
             const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw, &exact);
             r->gn = std::max<int64_t>(r->gn, (int64_t)gn_stats_workspace(x, bl, d.groups));
@@ -383,8 +404,12 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
                     r->splitk, (int64_t)conv_split_bytes(x, cout, bl.b[b], n));
             }
         };
-        if (l.op == VAE_OP_CONV)
+        if (l.op == VAE_OP_CONV) {
             split(cur, l.cout, conv_splits(d.flags, d.layers.data(), (int)d.layers.size(), (int)i));
+            Shape xs = cur;              // its input, at most 4 bytes a value
+            xs.dtype = VAE_DTYPE_F32;
+            carry(xs);
+        }
         if (l.op == VAE_OP_RES || l.op == VAE_OP_RES_RMS) {
             Shape xs = cur;
             xs.dtype = d.dtype;
@@ -441,7 +466,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
 }
 
 struct Layout {
-    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, status, total;
+    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, carry, status, total;
     int64_t act_bytes;
 };
 
@@ -467,6 +492,8 @@ Layout layout_of(const Req& r) {
     off += align_up((size_t)r.tile, 256);
     L.attn = off;
     off += align_up((size_t)r.attn, 256);
+    L.carry = off;
+    off += align_up((size_t)r.carry, 256);
     L.status = off;          // the decode's status word (vae_decode_status)
     off += 256;
     L.total = off;
@@ -496,6 +523,11 @@ struct Runner {
     }
 
     bool stats_ready = false;  // mean/rstd already hold the statistics of the next GN's input
+    // Clip-by-clip decode: activations keep kCarry frames of headroom, where every causal conv
+    // puts its carried input frames (copies of frame 0 in the first clip).
+    bool clips = false;
+    bool first_clip = true;
+    size_t carry_off = 0;      // next conv's carried frames in the workspace (per run)
     // The decode's status word in the workspace: set when a norm's statistics are not finite.
     uint32_t* status() { return reinterpret_cast<uint32_t*>(ws + L.status); }
     bool per_patch = false;    // launch every conv, GroupNorm pass and upsampling per patch box
@@ -587,7 +619,33 @@ struct Runner {
         }
         const int32_t k = up ? up->st * up->sh * up->sw : 1;
         const int64_t cout = y.c * k;
-        vae_tensor_t xl = x;                       // the conv's input grid
+        // In a clip-by-clip decode x sits kCarry frames past the start of its buffer: put the
+        // carried frames there (copies of frame 0 in the first clip, the causal padding) and run
+        // the conv over the extended clip, writing only the clip's own frames.
+        vae_tensor_t xe = x;
+        int32_t t0 = 0, tdrop = -1;
+        uint8_t* carry = nullptr;
+        const int64_t fb = Shape{x.n, x.t, x.h, x.w, x.c, x.dtype}.frame_bytes();
+        if (clips) {
+            if (!conv_uses_mfma_c(x, cout, d->dtype))
+                return fail(VAE_ERR_UNSUPPORTED, "a clip-by-clip decode runs its convs on the "
+                                                 "matrix cores (bf16, 32k input channels)");
+            uint8_t* head = static_cast<uint8_t*>(x.data) - kCarry * fb;
+            carry = ws + L.carry + carry_off;
+            carry_off += align_up((size_t)(kCarry * fb), 256);
+            if (first_clip) {
+                for (int64_t f = 0; f < kCarry; ++f)
+                    VAE_TRY(launch_copy(head + f * fb, x.data, fb, s));
+            } else {
+                VAE_TRY(launch_copy(head, carry, kCarry * fb, s));
+            }
+            xe.data = head;
+            xe.t = x.t + kCarry;
+            t0 = (int32_t)kCarry;
+            const int32_t st = up ? up->st : 1;
+            tdrop = (int32_t)kCarry * st + (first_clip ? st - 1 : 0);
+        }
+        vae_tensor_t xl = xe;                      // the conv's input grid
         xl.h <<= lsh;
         xl.w <<= lsw;
         BoxList launches;                          // one launch per entry
@@ -595,7 +653,13 @@ struct Runner {
             launches = bl;
         } else {
             launches.n = 1;
-            launches.b[0] = whole_box(xl);
+            launches.b[0] = whole_box(x);
+            launches.b[0].h1 = (int32_t)xl.h;
+            launches.b[0].w1 = (int32_t)xl.w;
+        }
+        for (int i = 0; i < launches.n; ++i) {    // the clip's own frames of the extended grid
+            launches.b[i].t0 += t0;
+            launches.b[i].t1 += t0;
         }
         int64_t slots[kMaxBoxes], total = 0;
         for (int i = 0; i < launches.n; ++i) {
@@ -603,7 +667,7 @@ struct Runner {
             if (b.t0 < 0 || b.h0 < 0 || b.w0 < 0 || b.t1 > xl.t || b.h1 > xl.h || b.w1 > xl.w ||
                 b.volume() <= 0)
                 return fail(VAE_ERR_INVALID_ARG, "conv patch box outside the activation");
-            slots[i] = gn_next ? conv_gn_slots(x, y.c, d->dtype, b, d->groups, k) : 0;
+            slots[i] = gn_next ? conv_gn_slots(xe, y.c, d->dtype, b, d->groups, k) : 0;
             total += slots[i];
         }
         double* part = reinterpret_cast<double*>(ws + L.gn);
@@ -616,12 +680,13 @@ struct Runner {
                         up ? up->sw : 1, lsh, lsw};
             fz.slot0 = slot0;
             fz.slot_stride = total;
+            fz.tdrop = tdrop;
             // a launch too small to fill the chip splits its K dimension over the scratch
             fz.splits = conv_split_count(xl, cout, d->dtype, b, (cf & VAE_CONV_SPLIT_FP32) != 0);
             if (fz.splits > 1) fz.part = reinterpret_cast<float*>(ws + L.splitk);
             slot0 += slots[i];
-            VAE_TRY(launch_conv3d(x, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]), res,
-                                  y, b, cf, s, &fz));
+            VAE_TRY(launch_conv3d(xe, w, d->dtype, static_cast<const float*>(d->ptrs[wi + 1]),
+                                  res, y, b, cf, s, &fz));
             const double pos = (double)b.volume() * x.n;
             const double flops = 2.0 * 27.0 * (double)x.c * (double)cout * pos;
             // input read once (at its own resolution), output (and residual) once
@@ -629,6 +694,8 @@ struct Runner {
                                  (double)b.volume() * out_pos;
             VAE_TRY(mark_patch(i, VAE_KIND_CONV, layer, flops, bytes));
         }
+        if (clips)   // the last kCarry frames of the extended input carry on to the next clip
+            VAE_TRY(launch_copy(carry, static_cast<uint8_t*>(xe.data) + x.t * fb, kCarry * fb, s));
         if (total > 0) {
             // merged into mean/rstd here (all patches, in a fixed order); timed as shared work
             VAE_TRY(launch_gn_finalize_slots(part, total, (int32_t)y.n, d->groups, d->eps,
@@ -717,14 +784,26 @@ struct Runner {
     vae_status_t run(const vae_tensor_t& in, const std::vector<Box>& boxes,
                      const vae_tensor_t& final_out) {
         std::vector<Shape> shapes;
-        walk(*d, shape_of(in), &shapes, nullptr, nullptr, nullptr);
+        VAE_TRY(walk(*d, shape_of(in), &shapes, nullptr, nullptr, nullptr,
+                     !clips || first_clip));
         stats_ready = false;
+        carry_off = 0;
         vae_tensor_t cur = in;
         int cur_buf = -1;  // -1: the caller's input, never written
         int ch = 1, cw = 1, fh = 1, fw = 1;
         int32_t near_lsh = 0, near_lsw = 0;   // a nearest upsampling the next conv reads
         size_t p = 0;
-        auto buf = [&](int i, const Shape& sh) { return tensor_of(ws + L.buf[i], sh); };
+        // a buffer's tensor; in a clip-by-clip decode it starts kCarry frames into the buffer
+        auto buf = [&](int i, const Shape& sh) {
+            return tensor_of(ws + L.buf[i] + (clips ? kCarry * sh.frame_bytes() : 0), sh);
+        };
+        if (clips) {
+            // the clip's latent goes into a buffer too, so that its first conv has headroom
+            vae_tensor_t c = buf(0, shape_of(in));
+            VAE_TRY(launch_copy(c.data, in.data, shape_of(in).bytes(), s));
+            cur = c;
+            cur_buf = 0;
+        }
         auto free_buf = [&](int avoid1, int avoid2) {
             for (int i = 0; i < 3; ++i)
                 if (i != avoid1 && i != avoid2) return i;
@@ -882,6 +961,10 @@ struct Runner {
                 cur = y;
                 cur_buf = last ? -2 : nb;
             } else {  // D2S / NEAREST
+                if (clips && l.op == VAE_OP_D2S && l.st > 1)
+                    return fail(VAE_ERR_UNSUPPORTED,
+                                "a clip-by-clip decode needs its temporal depth-to-space fused into "
+                                "a matrix-core conv");
                 const int nb = free_buf(cur_buf, -1);
                 vae_tensor_t y = last ? final_out : buf(nb, os);
                 const int mode = l.op == VAE_OP_D2S ? VAE_UPSAMPLE_D2S : VAE_UPSAMPLE_NEAREST;
@@ -905,6 +988,11 @@ vae_status_t plan_output(const vae_decoder& d, const vae_tiling_desc_t& desc, Sh
     VAE_TRY(walk(d, in, &shapes, st, sh, sw));
     *out = shapes.back();
     return VAE_OK;
+}
+
+// Whether a decode runs clip by clip: a patch-halo decode longer than the decoder's clip.
+bool clipped(const vae_decoder& d, const vae_tiling_desc_t& desc) {
+    return d.clip > 0 && desc.mode == VAE_TILING_PATCH_HALO && desc.t > d.clip;
 }
 
 vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layout* L,
@@ -937,8 +1025,12 @@ vae_status_t size_for(const vae_decoder& d, const vae_tiling_desc_t& desc, Layou
         for (const vae_tile_t& t : *tiles)
             boxes.push_back(Box{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
                                 t.latent.w1});
-        VAE_TRY(requirements(d, Shape{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype}, boxes,
-                             false, &r));
+        if (clipped(d, desc))   // sized for one clip without the frame drop, plus headroom
+            VAE_TRY(requirements(d, Shape{desc.n, d.clip, desc.h, desc.w, d.latent_c, d.dtype},
+                                 boxes, false, &r, kCarry));
+        else
+            VAE_TRY(requirements(d, Shape{desc.n, desc.t, desc.h, desc.w, d.latent_c, d.dtype},
+                                 boxes, false, &r));
     } else {
         for (const vae_tile_t& t : *tiles) {
             Shape in{desc.n, t.latent.t1 - t.latent.t0, t.latent.h1 - t.latent.h0,
@@ -1229,7 +1321,31 @@ VAE_API vae_status_t vae_decode_tiled(const vae_decoder_t* dec_c, const vae_tens
             boxes.push_back(Box{t.latent.t0, t.latent.t1, t.latent.h0, t.latent.h1, t.latent.w0,
                                 t.latent.w1});
         r.per_patch = dec->launch == VAE_LAUNCH_PER_PATCH && boxes.size() > 1;
-        VAE_TRY(r.run(*latent, boxes, *out));
+        if (!clipped(*dec, *desc)) {
+            VAE_TRY(r.run(*latent, boxes, *out));
+            return VAE_OK;
+        }
+        // clip by clip: clip c decodes latent frames [c0, c0 + n) into output frames
+        // [o0, o1), each conv carrying its last two input frames into the next clip
+        if (latent->n != 1)
+            return fail(VAE_ERR_UNSUPPORTED, "a clip-by-clip decode takes one sample");
+        const int64_t R = desc->scale_t;
+        const int64_t lf = Shape{latent->n, 1, latent->h, latent->w, latent->c,
+                                 latent->dtype}.frame_bytes();
+        const int64_t of = Shape{out->n, 1, out->h, out->w, out->c, out->dtype}.frame_bytes();
+        r.clips = true;
+        for (int64_t c0 = 0, c = 0; c0 < latent->t; c0 += dec->clip, ++c) {
+            const int64_t n = std::min<int64_t>(dec->clip, latent->t - c0);
+            const int64_t o0 = c0 == 0 ? 0 : (c0 - 1) * R + 1, o1 = (c0 + n - 1) * R + 1;
+            vae_tensor_t lc = *latent, oc = *out;
+            lc.data = static_cast<uint8_t*>(latent->data) + c0 * lf;
+            lc.t = n;
+            oc.data = static_cast<uint8_t*>(out->data) + o0 * of;
+            oc.t = o1 - o0;
+            r.first_clip = c0 == 0;
+            r.tile = (int32_t)c;
+            VAE_TRY(r.run(lc, boxes, oc));
+        }
     } else {
         AxisTiling ax[3];
         overlap_axes(*desc, ax);
@@ -1267,6 +1383,24 @@ VAE_API vae_status_t vae_decoder_set_launch(vae_decoder_t* dec, int32_t launch) 
     if (launch != VAE_LAUNCH_MERGED && launch != VAE_LAUNCH_PER_PATCH)
         return fail(VAE_ERR_INVALID_ARG, "launch must be VAE_LAUNCH_MERGED or VAE_LAUNCH_PER_PATCH");
     dec->launch = launch;
+    return VAE_OK;
+}
+
+VAE_API vae_status_t vae_decoder_set_clip_frames(vae_decoder_t* dec, int32_t frames) {
+    clear_error();
+    if (!dec) return fail(VAE_ERR_INVALID_ARG, "decoder is NULL");
+    if (frames < 0) return fail(VAE_ERR_INVALID_ARG, "clip frames must be >= 0", -1, frames);
+    if (frames > 0) {
+        if (dec->dtype != VAE_DTYPE_BF16)
+            return fail(VAE_ERR_UNSUPPORTED, "a clip-by-clip decode needs a bf16 plan");
+        for (const vae_layer_desc_t& l : dec->layers)
+            if (l.op != VAE_OP_CONV && l.op != VAE_OP_RES_RMS && l.op != VAE_OP_RMS_SILU &&
+                l.op != VAE_OP_ATTN && l.op != VAE_OP_D2S && l.op != VAE_OP_NEAREST)
+                return fail(VAE_ERR_UNSUPPORTED,
+                            "a clip-by-clip decode takes convs, RMS norms, frame attention and "
+                            "upsamplings only (GroupNorm statistics span every frame)");
+    }
+    dec->clip = frames;
     return VAE_OK;
 }
 

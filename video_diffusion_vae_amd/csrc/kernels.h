@@ -39,6 +39,9 @@ struct ConvFuse {
     int64_t slot0 = 0, slot_stride = 0;
     float* part = nullptr;
     int32_t splits = 1;
+    // Frames of the depth-to-space output dropped before y's frame 0 (see MfmaArgs::tdrop);
+    // -1: st - 1, the causal drop.
+    int32_t tdrop = -1;
 };
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
@@ -143,6 +146,8 @@ vae_status_t launch_merge_finalize(const vae_tensor_t& out, const AxisTiling& at
                                    const AxisTiling& ah, const AxisTiling& aw,
                                    hipStream_t stream);
 vae_status_t launch_zero(void* p, int64_t bytes, hipStream_t stream);
+// A device-to-device copy of `bytes` (16-byte aligned pointers and size), as a kernel.
+vae_status_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 // Copy x[:, box] (latent grid) into the dense tensor y (shape of the box).
 vae_status_t launch_crop(const vae_tensor_t& x, const Box& box, const vae_tensor_t& y,
                          hipStream_t stream);

@@ -155,6 +155,14 @@ __global__ __launch_bounds__(64) void zero_tail_kernel(uint8_t* p, int64_t n) {
     if ((int64_t)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
+// dst[i] = src[i] for n 16-byte words; the ranges must not overlap.
+__global__ __launch_bounds__(kThreads) void copy_kernel(uint4* __restrict__ dst,
+                                                        const uint4* __restrict__ src, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * kThreads)
+        dst[i] = src[i];
+}
+
 // grid (box rows, N): copy one contiguous row segment of bytes.
 __global__ __launch_bounds__(kThreads) void crop_kernel(const uint8_t* __restrict__ x,
                                                         uint8_t* __restrict__ y, int32_t T,
@@ -251,6 +259,18 @@ vae_status_t launch_zero(void* p, int64_t bytes, hipStream_t stream) {
                            static_cast<uint8_t*>(p) + n16 * 16, bytes % 16);
         VAE_HIP_CHECK(hipGetLastError());
     }
+    return VAE_OK;
+}
+
+vae_status_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+    if (bytes <= 0) return VAE_OK;
+    if ((uintptr_t)dst % 16 || (uintptr_t)src % 16 || bytes % 16)
+        return fail(VAE_ERR_INVALID_ARG, "copy: pointers and size must be 16-byte multiples");
+    const int64_t n16 = bytes / 16;
+    const int64_t blocks = std::min<int64_t>(ceil_div(n16, kThreads), 65536);
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16);
+    VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
 
