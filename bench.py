@@ -118,7 +118,9 @@ def activations_note(operands):
     return "fp32 between ops, bf16 norm outputs inside res blocks"
 
 
-def workload_name(kind, mode, tile_t=0, stride_t=0):
+def workload_name(kind, mode, tile_t=0, stride_t=0, clip=0):
+    if clip and mode in ("patch", "per_patch"):
+        return workload_name(kind, mode) + f"_causal_clips_of_{clip}"
     if kind in ("ltx2_enc", "ltx2_enc_strided"):
         prefix = "ltx2_720p_encode_" + ("strided_" if kind == "ltx2_enc_strided" else "")
         return prefix + ("untiled" if mode == "patch" else "overlap_blend_2x3")
@@ -388,6 +390,12 @@ def main():
                     help="overlap mode: also cut T into clips of this many latent frames")
     ap.add_argument("--stride-t", type=int, default=0,
                     help="overlap mode: latent frames between clip starts (below --tile-t)")
+    ap.add_argument("--clip", type=int, default=0,
+                    help="patch modes: decode in causal clips of this many latent frames, each "
+                         "conv carrying its last two input frames (plans without GroupNorm)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one decode in a HIP graph and time its replays; value "
+                         "is then the replayed decode's rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames of the oracle's sample (default 2 for ltx2, 1 for wan)")
@@ -430,9 +438,15 @@ def main():
     dec = v.upload_decoder(spec, params, dev, operands=args.operands)
     if args.mode == "per_patch":
         dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
+    if args.clip:
+        if args.mode == "overlap":
+            print("--clip is for the patch modes (--tile-t cuts overlap tiles in T)",
+                  file=sys.stderr)
+            sys.exit(2)
+        dec.set_clip_frames(args.clip)
     zp = v.pad_latent(z, spec)            # zero channels up to a multiple of 32 (48 -> 64)
     zd = torch.as_tensor(zp).to(device=dev, dtype=torch.bfloat16)
-    workload = workload_name(args.workload, args.mode, args.tile_t, args.stride_t)
+    workload = workload_name(args.workload, args.mode, args.tile_t, args.stride_t, args.clip)
     if args.mode in ("patch", "per_patch"):
         if encoder and args.mode == "per_patch":
             print("--workload ltx2_enc runs untiled or overlap-tiled", file=sys.stderr)
@@ -454,6 +468,29 @@ def main():
     torch.cuda.synchronize(dev)
     log(f"[bench] {args.warmup} warmup steps done")
 
+    graph_ms = None
+    if args.graph:
+        # the decode enqueues kernels only, so the whole launch sequence (every layer, patch and
+        # clip) captures into one graph; timed over the replays alone
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            dec.vae_decode_tiled(zd, desc, out, ws)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dec.vae_decode_tiled(zd, desc, out, ws)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        graph_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+        del graph
+        log(f"[bench] {args.steps} graph replays: {graph_ms:.2f} ms/step")
+
     dec.set_timing(True)
     per_op, step_s, enqueue_s = [], [], []
     torch.cuda.synchronize(dev)
@@ -468,6 +505,9 @@ def main():
     elapsed = time.perf_counter() - t0
     dec.set_timing(False)
     ms = elapsed * 1000.0 / args.steps
+    eager_ms = ms
+    if graph_ms is not None:
+        ms = graph_ms
     video = z.shape if encoder else out_shape          # pixel-frames of the video side
     px = video[1] * video[2] * video[3]
     value = px / (ms / 1000.0) / 1e6
@@ -512,6 +552,9 @@ def main():
     timing = {"step_ms_p10": round(pct(step_s, 10), 3), "step_ms_p50": round(pct(step_s, 50), 3),
               "step_ms_p90": round(pct(step_s, 90), 3),
               "host_enqueue_ms_p50": round(pct(enqueue_s, 50), 3)}
+    if graph_ms is not None:
+        timing["graph_replay_ms_per_step"] = round(graph_ms, 3)
+        timing["eager_ms_per_step"] = round(eager_ms, 3)
 
     passes = standalone_passes(v, dev) if args.workload == "ltx2" else None
     for name, p in (passes or {}).items():
@@ -521,7 +564,7 @@ def main():
     # shape: the launches one rank of the split runs, timed inside a per-patch decode.
     quarter = None
     if args.workload in ("ltx2", "wan") and args.mode in ("patch", "per_patch") and \
-            not args.no_quarter:
+            not args.no_quarter and not args.clip:
         if args.mode == "per_patch":
             q_ops, q_steps = per_op, args.steps
         else:
@@ -558,7 +601,9 @@ def main():
                    ("input" if encoder else "latent"): list(spec["input" if encoder else "latent"]),
                    "output": [out_shape[0], out_shape[4]] + list(out_shape[1:4]),
                    "parallelism": "none (1 GPU)",
-                   "launch": LAUNCH_NOTE[args.mode],
+                   "launch": LAUNCH_NOTE[args.mode] + (
+                       f"; causal clips of {args.clip} latent frames" if args.clip else "") + (
+                       "; replayed from a HIP graph" if args.graph else ""),
                    "operands": OPERANDS[args.operands],
                    "activations": activations_note(args.operands),
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},

@@ -2,9 +2,9 @@
 
 vae_decode_tiled enqueues kernels only: no allocation, copy, memset, event or synchronisation
 (with op timing off). A caller can therefore capture a whole decode, every layer of every
-patch or tile, in one graph and replay it with a single launch. Each replay below runs after
-eager work that overwrites the output and the whole workspace, and must equal the eager decode
-bit for bit.
+patch, tile or causal clip, in one graph and replay it with a single launch. Each replay below
+runs after eager work that overwrites the output and the whole workspace, and must equal the
+eager decode bit for bit.
 """
 import pytest
 
@@ -31,6 +31,11 @@ CASES = [
     ("ltx2_enc_small", "patch", dict(patches=(1, 1))),             # the encoder, untiled
     ("ltx2_enc_small", "patch", dict(patches=(2, 2), down=(8, 32, 32))),
     ("ltx2_enc_small", "overlap", dict(down=(8, 32, 32))),         # latent-grid tiles
+    # every conv, GroupNorm pass and upsampling launched per patch box
+    ("ltx2_tiny", "patch", dict(patches=(2, 2), launch="per_patch")),
+    # causal clips, each conv carrying its last two input frames (merged and per patch)
+    ("wan_tiny", "patch", dict(patches=(2, 2), clip=1)),
+    ("wan_tiny", "patch", dict(patches=(2, 2), clip=2, launch="per_patch")),
 ]
 
 
@@ -42,6 +47,11 @@ def test_decode_replays_from_a_hip_graph(v, name, mode, kw):
     zp = v.pad_latent(z, spec)
     zd = dev(zp, spec["dtype"])
     dec = v.upload_decoder(spec, vae_synth.decoder_params(spec))
+    kw = dict(kw)
+    if kw.pop("launch", None) == "per_patch":
+        dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
+    if "clip" in kw:
+        dec.set_clip_frames(kw.pop("clip"))
     scale = spec.get("scale", (1, 1, 1))
     if mode == "patch":
         desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, zp.shape, scale, **kw)
