@@ -396,6 +396,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also capture one decode in a HIP graph and time its replays; value "
                          "is then the replayed decode's rate")
+    ap.add_argument("--norm-in-conv", action="store_true",
+                    help="the convs apply GroupNorm + SiLU while staging their input instead of "
+                         "separate normalise passes (VAE_DECODE_NORM_IN_CONV)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="latent frames of the oracle's sample (default 2 for ltx2, 1 for wan)")
@@ -435,7 +438,8 @@ def main():
     out_shape = output_shape(spec, z.shape)
     params = vae_synth.decoder_params(spec)
     dev = torch.device("cuda:0")
-    dec = v.upload_decoder(spec, params, dev, operands=args.operands)
+    dec = v.upload_decoder(spec, params, dev, operands=args.operands,
+                           norm_in_conv=args.norm_in_conv)
     if args.mode == "per_patch":
         dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
     if args.clip:
@@ -603,7 +607,8 @@ def main():
                    "parallelism": "none (1 GPU)",
                    "launch": LAUNCH_NOTE[args.mode] + (
                        f"; causal clips of {args.clip} latent frames" if args.clip else "") + (
-                       "; replayed from a HIP graph" if args.graph else ""),
+                       "; replayed from a HIP graph" if args.graph else "") + (
+                       "; GroupNorm applied in conv staging" if args.norm_in_conv else ""),
                    "operands": OPERANDS[args.operands],
                    "activations": activations_note(args.operands),
                    "conv_tflop_per_step": round(conv_flops(spec, z.shape) / 1e12, 3)},

@@ -183,6 +183,19 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
  * deterministic and differs from the unsplit conv only in the order of the fp32 additions. The
  * workspace query includes those bytes when the flag is given.
  *
+ * Input GroupNorm + SiLU (in_scale_shift non-NULL): the conv reads silu(x * scale_c + shift_c)
+ * instead of x, with [N][Cin][2] fp32 (scale, shift) per (sample, input channel) as
+ * vae_groupnorm_scale_shift writes them (device, 16-byte aligned). Each value is formed as its
+ * input tile is staged and rounded to the operand type (bf16; fp16 with
+ * VAE_CONV_PACKED_F16_WEIGHTS), exactly as vae_groupnorm_apply would have stored it: the result
+ * equals vae_groupnorm_apply into a bf16 (fp16) tensor followed by the conv, without writing and
+ * re-reading that tensor. The zero padding at the image borders pads the normalised tensor. The
+ * pages name the fusion of the norm and SiLU into neighbouring kernels as a decode speed-up (P5,
+ * conversation on the native Wan VAE's kernel fusions). Needs the MFMA path with packed weights
+ * and no VAE_CONV_SPLIT_FP32:
+ * x fp32 with VAE_CONV_PACKED_WEIGHTS or VAE_CONV_PACKED_F16_WEIGHTS, or x fp16 with
+ * VAE_CONV_PACKED_WEIGHTS (UNSUPPORTED otherwise).
+ *
  * Errors: those of vae_conv3d_causal; INVALID_ARG when y's shape does not match the factors;
  * UNSUPPORTED for a depth-to-space or an input upsampling off the MFMA path, for an input
  * upsampling factor that is not a power of two, for a channel count not divisible by gn_groups,
@@ -205,6 +218,7 @@ typedef struct vae_conv_fused {
     void* ws;
     size_t ws_bytes;
     int32_t in_up_sh, in_up_sw;     /* nearest upsampling of x read by the conv; 0 = none */
+    const float* in_scale_shift;    /* input GroupNorm + SiLU, [N][Cin][2] fp32, device; or NULL */
 } vae_conv_fused_t;
 VAE_API vae_status_t vae_conv3d_causal_fused_workspace(const vae_conv_fused_t* args,
                                                        size_t* bytes);
@@ -334,6 +348,21 @@ VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t*
                                          int32_t groups, const float* mean_rstd,
                                          const float* gamma, const float* beta,
                                          int32_t apply_silu, vae_tensor_t* y, vae_stream_t stream);
+
+/* The normalise step as a per-channel affine map, for a conv that applies it while staging its
+ * input (vae_conv_fused_t.in_scale_shift): scale_shift[N][channels][2] fp32 (device, 16-byte
+ * aligned) receives, for channel c of group g = c / (channels / groups),
+ *   scale = rstd[n][g] * gamma[c],  shift = beta[c] - mean[n][g] * scale
+ * (gamma = NULL reads as 1, beta = NULL as 0), from mean_rstd[N][groups][2] as
+ * vae_groupnorm_combine writes it. silu(x * scale + shift) is then exactly the value
+ * vae_groupnorm_apply(apply_silu = 1) computes for x (P4, PatchGroupNorm commit: the global
+ * mean and biased variance). INVALID_ARG for n < 0,
+ * groups < 1, channels not a multiple of groups or of 8, a NULL mean_rstd or scale_shift, or a
+ * misaligned scale_shift. */
+VAE_API vae_status_t vae_groupnorm_scale_shift(const float* mean_rstd, int32_t n, int32_t channels,
+                                               int32_t groups, const float* gamma,
+                                               const float* beta, float* scale_shift,
+                                               vae_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* RMS norm and frame attention (Wan-style decoders)                                          */
@@ -526,6 +555,15 @@ VAE_API vae_status_t vae_tile_merge(const vae_tensor_t* tile_out, const vae_tile
  * output of the first conv of each RES and RES_RMS block, which only its block's second norm
  * reads, in fp16 instead of fp32 (half the bytes written and read back). Activations must stay
  * below 65504 in magnitude in both places.
+ * VAE_DECODE_NORM_IN_CONV: GroupNorm apply + SiLU is done by the conv that reads the norm's
+ * output, while it stages its input (vae_conv_fused_t.in_scale_shift), wherever that conv runs
+ * on the matrix cores with packed weights (vae_decoder_pack_weights) and without the fp32 split,
+ * reading fp32 (or fp16 with bf16 weights): the first and second norm of every RES block and a
+ * GN_SILU followed by a CONV. The normalised tensor is then never written; the results are the
+ * same bit for bit. The norm's statistics still come from the producing conv's epilogue (or a
+ * statistics pass). Off by default: on gfx950 those convs then stage through their tile buffer
+ * instead of the faster frame ring (which has no registers left for the norm beside 128-channel
+ * tiles), and the decode is slower overall than with separate normalise passes.
  * The parameter pointers come in plan order:
  *  conv, conv_down -> (weight, bias);
  *  GN or RMS -> (gamma, beta);
@@ -547,12 +585,14 @@ typedef struct vae_layer_desc {
     int32_t pad;       /* VAE_OP_CONV_DOWN: VAE_PAD_AROUND or VAE_PAD_AFTER; 0 otherwise */
 } vae_layer_desc_t;
 
-enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1, VAE_DECODE_F16_OPERANDS = 2 };
+enum { VAE_DECODE_SPLIT_FP32_OPERANDS = 1, VAE_DECODE_F16_OPERANDS = 2,
+       VAE_DECODE_NORM_IN_CONV = 4 };
 typedef struct vae_decoder_spec {
     int32_t dtype;              /* weights and convolution operands: VAE_DTYPE_* */
     int32_t act_dtype;          /* activations stored between ops (conv outputs, residual
                                    stream): VAE_DTYPE_F32 */
-    int32_t flags;              /* VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS or 0 */
+    int32_t flags;              /* VAE_DECODE_SPLIT_FP32_OPERANDS or VAE_DECODE_F16_OPERANDS,
+                                   plus VAE_DECODE_NORM_IN_CONV; or 0 */
     int32_t latent_channels;
     int32_t groups;
     float eps;

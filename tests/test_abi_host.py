@@ -379,6 +379,34 @@ def test_fused_conv_validation_needs_no_gpu(v):
     with pytest.raises(v.VaeError) as e:          # factors must be powers of two
         v.vae_conv3d_causal_fused_workspace(x, w, y, d2s=(2, 2, 2), in_up=(3, 1))
     assert e.value.status == v.VAE_ERR_UNSUPPORTED
+    # an input GroupNorm: fp32 (or fp16 with bf16-packed weights), packed weights, no fp32 split
+    xf = torch.zeros((1, 2, 4, 8, 64), dtype=torch.float32)
+    xh = torch.zeros((1, 2, 4, 8, 64), dtype=torch.float16)
+    ab = torch.zeros((1, 64, 2), dtype=torch.float32)
+    P, PH = v.VAE_CONV_PACKED_WEIGHTS, v.VAE_CONV_PACKED_F16_WEIGHTS
+    for xx, fl in ((xf, P), (xf, PH), (xh, P)):
+        assert v.vae_conv3d_causal_fused_workspace(xx, w, y, d2s=(2, 2, 2), flags=fl,
+                                                   in_scale_shift=ab) == 0
+    for xx, fl, status in ((xf, 0, v.VAE_ERR_UNSUPPORTED),                 # standard weights
+                           (xf, P | v.VAE_CONV_SPLIT_FP32, v.VAE_ERR_UNSUPPORTED),
+                           (x, P, v.VAE_ERR_UNSUPPORTED),                  # bf16 x
+                           (xh, PH, v.VAE_ERR_UNSUPPORTED)):               # fp16 x, fp16 weights
+        with pytest.raises(v.VaeError) as e:
+            v.vae_conv3d_causal_fused_workspace(xx, w, y, d2s=(2, 2, 2), flags=fl,
+                                                in_scale_shift=ab)
+        assert e.value.status == status, (xx.dtype, fl)
+    with pytest.raises(v.VaeError) as e:          # the scale and shift must be 16-byte aligned
+        v.vae_conv3d_causal_fused_workspace(xf, w, y, d2s=(2, 2, 2), flags=P,
+                                            in_scale_shift=ab.view(-1)[1:])
+    assert e.value.status == v.VAE_ERR_INVALID_ARG
+    # vae_groupnorm_scale_shift refuses before launching: channels not a multiple of groups, a
+    # misaligned output
+    mr = ctypes.c_void_p(1 << 40)
+    assert v.LIB.vae_groupnorm_scale_shift(mr, 1, 60, 8, None, None, ctypes.c_void_p(1 << 41),
+                                           None) == v.VAE_ERR_INVALID_ARG
+    assert v.LIB.vae_groupnorm_scale_shift(mr, 1, 64, 8, None, None,
+                                           ctypes.c_void_p((1 << 41) + 4),
+                                           None) == v.VAE_ERR_INVALID_ARG
 
 
 def test_space_to_depth_validation_needs_no_gpu(v):

@@ -286,6 +286,43 @@ def test_packed_and_standard_weights_decode_identically(v, operands):
     assert torch.equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("name,patches,launch,operands", [
+    ("ltx2_tiny", (1, 2), "merged", "f16"),
+    ("ltx2_tiny", (2, 2), "per_patch", "f16"),
+    ("ltx2_tiny", (1, 2), "merged", "bf16"),
+    ("ltx2_tiny_n2", (1, 1), "merged", "f16"),
+    ("mixed_rms_gn", (1, 2), "per_patch", "f16"),
+    ("mixed_rms_gn", (1, 1), "merged", "bf16"),
+])
+def test_norm_in_conv_staging_decodes_identically(v, name, patches, launch, operands):
+    """With VAE_DECODE_NORM_IN_CONV every GroupNorm that a packed MFMA conv can apply while
+    staging (both norms of each residual block, the GN_SILU before conv_out) gives the decode of
+    separate normalise passes bit for bit, with no normalise pass left."""
+    import torch
+    spec = spec_of(name)
+    z = ndhwc(vae_synth.latent(spec))
+    zd = dev(z, "bf16")
+    desc = v.tiling_desc(v.VAE_TILING_PATCH_HALO, z.shape, spec["scale"], patches=patches)
+    outs, kinds = [], []
+    for fused in (False, True):
+        dec = v.upload_decoder(spec, params_of(name), operands=operands, norm_in_conv=fused)
+        if launch == "per_patch":
+            dec.set_launch(v.VAE_LAUNCH_PER_PATCH)
+        dec.set_timing(True)
+        ws = torch.empty(dec.workspace_size(desc), dtype=torch.uint8, device="cuda")
+        out = torch.full(oracle.output_shape(spec, z.shape), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        dec.vae_decode_tiled(zd, desc, out, ws)
+        torch.cuda.synchronize()
+        gn_bytes = sum(r["bytes"] for r in dec.timing() if r["kind"] == "gn")
+        outs.append(out)
+        kinds.append(gn_bytes)
+        dec.close()
+    assert torch.equal(outs[0], outs[1])
+    assert kinds[1] < kinds[0]        # the normalise passes are gone
+    _bf16_bar(host(outs[1]), oracle_out(name, "whole"))
+
+
 # ------------------------------------------------------------------------------------------------
 # Per-patch launches: every conv, GroupNorm pass and upsampling once per patch box, over that box
 # only, with the GroupNorm statistics merged across the boxes (one rank's share of a patch split).

@@ -864,3 +864,126 @@ def test_conv3d_folded_nearest_upsampling(v, case):
     bx = bx or (0, t, 0, h * sh, 0, w * sw)
     sl = (slice(None), slice(bx[0], bx[1]), slice(bx[2], bx[3]), slice(bx[4], bx[5]))
     assert rel_max_abs(host(y1)[sl], ref[sl]) <= 1e-4
+
+
+# GroupNorm + SiLU applied by the conv while it stages its input (in_scale_shift).
+# (N, T, H, W), Cin, C (after the depth-to-space), d2s, x dtype, operand dtype, y dtype,
+# residual, box, groups, split over K
+NORM_IN_CASES = [
+    ((1, 3, 9, 17), 64, 128, (1, 1, 1), "f32", "bf16", "f32", True, None, 32, False),
+    ((1, 5, 10, 20), 128, 128, (1, 1, 1), "f16", "bf16", "f16", False, None, 32, False),
+    ((2, 2, 8, 16), 32, 48, (1, 1, 1), "f32", "f16", "f32", False, None, 8, False),   # conv_out
+    ((1, 4, 11, 23), 256, 256, (1, 1, 1), "f16", "bf16", "f32", True, (1, 4, 2, 9, 5, 15), 32,
+     False),
+    ((1, 3, 6, 10), 128, 32, (2, 2, 2), "f32", "bf16", "f32", False, None, 32, False),  # d2s
+    ((1, 16, 22, 10), 256, 256, (1, 1, 1), "f16", "bf16", "f32", True, None, 32, True),
+    ((1, 2, 16, 4), 64, 64, (1, 1, 1), "f32", "bf16", "bf16", False, None, 16, False),  # narrow
+]
+
+
+@pytest.mark.parametrize("case", NORM_IN_CASES)
+def test_conv3d_applies_input_groupnorm(v, case):
+    """The conv reads silu(x * scale + shift) (the scale and shift of a GroupNorm from
+    vae_groupnorm_scale_shift), rounding it to its operand type while staging: bit for bit what
+    vae_groupnorm_apply into a bf16 (fp16) tensor followed by the conv gives, and the oracle's
+    conv of the rounded normalised input. The oracle normalises in fp64, the kernel in fp32, so
+    at a rounding tie the two operands can land one bf16 (fp16) step apart: about one operand in
+    2^15, each moving an output by about |w| * ulp(z) (2e-5 of the largest output here). The
+    oracle bar is therefore 3e-4 relative for fp32 outputs (some ten such steps on one output);
+    the bit-exact match with the separate pass pins the kernel's own rounding."""
+    import torch
+    (n, t, h, w), cin, c, (st, sh, sw), xdt, odt, ydt, use_res, bx, groups, splitk = case
+    k = NORM_IN_CASES.index(case)
+    cout = c * st * sh * sw
+    _, wt, b, _ = _conv_inputs((n, t, h, w), cin, cout, "bf16", 120 + k)
+    x = ndhwc(vae_synth.normal((n, cin, t, h, w), [121, k], scale=1.7, mean=0.4))
+    if xdt == "f16":
+        x = round_f16(x)
+    gamma = vae_synth.normal((cin,), [122, k], scale=0.3, mean=1.0)
+    beta = vae_synth.normal((cin,), [123, k], scale=0.2)
+    cnt, mean, m2 = oracle.group_moments(x, groups)
+    var = m2 / cnt
+    eps = 1e-6
+    z = oracle.silu(oracle.normalize_with(x, groups, mean, var, eps, gamma, beta))
+    zop = vae_synth.round_bf16(z).astype(np.float64) if odt == "bf16" else round_f16(z)
+    yshape = (n, st * t - (st - 1), sh * h, sw * w, c)
+    r = ndhwc(vae_synth.normal((n, c) + yshape[1:4], [124, k], dtype="bf16")) if use_res else None
+    ref = oracle.depth_to_space(oracle.causal_conv3d(zop, wt, b), st, sh, sw)
+    if use_res:
+        ref = ref + r
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    xd = dev(x, xdt)
+    wd = v.conv_weight_layout(wt, torch.bfloat16, "cuda")
+    if odt == "f16":
+        wp = v.vae_conv_weight_pack_f16(wd).view(torch.bfloat16)
+        flags = v.VAE_CONV_PACKED_F16_WEIGHTS
+    else:
+        wp = v.vae_conv_weight_pack(wd).view(torch.bfloat16)
+        flags = v.VAE_CONV_PACKED_WEIGHTS
+    if splitk:
+        flags |= v.VAE_CONV_SPLIT_K
+    bd = torch.as_tensor(b, dtype=torch.float32, device="cuda")
+    rd = dev(r, ydt) if use_res else None
+    mr = torch.as_tensor(np.stack([mean, 1 / np.sqrt(var + eps)], -1), dtype=torch.float32,
+                         device="cuda")
+    gd = torch.as_tensor(gamma, dtype=torch.float32, device="cuda")
+    bt = torch.as_tensor(beta, dtype=torch.float32, device="cuda")
+    ab = torch.empty((n, cin, 2), dtype=torch.float32, device="cuda")
+    v.vae_groupnorm_scale_shift(mr, cin, groups, gd, bt, ab)
+    # the separate pass: the normalised tensor in the operand dtype, then the conv
+    g = torch.empty(xd.shape, dtype=tdt[odt], device="cuda")
+    v.vae_groupnorm_apply(xd, None, groups, mr, gd, bt, True, g)
+    outs = []
+    for src, fused in ((g, False), (xd, True)):
+        y = torch.full(yshape, 7.0, device="cuda", dtype=tdt[ydt])
+        v.vae_conv3d_causal_fused(src, wp, bd, rd, y, bx, flags, d2s=(st, sh, sw),
+                                  in_scale_shift=ab if fused else None)
+        outs.append(y)
+    torch.cuda.synchronize()
+    sep, got = host(outs[0]), host(outs[1])
+    diff = np.abs(sep - got)
+    assert torch.equal(outs[0], outs[1]), \
+        f"fused input norm differs from the separate pass: {int((diff > 0).sum())} values, " \
+        f"max {diff.max():.3g}; vs oracle {rel_max_abs(got, ref):.3g} (fused), " \
+        f"{rel_max_abs(sep, ref):.3g} (separate)"
+    if bx is None:
+        g_, rf = got, ref
+    else:   # the box in the conv's input grid; y's frames and columns scale with the factors
+        t0, t1 = max(0, st * bx[0] - (st - 1)), st * bx[1] - (st - 1)
+        sl = (slice(None), slice(t0, t1), slice(sh * bx[2], sh * bx[3]),
+              slice(sw * bx[4], sw * bx[5]))
+        mask = np.zeros(got.shape, bool)
+        mask[sl] = True
+        assert np.all(got[~mask] == 7.0), "conv wrote outside its box"
+        g_, rf = got[sl], ref[sl]
+    if ydt == "f32":
+        assert rel_max_abs(g_, rf) <= 3e-4
+    else:
+        bound = bf16_round_bound(rf) if ydt == "bf16" else f16_round_bound(rf)
+        assert np.all(np.abs(g_ - rf) <= bound + 3e-4 * np.abs(rf).max())
+
+
+def test_groupnorm_scale_shift_matches_oracle(v):
+    """scale = rstd * gamma, shift = beta - mean * scale per (sample, channel); NULL gamma and
+    beta read as 1 and 0."""
+    import torch
+    n, c, groups = 2, 96, 8
+    mean = vae_synth.normal((n, groups), [125, 0], scale=2.0)
+    rstd = np.abs(vae_synth.normal((n, groups), [125, 1])) + 0.1
+    gamma = vae_synth.normal((c,), [125, 2], mean=1.0, scale=0.3)
+    beta = vae_synth.normal((c,), [125, 3], scale=0.2)
+    mr = torch.as_tensor(np.stack([mean, rstd], -1), dtype=torch.float32, device="cuda")
+    for gm, bt in ((gamma, beta), (None, None)):
+        ab = torch.empty((n, c, 2), dtype=torch.float32, device="cuda")
+        v.vae_groupnorm_scale_shift(
+            mr, c, groups, None if gm is None else torch.as_tensor(gm, device="cuda"),
+            None if bt is None else torch.as_tensor(bt, device="cuda"), ab)
+        torch.cuda.synchronize()
+        got = ab.cpu().numpy().astype(np.float64)
+        g = np.repeat(np.arange(groups), c // groups)
+        m32 = mean.astype(np.float32).astype(np.float64)[:, g]
+        r32 = rstd.astype(np.float32).astype(np.float64)[:, g]
+        sc = r32 * (1.0 if gm is None else gm[None, :])
+        shf = (0.0 if bt is None else bt[None, :]) - m32 * sc
+        np.testing.assert_allclose(got[..., 0], sc, rtol=1e-6)
+        np.testing.assert_allclose(got[..., 1], shf, rtol=1e-5, atol=1e-6)

@@ -20,7 +20,7 @@ VAE_STATUS_NONFINITE = 1
 VAE_MERGE_ZERO, VAE_MERGE_FINALIZE = 1, 2
 VAE_CONV_SPLIT_FP32, VAE_CONV_PACKED_WEIGHTS, VAE_CONV_PACKED_F16_WEIGHTS = 1, 2, 4
 VAE_CONV_SPLIT_K = 8
-VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS = 1, 2
+VAE_DECODE_SPLIT_FP32_OPERANDS, VAE_DECODE_F16_OPERANDS, VAE_DECODE_NORM_IN_CONV = 1, 2, 4
 VAE_OP_CONV, VAE_OP_RES, VAE_OP_GN_SILU, VAE_OP_D2S, VAE_OP_NEAREST = 1, 2, 3, 4, 5
 VAE_OP_RES_RMS, VAE_OP_RMS_SILU, VAE_OP_ATTN, VAE_OP_S2D, VAE_OP_CONV_DOWN = 6, 7, 8, 9, 10
 VAE_PAD_AROUND, VAE_PAD_AFTER = 0, 1
@@ -36,7 +36,8 @@ EXPORTS = (
     "vae_decoder_pack_weights",
     "vae_groupnorm_silu_workspace", "vae_groupnorm_silu", "vae_groupnorm_silu_noalloc",
     "vae_groupnorm_stats_workspace",
-    "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply", "vae_rmsnorm_silu",
+    "vae_groupnorm_stats", "vae_groupnorm_combine", "vae_groupnorm_apply",
+    "vae_groupnorm_scale_shift", "vae_rmsnorm_silu",
     "vae_frame_attention_workspace", "vae_frame_attention", "vae_upsample", "vae_space_to_depth",
     "vae_tile_split", "vae_tile_merge", "vae_decoder_create", "vae_decoder_destroy",
     "vae_decoder_set_launch", "vae_decoder_set_clip_frames", "vae_decode_workspace_size",
@@ -67,7 +68,7 @@ class vae_conv_fused_t(ctypes.Structure):
                 ("gn_groups", ctypes.c_int32), ("gn_eps", ctypes.c_float),
                 ("gn_mean_rstd", ctypes.c_void_p), ("ws", ctypes.c_void_p),
                 ("ws_bytes", ctypes.c_size_t), ("in_up_sh", ctypes.c_int32),
-                ("in_up_sw", ctypes.c_int32)]
+                ("in_up_sw", ctypes.c_int32), ("in_scale_shift", ctypes.c_void_p)]
 
 class vae_error_info_t(ctypes.Structure):
     _fields_ = [("status", ctypes.c_int32), ("axis", ctypes.c_int32), ("extent", ctypes.c_int64),
@@ -140,6 +141,7 @@ def _load():
         "vae_groupnorm_stats": ([T, B, I32, I32, P, P, SZ, P], I32),
         "vae_groupnorm_combine": ([P, I32, I32, I32, F, P, P], I32),
         "vae_groupnorm_apply": ([T, B, I32, P, P, P, I32, T, P], I32),
+        "vae_groupnorm_scale_shift": ([P, I32, I32, I32, P, P, P, P], I32),
         "vae_rmsnorm_silu": ([T, F, P, P, I32, T, P], I32),
         "vae_frame_attention_workspace": ([T, ctypes.POINTER(SZ)], I32),
         "vae_frame_attention": ([T, F, P, P, P, P, P, P, T, P, SZ, P], I32),
@@ -273,7 +275,7 @@ def vae_conv3d_causal(x, weight, bias, residual, y, out_box=None, flags=0, strea
 
 
 def _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
-                gn_mean_rstd, ws, in_up=(0, 0)):
+                gn_mean_rstd, ws, in_up=(0, 0), in_scale_shift=None):
     keep = [tensor_desc(x), tensor_desc(y),
             tensor_desc(residual) if residual is not None else None, box(out_box)]
     a = vae_conv_fused_t()
@@ -292,13 +294,14 @@ def _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn
     a.ws = _ptr(ws)
     a.ws_bytes = ws.numel() if ws is not None else 0
     a.in_up_sh, a.in_up_sw = (int(f) for f in in_up)
+    a.in_scale_shift = _ptr(in_scale_shift)
     return a, keep
 
 
 def vae_conv3d_causal_fused_workspace(x, weight, y, out_box=None, d2s=(0, 0, 0), gn_groups=0,
-                                      in_up=(0, 0), flags=0):
+                                      in_up=(0, 0), flags=0, in_scale_shift=None):
     a, keep = _fused_args(x, weight, None, None, y, out_box, flags, d2s, gn_groups, 0.0, None,
-                          None, in_up)
+                          None, in_up, in_scale_shift)
     n = ctypes.c_size_t(0)
     _check(LIB.vae_conv3d_causal_fused_workspace(ctypes.byref(a), ctypes.byref(n)))
     return n.value
@@ -306,15 +309,17 @@ def vae_conv3d_causal_fused_workspace(x, weight, y, out_box=None, d2s=(0, 0, 0),
 
 def vae_conv3d_causal_fused(x, weight, bias, residual, y, out_box=None, flags=0, d2s=(0, 0, 0),
                             gn_groups=0, gn_eps=1e-6, gn_mean_rstd=None, ws=None, stream=None,
-                            in_up=(0, 0)):
+                            in_up=(0, 0), in_scale_shift=None):
     """Causal Conv3d of the nearest upsampling of x by in_up = (sh, sw), with a fused
     depth-to-space (d2s = (st, sh, sw), y is then the upsampled tensor) and/or the statistics of a
-    GroupNorm over y (gn_mean_rstd [N, gn_groups, 2] fp32)."""
+    GroupNorm over y (gn_mean_rstd [N, gn_groups, 2] fp32). With in_scale_shift ([N, Cin, 2]
+    fp32, vae_groupnorm_scale_shift) the conv reads silu(x * scale + shift)."""
     if ws is None:
-        n = vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups, in_up, flags)
+        n = vae_conv3d_causal_fused_workspace(x, weight, y, out_box, d2s, gn_groups, in_up, flags,
+                                              in_scale_shift)
         ws = _workspace(n, x.device) if n else None
     a, keep = _fused_args(x, weight, bias, residual, y, out_box, flags, d2s, gn_groups, gn_eps,
-                          gn_mean_rstd, ws, in_up)
+                          gn_mean_rstd, ws, in_up, in_scale_shift)
     _check(LIB.vae_conv3d_causal_fused(ctypes.byref(a), _stream(stream)))
     return y
 
@@ -400,6 +405,15 @@ def vae_groupnorm_apply(x, out_box, groups, mean_rstd, gamma, beta, apply_silu, 
                                    _ptr(gamma), _ptr(beta), int(apply_silu), ctypes.byref(yd),
                                    _stream(stream)))
     return y
+
+
+def vae_groupnorm_scale_shift(mean_rstd, channels, groups, gamma, beta, scale_shift,
+                              stream=None):
+    """scale_shift [N, channels, 2] fp32 of the normalise step for mean_rstd [N, groups, 2]."""
+    _check(LIB.vae_groupnorm_scale_shift(_ptr(mean_rstd), int(mean_rstd.shape[0]), int(channels),
+                                         int(groups), _ptr(gamma), _ptr(beta), _ptr(scale_shift),
+                                         _stream(stream)))
+    return scale_shift
 
 
 def vae_rmsnorm_silu(x, eps, gamma, beta, apply_silu, y, stream=None):

@@ -323,9 +323,11 @@ vae_status_t check_residual(const vae_tensor_t* r, const vae_tensor_t& x, const 
 }
 
 // fp16 tensors and the packed-weight flags (shared by both conv calls).
+// `norm`: the conv normalises x while staging it (fp32 x with either packed flag, fp16 x with
+// bf16-packed weights).
 vae_status_t check_conv_dtypes(const vae_tensor_t& x, const vae_tensor_t& y,
                                const vae_tensor_t* residual, int64_t cout, int32_t weight_dtype,
-                               int32_t flags) {
+                               int32_t flags, bool norm = false) {
     const int32_t packs = VAE_CONV_PACKED_WEIGHTS | VAE_CONV_PACKED_F16_WEIGHTS;
     if (flags & ~(VAE_CONV_SPLIT_FP32 | packs | VAE_CONV_SPLIT_K))
         return fail(VAE_ERR_INVALID_ARG, "unknown conv flags");
@@ -340,10 +342,21 @@ vae_status_t check_conv_dtypes(const vae_tensor_t& x, const vae_tensor_t& y,
         if (y.dtype == VAE_DTYPE_F16 && x.dtype == VAE_DTYPE_F32)
             return fail(VAE_ERR_UNSUPPORTED, "an fp16 y needs a bf16 or fp16 x");
     }
-    if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && x.dtype != VAE_DTYPE_F16)
-        return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 x");
-    if ((flags & VAE_CONV_PACKED_WEIGHTS) && x.dtype == VAE_DTYPE_F16)
-        return fail(VAE_ERR_INVALID_ARG, "an fp16 x takes fp16-packed weights");
+    if (norm) {
+        if (!(flags & packs) || (flags & VAE_CONV_SPLIT_FP32) || !mfma)
+            return fail(VAE_ERR_UNSUPPORTED,
+                        "an input GroupNorm needs packed weights, no fp32 split, bf16 weights, "
+                        "Cin % 32 == 0 and Cout % 4 == 0", 4, x.c, 32);
+        if (x.dtype != VAE_DTYPE_F32 &&
+            !(x.dtype == VAE_DTYPE_F16 && (flags & VAE_CONV_PACKED_WEIGHTS)))
+            return fail(VAE_ERR_UNSUPPORTED, "an input GroupNorm reads fp32 x, or fp16 x with "
+                                             "bf16-packed weights");
+    } else {
+        if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && x.dtype != VAE_DTYPE_F16)
+            return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 x");
+        if ((flags & VAE_CONV_PACKED_WEIGHTS) && x.dtype == VAE_DTYPE_F16)
+            return fail(VAE_ERR_INVALID_ARG, "an fp16 x takes fp16-packed weights");
+    }
     if ((flags & packs) && !mfma)
         return fail(VAE_ERR_UNSUPPORTED,
                     "packed weights need bf16 weights, Cin % 32 == 0 and Cout % 4 == 0", 4, x.c,
@@ -432,7 +445,10 @@ vae_status_t check_fused(const vae_conv_fused_t* a, FusedPlan* p, bool run) {
     p->ybox = Box{std::max(0, p->st * b.t0 - (p->st - 1)), p->st * b.t1 - (p->st - 1),
                   p->sh * b.h0, p->sh * b.h1, p->sw * b.w0, p->sw * b.w1};
     const bool mfma = conv_uses_mfma_c(x, y.c * p->k, a->weight_dtype);
-    VAE_TRY(check_conv_dtypes(x, y, a->residual, y.c * p->k, a->weight_dtype, a->flags));
+    const bool norm = a->in_scale_shift != nullptr;
+    VAE_TRY(check_conv_dtypes(x, y, a->residual, y.c * p->k, a->weight_dtype, a->flags, norm));
+    if (norm && reinterpret_cast<uintptr_t>(a->in_scale_shift) % 16)
+        return fail(VAE_ERR_INVALID_ARG, "in_scale_shift must be 16-byte aligned");
     if ((p->k > 1 || p->lsh || p->lsw) && !mfma)
         return fail(VAE_ERR_UNSUPPORTED,
                     "a fused depth-to-space or input upsampling needs bf16 weights, Cin % 32 == 0 "
@@ -555,6 +571,7 @@ VAE_API vae_status_t vae_conv3d_causal_fused(const vae_conv_fused_t* args, vae_s
         fz.part = reinterpret_cast<float*>(static_cast<uint8_t*>(a.ws) + split_off);
         fz.splits = splits;
     }
+    fz.in_ab = a.in_scale_shift;
     VAE_TRY(launch_conv3d(x, a.weight, a.weight_dtype, a.bias, a.residual, y, p.cbox, a.flags, s,
                           &fz));
     if (!a.gn_groups) return VAE_OK;
@@ -714,6 +731,23 @@ VAE_API vae_status_t vae_groupnorm_apply(const vae_tensor_t* x, const vae_box_t*
     VAE_TRY(check_box(box, *x, "box"));
     return launch_gn_apply(*x, to_box(box, *x), groups, mean_rstd, gamma, beta, apply_silu != 0,
                            *y, as_stream(stream));
+}
+
+VAE_API vae_status_t vae_groupnorm_scale_shift(const float* mean_rstd, int32_t n, int32_t channels,
+                                               int32_t groups, const float* gamma,
+                                               const float* beta, float* scale_shift,
+                                               vae_stream_t stream) {
+    clear_error();
+    if (!mean_rstd || !scale_shift)
+        return fail(VAE_ERR_INVALID_ARG, "mean_rstd and scale_shift must not be NULL");
+    if (n < 0 || groups < 1 || channels < 1 || channels % groups || channels % 8)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "need n >= 0, groups >= 1 and channels a multiple of groups and of 8", 4,
+                    channels, 8);
+    if (reinterpret_cast<uintptr_t>(scale_shift) % 16)
+        return fail(VAE_ERR_INVALID_ARG, "scale_shift must be 16-byte aligned");
+    return launch_gn_scale_shift(mean_rstd, n, channels, groups, gamma, beta, scale_shift,
+                                 as_stream(stream));
 }
 
 VAE_API vae_status_t vae_groupnorm_silu(const vae_tensor_t* x, const vae_box_t* boxes,

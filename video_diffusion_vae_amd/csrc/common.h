@@ -44,6 +44,27 @@ template <> struct Elem<float> {
     static constexpr int kVec = 4;
 };
 
+// GroupNorm apply as a per-channel affine map, and the SiLU after it. Every kernel that applies a
+// GroupNorm (the normalise pass, the convs that normalise while staging) goes through these two,
+// so that their results agree bit for bit: explicit fused multiply-adds leave the compiler no
+// contraction to choose.
+__host__ __device__ inline void gn_scale_shift_of(float mean, float rstd, float gamma, float beta,
+                                                  float& scale, float& shift) {
+    scale = rstd * gamma;
+    shift = fmaf(-mean, scale, beta);
+}
+__device__ __forceinline__ float gn_silu_apply(float x, float scale, float shift) {
+    const float z = fmaf(x, scale, shift);
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+// v as an fp32 value the compiler must produce: a narrowing that follows is then a second
+// rounding of it, never folded with the operation that made v into one mixed-precision fma
+// (v_fma_mixlo_f16 rounds the exact product once). An empty asm statement, no instruction.
+__device__ __forceinline__ float materialise_f32(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // ------------------------------------------------------------------------------------------------
 // Error state (thread-local), filled by the ABI layer.
 // ------------------------------------------------------------------------------------------------

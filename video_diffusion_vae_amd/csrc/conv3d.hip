@@ -27,6 +27,15 @@ VAE_MFMA_EXTERN(32, uint16_t, false)
 VAE_MFMA_EXTERN(32, float, false)
 VAE_MFMA_EXTERN(32, float, true)
 VAE_MFMA_EXTERN(32, _Float16, false)
+VAE_MFMA_EXTERN(128, GnF32, false)
+VAE_MFMA_EXTERN(64, GnF32, false)
+VAE_MFMA_EXTERN(32, GnF32, false)
+VAE_MFMA_EXTERN(128, GnF16, false)
+VAE_MFMA_EXTERN(64, GnF16, false)
+VAE_MFMA_EXTERN(32, GnF16, false)
+VAE_MFMA_EXTERN(128, GnF32H, false)
+VAE_MFMA_EXTERN(64, GnF32H, false)
+VAE_MFMA_EXTERN(32, GnF32H, false)
 #undef VAE_MFMA_EXTERN
 }  // namespace mfma
 
@@ -81,7 +90,17 @@ __global__ __launch_bounds__(256) void conv3d_direct_kernel(
 template <int NT>
 vae_status_t run_mfma_in(const vae_tensor_t& x, const void* w, const float* bias,
                          const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                         bool split, bool packed, const ConvFuse* fz, hipStream_t stream) {
+                         bool split, bool packed, bool f16w, const ConvFuse* fz,
+                         hipStream_t stream) {
+    if (fz && fz->in_ab) {   // GroupNorm + SiLU while staging: bf16 or fp16 operands
+        if (x.dtype == VAE_DTYPE_F32 && f16w)
+            return run_mfma_out<NT, GnF32H, false>(x, w, bias, residual, y, box, packed, fz,
+                                                   stream);
+        if (x.dtype == VAE_DTYPE_F32)
+            return run_mfma_out<NT, GnF32, false>(x, w, bias, residual, y, box, packed, fz,
+                                                  stream);
+        return run_mfma_out<NT, GnF16, false>(x, w, bias, residual, y, box, packed, fz, stream);
+    }
     if (x.dtype == VAE_DTYPE_BF16)
         return run_mfma_out<NT, uint16_t, false>(x, w, bias, residual, y, box, packed, fz,
                                                  stream);
@@ -259,13 +278,28 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
     const bool xf = x.dtype == VAE_DTYPE_F32;
     const bool split = (flags & VAE_CONV_SPLIT_FP32) != 0;
     const bool packed = (flags & (VAE_CONV_PACKED_WEIGHTS | VAE_CONV_PACKED_F16_WEIGHTS)) != 0;
+    const bool f16w = (flags & VAE_CONV_PACKED_F16_WEIGHTS) != 0;
     const bool x16 = x.dtype == VAE_DTYPE_F16;
-    if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && !x16)
-        return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 input");
-    if ((flags & VAE_CONV_PACKED_WEIGHTS) && x16)
-        return fail(VAE_ERR_INVALID_ARG, "an fp16 input takes fp16-packed weights");
+    const bool norm = fz && fz->in_ab;
     const int32_t k = fz ? fz->st * fz->sh * fz->sw : 1;
     const int64_t cout = y.c * k;
+    if (norm) {
+        // a normalised input: fp32 (bf16 or fp16 operands) or fp16 (bf16 operands), packed
+        // weights, no split
+        if (!packed || split || !conv_uses_mfma_c(x, cout, weight_dtype))
+            return fail(VAE_ERR_UNSUPPORTED, "conv3d: an input GroupNorm needs the MFMA path with "
+                                             "packed weights and no fp32 split");
+        if (!xf && !(x16 && (flags & VAE_CONV_PACKED_WEIGHTS)))
+            return fail(VAE_ERR_UNSUPPORTED, "conv3d: an input GroupNorm reads fp32, or fp16 "
+                                             "with bf16-packed weights");
+        if (reinterpret_cast<uintptr_t>(fz->in_ab) % 16)
+            return fail(VAE_ERR_INVALID_ARG, "conv3d: the scale and shift must be 16-byte aligned");
+    } else {
+        if ((flags & VAE_CONV_PACKED_F16_WEIGHTS) && !x16)
+            return fail(VAE_ERR_INVALID_ARG, "fp16-packed weights go with an fp16 input");
+        if ((flags & VAE_CONV_PACKED_WEIGHTS) && x16)
+            return fail(VAE_ERR_INVALID_ARG, "an fp16 input takes fp16-packed weights");
+    }
     if (fz && (fz->lsh || fz->lsw) && !conv_uses_mfma_c(x, cout, weight_dtype))
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: a folded nearest upsampling needs the MFMA path");
     if ((x16 || y.dtype == VAE_DTYPE_F16) && !conv_uses_mfma_c(x, cout, weight_dtype))
@@ -281,11 +315,14 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
         // output-channel tile: 128 wide, or 64 / 32 for narrow outputs (conv_out's 48 or 12)
         switch (conv_nt(cout)) {
             case 128:
-                return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, fz, stream);
+                return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, f16w, fz,
+                                        stream);
             case 64:
-                return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, fz, stream);
+                return run_mfma_in<64>(x, w, bias, residual, y, box, split, packed, f16w, fz,
+                                       stream);
             default:
-                return run_mfma_in<32>(x, w, bias, residual, y, box, split, packed, fz, stream);
+                return run_mfma_in<32>(x, w, bias, residual, y, box, split, packed, f16w, fz,
+                                       stream);
         }
     }
     if (packed) return fail(VAE_ERR_UNSUPPORTED, "packed weights need the MFMA path");

@@ -36,6 +36,12 @@
 //    fp16 exactly after a 2^10 scale (packed that way ahead of time, or converted as each
 //    fragment is used with the standard layout); the sums are scaled back by 2^-10 before the
 //    epilogue, which is exact.
+//  - A GroupNorm + SiLU of the input can be applied while staging: the conv then reads the
+//    norm's input x (fp32 or fp16) and stages bf16(silu(x * scale_c + shift_c)) (or fp16, for a
+//    conv on fp16 operands), with a per-(sample, channel) scale and shift formed from the norm's
+//    statistics, gamma and beta. The operand is the value a separate normalisation pass would have
+//    stored, computed the same way, so the result is the same; the normalised tensor is never
+//    written or read back. Image padding stays zero (it pads the normalised tensor).
 //  - Epilogue. Where a wave's 32 channels are 32 consecutive channels of y (Cout and y's channel
 //    count multiples of 32), each lane stores its accumulator registers directly: one channel at
 //    16 positions, two runs of 32 channels per store instruction. Otherwise each wave parks one
@@ -133,6 +139,36 @@ struct MfmaArgs {
     int32_t splits;
     float* part;
     const float* reduce;
+    // Input GroupNorm + SiLU applied while staging (input tags below): fp32 (scale, shift) per
+    // (sample, input channel), [N][cin][2].
+    const float* nab;
+};
+
+// Input kinds. A plain element type stages as it is (bf16, fp16) or rounded to bf16 (fp32). The
+// tags read fp32 or fp16 and stage silu(x * scale + shift) as bf16 (GnF32, GnF16) or as fp16
+// (GnF32H, for fp16 weights).
+struct GnF32 {};
+struct GnF16 {};
+struct GnF32H {};
+template <typename TI> struct InT {
+    using raw = TI;                                       // element type in memory
+    static constexpr bool f16op = std::is_same<TI, _Float16>::value;   // fp16 MFMA operands
+    static constexpr bool norm = false;
+};
+template <> struct InT<GnF32> {
+    using raw = float;
+    static constexpr bool f16op = false;
+    static constexpr bool norm = true;
+};
+template <> struct InT<GnF16> {
+    using raw = _Float16;
+    static constexpr bool f16op = false;
+    static constexpr bool norm = true;
+};
+template <> struct InT<GnF32H> {
+    using raw = float;
+    static constexpr bool f16op = true;
+    static constexpr bool norm = true;
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -264,6 +300,79 @@ template <typename TI> __device__ __forceinline__ Raw8<TI> load_raw8(const TI* p
 }
 // Operand granule(s) of a unit: bf16 as is; fp32 rounded to bf16, or split into hi and lo.
 // A unit outside the image (in == false) is zero padding.
+// Operand granule of a normalised unit: silu(x * sc + sh) for each of the 8 channels, rounded
+// to bf16 (or fp16 with F16OP) exactly as the separate normalisation pass stores it.
+template <typename TR, bool F16OP>
+__device__ __forceinline__ uint4 norm_operand(const Raw8<TR>& r, bool in, const float (&sc)[8],
+                                              const float (&sh)[8]) {
+    float v[8];
+    if constexpr (sizeof(TR) == 2) {
+        const _Float16* h = reinterpret_cast<const _Float16*>(&r.v[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+    } else {
+        const float* f = reinterpret_cast<const float*>(&r.v[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = f[i];
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float z0 = gn_silu_apply(v[2 * i], sc[2 * i], sh[2 * i]);
+        const float z1 = gn_silu_apply(v[2 * i + 1], sc[2 * i + 1], sh[2 * i + 1]);
+        if constexpr (F16OP)   // rounded to fp32 first, as the normalise pass stores it
+            o[i] = (uint32_t)f16_bits(materialise_f32(z0)) |
+                   ((uint32_t)f16_bits(materialise_f32(z1)) << 16);
+        else
+            o[i] = (uint32_t)f32_to_bf16(z0) | ((uint32_t)f32_to_bf16(z1) << 16);
+    }
+    return in ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+}
+
+// norm_operand with the scale and shift read from LDS (tab: 8 channels' (scale, shift) pairs),
+// two channels at a time, each read volatile so that it is issued where it is used.
+template <typename TR, bool F16OP>
+__device__ __forceinline__ uint4 norm_operand_lds(const Raw8<TR>& r, bool in, const float* tab) {
+    float v[8];
+    if constexpr (sizeof(TR) == 2) {
+        const _Float16* h = reinterpret_cast<const _Float16*>(&r.v[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+    } else {
+        const float* f = reinterpret_cast<const float*>(&r.v[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = f[i];
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 p = *reinterpret_cast<const volatile f32x4*>(tab + 4 * i);
+        const float z0 = gn_silu_apply(v[2 * i], p.x, p.y);
+        const float z1 = gn_silu_apply(v[2 * i + 1], p.z, p.w);
+        if constexpr (F16OP)
+            o[i] = (uint32_t)f16_bits(materialise_f32(z0)) |
+                   ((uint32_t)f16_bits(materialise_f32(z1)) << 16);
+        else
+            o[i] = (uint32_t)f32_to_bf16(z0) | ((uint32_t)f32_to_bf16(z1) << 16);
+    }
+    return in ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+}
+
+// This thread's scale and shift for 8 channels from c (of sample n): [N][cin][2] fp32.
+__device__ __forceinline__ void load_norm8(const float* nab, int64_t n, int64_t cin, int c,
+                                           float (&sc)[8], float (&sh)[8]) {
+    const float4* q = reinterpret_cast<const float4*>(nab + (n * cin + c) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 v = q[i];
+        sc[2 * i] = v.x;
+        sh[2 * i] = v.y;
+        sc[2 * i + 1] = v.z;
+        sh[2 * i + 1] = v.w;
+    }
+}
+
 template <typename TI, bool SPLIT>
 __device__ __forceinline__ void to_operand(const Raw8<TI>& r, bool in, uint4& hi, uint4& lo) {
     const uint4 z = make_uint4(0, 0, 0, 0);
@@ -600,21 +709,30 @@ template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int
 __global__ __launch_bounds__(kMfmaThreads, 2)
 void conv3d_mfma_kernel(MfmaArgs a) {
     using S = BlockShape<TB, HB, WB>;
-    constexpr bool F16 = std::is_same<TI, _Float16>::value;   // fp16 operands
-    static_assert(!(F16 && SPLIT), "fp16 inputs are not split");
+    using TR = typename InT<TI>::raw;                         // the input's element type
+    constexpr bool F16 = InT<TI>::f16op;                      // fp16 operands
+    constexpr bool NORM = InT<TI>::norm;                      // GroupNorm + SiLU while staging
+    static_assert(!(F16 && SPLIT) && !(NORM && SPLIT), "fp16 or normalised inputs are not split");
     constexpr int HH = S::HH, HW = S::HW;
     constexpr int RP = S::kPitch;
     // With packed weights and bf16 (or split) operands the tile is staged through a ring of frame
     // slots (see below); otherwise through one tile buffer. The ring's extra registers fit two
     // waves per SIMD in those cases. Its schedule is written for blocks of 2 or 4 frames, and on
     // a narrow block (4 x 16 x 4) it needs more than half the registers of a SIMD: the narrow
-    // blocks stage through the tile buffer.
-    constexpr bool ROLL = PACKED && (sizeof(TI) == 2 || SPLIT) && TB <= 4 && WB >= 8;
+    // blocks stage through the tile buffer. So does a normalised input of 4-byte values (twice
+    // the raw registers of a 2-byte one), and any normalised input at NT = 128: the norm's
+    // arithmetic needs registers that the ring leaves free only beside 64-channel tiles (at
+    // NT = 128 it spills).
+    constexpr bool ROLL = PACKED && (sizeof(TR) == 2 || SPLIT) && TB <= 4 && WB >= 8 &&
+                          !(NORM && NT > 64);
     constexpr int NSP = TB == 2 ? 1 : 2;           // spare frame slots of the ring
     constexpr int NS = S::HT + NSP;                // frame slots of the ring
     constexpr int FB = HH * RP;                    // bytes of one frame slot
     constexpr int kSink = ROLL ? NS * FB : S::kBytes;   // 64 bytes absorbing padding units
     __shared__ __attribute__((aligned(16))) uint8_t halo[kSink + (ROLL ? 64 : 0)];
+    // A normalised input on the ring: each chunk's (scale, shift) table (32 channels x 2 fp32)
+    // in a ring of three, chunk c in slot c % 3, written two chunks ahead.
+    __shared__ __attribute__((aligned(16))) float ntab[ROLL && NORM ? 3 * 64 : 1];
 
     // WNN waves across the NT output channels (32 each), WM across the 256 positions.
     constexpr int WNN = NT / 32;
@@ -655,7 +773,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
 
     const int64_t cin = a.cin;
     const int xH = a.H >> a.lsh, xW = a.W >> a.lsw;      // x's own extents
-    const TI* xn = static_cast<const TI*>(a.x) + (int64_t)n * a.T * xH * xW * cin;
+    const TR* xn = static_cast<const TR*>(a.x) + (int64_t)n * a.T * xH * xW * cin;
 
     f32x16_t acc[MI];
 #pragma unroll
@@ -740,7 +858,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             fu_pos[i] = r | (c << 8) | (g << 16) | (valid ? 0 : 1 << 30);
             fu_lds[i] = r * RP + c * kRow + g * 16;
         }
-        Raw8<TI> fst[2][FST];                             // [1] only for a second held frame
+        Raw8<TR> fst[2][FST];                             // [1] only for a second held frame
         uint32_t fin[2] = {0, 0};                         // bit i: unit i inside the image
         auto frame_load = [&](int f, int c0, int reg) {
             int tg = t_blk - 2 + f;
@@ -753,17 +871,31 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 const bool in = (unsigned)hg < (unsigned)a.H && (unsigned)wg < (unsigned)a.W;
                 const int hc = hg < 0 ? 0 : (hg >= a.H ? a.H - 1 : hg);
                 const int wc = wg < 0 ? 0 : (wg >= a.W ? a.W - 1 : wg);
-                fst[reg][i] = load_raw8<TI>(xn + ((int64_t)(tg * xH + (hc >> a.lsh)) * xW +
+                fst[reg][i] = load_raw8<TR>(xn + ((int64_t)(tg * xH + (hc >> a.lsh)) * xW +
                                                   (wc >> a.lsw)) * cin +
                                             c0 + g * 8);
                 fin[reg] = in ? (fin[reg] | (1u << i)) : (fin[reg] & ~(1u << i));
             }
         };
-        auto frame_write = [&](int slot, int reg) {
+        // with NORM: the table of chunk kc, and this thread's 8 channels of it (channel group
+        // tid % 4 in every unit it stages)
+        auto ntab_value = [&](int kc) {   // one table entry per lane of a wave; kc is clamped
+            const int c = kc < kc1 ? kc : kc1 - 1;
+            return a.nab[((int64_t)n * cin + (int64_t)c * CK) * 2 + (tid & 63)];
+        };
+        auto frame_write = [&](int slot, int reg, int kcf) {
+            const float* tab = ntab + (kcf % 3) * 64 + (tid % UPP) * 16;
 #pragma unroll
             for (int i = 0; i < FST; ++i) {
                 uint4 hi, lo;
-                to_operand<TI, SPLIT>(fst[reg][i], (fin[reg] >> i) & 1u, hi, lo);
+                if constexpr (NORM) {
+                    // the table is read again for every unit, a channel pair at a time: only
+                    // four of its values are live at once
+                    hi = norm_operand_lds<TR, F16>(fst[reg][i], (fin[reg] >> i) & 1u, tab);
+                    lo = hi;
+                } else {
+                    to_operand<TR, SPLIT>(fst[reg][i], (fin[reg] >> i) & 1u, hi, lo);
+                }
                 uint8_t* dst = (fu_pos[i] >> 30) ? halo + kSink : halo + slot * FB + fu_lds[i];
                 *reinterpret_cast<uint4*>(dst) = hi;              // split: hi in bytes 0..31
                 if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = lo;
@@ -782,15 +914,21 @@ void conv3d_mfma_kernel(MfmaArgs a) {
         // prologue: chunk 0 into slots 0 .. HT-1 (its held frames stay in registers too, so that
         // the first chunk's step-0 rewrite is harmless), the first weights in flight
         int b = 0;
+        if constexpr (NORM) {   // the tables of the first two chunks (every wave writes the same)
+            const float t0 = ntab_value(kc0), t1 = ntab_value(kc0 + 1);
+            ntab[(kc0 % 3) * 64 + (tid & 63)] = t0;
+            ntab[((kc0 + 1) % 3) * 64 + (tid & 63)] = t1;
+            __syncthreads();
+        }
 #pragma unroll
         for (int f = 0; f < NIN; ++f) {
             frame_load(f, kc0 * CK, 0);
-            frame_write(f, 0);
+            frame_write(f, 0, kc0);
         }
 #pragma unroll
         for (int h = 0; h < NHOLD; ++h) {
             frame_load(NIN + h, kc0 * CK, h);
-            frame_write(NIN + h, h);
+            frame_write(NIN + h, h, kc0);
         }
 #pragma unroll
         for (int t = 0; t < PD; ++t) load_b(t, t, kc0 * CK);
@@ -807,6 +945,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             constexpr bool NEXT = decltype(next_c)::value;
             const int c0 = kc * CK;
             const int cn = (kc + 1) * CK;
+            float ntv = 0.0f;                     // NORM: chunk kc + 2's table entry in flight
             auto slot = [&](int f) { return (b + f + 2 * NS) % NS; };
             int abase[MI];
             auto set_phase = [&](int kt) {
@@ -840,10 +979,17 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                                   : (NHOLD > 1 && step == HLD[1]) ? 1 : -1;
                 if constexpr (step == 0) {
 #pragma unroll
-                    for (int h = 0; h < NHOLD; ++h) frame_write(slot(NIN + h), h);
+                    for (int h = 0; h < NHOLD; ++h) frame_write(slot(NIN + h), h, kc);
                 }
+                // NORM: the table of chunk kc + 2 is fetched early and written late in the chunk,
+                // into the slot of chunk kc - 1 (read last at its step 0); the chunk's closing
+                // barrier publishes it before chunk kc + 1 writes kc + 2's frames
+                constexpr bool tld = NORM && NEXT && step == LDK[0];
+                constexpr bool tst = NORM && NEXT && step == 40;
+                if constexpr (tld) ntv = ntab_value(kc + 2);
+                if constexpr (tst) ntab[((kc + 2) % 3) * 64 + (tid & 63)] = ntv;
                 if constexpr (ldk >= 0) frame_load(ldk, cn, 0);
-                if constexpr (wrk >= 0) frame_write(slot(wrk - NSP), 0);
+                if constexpr (wrk >= 0) frame_write(slot(wrk - NSP), 0, kc + 1);
                 if constexpr (hld >= 0) frame_load(NIN + hld, cn, hld);
                 if constexpr (step + 1 < 54) {
                     constexpr int nt = (step + 1) >> 1, nk = (step + 1) & 1;
@@ -859,10 +1005,13 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 for (int i = 0; i < MI; ++i) acc[i] = mfma_step<F16>(af[step & 1][i], bf, acc[i]);
                 constexpr int n_ld = (ldk >= 0) + (hld >= 0);
                 constexpr int n_wr = (wrk >= 0) + (step == 0 ? NHOLD : 0);
+                constexpr int n_tr = NORM ? 4 * FST * n_wr : 0;   // table reads of the writes
                 if constexpr (ldb) __builtin_amdgcn_sched_group_barrier(0x020, KB, 0);
-                if constexpr (n_ld > 0)
-                    __builtin_amdgcn_sched_group_barrier(0x020, n_ld * FST * (int)(sizeof(TI) / 2),
-                                                         0);
+                if constexpr (n_ld > 0 || tld)
+                    __builtin_amdgcn_sched_group_barrier(
+                        0x020, n_ld * FST * (int)(sizeof(TR) / 2) + (tld ? 1 : 0), 0);
+                if constexpr (tst) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                if constexpr (n_tr > 0) __builtin_amdgcn_sched_group_barrier(0x100, n_tr, 0);
                 if constexpr (n_wr > 0)
                     __builtin_amdgcn_sched_group_barrier(0x200, n_wr * FST * (SPLIT ? 2 : 1), 0);
 #pragma unroll
@@ -883,6 +1032,8 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     #pragma unroll
             for (int t = 0; t < PD; ++t) load_b(t, t, c0);   // in flight while the tile is staged
             __syncthreads();              // the previous chunk's LDS reads are done
+            float sc[NORM ? 8 : 1], sh[NORM ? 8 : 1];   // every unit of a thread: group tid % 4
+            if constexpr (NORM) load_norm8(a.nab, n, cin, c0 + (tid % UPP) * 8, sc, sh);
             for (int u = tid; u < S::kPos * UPP; u += kMfmaThreads) {
                 const int pos = u / UPP, g = u % UPP;
                 const int f = pos / (HH * HW);
@@ -895,10 +1046,11 @@ void conv3d_mfma_kernel(MfmaArgs a) {
                 uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
                 uint4 vl = make_uint4(0, 0, 0, 0);
                 if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
-                    const TI* src = xn + ((int64_t)(tg * xH + (hg >> a.lsh)) * xW + (wg >> a.lsw)) *
+                    const TR* src = xn + ((int64_t)(tg * xH + (hg >> a.lsh)) * xW + (wg >> a.lsw)) *
                                              cin + c0 + g * 8;
-                    if constexpr (SPLIT) split8<TI>(src, v, vl);
-                    else v = load8<TI>(src);
+                    if constexpr (NORM) v = norm_operand<TR, F16>(load_raw8<TR>(src), true, sc, sh);
+                    else if constexpr (SPLIT) split8<TR>(src, v, vl);
+                    else v = load8<TR>(src);
                 }
                 uint8_t* dst = &halo[(f * HH + r) * RP + c * kRow + g * 16];
                 *reinterpret_cast<uint4*>(dst) = v;            // split: hi in bytes 0..31 of the row
@@ -986,7 +1138,7 @@ void conv3d_mfma_kernel(MfmaArgs a) {
 template <int NT, typename TI, typename TO, int TB, int HB, int WB>
 __global__ __launch_bounds__(kMfmaThreads, 2)
 void conv3d_reduce_kernel(MfmaArgs a) {
-    constexpr bool F16 = std::is_same<TI, _Float16>::value;
+    constexpr bool F16 = InT<TI>::f16op;
     constexpr int WNN = NT / 32;
     constexpr int WM = kMfmaWaves / WNN;
     constexpr int MW = 256 / WM;
@@ -1119,6 +1271,9 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.sh = fz ? fz->sh : 1;
     a.sw = fz ? fz->sw : 1;
     a.tdrop = fz && fz->tdrop >= 0 ? fz->tdrop : a.st - 1;
+    a.nab = fz ? fz->in_ab : nullptr;
+    if (InT<TI>::norm != (a.nab != nullptr))
+        return fail(VAE_ERR_INVALID_ARG, "conv3d: input normalisation without its scale and shift");
     a.zc = (int32_t)y.c;
     a.cout = (int32_t)(y.c * a.st * a.sh * a.sw);
     a.yT = (int32_t)y.t;
@@ -1210,6 +1365,11 @@ vae_status_t run_narrow(BlockKind kind, const vae_tensor_t& x, const void* w, co
     VAE_NARROW_INST(PREFIX, NT, TI, SPLIT)                                                      \
     PREFIX template VAE_NARROW_SIG(NT, TI, _Float16, SPLIT, true);                              \
     PREFIX template VAE_NARROW_SIG(NT, TI, _Float16, SPLIT, false);
+// normalised inputs: packed weights, every output type
+#define VAE_NARROW_INST_GN(PREFIX, NT, TI)                                                      \
+    PREFIX template VAE_NARROW_SIG(NT, TI, float, false, true);                                 \
+    PREFIX template VAE_NARROW_SIG(NT, TI, uint16_t, false, true);                              \
+    PREFIX template VAE_NARROW_SIG(NT, TI, _Float16, false, true);
 
 template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED>
 vae_status_t run_block(const vae_tensor_t& x, const void* w, const float* bias,
@@ -1236,9 +1396,14 @@ template <int NT, typename TI, typename TO, bool SPLIT>
 vae_status_t run_mfma(const vae_tensor_t& x, const void* w, const float* bias,
                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
                       bool packed, const ConvFuse* fz, hipStream_t stream) {
-    if (packed)
+    if constexpr (InT<TI>::norm) {   // normalising staging is built for packed weights only
+        if (!packed) return fail(VAE_ERR_UNSUPPORTED, "conv3d: an input norm needs packed weights");
         return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, fz, stream);
-    return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, fz, stream);
+    } else {
+        if (packed)
+            return run_block<NT, TI, TO, SPLIT, true>(x, w, bias, residual, y, box, fz, stream);
+        return run_block<NT, TI, TO, SPLIT, false>(x, w, bias, residual, y, box, fz, stream);
+    }
 }
 
 template <int NT, typename TI, bool SPLIT>
@@ -1248,8 +1413,9 @@ vae_status_t run_mfma_out(const vae_tensor_t& x, const void* w, const float* bia
     if (y.dtype == VAE_DTYPE_F32)
         return run_mfma<NT, TI, float, SPLIT>(x, w, bias, residual, y, box, packed, fz, stream);
     if (y.dtype == VAE_DTYPE_F16) {
-        // fp16 outputs are the operand hand-off to an fp16-input conv, from a 2-byte input
-        if constexpr (sizeof(TI) == 2)
+        // fp16 outputs are the operand hand-off to an fp16-input conv, from a 2-byte input (or a
+        // normalised one)
+        if constexpr (sizeof(typename InT<TI>::raw) == 2 || InT<TI>::norm)
             return run_mfma<NT, TI, _Float16, SPLIT>(x, w, bias, residual, y, box, packed, fz,
                                                      stream);
         else

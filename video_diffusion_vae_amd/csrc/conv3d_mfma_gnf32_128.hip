@@ -1,0 +1,13 @@
+// MFMA conv kernels for NT = 128, fp32 input normalised to bf16 operands (a GroupNorm + SiLU
+// applied while staging; see conv3d_mfma.h).
+#include "conv3d_mfma.h"
+
+namespace vae {
+namespace mfma {
+VAE_NARROW_INST_GN(extern, 128, GnF32)
+template vae_status_t run_mfma_out<128, GnF32, false>(const vae_tensor_t&, const void*,
+                                                    const float*, const vae_tensor_t*,
+                                                    const vae_tensor_t&, const Box&, bool,
+                                                    const ConvFuse*, hipStream_t);
+}  // namespace mfma
+}  // namespace vae

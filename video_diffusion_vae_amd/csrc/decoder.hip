@@ -316,6 +316,7 @@ struct Req {
     int64_t tile = 0;     // one decoded tile, fp32 pixels (mode B)
     int64_t attn = 0;     // frame attention scratch
     int64_t carry = 0;    // carried input frames of every causal conv (clip-by-clip decodes)
+    int64_t ab = 0;       // a GroupNorm's per-channel scale and shift (applied by the next conv)
 };
 
 // Requirements of one run of the plan on an input of shape `in` with patch boxes `boxes`.
@@ -370,6 +371,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
             r->parts = std::max<int64_t>(r->parts, (int64_t)bl.n * cur.n * d.groups * 3 *
                                                        (int64_t)sizeof(double));
             r->mr = std::max<int64_t>(r->mr, cur.n * d.groups * 2 * (int64_t)sizeof(float));
+            r->ab = std::max<int64_t>(r->ab, cur.n * cur.c * 2 * (int64_t)sizeof(float));
         }
         // partials of GroupNorm statistics gathered by conv epilogues: over the whole grid, or
         // per patch box in rows holding every box's slots
@@ -466,7 +468,7 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
 }
 
 struct Layout {
-    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, carry, status, total;
+    size_t buf[3], gn, parts, splitk, mr, crop, tile, attn, carry, ab, status, total;
     int64_t act_bytes;
 };
 
@@ -494,6 +496,8 @@ Layout layout_of(const Req& r) {
     off += align_up((size_t)r.attn, 256);
     L.carry = off;
     off += align_up((size_t)r.carry, 256);
+    L.ab = off;
+    off += align_up((size_t)r.ab, 256);
     L.status = off;          // the decode's status word (vae_decode_status)
     off += 256;
     L.total = off;
@@ -523,6 +527,7 @@ struct Runner {
     }
 
     bool stats_ready = false;  // mean/rstd already hold the statistics of the next GN's input
+    bool pending_norm = false; // the next conv applies the norm whose scale and shift are formed
     // Clip-by-clip decode: activations keep kCarry frames of headroom, where every causal conv
     // puts its carried input frames (copies of frame 0 in the first clip).
     bool clips = false;
@@ -543,7 +548,9 @@ struct Runner {
         return st;
     }
 
-    vae_status_t gn(const vae_tensor_t& x, const vae_tensor_t& y, const BoxList& bl,
+    // A GroupNorm + SiLU of x into y. Without y (nullptr) only its statistics (mean/rstd) and
+    // the per-channel scale and shift are formed, for the conv that applies them as it stages x.
+    vae_status_t gn(const vae_tensor_t& x, const vae_tensor_t* y, const BoxList& bl,
                     const void* gamma, const void* beta, int layer) {
         double* stats = reinterpret_cast<double*>(ws + L.gn);
         double* parts = reinterpret_cast<double*>(ws + L.parts);
@@ -558,15 +565,24 @@ struct Runner {
         stats_ready = false;
         uint32_t* st = status();
         const double xe = (double)elem_size(x.dtype) * x.n * x.c;   // bytes per position
-        const double ye = (double)elem_size(y.dtype) * y.n * y.c;
+        auto scale_shift = [&]() {
+            return launch_gn_scale_shift(mr, (int32_t)x.n, (int32_t)x.c, d->groups,
+                                         static_cast<const float*>(gamma),
+                                         static_cast<const float*>(beta), norm_ab(), s);
+        };
         if (!per_patch) {
             if (!fused)
                 VAE_TRY(launch_gn_stats(x, bl, d->groups, stats, nullptr, mr, d->eps, s, st));
+            const double pos = (double)(x.t * x.h * x.w);
+            if (!y) {
+                VAE_TRY(scale_shift());
+                return mark(VAE_KIND_GN, layer, 0.0, fused ? 0.0 : pos * xe);
+            }
             // the patch boxes partition the tensor, so one apply launch covers them all
             VAE_TRY(launch_gn_apply(x, whole_box(x), d->groups, mr,
                                     static_cast<const float*>(gamma),
-                                    static_cast<const float*>(beta), true, y, s));
-            const double pos = (double)(x.t * x.h * x.w);
+                                    static_cast<const float*>(beta), true, *y, s));
+            const double ye = (double)elem_size(y->dtype) * y->n * y->c;
             return mark(VAE_KIND_GN, layer, 0.0, pos * ((fused ? 1.0 : 2.0) * xe + ye));
         }
         if (!fused) {
@@ -583,12 +599,30 @@ struct Runner {
             VAE_TRY(launch_gn_combine(parts, bl.n, (int32_t)x.n, d->groups, d->eps, mr, s, st));
             VAE_TRY(mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0));
         }
+        if (!y) {   // one scale and shift for every patch: shared work
+            VAE_TRY(scale_shift());
+            return mark_patch(-1, VAE_KIND_GN, layer, 0.0, 0.0);
+        }
+        const double ye = (double)elem_size(y->dtype) * y->n * y->c;
         for (int i = 0; i < bl.n; ++i) {
             VAE_TRY(launch_gn_apply(x, bl.b[i], d->groups, mr, static_cast<const float*>(gamma),
-                                    static_cast<const float*>(beta), true, y, s));
+                                    static_cast<const float*>(beta), true, *y, s));
             VAE_TRY(mark_patch(i, VAE_KIND_GN, layer, 0.0, (double)bl.b[i].volume() * (xe + ye)));
         }
         return VAE_OK;
+    }
+
+    float* norm_ab() { return reinterpret_cast<float*>(ws + L.ab); }
+
+    // Whether the conv with weights d->ptrs[wi] in layer `layer` (cout conv channels) applies
+    // the GroupNorm + SiLU of its input x while staging it (the norm's output is never written):
+    // an MFMA conv with packed weights and no fp32 split, reading fp32, or fp16 with bf16 weights.
+    bool fuse_norm(const vae_tensor_t& x, size_t wi, int layer, int64_t cout) const {
+        if (!(d->flags & VAE_DECODE_NORM_IN_CONV) || !d->packed[wi] ||
+            !conv_uses_mfma_c(x, cout, d->dtype) ||
+            conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer))
+            return false;
+        return x.dtype == VAE_DTYPE_F32 || (x.dtype == VAE_DTYPE_F16 && !conv_f16(*d, layer));
     }
 
     vae_status_t rms(const vae_tensor_t& x, const vae_tensor_t& y, const void* gamma,
@@ -605,17 +639,22 @@ struct Runner {
     // `lsh`, `lsw`: a nearest upsampling of x (log2 factors) that the conv reads while staging.
     // `bl`: the patch boxes in the conv's input grid; with per-patch launches the conv runs once
     // per box, and the statistics of all boxes land in one array that is merged once.
+    // `in_ab`: the scale and shift of a GroupNorm + SiLU of x that the conv applies while staging
+    // (fuse_norm), or null.
     vae_status_t conv(const vae_tensor_t& x, size_t wi, const vae_tensor_t* res,
                       const vae_tensor_t& y, int layer, bool gn_next, const BoxList& bl,
-                      const vae_layer_desc_t* up = nullptr, int32_t lsh = 0, int32_t lsw = 0) {
+                      const vae_layer_desc_t* up = nullptr, int32_t lsh = 0, int32_t lsw = 0,
+                      const float* in_ab = nullptr) {
         int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
                          ? VAE_CONV_SPLIT_FP32
                          : 0;
         const void* w = d->ptrs[wi];
         if (d->packed[wi]) {
-            // convs with fp16 operands were packed as fp16 (see vae_decoder_pack_weights)
+            // convs with fp16 operands were packed as fp16 (see vae_decoder_pack_weights); their
+            // input is fp16, or the fp32 input of the norm they apply
             w = d->packed[wi];
-            cf |= x.dtype == VAE_DTYPE_F16 ? VAE_CONV_PACKED_F16_WEIGHTS : VAE_CONV_PACKED_WEIGHTS;
+            const bool f16w = in_ab ? conv_f16(*d, layer) : x.dtype == VAE_DTYPE_F16;
+            cf |= f16w ? VAE_CONV_PACKED_F16_WEIGHTS : VAE_CONV_PACKED_WEIGHTS;
         }
         const int32_t k = up ? up->st * up->sh * up->sw : 1;
         const int64_t cout = y.c * k;
@@ -681,6 +720,7 @@ struct Runner {
             fz.slot0 = slot0;
             fz.slot_stride = total;
             fz.tdrop = tdrop;
+            fz.in_ab = in_ab;
             // a launch too small to fill the chip splits its K dimension over the scratch
             fz.splits = conv_split_count(xl, cout, d->dtype, b, (cf & VAE_CONV_SPLIT_FP32) != 0);
             if (fz.splits > 1) fz.part = reinterpret_cast<float*>(ws + L.splitk);
@@ -787,6 +827,7 @@ struct Runner {
         VAE_TRY(walk(*d, shape_of(in), &shapes, nullptr, nullptr, nullptr,
                      !clips || first_clip));
         stats_ready = false;
+        pending_norm = false;
         carry_off = 0;
         vae_tensor_t cur = in;
         int cur_buf = -1;  // -1: the caller's input, never written
@@ -826,8 +867,10 @@ struct Runner {
                 // ch, cw already hold a folded nearest upsampling: boxes in the conv's grid
                 const BoxList cb = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
                 VAE_TRY(conv(cur, p, nullptr, y, layer, gn_follows(*d, lo), cb,
-                             fuse_up ? &d->layers[li + 1] : nullptr, near_lsh, near_lsw));
+                             fuse_up ? &d->layers[li + 1] : nullptr, near_lsh, near_lsw,
+                             pending_norm ? norm_ab() : nullptr));
                 near_lsh = near_lsw = 0;
+                pending_norm = false;
                 p += 2;
                 cur = y;
                 cur_buf = out_last ? -2 : nb;
@@ -838,6 +881,8 @@ struct Runner {
                 }
             } else if (l.op == VAE_OP_RES) {
                 // x -> GN1 -> t1 -> conv1 -> t2 -> GN2 -> t1 -> conv2 (+ x) -> t2
+                // (a norm that its conv applies while staging writes no t1: the conv reads x or
+                // t2 itself, and y then goes to b1)
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
                 const int b1 = free_buf(cur_buf, -1);
                 const int b2 = free_buf(cur_buf, b1);
@@ -845,16 +890,21 @@ struct Runner {
                 gs.dtype = d->dtype;
                 as.dtype = res_mid_dtype(*d, l.cin);
                 vae_tensor_t t1 = buf(b1, gs), t2 = buf(b2, as);
-                VAE_TRY(gn(cur, t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
-                VAE_TRY(conv(t1, p + 2, nullptr, t2, layer, true, bl));
-                VAE_TRY(gn(t2, t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
+                const bool f1 = fuse_norm(cur, p + 2, layer, l.cin);
+                VAE_TRY(gn(cur, f1 ? nullptr : &t1, bl, d->ptrs[p], d->ptrs[p + 1], layer));
+                VAE_TRY(conv(f1 ? cur : t1, p + 2, nullptr, t2, layer, true, bl, nullptr, 0, 0,
+                             f1 ? norm_ab() : nullptr));
+                const bool f2 = fuse_norm(t2, p + 6, layer, l.cin);
+                VAE_TRY(gn(t2, f2 ? nullptr : &t1, bl, d->ptrs[p + 4], d->ptrs[p + 5], layer));
                 Shape ys = as;
-                ys.dtype = res_out_dtype(*d, li);   // conv1's output in b2 is dead by now
-                vae_tensor_t y = last ? final_out : buf(b2, ys);
-                VAE_TRY(conv(t1, p + 6, &cur, y, layer, gn_follows(*d, li), bl));
+                ys.dtype = res_out_dtype(*d, li);
+                const int yb = f2 ? b1 : b2;        // the buffer conv2 does not read
+                vae_tensor_t y = last ? final_out : buf(yb, ys);
+                VAE_TRY(conv(f2 ? t2 : t1, p + 6, &cur, y, layer, gn_follows(*d, li), bl, nullptr, 0,
+                             0, f2 ? norm_ab() : nullptr));
                 p += 8;
                 cur = y;
-                cur_buf = last ? -2 : b2;
+                cur_buf = last ? -2 : yb;
             } else if (l.op == VAE_OP_RES_RMS) {
                 // x -> RMS1 -> t1 -> conv1 -> t2 -> RMS2 -> t1 -> conv2 (+ x) -> t2
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
@@ -910,6 +960,14 @@ struct Runner {
                 p += 6;
                 cur = y;
                 cur_buf = last ? -2 : nb;
+            } else if (l.op == VAE_OP_GN_SILU && !last && d->layers[li + 1].op == VAE_OP_CONV &&
+                       fuse_norm(cur, p + 2, layer + 1, d->layers[li + 1].cout)) {
+                // the next conv applies the norm while staging its input: statistics, scale and
+                // shift only
+                const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
+                VAE_TRY(gn(cur, nullptr, bl, d->ptrs[p], d->ptrs[p + 1], layer));
+                p += 2;
+                pending_norm = true;
             } else if (l.op == VAE_OP_GN_SILU) {
                 const BoxList bl = scaled_boxes(boxes, cur.t, ch, cw, fh, fw);
                 vae_tensor_t y;
@@ -925,7 +983,7 @@ struct Runner {
                 } else {
                     y = cur;  // in place
                 }
-                VAE_TRY(gn(cur, y, bl, d->ptrs[p], d->ptrs[p + 1], layer));
+                VAE_TRY(gn(cur, &y, bl, d->ptrs[p], d->ptrs[p + 1], layer));
                 p += 2;
                 cur = y;
                 cur_buf = nb;
@@ -1087,7 +1145,8 @@ VAE_API vae_status_t vae_decoder_create(const vae_decoder_spec_t* spec,
     if (spec->act_dtype != VAE_DTYPE_F32)
         return fail(VAE_ERR_UNSUPPORTED, "activations between ops are stored in fp32 "
                                          "(act_dtype must be VAE_DTYPE_F32)");
-    if (spec->flags & ~(VAE_DECODE_SPLIT_FP32_OPERANDS | VAE_DECODE_F16_OPERANDS))
+    if (spec->flags &
+        ~(VAE_DECODE_SPLIT_FP32_OPERANDS | VAE_DECODE_F16_OPERANDS | VAE_DECODE_NORM_IN_CONV))
         return fail(VAE_ERR_INVALID_ARG, "unknown decoder flags");
     if ((spec->flags & VAE_DECODE_SPLIT_FP32_OPERANDS) && (spec->flags & VAE_DECODE_F16_OPERANDS))
         return fail(VAE_ERR_INVALID_ARG, "give one of the split and fp16 operand flags");

@@ -365,17 +365,17 @@ __global__ __launch_bounds__(kThreads) void gn_apply_kernel(
         const int g = c / cpg;
         const float gm = gamma ? gamma[c] : 1.0f;
         const float bt = beta ? beta[c] : 0.0f;
-        sc[k] = mr[2 * g + 1] * gm;
-        sh[k] = bt - mr[2 * g] * sc[k];
+        gn_scale_shift_of(mr[2 * g], mr[2 * g + 1], gm, bt, sc[k], sh[k]);
     }
     auto apply = [&](int e, const uint4& raw) {
         const TI* v = reinterpret_cast<const TI*>(&raw);
         TO out[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            float z = fmaf(Elem<TI>::load(v + k), sc[k], sh[k]);
-            if (silu) z = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-            Elem<TO>::store(out + k, z);
+            const float x = Elem<TI>::load(v + k);
+            // fp32 first, then the store's rounding (as a conv that normalises while staging)
+            Elem<TO>::store(out + k, materialise_f32(silu ? gn_silu_apply(x, sc[k], sh[k])
+                                                          : fmaf(x, sc[k], sh[k])));
         }
         if constexpr (sizeof(TO) * V == 16) {
             *reinterpret_cast<uint4*>(yr + (int64_t)e * V) = *reinterpret_cast<const uint4*>(out);
@@ -397,6 +397,22 @@ __global__ __launch_bounds__(kThreads) void gn_apply_kernel(
         for (int u = 0; u < 4; ++u) apply(e + u * kThreads, raw[u]);
     }
     for (; e < seg; e += kThreads) apply(e, *reinterpret_cast<const uint4*>(xr + (int64_t)e * V));
+}
+
+// One thread per (sample, channel): the apply kernel's scale and shift, stored for a conv that
+// normalises its input while staging it ([N][C][2] fp32).
+__global__ __launch_bounds__(kThreads) void gn_scale_shift_kernel(
+    const float* __restrict__ mean_rstd, int32_t C, int32_t groups, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* __restrict__ ab, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total) return;
+    const int64_t n = i / C;
+    const int c = (int)(i - n * C);
+    const int g = c / (C / groups);
+    const float* mr = mean_rstd + n * groups * 2;
+    const float gm = gamma ? gamma[c] : 1.0f;
+    const float bt = beta ? beta[c] : 0.0f;
+    gn_scale_shift_of(mr[2 * g], mr[2 * g + 1], gm, bt, ab[2 * i], ab[2 * i + 1]);
 }
 
 template <typename TI, typename TO>
@@ -477,6 +493,17 @@ vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int3
     hipLaunchKernelGGL(gn_finalize_slots_kernel, dim3((unsigned)groups, (unsigned)n),
                        dim3(kThreads), 0, stream, ws, slots, kSlotChunk, (int32_t)chunks, groups,
                        eps, mean_rstd, status);
+    VAE_HIP_CHECK(hipGetLastError());
+    return VAE_OK;
+}
+
+vae_status_t launch_gn_scale_shift(const float* mean_rstd, int32_t n, int32_t c, int32_t groups,
+                                   const float* gamma, const float* beta, float* ab,
+                                   hipStream_t stream) {
+    const int64_t total = (int64_t)n * c;
+    if (total == 0) return VAE_OK;
+    hipLaunchKernelGGL(gn_scale_shift_kernel, dim3((unsigned)ceil_div(total, kThreads)),
+                       dim3(kThreads), 0, stream, mean_rstd, c, groups, gamma, beta, ab, total);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }

@@ -42,6 +42,9 @@ struct ConvFuse {
     // Frames of the depth-to-space output dropped before y's frame 0 (see MfmaArgs::tdrop);
     // -1: st - 1, the causal drop.
     int32_t tdrop = -1;
+    // GroupNorm + SiLU of x applied while staging (MFMA path, packed weights): fp32 (scale,
+    // shift) per (sample, input channel), [N][Cin][2]; the conv reads silu(x * scale + shift).
+    const float* in_ab = nullptr;
 };
 vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
                            const float* bias, const vae_tensor_t* residual, const vae_tensor_t& y,
@@ -102,6 +105,10 @@ vae_status_t launch_gn_combine(const double* part, int32_t n_parts, int32_t n, i
 vae_status_t launch_gn_finalize_slots(double* ws, int64_t slots, int32_t n, int32_t groups,
                                       float eps, float* mean_rstd, hipStream_t stream,
                                       uint32_t* status = nullptr);
+// The apply step's per-(sample, channel) scale and shift, [N][C][2] fp32 (ConvFuse::in_ab).
+vae_status_t launch_gn_scale_shift(const float* mean_rstd, int32_t n, int32_t c, int32_t groups,
+                                   const float* gamma, const float* beta, float* ab,
+                                   hipStream_t stream);
 vae_status_t launch_gn_apply(const vae_tensor_t& x, const Box& box, int32_t groups,
                              const float* mean_rstd, const float* gamma, const float* beta,
                              bool silu, const vae_tensor_t& y, hipStream_t stream);

@@ -10,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 
 from ._binding import (Decoder, VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DECODE_F16_OPERANDS,
-                       VAE_DECODE_SPLIT_FP32_OPERANDS)
+                       VAE_DECODE_NORM_IN_CONV, VAE_DECODE_SPLIT_FP32_OPERANDS)
 
 # How convs that read an fp32 activation (the upsampling convs, conv_out) get their operands:
 # "f16" (one rounding to fp16, bf16 rate), "split" (bf16 hi + lo, twice the work) or "bf16".
@@ -60,7 +60,7 @@ def pad_latent(z, spec: dict):
 
 
 def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", operands="f16",
-                   packed=True):
+                   packed=True, norm_in_conv=False):
     """Build a Decoder for a layer plan ``spec`` with parameter dicts in plan order.
 
     Each parameter dict is {"kind": "conv", "w", "b"} or {"kind": "gn", "gamma", "beta"} holding
@@ -68,7 +68,9 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", ope
     takes "f32" only (it refuses bf16 storage, which misses the bf16 decode's accuracy bound).
     ``operands`` picks how convs that read an fp32 activation get their operands (OPERAND_FLAGS;
     bf16 plans only). ``packed`` gives the MFMA convs fragment-packed weight
-    copies. Returns the Decoder; it keeps the device tensors alive.
+    copies. ``norm_in_conv``: those convs apply the GroupNorm + SiLU of their input while staging
+    it, instead of a normalise pass of its own (VAE_DECODE_NORM_IN_CONV). Returns the Decoder; it
+    keeps the device tensors alive.
     """
     import torch
     tdt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
@@ -104,6 +106,8 @@ def upload_decoder(spec: dict, params: list, device="cuda", act_dtype="f32", ope
     code = VAE_DTYPE_BF16 if spec["dtype"] == "bf16" else VAE_DTYPE_F32
     act = VAE_DTYPE_BF16 if act_dtype == "bf16" else VAE_DTYPE_F32
     flags = OPERAND_FLAGS[operands] if code == VAE_DTYPE_BF16 else 0
+    if norm_in_conv:
+        flags |= VAE_DECODE_NORM_IN_CONV
     dec = Decoder(code, lc, spec["groups"], spec["eps"], layers, flat, act_dtype=act,
                   flags=flags)
     if packed:
