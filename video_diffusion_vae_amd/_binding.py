@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvae_mi355x.so")
+# VAE_MI355X_LIB points at another build of the library (e.g. the sanitized host build).
+LIB_PATH = os.environ.get("VAE_MI355X_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libvae_mi355x.so")
 
 VAE_OK, VAE_ERR_INVALID_ARG, VAE_ERR_UNSUPPORTED, VAE_ERR_HIP, VAE_ERR_WORKSPACE = range(5)
 VAE_DTYPE_BF16, VAE_DTYPE_F32, VAE_DTYPE_F16 = 1, 2, 3
