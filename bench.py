@@ -50,7 +50,7 @@ OPERANDS = {
              "hi+lo; fp32 accumulate",
     "bf16": "bf16 weights and operands; fp32 accumulate",
 }
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "conv3d_mfma_ltx2_720p_patch_halo_1x4_traffic.json")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "conv3d_mfma_ltx2_720p_decode_merged_traffic.json")
 
 
 def log(*a):
