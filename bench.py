@@ -340,7 +340,7 @@ def cpu_baseline(spec, params, frames=2):
     latent frames (an encoder: the input frames that fold into that many latent frames). `value`
     is the sample's own throughput, the video pixel-frames it produced (or consumed) per second:
     measured, not extrapolated. Per output frame the sample does slightly more conv work than the
-    full decode (the first latent frame decodes to one frame), so the figure leans high."""
+    full decode (the first latent frame decodes to one frame), so the figure leans low."""
     import threadpoolctl
     import oracle
     import vae_synth
