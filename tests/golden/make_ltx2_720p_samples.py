@@ -1,6 +1,6 @@
 """Write sampled oracle outputs of the 720p LTX-2-shaped decode to tests/golden/.
 
-Usage: python tests/golden/make_ltx2_720p_samples.py [whole|overlap]
+Usage: python tests/golden/make_ltx2_720p_samples.py [whole|overlap|band]
 
 This is the full-size parity reference. The oracle (fp64, CPU) decodes the latent
 [1,128,16,22,40] to [1,3,121,704,1280]: fp64 throughout, about 70 TFLOP and 20-40 minutes on
@@ -11,7 +11,11 @@ The GPU test decodes the same seeded latent and weights and compares at the samp
 
 Modes:
 - ``whole``: the untiled decode, which the patch-halo decode must equal;
-- ``overlap``: the overlap-blend decode with latent tile 16 and stride 14 (512/448 px).
+- ``overlap``: the overlap-blend decode with latent tile 16 and stride 14 (512/448 px);
+- ``band``: the untiled decode again, keeping every value of a 16-row band of output frame 60
+  (all 1280 columns, so the three seams of the 1x4 width split lie inside it) in
+  ``ltx2_720p_whole_band.npz``: a full-T decode compared at every value of a region of a frame
+  far past frame 0.
 
 Only ``oracle`` and ``vae_synth`` are used; nothing here touches the GPU path.
 """
@@ -29,6 +33,7 @@ import vae_synth   # noqa: E402
 
 N_RANDOM = 12288
 N_SEAM = 4096
+BAND = (60, 344, 360)     # output frame, first row, end row of the stored band
 
 
 def sample_positions(t_out, h_out, w_out, seams):
@@ -48,7 +53,7 @@ def main(mode: str):
     z = np.ascontiguousarray(vae_synth.latent(spec).transpose(0, 2, 3, 4, 1))
     params = vae_synth.decoder_params(spec)
     print(f"[golden] inputs ready in {time.time() - t0:.1f}s", flush=True)
-    if mode == "whole":
+    if mode in ("whole", "band"):
         out = oracle.decode(spec, z, params)
     elif mode == "overlap":
         out = oracle.decode_overlap_blend(spec, z, params, spec["overlap_tile"],
@@ -56,6 +61,14 @@ def main(mode: str):
     else:
         raise SystemExit(f"unknown mode {mode!r}")
     print(f"[golden] decode done in {time.time() - t0:.1f}s, shape {out.shape}", flush=True)
+    if mode == "band":
+        frame, r0, r1 = BAND
+        path = os.path.join(HERE, "ltx2_720p_whole_band.npz")
+        np.savez_compressed(path, frame=np.int32(frame), rows=np.array([r0, r1], np.int32),
+                            values=out[0, frame, r0:r1].astype(np.float64),
+                            out_min=out.min(), out_max=out.max(), shape=np.array(out.shape))
+        print(f"[golden] wrote {path} in {time.time() - t0:.1f}s", flush=True)
+        return
     _, t_out, h_out, w_out, _ = out.shape
     # patch seams of the 1x4 width split and the overlap-tile boundaries (in pixels)
     seams = [319, 320, 639, 640, 959, 960, 447, 448, 511, 512, 895, 896, 1023, 1024]

@@ -252,6 +252,30 @@ def test_ltx2_720p_patch_halo_against_golden(v, operands):
     assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
 
 
+@pytest.mark.parametrize("launch", ["merged", "per_patch"])
+def test_ltx2_720p_full_decode_band_every_value(v, launch):
+    """The full 720p decode (16 latent frames, GroupNorm statistics over all 121 output frames),
+    1x4 width patches: every value of a 16-row band of output frame 60, all 1280 columns (the
+    three patch seams inside it), against the oracle's full fp64 decode
+    (tests/golden/make_ltx2_720p_samples.py band)."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "ltx2_720p_whole_band.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path)
+    f, (r0, r1) = int(g["frame"]), (int(x) for x in g["rows"])
+    out = gpu_decode(v, "ltx2_720p", "patch", (1, 4), launch=launch)
+    assert tuple(out.shape) == tuple(int(d) for d in g["shape"])
+    got = out[0, f, r0:r1].double().cpu().numpy()
+    ref = g["values"]
+    assert got.shape == ref.shape == (16, 1280, 3)
+    p = 10 * np.log10((float(g["out_max"]) - float(g["out_min"])) ** 2 /
+                      np.mean((got - ref) ** 2))
+    m = float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)
+
+
 def test_ltx2_tiny_both_modes(v):
     got = host(gpu_decode(v, "ltx2_tiny", "patch", (1, 2)))
     _bf16_bar(got, oracle_out("ltx2_tiny", "whole"))

@@ -248,3 +248,23 @@ def test_wan_720p_six_frames_against_golden(v, clip):
     o = out.double()
     assert abs(float(o.mean()) - float(g["out_mean"])) <= 1e-3 * float(g["out_std"])
     assert abs(float(o.std()) / float(g["out_std"]) - 1.0) <= 1e-3
+
+
+def test_wan_720p_first_frames_of_the_full_decode_every_value(v):
+    """The full 21-frame Wan-shaped 720p decode ([1,48,21,44,80] -> [1,81,704,1280,3]) in 1 x 4
+    width patches. Its output frames 0..4 depend only on latent frames 0 and 1: the convs are
+    causal, the norms per position, the attention per frame and the temporal upsamplers causal
+    (pinned on the CPU by test_oracle_decoder's first-frames test). So the oracle decodes those two
+    latent frames alone (about half a minute on the CPU), and every one of the 13.5M values of
+    frames 0..4 of the full GPU decode is held to the bf16 bar: frames past frame 0 of a full-T
+    decode, at every value."""
+    spec = vae_synth.WAN_720P
+    got = _decode(v, "wan_720p", "patch", (1, 4))
+    assert tuple(got.shape) == (1, 81, 704, 1280, 3)
+    got = got[:, :5].double().cpu().numpy()
+    z = ndhwc(vae_synth.latent(spec))[:, :2]
+    ref = oracle.decode(vae_synth.with_latent(spec, (1, 48, 2, 44, 80), "wan_720p_2f"), z,
+                        _params("wan_720p"))
+    assert ref.shape == got.shape
+    p, m = psnr(got, ref), float(np.abs(got - ref).max())
+    assert p >= 50.0 and m <= 2e-2, (p, m)

@@ -261,3 +261,25 @@ def test_causal_clips_refuse_groupnorm_plans():
     z = ndhwc(vae_synth.latent(spec))
     with pytest.raises(AssertionError):
         oracle.decode_causal_clips(spec, z, vae_synth.decoder_params(spec), 1)
+
+
+def test_first_frames_of_a_time_local_plan_depend_on_the_first_latent_frames():
+    """For a plan whose every op is local in time (causal convs, RMS norms, per-frame attention,
+    causal upsamplers: the Wan-shaped plan), the first 1 + (k - 1) * 4 output frames of a decode
+    are the decode of the first k latent frames alone; the GPU's full-T Wan test relies on this.
+    A GroupNorm plan is the control: its statistics span every frame, so the same frames differ."""
+    spec = vae_synth.WAN_TINY
+    z = ndhwc(vae_synth.latent(spec))
+    p = vae_synth.decoder_params(spec, affine_seed=5)
+    full = oracle.decode(spec, z, p)
+    first = oracle.decode(vae_synth.with_latent(spec, (1, 48, 2, 4, 6), "wan_tiny_2f"), z[:, :2], p)
+    assert first.shape[1] == 5
+    np.testing.assert_allclose(full[:, :5], first, rtol=0, atol=1e-12 * np.abs(full).max())
+    gspec = vae_synth.LTX2_MID
+    gz = ndhwc(vae_synth.latent(gspec))
+    gp = vae_synth.decoder_params(gspec)
+    gfull = oracle.decode(gspec, gz, gp)
+    gfirst = oracle.decode(vae_synth.with_latent(gspec, (1, 128, 2, 4, 6), "ltx2_mid_2f"),
+                           gz[:, :2], gp)
+    n = gfirst.shape[1]
+    assert np.abs(gfull[:, :n] - gfirst).max() > 1e-3 * np.abs(gfull).max()

@@ -1250,11 +1250,13 @@ inline int64_t conv_workgroups(int64_t n, int64_t cout, const Box& box) {
            ceil_div(cout, conv_nt(cout));
 }
 
-template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
-vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
-                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
-                       const ConvFuse* fz, hipStream_t stream) {
-    MfmaArgs a;
+// The launch arguments every MFMA conv kernel shares, and the check that the box lies in the
+// input grid and every value the grid stores lies in y (and in the residual, which has y's
+// shape).
+inline vae_status_t mfma_common_args(const vae_tensor_t& x, const void* w, const float* bias,
+                                     const vae_tensor_t* residual, const vae_tensor_t& y,
+                                     const Box& box, const ConvFuse* fz, MfmaArgs* out) {
+    MfmaArgs& a = *out;
     a.x = x.data;
     a.w = static_cast<const uint16_t*>(w);
     a.bias = bias;
@@ -1272,22 +1274,35 @@ vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
     a.sw = fz ? fz->sw : 1;
     a.tdrop = fz && fz->tdrop >= 0 ? fz->tdrop : a.st - 1;
     a.nab = fz ? fz->in_ab : nullptr;
-    if (InT<TI>::norm != (a.nab != nullptr))
-        return fail(VAE_ERR_INVALID_ARG, "conv3d: input normalisation without its scale and shift");
     a.zc = (int32_t)y.c;
     a.cout = (int32_t)(y.c * a.st * a.sh * a.sw);
     a.yT = (int32_t)y.t;
     a.yH = (int32_t)y.h;
     a.yW = (int32_t)y.w;
     a.box = box;
-    // every position the grid stages lies in x, every value it stores lies in y (and in the
-    // residual, which has y's shape)
+    a.stats = nullptr;
+    a.groups = 1;
+    a.nslots = a.slot0 = 0;
+    a.splits = 1;
+    a.part = nullptr;
+    a.reduce = nullptr;
     if (box.t0 < 0 || box.h0 < 0 || box.w0 < 0 || box.t1 > a.T || box.h1 > a.H ||
         box.w1 > a.W || (int64_t)a.st * box.t1 - a.tdrop > a.yT ||
         (int64_t)a.sh * box.h1 > a.yH || (int64_t)a.sw * box.w1 > a.yW || y.n != x.n ||
         (residual && (residual->n != y.n || residual->t != y.t || residual->h != y.h ||
                       residual->w != y.w || residual->c != y.c)))
         return fail(VAE_ERR_INVALID_ARG, "conv3d: box outside the input, or outputs outside y");
+    return VAE_OK;
+}
+
+template <int NT, typename TI, typename TO, bool SPLIT, bool PACKED, int TB, int HB, int WB>
+vae_status_t run_shape(const vae_tensor_t& x, const void* w, const float* bias,
+                       const vae_tensor_t* residual, const vae_tensor_t& y, const Box& box,
+                       const ConvFuse* fz, hipStream_t stream) {
+    MfmaArgs a;
+    VAE_TRY(mfma_common_args(x, w, bias, residual, y, box, fz, &a));
+    if (InT<TI>::norm != (a.nab != nullptr))
+        return fail(VAE_ERR_INVALID_ARG, "conv3d: input normalisation without its scale and shift");
     a.nbt = (int32_t)ceil_div(box.bt(), TB);
     a.nbh = (int32_t)ceil_div(box.bh(), HB);
     a.nbw = (int32_t)ceil_div(box.bw(), WB);
