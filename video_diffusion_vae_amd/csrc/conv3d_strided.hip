@@ -10,15 +10,16 @@
 // (T - 1) / st + 1; H rows become (H + pt + pb - 3) / sh + 1.
 //
 // Matrix-core path (bf16 or fp16 x, fragment-packed weights, Cin % 32 == 0):
-//  - implicit GEMM over 128-position output blocks of 2 x 8 x 8 (the stride multiplies the input
-//    footprint: 5 x 17 x 17 positions at stride 2), 4 waves, NT output channels per workgroup;
+//  - implicit GEMM over output blocks of 2 x 8 x 8 positions, or 2 x 4 x 8 with 128-wide channel
+//    tiles (the stride multiplies the input footprint: 5 x 17 x 17 or 5 x 9 x 17 positions at
+//    stride 2), 4 waves, NT output channels per workgroup;
 //  - per 32-channel chunk the block's input footprint is staged in LDS (halo rows read in place,
 //    causal frames clamped, zeros outside the image), 80 bytes per position; lane l of a fragment
 //    read takes output column l % 8 at input column 2 * (l % 8), 160 bytes apart, so 8 lanes hit
 //    8 distinct 16-byte bank groups;
-//  - the footprint of a stride-2 block fills 116 KB of LDS: one workgroup per CU. All of a chunk's
-//    staging loads are issued before the first is written, so a chunk waits about one memory
-//    latency;
+//  - a 2 x 8 x 8 block's stride-2 footprint fills 116 KB of LDS (one workgroup per CU), a 2 x 4 x 8
+//    block's 61 KB (two per CU, one staging while the other computes). All of a chunk's staging
+//    loads are issued before the first is written, so a chunk waits about one memory latency;
 //  - weights and the epilogue (bias, residual, GroupNorm partials) as in conv3d_mfma.h.
 // Everything else runs on a direct kernel, one thread per output, fp32 accumulation.
 #include <algorithm>
@@ -29,13 +30,16 @@ namespace vae {
 namespace mfma {
 namespace {
 
-constexpr int kSTB = 2, kSHB = 8, kSWB = 8;   // output block, 128 positions
-constexpr int kSPos = kSTB * kSHB * kSWB;
+// Output block per workgroup: 2 x 8 x 8 (128 positions), or 2 x 4 x 8 (64) at NT = 128. The
+// smaller block's stride-2 footprint (61 KB of LDS) lets two workgroups share a CU, so one stages
+// while the other computes; with 128-wide channel tiles each still runs two MFMA tiles per wave.
+constexpr int kSTB = 2, kSWB = 8;
+constexpr int strided_hb(int nt) { return nt == 128 ? 4 : 8; }
 
-template <int ST, int SS>
+template <int ST, int SS, int HB>
 struct StridedShape {
     static constexpr int FT = (kSTB - 1) * ST + 3;   // input frames staged per block
-    static constexpr int FH = (kSHB - 1) * SS + 3;
+    static constexpr int FH = (HB - 1) * SS + 3;
     static constexpr int FW = (kSWB - 1) * SS + 3;
     static constexpr int kPos = FT * FH * FW;
     static constexpr int kBytes = kPos * kRow;
@@ -48,15 +52,16 @@ struct StridedArgs {
 };
 
 template <int NT, typename TI, typename TO, int ST, int SS>
-__global__ __launch_bounds__(kMfmaThreads, 1)
+__global__ __launch_bounds__(kMfmaThreads, NT == 128 ? 2 : 1)
 void conv3d_strided_kernel(StridedArgs sa) {
-    using S = StridedShape<ST, SS>;
+    constexpr int HB = strided_hb(NT);
+    using S = StridedShape<ST, SS, HB>;
     const MfmaArgs& a = sa.e;
     constexpr bool F16 = std::is_same<TI, _Float16>::value;
-    constexpr int TB = kSTB, HB = kSHB, WB = kSWB;
+    constexpr int TB = kSTB, WB = kSWB;
     constexpr int WNN = NT / 32;
     constexpr int WM = kMfmaWaves / WNN;
-    constexpr int MW = kSPos / WM;
+    constexpr int MW = TB * HB * WB / WM;
     constexpr int MI = MW / 32;
     constexpr int PD = 2, NB = PD + 1;
     constexpr int UNITS = S::kPos * 4;                   // 8-channel staging units per chunk
@@ -285,7 +290,7 @@ vae_status_t run_strided_mfma(const vae_tensor_t& x, const void* w, const float*
     a.yW = (int32_t)y.w;
     a.box = box;
     a.nbt = (int32_t)ceil_div(box.bt(), kSTB);
-    a.nbh = (int32_t)ceil_div(box.bh(), kSHB);
+    a.nbh = (int32_t)ceil_div(box.bh(), strided_hb(NT));
     a.nbw = (int32_t)ceil_div(box.bw(), kSWB);
     const int64_t mblocks = x.n * (int64_t)a.nbt * a.nbh * a.nbw;
     const int64_t total = mblocks * ceil_div(a.cout, NT);
@@ -365,7 +370,8 @@ int64_t conv_strided_gn_slots(const vae_tensor_t& y, const Box& box, int32_t gro
     const int64_t cpg = y.c / groups;
     if (cpg % 4 || 32 % cpg) return 0;
     const int wm = y.c >= 128 ? wave_rows<128>() : y.c > 32 ? wave_rows<64>() : wave_rows<32>();
-    return ceil_div(box.bt(), kSTB) * ceil_div(box.bh(), kSHB) * ceil_div(box.bw(), kSWB) * wm;
+    return ceil_div(box.bt(), kSTB) * ceil_div(box.bh(), strided_hb(conv_nt(y.c))) *
+           ceil_div(box.bw(), kSWB) * wm;
 }
 
 vae_status_t launch_conv3d_strided(const vae_tensor_t& x, const void* w, int32_t weight_dtype,
