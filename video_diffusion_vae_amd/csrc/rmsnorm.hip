@@ -8,7 +8,8 @@
 // NDHWC puts a position's C channels in one contiguous run. Each thread owns 8 consecutive
 // channels of one position (one 16-byte load for bf16, two for fp32); the C / 8 threads of a
 // position sum their squares with lane shuffles, and through LDS when a position spans two waves
-// (C = 1024 or 2048). A block of 256 threads covers 256 / (C / 8) positions per step.
+// (C = 1024 or 2048). A block of 256 threads covers 256 / (C / 8) positions per step, and each
+// thread loads its channels of four steps before reducing any, so that four loads are in flight.
 #include <algorithm>
 
 #include "kernels.h"
@@ -18,6 +19,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 8192;
+constexpr int kUnroll = 4;          // block steps (positions per thread) in flight at once
 
 template <typename TI, typename TO>
 __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict__ x,
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict
                                                             const float* __restrict__ gamma,
                                                             const float* __restrict__ beta,
                                                             int32_t silu, uint32_t* status) {
-    __shared__ float part[kThreads / 64];                  // one partial per wave
+    __shared__ float part[kUnroll][kThreads / 64];         // one partial per wave and position
     const int tpp = C / 8;                                 // threads per position
     const int ppb = kThreads / tpp;                        // positions per block step
     const int tid = threadIdx.x;
@@ -38,40 +40,60 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict
         sc[k] = gamma ? gamma[c0 + k] : 1.0f;
         sh[k] = beta ? beta[c0 + k] : 0.0f;
     }
-    for (int64_t p0 = (int64_t)blockIdx.x * ppb; p0 < positions; p0 += (int64_t)gridDim.x * ppb) {
-        const int64_t p = p0 + slot;
-        const bool valid = p < positions;
-        float v[8];
-        const TI* src = x + (valid ? p : 0) * C + c0;
+    // kUnroll block steps at a time: all their loads are in flight before the first reduction
+    const int64_t step = (int64_t)ppb * kUnroll;
+    for (int64_t p0 = (int64_t)blockIdx.x * step; p0 < positions; p0 += (int64_t)gridDim.x * step) {
+        float v[kUnroll][8];
+        bool valid[kUnroll];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = Elem<TI>::load(src + k);
-        float ss = 0.0f;
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t p = p0 + u * ppb + slot;
+            valid[u] = p < positions;
+            const TI* src = x + (valid[u] ? p : 0) * C + c0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ss = fmaf(v[k], v[k], ss);
+            for (int k = 0; k < 8; ++k) v[u][k] = Elem<TI>::load(src + k);
+        }
+        float ss[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            ss[u] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ss[u] = fmaf(v[u][k], v[u][k], ss[u]);
+        }
         // sum over the position's threads: within the wave, then across the two waves of a
         // position when tpp = 128 or 256
         const int span = tpp < 64 ? tpp : 64;
-        for (int off = 1; off < span; off <<= 1) ss += __shfl_xor(ss, off);
+        for (int off = 1; off < span; off <<= 1)
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) ss[u] += __shfl_xor(ss[u], off);
         if (tpp > 64) {
-            if (lane == 0) part[wave] = ss;
+            if (lane == 0)
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) part[u][wave] = ss[u];
             __syncthreads();
             const int w0 = (tid / tpp) * (tpp / 64);
-            float t = 0.0f;
-            for (int w = 0; w < tpp / 64; ++w) t += part[w0 + w];
-            ss = t;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                float t = 0.0f;
+                for (int w = 0; w < tpp / 64; ++w) t += part[u][w0 + w];
+                ss[u] = t;
+            }
             __syncthreads();
         }
-        // a non-finite sum of squares: an input value was inf or NaN (e.g. an activation past
-        // fp16's 65504 at an fp16 operand hand-off)
-        if (status && valid && !isfinite(ss)) *status = 1u;
-        const float r = 1.0f / sqrtf(ss / (float)C + eps);
-        if (valid) {
-            TO* dst = y + p * C + c0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float z = fmaf(v[k] * r, sc[k], sh[k]);
-                if (silu) z = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-                Elem<TO>::store(dst + k, z);
+        for (int u = 0; u < kUnroll; ++u) {
+            // a non-finite sum of squares: an input value was inf or NaN (e.g. an activation
+            // past fp16's 65504 at an fp16 operand hand-off)
+            if (status && valid[u] && !isfinite(ss[u])) *status = 1u;
+            const float r = 1.0f / sqrtf(ss[u] / (float)C + eps);
+            if (valid[u]) {
+                TO* dst = y + (p0 + u * ppb + slot) * C + c0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    float z = fmaf(v[u][k] * r, sc[k], sh[k]);
+                    if (silu) z = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+                    Elem<TO>::store(dst + k, z);
+                }
             }
         }
     }
@@ -82,7 +104,8 @@ void rms_launch(const vae_tensor_t& x, float eps, const float* gamma, const floa
                 const vae_tensor_t& y, hipStream_t stream, uint32_t* status) {
     const int64_t positions = vae::positions(x);
     const int ppb = kThreads / (int)(x.c / 8);
-    const int64_t blocks = std::min<int64_t>(ceil_div(positions, ppb), kMaxBlocks);
+    const int64_t blocks =
+        std::min<int64_t>(ceil_div(positions, (int64_t)ppb * kUnroll), kMaxBlocks);
     hipLaunchKernelGGL((rms_norm_kernel<TI, TO>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        static_cast<const TI*>(x.data), static_cast<TO*>(y.data), positions,
                        (int32_t)x.c, eps, gamma, beta, (int32_t)silu, status);
