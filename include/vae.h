@@ -176,12 +176,15 @@ VAE_API vae_status_t vae_conv3d_causal(const vae_tensor_t* x, const void* weight
  *  undefined afterwards.
  *
  * VAE_CONV_SPLIT_K (this call only; flags of vae_conv3d_causal must not hold it): when the MFMA
- * launch over out_box would fill fewer than the chip's 256 compute units (a small box, such as
- * one patch of the first decoder stages), the conv splits its K dimension (the input-channel
- * chunks) up to 4 ways. One launch stores each split's fp32 partial sums in ws, after the
+ * launch over out_box would give fewer than two workgroups per compute unit (512 on the chip's
+ * 256; a small box, such as one patch of the first decoder stages), the conv splits its K
+ * dimension (the input-channel chunks) up to 4 ways. One launch stores each split's fp32 partial sums in ws, after the
  * statistics partials; a second adds them in split order and runs the epilogue. The result is
  * deterministic and differs from the unsplit conv only in the order of the fp32 additions. The
- * workspace query includes those bytes when the flag is given.
+ * workspace query includes those bytes when the flag is given. A launch with Cout >= 128 and
+ * fewer than 256 workgroups also takes 64-wide output-channel tiles instead of 128, for twice the
+ * workgroups before the split: the conv's sums are the same, and its statistics partials cover
+ * 128 positions each instead of 256.
  *
  * Input GroupNorm + SiLU (in_scale_shift non-NULL): the conv reads silu(x * scale_c + shift_c)
  * instead of x, with [N][Cin][2] fp32 (scale, shift) per (sample, input channel) as

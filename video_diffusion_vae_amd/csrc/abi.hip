@@ -470,7 +470,8 @@ size_t fused_workspace(const vae_conv_fused_t* a, const FusedPlan& p, int64_t* s
     *slots = 0;
     size_t gn = 0;
     if (a->gn_groups) {
-        *slots = conv_gn_slots(*a->x, a->y->c, a->weight_dtype, p.cbox, a->gn_groups, p.k);
+        *slots = conv_gn_slots(*a->x, a->y->c, a->weight_dtype, p.cbox, a->gn_groups, p.k,
+                               (a->flags & VAE_CONV_SPLIT_K) != 0);
         if (*slots > 0) {
             gn = (size_t)(a->y->n * a->gn_groups * *slots * 3) * sizeof(double);
         } else {

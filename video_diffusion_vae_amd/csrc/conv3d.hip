@@ -192,27 +192,44 @@ bool conv_uses_mfma_c(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype)
     return weight_dtype == VAE_DTYPE_BF16 && x.c % kCK == 0 && cout % 4 == 0;
 }
 
+// Output-channel tile of one launch: conv_nt's width, but with `fill` (a launch allowed to split
+// over K to fill the chip) 64 where 128-wide tiles would give fewer than 256 workgroups, such as
+// one patch's share of the first stages: twice the workgroups before any split over K, so half the
+// split and half its partial sums. Measured on the 1x4 split's interior patch: its S0 convs 0.48
+// -> 0.455 ms, conv_in 0.082 -> 0.069 ms.
+static int launch_nt(int64_t n, int64_t cout, const Box& box, bool fill) {
+    const int nt = conv_nt(cout);
+    return fill && nt == 128 && conv_workgroups(n, cout, box) < 256 ? 64 : nt;
+}
+
+static int64_t launch_workgroups(int64_t n, int64_t cout, const Box& box, bool fill) {
+    return conv_workgroups(n, cout, box) / ceil_div(cout, conv_nt(cout)) *
+           ceil_div(cout, launch_nt(n, cout, box, fill));
+}
+
 int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, const Box& box,
-                      int32_t groups, int32_t k) {
+                      int32_t groups, int32_t k, bool fill) {
     const int64_t cout = yc * k;
     if (!conv_uses_mfma_c(x, cout, weight_dtype) || groups < 1 || yc % groups) return 0;
     if (k > 1 && yc % 32) return 0;      // a wave's 32 channels share one sub-position
     const int64_t cpg = yc / groups;
     if (cpg % 4 || 32 % cpg) return 0;   // a lane's four channels, a wave's 32, hold whole groups
     const BlockDims& d = kBlockDims[pick_block(box)];
-    const int wm = cout >= 128 ? wave_rows<128>() : cout > 32 ? wave_rows<64>() : wave_rows<32>();
+    const int nt = launch_nt(x.n, cout, box, fill);
+    const int wm = nt == 128 ? wave_rows<128>() : nt == 64 ? wave_rows<64>() : wave_rows<32>();
     return k * ceil_div(box.bt(), d.tb) * ceil_div(box.bh(), d.hb) * ceil_div(box.bw(), d.wb) * wm;
 }
 
-// A launch of fewer than 256 workgroups leaves CUs idle (256 CUs, two workgroups each when
-// busy). Splitting K s ways multiplies the workgroups by s: s is the largest count (up to 4) that
-// keeps the launch within one round of 512 workgroups, with at least two channel chunks per split.
+// A launch of fewer than 512 workgroups leaves CUs idle or alone (256 CUs, two workgroups each
+// when busy). Splitting K s ways multiplies the workgroups by s: s is the largest count (up to 4)
+// that keeps the launch within one round of 512 workgroups, with at least two channel chunks per
+// split.
 int32_t conv_split_count(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype, const Box& box,
                          bool split_fp32) {
     if (!conv_uses_mfma_c(x, cout, weight_dtype) || box.volume() == 0 || x.n == 0) return 1;
-    const int64_t wgs = conv_workgroups(x.n, cout, box);
+    const int64_t wgs = launch_workgroups(x.n, cout, box, true);
     const int64_t chunks = x.c / ((split_fp32 && x.dtype == VAE_DTYPE_F32) ? 16 : kCK);
-    if (wgs >= 256) return 1;
+    if (wgs >= 512) return 1;
     int64_t s = std::min<int64_t>({512 / wgs, chunks / 2, 4});
     return s >= 2 ? (int32_t)s : 1;
 }
@@ -220,8 +237,8 @@ int32_t conv_split_count(const vae_tensor_t& x, int64_t cout, int32_t weight_dty
 size_t conv_split_bytes(const vae_tensor_t& x, int64_t cout, const Box& box, int32_t splits) {
     if (splits <= 1) return 0;
     // one fp32 accumulator per (position of a 256-position block, channel of the tile)
-    return (size_t)splits * (size_t)conv_workgroups(x.n, cout, box) * 256 *
-           (size_t)conv_nt(cout) * sizeof(float);
+    return (size_t)splits * (size_t)launch_workgroups(x.n, cout, box, true) * 256 *
+           (size_t)launch_nt(x.n, cout, box, true) * sizeof(float);
 }
 
 int64_t packed_weight_elems(int64_t cout, int64_t cin) {
@@ -306,14 +323,15 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: fp16 tensors need the MFMA path");
     if (fz && k > 1 && !conv_uses_mfma_c(x, cout, weight_dtype))
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: a fused depth-to-space needs the MFMA path");
-    if (fz && fz->gn_ws && conv_gn_slots(x, y.c, weight_dtype, box, fz->groups, k) == 0)
+    if (fz && fz->gn_ws && conv_gn_slots(x, y.c, weight_dtype, box, fz->groups, k, false) == 0)
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: fused GroupNorm statistics need the MFMA path "
                                          "and 4, 8, 16 or 32 channels per group");
     if (fz && fz->part && fz->splits > 1 && !conv_uses_mfma_c(x, cout, weight_dtype))
         return fail(VAE_ERR_UNSUPPORTED, "conv3d: a split over K needs the MFMA path");
     if (conv_uses_mfma_c(x, cout, weight_dtype)) {
-        // output-channel tile: 128 wide, or 64 / 32 for narrow outputs (conv_out's 48 or 12)
-        switch (conv_nt(cout)) {
+        // output-channel tile: 128 wide, or 64 / 32 for narrow outputs (conv_out's 48 or 12) and
+        // for launches too small to fill the chip with 128-wide tiles
+        switch (launch_nt(x.n, cout, box, (flags & VAE_CONV_SPLIT_K) != 0)) {
             case 128:
                 return run_mfma_in<128>(x, w, bias, residual, y, box, split, packed, f16w, fz,
                                         stream);

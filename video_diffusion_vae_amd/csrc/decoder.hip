@@ -383,9 +383,9 @@ vae_status_t requirements(const vae_decoder& d, const Shape& in, const std::vect
                 // xs is the conv's input grid; the boxes scale with it (nearest folds included)
                 const BoxList bl = scaled_boxes(boxes, xs.t, ch, cw, fh, fw, &exact);
                 for (int b = 0; b < bl.n; ++b)
-                    slots += conv_gn_slots(x, ys.c, d.dtype, bl.b[b], d.groups, k);
+                    slots += conv_gn_slots(x, ys.c, d.dtype, bl.b[b], d.groups, k, true);
             } else {
-                slots = conv_gn_slots(x, ys.c, d.dtype, whole_box(x), d.groups, k);
+                slots = conv_gn_slots(x, ys.c, d.dtype, whole_box(x), d.groups, k, true);
             }
             r->gn = std::max<int64_t>(r->gn, ys.n * d.groups * slots * 3 * (int64_t)sizeof(double));
         };
@@ -645,9 +645,10 @@ struct Runner {
                       const vae_tensor_t& y, int layer, bool gn_next, const BoxList& bl,
                       const vae_layer_desc_t* up = nullptr, int32_t lsh = 0, int32_t lsw = 0,
                       const float* in_ab = nullptr) {
-        int32_t cf = conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer)
-                         ? VAE_CONV_SPLIT_FP32
-                         : 0;
+        // a launch too small to fill the chip may split over K and take narrower channel tiles
+        int32_t cf = VAE_CONV_SPLIT_K;
+        if (conv_splits(d->flags, d->layers.data(), (int)d->layers.size(), layer))
+            cf |= VAE_CONV_SPLIT_FP32;
         const void* w = d->ptrs[wi];
         if (d->packed[wi]) {
             // convs with fp16 operands were packed as fp16 (see vae_decoder_pack_weights); their
@@ -706,7 +707,7 @@ struct Runner {
             if (b.t0 < 0 || b.h0 < 0 || b.w0 < 0 || b.t1 > xl.t || b.h1 > xl.h || b.w1 > xl.w ||
                 b.volume() <= 0)
                 return fail(VAE_ERR_INVALID_ARG, "conv patch box outside the activation");
-            slots[i] = gn_next ? conv_gn_slots(xe, y.c, d->dtype, b, d->groups, k) : 0;
+            slots[i] = gn_next ? conv_gn_slots(xe, y.c, d->dtype, b, d->groups, k, true) : 0;
             total += slots[i];
         }
         double* part = reinterpret_cast<double*>(ws + L.gn);

@@ -53,11 +53,12 @@ vae_status_t launch_conv3d(const vae_tensor_t& x, const void* w, int32_t weight_
 bool conv_uses_mfma(const vae_tensor_t& x, const vae_tensor_t& y, int32_t weight_dtype);
 bool conv_uses_mfma_c(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype);
 // yc: channels of y; k = st * sh * sw of the fused depth-to-space (1 for none).
+// fill: the launch may take narrower channel tiles to fill the chip (VAE_CONV_SPLIT_K).
 int64_t conv_gn_slots(const vae_tensor_t& x, int64_t yc, int32_t weight_dtype, const Box& box,
-                      int32_t groups, int32_t k);
-// Split over K for launches that would leave most of the chip idle: the number of splits worth
-// making for a conv of x (its input grid) to `cout` channels over `box` (1: none), and the
-// scratch bytes of that many splits. `split_fp32`: the conv applies an fp32 x as hi + lo.
+                      int32_t groups, int32_t k, bool fill);
+// Split over K for launches that would leave most of the chip idle (VAE_CONV_SPLIT_K): the number
+// of splits worth making for a conv of x (its input grid) to `cout` channels over `box` (1: none),
+// and the scratch bytes of that many splits. `split_fp32`: the conv applies an fp32 x as hi + lo.
 int32_t conv_split_count(const vae_tensor_t& x, int64_t cout, int32_t weight_dtype, const Box& box,
                          bool split_fp32);
 size_t conv_split_bytes(const vae_tensor_t& x, int64_t cout, const Box& box, int32_t splits);
