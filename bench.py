@@ -326,9 +326,11 @@ def standalone_passes(v, dev, reps=5):
     # GroupNorm apply + SiLU at S3 (fp32 in, bf16 operand out), statistics given
     mr = torch.zeros((1, 32, 2), dtype=torch.float32, device=dev)
     mr[..., 1] = 1.0
+    gamma = torch.ones(128, dtype=torch.float32, device=dev)     # per-channel affine, as decoded
+    beta = torch.zeros(128, dtype=torch.float32, device=dev)
     yb = torch.empty(y.shape, dtype=torch.bfloat16, device=dev)
     out["gn_apply_silu_f32_to_bf16_s3"] = timed(
-        lambda: v.vae_groupnorm_apply(y, None, 32, mr, None, None, True, yb),
+        lambda: v.vae_groupnorm_apply(y, None, 32, mr, gamma, beta, True, yb),
         y.numel() * 4 + yb.numel() * 2)
     del y, yb
     torch.cuda.synchronize(dev)
