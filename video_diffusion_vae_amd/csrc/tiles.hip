@@ -62,7 +62,10 @@ __global__ __launch_bounds__(kThreads) void merge_finalize_kernel(float* __restr
 // once per element. With VEC, rows are read and written as float4: every row starts on a
 // 16-byte boundary, and element 4e + k lies in column (4e + k) / C. The arithmetic per element
 // is that of the kernels above.
-constexpr int kRowBlocks = 4096;           // at most this many blocks per sample
+// One block per row, up to the grid limit: many short blocks keep more loads in flight across the
+// chip than a few that loop over rows (the column table costs each block a few ramp evaluations
+// per thread, no memory traffic).
+constexpr int64_t kRowBlocks = INT32_MAX;
 constexpr int kMaxLdsColumns = 8192;       // per-column factors kept in LDS (32 KB)
 
 template <bool VEC>

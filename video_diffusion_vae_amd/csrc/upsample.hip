@@ -8,28 +8,22 @@
 // byte is read once and written once with 16-byte accesses.
 // Nearest: out(t, sh*h+dh, sw*w+dw) = in(t, h, w).
 //
-// The contiguous output segment of row (st*t+dt-(st-1), sh*h+dh) that the box's columns cover,
-// for one (input row t,h; sub-row dt,dh) pair, is cut into slices of 512 vectors, one block each.
+// One block handles one (input row t,h; sub-row dt,dh) pair. It writes the contiguous output
+// segment of row (st*t+dt-(st-1), sh*h+dh) that the box's columns cover.
 #include "kernels.h"
 
 namespace vae {
 namespace {
 
 constexpr int kThreads = 256;
-// Each block copies one slice of kSlice output vectors of a segment, kVecs per thread with all
-// loads in flight: many short blocks keep more loads in flight across the chip than one block per
-// segment looping over it.
-constexpr int kVecs = 2;
-constexpr int kSlice = kVecs * kThreads;
 
 template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void upsample_kernel(
     const T* __restrict__ x, T* __restrict__ y, int32_t xT, int32_t xH, int32_t xW, int32_t xC,
     int32_t yT, int32_t yH, int32_t yW, int32_t C, int32_t st, int32_t sh, int32_t sw,
-    int32_t d2s, Box b, int32_t slices) {
+    int32_t d2s, Box b) {
     const int n = blockIdx.z;
-    const int64_t row = blockIdx.x / slices;         // input row of the box
-    const int part = (int)(blockIdx.x - row * slices);
+    const int64_t row = blockIdx.x;                  // input row of the box
     const int sub = blockIdx.y;                      // dt * sh + dh
     const int t = b.t0 + (int)(row / b.bh());
     const int h = b.h0 + (int)(row % b.bh());
@@ -41,38 +35,16 @@ __global__ __launch_bounds__(kThreads) void upsample_kernel(
     T* yr = y + ((((int64_t)n * yT + to) * yH + ho) * yW + (int64_t)b.w0 * sw) * C;
     const int CV = C / V;
     const int seg = (int)b.bw() * sw * CV;           // output vectors in this segment
-    const int e0 = part * kSlice, e1 = e0 + kSlice < seg ? e0 + kSlice : seg;
-    // source of channel vector cv of output column wo (within the segment)
-    auto src_at = [&](int cv, int wo) {
-        const int wl = wo / sw, dw = wo - wl * sw;
+    for (int e = threadIdx.x; e < seg; e += kThreads) {
+        const int cv = e % CV;
+        const int wo = e / CV;                       // output column within the segment
+        const int wl = wo / sw, dw = wo % sw;
         const int slice = d2s ? (sub * sw + dw) : 0;
-        return xr + (int64_t)wl * xC + (int64_t)slice * C + cv * V;
-    };
-    auto src_of = [&](int e) { return src_at(e % CV, e / CV); };
-    if constexpr (V * sizeof(T) == 16) {
-        // When CV divides the block (every decoder width), a thread keeps one channel vector and
-        // its columns step by kThreads / CV: no division by CV per vector.
-        const bool fixed = kThreads % CV == 0;
-        const int cv_t = fixed ? (int)threadIdx.x % CV : 0;
-        const int wo_t = fixed ? (e0 + (int)threadIdx.x) / CV : 0;
-        const int wstep = fixed ? kThreads / CV : 0;
-        uint4 v[kVecs];
-#pragma unroll
-        for (int u = 0; u < kVecs; ++u) {
-            const int e = e0 + (int)threadIdx.x + u * kThreads;
-            if (e < e1)
-                v[u] = *reinterpret_cast<const uint4*>(fixed ? src_at(cv_t, wo_t + u * wstep)
-                                                              : src_of(e));
-        }
-#pragma unroll
-        for (int u = 0; u < kVecs; ++u) {
-            const int e = e0 + (int)threadIdx.x + u * kThreads;
-            if (e < e1) *reinterpret_cast<uint4*>(yr + (int64_t)e * V) = v[u];
-        }
-    } else {
-        for (int e = e0 + (int)threadIdx.x; e < e1; e += kThreads) {
-            const T* src = src_of(e);
-            T* dst = yr + (int64_t)e * V;
+        const T* src = xr + (int64_t)wl * xC + (int64_t)slice * C + cv * V;
+        T* dst = yr + (int64_t)e * V;
+        if (V * sizeof(T) == 16) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
 #pragma unroll
             for (int k = 0; k < V; ++k) dst[k] = src[k];
         }
@@ -82,24 +54,19 @@ __global__ __launch_bounds__(kThreads) void upsample_kernel(
 template <typename T>
 vae_status_t run(const vae_tensor_t& x, const Box& b, int32_t mode, int32_t st, int32_t sh,
                  int32_t sw, const vae_tensor_t& y, hipStream_t stream) {
-    constexpr int V16 = 16 / sizeof(T);
-    const int64_t vec = y.c % V16 == 0 ? V16 : 1;            // elements per vector
-    const int64_t seg = b.bw() * sw * (y.c / vec);           // output vectors per segment
-    const int32_t slices = (int32_t)ceil_div(seg, (int64_t)kSlice);
-    if (b.bt() * b.bh() * slices > INT32_MAX || st * sh > 65535 || x.n > 65535)
-        return fail(VAE_ERR_UNSUPPORTED, "upsample: grid too large");
-    dim3 grid((unsigned)(b.bt() * b.bh() * slices), (unsigned)(st * sh), (unsigned)x.n);
+    dim3 grid((unsigned)(b.bt() * b.bh()), (unsigned)(st * sh), (unsigned)x.n);
     const int32_t d2s = mode == VAE_UPSAMPLE_D2S;
-    if (vec == V16)
+    constexpr int V16 = 16 / sizeof(T);
+    if (y.c % V16 == 0)
         hipLaunchKernelGGL((upsample_kernel<T, V16>), grid, dim3(kThreads), 0, stream,
                            static_cast<const T*>(x.data), static_cast<T*>(y.data), (int32_t)x.t,
                            (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, (int32_t)y.t, (int32_t)y.h,
-                           (int32_t)y.w, (int32_t)y.c, st, sh, sw, d2s, b, slices);
+                           (int32_t)y.w, (int32_t)y.c, st, sh, sw, d2s, b);
     else
         hipLaunchKernelGGL((upsample_kernel<T, 1>), grid, dim3(kThreads), 0, stream,
                            static_cast<const T*>(x.data), static_cast<T*>(y.data), (int32_t)x.t,
                            (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, (int32_t)y.t, (int32_t)y.h,
-                           (int32_t)y.w, (int32_t)y.c, st, sh, sw, d2s, b, slices);
+                           (int32_t)y.w, (int32_t)y.c, st, sh, sw, d2s, b);
     VAE_HIP_CHECK(hipGetLastError());
     return VAE_OK;
 }
