@@ -1027,6 +1027,46 @@ void conv3d_mfma_kernel(MfmaArgs a) {
         for (int kc = kc0; kc + 1 < kc1; ++kc) chunk(kc, std::true_type{});
         chunk(kc1 - 1, std::false_type{});
     } else {
+        // Thread tid stages units tid + 256 k of each chunk's tile: unit_load issues a unit's load
+        // (none outside the image: zero padding), unit_store converts it and writes it to LDS.
+        constexpr int NUNIT = S::kPos * UPP;
+        constexpr int NU = (NUNIT + kMfmaThreads - 1) / kMfmaThreads;
+        auto unit_load = [&](int k, int c0x, Raw8<TR>& raw, bool& in, int& dst) {
+            const int u = tid + k * kMfmaThreads;
+            const bool valid = u < NUNIT;
+            const int pos = (valid ? u : 0) / UPP, g = (valid ? u : 0) % UPP;
+            const int f = pos / (HH * HW);
+            const int rem = pos - f * (HH * HW);
+            const int r = rem / HW;
+            const int c = rem - r * HW;
+            int tg = t_blk - 2 + f;
+            tg = tg < 0 ? 0 : tg;                          // causal: frames before 0 read frame 0
+            const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
+            in = valid && tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W;
+            if (in)
+                raw = load_raw8<TR>(xn + ((int64_t)(tg * xH + (hg >> a.lsh)) * xW + (wg >> a.lsw)) *
+                                             cin + c0x + g * 8);
+            dst = valid ? (f * HH + r) * RP + c * kRow + g * 16 : -1;
+        };
+        // sc, sh: the chunk's per-channel scale and shift of a normalised input (unused otherwise)
+        auto unit_store = [&](const Raw8<TR>& raw, bool in, int dst, const auto& sc,
+                              const auto& sh) {
+            if (dst < 0) return;
+            uint4 v, vl;
+            if constexpr (NORM) {
+                v = norm_operand<TR, F16>(raw, in, sc, sh);
+                vl = v;
+            } else {
+                to_operand<TR, SPLIT>(raw, in, v, vl);
+            }
+            uint8_t* d = &halo[dst];
+            *reinterpret_cast<uint4*>(d) = v;                  // split: hi in bytes 0..31 of the row
+            if constexpr (SPLIT) *reinterpret_cast<uint4*>(d + 32) = vl;  // lo in bytes 32..63
+        };
+        // A chunk's units are loaded in rounds of BATCH, a round's loads all in flight before its
+        // first write: one at a time, each unit would wait out a full memory latency. (Loading the
+        // next chunk's whole tile into registers while this one computes measured the same.)
+        constexpr int BATCH = (NT == 128 ? 4 : 8) / (int)(sizeof(TR) / 2);
         for (int kc = kc0; kc < kc1; ++kc) {
             const int c0 = kc * CK;
     #pragma unroll
@@ -1034,28 +1074,17 @@ void conv3d_mfma_kernel(MfmaArgs a) {
             __syncthreads();              // the previous chunk's LDS reads are done
             float sc[NORM ? 8 : 1], sh[NORM ? 8 : 1];   // every unit of a thread: group tid % 4
             if constexpr (NORM) load_norm8(a.nab, n, cin, c0 + (tid % UPP) * 8, sc, sh);
-            for (int u = tid; u < S::kPos * UPP; u += kMfmaThreads) {
-                const int pos = u / UPP, g = u % UPP;
-                const int f = pos / (HH * HW);
-                const int rem = pos - f * (HH * HW);
-                const int r = rem / HW;
-                const int c = rem - r * HW;
-                int tg = t_blk - 2 + f;
-                tg = tg < 0 ? 0 : tg;                      // causal: frames before 0 read frame 0
-                const int hg = h_blk - 1 + r, wg = w_blk - 1 + c;
-                uint4 v = make_uint4(0, 0, 0, 0);          // outside the image: zero padding
-                uint4 vl = make_uint4(0, 0, 0, 0);
-                if (tg < a.T && hg >= 0 && hg < a.H && wg >= 0 && wg < a.W) {
-                    const TR* src = xn + ((int64_t)(tg * xH + (hg >> a.lsh)) * xW + (wg >> a.lsw)) *
-                                             cin + c0 + g * 8;
-                    if constexpr (NORM) v = norm_operand<TR, F16>(load_raw8<TR>(src), true, sc, sh);
-                    else if constexpr (SPLIT) split8<TR>(src, v, vl);
-                    else v = load8<TR>(src);
-                }
-                uint8_t* dst = &halo[(f * HH + r) * RP + c * kRow + g * 16];
-                *reinterpret_cast<uint4*>(dst) = v;            // split: hi in bytes 0..31 of the row
-                if constexpr (SPLIT) *reinterpret_cast<uint4*>(dst + 32) = vl;  // lo in bytes 32..63
-            }
+            static_for<0, (NU + BATCH - 1) / BATCH>([&](auto round_c) {
+                constexpr int R0 = decltype(round_c)::value * BATCH;
+                constexpr int NR = NU - R0 < BATCH ? NU - R0 : BATCH;
+                Raw8<TR> raw[NR] = {};
+                bool inb[NR];
+                int dst[NR];
+#pragma unroll
+                for (int k = 0; k < NR; ++k) unit_load(R0 + k, c0, raw[k], inb[k], dst[k]);
+#pragma unroll
+                for (int k = 0; k < NR; ++k) unit_store(raw[k], inb[k], dst[k], sc, sh);
+            });
             __syncthreads();
 
             // 54 k steps (27 taps x 2). The A fragments of step s + 1 are read from LDS while the
