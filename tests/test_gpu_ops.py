@@ -97,6 +97,9 @@ NARROW_CASES = [
     ((2, 16, 9, 10), 32, 64, "bf16", "bf16", True, None),               # 16 x 8 x 2, N = 2
     ((1, 17, 13, 30), 64, 128, "bf16", "f32", True, (1, 17, 2, 13, 10, 20)),   # 16 x 8 x 2 box
     ((1, 16, 12, 12), 64, 48, "f32", "f32", False, None),               # 16 x 4 x 4, Cout 48
+    # 32-wide channel tiles: staging rounds of 8 units, then a last round of 4 or 3
+    ((1, 16, 22, 10), 96, 32, "bf16", "f32", True, None),               # 16 x 8 x 2, Cout 32
+    ((1, 4, 16, 12), 64, 12, "bf16", "bf16", False, None),              # 4 x 16 x 4, Cout 12
 ]
 
 
