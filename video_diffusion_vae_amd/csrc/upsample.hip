@@ -8,8 +8,10 @@
 // byte is read once and written once with 16-byte accesses.
 // Nearest: out(t, sh*h+dh, sw*w+dw) = in(t, h, w).
 //
-// One block handles one (input row t,h; sub-row dt,dh) pair. It writes the contiguous output
-// segment of row (st*t+dt-(st-1), sh*h+dh) that the box's columns cover.
+// upsample_kernel (nearest, and depth-to-space with vectors that do not divide C): one block per
+// (input row t,h; sub-row dt,dh) pair writes the contiguous output segment of row
+// (st*t+dt-(st-1), sh*h+dh) that the box's columns cover. d2s_rows_kernel (depth-to-space with
+// 16-byte vectors) goes by input rows instead: contiguous reads, writes in runs of sw*C.
 #include "kernels.h"
 
 namespace vae {
@@ -51,12 +53,65 @@ __global__ __launch_bounds__(kThreads) void upsample_kernel(
     }
 }
 
+// Depth-to-space by input rows: one block per slice of 512 16-byte vectors of an input row
+// segment (two per thread, both loads in flight). The reads are contiguous; each vector goes to
+// its output position, so the writes come in runs of sw * C elements (one output row segment of
+// one sub-row per input position).
+template <typename T, int V>
+__global__ __launch_bounds__(kThreads) void d2s_rows_kernel(
+    const T* __restrict__ x, T* __restrict__ y, int32_t xT, int32_t xH, int32_t xW, int32_t xC,
+    int32_t yT, int32_t yH, int32_t yW, int32_t C, int32_t st, int32_t sh, int32_t sw, Box b,
+    int32_t slices) {
+    constexpr int kVecs = 2;
+    const int n = blockIdx.y;
+    const int64_t row = blockIdx.x / slices;
+    const int part = (int)(blockIdx.x - row * slices);
+    const int t = b.t0 + (int)(row / b.bh());
+    const int h = b.h0 + (int)(row % b.bh());
+    const T* xr = x + ((((int64_t)n * xT + t) * xH + h) * xW + b.w0) * xC;
+    const int XV = xC / V, CV = C / V;
+    const int seg = (int)b.bw() * XV;                // input vectors in this row segment
+    uint4 v[kVecs];
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+        const int e = part * kVecs * kThreads + u * kThreads + (int)threadIdx.x;
+        if (e < seg) v[u] = *reinterpret_cast<const uint4*>(xr + (int64_t)e * V);
+    }
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+        const int e = part * kVecs * kThreads + u * kThreads + (int)threadIdx.x;
+        if (e >= seg) continue;
+        const int wl = e / XV, j = e - wl * XV;      // input column, vector within the position
+        const int p = j / CV, cv = j - p * CV;       // sub-position ((dt*sh + dh)*sw + dw)
+        const int dw = p % sw, dh = (p / sw) % sh, dt = p / (sw * sh);
+        const int to = st * t + dt - (st - 1);
+        if (to < 0) continue;                        // causal drop of the first st-1 frames
+        const int64_t o = ((((int64_t)n * yT + to) * yH + sh * h + dh) * yW +
+                           (int64_t)sw * (b.w0 + wl) + dw) * C + cv * V;
+        *reinterpret_cast<uint4*>(y + o) = v[u];
+    }
+}
+
 template <typename T>
 vae_status_t run(const vae_tensor_t& x, const Box& b, int32_t mode, int32_t st, int32_t sh,
                  int32_t sw, const vae_tensor_t& y, hipStream_t stream) {
+    constexpr int V16 = 16 / sizeof(T);
+    if (mode == VAE_UPSAMPLE_D2S && y.c % V16 == 0) {
+        const int64_t seg = b.bw() * (x.c / V16);
+        const int64_t slices = ceil_div(seg, (int64_t)(2 * kThreads));
+        if (b.bt() * b.bh() * slices <= INT32_MAX && x.n <= 65535) {
+            const dim3 g2((unsigned)(b.bt() * b.bh() * slices), (unsigned)x.n);
+            hipLaunchKernelGGL((d2s_rows_kernel<T, V16>), g2, dim3(kThreads), 0, stream,
+                               static_cast<const T*>(x.data), static_cast<T*>(y.data),
+                               (int32_t)x.t, (int32_t)x.h, (int32_t)x.w, (int32_t)x.c,
+                               (int32_t)y.t, (int32_t)y.h, (int32_t)y.w, (int32_t)y.c, st, sh, sw,
+                               b, (int32_t)slices);
+            VAE_HIP_CHECK(hipGetLastError());
+            return VAE_OK;
+        }
+    }
     dim3 grid((unsigned)(b.bt() * b.bh()), (unsigned)(st * sh), (unsigned)x.n);
     const int32_t d2s = mode == VAE_UPSAMPLE_D2S;
-    constexpr int V16 = 16 / sizeof(T);
     if (y.c % V16 == 0)
         hipLaunchKernelGGL((upsample_kernel<T, V16>), grid, dim3(kThreads), 0, stream,
                            static_cast<const T*>(x.data), static_cast<T*>(y.data), (int32_t)x.t,
