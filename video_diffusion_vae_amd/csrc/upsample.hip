@@ -96,7 +96,8 @@ template <typename T>
 vae_status_t run(const vae_tensor_t& x, const Box& b, int32_t mode, int32_t st, int32_t sh,
                  int32_t sw, const vae_tensor_t& y, hipStream_t stream) {
     constexpr int V16 = 16 / sizeof(T);
-    if (mode == VAE_UPSAMPLE_D2S && y.c % V16 == 0) {
+    // by input rows when its writes come in runs of at least a 128-byte line (sw * C elements)
+    if (mode == VAE_UPSAMPLE_D2S && y.c % V16 == 0 && sw * y.c * (int64_t)sizeof(T) >= 128) {
         const int64_t seg = b.bw() * (x.c / V16);
         const int64_t slices = ceil_div(seg, (int64_t)(2 * kThreads));
         if (b.bt() * b.bh() * slices <= INT32_MAX && x.n <= 65535) {
