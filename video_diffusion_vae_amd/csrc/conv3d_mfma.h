@@ -751,13 +751,15 @@ void conv3d_mfma_kernel(MfmaArgs a) {
     const int split = __builtin_amdgcn_readfirstlane(logical / per_split);
     const int tile = __builtin_amdgcn_readfirstlane(logical - split * per_split);
     const int nt = __builtin_amdgcn_readfirstlane(tile / a.n_mblocks);
+    // block order within a channel tile: T fastest, so that the workgroups an XCD runs at once
+    // are temporal neighbours, which stage 2 of their TB + 2 frames in common (hits in its L2)
     int mb = tile - nt * a.n_mblocks;
+    const int bt_i = mb % a.nbt;
+    mb /= a.nbt;
     const int bw_i = mb % a.nbw;
     mb /= a.nbw;
     const int bh_i = mb % a.nbh;
-    mb /= a.nbh;
-    const int bt_i = mb % a.nbt;
-    const int n = mb / a.nbt;
+    const int n = mb / a.nbh;
     const int t_blk = a.box.t0 + bt_i * TB;
     const int h_blk = a.box.h0 + bh_i * HB;
     const int w_blk = a.box.w0 + bw_i * WB;
@@ -1175,13 +1177,15 @@ void conv3d_reduce_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(16))) float ep[kMfmaWaves * 32 * kEp];
     const int tile = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
     const int nt = __builtin_amdgcn_readfirstlane(tile / a.n_mblocks);
+    // block order within a channel tile: T fastest, so that the workgroups an XCD runs at once
+    // are temporal neighbours, which stage 2 of their TB + 2 frames in common (hits in its L2)
     int mb = tile - nt * a.n_mblocks;
+    const int bt_i = mb % a.nbt;
+    mb /= a.nbt;
     const int bw_i = mb % a.nbw;
     mb /= a.nbw;
     const int bh_i = mb % a.nbh;
-    mb /= a.nbh;
-    const int bt_i = mb % a.nbt;
-    const int n = mb / a.nbt;
+    const int n = mb / a.nbh;
     const int t_blk = a.box.t0 + bt_i * TB;
     const int h_blk = a.box.h0 + bh_i * HB;
     const int w_blk = a.box.w0 + bw_i * WB;
