@@ -178,49 +178,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return (bid % kXcds) * per + bid / kXcds;
 }
 
-// 8 input channels starting at p, as 8 bf16 in one 16-byte word.
-template <typename TI> __device__ __forceinline__ uint4 load8(const TI* p);
-template <> __device__ __forceinline__ uint4 load8<uint16_t>(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-template <> __device__ __forceinline__ uint4 load8<_Float16>(const _Float16* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-template <> __device__ __forceinline__ uint4 load8<float>(const float* p) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    uint4 r;
-    r.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
-    r.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
-    r.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
-    r.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
-    return r;
-}
-
-// The hi + lo bf16 split of 8 fp32 values: hi = bf16(x), lo = bf16(x - hi).
-template <typename TI> __device__ __forceinline__ void split8(const TI* p, uint4& hi, uint4& lo);
-template <> __device__ __forceinline__ void split8<uint16_t>(const uint16_t* p, uint4& hi,
-                                                             uint4& lo) {
-    hi = *reinterpret_cast<const uint4*>(p);
-    lo = make_uint4(0, 0, 0, 0);
-}
-template <> __device__ __forceinline__ void split8<float>(const float* p, uint4& hi, uint4& lo) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint16_t h0 = f32_to_bf16(v[2 * i]), h1 = f32_to_bf16(v[2 * i + 1]);
-        const uint16_t l0 = f32_to_bf16(v[2 * i] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(v[2 * i + 1] - bf16_to_f32(h1));
-        h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-    hi = make_uint4(h[0], h[1], h[2], h[3]);
-    lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
 template <typename TO> __device__ __forceinline__ void load4(const TO* p, float* v);
 template <> __device__ __forceinline__ void load4<float>(const float* p, float* v) {
     const float4 a = *reinterpret_cast<const float4*>(p);
