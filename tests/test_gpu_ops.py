@@ -605,6 +605,13 @@ UP_CASES = [
     ("f32", (1, 1, 3, 3, 4), "nearest", (1, 2, 3), (0, 1, 1, 3, 0, 2)),
     ("f16", (1, 3, 4, 5, 64), "d2s", (2, 2, 2), None),
     ("f16", (1, 2, 3, 4, 16), "nearest", (1, 2, 2), (0, 2, 1, 3, 0, 4)),
+    # depth-to-space whose output rows come in runs of at least 128 bytes (sw * C): the kernel
+    # that goes by input rows, with ragged 512-vector slices and boxes
+    ("f32", (1, 3, 4, 6, 256), "d2s", (2, 2, 2), None),
+    ("bf16", (1, 2, 3, 5, 512), "d2s", (2, 2, 2), None),
+    ("bf16", (2, 3, 4, 6, 256), "d2s", (1, 2, 2), (1, 3, 1, 4, 2, 6)),
+    ("f16", (1, 2, 3, 4, 512), "d2s", (2, 2, 2), (0, 2, 0, 3, 1, 3)),
+    ("f32", (1, 2, 3, 70, 128), "d2s", (1, 1, 2), None),
 ]
 
 
