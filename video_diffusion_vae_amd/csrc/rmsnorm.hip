@@ -22,7 +22,9 @@ constexpr int kThreads = 256;
 // flight across the chip than a few that loop. Their set-up is one (gamma, beta) pair per thread
 // into an LDS table. Measured over the Wan-shaped 720p decode's RMS norms: 10.65 ms with 8192
 // looping blocks (four steps in flight), 11.1 ms short blocks with (gamma, beta) loaded per
-// thread, 9.85 ms with the table, 9.77 ms with two steps per block, 11.0 ms with one.
+// thread, 9.85 ms with the table, 9.77 ms with two steps per block, 11.0 ms with one. Filling the
+// table after the block's activation loads are issued (one memory latency instead of two, which
+// is what the GroupNorm apply needed) measured slower here: 9.76-9.88 -> 10.41-10.43 ms.
 constexpr int64_t kMaxBlocks = INT32_MAX;
 constexpr int kMaxC = 2048;                  // C / 8 <= 256 threads per position
 constexpr int kUnroll = 2;          // block steps (positions per thread) in flight at once
