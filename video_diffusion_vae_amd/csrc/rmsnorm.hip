@@ -24,7 +24,9 @@ constexpr int kThreads = 256;
 // looping blocks (four steps in flight), 11.1 ms short blocks with (gamma, beta) loaded per
 // thread, 9.85 ms with the table, 9.77 ms with two steps per block, 11.0 ms with one. Filling the
 // table after the block's activation loads are issued (one memory latency instead of two, which
-// is what the GroupNorm apply needed) measured slower here: 9.76-9.88 -> 10.41-10.43 ms.
+// is what the GroupNorm apply needed) measured slower here: 9.76-9.88 -> 10.41-10.43 ms. The
+// fp16-output instances hold 80 registers (6 waves per SIMD); bounding them to 8 waves spills
+// (12.5 ms), to 7 waves changes nothing (9.81-9.83 ms).
 constexpr int64_t kMaxBlocks = INT32_MAX;
 constexpr int kMaxC = 2048;                  // C / 8 <= 256 threads per position
 constexpr int kUnroll = 2;          // block steps (positions per thread) in flight at once
