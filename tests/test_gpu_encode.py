@@ -29,7 +29,11 @@ def v():
 
 S2D_CASES = [
     # (N, T, H, W, C), dtype, (st, sh, sw)
-    ((1, 9, 16, 24, 4), "bf16", (1, 4, 4)),      # the patchify of a padded video: 8-byte rows
+    ((1, 9, 16, 24, 4), "bf16", (1, 4, 4)),      # the patchify of a padded video: pairs of
+                                                 # sub-positions in 16-byte vectors
+    ((1, 5, 8, 12, 2), "f32", (2, 2, 2)),        # fp32 pairs, causal front copy
+    ((2, 4, 6, 8, 4), "f16", (1, 2, 4)),         # fp16 pairs, two samples
+    ((1, 3, 4, 6, 4), "bf16", (2, 2, 1)),        # sw odd: 8-byte vectors
     ((1, 5, 8, 12, 32), "f32", (2, 2, 2)),       # 16-byte vectors, causal front copy
     ((2, 3, 4, 6, 64), "bf16", (2, 2, 2)),
     ((1, 9, 6, 10, 3), "f32", (4, 2, 1)),        # scalar rows, three front copies

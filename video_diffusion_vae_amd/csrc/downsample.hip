@@ -11,6 +11,9 @@
 // sh*h + dh). Writes are fully contiguous. A wave's reads cover, for each sub-row, consecutive
 // input columns, i.e. whole input lines spread over the wave (with 4 bf16 channels, the patchify
 // of a padded video: 16 pieces of 8 bytes per output position, each line read once).
+// When a 16-byte vector holds G = 2 whole sub-positions (C = 4 bf16 or 2 fp32 channels) and G
+// divides sw, the sub-positions (dw, dw + 1) of one output vector are neighbouring columns of one
+// input row, so the pair moves as one 16-byte vector.
 #include "kernels.h"
 
 namespace vae {
@@ -18,15 +21,16 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T, int V>
+// V elements per vector; G sub-positions per vector (1, or 2 with V = 2 * C)
+template <typename T, int V, int G>
 __global__ __launch_bounds__(kThreads) void space_to_depth_kernel(
     const T* __restrict__ x, T* __restrict__ y, int32_t xT, int32_t xH, int32_t xW, int32_t C,
     int32_t yT, int32_t yH, int32_t yW, int32_t st, int32_t sh, int32_t sw) {
     const int n = blockIdx.y;
     const int64_t row = blockIdx.x;                  // output row t * yH + h
     const int t = (int)(row / yH), h = (int)(row % yH);
-    const int CV = C / V;                            // vectors per sub-position
-    const int kv = st * sh * sw * CV;                // vectors per output position
+    const int CV = G > 1 ? 1 : C / V;                // vectors per sub-position (group)
+    const int kv = st * sh * sw * CV / G;            // vectors per output position
     const int seg = yW * kv;                         // vectors in the output row
     const int64_t xrow = (int64_t)xW * C;
     const T* xn = x + (int64_t)n * xT * xH * xrow;
@@ -34,7 +38,8 @@ __global__ __launch_bounds__(kThreads) void space_to_depth_kernel(
     for (int e = threadIdx.x; e < seg; e += kThreads) {
         const int wo = e / kv;
         const int j = e - wo * kv;
-        const int p = j / CV, cv = j - p * CV;       // sub-position ((dt*sh + dh)*sw + dw)
+        const int pg = j / CV, cv = j - pg * CV;
+        const int p = pg * G;                        // sub-position ((dt*sh + dh)*sw + dw)
         const int dw = p % sw, dh = (p / sw) % sh, dt = p / (sw * sh);
         int ti = st * t + dt - (st - 1);
         ti = ti < 0 ? 0 : ti;                        // the causal front copies of frame 0
@@ -52,11 +57,11 @@ __global__ __launch_bounds__(kThreads) void space_to_depth_kernel(
     }
 }
 
-template <typename T, int V>
+template <typename T, int V, int G = 1>
 void launch(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw, const vae_tensor_t& y,
             hipStream_t stream) {
     const dim3 grid((unsigned)(y.t * y.h), (unsigned)x.n);
-    hipLaunchKernelGGL((space_to_depth_kernel<T, V>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((space_to_depth_kernel<T, V, G>), grid, dim3(kThreads), 0, stream,
                        static_cast<const T*>(x.data), static_cast<T*>(y.data), (int32_t)x.t,
                        (int32_t)x.h, (int32_t)x.w, (int32_t)x.c, (int32_t)y.t, (int32_t)y.h,
                        (int32_t)y.w, st, sh, sw);
@@ -67,6 +72,7 @@ void run(const vae_tensor_t& x, int32_t st, int32_t sh, int32_t sw, const vae_te
          hipStream_t stream) {
     constexpr int V16 = 16 / sizeof(T), V8 = 8 / sizeof(T);
     if (x.c % V16 == 0) launch<T, V16>(x, st, sh, sw, y, stream);
+    else if (2 * x.c == V16 && sw % 2 == 0) launch<T, V16, 2>(x, st, sh, sw, y, stream);
     else if (x.c % V8 == 0) launch<T, V8>(x, st, sh, sw, y, stream);
     else launch<T, 1>(x, st, sh, sw, y, stream);
 }
