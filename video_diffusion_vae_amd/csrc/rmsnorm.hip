@@ -26,10 +26,20 @@ constexpr int kThreads = 256;
 // table after the block's activation loads are issued (one memory latency instead of two, which
 // is what the GroupNorm apply needed) measured slower here: 9.76-9.88 -> 10.41-10.43 ms. The
 // fp16-output instances hold 80 registers (6 waves per SIMD); bounding them to 8 waves spills
-// (12.5 ms), to 7 waves changes nothing (9.81-9.83 ms).
+// (12.5 ms), to 7 waves changes nothing (9.81-9.83 ms). Stores carry the nontemporal hint
+// (9.82-9.85 -> 9.62-9.69 ms); on the loads it made the pass slower (10.03-10.08 ms), as on both.
 constexpr int64_t kMaxBlocks = INT32_MAX;
 constexpr int kMaxC = 2048;                  // C / 8 <= 256 threads per position
 constexpr int kUnroll = 2;          // block steps (positions per thread) in flight at once
+
+// Elem<T>::store with the nontemporal hint (the backend merges a thread's 8 into 16-byte stores)
+__device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(_Float16* p, float v) {
+    __builtin_nontemporal_store((_Float16)v, p);
+}
+__device__ __forceinline__ void store_nt(uint16_t* p, float v) {
+    __builtin_nontemporal_store(f32_to_bf16(v), p);
+}
 
 template <typename TI, typename TO>
 __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict__ x,
@@ -107,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void rms_norm_kernel(const TI* __restrict
                 for (int k = 0; k < 8; ++k) {
                     float z = fmaf(v[u][k] * r, sc[k], sh[k]);
                     if (silu) z = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-                    Elem<TO>::store(dst + k, z);
+                    store_nt(dst + k, z);
                 }
             }
         }
