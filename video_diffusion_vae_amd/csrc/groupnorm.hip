@@ -399,7 +399,8 @@ __global__ __launch_bounds__(kThreads) void gn_apply_kernel(
     }
     // Streaming accesses: x is read once and y is next read by another kernel, long after the
     // caches have turned over, so both go with the nontemporal hint (measured 3% faster at the
-    // decode's fp32 -> bf16 shapes).
+    // decode's fp32 -> bf16 shapes; the hint on the stores alone or the loads alone is slower
+    // than on both: 5.02-5.05 and 5.19-5.24 ms per decode against 4.84-4.85 ms).
     auto apply = [&](int e, const u32x4_t& raw) {
         const TI* v = reinterpret_cast<const TI*>(&raw);
         TO out[V];
