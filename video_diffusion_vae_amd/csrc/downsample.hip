@@ -11,7 +11,7 @@
 // sh*h + dh). Writes are fully contiguous. A wave's reads cover, for each sub-row, consecutive
 // input columns, i.e. whole input lines spread over the wave (with 4 bf16 channels, the patchify
 // of a padded video: 16 pieces of 8 bytes per output position, each line read once).
-// When a 16-byte vector holds G = 2 whole sub-positions (C = 4 bf16 or 2 fp32 channels) and G
+// When a 16-byte vector holds G = 2 whole sub-positions (C = 4 bf16/fp16 or 2 fp32 channels) and G
 // divides sw, the sub-positions (dw, dw + 1) of one output vector are neighbouring columns of one
 // input row, so the pair moves as one 16-byte vector.
 #include "kernels.h"
